@@ -1,0 +1,155 @@
+"""Pins of the oracle's rotation (O1), attention (O5) and cache builder (CPU)."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import rotate, attention, cache, placement, quant
+from oracle.rounding import bf16_bits_to_f64, f64_to_bf16_bits
+from synth import bf16_from_f32, get
+
+
+def _haar(rng, d=128):
+    q, r = np.linalg.qr(rng.standard_normal((d, d)))
+    return q * np.sign(np.diag(r))[None, :]
+
+
+def test_generated_rotations_are_orthogonal():
+    rk, rv = get("c2_qwen3_8b_bs1").rotations()
+    for r in np.concatenate([rk, rv]):
+        r = r.astype(np.float64)
+        assert np.abs(r.T @ r - np.eye(128)).max() < 2e-6   # fp32-rounded Q factor
+    q = _haar(np.random.default_rng(0))
+    assert np.abs(q.T @ q - np.eye(128)).max() < 1e-13
+
+
+def test_rotation_preserves_inner_products():
+    # orthogonal x' = x R keeps q.k (attention scores) unchanged before rounding
+    rng = np.random.default_rng(1)
+    r = _haar(rng)
+    q = rng.standard_normal((50, 128))
+    k = rng.standard_normal((70, 128))
+    lhs = rotate.rotate_f64(q, r) @ rotate.rotate_f64(k, r).T
+    rhs = q @ k.T
+    scale = np.linalg.norm(q, axis=1)[:, None] * np.linalg.norm(k, axis=1)[None, :]
+    assert (np.abs(lhs - rhs) <= 1e-12 * scale).all()
+    assert np.allclose(np.linalg.norm(rotate.rotate_f64(q, r), axis=1), np.linalg.norm(q, axis=1), rtol=1e-13)
+
+
+def test_rotation_orientation_signed_permutation():
+    # x' = x . R with R[i, pi(i)] = s_i  ->  x'[pi(i)] = s_i x[i] (catches R vs R^T)
+    rng = np.random.default_rng(2)
+    pi = rng.permutation(128)
+    s = rng.choice([-1.0, 1.0], 128)
+    r = np.zeros((128, 128), np.float32)
+    r[np.arange(128), pi] = s
+    xb = bf16_from_f32(rng.standard_normal((9, 128)).astype(np.float32))
+    out = rotate.rotate_to_bf16(xb, r)
+    x = bf16_bits_to_f64(xb)
+    exp = np.zeros_like(x)
+    exp[:, pi] = x * s
+    assert np.array_equal(bf16_bits_to_f64(out), exp)
+    assert np.array_equal(rotate.rotate_to_bf16(xb, np.eye(128, dtype=np.float32)), xb)
+
+
+def test_rotation_correctly_rounded_small_exact():
+    rng = np.random.default_rng(3)
+    r = _haar(rng).astype(np.float32)
+    xb = bf16_from_f32(rng.standard_normal((3, 128)).astype(np.float32))
+    out = rotate.rotate_to_bf16(xb, r)
+    x = bf16_bits_to_f64(xb)
+    rd = r.astype(np.float64)
+    for i in range(3):
+        for j in range(0, 128, 9):
+            assert out[i, j] == rotate.exact_row_dot_bf16(x[i], rd[:, j])
+
+
+def test_rotation_guard_catches_fp64_double_rounding():
+    # exact x.R = 1 + 2^-8 + 2^-60 lies just above a bf16 tie; the fp64 sum
+    # drops 2^-60 and lands on the tie (-> 1.0); the guard recomputes exactly.
+    x = np.zeros((1, 128), np.float32)
+    x[0, :3] = 1.0
+    r = np.zeros((128, 128), np.float32)
+    r[0, 0], r[1, 0], r[2, 0] = 1.0, 2.0 ** -8, 2.0 ** -60
+    r[0, 1], r[1, 1] = 1.0, 2.0 ** -8            # exact tie -> even -> 1.0
+    out = rotate.rotate_to_bf16(bf16_from_f32(x), r)
+    assert bf16_bits_to_f64(out[0, 0]) == 1.0 + 2.0 ** -7
+    assert bf16_bits_to_f64(out[0, 1]) == 1.0
+    naive = f64_to_bf16_bits(bf16_bits_to_f64(bf16_from_f32(x)) @ r.astype(np.float64))
+    assert bf16_bits_to_f64(naive[0, 0]) == 1.0          # what the unguarded path gives
+
+
+def _brute_attention(q, k, v):
+    """softmax(q k^T / sqrt(d)) v with plain Python loops and math.exp."""
+    d = len(q)
+    logits = [sum(q[i] * kr[i] for i in range(d)) / math.sqrt(d) for kr in k]
+    m = max(logits)
+    w = [math.exp(l - m) for l in logits]
+    tot = sum(w)
+    return [sum(w[t] * v[t][j] for t in range(len(v))) / tot for j in range(d)]
+
+
+@pytest.mark.parametrize("t", [1, 2, 5, 8])
+def test_attention_brute_force(t):
+    rng = np.random.default_rng(10 + t)
+    q = rng.standard_normal((3, 128)) * 2
+    k = rng.standard_normal((t, 128))
+    v = rng.standard_normal((t, 128))
+    got = attention.attend(q, k, v)
+    for i in range(3):
+        assert np.allclose(got[i], _brute_attention(q[i].tolist(), k.tolist(), v.tolist()),
+                           rtol=0, atol=1e-13)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(20)
+    k = rng.standard_normal((7, 128))
+    v = rng.standard_normal((7, 128))
+    q = rng.standard_normal((4, 128))
+    one = attention.attend(q, k[:1], v[:1])
+    assert np.array_equal(one, np.repeat(v[:1], 4, axis=0))           # single token
+    assert np.allclose(attention.attend(np.zeros((2, 128)), k, v), v.mean(0), atol=1e-15)
+
+
+def test_split_merge_equals_unsplit():
+    rng = np.random.default_rng(21)
+    k = rng.standard_normal((300, 128)) * 2
+    v = rng.standard_normal((300, 128))
+    q = rng.standard_normal((4, 128)) * 3
+    full = attention.attend(q, k, v)
+    for cuts in ([150], [1, 2, 299], [17, 100, 101, 250], list(range(10, 300, 10))):
+        assert np.abs(attention.attend_split(q, k, v, cuts) - full).max() <= 1e-14
+
+
+def test_unrotate_orientation_and_basis_invariance():
+    rng = np.random.default_rng(22)
+    rk, rv = _haar(rng), _haar(rng)
+    q = rng.standard_normal((4, 128))
+    k = rng.standard_normal((40, 128))
+    v = rng.standard_normal((40, 128))
+    # attention in the rotated basis, un-rotated with R_V^T, equals attention
+    # in the original basis (no quantization, no rounding)
+    o = attention.decode_head(rotate.rotate_f64(q, rk), rotate.rotate_f64(k, rk),
+                              rotate.rotate_f64(v, rv), rv)
+    assert np.abs(o - attention.attend(q, k, v)).max() < 1e-12
+
+
+def test_head_cache_identity_rotation_segments():
+    w = get("c1_tiny")
+    n = 700
+    k = w.keys(0, 0, n)[:, 0]
+    v = w.values(0, 0, n)[:, 0]
+    eye = np.eye(128, dtype=np.float32)
+    hc = cache.HeadCache(k, v, eye, eye, np.float32(0.9), np.float32(0.9), 128, 4, 128, 16)
+    assert np.array_equal(hc.k_rot, k) and np.array_equal(hc.v_rot, v)
+    a, b = hc.int2
+    assert (a, b) == (4, placement.s_quant(n, 4, 128, 16))
+    c, s16, z16 = quant.quantize_rows(bf16_bits_to_f64(k[a:b]), np.float32(0.9), 128)
+    assert np.array_equal(c, hc.kc) and np.array_equal(s16, hc.ks)
+    kd, vd = hc.dequant_f32()
+    assert np.array_equal(kd[:4], bf16_bits_to_f64(k[:4]).astype(np.float32))
+    assert np.array_equal(kd[b:], bf16_bits_to_f64(k[b:]).astype(np.float32))
+    assert np.array_equal(kd[a:b], quant.dequant_rows(c, s16, z16, 128).astype(np.float32))
+    rows = hc.window_rows()
+    assert sorted(rows.values()) == list(range(4)) + list(range(b, n))
