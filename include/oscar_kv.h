@@ -1,0 +1,209 @@
+/*
+ * liboscar_kv -- INT2 KV cache with a fixed per-head rotation and clipped
+ * asymmetric 2-bit quantization, BF16 sink / recent windows, and paged GQA
+ * decode attention over the mixed cache.  MI355X (gfx950) only.
+ *
+ * Sources (the pages this library implements):
+ *  [OSCAR]  "OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV
+ *           Cache Quantization", paperlayer.ai summary: section 3 (fixed
+ *           rotations and clipping thresholds, affine asymmetric INT2 with
+ *           scale and zero point, per-token groups), section 4 (mixed
+ *           precision paged cache with BF16 sink and recent windows, fused
+ *           clip-quantize-pack writing four 2-bit codes per byte, demotion
+ *           of the oldest recent tokens, decode attention that unpacks INT2
+ *           and accumulates in floating point, segments merged after two
+ *           launches), section 5 (R = U . H_Had . P_br), appendix B
+ *           (Algorithm 1: rotate before the cache write).
+ *  [OScaR]  OScaR reading notes (zhongzhuzhou.org): uniform quantizer and
+ *           dequantizer formulas, orthogonal transforms preserve q.k.
+ *  [WUSH]   WUSH-KV notes (paper.rainbus.top), "method step details": the
+ *           key transform is applied after RoPE to new keys and queries;
+ *           S_quant advances over S_flush-aligned segments beyond the
+ *           S_sink / S_keep windows; kappa-quantile clipped affine quantizer.
+ *
+ * Conventions
+ *  - head_dim D = 128, page size P = 16, G in {32, 64, 128}, ng = 128 / G.
+ *  - Rows are row vectors: x' = x . R with R row-major [128][128] fp32.
+ *    Keys and queries use R_K of their KV head (query head hq belongs to KV
+ *    head hq / g, g = Hq / Hkv); values use R_V.  The decode output is
+ *    returned in the original basis: o = o' . R_V^T.
+ *  - bf16 and fp16 values travel as uint16_t bit patterns.
+ *  - Every pointer argument is a DEVICE pointer unless its name ends in
+ *    _host.  The caller owns all memory; the library allocates nothing and
+ *    keeps no state between calls.
+ *  - Calls enqueue work on `stream` (a hipStream_t; NULL = default stream)
+ *    and return without waiting.  Calls that touch the same cache or the
+ *    same workspace must be ordered on one stream by the caller.
+ *  - All argument checks run on the host before anything is enqueued; on a
+ *    non-zero status nothing was enqueued (except OSCAR_ERR_HIP, which
+ *    reports a failed launch).  Non-finite inputs, and rotated values whose
+ *    magnitude exceeds the fp16 range, are outside the contract.
+ *
+ * Cache placement (per cache row, after `len` tokens)            [OSCAR s4, WUSH]
+ *  S_quant(len) = S_sink + S_flush * max(0, floor((len - S_sink - S_keep) / S_flush))
+ *  position p < min(len, S_sink)          -> sink window, bf16, slot p
+ *  S_sink <= p < S_quant                   -> INT2, logical page (p - S_sink) / 16,
+ *                                            slot (p - S_sink) % 16
+ *  max(S_quant, S_sink) <= p < len         -> recent ring, bf16,
+ *                                            slot (p - S_sink) mod R,
+ *                                            R = roundup16(S_keep + S_flush)
+ *  Rows are always the bf16 rounding of the exact x . R; INT2 rows are the
+ *  quantization of that bf16 row, so the cache does not depend on how the
+ *  tokens were grouped into append calls.
+ *
+ * Quantizer (one token, one KV head, one group of G channels)    [OSCAR s3, OScaR, WUSH]
+ *  s = the group's values sorted; for q in {kappa, 1 - kappa}:
+ *  h = (G - 1) q, i = floor(h), v(q) = s[i] + (h - i) (s[min(i+1, G-1)] - s[i])
+ *  (fp64, in this order); hi = v(kappa), lo = v(1 - kappa);
+ *  scale = fp16_rne((hi - lo) / 3), zero = fp16_rne(lo) (one rounding from fp64);
+ *  code = [x > zero + scale/2] + [x >= zero + 3 scale/2] + [x > zero + 5 scale/2],
+ *  or 0 when scale == 0; dequantized value = scale * code + zero.
+ *
+ * On-HBM layout
+ *  pages: uint8 [num_pages][Hkv][PB], PB = 1024 + 128 * ng bytes per page-head:
+ *   [0, 512)           K codes, uint32 word (8 t + w) holds channels 16 w + i
+ *                      (i = 0..15) of slot t at bits 2i .. 2i+1.
+ *   [512, 1024)        V codes, uint32 word u = 2 (16 a + m) + e holds
+ *                      code(slot 4a + 2e,     channel 8m + j) at bits 2j .. 2j+1,
+ *                      code(slot 4a + 2e + 1, channel 8m + j) at bits 16+2j .. 17+2j
+ *                      (a = 0..3, m = 0..15, e = 0..1, j = 0..7).
+ *   [1024, 1024+64ng)  K params, uint32 word (16 gr + t): fp16 scale (bits 0..15),
+ *                      fp16 zero (bits 16..31) of group gr, slot t.
+ *   [1024+64ng, PB)    V params, same order.
+ *  block_table: int32 [max_seqs][max_pages_per_seq]: physical page of logical
+ *   INT2 page m of a cache row.  Entries outside [0, num_pages) are skipped.
+ *  win: bf16 [max_seqs][Hkv][NB][2][16][128], NB = ceil(S_sink/16) + R/16;
+ *   block b < ceil(S_sink/16) holds sink slots 16b + t, the rest hold ring
+ *   slots 16 (b - ceil(S_sink/16)) + t.  Part 0 (K) is row-major (element
+ *   128 t + c); part 1 (V) holds (t, c) at element
+ *   32 (16 (t/4) + c/8) + 4 (c%8) + t%4.
+ *  pages and win must be zero-filled once when allocated (slots that were
+ *  never written are read with zero weight, so they must hold finite data).
+ *
+ * Status codes: 0 on success, a negative OSCAR_ERR_* otherwise.
+ */
+#ifndef OSCAR_KV_H
+#define OSCAR_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OSCAR_HEAD_DIM 128
+#define OSCAR_PAGE_SIZE 16
+#define OSCAR_MAX_KV_HEADS 64
+
+enum oscar_status {
+  OSCAR_OK = 0,
+  OSCAR_ERR_NULL = -1,       /* a required pointer is NULL */
+  OSCAR_ERR_SHAPE = -2,      /* head_dim != 128, page_size != 16, Hq % Hkv, Hkv out of range */
+  OSCAR_ERR_GROUP = -3,      /* group_size not in {32, 64, 128} */
+  OSCAR_ERR_CLIP = -4,       /* a clip ratio is not in [0.5, 1] */
+  OSCAR_ERR_WINDOW = -5,     /* s_sink < 0, s_keep < 0 or s_flush < 1 */
+  OSCAR_ERR_CAPACITY = -6,   /* slot, length or page count beyond the cache */
+  OSCAR_ERR_WORKSPACE = -7,  /* workspace smaller than oscar_workspace_size() */
+  OSCAR_ERR_DEVICE = -8,     /* current device is not gfx950 */
+  OSCAR_ERR_HIP = -9,        /* a HIP runtime call or launch failed */
+  OSCAR_ERR_ARG = -10        /* other invalid argument (counts, ranges, duplicates) */
+};
+
+typedef struct {
+  int32_t head_dim;           /* must be 128 */
+  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* Hkv, 1 .. 64 */
+  int32_t group_size;         /* G: 32, 64 or 128 channels per quantization group */
+  int32_t page_size;          /* must be 16 */
+  int32_t s_sink;             /* BF16 sink window (first tokens), >= 0 */
+  int32_t s_keep;             /* BF16 recent window kept after a flush, >= 0 */
+  int32_t s_flush;            /* flush granularity, >= 1 */
+  int32_t max_seqs;           /* cache rows */
+  int32_t max_pages_per_seq;  /* block table width */
+  int32_t num_pages;          /* physical pages in the pool */
+  float clip_k[OSCAR_MAX_KV_HEADS]; /* kappa for keys, per KV head, in [0.5, 1] */
+  float clip_v[OSCAR_MAX_KV_HEADS]; /* kappa for values, per KV head, in [0.5, 1] */
+} oscar_kv_config;
+
+typedef struct {
+  oscar_kv_config cfg;
+  uint8_t* pages;             /* [num_pages][Hkv][PB] INT2 pages (layout above) */
+  const int32_t* block_table; /* [max_seqs][max_pages_per_seq] */
+  uint16_t* win;              /* [max_seqs][Hkv][NB][2][16][128] bf16 windows */
+  const float* r_k;           /* [Hkv][128][128] fp32 key/query rotation */
+  const float* r_v;           /* [Hkv][128][128] fp32 value rotation */
+} oscar_kv_cache;
+
+/* Checks a configuration; returns OSCAR_OK or the first failing OSCAR_ERR_*. */
+int oscar_check_config(const oscar_kv_config* cfg);
+
+/* Byte sizes of the caller-allocated cache buffers (0 for an invalid cfg). */
+size_t oscar_page_head_bytes(int32_t group_size);
+size_t oscar_pages_bytes(const oscar_kv_config* cfg);
+size_t oscar_win_bytes(const oscar_kv_config* cfg);
+int32_t oscar_ring_capacity(const oscar_kv_config* cfg);
+/* Longest sequence a cache row can hold (INT2 pages + ring + sink). */
+int64_t oscar_max_seq_len(const oscar_kv_config* cfg);
+
+/* Workspace bytes needed by oscar_rotate_quant_append with at most
+ * `max_new_tokens` new tokens per call and by oscar_int2_decode_attn with at
+ * most `n_seqs` sequences per call.  The first part of the workspace holds
+ * counters that must be zero before the first call (zero-fill the whole
+ * buffer once); the library leaves them at zero after every call. */
+size_t oscar_workspace_size(const oscar_kv_config* cfg, int32_t n_seqs, int64_t max_new_tokens);
+
+/* Append new tokens of n_seqs sequences: rotate, place, flush, quantize.
+ * [OSCAR s4 "KV Cache Update", appendix B; WUSH "method step details"]
+ *  seq_slots[i]   cache row of sequence i (distinct, < max_seqs)
+ *  len_before[i]  tokens already in that row
+ *  cu_new[i]      prefix sums of new-token counts, cu_new[0] = 0,
+ *                 new tokens of sequence i are rows cu_new[i] .. cu_new[i+1]-1
+ *  (_host arrays are read on the host for checks and launch sizes; the
+ *  device arrays must hold the same values)
+ *  k, v           bf16 [cu_new[n]][Hkv][128] post-RoPE keys / values
+ *  q              bf16 [cu_new[n]][Hq][128] post-RoPE queries, or NULL
+ *  q_rot          bf16 [cu_new[n]][Hq][128] out: q . R_K, or NULL (needs q)
+ *  k_rot, v_rot   bf16 [cu_new[n]][Hkv][128] out: the rotated rows, or NULL
+ * Positions that the flush rule moves to INT2 are quantized into the pages
+ * (previously recent rows are read from the ring before it is overwritten),
+ * the rest go to the sink or the ring.  The block table must already map
+ * every logical page below ceil((S_quant(len_after) - S_sink) / 16). */
+int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
+                              const int32_t* seq_slots_host, const int32_t* len_before_host,
+                              const int32_t* cu_new_host,
+                              const int32_t* seq_slots, const int32_t* len_before,
+                              const int32_t* cu_new,
+                              const uint16_t* k, const uint16_t* v, const uint16_t* q,
+                              uint16_t* q_rot, uint16_t* k_rot, uint16_t* v_rot,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode attention of one query token per sequence over its whole cache row.
+ * [OSCAR s2, s4 "Decoding Attention Kernel"; OScaR "KV cache"]
+ *  seq_lens[i]    tokens in the row, including the token just appended (>= 1)
+ *  q_rot          bf16 [n_seqs][Hq][128] rotated queries (from the append call)
+ *  out            fp32 [n_seqs][Hq][128]: softmax(q' K^T / sqrt(128)) V . R_V^T
+ * Split-K over the context: partial results (max, sum, unnormalized output)
+ * go to the workspace and the last work-group of each (sequence, KV head)
+ * merges them (log-sum-exp) and applies R_V^T. */
+int oscar_int2_decode_attn(const oscar_kv_cache* cache, int32_t n_seqs,
+                           const int32_t* seq_slots_host, const int32_t* seq_lens_host,
+                           const int32_t* seq_slots, const int32_t* seq_lens,
+                           const uint16_t* q_rot, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* For checking: the decoded rows of positions [tok_begin, tok_end) of one
+ * cache row holding seq_len tokens, in the rotated basis: bf16 window rows
+ * widened to fp32, INT2 rows as scale * code + zero rounded once to fp32.
+ *  k_out, v_out   fp32 [tok_end - tok_begin][Hkv][128] */
+int oscar_dequant(const oscar_kv_cache* cache, int32_t seq_slot, int32_t seq_len,
+                  int32_t tok_begin, int32_t tok_end, float* k_out, float* v_out, void* stream);
+
+/* Text for a status code (static storage). */
+const char* oscar_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_KV_H */

@@ -1,0 +1,167 @@
+"""The C ABI on the host: symbols, sizes and every argument check (no GPU).
+
+All checks in liboscar_kv run on the host before anything is enqueued, so the
+error paths are exercised here without a device.  Pointers in these calls are
+dummies that are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from ultra_bit_kv_amd import _lib
+from ultra_bit_kv_amd._lib import KvCache, KvConfig
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oscar_kv.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("liboscar_kv.so not built")
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(oscar_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("oscar_rotate_quant_append", "oscar_int2_decode_attn", "oscar_dequant",
+              "oscar_workspace_size", "oscar_status_string", "oscar_check_config"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def cfg(**kw):
+    c = KvConfig()
+    c.head_dim, c.num_q_heads, c.num_kv_heads, c.group_size, c.page_size = 128, 32, 8, 64, 16
+    c.s_sink, c.s_keep, c.s_flush = 64, 256, 16
+    c.max_seqs, c.max_pages_per_seq, c.num_pages = 4, 100, 400
+    for h in range(64):
+        c.clip_k[h] = 0.96
+        c.clip_v[h] = 0.92
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("kw, status", [
+    ({}, 0),
+    ({"head_dim": 64}, -2), ({"page_size": 32}, -2), ({"num_kv_heads": 0}, -2),
+    ({"num_kv_heads": 65}, -2), ({"num_q_heads": 30}, -2),
+    ({"group_size": 48}, -3), ({"group_size": 256}, -3),
+    ({"s_flush": 0}, -5), ({"s_sink": -1}, -5), ({"s_keep": -3}, -5),
+    ({"max_seqs": 0}, -6),
+])
+def test_check_config(L, kw, status):
+    c = cfg(**kw)
+    assert L.oscar_check_config(ctypes.byref(c)) == status
+    assert L.oscar_status_string(status)
+
+
+def test_clip_range_checked(L):
+    for bad in (0.49, 1.01, float("nan")):
+        c = cfg()
+        c.clip_v[3] = bad
+        assert L.oscar_check_config(ctypes.byref(c)) == -4
+    c = cfg()
+    c.clip_k[7], c.clip_v[0] = 0.5, 1.0
+    assert L.oscar_check_config(ctypes.byref(c)) == 0
+    c.clip_k[8] = 7.0      # beyond num_kv_heads: ignored
+    assert L.oscar_check_config(ctypes.byref(c)) == 0
+
+
+def test_sizes(L):
+    for g, pb in ((128, 1152), (64, 1280), (32, 1536)):
+        assert L.oscar_page_head_bytes(g) == pb
+    assert L.oscar_page_head_bytes(48) == 0
+    c = cfg()
+    assert L.oscar_pages_bytes(ctypes.byref(c)) == 400 * 8 * 1280
+    assert L.oscar_ring_capacity(ctypes.byref(c)) == 272
+    nb = 64 // 16 + 272 // 16
+    assert L.oscar_win_bytes(ctypes.byref(c)) == 4 * 8 * nb * 2 * 16 * 128 * 2
+    # longest row: S_quant(len) - S_sink <= 16 * 100
+    mx = L.oscar_max_seq_len(ctypes.byref(c))
+    assert mx == 64 + 256 + (100 + 1) * 16 - 1
+    assert L.oscar_workspace_size(ctypes.byref(c), 4, 1000) > 2 * 1000 * 8 * 128 * 2
+    c5 = cfg(s_flush=24)
+    mx5 = L.oscar_max_seq_len(ctypes.byref(c5))
+    # len = mx5 fits, len = mx5 + 1 needs one more page than the row has
+    sq = lambda n: 64 + 24 * max(0, (n - 64 - 256) // 24)
+    assert -(-(sq(mx5) - 64) // 16) <= 100 < -(-(sq(mx5 + 1) - 64) // 16)
+
+
+DUMMY = ctypes.c_void_p(0x1000)
+
+
+def _cache(c):
+    return KvCache(c, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+
+
+def _i32(a):
+    a = np.ascontiguousarray(np.asarray(a, np.int32))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def append(L, c, slots, lb, n_new, ws_bytes=1 << 40, k=DUMMY, q=None, q_rot=None, cache=None):
+    cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+    keep = [_i32(slots), _i32(lb), _i32(cu)]
+    return L.oscar_rotate_quant_append(
+        ctypes.byref(cache or _cache(c)), len(slots), keep[0][1], keep[1][1], keep[2][1],
+        DUMMY, DUMMY, DUMMY, k, DUMMY, q, q_rot, None, None, DUMMY, ws_bytes, None)
+
+
+def decode(L, c, slots, lens, ws_bytes=1 << 40, out=DUMMY):
+    keep = [_i32(slots), _i32(lens)]
+    return L.oscar_int2_decode_attn(ctypes.byref(_cache(c)), len(slots), keep[0][1], keep[1][1],
+                                    DUMMY, DUMMY, DUMMY, out, DUMMY, ws_bytes, None)
+
+
+def test_append_argument_checks(L):
+    c = cfg()
+    assert append(L, c, [0], [0], [5], k=None) == -1                 # null keys
+    assert append(L, c, [0], [0], [5], q=None, q_rot=DUMMY) == -1    # q_rot without q
+    assert append(L, c, [4], [0], [5]) == -6                          # slot >= max_seqs
+    assert append(L, c, [1, 1], [0, 0], [5, 5]) == -10                # duplicate slot
+    assert append(L, c, [0], [-1], [5]) == -10                        # negative length
+    mx = L.oscar_max_seq_len(ctypes.byref(c))
+    assert append(L, c, [0], [mx], [1]) == -6                         # beyond the row
+    assert append(L, c, [0], [0], [5], ws_bytes=10) == -7             # workspace
+    bad = cfg(group_size=7)
+    assert append(L, bad, [0], [0], [5]) == -3
+    # a valid call reaches the device check: without a GPU that is a HIP error
+    st = append(L, c, [0, 2], [0, 10], [5, 7])
+    assert st in (-9, -8, 0)
+
+
+def test_decode_argument_checks(L):
+    c = cfg()
+    assert decode(L, c, [0], [0]) == -10                              # empty context
+    assert decode(L, c, [9], [10]) == -6
+    assert decode(L, c, [0], [10], out=None) == -1
+    assert decode(L, c, [0], [10], ws_bytes=100) == -7
+    assert decode(L, c, [0, 1, 2, 3, 0], [5] * 5) == -10              # n_seqs > max_seqs
+    mx = L.oscar_max_seq_len(ctypes.byref(c))
+    assert decode(L, c, [0], [mx + 1]) == -6
+    assert decode(L, c, [0], [mx]) in (-9, -8, 0)
+
+
+def test_dequant_argument_checks(L):
+    c = cfg()
+    cache = _cache(c)
+    f = L.oscar_dequant
+    assert f(ctypes.byref(cache), 0, 100, 50, 40, DUMMY, DUMMY, None) == -10
+    assert f(ctypes.byref(cache), 0, 100, 0, 101, DUMMY, DUMMY, None) == -10
+    assert f(ctypes.byref(cache), 5, 100, 0, 10, DUMMY, DUMMY, None) == -6
+    assert f(ctypes.byref(cache), 0, 100, 0, 10, None, DUMMY, None) == -1

@@ -1,0 +1,180 @@
+"""GPU parity: liboscar_kv (through the C ABI) against the CPU oracle.
+
+Bars (fixed by the method's contract):
+* rotated rows (q_rot, window rows), INT2 codes, fp16 scales / zero points and
+  dequantized rows: bit-exact;
+* decode attention: max-abs <= 2e-3 and rel-L2 <= 1e-3 (fp32 accumulation).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import layout, placement
+from oracle.rounding import bf16_bits_to_f64
+from synth import get
+from tests.oscar_testlib import (make_cache, fill, oracle_head, oracle_q_rot, oracle_decode,
+                                 compare_attention)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ultra_bit_kv_amd import lib
+    lib()
+
+
+def small(name):
+    """Reduced-size variants of the five workloads (ragged, several tiles)."""
+    if name == "c1":
+        return get("c1_tiny"), [1024]
+    if name == "c2s":
+        return get("c2_qwen3_8b_bs1").scaled(lengths=("list", (1500,))), [1500]
+    if name == "c3s":
+        w = get("c3_bs64").scaled(n_seqs=3, lengths=("list", (333, 517, 1000)))
+        return w, [333, 517, 1000]
+    if name == "c4s":
+        return get("c4_long_bs1").scaled(lengths=("list", (1400,))), [1400]
+    if name == "c5s":
+        w = get("c5_qwen3_32b_step").scaled(n_seqs=2, lengths=("list", (700, 1000)))
+        return w, [700, 1000]
+    if name == "demote1":   # OSCAR's one-token demotion, no sink
+        w = get("c1_tiny").scaled(s_sink=0, s_keep=5, s_flush=1, group=64)
+        return w, [300]
+    if name == "oddflush":  # flush not page aligned, odd sink
+        w = get("c3_bs64").scaled(n_seqs=2, hkv=2, hq=8, s_sink=5, s_keep=40, s_flush=24,
+                                   group=32, lengths=("list", (250, 401)))
+        return w, [250, 401]
+    raise KeyError(name)
+
+
+CASES = ["c1", "c2s", "c3s", "c4s", "c5s", "demote1", "oddflush"]
+
+
+def _check_head(cache, w, i, h, L, hc):
+    """Bit-exact comparison of one (sequence, KV head) of the cache."""
+    ng = 128 // w.group
+    bt = cache.host_block_table
+    a, b = hc.int2
+    for m in range(placement.n_int2_pages(L, w.s_sink, w.s_keep, w.s_flush)):
+        blk = cache.page_head(int(bt[i, m]), h)
+        kc, vc, ks, kz, vs, vz = layout.unpack_page_head(blk, w.group)
+        _, nv = hc.page_block(m)
+        r = slice(16 * m, 16 * m + nv)
+        assert np.array_equal(kc[:nv], hc.kc[r]), (i, h, m)
+        assert np.array_equal(vc[:nv], hc.vc[r]), (i, h, m)
+        assert np.array_equal(ks[:nv], hc.ks[r]) and np.array_equal(kz[:nv], hc.kz[r]), (i, h, m)
+        assert np.array_equal(vs[:nv], hc.vs[r]) and np.array_equal(vz[:nv], hc.vz[r]), (i, h, m)
+        assert ks.shape[1] == ng
+    wb = cache.window_blocks(i, h)
+    for (blk, t), p in hc.window_rows().items():
+        k_rows, v_rows = layout.unpack_window_block(wb[blk])
+        assert np.array_equal(k_rows[t], hc.k_rot[p]), (i, h, p)
+        assert np.array_equal(v_rows[t], hc.v_rot[p]), (i, h, p)
+    kd, vd = cache.dequant(i, L, 0, L)
+    kd = kd[:, h].cpu().numpy()
+    vd = vd[:, h].cpu().numpy()
+    ek, ev = hc.dequant_f32()
+    assert np.array_equal(kd.view(np.uint32), ek.view(np.uint32)), (i, h)
+    assert np.array_equal(vd.view(np.uint32), ev.view(np.uint32)), (i, h)
+
+
+@pytest.mark.parametrize("identity", [True, False])
+@pytest.mark.parametrize("name", CASES)
+def test_append_bit_exact_and_decode(name, identity):
+    w, lens = small(name)
+    print(f"[case] {name} identity={identity} lens={lens}", flush=True)
+    cache = make_cache(w, lens, identity=identity)
+    q_rot = fill(cache, w, lens, chunk=300)
+    r_k, r_v = cache.host_r
+    out = cache.decode(__import__("ultra_bit_kv_amd").SeqBatch(range(len(lens)), lens), q_rot)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    qr = q_rot.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    worst = (0.0, 0.0)
+    for i, L in enumerate(lens):
+        assert np.array_equal(qr[i], oracle_q_rot(w, i, L, r_k)), i
+        for h in range(w.hkv):
+            hc = oracle_head(w, i, h, L, r_k, r_v)
+            _check_head(cache, w, i, h, L, hc)
+            want = oracle_decode(w, i, h, L, r_k, r_v, hc)
+            err, rel, ok = compare_attention(out[i, h * w.g:(h + 1) * w.g], want)
+            worst = (max(worst[0], err), max(worst[1], rel))
+            assert ok, (name, i, h, err, rel)
+    print(f"[case] {name} max_abs={worst[0]:.3e} rel_l2={worst[1]:.3e}", flush=True)
+
+
+def test_path_independence():
+    """Chunked prefill and token-by-token appends give the same cache bytes."""
+    from ultra_bit_kv_amd import SeqBatch
+    w = get("c3_bs64").scaled(n_seqs=2, hkv=2, hq=8, lengths=("list", (420, 610)))
+    lens = [420, 610]
+    c1 = make_cache(w, lens)
+    q1 = fill(c1, w, lens, chunk=4096)
+    c2 = make_cache(w, lens)
+    # first 300 tokens in odd chunks, the rest one token at a time
+    done = [0, 0]
+    sizes = [37, 1, 150, 112]
+    for n in sizes:
+        k = np.concatenate([w.keys(i, done[i], done[i] + n) for i in range(2)])
+        v = np.concatenate([w.values(i, done[i], done[i] + n) for i in range(2)])
+        c2.append_tokens([0, 1], done, [n, n], k, v)
+        done = [d + n for d in done]
+    while any(d < L - 1 for d, L in zip(done, lens)):
+        idx = [i for i in range(2) if done[i] < lens[i] - 1]
+        k = np.concatenate([w.keys(i, done[i], done[i] + 1) for i in idx])
+        v = np.concatenate([w.values(i, done[i], done[i] + 1) for i in idx])
+        c2.append_tokens(idx, [done[i] for i in idx], [1] * len(idx), k, v)
+        for i in idx:
+            done[i] += 1
+    k = np.concatenate([w.keys(i, lens[i] - 1, lens[i]) for i in range(2)])
+    v = np.concatenate([w.values(i, lens[i] - 1, lens[i]) for i in range(2)])
+    q = np.concatenate([w.queries(i, lens[i] - 1, lens[i]) for i in range(2)])
+    q2, _, _ = c2.append_tokens([0, 1], [L - 1 for L in lens], [1, 1], k, v, q)
+    for i, L in enumerate(lens):
+        kd1, vd1 = c1.dequant(i, L, 0, L)
+        kd2, vd2 = c2.dequant(i, L, 0, L)
+        assert torch.equal(kd1, kd2) and torch.equal(vd1, vd2)
+    b = SeqBatch([0, 1], lens)
+    assert torch.equal(c1.decode(b, q1), c2.decode(b, q2))
+
+
+def test_decode_deterministic_and_edge_lengths():
+    """Repeated calls are bitwise equal; short contexts (sink only, ring only,
+    first flush) match the oracle."""
+    from ultra_bit_kv_amd import SeqBatch
+    w = get("c3_bs64").scaled(n_seqs=9, hkv=2, hq=8)
+    lens = [1, 2, 63, 64, 65, 319, 320, 336, 337]
+    w = w.scaled(lengths=("list", tuple(lens)))
+    cache = make_cache(w, lens)
+    q_rot = fill(cache, w, lens, chunk=64)
+    b = SeqBatch(range(len(lens)), lens)
+    o1 = cache.decode(b, q_rot)
+    o2 = cache.decode(b, q_rot)
+    assert torch.equal(o1, o2)
+    out = o1.cpu().numpy()
+    r_k, r_v = cache.host_r
+    for i, L in enumerate(lens):
+        for h in range(w.hkv):
+            want = oracle_decode(w, i, h, L, r_k, r_v)
+            err, rel, ok = compare_attention(out[i, h * w.g:(h + 1) * w.g], want)
+            assert ok, (L, h, err, rel)
+
+
+def test_decode_many_splits_long_context():
+    """Thousands of INT2 pages, many splits, G = 32 (4 groups per row)."""
+    from ultra_bit_kv_amd import SeqBatch
+    w = get("c4_long_bs1").scaled(hkv=2, hq=8, lengths=("list", (20000,)))
+    lens = [20000]
+    cache = make_cache(w, lens)
+    q_rot = fill(cache, w, lens, chunk=8192)
+    out = cache.decode(SeqBatch([0], lens), q_rot).cpu().numpy()
+    r_k, r_v = cache.host_r
+    for h in range(w.hkv):
+        want = oracle_decode(w, 0, h, 20000, r_k, r_v)
+        err, rel, ok = compare_attention(out[0, h * w.g:(h + 1) * w.g], want)
+        assert ok, (h, err, rel)

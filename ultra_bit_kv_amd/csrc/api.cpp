@@ -1,0 +1,336 @@
+// liboscar_kv host side: argument checks, the closed-form flush planner, the
+// split-K planner, workspace layout and kernel launches.  See oscar_kv.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "oscar_internal.h"
+#include "../../include/oscar_kv.h"
+
+namespace {
+
+using namespace oscar;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// S_quant of the flush rule (WUSH-KV notes, "method step details").
+int64_t s_quant(int64_t len, const oscar_kv_config& c) {
+  const int64_t num = len - c.s_sink - c.s_keep;
+  const int64_t k = num >= 0 ? num / c.s_flush : 0;
+  return c.s_sink + (int64_t)c.s_flush * k;
+}
+
+int64_t int2_pages(int64_t len, const oscar_kv_config& c) {
+  const int64_t nq = s_quant(len, c) - c.s_sink;
+  return nq > 0 ? (nq + kPage - 1) / kPage : 0;
+}
+
+int ring_cap(const oscar_kv_config& c) {
+  return (c.s_keep + c.s_flush + kPage - 1) / kPage * kPage;
+}
+
+int ng_of(const oscar_kv_config& c) { return kD / c.group_size; }
+
+// Query heads per decode pass: columns of a 16-wide MFMA tile are
+// (group, head) pairs, so hp * ng <= 16, hp a power of two.
+DecodePlan head_passes(const oscar_kv_config& c) {
+  const int g = c.num_q_heads / c.num_kv_heads;
+  int hp = 1;
+  while (hp < g) hp *= 2;
+  hp = std::min(hp, 16 / ng_of(c));
+  DecodePlan p{};
+  p.hp = hp;
+  p.passes = (g + hp - 1) / hp;
+  p.splits = 1;
+  return p;
+}
+
+// Upper bound on splits for n_seqs sequences: keep about 4096 work-groups in
+// flight at most, at most 128 per (sequence, KV head, pass).
+int max_splits(const oscar_kv_config& c, int n_seqs) {
+  const DecodePlan p = head_passes(c);
+  const long long rows = (long long)std::max(1, n_seqs) * c.num_kv_heads * p.passes;
+  long long s = (4096 + rows - 1) / rows;
+  return (int)std::max(1LL, std::min(128LL, s));
+}
+
+size_t counters_bytes(const oscar_kv_config& c) {
+  const DecodePlan p = head_passes(c);
+  return align_up((size_t)c.max_seqs * c.num_kv_heads * p.passes * sizeof(uint32_t));
+}
+
+size_t partials_bytes(const oscar_kv_config& c, int n_seqs) {
+  const DecodePlan p = head_passes(c);
+  const size_t rec = (size_t)p.hp * kD + 2 * p.hp;
+  return align_up((size_t)n_seqs * c.num_kv_heads * p.passes * max_splits(c, n_seqs) * rec *
+                  sizeof(float));
+}
+
+size_t staging_bytes(const oscar_kv_config& c, int64_t n_tok) {
+  return 2 * align_up((size_t)n_tok * c.num_kv_heads * kD * sizeof(uint16_t));
+}
+
+CacheArgs make_args(const oscar_kv_cache& k) {
+  const oscar_kv_config& c = k.cfg;
+  CacheArgs a{};
+  a.pages = k.pages;
+  a.block_table = k.block_table;
+  a.win = k.win;
+  a.r_k = k.r_k;
+  a.r_v = k.r_v;
+  a.hq = c.num_q_heads;
+  a.hkv = c.num_kv_heads;
+  a.g = c.num_q_heads / c.num_kv_heads;
+  a.group = c.group_size;
+  a.ng = ng_of(c);
+  a.s_sink = c.s_sink;
+  a.s_keep = c.s_keep;
+  a.s_flush = c.s_flush;
+  a.ring_cap = ring_cap(c);
+  a.sink_blocks = (c.s_sink + kPage - 1) / kPage;
+  a.win_blocks = a.sink_blocks + a.ring_cap / kPage;
+  a.max_seqs = c.max_seqs;
+  a.max_pages = c.max_pages_per_seq;
+  a.num_pages = c.num_pages;
+  a.page_bytes = (int)oscar_page_head_bytes(c.group_size);
+  return a;
+}
+
+// gfx950 check, once per device.
+int check_device() {
+  static std::mutex mu;
+  static int known[64] = {0};   // 0 unknown, 1 ok, -1 not gfx950
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return OSCAR_ERR_HIP;
+  if (dev < 0 || dev >= 64) return OSCAR_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return OSCAR_ERR_HIP;
+    known[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  return known[dev] == 1 ? OSCAR_OK : OSCAR_ERR_DEVICE;
+}
+
+thread_local char g_last_hip[160] = "";
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return OSCAR_OK;
+  std::snprintf(g_last_hip, sizeof g_last_hip, "HIP runtime error: %s", hipGetErrorString(e));
+  return OSCAR_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oscar_check_config(const oscar_kv_config* c) {
+  if (!c) return OSCAR_ERR_NULL;
+  if (c->head_dim != kD || c->page_size != kPage) return OSCAR_ERR_SHAPE;
+  if (c->num_kv_heads < 1 || c->num_kv_heads > OSCAR_MAX_KV_HEADS) return OSCAR_ERR_SHAPE;
+  if (c->num_q_heads < c->num_kv_heads || c->num_q_heads % c->num_kv_heads != 0)
+    return OSCAR_ERR_SHAPE;
+  if (c->num_q_heads / c->num_kv_heads > 256) return OSCAR_ERR_SHAPE;
+  if (c->group_size != 32 && c->group_size != 64 && c->group_size != 128) return OSCAR_ERR_GROUP;
+  for (int h = 0; h < c->num_kv_heads; ++h) {
+    const float a = c->clip_k[h], b = c->clip_v[h];
+    if (!(a >= 0.5f && a <= 1.0f) || !(b >= 0.5f && b <= 1.0f)) return OSCAR_ERR_CLIP;
+  }
+  if (c->s_sink < 0 || c->s_keep < 0 || c->s_flush < 1) return OSCAR_ERR_WINDOW;
+  if (c->s_sink > (1 << 20) || c->s_keep > (1 << 20) || c->s_flush > (1 << 20))
+    return OSCAR_ERR_WINDOW;
+  if (c->max_seqs < 1 || c->max_pages_per_seq < 0 || c->num_pages < 0) return OSCAR_ERR_CAPACITY;
+  return OSCAR_OK;
+}
+
+size_t oscar_page_head_bytes(int32_t group_size) {
+  if (group_size != 32 && group_size != 64 && group_size != 128) return 0;
+  return 1024 + 128 * (size_t)(kD / group_size);
+}
+
+size_t oscar_pages_bytes(const oscar_kv_config* c) {
+  if (oscar_check_config(c) != OSCAR_OK) return 0;
+  return (size_t)c->num_pages * c->num_kv_heads * oscar_page_head_bytes(c->group_size);
+}
+
+int32_t oscar_ring_capacity(const oscar_kv_config* c) {
+  if (oscar_check_config(c) != OSCAR_OK) return 0;
+  return ring_cap(*c);
+}
+
+size_t oscar_win_bytes(const oscar_kv_config* c) {
+  if (oscar_check_config(c) != OSCAR_OK) return 0;
+  const size_t blocks = (c->s_sink + kPage - 1) / kPage + ring_cap(*c) / kPage;
+  return (size_t)c->max_seqs * c->num_kv_heads * blocks * 2 * kPage * kD * sizeof(uint16_t);
+}
+
+int64_t oscar_max_seq_len(const oscar_kv_config* c) {
+  if (oscar_check_config(c) != OSCAR_OK) return 0;
+  // largest len with S_quant(len) - S_sink <= 16 * max_pages_per_seq
+  const int64_t kmax = (int64_t)kPage * c->max_pages_per_seq / c->s_flush;
+  return (int64_t)c->s_sink + c->s_keep + (kmax + 1) * c->s_flush - 1;
+}
+
+size_t oscar_workspace_size(const oscar_kv_config* c, int32_t n_seqs, int64_t max_new_tokens) {
+  if (oscar_check_config(c) != OSCAR_OK || n_seqs < 0 || max_new_tokens < 0) return 0;
+  return counters_bytes(*c) +
+         std::max(partials_bytes(*c, std::max(1, (int)n_seqs)), staging_bytes(*c, max_new_tokens));
+}
+
+const char* oscar_status_string(int status) {
+  switch (status) {
+    case OSCAR_OK: return "ok";
+    case OSCAR_ERR_NULL: return "a required pointer is NULL";
+    case OSCAR_ERR_SHAPE: return "unsupported shape (head_dim, page_size or head counts)";
+    case OSCAR_ERR_GROUP: return "group_size must be 32, 64 or 128";
+    case OSCAR_ERR_CLIP: return "clip ratios must lie in [0.5, 1]";
+    case OSCAR_ERR_WINDOW: return "invalid window sizes (s_sink, s_keep >= 0, s_flush >= 1)";
+    case OSCAR_ERR_CAPACITY: return "slot, length or page count exceeds the cache";
+    case OSCAR_ERR_WORKSPACE: return "workspace too small";
+    case OSCAR_ERR_DEVICE: return "current device is not gfx950";
+    case OSCAR_ERR_HIP: return g_last_hip[0] ? g_last_hip : "HIP runtime error";
+    case OSCAR_ERR_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}
+
+int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
+                              const int32_t* seq_slots_host, const int32_t* len_before_host,
+                              const int32_t* cu_new_host, const int32_t* seq_slots,
+                              const int32_t* len_before, const int32_t* cu_new, const uint16_t* k,
+                              const uint16_t* v, const uint16_t* q, uint16_t* q_rot,
+                              uint16_t* k_rot, uint16_t* v_rot, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!cache) return OSCAR_ERR_NULL;
+  const oscar_kv_config& c = cache->cfg;
+  int st = oscar_check_config(&c);
+  if (st != OSCAR_OK) return st;
+  if (!seq_slots_host || !len_before_host || !cu_new_host || !seq_slots || !len_before ||
+      !cu_new || !k || !v || !workspace || !cache->pages || !cache->block_table || !cache->win ||
+      !cache->r_k || !cache->r_v)
+    return OSCAR_ERR_NULL;
+  if (q_rot && !q) return OSCAR_ERR_NULL;
+  if (n_seqs < 1 || n_seqs > c.max_seqs) return OSCAR_ERR_ARG;
+  if (cu_new_host[0] != 0) return OSCAR_ERR_ARG;
+  const int64_t max_len = oscar_max_seq_len(&c);
+  std::vector<char> seen(c.max_seqs, 0);
+  int max_q = 0, max_new = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int slot = seq_slots_host[i];
+    if (slot < 0 || slot >= c.max_seqs) return OSCAR_ERR_CAPACITY;
+    if (seen[slot]) return OSCAR_ERR_ARG;
+    seen[slot] = 1;
+    const int64_t n_new = (int64_t)cu_new_host[i + 1] - cu_new_host[i];
+    const int64_t lb = len_before_host[i];
+    if (n_new < 0 || lb < 0) return OSCAR_ERR_ARG;
+    if (lb + n_new > max_len) return OSCAR_ERR_CAPACITY;
+    if (int2_pages(lb + n_new, c) > c.max_pages_per_seq) return OSCAR_ERR_CAPACITY;
+    if (int2_pages(lb + n_new, c) > 0 && c.num_pages < 1) return OSCAR_ERR_CAPACITY;
+    max_q = std::max<int>(max_q, (int)(s_quant(lb + n_new, c) - s_quant(lb, c)));
+    max_new = std::max<int>(max_new, (int)n_new);
+  }
+  const int64_t n_tok = cu_new_host[n_seqs];
+  if (n_tok > (int64_t)1 << 30) return OSCAR_ERR_ARG;
+  const size_t need = counters_bytes(c) + staging_bytes(c, n_tok);
+  if (workspace_bytes < need) return OSCAR_ERR_WORKSPACE;
+  if ((st = check_device()) != OSCAR_OK) return st;
+  if (n_tok == 0) return OSCAR_OK;
+
+  hipStream_t sm = (hipStream_t)stream;
+  const CacheArgs a = make_args(*cache);
+  ClipArgs clip{};
+  for (int h = 0; h < c.num_kv_heads; ++h) {
+    clip.k[h] = c.clip_k[h];
+    clip.v[h] = c.clip_v[h];
+  }
+  SeqArgs sa{seq_slots, len_before, cu_new, n_seqs};
+  uint8_t* ws = (uint8_t*)workspace + counters_bytes(c);
+  uint16_t* stage_k = (uint16_t*)ws;
+  uint16_t* stage_v = (uint16_t*)(ws + staging_bytes(c, n_tok) / 2);
+
+  // 1. rotate new rows (queries straight to q_rot)
+  if ((st = hip_status(launch_rotate(k, (int)n_tok, c.num_kv_heads, 1, cache->r_k, stage_k, k_rot,
+                                     sm))) != OSCAR_OK)
+    return st;
+  if ((st = hip_status(launch_rotate(v, (int)n_tok, c.num_kv_heads, 1, cache->r_v, stage_v, v_rot,
+                                     sm))) != OSCAR_OK)
+    return st;
+  if (q_rot) {
+    const int g = c.num_q_heads / c.num_kv_heads;
+    if ((st = hip_status(launch_rotate(q, (int)n_tok, c.num_q_heads, g, cache->r_k, q_rot,
+                                       nullptr, sm))) != OSCAR_OK)
+      return st;
+  }
+  // 2. quantize every position that crosses S_quant (reads the ring first)
+  if ((st = hip_status(launch_quantize(a, clip, sa, stage_k, stage_v, max_q, sm))) != OSCAR_OK)
+    return st;
+  // 3. new rows that stay BF16 go to the sink / ring
+  return hip_status(launch_place(a, sa, stage_k, stage_v, max_new, sm));
+}
+
+int oscar_int2_decode_attn(const oscar_kv_cache* cache, int32_t n_seqs,
+                           const int32_t* seq_slots_host, const int32_t* seq_lens_host,
+                           const int32_t* seq_slots, const int32_t* seq_lens,
+                           const uint16_t* q_rot, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!cache) return OSCAR_ERR_NULL;
+  const oscar_kv_config& c = cache->cfg;
+  int st = oscar_check_config(&c);
+  if (st != OSCAR_OK) return st;
+  if (!seq_slots_host || !seq_lens_host || !seq_slots || !seq_lens || !q_rot || !out ||
+      !workspace || !cache->pages || !cache->block_table || !cache->win || !cache->r_v)
+    return OSCAR_ERR_NULL;
+  if (n_seqs < 1 || n_seqs > c.max_seqs) return OSCAR_ERR_ARG;
+  const int64_t max_len = oscar_max_seq_len(&c);
+  int64_t max_units = 0;
+  const int ring_blocks = ring_cap(c) / kPage;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int slot = seq_slots_host[i];
+    const int64_t len = seq_lens_host[i];
+    if (slot < 0 || slot >= c.max_seqs) return OSCAR_ERR_CAPACITY;
+    if (len < 1) return OSCAR_ERR_ARG;
+    if (len > max_len || int2_pages(len, c) > c.max_pages_per_seq) return OSCAR_ERR_CAPACITY;
+    if (int2_pages(len, c) > 0 && c.num_pages < 1) return OSCAR_ERR_CAPACITY;
+    const int64_t pairs = (int2_pages(len, c) + 1) / 2;
+    const int64_t win = (std::min<int64_t>(len, c.s_sink) + kPage - 1) / kPage + ring_blocks;
+    max_units = std::max(max_units, pairs + 4 * win);
+  }
+  DecodePlan plan = head_passes(c);
+  // about 4 units (page pairs; window blocks count 4) per wave, 4 waves per group
+  const int want = (int)std::max<int64_t>(1, (max_units + 15) / 16);
+  plan.splits = std::min(max_splits(c, n_seqs), want);
+  const size_t need = counters_bytes(c) + partials_bytes(c, n_seqs);
+  if (workspace_bytes < need) return OSCAR_ERR_WORKSPACE;
+  if ((st = check_device()) != OSCAR_OK) return st;
+
+  const CacheArgs a = make_args(*cache);
+  SeqArgs sa{seq_slots, seq_lens, nullptr, n_seqs};
+  uint32_t* counters = (uint32_t*)workspace;
+  float* partials = (float*)((uint8_t*)workspace + counters_bytes(c));
+  return hip_status(
+      launch_decode(a, sa, plan, q_rot, out, partials, counters, (hipStream_t)stream));
+}
+
+int oscar_dequant(const oscar_kv_cache* cache, int32_t seq_slot, int32_t seq_len,
+                  int32_t tok_begin, int32_t tok_end, float* k_out, float* v_out, void* stream) {
+  if (!cache) return OSCAR_ERR_NULL;
+  const oscar_kv_config& c = cache->cfg;
+  int st = oscar_check_config(&c);
+  if (st != OSCAR_OK) return st;
+  if (!k_out || !v_out || !cache->pages || !cache->block_table || !cache->win)
+    return OSCAR_ERR_NULL;
+  if (seq_slot < 0 || seq_slot >= c.max_seqs) return OSCAR_ERR_CAPACITY;
+  if (seq_len < 0 || seq_len > oscar_max_seq_len(&c) ||
+      int2_pages(seq_len, c) > c.max_pages_per_seq)
+    return OSCAR_ERR_CAPACITY;
+  if (tok_begin < 0 || tok_end < tok_begin || tok_end > seq_len) return OSCAR_ERR_ARG;
+  if ((st = check_device()) != OSCAR_OK) return st;
+  return hip_status(launch_dequant(make_args(*cache), seq_slot, seq_len, tok_begin, tok_end, k_out,
+                                   v_out, (hipStream_t)stream));
+}
+
+}  // extern "C"

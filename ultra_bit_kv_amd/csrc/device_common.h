@@ -1,0 +1,72 @@
+// Device helpers shared by the liboscar_kv kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "oscar_internal.h"
+
+namespace oscar {
+
+// ---------------------------------------------------------------------------
+// Single round-to-nearest-even conversions from fp64.
+//
+// The cache stores the bf16 rounding of each rotated row and fp16 scale /
+// zero-point values (OSCAR summary page, sections 3-4).  Both conversions go
+// straight from the fp64 value: |x| is scaled by an exact power of two so
+// that its quantum becomes 1, rounded to an integer with rint (IEEE
+// round-half-even), and the integer is placed into the target's fields.  A
+// significand that rounds up to the next power of two carries into the
+// exponent field by the addition itself.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t round_f64_to_short_float(double x, int emin, int mant_bits,
+                                                             int bias, uint32_t inf_bits,
+                                                             uint32_t nan_bits) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+  const double a = __builtin_fabs(x);
+  if (a != a) return (uint16_t)(sign | nan_bits);
+  if (a == __builtin_inf()) return (uint16_t)(sign | inf_bits);
+  const int expf = (int)((b >> 52) & 0x7FFu);
+  if (expf == 0) return (uint16_t)sign;       // zero or below 2^-1022: rounds to zero
+  const int e = expf - 1023;                  // floor(log2 |x|)
+  const int eq = (e > emin ? e : emin) - mant_bits;
+  const double m = __builtin_ldexp(a, -eq);   // exact: power-of-two scaling
+  const uint32_t mi = (uint32_t)__builtin_rint(m);
+  uint32_t bits;
+  if (e >= emin)
+    bits = ((uint32_t)(e + bias) << mant_bits) + mi - (1u << mant_bits);
+  else
+    bits = mi;                                  // subnormal (mi == 2^mant_bits is the min normal)
+  if (bits >= inf_bits) bits = inf_bits;
+  return (uint16_t)(sign | bits);
+}
+
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  return round_f64_to_short_float(x, -126, 7, 127, 0x7F80u, 0x7FC0u);
+}
+
+__device__ __forceinline__ uint16_t f64_to_f16_rne(double x) {
+  return round_f64_to_short_float(x, -14, 10, 15, 0x7C00u, 0x7E00u);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ double f16_bits_to_f64(uint32_t bits16) {
+  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
+  return (double)h;
+}
+
+// ---------------------------------------------------------------------------
+// Positions, windows and pages of one cache row (the placement rule of the
+// OSCAR summary page, section 4, with the WUSH-KV flush boundary S_quant).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int s_quant_of(int len, int s_sink, int s_keep, int s_flush) {
+  int num = len - s_sink - s_keep;
+  int k = num >= 0 ? num / s_flush : 0;
+  return s_sink + s_flush * k;
+}
+
+}  // namespace oscar

@@ -1,0 +1,192 @@
+// Clip-quantize-pack of rows that move to INT2, and window placement of new rows.
+//
+// OSCAR summary page, section 3 "Scale Determination and Clipping" (affine
+// asymmetric INT2, scale and zero point, percentile clipping, per-token
+// groups) and section 4 "KV Cache Update" (four 2-bit codes per byte; the
+// same clip-quantize step serves prefill rows and rows demoted from the
+// recent window).  WUSH-KV notes, "method step details": quantize the
+// S_flush-aligned segments beyond the S_sink / S_keep windows and advance
+// S_quant; the OSCAR-style quantizer clips at the kappa-quantile.  OScaR
+// notes, "integer quantization basics": Q = clamp(round(x / Delta + z), 0, 3).
+//
+// One work-group quantizes one (sequence, position, KV head): wave 0 the key
+// row, wave 1 the value row.  The order statistics a quantile needs are found
+// by ranking (ties broken by channel index, so every rank is held by exactly
+// one element); the quantile, step and zero point are computed in fp64 with
+// contraction disabled, rounded once to fp16, and codes are decided against
+// the exact thresholds zero + (k - 1/2) scale.
+#include "device_common.h"
+
+namespace oscar {
+
+__device__ __forceinline__ int v_window_index(int t, int c) {
+  return 32 * (16 * (t >> 2) + (c >> 3)) + 4 * (c & 7) + (t & 3);
+}
+
+__device__ __forceinline__ double lerp_quantile(double a, double b, double f) {
+#pragma clang fp contract(off)
+  return a + f * (b - a);
+}
+
+__global__ __launch_bounds__(128) void quantize_kernel(CacheArgs c, ClipArgs clip, SeqArgs s,
+                                                       const uint16_t* __restrict__ stage_k,
+                                                       const uint16_t* __restrict__ stage_v) {
+#pragma clang fp contract(off)
+  __shared__ float vals[2][kD];
+  __shared__ float sel[2][4][4];
+  __shared__ uint32_t nib[2][64];
+
+  const int i = blockIdx.z, h = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;   // w: 0 = K, 1 = V
+  const int slot = s.slots[i];
+  const int lb = s.lens[i];
+  const int n_new = s.cu_new[i + 1] - s.cu_new[i];
+  if (slot < 0 || slot >= c.max_seqs || lb < 0 || n_new < 0) return;
+  const int la = lb + n_new;
+  const int sqb = s_quant_of(lb, c.s_sink, c.s_keep, c.s_flush);
+  const int sqa = s_quant_of(la, c.s_sink, c.s_keep, c.s_flush);
+  const int p = sqb + blockIdx.x;
+  if (p >= sqa) return;
+  const int m = (p - c.s_sink) / kPage, t = (p - c.s_sink) % kPage;
+  if (m >= c.max_pages) return;
+  const int phys = c.block_table[(size_t)slot * c.max_pages + m];
+  if (phys < 0 || phys >= c.num_pages) return;
+
+  // ---- source row: old rows from the recent ring, new rows from staging
+  uint32_t pair;
+  if (p < lb) {
+    const int r = (p - c.s_sink) % c.ring_cap;
+    const uint16_t* blk = c.win + (((size_t)slot * c.hkv + h) * c.win_blocks + c.sink_blocks +
+                                   r / kPage) * (2 * kPage * kD);
+    const int tt = r % kPage;
+    if (w == 0) {
+      pair = *(const uint32_t*)(blk + tt * kD + 2 * lane);
+    } else {
+      const uint16_t* vb = blk + kPage * kD;
+      pair = (uint32_t)vb[v_window_index(tt, 2 * lane)] |
+             ((uint32_t)vb[v_window_index(tt, 2 * lane + 1)] << 16);
+    }
+  } else {
+    const size_t tok = (size_t)s.cu_new[i] + (p - lb);
+    const uint16_t* src = (w == 0 ? stage_k : stage_v) + (tok * c.hkv + h) * kD;
+    pair = *(const uint32_t*)(src + 2 * lane);
+  }
+  const float x0 = bf16_bits_to_f32(pair & 0xFFFFu);
+  const float x1 = bf16_bits_to_f32(pair >> 16);
+  vals[w][2 * lane] = x0;
+  vals[w][2 * lane + 1] = x1;
+  __syncthreads();
+
+  // ---- ranks inside the group (G channels), order statistics for the quantiles
+  const int G = c.group;
+  const int gi = (2 * lane) / G;               // both of this lane's channels are in group gi
+  const int gs = gi * G;
+  const int c0 = 2 * lane, c1 = 2 * lane + 1;
+  int r0 = 0, r1 = 0;
+  for (int jj = 0; jj < G; ++jj) {
+    const int j = gs + ((jj + gi) & (G - 1));  // per-group start offset avoids bank conflicts
+    const float v = vals[w][j];
+    r0 += (v < x0) || (v == x0 && j < c0);
+    r1 += (v < x1) || (v == x1 && j < c1);
+  }
+  const double kap = (double)(w == 0 ? clip.k[h] : clip.v[h]);
+  const double q_hi = kap, q_lo = 1.0 - kap;
+  const double h_hi = (double)(G - 1) * q_hi, h_lo = (double)(G - 1) * q_lo;
+  const double fl_hi = __builtin_floor(h_hi), fl_lo = __builtin_floor(h_lo);
+  const int i_hi = (int)fl_hi, i_lo = (int)fl_lo;
+  const int want[4] = {i_lo, min(i_lo + 1, G - 1), i_hi, min(i_hi + 1, G - 1)};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (r0 == want[k]) sel[w][gi][k] = x0;
+    if (r1 == want[k]) sel[w][gi][k] = x1;
+  }
+  __syncthreads();
+
+  const double lo = lerp_quantile((double)sel[w][gi][0], (double)sel[w][gi][1], h_lo - fl_lo);
+  const double hi = lerp_quantile((double)sel[w][gi][2], (double)sel[w][gi][3], h_hi - fl_hi);
+  const double delta = (hi - lo) / 3.0;
+  const uint32_t s16 = f64_to_f16_rne(delta);
+  const uint32_t z16 = f64_to_f16_rne(lo);
+  const double sc = f16_bits_to_f64(s16), ze = f16_bits_to_f64(z16);
+  const double t1 = ze + 0.5 * sc, t2 = ze + 1.5 * sc, t3 = ze + 2.5 * sc;
+  uint32_t q0 = 0, q1 = 0;
+  if (sc != 0.0) {
+    const double d0 = (double)x0, d1 = (double)x1;
+    q0 = (uint32_t)(d0 > t1) + (uint32_t)(d0 >= t2) + (uint32_t)(d0 > t3);
+    q1 = (uint32_t)(d1 > t1) + (uint32_t)(d1 >= t2) + (uint32_t)(d1 > t3);
+  }
+  nib[w][lane] = q0 | (q1 << 2);
+  __syncthreads();
+
+  // ---- pack and store into the page-head block (layout in oscar_kv.h)
+  uint8_t* base = c.pages + ((size_t)phys * c.hkv + h) * c.page_bytes;
+  if (w == 0) {
+    if (lane < 8) {   // word (8t + lane): channels 16 lane .. 16 lane + 15 = nibbles 8 lane .. 8 lane + 7
+      uint32_t word = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) word |= nib[0][8 * lane + k] << (4 * k);
+      ((uint32_t*)base)[8 * t + lane] = word;
+    }
+  } else {
+    if (lane < 16) {  // half-word of channels 8 lane .. 8 lane + 7 of slot t
+      uint32_t hw = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) hw |= nib[1][4 * lane + k] << (4 * k);
+      const int u = 2 * (16 * (t >> 2) + lane) + ((t & 3) >> 1);
+      ((uint16_t*)(base + 512))[2 * u + (t & 1)] = (uint16_t)hw;
+    }
+  }
+  if ((2 * lane) % G == 0) {
+    uint32_t* prm = (uint32_t*)(base + 1024 + (w == 0 ? 0 : 64 * c.ng));
+    prm[16 * gi + t] = s16 | (z16 << 16);
+  }
+}
+
+hipError_t launch_quantize(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
+                           const uint16_t* stage_k, const uint16_t* stage_v, int max_q,
+                           hipStream_t stream) {
+  if (max_q <= 0 || s.n_seqs <= 0) return hipSuccess;
+  dim3 grid(max_q, c.hkv, s.n_seqs);
+  hipLaunchKernelGGL(quantize_kernel, grid, dim3(128), 0, stream, c, clip, s, stage_k, stage_v);
+  return hipGetLastError();
+}
+
+// New rows that stay in BF16: sink positions and positions at or beyond S_quant.
+__global__ __launch_bounds__(128) void place_kernel(CacheArgs c, SeqArgs s,
+                                                    const uint16_t* __restrict__ stage_k,
+                                                    const uint16_t* __restrict__ stage_v) {
+  const int i = blockIdx.z, h = blockIdx.y, ti = blockIdx.x;
+  const int ch = threadIdx.x;
+  const int slot = s.slots[i];
+  const int lb = s.lens[i];
+  const int n_new = s.cu_new[i + 1] - s.cu_new[i];
+  if (slot < 0 || slot >= c.max_seqs || lb < 0 || ti >= n_new) return;
+  const int p = lb + ti;
+  const int sqa = s_quant_of(lb + n_new, c.s_sink, c.s_keep, c.s_flush);
+  int blk, tt;
+  if (p < c.s_sink) {
+    blk = p / kPage;
+    tt = p % kPage;
+  } else if (p >= sqa) {
+    const int r = (p - c.s_sink) % c.ring_cap;
+    blk = c.sink_blocks + r / kPage;
+    tt = r % kPage;
+  } else {
+    return;  // quantized straight into the pages
+  }
+  uint16_t* wb = c.win + (((size_t)slot * c.hkv + h) * c.win_blocks + blk) * (2 * kPage * kD);
+  const size_t tok = (size_t)s.cu_new[i] + ti;
+  const size_t src = (tok * c.hkv + h) * kD + ch;
+  wb[tt * kD + ch] = stage_k[src];
+  wb[kPage * kD + v_window_index(tt, ch)] = stage_v[src];
+}
+
+hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* stage_k,
+                        const uint16_t* stage_v, int max_new, hipStream_t stream) {
+  if (max_new <= 0 || s.n_seqs <= 0) return hipSuccess;
+  dim3 grid(max_new, c.hkv, s.n_seqs);
+  hipLaunchKernelGGL(place_kernel, grid, dim3(128), 0, stream, c, s, stage_k, stage_v);
+  return hipGetLastError();
+}
+
+}  // namespace oscar

@@ -1,0 +1,73 @@
+// Internal declarations shared by the host library and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oscar {
+
+constexpr int kD = 128;          // head dim
+constexpr int kPage = 16;        // tokens per page / window block
+constexpr int kMaxKvHeads = 64;
+
+// Everything a kernel needs to address one cache, passed by value.
+struct CacheArgs {
+  uint8_t* pages;
+  const int32_t* block_table;
+  uint16_t* win;
+  const float* r_k;
+  const float* r_v;
+  int hq, hkv, g;                // query heads, KV heads, hq / hkv
+  int group, ng;                 // quantization group size and groups per row
+  int s_sink, s_keep, s_flush;
+  int ring_cap;                  // roundup16(s_keep + s_flush)
+  int sink_blocks, win_blocks;   // ceil(s_sink / 16), sink_blocks + ring_cap / 16
+  int max_seqs, max_pages, num_pages;
+  int page_bytes;                // bytes of one page-head block
+};
+
+struct ClipArgs {
+  float k[kMaxKvHeads];
+  float v[kMaxKvHeads];
+};
+
+// Per-call sequence metadata (device arrays provided by the caller).
+struct SeqArgs {
+  const int32_t* slots;
+  const int32_t* lens;           // len_before (append) or seq_len (decode)
+  const int32_t* cu_new;         // append only
+  int n_seqs;
+};
+
+// ---- launchers (each returns hipGetLastError() of its launch) -------------
+
+// dst[t][h][:] = bf16_rne(src[t][h][:] . R[h / g]) for t < n_tok, h < heads.
+// dst_b (optional) receives a copy.
+hipError_t launch_rotate(const uint16_t* src, int n_tok, int heads, int g, const float* r,
+                         uint16_t* dst_a, uint16_t* dst_b, hipStream_t stream);
+
+// Quantize every position that moves to INT2 in this append, from the ring
+// (old rows) or the staging rows (new tokens), into the pages.
+hipError_t launch_quantize(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
+                           const uint16_t* stage_k, const uint16_t* stage_v, int max_q,
+                           hipStream_t stream);
+
+// Copy staging rows of new tokens that land in the sink or the ring.
+hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* stage_k,
+                        const uint16_t* stage_v, int max_new, hipStream_t stream);
+
+// Decoded rows of one cache row.
+hipError_t launch_dequant(const CacheArgs& c, int slot, int len, int t0, int t1, float* k_out,
+                          float* v_out, hipStream_t stream);
+
+// INT2 split-K decode with in-kernel merge and un-rotation.
+struct DecodePlan {
+  int splits;                    // work-groups per (sequence, KV head, head pass)
+  int hp;                        // query heads handled per pass (<= 16 / ng)
+  int passes;                    // ceil(g / hp)
+};
+hipError_t launch_decode(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
+                         const uint16_t* q_rot, float* out, float* partials,
+                         uint32_t* counters, hipStream_t stream);
+
+}  // namespace oscar
