@@ -1,0 +1,267 @@
+"""Benchmark: INT2 paged decode attention (OSCAR-style cache) on one MI355X.
+
+Workload (default): bs64 decode, 32 query / 8 KV heads, head_dim 128, context
+lengths U[4096, 8192] per sequence, G = 64, windows 64 / 256 (flush 16),
+clip 0.96 / 0.92, shuffled pages.  One step = one decode step of every
+sequence through the whole hot path: oscar_rotate_quant_append with one new
+token per sequence (rotate q/k/v, flush + quantize, window placement) and then
+oscar_int2_decode_attn over the whole cache.  The step cycles through
+``--layers`` independent layer caches (copies of the same populated cache), so
+each step reads a cache that is not resident in the 256 MB MALL, as in a
+multi-layer model.
+
+Prints one JSON line.  `value` = sequences decoded per second (tokens/s).
+`roofline` is for the decode kernel: algorithmic bytes per launch (INT2
+token-heads x (64 + 1024/G) B + BF16 window token-heads x 512 B + block-table
+entries x 4 B + q' in + output out) over its average duration, measured with
+HIP events on the stream it runs on.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "int2_decode_c3_bs64_traffic.json")
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    for f in ("k_decode.hip", "device_common.h", "oscar_internal.h"):
+        h.update(open(os.path.join(ROOT, "ultra_bit_kv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, lens):
+    """Bytes one decode launch must move, from the cache format (per unit figures)."""
+    from oracle import placement   # pure integer placement rule
+    per_int2 = 64 + 1024 // w.group
+    total = 0
+    for L in lens:
+        sink, int2, recent = placement.segments(int(L), w.s_sink, w.s_keep, w.s_flush)
+        n_int2 = int2[1] - int2[0]
+        n_bf16 = (sink[1] - sink[0]) + (recent[1] - recent[0])
+        total += w.hkv * (n_int2 * per_int2 + n_bf16 * 512) + 4 * (-(-n_int2 // 16))
+    total += len(lens) * w.hq * 128 * (2 + 4)     # q' (bf16) in, output (fp32) out
+    return total
+
+
+def read_traffic(src_hash):
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != src_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, lens, seconds=12.0, n_sample=4):
+    """The oracle's decode step (rotate the new q/k/v rows, fp64 attention over
+    the decoded cache, un-rotate) on a sample of sequences, on the host cores."""
+    from threadpoolctl import threadpool_info
+    from oracle import rotate, attention
+    from oracle.rounding import bf16_bits_to_f64
+    from tests.oscar_testlib import oracle_head
+    r_k, r_v = w.rotations()
+    sample = list(range(n_sample))
+    heads = {}
+    for i in sample:
+        for h in range(w.hkv):
+            heads[(i, h)] = oracle_head(w, i, h, int(lens[i]), r_k, r_v)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for i in sample:
+            L = int(lens[i])
+            q = w.queries(i, L - 1, L)
+            kq = w.keys(i, L - 1, L)
+            vq = w.values(i, L - 1, L)
+            qr = rotate.rotate_heads_to_bf16(q, r_k, g=w.g)[0]
+            rotate.rotate_heads_to_bf16(kq, r_k)
+            rotate.rotate_heads_to_bf16(vq, r_v)
+            for h in range(w.hkv):
+                hc = heads[(i, h)]
+                attention.decode_head(bf16_bits_to_f64(qr[h * w.g:(h + 1) * w.g]), hc.k_dec,
+                                      hc.v_dec, r_v[h])
+            steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": steps / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 oracle decode step (rotate the new q/k/v rows, attention over the "
+                       f"decoded cache for all {w.hkv} KV heads, un-rotate) for {n_sample} of the "
+                       f"{len(lens)} sequences, repeated for {el:.1f} s ({steps} sequence-steps); "
+                       f"decoded caches built beforehand, untimed")}
+
+
+def copy_calibration(nbytes):
+    """A plain device copy of known size (for scaling FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--config", default="c3_bs64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="only run a device copy of this many bytes (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (the decode path shards by "
+              "sequence / KV head with no exchange; multi-GPU runs are not part of it)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    from synth import get
+    from ultra_bit_kv_amd import SeqBatch, as_bf16
+    from tests.oscar_testlib import make_cache, fill
+
+    w = get(args.config)
+    lens0 = w.lengths_after()                 # context of the first timed step, per layer
+    n = len(lens0)
+    total_steps = args.warmup + args.steps
+    per_layer = -(-total_steps // args.layers)
+    grow = [int(L) + per_layer for L in lens0]
+    t_setup = time.perf_counter()
+
+    # layer 0 is populated through the library's own append path with L0 - 1
+    # tokens; the other layers are copies.  Layer step k appends position
+    # L0 - 1 + k, so the first step of every layer decodes a context of L0.
+    base = make_cache(w, grow, max_seqs=n)
+    fill(base, w, [int(L) - 1 for L in lens0], chunk=8192)
+    layers = [base]
+    for _ in range(1, args.layers):
+        c = make_cache(w, grow, max_seqs=n)
+        c.pages.copy_(base.pages)
+        c.win.copy_(base.win)
+        layers.append(c)
+    torch.cuda.synchronize()
+
+    # per-step inputs (resident in HBM before timing) and per-sequence arrays
+    slots = np.arange(n, dtype=np.int32)
+    steps_in = []
+    first = [int(L) - 1 for L in lens0]      # position appended at a layer's first step
+    kseq = [w.keys(i, p, p + per_layer) for i, p in enumerate(first)]
+    vseq = [w.values(i, p, p + per_layer) for i, p in enumerate(first)]
+    qseq = [w.queries(i, p, p + per_layer) for i, p in enumerate(first)]
+    for k in range(per_layer):
+        pos = [p + k for p in first]
+        steps_in.append({
+            "app": SeqBatch(slots, pos, [1] * n),
+            "dec": SeqBatch(slots, [p + 1 for p in pos]),
+            "k": as_bf16(np.stack([x[k] for x in kseq])),
+            "v": as_bf16(np.stack([x[k] for x in vseq])),
+            "q": as_bf16(np.stack([x[k] for x in qseq])),
+        })
+    q_rot = torch.empty((n, w.hq, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((n, w.hq, 128), dtype=torch.float32, device="cuda")
+    for c in layers:
+        c.workspace_for(n, n)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def step(s, ev=None):
+        c = layers[s % args.layers]
+        d = steps_in[s // args.layers]
+        c.append(d["app"], d["k"], d["v"], d["q"], q_rot=q_rot)
+        if ev is not None:
+            ev[0].record()
+        c.decode(d["dec"], q_rot, out)
+        if ev is not None:
+            ev[1].record()
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for j in range(args.steps):
+        step(args.warmup + j, evs[j])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg_ms = float(np.mean(dec_ms))
+
+    # algorithmic bytes of the average decode launch (lengths grow during the run)
+    byts = []
+    for j in range(args.steps):
+        s = args.warmup + j
+        k = s // args.layers
+        byts.append(algorithmic_bytes(w, [int(L) + k for L in lens0]))
+    bytes_per_launch = float(np.mean(byts))
+    achieved = bytes_per_launch / (dec_avg_ms * 1e-3) / 1e9
+    src_hash = decode_source_hash()
+    traffic = read_traffic(src_hash)
+
+    res = {
+        "metric": "INT2 paged decode-attn tokens/s + achieved HBM GB/s vs peak (bs1, bs64)",
+        "value": n / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int2",
+        "data": "synthetic (seeded; Qwen3-8B-shaped heads, no weights needed)",
+        "config": {
+            "workload": f"{w.name}: {w.description}",
+            "batch": n, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": 128, "group": w.group,
+            "windows": [w.s_sink, w.s_keep, w.s_flush], "context_min": int(lens0.min()),
+            "context_max": int(lens0.max()), "layers_cycled": args.layers,
+            "step": "rotate_quant_append(1 token/seq) + int2_decode_attn",
+            "decode_ms": dec_avg_ms, "append_ms": ms_step - dec_avg_ms,
+            "decode_kernel_source": src_hash,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+            "kernel": "int2_decode_kernel", "algorithmic_bytes_per_launch": bytes_per_launch,
+        },
+        "cpu_baseline": None,
+        "setup_s": setup_s,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, lens0, seconds=args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -148,9 +148,9 @@ int64_t oscar_max_seq_len(const oscar_kv_config* cfg);
 
 /* Workspace bytes needed by oscar_rotate_quant_append with at most
  * `max_new_tokens` new tokens per call and by oscar_int2_decode_attn with at
- * most `n_seqs` sequences per call.  The first part of the workspace holds
- * counters that must be zero before the first call (zero-fill the whole
- * buffer once); the library leaves them at zero after every call. */
+ * most `n_seqs` sequences per call.  The workspace holds scratch data of one
+ * call only (staged rotated rows, split partials); its content need not be
+ * initialized and is not used across calls. */
 size_t oscar_workspace_size(const oscar_kv_config* cfg, int32_t n_seqs, int64_t max_new_tokens);
 
 /* Append new tokens of n_seqs sequences: rotate, place, flush, quantize.
@@ -183,9 +183,9 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
  *  seq_lens[i]    tokens in the row, including the token just appended (>= 1)
  *  q_rot          bf16 [n_seqs][Hq][128] rotated queries (from the append call)
  *  out            fp32 [n_seqs][Hq][128]: softmax(q' K^T / sqrt(128)) V . R_V^T
- * Split-K over the context: partial results (max, sum, unnormalized output)
- * go to the workspace and the last work-group of each (sequence, KV head)
- * merges them (log-sum-exp) and applies R_V^T. */
+ * Split-K over the context: one launch writes partial results (max, sum,
+ * unnormalized output) of each context split to the workspace, a second
+ * launch merges them (log-sum-exp) and applies R_V^T. */
 int oscar_int2_decode_attn(const oscar_kv_cache* cache, int32_t n_seqs,
                            const int32_t* seq_slots_host, const int32_t* seq_lens_host,
                            const int32_t* seq_slots, const int32_t* seq_lens,

@@ -34,10 +34,10 @@ BLOCK = 256
 
 
 def bf16_from_f32(x):
-    """fp32 -> bf16 bits, round to nearest even (finite inputs)."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    """fp32 -> bf16 bits, round to nearest even (torch's CPU cast, multi-threaded)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 @dataclass(frozen=True)

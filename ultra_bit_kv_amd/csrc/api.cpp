@@ -49,18 +49,24 @@ DecodePlan head_passes(const oscar_kv_config& c) {
   return p;
 }
 
-// Upper bound on splits for n_seqs sequences: keep about 4096 work-groups in
-// flight at most, at most 128 per (sequence, KV head, pass).
+// A decode work-group stages the page ids of its split in LDS: at most this
+// many page pairs per split.
+constexpr int kMaxPairsPerSplit = 256;
+
+int min_splits(const oscar_kv_config& c) {
+  const int pairs = (c.max_pages_per_seq + 1) / 2;
+  return std::max(1, (pairs + kMaxPairsPerSplit - 1) / kMaxPairsPerSplit);
+}
+
+// Upper bound on splits for n_seqs sequences: about 4096 work-groups at most,
+// at most 128 per (sequence, KV head, pass), and never fewer than the LDS
+// page-list limit requires.
 int max_splits(const oscar_kv_config& c, int n_seqs) {
   const DecodePlan p = head_passes(c);
   const long long rows = (long long)std::max(1, n_seqs) * c.num_kv_heads * p.passes;
   long long s = (4096 + rows - 1) / rows;
-  return (int)std::max(1LL, std::min(128LL, s));
-}
-
-size_t counters_bytes(const oscar_kv_config& c) {
-  const DecodePlan p = head_passes(c);
-  return align_up((size_t)c.max_seqs * c.num_kv_heads * p.passes * sizeof(uint32_t));
+  s = std::max(1LL, std::min(128LL, s));
+  return (int)std::max<long long>(s, min_splits(c));
 }
 
 size_t partials_bytes(const oscar_kv_config& c, int n_seqs) {
@@ -177,8 +183,7 @@ int64_t oscar_max_seq_len(const oscar_kv_config* c) {
 
 size_t oscar_workspace_size(const oscar_kv_config* c, int32_t n_seqs, int64_t max_new_tokens) {
   if (oscar_check_config(c) != OSCAR_OK || n_seqs < 0 || max_new_tokens < 0) return 0;
-  return counters_bytes(*c) +
-         std::max(partials_bytes(*c, std::max(1, (int)n_seqs)), staging_bytes(*c, max_new_tokens));
+  return std::max(partials_bytes(*c, std::max(1, (int)n_seqs)), staging_bytes(*c, max_new_tokens));
 }
 
 const char* oscar_status_string(int status) {
@@ -235,7 +240,7 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
   }
   const int64_t n_tok = cu_new_host[n_seqs];
   if (n_tok > (int64_t)1 << 30) return OSCAR_ERR_ARG;
-  const size_t need = counters_bytes(c) + staging_bytes(c, n_tok);
+  const size_t need = staging_bytes(c, n_tok);
   if (workspace_bytes < need) return OSCAR_ERR_WORKSPACE;
   if ((st = check_device()) != OSCAR_OK) return st;
   if (n_tok == 0) return OSCAR_OK;
@@ -248,23 +253,19 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
     clip.v[h] = c.clip_v[h];
   }
   SeqArgs sa{seq_slots, len_before, cu_new, n_seqs};
-  uint8_t* ws = (uint8_t*)workspace + counters_bytes(c);
+  uint8_t* ws = (uint8_t*)workspace;
   uint16_t* stage_k = (uint16_t*)ws;
   uint16_t* stage_v = (uint16_t*)(ws + staging_bytes(c, n_tok) / 2);
 
-  // 1. rotate new rows (queries straight to q_rot)
-  if ((st = hip_status(launch_rotate(k, (int)n_tok, c.num_kv_heads, 1, cache->r_k, stage_k, k_rot,
-                                     sm))) != OSCAR_OK)
-    return st;
-  if ((st = hip_status(launch_rotate(v, (int)n_tok, c.num_kv_heads, 1, cache->r_v, stage_v, v_rot,
-                                     sm))) != OSCAR_OK)
-    return st;
-  if (q_rot) {
-    const int g = c.num_q_heads / c.num_kv_heads;
-    if ((st = hip_status(launch_rotate(q, (int)n_tok, c.num_q_heads, g, cache->r_k, q_rot,
-                                       nullptr, sm))) != OSCAR_OK)
-      return st;
-  }
+  // 1. rotate new rows: keys and values to staging, queries straight to q_rot
+  RotateJobs jobs{};
+  jobs.job[0] = RotateJob{k, cache->r_k, stage_k, k_rot, c.num_kv_heads, 1};
+  jobs.job[1] = RotateJob{v, cache->r_v, stage_v, v_rot, c.num_kv_heads, 1};
+  jobs.n = 2;
+  if (q_rot)
+    jobs.job[jobs.n++] = RotateJob{q, cache->r_k, q_rot, nullptr, c.num_q_heads,
+                                   c.num_q_heads / c.num_kv_heads};
+  if ((st = hip_status(launch_rotate(jobs, (int)n_tok, sm))) != OSCAR_OK) return st;
   // 2. quantize every position that crosses S_quant (reads the ring first)
   if ((st = hip_status(launch_quantize(a, clip, sa, stage_k, stage_v, max_q, sm))) != OSCAR_OK)
     return st;
@@ -302,17 +303,14 @@ int oscar_int2_decode_attn(const oscar_kv_cache* cache, int32_t n_seqs,
   DecodePlan plan = head_passes(c);
   // about 4 units (page pairs; window blocks count 4) per wave, 4 waves per group
   const int want = (int)std::max<int64_t>(1, (max_units + 15) / 16);
-  plan.splits = std::min(max_splits(c, n_seqs), want);
-  const size_t need = counters_bytes(c) + partials_bytes(c, n_seqs);
+  plan.splits = std::max(min_splits(c), std::min(max_splits(c, n_seqs), want));
+  const size_t need = partials_bytes(c, n_seqs);
   if (workspace_bytes < need) return OSCAR_ERR_WORKSPACE;
   if ((st = check_device()) != OSCAR_OK) return st;
 
   const CacheArgs a = make_args(*cache);
   SeqArgs sa{seq_slots, seq_lens, nullptr, n_seqs};
-  uint32_t* counters = (uint32_t*)workspace;
-  float* partials = (float*)((uint8_t*)workspace + counters_bytes(c));
-  return hip_status(
-      launch_decode(a, sa, plan, q_rot, out, partials, counters, (hipStream_t)stream));
+  return hip_status(launch_decode(a, sa, plan, q_rot, out, (float*)workspace, (hipStream_t)stream));
 }
 
 int oscar_dequant(const oscar_kv_cache* cache, int32_t seq_slot, int32_t seq_len,

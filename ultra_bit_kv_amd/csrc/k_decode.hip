@@ -5,11 +5,10 @@
 //   o = softmax(q' K^T / sqrt(128)) V . R_V^T
 // over the BF16 sink rows, the INT2 middle (dequantized as scale * code +
 // zero) and the BF16 recent rows of one cache row, for the g query heads of
-// each KV head.  The pages' decoder processes sequence segments in two
-// launches and merges them; here the context of each (sequence, KV head) is
-// split over work-groups, each writes a partial (max, sum, unnormalized
-// output), and the last work-group to finish merges them by log-sum-exp and
-// applies R_V^T, all in one launch.
+// each KV head.  As in the pages' decoder, segments of the context are
+// processed by separate work-groups of one launch, each writing a partial
+// (max, sum, unnormalized output), and a second launch merges them by
+// log-sum-exp and applies R_V^T.
 //
 // Work-group = 4 waves; one (sequence, KV head, query-head pass, split).
 // Column n (0..15) of every MFMA tile is (group gi = n / HP, head hl = n % HP).
@@ -115,19 +114,21 @@ __device__ __forceinline__ void softmax_step(float (&x)[N], float (&p)[N], Softm
   }
 }
 
+constexpr int kMaxWgPages = 512;   // page ids staged per work-group (<= 256 pairs per split)
+
 template <int NG, int HP>
 __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s, int splits,
                                                           int passes,
                                                           const uint16_t* __restrict__ q_rot,
-                                                          float* __restrict__ out,
-                                                          float* __restrict__ partials,
-                                                          uint32_t* __restrict__ counters) {
+                                                          float* __restrict__ partials) {
   constexpr int G = kD / NG;
   constexpr int PW = HP * kD + 2 * HP;   // floats per partial record
   __shared__ float red_m[4][HP];
   __shared__ float red_l[4][HP];
   __shared__ float red_o[4][HP][kD];
-  __shared__ int s_last;
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[HP][kD];
+  __shared__ float s_qsum[HP * NG];
+  __shared__ int s_pages[kMaxWgPages];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -143,43 +144,7 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
   if (!row_ok) len = 0;
   const int nh = min(HP, c.g - pass * HP);   // valid heads in this pass
 
-  // ---- columns and query operands
-  const int n = r16, gi = n / HP, hl = n % HP;
-  const int hqi = pass * HP + hl;
-  const bool colv = (gi < NG) && (hl < nh);
-  const uint16_t* qrow =
-      q_rot + ((size_t)(row_ok ? i : 0) * c.hq + (size_t)h * c.g + (colv ? hqi : pass * HP)) * kD;
-  const int grp_q = (NG == 1) ? 0 : (NG == 2 ? (qd >> 1) : qd);   // group of channels 32qd..32qd+31
-  const bool bval = colv && (gi == grp_q);
-  const float C2 = kLog2e * 0.08838834764831845f;                // log2(e) / sqrt(128)
-  const float K1 = C2 * 16777216.0f;                              // undo the 2^-24 code scaling
-
-  half8 bq[4];
-  bf16x8 bw[4];
-#pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int ch = 32 * qd + 16 * (cc >> 1) + 4 * (cc & 1) + v + 8 * e;
-        const float qv = bval ? bf16_bits_to_f32(qrow[ch]) : 0.0f;
-        bq[cc][2 * v + e] = (_Float16)(qv * (1.0f / (float)(1 << (2 * v))));
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint16_t bits = colv ? qrow[32 * qd + 8 * cc + e] : (uint16_t)0;
-      bw[cc][e] = __builtin_bit_cast(__bf16, bits);
-    }
-  }
-  float qsum = 0.0f;
-  if (colv) {
-    for (int ch = gi * G; ch < (gi + 1) * G; ++ch) qsum += bf16_bits_to_f32(qrow[ch]);
-  }
-  const float qsC = qsum * C2;
-
-  // ---- this split's share of the context
+  // ---- this split's share of the INT2 pages
   const int sq = s_quant_of(len, c.s_sink, c.s_keep, c.s_flush);
   const int nq = sq > c.s_sink ? sq - c.s_sink : 0;               // INT2 tokens
   const int n_pages = (nq + kPage - 1) / kPage;
@@ -187,6 +152,66 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
   const int pb = (int)((long long)split * n_pairs / splits);
   const int pe = (int)((long long)(split + 1) * n_pairs / splits);
   const int32_t* bt = c.block_table + (size_t)(row_ok ? slot : 0) * c.max_pages;
+
+  // ---- stage the query rows of this pass and the split's page ids in LDS
+  const uint16_t* qbase =
+      q_rot + ((size_t)(row_ok ? i : 0) * c.hq + (size_t)h * c.g + (size_t)pass * HP) * kD;
+  for (int t = tid; t < HP * 16; t += 256) {
+    const int hh = t >> 4, part = t & 15;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (hh < nh) v = *(const u32x4*)(qbase + (size_t)hh * kD + 8 * part);
+    *(u32x4*)(&s_q[hh][8 * part]) = v;
+  }
+  const int n_wg_pages = min(2 * (pe - pb), kMaxWgPages);
+  for (int t = tid; t < n_wg_pages; t += 256) {
+    const int pg = 2 * pb + t;
+    int ph = -1;
+    if (pg < n_pages && pg < c.max_pages) ph = bt[pg];
+    s_pages[t] = (ph >= 0 && ph < c.num_pages) ? ph : -1;
+  }
+  __syncthreads();
+  if (tid < HP * NG) {   // sum of each (group, head) slice of q', column n = group * HP + head
+    const int hh = tid % HP, gg = tid / HP;
+    float sum = 0.0f;
+    for (int ch = gg * G; ch < (gg + 1) * G; ++ch) sum += bf16_bits_to_f32(s_q[hh][ch]);
+    s_qsum[tid] = sum;
+  }
+  __syncthreads();
+
+  // ---- per-lane MFMA operands for column n = (group gi, head hl)
+  const int n = r16, gi = n / HP, hl = n % HP;
+  const bool colv = (gi < NG) && (hl < nh);
+  const int grp_q = (NG == 1) ? 0 : (NG == 2 ? (qd >> 1) : qd);   // group of channels 32qd..32qd+31
+  const bool bval = colv && (gi == grp_q);
+  const float C2 = kLog2e * 0.08838834764831845f;                // log2(e) / sqrt(128)
+  const float K1 = C2 * 16777216.0f;                              // undo the 2^-24 code scaling
+  const float qsC = colv ? s_qsum[n] * C2 : 0.0f;
+
+  u32x4 wq[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    wq[cc] = colv ? *(const u32x4*)(&s_q[hl][32 * qd + 8 * cc]) : z;
+  }
+  bf16x8 bw[4];
+  half8 bq[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    bw[cc] = __builtin_bit_cast(bf16x8, wq[cc]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        // K index 8 qd + 2v + e of chunk cc <-> channel 32 qd + cl
+        const int cl = 16 * (cc >> 1) + 4 * (cc & 1) + v + 8 * e;
+        const uint32_t word = wq[cl >> 3][(cl & 7) >> 1];
+        const uint32_t bits = (cl & 1) ? (word >> 16) : (word & 0xFFFFu);
+        const float qv = bval ? bf16_bits_to_f32(bits) : 0.0f;
+        bq[cc][2 * v + e] = (_Float16)(qv * (1.0f / (float)(1 << (2 * v))));
+      }
+    }
+  }
+
   const size_t head_off = (size_t)h * c.page_bytes;
   const size_t page_stride = (size_t)c.hkv * c.page_bytes;
   const int gsel = gi < NG ? gi : 0;                              // in-bounds group for params
@@ -199,23 +224,25 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
   struct Pair {
     u32x2 ka, kb, va, vb;
     u32x4 kpa, kpb, vpa, vpb;
-    int pa;
+    int tok;      // INT2 token index of slot 0 of page A
     bool oka, okb;
   };
-  auto load_pair = [&](int pp, Pair& d) {
-    const int pa = 2 * pp, pbq = 2 * pp + 1;
-    int phys_a = pa < c.max_pages ? bt[pa] : -1;
-    int phys_b = (pbq < n_pages && pbq < c.max_pages) ? bt[pbq] : -1;
-    d.oka = phys_a >= 0 && phys_a < c.num_pages;
-    d.okb = phys_b >= 0 && phys_b < c.num_pages;
-    if (!d.oka) phys_a = 0;
-    if (!d.okb) phys_b = phys_a;
-    d.pa = pa;
-    const uint8_t* A = c.pages + (size_t)phys_a * page_stride + head_off;
-    const uint8_t* B = c.pages + (size_t)phys_b * page_stride + head_off;
-    const int koff = (r16 * 8 + 2 * qd) * 4;
-    const int poff = 1024 + 4 * (16 * gsel + 4 * qd);
-    const int vpoff = poff + 64 * NG;
+  // pairs of this wave: local index wave + 4k, k < npw (interleaved over the 4 waves)
+  const int nw = pe - pb;
+  const int npw = nw > wave ? (nw - wave + 3) / 4 : 0;
+  const int koff = (r16 * 8 + 2 * qd) * 4;
+  const int poff = 1024 + 4 * (16 * gsel + 4 * qd);
+  const int vpoff = poff + 64 * NG;
+  auto load_pair = [&](int k, Pair& d) {
+    const int local = wave + 4 * min(k, npw - 1);     // tail loads re-read the last pair
+    int pa = s_pages[2 * local], pbq = s_pages[2 * local + 1];
+    d.oka = pa >= 0;
+    d.okb = pbq >= 0;
+    if (!d.oka) pa = 0;
+    if (!d.okb) pbq = pa;
+    d.tok = 32 * (pb + local);
+    const uint8_t* A = c.pages + (size_t)pa * page_stride + head_off;
+    const uint8_t* B = c.pages + (size_t)pbq * page_stride + head_off;
     d.ka = *(const u32x2*)(A + koff);
     d.kb = *(const u32x2*)(B + koff);
     d.va = *(const u32x2*)(A + 512 + 8 * lane);
@@ -256,7 +283,7 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
         if constexpr (HP <= 1) x[k] += row_ror<1>(x[k]);
       }
     }
-    const int ta = 16 * d.pa + 4 * qd;   // INT2 token index of row 0 of tile A in this lane
+    const int ta = d.tok + 4 * qd;   // INT2 token index of row 0 of tile A in this lane
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (!(d.oka && ta + r < nq)) x[r] = kNegInf;
@@ -282,14 +309,14 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
     }
   };
 
-  {
-    int pp = pb + wave;
-    Pair cur, nxt;
-    if (pp < pe) load_pair(pp, cur);
-    for (; pp < pe; pp += 4) {
-      if (pp + 4 < pe) load_pair(pp + 4, nxt);
-      process_pair(cur);
-      cur = nxt;
+  if (npw > 0) {   // ping-pong: the loads of the next pair are in flight while one is processed
+    Pair pa_, pb_;
+    load_pair(0, pa_);
+    for (int k = 0; k < npw; k += 2) {
+      load_pair(k + 1, pb_);
+      process_pair(pa_);
+      load_pair(k + 2, pa_);
+      if (k + 1 < npw) process_pair(pb_);
     }
   }
   // INT2 accumulators carry code * 4^(j%4) * 2^-24: bring them to true scale
@@ -374,8 +401,7 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
   __syncthreads();
 
   // ---- merge the 4 waves -> this work-group's partial record
-  const size_t rec_base = (((size_t)i * c.hkv + h) * passes + pass) * splits;
-  float* rec = partials + (rec_base + split) * PW;
+  float* rec = partials + ((((size_t)i * c.hkv + h) * passes + pass) * splits + split) * PW;
   for (int idx = tid; idx < nh * kD; idx += 256) {
     const int hh = idx / kD, ch = idx % kD;
     float M = red_m[0][hh];
@@ -396,20 +422,36 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
     }
     rec[2 * HP + hh * kD + ch] = O;
   }
+}
 
-  // ---- the last work-group of this (sequence, KV head, pass) merges all splits
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(&counters[((size_t)i * c.hkv + h) * passes + pass], 1u);
-    s_last = (prev == (uint32_t)(splits - 1));
+// Log-sum-exp merge of the split partials of one (sequence, KV head, pass),
+// then o = o' . R_V^T with R_V staged in LDS (rows padded to 129 floats so the
+// row-per-thread reads of a wave fall in distinct banks).
+template <int HP>
+__global__ __launch_bounds__(256) void merge_unrotate_kernel(CacheArgs c, SeqArgs s, int splits,
+                                                             int passes,
+                                                             const float* __restrict__ partials,
+                                                             float* __restrict__ out) {
+  constexpr int PW = HP * kD + 2 * HP;
+  __shared__ float rv[kD][kD + 1];
+  __shared__ float fin[HP][kD];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x / passes, pass = blockIdx.x % passes;
+  const int i = blockIdx.y;
+  const int slot = s.slots[i];
+  const bool row_ok = slot >= 0 && slot < c.max_seqs && s.lens[i] >= 1;
+  const int nh = min(HP, c.g - pass * HP);
+
+  const float4* rg = (const float4*)(c.r_v + (size_t)h * kD * kD);
+  for (int t = tid; t < kD * kD / 4; t += 256) {
+    const float4 v = rg[t];
+    const int row = (4 * t) / kD, col = (4 * t) % kD;
+    rv[row][col] = v.x;
+    rv[row][col + 1] = v.y;
+    rv[row][col + 2] = v.z;
+    rv[row][col + 3] = v.w;
   }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  float(*fin)[kD] = red_o[0];
-  const float* recs = partials + rec_base * PW;
+  const float* recs = partials + (((size_t)i * c.hkv + h) * passes + pass) * splits * PW;
   for (int idx = tid; idx < nh * kD; idx += 256) {
     const int hh = idx / kD, ch = idx % kD;
     float M = kNegInf;
@@ -424,57 +466,56 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
     fin[hh][ch] = O / L;
   }
   __syncthreads();
-  const float* rv = c.r_v + (size_t)h * kD * kD;
+  if (!row_ok) return;
   for (int idx = tid; idx < nh * kD; idx += 256) {
     const int hh = idx / kD, jo = idx % kD;
-    const float* row = rv + (size_t)jo * kD;   // o_j = sum_c o'_c R_V[j][c]
     float sum = 0.0f;
 #pragma unroll 8
-    for (int cc = 0; cc < kD; ++cc) sum = __builtin_fmaf(fin[hh][cc], row[cc], sum);
-    if (row_ok)
-      out[((size_t)i * c.hq + (size_t)h * c.g + pass * HP + hh) * kD + jo] = sum;
+    for (int cc = 0; cc < kD; ++cc) sum = __builtin_fmaf(fin[hh][cc], rv[jo][cc], sum);
+    out[((size_t)i * c.hq + (size_t)h * c.g + pass * HP + hh) * kD + jo] = sum;
   }
-  if (tid == 0) counters[((size_t)i * c.hkv + h) * passes + pass] = 0u;
 }
 
 template <int NG, int HP>
 static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                                   const uint16_t* q_rot, float* out, float* partials,
-                                  uint32_t* counters, hipStream_t stream) {
+                                  hipStream_t stream) {
   dim3 grid(plan.splits, c.hkv * plan.passes, s.n_seqs);
   hipLaunchKernelGGL((int2_decode_kernel<NG, HP>), grid, dim3(256), 0, stream, c, s, plan.splits,
-                     plan.passes, q_rot, out, partials, counters);
+                     plan.passes, q_rot, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 mgrid(c.hkv * plan.passes, s.n_seqs);
+  hipLaunchKernelGGL((merge_unrotate_kernel<HP>), mgrid, dim3(256), 0, stream, c, s, plan.splits,
+                     plan.passes, partials, out);
   return hipGetLastError();
 }
 
 template <int NG>
 static hipError_t dispatch_hp(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                               const uint16_t* q_rot, float* out, float* partials,
-                              uint32_t* counters, hipStream_t stream) {
+                              hipStream_t stream) {
   switch (plan.hp) {
-    case 1: return launch_decode_t<NG, 1>(c, s, plan, q_rot, out, partials, counters, stream);
-    case 2: return launch_decode_t<NG, 2>(c, s, plan, q_rot, out, partials, counters, stream);
-    case 4: return launch_decode_t<NG, 4>(c, s, plan, q_rot, out, partials, counters, stream);
+    case 1: return launch_decode_t<NG, 1>(c, s, plan, q_rot, out, partials, stream);
+    case 2: return launch_decode_t<NG, 2>(c, s, plan, q_rot, out, partials, stream);
+    case 4: return launch_decode_t<NG, 4>(c, s, plan, q_rot, out, partials, stream);
     case 8:
-      if constexpr (NG <= 2)
-        return launch_decode_t<NG, 8>(c, s, plan, q_rot, out, partials, counters, stream);
+      if constexpr (NG <= 2) return launch_decode_t<NG, 8>(c, s, plan, q_rot, out, partials, stream);
       break;
     case 16:
-      if constexpr (NG == 1)
-        return launch_decode_t<NG, 16>(c, s, plan, q_rot, out, partials, counters, stream);
+      if constexpr (NG == 1) return launch_decode_t<NG, 16>(c, s, plan, q_rot, out, partials, stream);
       break;
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
-                         const uint16_t* q_rot, float* out, float* partials, uint32_t* counters,
-                         hipStream_t stream) {
+                         const uint16_t* q_rot, float* out, float* partials, hipStream_t stream) {
   if (s.n_seqs <= 0) return hipSuccess;
   switch (c.ng) {
-    case 1: return dispatch_hp<1>(c, s, plan, q_rot, out, partials, counters, stream);
-    case 2: return dispatch_hp<2>(c, s, plan, q_rot, out, partials, counters, stream);
-    case 4: return dispatch_hp<4>(c, s, plan, q_rot, out, partials, counters, stream);
+    case 1: return dispatch_hp<1>(c, s, plan, q_rot, out, partials, stream);
+    case 2: return dispatch_hp<2>(c, s, plan, q_rot, out, partials, stream);
+    case 4: return dispatch_hp<4>(c, s, plan, q_rot, out, partials, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -41,10 +41,20 @@ struct SeqArgs {
 
 // ---- launchers (each returns hipGetLastError() of its launch) -------------
 
-// dst[t][h][:] = bf16_rne(src[t][h][:] . R[h / g]) for t < n_tok, h < heads.
-// dst_b (optional) receives a copy.
-hipError_t launch_rotate(const uint16_t* src, int n_tok, int heads, int g, const float* r,
-                         uint16_t* dst_a, uint16_t* dst_b, hipStream_t stream);
+// One rotation job: dst[t][h][:] = bf16_rne(src[t][h][:] . r[h / g]) for
+// t < n_tok, h < heads; dst_b (optional) receives a copy.
+struct RotateJob {
+  const uint16_t* src;
+  const float* r;
+  uint16_t* dst_a;
+  uint16_t* dst_b;
+  int heads, g;
+};
+struct RotateJobs {
+  RotateJob job[3];
+  int n;
+};
+hipError_t launch_rotate(const RotateJobs& jobs, int n_tok, hipStream_t stream);
 
 // Quantize every position that moves to INT2 in this append, from the ring
 // (old rows) or the staging rows (new tokens), into the pages.
@@ -60,14 +70,13 @@ hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* st
 hipError_t launch_dequant(const CacheArgs& c, int slot, int len, int t0, int t1, float* k_out,
                           float* v_out, hipStream_t stream);
 
-// INT2 split-K decode with in-kernel merge and un-rotation.
+// INT2 split-K decode (partials to the workspace) and the merge / un-rotation launch.
 struct DecodePlan {
   int splits;                    // work-groups per (sequence, KV head, head pass)
   int hp;                        // query heads handled per pass (<= 16 / ng)
   int passes;                    // ceil(g / hp)
 };
 hipError_t launch_decode(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
-                         const uint16_t* q_rot, float* out, float* partials,
-                         uint32_t* counters, hipStream_t stream);
+                         const uint16_t* q_rot, float* out, float* partials, hipStream_t stream);
 
 }  // namespace oscar
