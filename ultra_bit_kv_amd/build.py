@@ -15,6 +15,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liboscar_kv.so")
 SOURCES = ["api.cpp", "k_rotate.hip", "k_quant.hip", "k_dequant.hip", "k_decode.hip"]
+# The decode kernel keeps its MFMA accumulators in VGPRs so the (rare) online
+# softmax rescale multiplies them in place instead of copying AGPRs each step.
+EXTRA = {"k_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 # Packed fp32 VALU ops are turned off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -49,7 +52,8 @@ def build(verbose=False):
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"]
-        cmds.append([cc] + lang + COMMON + DEVICE_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc] + lang + COMMON + DEVICE_FLAGS + EXTRA.get(src, []) +
+                    ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))

@@ -8,7 +8,7 @@
 #include <vector>
 
 #include "oscar_internal.h"
-#include "../../include/oscar_kv.h"
+#include "oscar_kv.h"
 
 namespace {
 
@@ -36,16 +36,22 @@ int ring_cap(const oscar_kv_config& c) {
 int ng_of(const oscar_kv_config& c) { return kD / c.group_size; }
 
 // Query heads per decode pass: columns of a 16-wide MFMA tile are
-// (group, head) pairs, so hp * ng <= 16, hp a power of two.
+// (group, head) pairs, so hp * ng <= 16.  With more than one group the
+// columns of one head are hp apart and the group sum is log2(16 / hp) DPP
+// rotations, so hp = 16 / ng; with one group hp just covers g.
 DecodePlan head_passes(const oscar_kv_config& c) {
   const int g = c.num_q_heads / c.num_kv_heads;
-  int hp = 1;
-  while (hp < g) hp *= 2;
-  hp = std::min(hp, 16 / ng_of(c));
+  int hp = 16 / ng_of(c);
+  if (ng_of(c) == 1) {
+    hp = 1;
+    while (hp < g && hp < 16) hp *= 2;
+  }
   DecodePlan p{};
   p.hp = hp;
   p.passes = (g + hp - 1) / hp;
-  p.splits = 1;
+  p.wh = c.num_kv_heads % 4 == 0 ? 4 : (c.num_kv_heads % 2 == 0 ? 2 : 1);
+  p.quota = 1;
+  p.smax = 1;
   return p;
 }
 
@@ -58,14 +64,14 @@ int min_splits(const oscar_kv_config& c) {
   return std::max(1, (pairs + kMaxPairsPerSplit - 1) / kMaxPairsPerSplit);
 }
 
-// Upper bound on splits for n_seqs sequences: about 4096 work-groups at most,
-// at most 128 per (sequence, KV head, pass), and never fewer than the LDS
-// page-list limit requires.
+// Most splits per sequence the workspace is sized for: about 16K partial
+// records in total, at most 256 per (sequence, KV head, pass), and never
+// fewer than the LDS page-list limit requires.
 int max_splits(const oscar_kv_config& c, int n_seqs) {
   const DecodePlan p = head_passes(c);
   const long long rows = (long long)std::max(1, n_seqs) * c.num_kv_heads * p.passes;
-  long long s = (4096 + rows - 1) / rows;
-  s = std::max(1LL, std::min(128LL, s));
+  long long s = (16384 + rows - 1) / rows;
+  s = std::max(1LL, std::min(256LL, s));
   return (int)std::max<long long>(s, min_splits(c));
 }
 
@@ -106,10 +112,11 @@ CacheArgs make_args(const oscar_kv_cache& k) {
   return a;
 }
 
-// gfx950 check, once per device.
-int check_device() {
+// gfx950 check and compute-unit count, once per device.
+int check_device(int* cus = nullptr) {
   static std::mutex mu;
   static int known[64] = {0};   // 0 unknown, 1 ok, -1 not gfx950
+  static int n_cu[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return OSCAR_ERR_HIP;
   if (dev < 0 || dev >= 64) return OSCAR_ERR_DEVICE;
@@ -118,8 +125,22 @@ int check_device() {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return OSCAR_ERR_HIP;
     known[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    n_cu[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   }
+  if (cus) *cus = n_cu[dev];
   return known[dev] == 1 ? OSCAR_OK : OSCAR_ERR_DEVICE;
+}
+
+// Decode work of a row of len tokens in page pairs (a window block = 3
+// pairs); the kernels compute the same numbers from the device lengths.
+constexpr int kWinCost = 3;
+int64_t decode_cost(int64_t len, const oscar_kv_config& c) {
+  const int64_t pairs = (int2_pages(len, c) + 1) / 2;
+  const int64_t sq = s_quant(len, c);
+  const int64_t nsink = std::min<int64_t>(len, c.s_sink);
+  const int64_t ring_lo = std::max<int64_t>(sq, c.s_sink);
+  const int64_t wu = (nsink + kPage - 1) / kPage + (len > ring_lo ? ring_cap(c) / kPage : 0);
+  return pairs + kWinCost * wu;
 }
 
 thread_local char g_last_hip[160] = "";
@@ -287,8 +308,6 @@ int oscar_int2_decode_attn(const oscar_kv_cache* cache, int32_t n_seqs,
     return OSCAR_ERR_NULL;
   if (n_seqs < 1 || n_seqs > c.max_seqs) return OSCAR_ERR_ARG;
   const int64_t max_len = oscar_max_seq_len(&c);
-  int64_t max_units = 0;
-  const int ring_blocks = ring_cap(c) / kPage;
   for (int i = 0; i < n_seqs; ++i) {
     const int slot = seq_slots_host[i];
     const int64_t len = seq_lens_host[i];
@@ -296,18 +315,38 @@ int oscar_int2_decode_attn(const oscar_kv_cache* cache, int32_t n_seqs,
     if (len < 1) return OSCAR_ERR_ARG;
     if (len > max_len || int2_pages(len, c) > c.max_pages_per_seq) return OSCAR_ERR_CAPACITY;
     if (int2_pages(len, c) > 0 && c.num_pages < 1) return OSCAR_ERR_CAPACITY;
-    const int64_t pairs = (int2_pages(len, c) + 1) / 2;
-    const int64_t win = (std::min<int64_t>(len, c.s_sink) + kPage - 1) / kPage + ring_blocks;
-    max_units = std::max(max_units, pairs + 4 * win);
   }
+  if (workspace_bytes < partials_bytes(c, n_seqs)) return OSCAR_ERR_WORKSPACE;
+  int cus = 256;
+  if ((st = check_device(&cus)) != OSCAR_OK) return st;
+  // Context splits: a fixed work quota per work-group.  Choose the smallest
+  // quota whose work-groups all fit in one round of the device (12 waves per
+  // compute unit at this kernel's register use), so no work-group waits for
+  // a second round; long sequences get more splits.
   DecodePlan plan = head_passes(c);
-  // about 4 units (page pairs; window blocks count 4) per wave, 4 waves per group
-  const int want = (int)std::max<int64_t>(1, (max_units + 15) / 16);
-  plan.splits = std::max(min_splits(c), std::min(max_splits(c, n_seqs), want));
-  const size_t need = partials_bytes(c, n_seqs);
-  if (workspace_bytes < need) return OSCAR_ERR_WORKSPACE;
-  if ((st = check_device()) != OSCAR_OK) return st;
-
+  const int64_t rows = (int64_t)(c.num_kv_heads / plan.wh) * plan.passes;
+  const int64_t slots = (int64_t)cus * (12 / plan.wh);
+  std::vector<int64_t> cost(n_seqs);
+  int64_t total = 0, max_cost = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    cost[i] = decode_cost(seq_lens_host[i], c);
+    total += cost[i];
+    max_cost = std::max(max_cost, cost[i]);
+  }
+  const int cap = max_splits(c, n_seqs);
+  int64_t quota = std::max<int64_t>(2, (total * rows + slots - 1) / slots);
+  quota = std::max<int64_t>(quota, (max_cost + cap - 1) / cap);
+  for (;; quota += std::max<int64_t>(1, quota / 16)) {
+    if (quota >= kMaxPairsPerSplit) {
+      quota = kMaxPairsPerSplit;
+      break;
+    }
+    int64_t wgs = 0;
+    for (int i = 0; i < n_seqs; ++i) wgs += (cost[i] + quota - 1) / quota;
+    if (wgs * rows <= slots) break;
+  }
+  plan.quota = (int)quota;
+  plan.smax = (int)std::max<int64_t>(1, (max_cost + quota - 1) / quota);
   const CacheArgs a = make_args(*cache);
   SeqArgs sa{seq_slots, seq_lens, nullptr, n_seqs};
   return hip_status(launch_decode(a, sa, plan, q_rot, out, (float*)workspace, (hipStream_t)stream));

@@ -10,8 +10,9 @@
 // (max, sum, unnormalized output), and a second launch merges them by
 // log-sum-exp and applies R_V^T.
 //
-// Work-group = 4 waves; one (sequence, KV head, query-head pass, split).
-// Column n (0..15) of every MFMA tile is (group gi = n / HP, head hl = n % HP).
+// Work-group = (sequence, context split, group of adjacent KV heads), one
+// wave per KV head.  Column n (0..15) of every MFMA tile is (group gi = n / HP,
+// head hl = n % HP).
 //
 // INT2 page pair (32 tokens), per wave:
 //   QK^T: A = K codes [16 tokens x 32 channels] per instruction, taken as fp16
@@ -76,6 +77,19 @@ __device__ __forceinline__ float f16hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// fp16 pair (a * lo16(wa), b * lo16(wb)), rounded to fp16.
+__device__ __forceinline__ uint32_t mul_f32_by_f16lo_pack(float a, uint32_t wa, float b,
+                                                          uint32_t wb) {
+  const half2_t ha = __builtin_bit_cast(half2_t, wa);
+  const half2_t hb = __builtin_bit_cast(half2_t, wb);
+  half2_t r;
+  r.x = (_Float16)(a * (float)ha.x);
+  r.y = (_Float16)(b * (float)hb.x);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
@@ -87,16 +101,17 @@ struct SoftmaxState {
   float z;   // this lane's share of sum_t p_t * zero_v[t][group]
 };
 
-// Online-softmax update with a lazy max: the reference max only moves when a
-// logit exceeds it by more than 8 (so p <= 2^8), which keeps most tiles free
-// of the accumulator rescale.
+// Online-softmax update with a lazy max.  x holds logits in raw units; the
+// log2-domain logit is scale * x (scale > 0).  The reference max only moves
+// when a logit exceeds it by more than 8 (so p <= 2^8), which keeps most
+// tiles free of the accumulator rescale.
 template <int N>
-__device__ __forceinline__ void softmax_step(float (&x)[N], float (&p)[N], SoftmaxState& st,
-                                             float4_t (&acc)[8]) {
+__device__ __forceinline__ void softmax_step(const float (&x)[N], float scale, float (&p)[N],
+                                             SoftmaxState& st, float4_t (&acc)[8]) {
   float tmax = x[0];
 #pragma unroll
   for (int k = 1; k < N; ++k) tmax = fmaxf(tmax, x[k]);
-  tmax = rows_max(tmax);
+  tmax = rows_max(tmax) * scale;
   if (__any(tmax > st.m + 8.0f)) {
     const float m_new = fmaxf(st.m, tmax);
     const float alpha = m_new > st.m ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.0f;
@@ -109,32 +124,43 @@ __device__ __forceinline__ void softmax_step(float (&x)[N], float (&p)[N], Softm
   const float mref = st.m == kNegInf ? 0.0f : st.m;
 #pragma unroll
   for (int k = 0; k < N; ++k) {
-    p[k] = __builtin_amdgcn_exp2f(x[k] - mref);
+    p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k], scale, -mref));
     st.l += p[k];
   }
 }
 
 constexpr int kMaxWgPages = 512;   // page ids staged per work-group (<= 256 pairs per split)
+constexpr int kPrefetch = 2;       // page pairs in flight per wave ahead of the one processed
+constexpr int kWinCost = 3;        // a BF16 window block (8 KB) costs about three page pairs
 
-template <int NG, int HP>
-__global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s, int splits,
-                                                          int passes,
-                                                          const uint16_t* __restrict__ q_rot,
-                                                          float* __restrict__ partials) {
+// Splits of one sequence's context: the work quota per split (INT2 page
+// pairs, a BF16 window block counting as kWinCost pairs) is a launch
+// constant, so the number of splits follows the sequence length.
+__device__ __forceinline__ int splits_of(int n_pairs, int n_wu, int quota) {
+  const int cost = n_pairs + kWinCost * n_wu;
+  return cost > 0 ? (cost + quota - 1) / quota : 1;
+}
+
+// Work-group = (sequence, split, group of WH adjacent KV heads); wave w owns
+// KV head WH * group + w.  All waves walk the same pages, so each page is
+// fetched as one contiguous run of WH page-head blocks.
+template <int NG, int HP, int PF, int WH>
+__global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqArgs s, int quota,
+                                                              int passes, int smax,
+                                                              const uint16_t* __restrict__ q_rot,
+                                                              float* __restrict__ partials) {
   constexpr int G = kD / NG;
   constexpr int PW = HP * kD + 2 * HP;   // floats per partial record
-  __shared__ float red_m[4][HP];
-  __shared__ float red_l[4][HP];
-  __shared__ float red_o[4][HP][kD];
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[HP][kD];
-  __shared__ float s_qsum[HP * NG];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[WH][HP][kD];
+  __shared__ float s_qsum[WH][HP * NG];
   __shared__ int s_pages[kMaxWgPages];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = blockIdx.x;
-  const int h = blockIdx.y / passes, pass = blockIdx.y % passes;
+  const int hgrp = blockIdx.y / passes, pass = blockIdx.y % passes;
+  const int h = hgrp * WH + wave;
   const int i = blockIdx.z;
   const int r16 = lane & 15, qd = lane >> 4;
 
@@ -144,37 +170,71 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
   if (!row_ok) len = 0;
   const int nh = min(HP, c.g - pass * HP);   // valid heads in this pass
 
-  // ---- this split's share of the INT2 pages
+  // ---- this split's share of the context: INT2 page pairs and BF16 window blocks
   const int sq = s_quant_of(len, c.s_sink, c.s_keep, c.s_flush);
   const int nq = sq > c.s_sink ? sq - c.s_sink : 0;               // INT2 tokens
   const int n_pages = (nq + kPage - 1) / kPage;
   const int n_pairs = (n_pages + 1) / 2;
-  const int pb = (int)((long long)split * n_pairs / splits);
-  const int pe = (int)((long long)(split + 1) * n_pairs / splits);
   const int32_t* bt = c.block_table + (size_t)(row_ok ? slot : 0) * c.max_pages;
 
-  // ---- stage the query rows of this pass and the split's page ids in LDS
-  const uint16_t* qbase =
-      q_rot + ((size_t)(row_ok ? i : 0) * c.hq + (size_t)h * c.g + (size_t)pass * HP) * kD;
-  for (int t = tid; t < HP * 16; t += 256) {
-    const int hh = t >> 4, part = t & 15;
+  const int nsink = min(len, c.s_sink);
+  const int sb_n = (nsink + kPage - 1) / kPage;
+  const int ring_lo = max(sq, c.s_sink);
+  const int cnt = len > ring_lo ? len - ring_lo : 0;
+  const int b0 = (ring_lo - c.s_sink) % c.ring_cap;
+  const int rb_n = cnt > 0 ? c.ring_cap / kPage : 0;
+  const int n_wu = sb_n + rb_n;
+  const int n_split = min(splits_of(n_pairs, n_wu, quota), smax);
+  if (split >= n_split) return;                                   // uniform for the group
+  const int pb = (int)((long long)split * n_pairs / n_split);
+  const int pe = (int)((long long)(split + 1) * n_pairs / n_split);
+  const int wb = (int)((long long)split * n_wu / n_split);
+  const int we = (int)((long long)(split + 1) * n_wu / n_split);
+  const uint16_t* wbase = c.win + ((size_t)(row_ok ? slot : 0) * c.hkv + h) * c.win_blocks *
+                                      (2 * kPage * kD);
+  struct Win {
+    u32x4 kl[4], vl[4];
+    int u;
+  };
+  auto win_block = [&](int u) { return u < sb_n ? u : c.sink_blocks + (u - sb_n); };
+  auto win_slot_ok = [&](int u, int t) {
+    if (u < sb_n) return kPage * u + t < nsink;
+    const int off = (kPage * (u - sb_n) + t - b0 + c.ring_cap) % c.ring_cap;
+    return off < cnt;
+  };
+  auto load_win = [&](int u, Win& W) {
+    W.u = u;
+    const uint16_t* bp = wbase + (size_t)win_block(u) * (2 * kPage * kD);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      W.kl[k] = *(const u32x4*)(bp + r16 * kD + 32 * qd + 8 * k);
+      W.vl[k] = *(const u32x4*)(bp + kPage * kD + 32 * (16 * qd + r16) + 8 * k);
+    }
+  };
+  // ---- stage the query rows (WH heads x this pass) and the split's page ids in LDS
+  for (int t = tid; t < WH * HP * 16; t += 64 * WH) {
+    const int ww = t / (HP * 16), hh = (t / 16) % HP, part = t & 15;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (hh < nh) v = *(const u32x4*)(qbase + (size_t)hh * kD + 8 * part);
-    *(u32x4*)(&s_q[hh][8 * part]) = v;
+    if (hh < nh) {
+      const size_t qh = (size_t)(hgrp * WH + ww) * c.g + (size_t)pass * HP + hh;
+      v = *(const u32x4*)(q_rot + ((size_t)(row_ok ? i : 0) * c.hq + qh) * kD + 8 * part);
+    }
+    *(u32x4*)(&s_q[ww][hh][8 * part]) = v;
   }
   const int n_wg_pages = min(2 * (pe - pb), kMaxWgPages);
-  for (int t = tid; t < n_wg_pages; t += 256) {
+  for (int t = tid; t < n_wg_pages; t += 64 * WH) {
     const int pg = 2 * pb + t;
     int ph = -1;
     if (pg < n_pages && pg < c.max_pages) ph = bt[pg];
     s_pages[t] = (ph >= 0 && ph < c.num_pages) ? ph : -1;
   }
   __syncthreads();
-  if (tid < HP * NG) {   // sum of each (group, head) slice of q', column n = group * HP + head
-    const int hh = tid % HP, gg = tid / HP;
+  for (int t = tid; t < WH * HP * NG; t += 64 * WH) {   // (group, head) slices of q', column order
+    const int ww = t / (HP * NG), col = t % (HP * NG);
+    const int hh = col % HP, gg = col / HP;
     float sum = 0.0f;
-    for (int ch = gg * G; ch < (gg + 1) * G; ++ch) sum += bf16_bits_to_f32(s_q[hh][ch]);
-    s_qsum[tid] = sum;
+    for (int ch = gg * G; ch < (gg + 1) * G; ++ch) sum += bf16_bits_to_f32(s_q[ww][hh][ch]);
+    s_qsum[ww][col] = sum;
   }
   __syncthreads();
 
@@ -185,13 +245,14 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
   const bool bval = colv && (gi == grp_q);
   const float C2 = kLog2e * 0.08838834764831845f;                // log2(e) / sqrt(128)
   const float K1 = C2 * 16777216.0f;                              // undo the 2^-24 code scaling
-  const float qsC = colv ? s_qsum[n] * C2 : 0.0f;
+  // INT2 logits in raw units x = s * D + z * qsum * 2^-24, log2 logit = K1 * x
+  const float qz = colv ? s_qsum[wave][n] * (1.0f / 16777216.0f) : 0.0f;
 
   u32x4 wq[4];
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    wq[cc] = colv ? *(const u32x4*)(&s_q[hl][32 * qd + 8 * cc]) : z;
+    wq[cc] = colv ? *(const u32x4*)(&s_q[wave][hl][32 * qd + 8 * cc]) : z;
   }
   bf16x8 bw[4];
   half8 bq[4];
@@ -227,14 +288,12 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
     int tok;      // INT2 token index of slot 0 of page A
     bool oka, okb;
   };
-  // pairs of this wave: local index wave + 4k, k < npw (interleaved over the 4 waves)
-  const int nw = pe - pb;
-  const int npw = nw > wave ? (nw - wave + 3) / 4 : 0;
+  const int np = pe - pb;                                         // pairs of this split
   const int koff = (r16 * 8 + 2 * qd) * 4;
   const int poff = 1024 + 4 * (16 * gsel + 4 * qd);
   const int vpoff = poff + 64 * NG;
   auto load_pair = [&](int k, Pair& d) {
-    const int local = wave + 4 * min(k, npw - 1);     // tail loads re-read the last pair
+    const int local = min(k, np - 1);                             // tail loads re-read the last pair
     int pa = s_pages[2 * local], pbq = s_pages[2 * local + 1];
     d.oka = pa >= 0;
     d.okb = pbq >= 0;
@@ -271,10 +330,10 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
     float x[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      x[r] = f16lo(d.kpa[r]) * (da[r] * K1) + f16hi(d.kpa[r]) * qsC;
-      x[4 + r] = f16lo(d.kpb[r]) * (db[r] * K1) + f16hi(d.kpb[r]) * qsC;
+      x[r] = __builtin_fmaf(f16lo(d.kpa[r]), da[r], f16hi(d.kpa[r]) * qz);
+      x[4 + r] = __builtin_fmaf(f16lo(d.kpb[r]), db[r], f16hi(d.kpb[r]) * qz);
     }
-    if constexpr (NG > 1) {
+    if constexpr (NG > 1) {   // sum the group partials: lanes n, n +- HP, ... of a 16-lane row
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         if constexpr (HP <= 8) x[k] += row_ror<8>(x[k]);
@@ -283,20 +342,26 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
         if constexpr (HP <= 1) x[k] += row_ror<1>(x[k]);
       }
     }
-    const int ta = d.tok + 4 * qd;   // INT2 token index of row 0 of tile A in this lane
+    if (!(d.oka && d.okb && d.tok + 32 <= nq)) {   // the pair holds slots past S_quant
+      const int ta = d.tok + 4 * qd;   // INT2 token index of row 0 of tile A in this lane
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (!(d.oka && ta + r < nq)) x[r] = kNegInf;
-      if (!(d.okb && ta + 16 + r < nq)) x[4 + r] = kNegInf;
+      for (int r = 0; r < 4; ++r) {
+        if (!(d.oka && ta + r < nq)) x[r] = kNegInf;
+        if (!(d.okb && ta + 16 + r < nq)) x[4 + r] = kNegInf;
+      }
     }
     float p[8];
-    softmax_step<8>(x, p, st, acc);
-    half8 pv;
+    softmax_step<8>(x, K1, p, st, acc);
+    u32x4 pw;   // P' = p * scale_v as fp16, k index 8 qd + e <-> (e < 4 ? A : B) row e % 4
+    pw[0] = mul_f32_by_f16lo_pack(p[0], d.vpa[0], p[1], d.vpa[1]);
+    pw[1] = mul_f32_by_f16lo_pack(p[2], d.vpa[2], p[3], d.vpa[3]);
+    pw[2] = mul_f32_by_f16lo_pack(p[4], d.vpb[0], p[5], d.vpb[1]);
+    pw[3] = mul_f32_by_f16lo_pack(p[6], d.vpb[2], p[7], d.vpb[3]);
+    const half8 pv = __builtin_bit_cast(half8, pw);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pv[r] = (_Float16)(p[r] * f16lo(d.vpa[r]));
-      pv[4 + r] = (_Float16)(p[4 + r] * f16lo(d.vpb[r]));
-      st.z += p[r] * f16hi(d.vpa[r]) + p[4 + r] * f16hi(d.vpb[r]);
+      st.z = __builtin_fmaf(p[r], f16hi(d.vpa[r]), st.z);
+      st.z = __builtin_fmaf(p[4 + r], f16hi(d.vpb[r]), st.z);
     }
     const uint32_t w0 = d.va[0], w1 = d.va[1], w2 = d.vb[0], w3 = d.vb[1];
     const uint32_t s0 = w0 >> 8, s1 = w1 >> 8, s2 = w2 >> 8, s3 = w3 >> 8;
@@ -309,64 +374,16 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
     }
   };
 
-  if (npw > 0) {   // ping-pong: the loads of the next pair are in flight while one is processed
-    Pair pa_, pb_;
-    load_pair(0, pa_);
-    for (int k = 0; k < npw; k += 2) {
-      load_pair(k + 1, pb_);
-      process_pair(pa_);
-      load_pair(k + 2, pa_);
-      if (k + 1 < npw) process_pair(pb_);
-    }
-  }
-  // INT2 accumulators carry code * 4^(j%4) * 2^-24: bring them to true scale
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] *= 16777216.0f / (float)(1 << (2 * (j & 3)));
-
-  // ---- BF16 window blocks (sink, then ring)
-  const int nsink = min(len, c.s_sink);
-  const int sb_n = (nsink + kPage - 1) / kPage;
-  const int ring_lo = max(sq, c.s_sink);
-  const int cnt = len > ring_lo ? len - ring_lo : 0;
-  const int b0 = (ring_lo - c.s_sink) % c.ring_cap;
-  const int rb_n = cnt > 0 ? c.ring_cap / kPage : 0;
-  const int n_wu = sb_n + rb_n;
-  const int wb = (int)((long long)split * n_wu / splits);
-  const int we = (int)((long long)(split + 1) * n_wu / splits);
-  const uint16_t* wbase = c.win + ((size_t)(row_ok ? slot : 0) * c.hkv + h) * c.win_blocks *
-                                      (2 * kPage * kD);
-  for (int u = wb + wave; u < we; u += 4) {
-    int blk, first;   // window block and the slot index of its slot 0 in its segment
-    const bool is_sink = u < sb_n;
-    if (is_sink) {
-      blk = u;
-      first = kPage * u;
-    } else {
-      blk = c.sink_blocks + (u - sb_n);
-      first = kPage * (u - sb_n);
-    }
-    auto slot_ok = [&](int t) {
-      if (is_sink) return first + t < nsink;
-      const int off = (first + t - b0 + c.ring_cap) % c.ring_cap;
-      return off < cnt;
-    };
-    if (!__any(slot_ok(r16))) continue;
-    const uint16_t* bp = wbase + (size_t)blk * (2 * kPage * kD);
-    u32x4 kl[4], vl[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      kl[k] = *(const u32x4*)(bp + r16 * kD + 32 * qd + 8 * k);
-      vl[k] = *(const u32x4*)(bp + kPage * kD + 32 * (16 * qd + r16) + 8 * k);
-    }
+  auto process_win = [&](const Win& W) {
     float4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kl[cc]), bw[cc], d, 0,
-                                                  0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, W.kl[cc]), bw[cc], d,
+                                                  0, 0, 0);
     float x[4], p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = slot_ok(4 * qd + r) ? d[r] * C2 : kNegInf;
-    softmax_step<4>(x, p, st, acc);
+    for (int r = 0; r < 4; ++r) x[r] = win_slot_ok(W.u, 4 * qd + r) ? d[r] : kNegInf;
+    softmax_step<4>(x, C2, p, st, acc);
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -377,70 +394,101 @@ __global__ __launch_bounds__(256) void int2_decode_kernel(CacheArgs c, SeqArgs s
     const short4_t plo = {(short)lo[0], (short)lo[1], (short)lo[2], (short)lo[3]};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const u32x4 src = vl[j >> 1];
+      const u32x4 src = W.vl[j >> 1];
       const u32x2 pr = (j & 1) ? u32x2{src[2], src[3]} : u32x2{src[0], src[1]};
       const short4_t a = __builtin_bit_cast(short4_t, pr);
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, acc[j], 0, 0, 0);
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, acc[j], 0, 0, 0);
     }
+  };
+
+  // ---- INT2 ring: PF page pairs in flight ahead of the one being processed
+  Pair ring[PF];
+  if (np > 0) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) load_pair(j, ring[j]);
   }
 
-  // ---- wave totals -> LDS
-  st.l = rows_sum(st.l);
-  st.z = rows_sum(st.z);
-  if (qd == 0 && gi == 0) {
-    red_m[wave][hl] = st.m;
-    red_l[wave][hl] = st.l;
-  }
-  if (bval) {   // lane holds channels 32qd .. 32qd+31 of its head, in its own group
+  // ---- INT2 page pairs: accumulate in code units (code * 4^(j%4) * 2^-24)
+  if (np > 0) {
+    for (int k = 0; k < np; k += PF) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) red_o[wave][hl][32 * qd + 8 * r + j] = acc[j][r] + st.z;
-  }
-  __syncthreads();
-
-  // ---- merge the 4 waves -> this work-group's partial record
-  float* rec = partials + ((((size_t)i * c.hkv + h) * passes + pass) * splits + split) * PW;
-  for (int idx = tid; idx < nh * kD; idx += 256) {
-    const int hh = idx / kD, ch = idx % kD;
-    float M = red_m[0][hh];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w][hh]);
-    float L = 0.0f, O = 0.0f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float wt = __builtin_amdgcn_exp2f(red_m[w][hh] - M);
-        L += wt * red_l[w][hh];
-        O += wt * red_o[w][hh][ch];
+      for (int j = 0; j < PF; ++j) {
+        if (k + j < np) process_pair(ring[j]);
+        load_pair(k + j + PF, ring[j]);
       }
     }
-    if (ch == 0) {
-      rec[hh] = M;
-      rec[HP + hh] = L;
-    }
-    rec[2 * HP + hh * kD + ch] = O;
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] *= 16777216.0f / (float)(1 << (2 * (j & 3)));
+
+  // ---- BF16 window blocks (true scale), one block in flight ahead
+  if (wb < we) {
+    Win wa, wn;
+    load_win(wb, wa);
+    for (int u = wb; u < we; ++u) {
+      if (u + 1 < we) load_win(u + 1, wn);
+      if (__any(win_slot_ok(u, r16))) process_win(wa);
+      wa = wn;
+    }
+  }
+
+  // ---- this wave's partial record: (max, sum, unnormalized o') per head of the pass
+  st.l = rows_sum(st.l);
+  st.z = rows_sum(st.z);
+  float* rec = partials + ((((size_t)i * c.hkv + h) * passes + pass) * smax + split) * PW;
+  if (qd == 0 && gi == 0 && hl < nh) {
+    rec[hl] = st.m;
+    rec[HP + hl] = st.l;
+  }
+  if (bval) {   // lane holds channels 32qd .. 32qd+31 of its head, in its own group
+    float* o = rec + 2 * HP + hl * kD + 32 * qd;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float4_t lo = {acc[0][r] + st.z, acc[1][r] + st.z, acc[2][r] + st.z, acc[3][r] + st.z};
+      const float4_t hi = {acc[4][r] + st.z, acc[5][r] + st.z, acc[6][r] + st.z, acc[7][r] + st.z};
+      *(float4_t*)(o + 8 * r) = lo;
+      *(float4_t*)(o + 8 * r + 4) = hi;
+    }
+  }
+}
+
+// Number of window units (sink blocks + ring blocks visited) of a row of len tokens.
+__device__ __forceinline__ int window_units(const CacheArgs& c, int len, int sq) {
+  const int nsink = min(len, c.s_sink);
+  const int ring_lo = max(sq, c.s_sink);
+  return (nsink + kPage - 1) / kPage + (len > ring_lo ? c.ring_cap / kPage : 0);
 }
 
 // Log-sum-exp merge of the split partials of one (sequence, KV head, pass),
 // then o = o' . R_V^T with R_V staged in LDS (rows padded to 129 floats so the
-// row-per-thread reads of a wave fall in distinct banks).
+// row-per-thread reads of a wave fall in distinct banks).  The per-split
+// maxima and sums are gathered first (one round of loads), then each output
+// channel sums its splits with batched loads.
 template <int HP>
-__global__ __launch_bounds__(256) void merge_unrotate_kernel(CacheArgs c, SeqArgs s, int splits,
-                                                             int passes,
+__global__ __launch_bounds__(256) void merge_unrotate_kernel(CacheArgs c, SeqArgs s, int quota,
+                                                             int passes, int smax,
                                                              const float* __restrict__ partials,
                                                              float* __restrict__ out) {
   constexpr int PW = HP * kD + 2 * HP;
+  constexpr int kMaxS = 256;
   __shared__ float rv[kD][kD + 1];
   __shared__ float fin[HP][kD];
+  __shared__ float s_w[kMaxS][HP];
+  __shared__ float s_l[HP];
   const int tid = threadIdx.x;
   const int h = blockIdx.x / passes, pass = blockIdx.x % passes;
   const int i = blockIdx.y;
-  const int slot = s.slots[i];
-  const bool row_ok = slot >= 0 && slot < c.max_seqs && s.lens[i] >= 1;
   const int nh = min(HP, c.g - pass * HP);
+  const int slot = s.slots[i];
+  int len = s.lens[i];
+  const bool row_ok = slot >= 0 && slot < c.max_seqs && len >= 1;
+  if (!row_ok) len = 0;
+  const int sq = s_quant_of(len, c.s_sink, c.s_keep, c.s_flush);
+  const int nq = sq > c.s_sink ? sq - c.s_sink : 0;
+  const int n_pairs = ((nq + kPage - 1) / kPage + 1) / 2;
+  const int n_split = min(min(splits_of(n_pairs, window_units(c, len, sq), quota), smax), kMaxS);
+  const float* recs = partials + (((size_t)i * c.hkv + h) * passes + pass) * smax * PW;
 
   const float4* rg = (const float4*)(c.r_v + (size_t)h * kD * kD);
   for (int t = tid; t < kD * kD / 4; t += 256) {
@@ -451,19 +499,27 @@ __global__ __launch_bounds__(256) void merge_unrotate_kernel(CacheArgs c, SeqArg
     rv[row][col + 2] = v.z;
     rv[row][col + 3] = v.w;
   }
-  const float* recs = partials + (((size_t)i * c.hkv + h) * passes + pass) * splits * PW;
+  for (int t = tid; t < n_split * nh; t += 256) s_w[t / nh][t % nh] = recs[(size_t)(t / nh) * PW + t % nh];
+  __syncthreads();
+  if (tid < nh) {   // log-sum-exp weights of the splits of head tid
+    float M = kNegInf;
+    for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, s_w[sp][tid]);
+    float L = 0.0f;
+    for (int sp = 0; sp < n_split; ++sp) {
+      const float wt = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s_w[sp][tid] - M);
+      L += wt * recs[(size_t)sp * PW + HP + tid];
+      s_w[sp][tid] = wt;
+    }
+    s_l[tid] = L;
+  }
+  __syncthreads();
   for (int idx = tid; idx < nh * kD; idx += 256) {
     const int hh = idx / kD, ch = idx % kD;
-    float M = kNegInf;
-    for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, recs[(size_t)sp * PW + hh]);
-    float L = 0.0f, O = 0.0f;
-    for (int sp = 0; sp < splits; ++sp) {
-      const float* r = recs + (size_t)sp * PW;
-      const float wt = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(r[hh] - M);
-      L += wt * r[HP + hh];
-      O += wt * r[2 * HP + hh * kD + ch];
-    }
-    fin[hh][ch] = O / L;
+    const float* o = recs + 2 * HP + hh * kD + ch;
+    float O = 0.0f;
+#pragma unroll 8
+    for (int sp = 0; sp < n_split; ++sp) O = __builtin_fmaf(s_w[sp][hh], o[(size_t)sp * PW], O);
+    fin[hh][ch] = O / s_l[hh];
   }
   __syncthreads();
   if (!row_ok) return;
@@ -480,14 +536,27 @@ template <int NG, int HP>
 static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                                   const uint16_t* q_rot, float* out, float* partials,
                                   hipStream_t stream) {
-  dim3 grid(plan.splits, c.hkv * plan.passes, s.n_seqs);
-  hipLaunchKernelGGL((int2_decode_kernel<NG, HP>), grid, dim3(256), 0, stream, c, s, plan.splits,
-                     plan.passes, q_rot, partials);
+  const int wh = plan.wh;
+  dim3 grid(plan.smax, (c.hkv / wh) * plan.passes, s.n_seqs);
+  switch (wh) {
+    case 4:
+      hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 4>), grid, dim3(256), 0, stream,
+                         c, s, plan.quota, plan.passes, plan.smax, q_rot, partials);
+      break;
+    case 2:
+      hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 2>), grid, dim3(128), 0, stream,
+                         c, s, plan.quota, plan.passes, plan.smax, q_rot, partials);
+      break;
+    default:
+      hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 1>), grid, dim3(64), 0, stream,
+                         c, s, plan.quota, plan.passes, plan.smax, q_rot, partials);
+      break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 mgrid(c.hkv * plan.passes, s.n_seqs);
-  hipLaunchKernelGGL((merge_unrotate_kernel<HP>), mgrid, dim3(256), 0, stream, c, s, plan.splits,
-                     plan.passes, partials, out);
+  hipLaunchKernelGGL((merge_unrotate_kernel<HP>), mgrid, dim3(256), 0, stream, c, s, plan.quota,
+                     plan.passes, plan.smax, partials, out);
   return hipGetLastError();
 }
 

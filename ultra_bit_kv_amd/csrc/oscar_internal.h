@@ -72,9 +72,11 @@ hipError_t launch_dequant(const CacheArgs& c, int slot, int len, int t0, int t1,
 
 // INT2 split-K decode (partials to the workspace) and the merge / un-rotation launch.
 struct DecodePlan {
-  int splits;                    // work-groups per (sequence, KV head, head pass)
+  int quota;                     // work per context split, in page pairs (a window block = 3)
+  int smax;                      // most splits of any sequence (grid x)
   int hp;                        // query heads handled per pass (<= 16 / ng)
   int passes;                    // ceil(g / hp)
+  int wh;                        // KV heads (waves) per work-group
 };
 hipError_t launch_decode(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                          const uint16_t* q_rot, float* out, float* partials, hipStream_t stream);
