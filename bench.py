@@ -11,10 +11,10 @@ each step reads a cache that is not resident in the 256 MB MALL, as in a
 multi-layer model.
 
 Prints one JSON line.  `value` = sequences decoded per second (tokens/s).
-`roofline` is for the decode kernel: algorithmic bytes per launch (INT2
-token-heads x (64 + 1024/G) B + BF16 window token-heads x 512 B + block-table
-entries x 4 B + q' in + output out) over its average duration, measured with
-HIP events on the stream it runs on.
+`roofline` is for the decode split kernel (all cache traffic): algorithmic
+bytes per launch (INT2 token-heads x (64 + 1024/G) B + BF16 window
+token-heads x 512 B + block-table entries x 4 B + q' in) over its average
+duration, measured with HIP events on the stream it runs on.
 """
 
 import argparse
@@ -41,16 +41,20 @@ def decode_source_hash():
 
 
 def algorithmic_bytes(w, lens):
-    """Bytes one decode launch must move, from the cache format (per unit figures)."""
-    from oracle import placement   # pure integer placement rule
+    """Bytes the split launch of one decode step must move, from the cache
+    format: every INT2 token-head (codes + fp16 scale/zero per group), every
+    BF16 window token-head (K and V rows), one block-table entry per INT2
+    page, and the rotated queries (bf16).  The flush boundary S_quant is the
+    closed form of the placement rule."""
     per_int2 = 64 + 1024 // w.group
     total = 0
     for L in lens:
-        sink, int2, recent = placement.segments(int(L), w.s_sink, w.s_keep, w.s_flush)
-        n_int2 = int2[1] - int2[0]
-        n_bf16 = (sink[1] - sink[0]) + (recent[1] - recent[0])
+        L = int(L)
+        s_quant = w.s_sink + w.s_flush * max(0, (L - w.s_sink - w.s_keep) // w.s_flush)
+        n_int2 = max(0, s_quant - w.s_sink)
+        n_bf16 = min(L, w.s_sink) + max(0, L - max(s_quant, w.s_sink))
         total += w.hkv * (n_int2 * per_int2 + n_bf16 * 512) + 4 * (-(-n_int2 // 16))
-    total += len(lens) * w.hq * 128 * (2 + 4)     # q' (bf16) in, output (fp32) out
+    total += len(lens) * w.hq * 128 * 2           # q' (bf16) in
     return total
 
 
@@ -193,16 +197,21 @@ def main():
         c = layers[s % args.layers]
         d = steps_in[s // args.layers]
         c.append(d["app"], d["k"], d["v"], d["q"], q_rot=q_rot)
+        # the decode step as its two launches, timed apart: the split kernel
+        # (all cache traffic) and the log-sum-exp merge / un-rotation
         if ev is not None:
             ev[0].record()
-        c.decode(d["dec"], q_rot, out)
+        c.decode_partials(d["dec"], q_rot)
         if ev is not None:
             ev[1].record()
+        c.decode_merge(d["dec"], out)
+        if ev is not None:
+            ev[2].record()
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
            for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -214,8 +223,9 @@ def main():
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_avg_ms = float(np.mean(dec_ms))
+    dec_avg_ms = float(np.mean([a.elapsed_time(c) for a, b, c in evs]))
+    split_avg_ms = float(np.mean([a.elapsed_time(b) for a, b, c in evs]))
+    merge_avg_ms = float(np.mean([b.elapsed_time(c) for a, b, c in evs]))
 
     # algorithmic bytes of the average decode launch (lengths grow during the run)
     byts = []
@@ -224,7 +234,7 @@ def main():
         k = s // args.layers
         byts.append(algorithmic_bytes(w, [int(L) + k for L in lens0]))
     bytes_per_launch = float(np.mean(byts))
-    achieved = bytes_per_launch / (dec_avg_ms * 1e-3) / 1e9
+    achieved = bytes_per_launch / (split_avg_ms * 1e-3) / 1e9
     src_hash = decode_source_hash()
     traffic = read_traffic(src_hash)
 
@@ -246,8 +256,10 @@ def main():
             "batch": n, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": 128, "group": w.group,
             "windows": [w.s_sink, w.s_keep, w.s_flush], "context_min": int(lens0.min()),
             "context_max": int(lens0.max()), "layers_cycled": args.layers,
-            "step": "rotate_quant_append(1 token/seq) + int2_decode_attn",
-            "decode_ms": dec_avg_ms, "append_ms": ms_step - dec_avg_ms,
+            "step": "rotate_quant_append(1 token/seq) + int2_decode_partials + int2_decode_merge",
+            "decode_ms": dec_avg_ms, "decode_split_ms": split_avg_ms,
+            "decode_merge_ms": merge_avg_ms, "append_ms": ms_step - dec_avg_ms,
+            "decode_call_GBs": bytes_per_launch / (dec_avg_ms * 1e-3) / 1e9,
             "decode_kernel_source": src_hash,
         },
         "roofline": {

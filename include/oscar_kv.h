@@ -192,6 +192,26 @@ int oscar_int2_decode_attn(const oscar_kv_cache* cache, int32_t n_seqs,
                            const uint16_t* q_rot, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two launches of oscar_int2_decode_attn as separate calls, for callers
+ * that schedule or time them apart [OSCAR s4 "Decoding Attention Kernel":
+ * the split-K partials and their log-sum-exp merge].  A merge call must
+ * follow the partials call of the same step on the same stream, with the
+ * same cache, sequence arguments and workspace; together they compute
+ * exactly what oscar_int2_decode_attn computes.
+ *  oscar_int2_decode_partials: q_rot as above; writes the partial records
+ *                              (max, sum, unnormalized o' per context split)
+ *                              to the workspace.
+ *  oscar_int2_decode_merge:    out as above; reads those records. */
+int oscar_int2_decode_partials(const oscar_kv_cache* cache, int32_t n_seqs,
+                               const int32_t* seq_slots_host, const int32_t* seq_lens_host,
+                               const int32_t* seq_slots, const int32_t* seq_lens,
+                               const uint16_t* q_rot,
+                               void* workspace, size_t workspace_bytes, void* stream);
+int oscar_int2_decode_merge(const oscar_kv_cache* cache, int32_t n_seqs,
+                            const int32_t* seq_slots_host, const int32_t* seq_lens_host,
+                            const int32_t* seq_slots, const int32_t* seq_lens, float* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* For checking: the decoded rows of positions [tok_begin, tok_end) of one
  * cache row holding seq_len tokens, in the rotated basis: bf16 window rows
  * widened to fp32, INT2 rows as scale * code + zero rounded once to fp32.

@@ -157,6 +157,19 @@ def test_decode_argument_checks(L):
     assert decode(L, c, [0], [mx]) in (-9, -8, 0)
 
 
+def test_decode_phase_argument_checks(L):
+    c = cfg()
+    keep = [_i32([0]), _i32([10])]
+    part = lambda q, ws=1 << 40: L.oscar_int2_decode_partials(
+        ctypes.byref(_cache(c)), 1, keep[0][1], keep[1][1], DUMMY, DUMMY, q, DUMMY, ws, None)
+    merge = lambda out, ws=1 << 40: L.oscar_int2_decode_merge(
+        ctypes.byref(_cache(c)), 1, keep[0][1], keep[1][1], DUMMY, DUMMY, out, DUMMY, ws, None)
+    assert part(None) == -1                                           # the split needs q_rot
+    assert merge(None) == -1                                          # the merge needs out
+    assert part(DUMMY, ws=100) == -7 and merge(DUMMY, ws=100) == -7
+    assert part(DUMMY) in (-9, -8, 0) and merge(DUMMY) in (-9, -8, 0)
+
+
 def test_dequant_argument_checks(L):
     c = cfg()
     cache = _cache(c)

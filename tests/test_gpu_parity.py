@@ -156,6 +156,9 @@ def test_decode_deterministic_and_edge_lengths():
     o1 = cache.decode(b, q_rot)
     o2 = cache.decode(b, q_rot)
     assert torch.equal(o1, o2)
+    # the two-call form (split launch, then merge launch) computes the same bits
+    cache.decode_partials(b, q_rot)
+    assert torch.equal(cache.decode_merge(b), o1)
     out = o1.cpu().numpy()
     r_k, r_v = cache.host_r
     for i, L in enumerate(lens):

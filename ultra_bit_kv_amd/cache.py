@@ -165,6 +165,26 @@ class OscarKVCache:
         check(st, "oscar_int2_decode_attn")
         return out
 
+    def decode_partials(self, batch, q_rot):
+        """oscar_int2_decode_partials: the split launch of a decode step."""
+        assert q_rot.dtype == torch.bfloat16 and q_rot.shape == (batch.n, self.hq, D)
+        ws = self.workspace_for(batch.n, 0)
+        st = lib().oscar_int2_decode_partials(
+            ctypes.byref(self.st), batch.n, _hp(batch.slots), _hp(batch.lens), _p(batch.d_slots),
+            _p(batch.d_lens), _p(q_rot), _p(ws), ws.numel(), current_stream())
+        check(st, "oscar_int2_decode_partials")
+
+    def decode_merge(self, batch, out=None):
+        """oscar_int2_decode_merge: the merge launch of the same decode step."""
+        if out is None:
+            out = torch.empty((batch.n, self.hq, D), dtype=torch.float32, device=self.device)
+        ws = self.workspace_for(batch.n, 0)
+        st = lib().oscar_int2_decode_merge(
+            ctypes.byref(self.st), batch.n, _hp(batch.slots), _hp(batch.lens), _p(batch.d_slots),
+            _p(batch.d_lens), _p(out), _p(ws), ws.numel(), current_stream())
+        check(st, "oscar_int2_decode_merge")
+        return out
+
     def dequant(self, slot, seq_len, t0, t1):
         """oscar_dequant: decoded (k, v) fp32 [t1 - t0, Hkv, 128], rotated basis."""
         k = torch.empty((max(0, t1 - t0), self.hkv, D), dtype=torch.float32, device=self.device)

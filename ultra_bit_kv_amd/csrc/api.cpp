@@ -294,18 +294,25 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
   return hip_status(launch_place(a, sa, stage_k, stage_v, max_new, sm));
 }
 
-int oscar_int2_decode_attn(const oscar_kv_cache* cache, int32_t n_seqs,
-                           const int32_t* seq_slots_host, const int32_t* seq_lens_host,
-                           const int32_t* seq_slots, const int32_t* seq_lens,
-                           const uint16_t* q_rot, float* out, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and the split plan shared by the decode entry points.  The plan
+// depends only on the configuration, the host lengths and the device, so the
+// split and merge calls of one decode step compute the same plan.
+int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_slots_host,
+                const int32_t* seq_lens_host, const int32_t* seq_slots, const int32_t* seq_lens,
+                const uint16_t* q_rot, float* out, void* workspace, size_t workspace_bytes,
+                void* stream, int phases) {
   if (!cache) return OSCAR_ERR_NULL;
   const oscar_kv_config& c = cache->cfg;
   int st = oscar_check_config(&c);
   if (st != OSCAR_OK) return st;
-  if (!seq_slots_host || !seq_lens_host || !seq_slots || !seq_lens || !q_rot || !out ||
-      !workspace || !cache->pages || !cache->block_table || !cache->win || !cache->r_v)
+  if (!seq_slots_host || !seq_lens_host || !seq_slots || !seq_lens || !workspace ||
+      !cache->pages || !cache->block_table || !cache->win || !cache->r_v)
     return OSCAR_ERR_NULL;
+  if (((phases & kDecodeSplit) && !q_rot) || ((phases & kDecodeMerge) && !out)) return OSCAR_ERR_NULL;
   if (n_seqs < 1 || n_seqs > c.max_seqs) return OSCAR_ERR_ARG;
   const int64_t max_len = oscar_max_seq_len(&c);
   for (int i = 0; i < n_seqs; ++i) {
@@ -349,8 +356,40 @@ int oscar_int2_decode_attn(const oscar_kv_cache* cache, int32_t n_seqs,
   plan.smax = (int)std::max<int64_t>(1, (max_cost + quota - 1) / quota);
   const CacheArgs a = make_args(*cache);
   SeqArgs sa{seq_slots, seq_lens, nullptr, n_seqs};
-  return hip_status(launch_decode(a, sa, plan, q_rot, out, (float*)workspace, (hipStream_t)stream));
+  return hip_status(
+      launch_decode(a, sa, plan, q_rot, out, (float*)workspace, phases, (hipStream_t)stream));
 }
+
+}  // namespace
+
+extern "C" {
+
+int oscar_int2_decode_attn(const oscar_kv_cache* cache, int32_t n_seqs,
+                           const int32_t* seq_slots_host, const int32_t* seq_lens_host,
+                           const int32_t* seq_slots, const int32_t* seq_lens,
+                           const uint16_t* q_rot, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return decode_step(cache, n_seqs, seq_slots_host, seq_lens_host, seq_slots, seq_lens, q_rot, out,
+                     workspace, workspace_bytes, stream, kDecodeSplit | kDecodeMerge);
+}
+
+int oscar_int2_decode_partials(const oscar_kv_cache* cache, int32_t n_seqs,
+                               const int32_t* seq_slots_host, const int32_t* seq_lens_host,
+                               const int32_t* seq_slots, const int32_t* seq_lens,
+                               const uint16_t* q_rot, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return decode_step(cache, n_seqs, seq_slots_host, seq_lens_host, seq_slots, seq_lens, q_rot,
+                     nullptr, workspace, workspace_bytes, stream, kDecodeSplit);
+}
+
+int oscar_int2_decode_merge(const oscar_kv_cache* cache, int32_t n_seqs,
+                            const int32_t* seq_slots_host, const int32_t* seq_lens_host,
+                            const int32_t* seq_slots, const int32_t* seq_lens, float* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_step(cache, n_seqs, seq_slots_host, seq_lens_host, seq_slots, seq_lens, nullptr,
+                     out, workspace, workspace_bytes, stream, kDecodeMerge);
+}
+
 
 int oscar_dequant(const oscar_kv_cache* cache, int32_t seq_slot, int32_t seq_len,
                   int32_t tok_begin, int32_t tok_end, float* k_out, float* v_out, void* stream) {

@@ -535,56 +535,62 @@ __global__ __launch_bounds__(256) void merge_unrotate_kernel(CacheArgs c, SeqArg
 template <int NG, int HP>
 static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                                   const uint16_t* q_rot, float* out, float* partials,
-                                  hipStream_t stream) {
+                                  int phases, hipStream_t stream) {
   const int wh = plan.wh;
-  dim3 grid(plan.smax, (c.hkv / wh) * plan.passes, s.n_seqs);
-  switch (wh) {
-    case 4:
-      hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 4>), grid, dim3(256), 0, stream,
-                         c, s, plan.quota, plan.passes, plan.smax, q_rot, partials);
-      break;
-    case 2:
-      hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 2>), grid, dim3(128), 0, stream,
-                         c, s, plan.quota, plan.passes, plan.smax, q_rot, partials);
-      break;
-    default:
-      hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 1>), grid, dim3(64), 0, stream,
-                         c, s, plan.quota, plan.passes, plan.smax, q_rot, partials);
-      break;
+  if (phases & kDecodeSplit) {
+    dim3 grid(plan.smax, (c.hkv / wh) * plan.passes, s.n_seqs);
+    switch (wh) {
+      case 4:
+        hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 4>), grid, dim3(256), 0, stream,
+                           c, s, plan.quota, plan.passes, plan.smax, q_rot, partials);
+        break;
+      case 2:
+        hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 2>), grid, dim3(128), 0, stream,
+                           c, s, plan.quota, plan.passes, plan.smax, q_rot, partials);
+        break;
+      default:
+        hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 1>), grid, dim3(64), 0, stream,
+                           c, s, plan.quota, plan.passes, plan.smax, q_rot, partials);
+        break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 mgrid(c.hkv * plan.passes, s.n_seqs);
-  hipLaunchKernelGGL((merge_unrotate_kernel<HP>), mgrid, dim3(256), 0, stream, c, s, plan.quota,
-                     plan.passes, plan.smax, partials, out);
-  return hipGetLastError();
+  if (phases & kDecodeMerge) {
+    dim3 mgrid(c.hkv * plan.passes, s.n_seqs);
+    hipLaunchKernelGGL((merge_unrotate_kernel<HP>), mgrid, dim3(256), 0, stream, c, s, plan.quota,
+                       plan.passes, plan.smax, partials, out);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <int NG>
 static hipError_t dispatch_hp(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                               const uint16_t* q_rot, float* out, float* partials,
-                              hipStream_t stream) {
+                              int phases, hipStream_t stream) {
   switch (plan.hp) {
-    case 1: return launch_decode_t<NG, 1>(c, s, plan, q_rot, out, partials, stream);
-    case 2: return launch_decode_t<NG, 2>(c, s, plan, q_rot, out, partials, stream);
-    case 4: return launch_decode_t<NG, 4>(c, s, plan, q_rot, out, partials, stream);
+    case 1: return launch_decode_t<NG, 1>(c, s, plan, q_rot, out, partials, phases, stream);
+    case 2: return launch_decode_t<NG, 2>(c, s, plan, q_rot, out, partials, phases, stream);
+    case 4: return launch_decode_t<NG, 4>(c, s, plan, q_rot, out, partials, phases, stream);
     case 8:
-      if constexpr (NG <= 2) return launch_decode_t<NG, 8>(c, s, plan, q_rot, out, partials, stream);
+      if constexpr (NG <= 2) return launch_decode_t<NG, 8>(c, s, plan, q_rot, out, partials, phases, stream);
       break;
     case 16:
-      if constexpr (NG == 1) return launch_decode_t<NG, 16>(c, s, plan, q_rot, out, partials, stream);
+      if constexpr (NG == 1) return launch_decode_t<NG, 16>(c, s, plan, q_rot, out, partials, phases, stream);
       break;
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
-                         const uint16_t* q_rot, float* out, float* partials, hipStream_t stream) {
+                         const uint16_t* q_rot, float* out, float* partials, int phases,
+                         hipStream_t stream) {
   if (s.n_seqs <= 0) return hipSuccess;
   switch (c.ng) {
-    case 1: return dispatch_hp<1>(c, s, plan, q_rot, out, partials, stream);
-    case 2: return dispatch_hp<2>(c, s, plan, q_rot, out, partials, stream);
-    case 4: return dispatch_hp<4>(c, s, plan, q_rot, out, partials, stream);
+    case 1: return dispatch_hp<1>(c, s, plan, q_rot, out, partials, phases, stream);
+    case 2: return dispatch_hp<2>(c, s, plan, q_rot, out, partials, phases, stream);
+    case 4: return dispatch_hp<4>(c, s, plan, q_rot, out, partials, phases, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -78,7 +78,10 @@ struct DecodePlan {
   int passes;                    // ceil(g / hp)
   int wh;                        // KV heads (waves) per work-group
 };
+constexpr int kDecodeSplit = 1;   // the split kernel: partial records to the workspace
+constexpr int kDecodeMerge = 2;   // the merge / un-rotation kernel: partials to out
 hipError_t launch_decode(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
-                         const uint16_t* q_rot, float* out, float* partials, hipStream_t stream);
+                         const uint16_t* q_rot, float* out, float* partials, int phases,
+                         hipStream_t stream);
 
 }  // namespace oscar
