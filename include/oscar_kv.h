@@ -29,7 +29,8 @@
  *    returned in the original basis: o = o' . R_V^T.
  *  - bf16 and fp16 values travel as uint16_t bit patterns.
  *  - Every pointer argument is a DEVICE pointer unless its name ends in
- *    _host.  The caller owns all memory; the library allocates nothing and
+ *    _host.  Device buffers (cache arrays, rows, workspace, output) must be
+ *    16-byte aligned (OSCAR_ERR_ARG otherwise).  The caller owns all memory; the library allocates nothing and
  *    keeps no state between calls.
  *  - Calls enqueue work on `stream` (a hipStream_t; NULL = default stream)
  *    and return without waiting.  Calls that touch the same cache or the

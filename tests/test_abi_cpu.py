@@ -157,6 +157,13 @@ def test_decode_argument_checks(L):
     assert decode(L, c, [0], [mx]) in (-9, -8, 0)
 
 
+def test_misaligned_pointers_are_rejected(L):
+    c = cfg()
+    bad = ctypes.c_void_p(DUMMY.value + 4)
+    assert decode(L, c, [0], [10], out=bad) == -10
+    assert append(L, c, [0], [0], [5], k=bad) == -10
+
+
 def test_decode_phase_argument_checks(L):
     c = cfg()
     keep = [_i32([0]), _i32([10])]

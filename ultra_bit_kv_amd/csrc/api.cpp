@@ -15,6 +15,17 @@ namespace {
 using namespace oscar;
 
 constexpr size_t kAlign = 256;
+// Config limits: with them every row's decode work fits kMaxSplits splits of
+// kMaxPairsPerSplit units (32768 pairs + 3 * 1281 window blocks < 65536).
+constexpr int kMaxSink = 4096, kMaxKeep = 8192, kMaxFlush = 8192;
+constexpr int kMaxPagesPerSeq = 65536;
+static_assert((kMaxPagesPerSeq / 2) +
+                      kWinCost * (kMaxSink / kPage + (kMaxKeep + kMaxFlush) / kPage + 1) <=
+                  (int64_t)kMaxSplits * kMaxPairsPerSplit,
+              "decode work of the largest row must fit the split limits");
+// Split launch sizing: the work-groups of a launch fill this share of the
+// resident slots, so none waits for a second round.
+constexpr int kFillPercent = 97;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // S_quant of the flush rule (WUSH-KV notes, "method step details").
@@ -55,30 +66,37 @@ DecodePlan head_passes(const oscar_kv_config& c) {
   return p;
 }
 
-// A decode work-group stages the page ids of its split in LDS: at most this
-// many page pairs per split.
-constexpr int kMaxPairsPerSplit = 256;
-
-int min_splits(const oscar_kv_config& c) {
-  const int pairs = (c.max_pages_per_seq + 1) / 2;
-  return std::max(1, (pairs + kMaxPairsPerSplit - 1) / kMaxPairsPerSplit);
+// Largest decode work (page pairs, a window block = kWinCost) of any row.
+int64_t max_row_cost(const oscar_kv_config& c) {
+  const int64_t pairs = ((int64_t)c.max_pages_per_seq + 1) / 2;
+  const int64_t wu = (c.s_sink + kPage - 1) / kPage + ring_cap(c) / kPage;
+  return pairs + kWinCost * wu;
 }
 
-// Most splits per sequence the workspace is sized for: about 16K partial
-// records in total, at most 256 per (sequence, KV head, pass), and never
-// fewer than the LDS page-list limit requires.
+// Fewest splits that keep every split within kMaxPairsPerSplit units (the
+// page-id list a work-group stages in LDS).
+int min_splits(const oscar_kv_config& c) {
+  return (int)std::max<int64_t>(1, (max_row_cost(c) + kMaxPairsPerSplit - 1) / kMaxPairsPerSplit);
+}
+
+// Most splits per (sequence, KV head, pass) the workspace is sized for:
+// about 16K partial records per launch, at most kMaxSplits, and never fewer
+// than min_splits (the config limits keep min_splits <= kMaxSplits).
 int max_splits(const oscar_kv_config& c, int n_seqs) {
   const DecodePlan p = head_passes(c);
-  const long long rows = (long long)std::max(1, n_seqs) * c.num_kv_heads * p.passes;
+  const int ns = std::min(std::max(1, n_seqs), kMaxScanSeqs);
+  const long long rows = (long long)ns * c.num_kv_heads * p.passes;
   long long s = (16384 + rows - 1) / rows;
-  s = std::max(1LL, std::min(256LL, s));
+  s = std::max(1LL, std::min((long long)kMaxSplits, s));
   return (int)std::max<long long>(s, min_splits(c));
 }
 
+// Split partial records of one decode launch (at most kMaxScanSeqs sequences).
 size_t partials_bytes(const oscar_kv_config& c, int n_seqs) {
   const DecodePlan p = head_passes(c);
   const size_t rec = (size_t)p.hp * kD + 2 * p.hp;
-  return align_up((size_t)n_seqs * c.num_kv_heads * p.passes * max_splits(c, n_seqs) * rec *
+  const int ns = std::min(std::max(1, n_seqs), kMaxScanSeqs);
+  return align_up((size_t)ns * c.num_kv_heads * p.passes * max_splits(c, ns) * rec *
                   sizeof(float));
 }
 
@@ -131,16 +149,34 @@ int check_device(int* cus = nullptr) {
   return known[dev] == 1 ? OSCAR_OK : OSCAR_ERR_DEVICE;
 }
 
-// Decode work of a row of len tokens in page pairs (a window block = 3
-// pairs); the kernels compute the same numbers from the device lengths.
-constexpr int kWinCost = 3;
+// Decode work of a row of len tokens (page pairs, a window block = kWinCost);
+// the kernels compute the same numbers from the device lengths with the same
+// function.
 int64_t decode_cost(int64_t len, const oscar_kv_config& c) {
-  const int64_t pairs = (int2_pages(len, c) + 1) / 2;
-  const int64_t sq = s_quant(len, c);
-  const int64_t nsink = std::min<int64_t>(len, c.s_sink);
-  const int64_t ring_lo = std::max<int64_t>(sq, c.s_sink);
-  const int64_t wu = (nsink + kPage - 1) / kPage + (len > ring_lo ? ring_cap(c) / kPage : 0);
-  return pairs + kWinCost * wu;
+  const DecodeWork w = decode_work((int)len, c.s_sink, c.s_keep, c.s_flush, ring_cap(c));
+  return w.n_pairs + (int64_t)kWinCost * w.n_wu;
+}
+
+// Resident split work-groups per compute unit, once per (device, kernel shape).
+int decode_slots_per_cu(const CacheArgs& a, const DecodePlan& plan) {
+  static std::mutex mu;
+  static std::vector<std::pair<long long, int>> memo;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const long long key = ((((long long)dev * 8 + a.ng) * 32 + plan.hp) * 8 + plan.wh);
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& m : memo)
+    if (m.first == key) return m.second;
+  const int n = decode_wgs_per_cu(a, plan);
+  memo.emplace_back(key, n);
+  return n;
+}
+
+// Kernels read rows and page blocks with 16-byte vector loads.
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+bool cache_aligned(const oscar_kv_cache& k) {
+  return aligned16(k.pages) && aligned16(k.win) && aligned16(k.r_k) && aligned16(k.r_v) &&
+         aligned16(k.block_table);
 }
 
 thread_local char g_last_hip[160] = "";
@@ -168,9 +204,9 @@ int oscar_check_config(const oscar_kv_config* c) {
     if (!(a >= 0.5f && a <= 1.0f) || !(b >= 0.5f && b <= 1.0f)) return OSCAR_ERR_CLIP;
   }
   if (c->s_sink < 0 || c->s_keep < 0 || c->s_flush < 1) return OSCAR_ERR_WINDOW;
-  if (c->s_sink > (1 << 20) || c->s_keep > (1 << 20) || c->s_flush > (1 << 20))
-    return OSCAR_ERR_WINDOW;
+  if (c->s_sink > kMaxSink || c->s_keep > kMaxKeep || c->s_flush > kMaxFlush) return OSCAR_ERR_WINDOW;
   if (c->max_seqs < 1 || c->max_pages_per_seq < 0 || c->num_pages < 0) return OSCAR_ERR_CAPACITY;
+  if (c->max_pages_per_seq > kMaxPagesPerSeq) return OSCAR_ERR_CAPACITY;
   return OSCAR_OK;
 }
 
@@ -240,11 +276,15 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
       !cache->r_k || !cache->r_v)
     return OSCAR_ERR_NULL;
   if (q_rot && !q) return OSCAR_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(q_rot) || !aligned16(k_rot) ||
+      !aligned16(v_rot) || !cache_aligned(*cache) || !aligned16(workspace))
+    return OSCAR_ERR_ARG;
   if (n_seqs < 1 || n_seqs > c.max_seqs) return OSCAR_ERR_ARG;
   if (cu_new_host[0] != 0) return OSCAR_ERR_ARG;
   const int64_t max_len = oscar_max_seq_len(&c);
   std::vector<char> seen(c.max_seqs, 0);
-  int max_q = 0, max_new = 0;
+  int64_t total_q = 0;
+  int max_new = 0;
   for (int i = 0; i < n_seqs; ++i) {
     const int slot = seq_slots_host[i];
     if (slot < 0 || slot >= c.max_seqs) return OSCAR_ERR_CAPACITY;
@@ -256,11 +296,11 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
     if (lb + n_new > max_len) return OSCAR_ERR_CAPACITY;
     if (int2_pages(lb + n_new, c) > c.max_pages_per_seq) return OSCAR_ERR_CAPACITY;
     if (int2_pages(lb + n_new, c) > 0 && c.num_pages < 1) return OSCAR_ERR_CAPACITY;
-    max_q = std::max<int>(max_q, (int)(s_quant(lb + n_new, c) - s_quant(lb, c)));
+    total_q += s_quant(lb + n_new, c) - s_quant(lb, c);
     max_new = std::max<int>(max_new, (int)n_new);
   }
   const int64_t n_tok = cu_new_host[n_seqs];
-  if (n_tok > (int64_t)1 << 30) return OSCAR_ERR_ARG;
+  if (n_tok > (int64_t)1 << 30 || total_q > (int64_t)1 << 30) return OSCAR_ERR_ARG;
   const size_t need = staging_bytes(c, n_tok);
   if (workspace_bytes < need) return OSCAR_ERR_WORKSPACE;
   if ((st = check_device()) != OSCAR_OK) return st;
@@ -288,7 +328,7 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
                                    c.num_q_heads / c.num_kv_heads};
   if ((st = hip_status(launch_rotate(jobs, (int)n_tok, sm))) != OSCAR_OK) return st;
   // 2. quantize every position that crosses S_quant (reads the ring first)
-  if ((st = hip_status(launch_quantize(a, clip, sa, stage_k, stage_v, max_q, sm))) != OSCAR_OK)
+  if ((st = hip_status(launch_quantize(a, clip, sa, stage_k, stage_v, (int)total_q, sm))) != OSCAR_OK)
     return st;
   // 3. new rows that stay BF16 go to the sink / ring
   return hip_status(launch_place(a, sa, stage_k, stage_v, max_new, sm));
@@ -313,6 +353,8 @@ int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_
       !cache->pages || !cache->block_table || !cache->win || !cache->r_v)
     return OSCAR_ERR_NULL;
   if (((phases & kDecodeSplit) && !q_rot) || ((phases & kDecodeMerge) && !out)) return OSCAR_ERR_NULL;
+  if (!aligned16(q_rot) || !aligned16(out) || !cache_aligned(*cache) || !aligned16(workspace))
+    return OSCAR_ERR_ARG;
   if (n_seqs < 1 || n_seqs > c.max_seqs) return OSCAR_ERR_ARG;
   const int64_t max_len = oscar_max_seq_len(&c);
   for (int i = 0; i < n_seqs; ++i) {
@@ -326,38 +368,54 @@ int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_
   if (workspace_bytes < partials_bytes(c, n_seqs)) return OSCAR_ERR_WORKSPACE;
   int cus = 256;
   if ((st = check_device(&cus)) != OSCAR_OK) return st;
-  // Context splits: a fixed work quota per work-group.  Choose the smallest
-  // quota whose work-groups all fit in one round of the device (12 waves per
-  // compute unit at this kernel's register use), so no work-group waits for
-  // a second round; long sequences get more splits.
+  const CacheArgs a = make_args(*cache);
   DecodePlan plan = head_passes(c);
   const int64_t rows = (int64_t)(c.num_kv_heads / plan.wh) * plan.passes;
-  const int64_t slots = (int64_t)cus * (12 / plan.wh);
-  std::vector<int64_t> cost(n_seqs);
-  int64_t total = 0, max_cost = 0;
-  for (int i = 0; i < n_seqs; ++i) {
-    cost[i] = decode_cost(seq_lens_host[i], c);
-    total += cost[i];
-    max_cost = std::max(max_cost, cost[i]);
-  }
-  const int cap = max_splits(c, n_seqs);
-  int64_t quota = std::max<int64_t>(2, (total * rows + slots - 1) / slots);
-  quota = std::max<int64_t>(quota, (max_cost + cap - 1) / cap);
-  for (;; quota += std::max<int64_t>(1, quota / 16)) {
-    if (quota >= kMaxPairsPerSplit) {
-      quota = kMaxPairsPerSplit;
-      break;
+  const int64_t slots =
+      std::max<int64_t>(1, (int64_t)cus * decode_slots_per_cu(a, plan) * kFillPercent / 100);
+  // Launches of at most kMaxScanSeqs sequences, in stream order.
+  for (int s0 = 0; s0 < n_seqs; s0 += kMaxScanSeqs) {
+    const int ns = std::min(kMaxScanSeqs, n_seqs - s0);
+    // Context splits: a work quota per split.  The smallest quota whose work
+    // items (one work-group each) all fit in one round of resident
+    // work-groups, so none waits for a second round; long sequences get
+    // more splits.  The quota never leaves the split limits.
+    std::vector<int64_t> cost(ns);
+    int64_t total = 0, max_cost = 0;
+    for (int i = 0; i < ns; ++i) {
+      cost[i] = decode_cost(seq_lens_host[s0 + i], c);
+      total += cost[i];
+      max_cost = std::max(max_cost, cost[i]);
     }
-    int64_t wgs = 0;
-    for (int i = 0; i < n_seqs; ++i) wgs += (cost[i] + quota - 1) / quota;
-    if (wgs * rows <= slots) break;
+    const int cap = max_splits(c, ns);
+    auto items_of = [&](int64_t q) {
+      int64_t n = 0;
+      for (int i = 0; i < ns; ++i) n += std::max<int64_t>(1, (cost[i] + q - 1) / q);
+      return n * rows;
+    };
+    int64_t quota = std::max<int64_t>(2, (total * rows + slots - 1) / slots);
+    quota = std::max<int64_t>(quota, (max_cost + cap - 1) / cap);
+    quota = std::min<int64_t>(quota, kMaxPairsPerSplit);
+    if (items_of(quota) > slots) {   // smallest quota in (quota, limit] that fits (items fall as quota grows)
+      int64_t lo = quota, hi = kMaxPairsPerSplit;
+      while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) / 2;
+        (items_of(mid) > slots ? lo : hi) = mid;
+      }
+      quota = hi;
+    }
+    int64_t smax = 1;
+    for (int i = 0; i < ns; ++i) smax = std::max<int64_t>(smax, (cost[i] + quota - 1) / quota);
+    plan.quota = (int)quota;
+    plan.smax = (int)smax;
+    plan.grid = (int)items_of(quota);
+    const SeqArgs sa{seq_slots + s0, seq_lens + s0, nullptr, ns};
+    const size_t qo = (size_t)s0 * c.num_q_heads * kD;
+    st = hip_status(launch_decode(a, sa, plan, q_rot ? q_rot + qo : nullptr, out ? out + qo : nullptr,
+                                  (float*)workspace, phases, (hipStream_t)stream));
+    if (st != OSCAR_OK) return st;
   }
-  plan.quota = (int)quota;
-  plan.smax = (int)std::max<int64_t>(1, (max_cost + quota - 1) / quota);
-  const CacheArgs a = make_args(*cache);
-  SeqArgs sa{seq_slots, seq_lens, nullptr, n_seqs};
-  return hip_status(
-      launch_decode(a, sa, plan, q_rot, out, (float*)workspace, phases, (hipStream_t)stream));
+  return OSCAR_OK;
 }
 
 }  // namespace

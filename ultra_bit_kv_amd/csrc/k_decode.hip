@@ -129,21 +129,26 @@ __device__ __forceinline__ void softmax_step(const float (&x)[N], float scale, f
   }
 }
 
-constexpr int kMaxWgPages = 512;   // page ids staged per work-group (<= 256 pairs per split)
+constexpr int kMaxWgPages = 2 * kMaxPairsPerSplit;   // page ids staged per work-group
 constexpr int kPrefetch = 2;       // page pairs in flight per wave ahead of the one processed
-constexpr int kWinCost = 3;        // a BF16 window block (8 KB) costs about three page pairs
 
-// Splits of one sequence's context: the work quota per split (INT2 page
-// pairs, a BF16 window block counting as kWinCost pairs) is a launch
-// constant, so the number of splits follows the sequence length.
-__device__ __forceinline__ int splits_of(int n_pairs, int n_wu, int quota) {
-  const int cost = n_pairs + kWinCost * n_wu;
-  return cost > 0 ? (cost + quota - 1) / quota : 1;
+// Issue priority of the calling wave from its remaining share of the work:
+// waves of one SIMD otherwise issue oldest-first, so the first work-groups
+// on a compute unit run ahead and the last ones finish alone.
+__device__ __forceinline__ void set_priority(int remaining, int total) {
+  const int p = (4 * remaining - 1) / total;   // 0..3
+  if (p >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (p == 2) __builtin_amdgcn_s_setprio(2);
+  else if (p == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
 }
 
-// Work-group = (sequence, split, group of WH adjacent KV heads); wave w owns
-// KV head WH * group + w.  All waves walk the same pages, so each page is
-// fetched as one contiguous run of WH page-head blocks.
+// Work-group = one work item (sequence, context split, group of WH adjacent
+// KV heads, query-head pass); items are numbered sequence-major, then split,
+// then head group, and the launch has exactly one work-group per item.  A
+// work-group finds its item from a prefix sum over the sequences' item
+// counts.  Wave w owns KV head WH * group + w; all waves walk the same pages,
+// so each page is fetched as one contiguous run of WH page-head blocks.
 template <int NG, int HP, int PF, int WH>
 __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqArgs s, int quota,
                                                               int passes, int smax,
@@ -151,18 +156,60 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
                                                               float* __restrict__ partials) {
   constexpr int G = kD / NG;
   constexpr int PW = HP * kD + 2 * HP;   // floats per partial record
+  constexpr int NT = 64 * WH;
   __shared__ __attribute__((aligned(16))) uint16_t s_q[WH][HP][kD];
   __shared__ float s_qsum[WH][HP * NG];
   __shared__ int s_pages[kMaxWgPages];
+  __shared__ int s_wsum[WH];
+  __shared__ int s_item[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int split = blockIdx.x;
-  const int hgrp = blockIdx.y / passes, pass = blockIdx.y % passes;
-  const int h = hgrp * WH + wave;
-  const int i = blockIdx.z;
   const int r16 = lane & 15, qd = lane >> 4;
+  const int rows = (c.hkv / WH) * passes;
+
+  // ---- the item of this work-group: sequence i with prefix(i) <= item < prefix(i + 1)
+  {
+    auto seq_items = [&](int k) {
+      const int sl = s.slots[k];
+      const int ln = s.lens[k];
+      const bool ok = sl >= 0 && sl < c.max_seqs && ln >= 1;
+      const DecodeWork wk = decode_work(ok ? ln : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap);
+      return decode_splits(wk, quota, smax) * rows;
+    };
+    const int n = s.n_seqs, per = (n + NT - 1) / NT;
+    const int k0 = min(tid * per, n), k1 = min(k0 + per, n);
+    int run = 0;
+    for (int k = k0; k < k1; ++k) run += seq_items(k);
+    int incl = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    if (tid == 0) s_item[0] = -1;
+    __syncthreads();
+    int off = incl - run;
+    for (int w2 = 0; w2 < wave; ++w2) off += s_wsum[w2];
+    const int item = blockIdx.x;
+    for (int k = k0; k < k1; ++k) {
+      const int q = seq_items(k);
+      if (item >= off && item < off + q) {   // exactly one (k, thread) matches
+        s_item[0] = k;
+        s_item[1] = item - off;
+      }
+      off += q;
+    }
+    __syncthreads();
+  }
+  if (s_item[0] < 0) return;   // uniform: the device lengths give fewer items than the grid
+  const int i = __builtin_amdgcn_readfirstlane(s_item[0]);
+  const int local = __builtin_amdgcn_readfirstlane(s_item[1]);
+  const int split = local / rows, row = local % rows;
+  const int hgrp = row / passes, pass = row % passes;
+  const int h = hgrp * WH + wave;
 
   const int slot = s.slots[i];
   int len = s.lens[i];
@@ -184,12 +231,14 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int b0 = (ring_lo - c.s_sink) % c.ring_cap;
   const int rb_n = cnt > 0 ? c.ring_cap / kPage : 0;
   const int n_wu = sb_n + rb_n;
-  const int n_split = min(splits_of(n_pairs, n_wu, quota), smax);
-  if (split >= n_split) return;                                   // uniform for the group
-  const int pb = (int)((long long)split * n_pairs / n_split);
-  const int pe = (int)((long long)(split + 1) * n_pairs / n_split);
-  const int wb = (int)((long long)split * n_wu / n_split);
-  const int we = (int)((long long)(split + 1) * n_wu / n_split);
+  const int n_split = decode_splits(DecodeWork{n_pairs, n_wu}, quota, smax);
+  // (products stay below 2^31 within the config limits)
+  const int pb = (int)((unsigned)(split * n_pairs) / (unsigned)n_split);
+  const int pe = (int)((unsigned)((split + 1) * n_pairs) / (unsigned)n_split);
+  const int wb = (int)((unsigned)(split * n_wu) / (unsigned)n_split);
+  const int we = (int)((unsigned)((split + 1) * n_wu) / (unsigned)n_split);
+  const int total_units = max(1, (pe - pb) + kWinCost * (we - wb));
+  set_priority(total_units, total_units);
   const uint16_t* wbase = c.win + ((size_t)(row_ok ? slot : 0) * c.hkv + h) * c.win_blocks *
                                       (2 * kPage * kD);
   struct Win {
@@ -288,7 +337,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     int tok;      // INT2 token index of slot 0 of page A
     bool oka, okb;
   };
-  const int np = pe - pb;                                         // pairs of this split
+  const int np = min(pe - pb, kMaxPairsPerSplit);                 // pairs of this split
   const int koff = (r16 * 8 + 2 * qd) * 4;
   const int poff = 1024 + 4 * (16 * gsel + 4 * qd);
   const int vpoff = poff + 64 * NG;
@@ -412,6 +461,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   // ---- INT2 page pairs: accumulate in code units (code * 4^(j%4) * 2^-24)
   if (np > 0) {
     for (int k = 0; k < np; k += PF) {
+      set_priority(total_units - k, total_units);
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
         if (k + j < np) process_pair(ring[j]);
@@ -427,6 +477,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     Win wa, wn;
     load_win(wb, wa);
     for (int u = wb; u < we; ++u) {
+      set_priority(kWinCost * (we - u), total_units);
       if (u + 1 < we) load_win(u + 1, wn);
       if (__any(win_slot_ok(u, r16))) process_win(wa);
       wa = wn;
@@ -453,18 +504,12 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   }
 }
 
-// Number of window units (sink blocks + ring blocks visited) of a row of len tokens.
-__device__ __forceinline__ int window_units(const CacheArgs& c, int len, int sq) {
-  const int nsink = min(len, c.s_sink);
-  const int ring_lo = max(sq, c.s_sink);
-  return (nsink + kPage - 1) / kPage + (len > ring_lo ? c.ring_cap / kPage : 0);
-}
-
 // Log-sum-exp merge of the split partials of one (sequence, KV head, pass),
 // then o = o' . R_V^T with R_V staged in LDS (rows padded to 129 floats so the
-// row-per-thread reads of a wave fall in distinct banks).  The per-split
-// maxima and sums are gathered first (one round of loads), then each output
-// channel sums its splits with batched loads.
+// row-per-thread reads of a wave fall in distinct banks).  Every global load
+// of the work-group (R_V, the split maxima and sums, the first kChunk split
+// outputs of each channel) is issued before the first wait, so the merge
+// costs about one memory round trip.
 template <int HP>
 __global__ __launch_bounds__(256) void merge_unrotate_kernel(CacheArgs c, SeqArgs s, int quota,
                                                              int passes, int smax,
@@ -472,10 +517,15 @@ __global__ __launch_bounds__(256) void merge_unrotate_kernel(CacheArgs c, SeqArg
                                                              float* __restrict__ out) {
   constexpr int PW = HP * kD + 2 * HP;
   constexpr int kMaxS = 256;
+  constexpr int kChunk = 8;                      // split outputs per channel per load round
+  constexpr int kOut = (HP * kD + 255) / 256;    // output channels per thread
   __shared__ float rv[kD][kD + 1];
   __shared__ float fin[HP][kD];
-  __shared__ float s_w[kMaxS][HP];
-  __shared__ float s_l[HP];
+  __shared__ float s_M[HP], s_L[HP];
+  // per-split maxima and sums, [smax][HP] each, in dynamic LDS (2 * smax * HP floats)
+  extern __shared__ float s_dyn[];
+  float (*s_m)[HP] = (float (*)[HP])s_dyn;
+  float (*s_l)[HP] = (float (*)[HP])(s_dyn + (size_t)smax * HP);
   const int tid = threadIdx.x;
   const int h = blockIdx.x / passes, pass = blockIdx.x % passes;
   const int i = blockIdx.y;
@@ -484,42 +534,74 @@ __global__ __launch_bounds__(256) void merge_unrotate_kernel(CacheArgs c, SeqArg
   int len = s.lens[i];
   const bool row_ok = slot >= 0 && slot < c.max_seqs && len >= 1;
   if (!row_ok) len = 0;
-  const int sq = s_quant_of(len, c.s_sink, c.s_keep, c.s_flush);
-  const int nq = sq > c.s_sink ? sq - c.s_sink : 0;
-  const int n_pairs = ((nq + kPage - 1) / kPage + 1) / 2;
-  const int n_split = min(min(splits_of(n_pairs, window_units(c, len, sq), quota), smax), kMaxS);
+  const DecodeWork wk = decode_work(len, c.s_sink, c.s_keep, c.s_flush, c.ring_cap);
+  const int n_split = min(decode_splits(wk, quota, smax), kMaxS);
   const float* recs = partials + (((size_t)i * c.hkv + h) * passes + pass) * smax * PW;
 
+  // ---- issue: R_V, per-split (max, sum), first chunk of split outputs
   const float4* rg = (const float4*)(c.r_v + (size_t)h * kD * kD);
-  for (int t = tid; t < kD * kD / 4; t += 256) {
-    const float4 v = rg[t];
-    const int row = (4 * t) / kD, col = (4 * t) % kD;
-    rv[row][col] = v.x;
-    rv[row][col + 1] = v.y;
-    rv[row][col + 2] = v.z;
-    rv[row][col + 3] = v.w;
+  float4 rvv[kD * kD / 4 / 256];
+#pragma unroll
+  for (int t = 0; t < kD * kD / 4 / 256; ++t) rvv[t] = rg[tid + 256 * t];
+  for (int t = tid; t < n_split * nh; t += 256) {
+    const int sp = t / nh, hh = t % nh;
+    s_m[sp][hh] = recs[(size_t)sp * PW + hh];
+    s_l[sp][hh] = recs[(size_t)sp * PW + HP + hh];
   }
-  for (int t = tid; t < n_split * nh; t += 256) s_w[t / nh][t % nh] = recs[(size_t)(t / nh) * PW + t % nh];
-  __syncthreads();
-  if (tid < nh) {   // log-sum-exp weights of the splits of head tid
-    float M = kNegInf;
-    for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, s_w[sp][tid]);
-    float L = 0.0f;
-    for (int sp = 0; sp < n_split; ++sp) {
-      const float wt = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s_w[sp][tid] - M);
-      L += wt * recs[(size_t)sp * PW + HP + tid];
-      s_w[sp][tid] = wt;
-    }
-    s_l[tid] = L;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < nh * kD; idx += 256) {
+  float ov[kOut][kChunk];
+#pragma unroll
+  for (int k = 0; k < kOut; ++k) {
+    const int idx = tid + 256 * k;
     const int hh = idx / kD, ch = idx % kD;
     const float* o = recs + 2 * HP + hh * kD + ch;
-    float O = 0.0f;
-#pragma unroll 8
-    for (int sp = 0; sp < n_split; ++sp) O = __builtin_fmaf(s_w[sp][hh], o[(size_t)sp * PW], O);
-    fin[hh][ch] = O / s_l[hh];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j)
+      ov[k][j] = (hh < nh && j < n_split) ? o[(size_t)j * PW] : 0.0f;
+  }
+#pragma unroll
+  for (int t = 0; t < kD * kD / 4 / 256; ++t) {
+    const int e = 4 * (tid + 256 * t);
+    const int row = e / kD, col = e % kD;
+    rv[row][col] = rvv[t].x;
+    rv[row][col + 1] = rvv[t].y;
+    rv[row][col + 2] = rvv[t].z;
+    rv[row][col + 3] = rvv[t].w;
+  }
+  __syncthreads();
+  if (tid < nh) {   // log-sum-exp of head tid over its splits
+    float M = kNegInf;
+    for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, s_m[sp][tid]);
+    float L = 0.0f;
+    for (int sp = 0; sp < n_split; ++sp)
+      L += (M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s_m[sp][tid] - M)) * s_l[sp][tid];
+    s_M[tid] = M;
+    s_L[tid] = L;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kOut; ++k) {
+    const int idx = tid + 256 * k;
+    const int hh = idx / kD, ch = idx % kD;
+    if (hh < nh) {
+      const float M = s_M[hh];
+      auto weight = [&](int sp) {
+        return M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s_m[sp][hh] - M);
+      };
+      float O = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j)
+        if (j < n_split) O = __builtin_fmaf(weight(j), ov[k][j], O);
+      const float* o = recs + 2 * HP + hh * kD + ch;
+      for (int sp0 = kChunk; sp0 < n_split; sp0 += kChunk) {   // long contexts: more rounds
+        float v[kChunk];
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) v[j] = sp0 + j < n_split ? o[(size_t)(sp0 + j) * PW] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j)
+          if (sp0 + j < n_split) O = __builtin_fmaf(weight(sp0 + j), v[j], O);
+      }
+      fin[hh][ch] = O / s_L[hh];
+    }
   }
   __syncthreads();
   if (!row_ok) return;
@@ -538,7 +620,7 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
                                   int phases, hipStream_t stream) {
   const int wh = plan.wh;
   if (phases & kDecodeSplit) {
-    dim3 grid(plan.smax, (c.hkv / wh) * plan.passes, s.n_seqs);
+    const dim3 grid(plan.grid);
     switch (wh) {
       case 4:
         hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 4>), grid, dim3(256), 0, stream,
@@ -558,11 +640,55 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
   }
   if (phases & kDecodeMerge) {
     dim3 mgrid(c.hkv * plan.passes, s.n_seqs);
-    hipLaunchKernelGGL((merge_unrotate_kernel<HP>), mgrid, dim3(256), 0, stream, c, s, plan.quota,
-                       plan.passes, plan.smax, partials, out);
+    const size_t dyn = 2 * sizeof(float) * (size_t)(plan.smax < 256 ? plan.smax : 256) * HP;
+    hipLaunchKernelGGL((merge_unrotate_kernel<HP>), mgrid, dim3(256), dyn, stream, c, s,
+                       plan.quota, plan.passes, plan.smax, partials, out);
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+template <int NG, int HP>
+static int wgs_per_cu_t(int wh) {
+  int nb = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (wh) {
+    case 4:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, int2_decode_kernel<NG, HP, kPrefetch, 4>, 256, 0);
+      break;
+    case 2:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, int2_decode_kernel<NG, HP, kPrefetch, 2>, 128, 0);
+      break;
+    default:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, int2_decode_kernel<NG, HP, kPrefetch, 1>, 64, 0);
+      break;
+  }
+  return e == hipSuccess && nb > 0 ? nb : 1;
+}
+
+template <int NG>
+static int wgs_per_cu_ng(const DecodePlan& plan) {
+  switch (plan.hp) {
+    case 1: return wgs_per_cu_t<NG, 1>(plan.wh);
+    case 2: return wgs_per_cu_t<NG, 2>(plan.wh);
+    case 4: return wgs_per_cu_t<NG, 4>(plan.wh);
+    case 8:
+      if constexpr (NG <= 2) return wgs_per_cu_t<NG, 8>(plan.wh);
+      break;
+    case 16:
+      if constexpr (NG == 1) return wgs_per_cu_t<NG, 16>(plan.wh);
+      break;
+  }
+  return 1;
+}
+
+int decode_wgs_per_cu(const CacheArgs& c, const DecodePlan& plan) {
+  switch (c.ng) {
+    case 1: return wgs_per_cu_ng<1>(plan);
+    case 2: return wgs_per_cu_ng<2>(plan);
+    case 4: return wgs_per_cu_ng<4>(plan);
+  }
+  return 1;
 }
 
 template <int NG>
@@ -586,7 +712,7 @@ static hipError_t dispatch_hp(const CacheArgs& c, const SeqArgs& s, const Decode
 hipError_t launch_decode(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                          const uint16_t* q_rot, float* out, float* partials, int phases,
                          hipStream_t stream) {
-  if (s.n_seqs <= 0) return hipSuccess;
+  if (s.n_seqs <= 0 || plan.grid <= 0) return hipSuccess;
   switch (c.ng) {
     case 1: return dispatch_hp<1>(c, s, plan, q_rot, out, partials, phases, stream);
     case 2: return dispatch_hp<2>(c, s, plan, q_rot, out, partials, phases, stream);

@@ -9,8 +9,10 @@
 // S_quant; the OSCAR-style quantizer clips at the kappa-quantile.  OScaR
 // notes, "integer quantization basics": Q = clamp(round(x / Delta + z), 0, 3).
 //
-// One work-group quantizes one (sequence, position, KV head): wave 0 the key
-// row, wave 1 the value row.  The order statistics a quantile needs are found
+// One work-group quantizes one (quantized position, KV head): wave 0 the key
+// row, wave 1 the value row.  The positions of all sequences are numbered
+// consecutively (sequence-major); a work-group finds its sequence from a
+// prefix sum over the sequences' counts S_quant(after) - S_quant(before).  The order statistics a quantile needs are found
 // by ranking (ties broken by channel index, so every rank is held by exactly
 // one element); the quantile, step and zero point are computed in fp64 with
 // contraction disabled, rounded once to fp16, and codes are decided against
@@ -35,22 +37,53 @@ __global__ __launch_bounds__(128) void quantize_kernel(CacheArgs c, ClipArgs cli
   __shared__ float vals[2][kD];
   __shared__ float sel[2][4][4];
   __shared__ uint32_t nib[2][64];
+  __shared__ int s_run[2];
+  __shared__ int s_seq, s_before;
 
-  const int i = blockIdx.z, h = blockIdx.y;
+  const int h = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;   // w: 0 = K, 1 = V
+  const int item = blockIdx.x;
+  // ---- sequence of this position: prefix sum of the per-sequence counts
+  auto count_of = [&](int k) {
+    const int lb = s.lens[k];
+    const int nn = s.cu_new[k + 1] - s.cu_new[k];
+    if (s.slots[k] < 0 || s.slots[k] >= c.max_seqs || lb < 0 || nn < 0) return 0;
+    return s_quant_of(lb + nn, c.s_sink, c.s_keep, c.s_flush) -
+           s_quant_of(lb, c.s_sink, c.s_keep, c.s_flush);
+  };
+  {
+    const int n = s.n_seqs, per = (n + 127) / 128;
+    const int k0 = min((int)threadIdx.x * per, n), k1 = min(k0 + per, n);
+    int run = 0;
+    for (int k = k0; k < k1; ++k) run += count_of(k);
+    int incl = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 63) s_run[w] = incl;
+    if (threadIdx.x == 0) s_seq = -1;
+    __syncthreads();
+    int off = (w == 1 ? s_run[0] : 0) + incl - run;
+    for (int k = k0; k < k1; ++k) {
+      const int q = count_of(k);
+      if (item >= off && item < off + q) {   // exactly one (k, thread) matches
+        s_seq = k;
+        s_before = off;
+      }
+      off += q;
+    }
+    __syncthreads();
+  }
+  const int i = s_seq;
+  if (i < 0) return;   // uniform: the device counts do not reach this item
   const int slot = s.slots[i];
   const int lb = s.lens[i];
-  const int n_new = s.cu_new[i + 1] - s.cu_new[i];
-  if (slot < 0 || slot >= c.max_seqs || lb < 0 || n_new < 0) return;
-  const int la = lb + n_new;
   const int sqb = s_quant_of(lb, c.s_sink, c.s_keep, c.s_flush);
-  const int sqa = s_quant_of(la, c.s_sink, c.s_keep, c.s_flush);
-  const int p = sqb + blockIdx.x;
-  if (p >= sqa) return;
+  const int p = sqb + (item - s_before);
   const int m = (p - c.s_sink) / kPage, t = (p - c.s_sink) % kPage;
-  if (m >= c.max_pages) return;
-  const int phys = c.block_table[(size_t)slot * c.max_pages + m];
-  if (phys < 0 || phys >= c.num_pages) return;
+  const int phys = m < c.max_pages ? c.block_table[(size_t)slot * c.max_pages + m] : -1;
 
   // ---- source row: old rows from the recent ring, new rows from staging
   uint32_t pair;
@@ -71,6 +104,7 @@ __global__ __launch_bounds__(128) void quantize_kernel(CacheArgs c, ClipArgs cli
     const uint16_t* src = (w == 0 ? stage_k : stage_v) + (tok * c.hkv + h) * kD;
     pair = *(const uint32_t*)(src + 2 * lane);
   }
+  if (phys < 0 || phys >= c.num_pages) return;   // uniform: unmapped page, nothing to store
   const float x0 = bf16_bits_to_f32(pair & 0xFFFFu);
   const float x1 = bf16_bits_to_f32(pair >> 16);
   vals[w][2 * lane] = x0;
@@ -143,10 +177,10 @@ __global__ __launch_bounds__(128) void quantize_kernel(CacheArgs c, ClipArgs cli
 }
 
 hipError_t launch_quantize(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
-                           const uint16_t* stage_k, const uint16_t* stage_v, int max_q,
+                           const uint16_t* stage_k, const uint16_t* stage_v, int total_q,
                            hipStream_t stream) {
-  if (max_q <= 0 || s.n_seqs <= 0) return hipSuccess;
-  dim3 grid(max_q, c.hkv, s.n_seqs);
+  if (total_q <= 0 || s.n_seqs <= 0) return hipSuccess;
+  dim3 grid(total_q, c.hkv);
   hipLaunchKernelGGL(quantize_kernel, grid, dim3(128), 0, stream, c, clip, s, stage_k, stage_v);
   return hipGetLastError();
 }

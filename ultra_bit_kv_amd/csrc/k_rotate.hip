@@ -22,21 +22,37 @@ __global__ __launch_bounds__(256) void rotate_kernel(RotateJobs jobs, int n_tok)
   __shared__ double xs[TT][kD + 1];
   __shared__ float rs[kD][kD];
   const int tid = threadIdx.x;
-  int y = blockIdx.y, jb = 0;
-  while (jb < jobs.n - 1 && y >= jobs.job[jb].heads) {
-    y -= jobs.job[jb].heads;
-    ++jb;
+  // grid.y enumerates (job, head); the job is selected with constant indices
+  // so its fields stay in scalar registers
+  int y = blockIdx.y;
+  RotateJob jd = jobs.job[0];
+  if (jobs.n > 1 && y >= jobs.job[0].heads) {
+    y -= jobs.job[0].heads;
+    jd = jobs.job[1];
+    if (jobs.n > 2 && y >= jobs.job[1].heads) {
+      y -= jobs.job[1].heads;
+      jd = jobs.job[2];
+    }
   }
-  const RotateJob& jd = jobs.job[jb];
   const int h = y;
   const int t0 = blockIdx.x * TT;
+  // All global loads are issued before the first wait: R (16 x 16 B per
+  // thread) and the TT input rows (TT * 256 B, 16 B per thread).
+  static_assert(TT * kD == 8 * 256, "one 8-element chunk of the input rows per thread");
   const float4* rh = (const float4*)(jd.r + (size_t)(h / jd.g) * kD * kD);
-  for (int e = tid; e < kD * kD / 4; e += 256) *(float4*)(&rs[0][0] + 4 * e) = rh[e];
-  for (int e = tid; e < TT * kD; e += 256) {
-    const int t = e / kD, c = e % kD;
-    double v = 0.0;
-    if (t0 + t < n_tok) v = (double)bf16_bits_to_f32(jd.src[((size_t)(t0 + t) * jd.heads + h) * kD + c]);
-    xs[t][c] = v;
+  float4 rr[kD * kD / 4 / 256];
+#pragma unroll
+  for (int k = 0; k < kD * kD / 4 / 256; ++k) rr[k] = rh[tid + 256 * k];
+  const int xt = tid / 16, xc = 8 * (tid % 16);
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t xw = {0u, 0u, 0u, 0u};
+  if (t0 + xt < n_tok) xw = *(const u32x4_t*)(jd.src + ((size_t)(t0 + xt) * jd.heads + h) * kD + xc);
+#pragma unroll
+  for (int k = 0; k < kD * kD / 4 / 256; ++k) *(float4*)(&rs[0][0] + 4 * (tid + 256 * k)) = rr[k];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    xs[xt][xc + 2 * e] = (double)bf16_bits_to_f32(xw[e] & 0xFFFFu);
+    xs[xt][xc + 2 * e + 1] = (double)bf16_bits_to_f32(xw[e] >> 16);
   }
   __syncthreads();
 

@@ -57,9 +57,10 @@ struct RotateJobs {
 hipError_t launch_rotate(const RotateJobs& jobs, int n_tok, hipStream_t stream);
 
 // Quantize every position that moves to INT2 in this append, from the ring
-// (old rows) or the staging rows (new tokens), into the pages.
+// (old rows) or the staging rows (new tokens), into the pages.  total_q =
+// sum over sequences of S_quant(after) - S_quant(before) (< 2^31).
 hipError_t launch_quantize(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
-                           const uint16_t* stage_k, const uint16_t* stage_v, int max_q,
+                           const uint16_t* stage_k, const uint16_t* stage_v, int total_q,
                            hipStream_t stream);
 
 // Copy staging rows of new tokens that land in the sink or the ring.
@@ -70,14 +71,54 @@ hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* st
 hipError_t launch_dequant(const CacheArgs& c, int slot, int len, int t0, int t1, float* k_out,
                           float* v_out, hipStream_t stream);
 
+// ---- decode work split (shared by the host planner and the kernels) ------
+//
+// The decode work of one (sequence, group of KV heads, query-head pass) is
+// its INT2 page pairs plus its BF16 window blocks; a window block (8 KB per
+// head) counts as kWinCost page pairs (2.5 KB per head at G = 64, plus the
+// extra MFMA work of the bf16 path).  The work is cut into splits of at most
+// `quota` units; every split is one work-group of the split launch.
+constexpr int kWinCost = 3;
+constexpr int kMaxSplits = 256;            // splits per (sequence, row), merge LDS bound
+constexpr int kMaxPairsPerSplit = 256;     // page ids staged per work-group
+constexpr int kMaxScanSeqs = 2048;         // sequences per decode launch
+
+struct DecodeWork {
+  int n_pairs;                   // INT2 page pairs
+  int n_wu;                      // BF16 window blocks visited
+};
+
+__host__ __device__ inline DecodeWork decode_work(int len, int s_sink, int s_keep, int s_flush,
+                                                  int ring_cap) {
+  DecodeWork w{0, 0};
+  if (len < 1) return w;
+  const int num = len - s_sink - s_keep;
+  const int sq = s_sink + s_flush * (num >= 0 ? num / s_flush : 0);
+  const int nq = sq > s_sink ? sq - s_sink : 0;
+  w.n_pairs = ((nq + kPage - 1) / kPage + 1) / 2;
+  const int nsink = len < s_sink ? len : s_sink;
+  const int ring_lo = sq > s_sink ? sq : s_sink;
+  w.n_wu = (nsink + kPage - 1) / kPage + (len > ring_lo ? ring_cap / kPage : 0);
+  return w;
+}
+
+__host__ __device__ inline int decode_splits(DecodeWork w, int quota, int smax) {
+  const int cost = w.n_pairs + kWinCost * w.n_wu;
+  const int n = cost > 0 ? (cost + quota - 1) / quota : 1;
+  return n < smax ? n : smax;
+}
+
 // INT2 split-K decode (partials to the workspace) and the merge / un-rotation launch.
 struct DecodePlan {
   int quota;                     // work per context split, in page pairs (a window block = 3)
-  int smax;                      // most splits of any sequence (grid x)
+  int smax;                      // most splits of any sequence
   int hp;                        // query heads handled per pass (<= 16 / ng)
   int passes;                    // ceil(g / hp)
   int wh;                        // KV heads (waves) per work-group
+  int grid;                      // work-groups of the split launch (= its work items)
 };
+// Work-groups of the split kernel that fit on one compute unit.
+int decode_wgs_per_cu(const CacheArgs& c, const DecodePlan& plan);
 constexpr int kDecodeSplit = 1;   // the split kernel: partial records to the workspace
 constexpr int kDecodeMerge = 2;   // the merge / un-rotation kernel: partials to out
 hipError_t launch_decode(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
