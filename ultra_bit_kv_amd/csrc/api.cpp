@@ -327,6 +327,15 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
     jobs.job[jobs.n++] = RotateJob{q, cache->r_k, q_rot, nullptr, c.num_q_heads,
                                    c.num_q_heads / c.num_kv_heads};
   if ((st = hip_status(launch_rotate(jobs, (int)n_tok, sm))) != OSCAR_OK) return st;
+  // 2+3 in one launch when no new row lands on a ring slot the flush reads
+  bool disjoint = true;
+  for (int i = 0; disjoint && i < n_seqs; ++i) {
+    const int64_t n_new = (int64_t)cu_new_host[i + 1] - cu_new_host[i];
+    const int64_t lb = len_before_host[i];
+    if (n_new > 0 && (lb + n_new - 1) - s_quant(lb, c) >= a.ring_cap) disjoint = false;
+  }
+  if (disjoint)
+    return hip_status(launch_flush_place(a, clip, sa, stage_k, stage_v, (int)total_q, max_new, sm));
   // 2. quantize every position that crosses S_quant (reads the ring first)
   if ((st = hip_status(launch_quantize(a, clip, sa, stage_k, stage_v, (int)total_q, sm))) != OSCAR_OK)
     return st;

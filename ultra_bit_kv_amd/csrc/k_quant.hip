@@ -30,9 +30,13 @@ __device__ __forceinline__ double lerp_quantile(double a, double b, double f) {
   return a + f * (b - a);
 }
 
-__global__ __launch_bounds__(128) void quantize_kernel(CacheArgs c, ClipArgs clip, SeqArgs s,
-                                                       const uint16_t* __restrict__ stage_k,
-                                                       const uint16_t* __restrict__ stage_v) {
+// Quantize position `item` (of all the append's quantized positions) of KV
+// head h; run by a work-group of 128 threads.
+__device__ __forceinline__ void quantize_item(const CacheArgs& c, const ClipArgs& clip,
+                                              const SeqArgs& s,
+                                              const uint16_t* __restrict__ stage_k,
+                                              const uint16_t* __restrict__ stage_v, int item,
+                                              int h) {
 #pragma clang fp contract(off)
   __shared__ float vals[2][kD];
   __shared__ float sel[2][4][4];
@@ -40,9 +44,7 @@ __global__ __launch_bounds__(128) void quantize_kernel(CacheArgs c, ClipArgs cli
   __shared__ int s_run[2];
   __shared__ int s_seq, s_before;
 
-  const int h = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;   // w: 0 = K, 1 = V
-  const int item = blockIdx.x;
   // ---- sequence of this position: prefix sum of the per-sequence counts
   auto count_of = [&](int k) {
     const int lb = s.lens[k];
@@ -117,6 +119,7 @@ __global__ __launch_bounds__(128) void quantize_kernel(CacheArgs c, ClipArgs cli
   const int gs = gi * G;
   const int c0 = 2 * lane, c1 = 2 * lane + 1;
   int r0 = 0, r1 = 0;
+#pragma unroll 8
   for (int jj = 0; jj < G; ++jj) {
     const int j = gs + ((jj + gi) & (G - 1));  // per-group start offset avoids bank conflicts
     const float v = vals[w][j];
@@ -176,6 +179,12 @@ __global__ __launch_bounds__(128) void quantize_kernel(CacheArgs c, ClipArgs cli
   }
 }
 
+__global__ __launch_bounds__(128) void quantize_kernel(CacheArgs c, ClipArgs clip, SeqArgs s,
+                                                       const uint16_t* __restrict__ stage_k,
+                                                       const uint16_t* __restrict__ stage_v) {
+  quantize_item(c, clip, s, stage_k, stage_v, blockIdx.x, blockIdx.y);
+}
+
 hipError_t launch_quantize(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
                            const uint16_t* stage_k, const uint16_t* stage_v, int total_q,
                            hipStream_t stream) {
@@ -186,10 +195,10 @@ hipError_t launch_quantize(const CacheArgs& c, const ClipArgs& clip, const SeqAr
 }
 
 // New rows that stay in BF16: sink positions and positions at or beyond S_quant.
-__global__ __launch_bounds__(128) void place_kernel(CacheArgs c, SeqArgs s,
-                                                    const uint16_t* __restrict__ stage_k,
-                                                    const uint16_t* __restrict__ stage_v) {
-  const int i = blockIdx.z, h = blockIdx.y, ti = blockIdx.x;
+__device__ __forceinline__ void place_item(const CacheArgs& c, const SeqArgs& s,
+                                           const uint16_t* __restrict__ stage_k,
+                                           const uint16_t* __restrict__ stage_v, int ti, int h,
+                                           int i) {
   const int ch = threadIdx.x;
   const int slot = s.slots[i];
   const int lb = s.lens[i];
@@ -213,6 +222,39 @@ __global__ __launch_bounds__(128) void place_kernel(CacheArgs c, SeqArgs s,
   const size_t src = (tok * c.hkv + h) * kD + ch;
   wb[tt * kD + ch] = stage_k[src];
   wb[kPage * kD + v_window_index(tt, ch)] = stage_v[src];
+}
+
+__global__ __launch_bounds__(128) void place_kernel(CacheArgs c, SeqArgs s,
+                                                    const uint16_t* __restrict__ stage_k,
+                                                    const uint16_t* __restrict__ stage_v) {
+  place_item(c, s, stage_k, stage_v, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Quantize and place in one launch, for appends where no new row lands on a
+// ring slot that the flush reads (the two sets of work-groups then touch
+// disjoint memory).  Work-groups [0, total_q Hkv) quantize, the rest place.
+__global__ __launch_bounds__(128) void flush_place_kernel(CacheArgs c, ClipArgs clip, SeqArgs s,
+                                                          const uint16_t* __restrict__ stage_k,
+                                                          const uint16_t* __restrict__ stage_v,
+                                                          int total_q, int max_new) {
+  const int nq = total_q * c.hkv;
+  const int b = blockIdx.x;
+  if (b < nq) {
+    quantize_item(c, clip, s, stage_k, stage_v, b / c.hkv, b % c.hkv);
+  } else {
+    const int pb = b - nq;
+    place_item(c, s, stage_k, stage_v, pb % max_new, (pb / max_new) % c.hkv, pb / (max_new * c.hkv));
+  }
+}
+
+hipError_t launch_flush_place(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
+                              const uint16_t* stage_k, const uint16_t* stage_v, int total_q,
+                              int max_new, hipStream_t stream) {
+  if (s.n_seqs <= 0 || (total_q <= 0 && max_new <= 0)) return hipSuccess;
+  const long long grid = (long long)total_q * c.hkv + (long long)max_new * c.hkv * s.n_seqs;
+  hipLaunchKernelGGL(flush_place_kernel, dim3((unsigned)grid), dim3(128), 0, stream, c, clip, s,
+                     stage_k, stage_v, total_q, max_new > 0 ? max_new : 1);
+  return hipGetLastError();
 }
 
 hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* stage_k,

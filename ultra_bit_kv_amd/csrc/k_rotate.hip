@@ -10,18 +10,30 @@
 // is the rounding of the exact dot product (barring a tie closer than the fp64
 // accumulation error, ~1e-14 relative).
 //
+// The sums run on the fp64 matrix cores: v_mfma_f64_16x16x4f64 computes each
+// output as a chain of fused multiply-adds in ascending k starting from the
+// accumulator, so 32 chained instructions give exactly the sequential fp64
+// FMA chain over k = 0..127 for a 16-token x 16-column tile.  Lane l supplies
+// A[i = l % 16][k = l / 16], B[k = l / 16][j = l % 16] and receives
+// D[i = l / 16 + 4 v][j = l % 16], v = 0..3 (checked on gfx950).
+//
 // One launch rotates up to three row sets (keys, values, queries): grid.y
-// enumerates (set, head).  R of the head is staged in LDS with one round of
-// coalesced loads; a thread owns one output column j and TT/2 tokens.
+// enumerates (set, head), grid.z the two 64-column halves of the output.
+// Wave w of a work-group owns 16 output columns and keeps their slice of R
+// (one value per k-quad per lane) in registers; the work-group walks TB
+// blocks of 16 tokens, staging each block's input rows in LDS.
 #include "device_common.h"
 
 namespace oscar {
 
-template <int TT>
+typedef double double4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_r __attribute__((ext_vector_type(4)));
+
+template <int TB>
 __global__ __launch_bounds__(256) void rotate_kernel(RotateJobs jobs, int n_tok) {
-  __shared__ double xs[TT][kD + 1];
-  __shared__ float rs[kD][kD];
+  __shared__ uint16_t xs[16][kD + 8];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   // grid.y enumerates (job, head); the job is selected with constant indices
   // so its fields stay in scalar registers
   int y = blockIdx.y;
@@ -35,48 +47,42 @@ __global__ __launch_bounds__(256) void rotate_kernel(RotateJobs jobs, int n_tok)
     }
   }
   const int h = y;
-  const int t0 = blockIdx.x * TT;
-  // All global loads are issued before the first wait: R (16 x 16 B per
-  // thread) and the TT input rows (TT * 256 B, 16 B per thread).
-  static_assert(TT * kD == 8 * 256, "one 8-element chunk of the input rows per thread");
-  const float4* rh = (const float4*)(jd.r + (size_t)(h / jd.g) * kD * kD);
-  float4 rr[kD * kD / 4 / 256];
-#pragma unroll
-  for (int k = 0; k < kD * kD / 4 / 256; ++k) rr[k] = rh[tid + 256 * k];
-  const int xt = tid / 16, xc = 8 * (tid % 16);
-  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  u32x4_t xw = {0u, 0u, 0u, 0u};
-  if (t0 + xt < n_tok) xw = *(const u32x4_t*)(jd.src + ((size_t)(t0 + xt) * jd.heads + h) * kD + xc);
-#pragma unroll
-  for (int k = 0; k < kD * kD / 4 / 256; ++k) *(float4*)(&rs[0][0] + 4 * (tid + 256 * k)) = rr[k];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    xs[xt][xc + 2 * e] = (double)bf16_bits_to_f32(xw[e] & 0xFFFFu);
-    xs[xt][xc + 2 * e + 1] = (double)bf16_bits_to_f32(xw[e] >> 16);
-  }
-  __syncthreads();
+  const int j = 64 * blockIdx.z + 16 * wave + (lane & 15);   // output column of this lane
+  const int kq = lane >> 4;                                    // k offset inside a k-quad
 
-  constexpr int TPT = TT / 2;         // tokens per thread
-  const int j = tid % kD;             // output column
-  const int tb = (tid / kD) * TPT;
-  double acc[TPT];
+  // R[4 kb + kq][j] for kb = 0..31: this lane's share of the B operands
+  const float* R = jd.r + (size_t)(h / jd.g) * kD * kD;
+  float rb[kD / 4];
 #pragma unroll
-  for (int t = 0; t < TPT; ++t) acc[t] = 0.0;
-#pragma unroll 4
-  for (int k = 0; k < kD; ++k) {
-    const double rk = (double)rs[k][j];
+  for (int kb = 0; kb < kD / 4; ++kb) rb[kb] = R[(size_t)(4 * kb + kq) * kD + j];
+
+  const int xrow = tid / 16, xc = 8 * (tid % 16);   // staging: 16 rows x 16 chunks of 8 values
+  for (int b = 0; b < TB; ++b) {
+    const int t0 = (blockIdx.x * TB + b) * 16;
+    if (t0 >= n_tok) break;   // uniform
+    u32x4_r xw = {0u, 0u, 0u, 0u};
+    if (t0 + xrow < n_tok)
+      xw = *(const u32x4_r*)(jd.src + ((size_t)(t0 + xrow) * jd.heads + h) * kD + xc);
+    *(u32x4_r*)(&xs[xrow][xc]) = xw;
+    __syncthreads();
+
+    double4_t acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int t = 0; t < TPT; ++t) acc[t] = __builtin_fma(xs[tb + t][k], rk, acc[t]);
-  }
-#pragma unroll
-  for (int t = 0; t < TPT; ++t) {
-    const int tok = t0 + tb + t;
-    if (tok < n_tok) {
-      const uint16_t out = f64_to_bf16_rne(acc[t]);
-      const size_t o = ((size_t)tok * jd.heads + h) * kD + j;
-      jd.dst_a[o] = out;
-      if (jd.dst_b) jd.dst_b[o] = out;
+    for (int kb = 0; kb < kD / 4; ++kb) {
+      const double a = (double)bf16_bits_to_f32(xs[lane & 15][4 * kb + kq]);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)rb[kb], acc, 0, 0, 0);
     }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = t0 + kq + 4 * v;
+      if (tok < n_tok) {
+        const uint16_t out = f64_to_bf16_rne(acc[v]);
+        const size_t o = ((size_t)tok * jd.heads + h) * kD + j;
+        jd.dst_a[o] = out;
+        if (jd.dst_b) jd.dst_b[o] = out;
+      }
+    }
+    __syncthreads();   // the next block overwrites xs
   }
 }
 
@@ -84,8 +90,13 @@ hipError_t launch_rotate(const RotateJobs& jobs, int n_tok, hipStream_t stream) 
   if (n_tok <= 0 || jobs.n <= 0) return hipSuccess;
   int rows = 0;
   for (int k = 0; k < jobs.n; ++k) rows += jobs.job[k].heads;
-  dim3 grid((n_tok + 15) / 16, rows);
-  hipLaunchKernelGGL(rotate_kernel<16>, grid, dim3(256), 0, stream, jobs, n_tok);
+  const int blocks = (n_tok + 15) / 16;
+  if (blocks <= 64) {   // small calls (decode steps): one 16-token block per work-group
+    hipLaunchKernelGGL(rotate_kernel<1>, dim3(blocks, rows, 2), dim3(256), 0, stream, jobs, n_tok);
+  } else {              // prefill: each work-group reuses its R slice over 8 blocks
+    hipLaunchKernelGGL(rotate_kernel<8>, dim3((blocks + 7) / 8, rows, 2), dim3(256), 0, stream,
+                       jobs, n_tok);
+  }
   return hipGetLastError();
 }
 

@@ -63,6 +63,12 @@ hipError_t launch_quantize(const CacheArgs& c, const ClipArgs& clip, const SeqAr
                            const uint16_t* stage_k, const uint16_t* stage_v, int total_q,
                            hipStream_t stream);
 
+// Both of the above in one launch; only valid when no new row lands on a ring
+// slot that the flush still reads.
+hipError_t launch_flush_place(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
+                              const uint16_t* stage_k, const uint16_t* stage_v, int total_q,
+                              int max_new, hipStream_t stream);
+
 // Copy staging rows of new tokens that land in the sink or the ring.
 hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* stage_k,
                         const uint16_t* stage_v, int max_new, hipStream_t stream);
