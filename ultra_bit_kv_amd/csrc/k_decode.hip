@@ -132,16 +132,6 @@ __device__ __forceinline__ void softmax_step(const float (&x)[N], float scale, f
 constexpr int kMaxWgPages = 2 * kMaxPairsPerSplit;   // page ids staged per work-group
 constexpr int kPrefetch = 2;       // page pairs in flight per wave ahead of the one processed
 
-// Issue priority of the calling wave from its remaining share of the work:
-// waves of one SIMD otherwise issue oldest-first, so the first work-groups
-// on a compute unit run ahead and the last ones finish alone.
-__device__ __forceinline__ void set_priority(int remaining, int total) {
-  const int p = (4 * remaining - 1) / total;   // 0..3
-  if (p >= 3) __builtin_amdgcn_s_setprio(3);
-  else if (p == 2) __builtin_amdgcn_s_setprio(2);
-  else if (p == 1) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
-}
 
 // Work-group = one work item (sequence, context split, group of WH adjacent
 // KV heads, query-head pass); items are numbered sequence-major, then split,
@@ -154,14 +144,11 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
                                                               int passes, int smax,
                                                               const uint16_t* __restrict__ q_rot,
                                                               float* __restrict__ partials) {
-  constexpr int G = kD / NG;
   constexpr int PW = HP * kD + 2 * HP;   // floats per partial record
   constexpr int NT = 64 * WH;
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[WH][HP][kD];
-  __shared__ float s_qsum[WH][HP * NG];
   __shared__ int s_pages[kMaxWgPages];
   __shared__ int s_wsum[WH];
-  __shared__ int s_item[2];
+  __shared__ int s_item[4];   // sequence, item within it, its slot and length
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -171,9 +158,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
 
   // ---- the item of this work-group: sequence i with prefix(i) <= item < prefix(i + 1)
   {
-    auto seq_items = [&](int k) {
-      const int sl = s.slots[k];
-      const int ln = s.lens[k];
+    auto seq_items = [&](int sl, int ln) {
       const bool ok = sl >= 0 && sl < c.max_seqs && ln >= 1;
       const DecodeWork wk = decode_work(ok ? ln : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap);
       return decode_splits(wk, quota, smax) * rows;
@@ -181,7 +166,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     const int n = s.n_seqs, per = (n + NT - 1) / NT;
     const int k0 = min(tid * per, n), k1 = min(k0 + per, n);
     int run = 0;
-    for (int k = k0; k < k1; ++k) run += seq_items(k);
+    for (int k = k0; k < k1; ++k) run += seq_items(s.slots[k], s.lens[k]);
     int incl = run;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -195,10 +180,13 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     for (int w2 = 0; w2 < wave; ++w2) off += s_wsum[w2];
     const int item = blockIdx.x;
     for (int k = k0; k < k1; ++k) {
-      const int q = seq_items(k);
+      const int sl = s.slots[k], ln = s.lens[k];
+      const int q = seq_items(sl, ln);
       if (item >= off && item < off + q) {   // exactly one (k, thread) matches
         s_item[0] = k;
         s_item[1] = item - off;
+        s_item[2] = sl;
+        s_item[3] = ln;
       }
       off += q;
     }
@@ -211,8 +199,8 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int hgrp = row / passes, pass = row % passes;
   const int h = hgrp * WH + wave;
 
-  const int slot = s.slots[i];
-  int len = s.lens[i];
+  const int slot = __builtin_amdgcn_readfirstlane(s_item[2]);
+  int len = __builtin_amdgcn_readfirstlane(s_item[3]);
   const bool row_ok = slot >= 0 && slot < c.max_seqs && len >= 1;
   if (!row_ok) len = 0;
   const int nh = min(HP, c.g - pass * HP);   // valid heads in this pass
@@ -237,8 +225,6 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int pe = (int)((unsigned)((split + 1) * n_pairs) / (unsigned)n_split);
   const int wb = (int)((unsigned)(split * n_wu) / (unsigned)n_split);
   const int we = (int)((unsigned)((split + 1) * n_wu) / (unsigned)n_split);
-  const int total_units = max(1, (pe - pb) + kWinCost * (we - wb));
-  set_priority(total_units, total_units);
   const uint16_t* wbase = c.win + ((size_t)(row_ok ? slot : 0) * c.hkv + h) * c.win_blocks *
                                       (2 * kPage * kD);
   struct Win {
@@ -260,15 +246,22 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
       W.vl[k] = *(const u32x4*)(bp + kPage * kD + 32 * (16 * qd + r16) + 8 * k);
     }
   };
-  // ---- stage the query rows (WH heads x this pass) and the split's page ids in LDS
-  for (int t = tid; t < WH * HP * 16; t += 64 * WH) {
-    const int ww = t / (HP * 16), hh = (t / 16) % HP, part = t & 15;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (hh < nh) {
-      const size_t qh = (size_t)(hgrp * WH + ww) * c.g + (size_t)pass * HP + hh;
-      v = *(const u32x4*)(q_rot + ((size_t)(row_ok ? i : 0) * c.hq + qh) * kD + 8 * part);
-    }
-    *(u32x4*)(&s_q[ww][hh][8 * part]) = v;
+  // ---- per-lane MFMA column n = (group gi, head hl)
+  const int n = r16, gi = n / HP, hl = n % HP;
+  const bool colv = (gi < NG) && (hl < nh);
+  const int grp_q = (NG == 1) ? 0 : (NG == 2 ? (qd >> 1) : qd);   // group of channels 32qd..32qd+31
+  const bool bval = colv && (gi == grp_q);
+  const float C2 = kLog2e * 0.08838834764831845f;                // log2(e) / sqrt(128)
+  const float K1 = C2 * 16777216.0f;                              // undo the 2^-24 code scaling
+
+  // ---- the lane's 32 query channels straight into registers; the split's page ids to LDS
+  u32x4 wq[4];
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const uint16_t* qp = q_rot + ((size_t)i * c.hq + (size_t)h * c.g + (size_t)pass * HP +
+                                  (colv ? hl : 0)) * kD + 32 * qd;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) wq[cc] = colv ? *(const u32x4*)(qp + 8 * cc) : z;
   }
   const int n_wg_pages = min(2 * (pe - pb), kMaxWgPages);
   for (int t = tid; t < n_wg_pages; t += 64 * WH) {
@@ -277,32 +270,21 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     if (pg < n_pages && pg < c.max_pages) ph = bt[pg];
     s_pages[t] = (ph >= 0 && ph < c.num_pages) ? ph : -1;
   }
-  __syncthreads();
-  for (int t = tid; t < WH * HP * NG; t += 64 * WH) {   // (group, head) slices of q', column order
-    const int ww = t / (HP * NG), col = t % (HP * NG);
-    const int hh = col % HP, gg = col / HP;
-    float sum = 0.0f;
-    for (int ch = gg * G; ch < (gg + 1) * G; ++ch) sum += bf16_bits_to_f32(s_q[ww][hh][ch]);
-    s_qsum[ww][col] = sum;
-  }
-  __syncthreads();
-
-  // ---- per-lane MFMA operands for column n = (group gi, head hl)
-  const int n = r16, gi = n / HP, hl = n % HP;
-  const bool colv = (gi < NG) && (hl < nh);
-  const int grp_q = (NG == 1) ? 0 : (NG == 2 ? (qd >> 1) : qd);   // group of channels 32qd..32qd+31
-  const bool bval = colv && (gi == grp_q);
-  const float C2 = kLog2e * 0.08838834764831845f;                // log2(e) / sqrt(128)
-  const float K1 = C2 * 16777216.0f;                              // undo the 2^-24 code scaling
-  // INT2 logits in raw units x = s * D + z * qsum * 2^-24, log2 logit = K1 * x
-  const float qz = colv ? s_qsum[wave][n] * (1.0f / 16777216.0f) : 0.0f;
-
-  u32x4 wq[4];
+  // group sums of q' for the zero-point term: each lane adds its 32 channels
+  // if they lie in its column's group, then the four lanes of the column add up
+  float qsum = 0.0f;
+  if (bval) {
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    wq[cc] = colv ? *(const u32x4*)(&s_q[wave][hl][32 * qd + 8 * cc]) : z;
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qsum += bf16_bits_to_f32(wq[cc][e] & 0xFFFFu) + bf16_bits_to_f32(wq[cc][e] >> 16);
   }
+  qsum = rows_sum(qsum);
+  // INT2 logits in raw units x = s * D + z * qsum * 2^-24, log2 logit = K1 * x
+  const float qz = colv ? qsum * (1.0f / 16777216.0f) : 0.0f;
+  __syncthreads();   // page ids visible
+
   bf16x8 bw[4];
   half8 bq[4];
 #pragma unroll
@@ -461,7 +443,6 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   // ---- INT2 page pairs: accumulate in code units (code * 4^(j%4) * 2^-24)
   if (np > 0) {
     for (int k = 0; k < np; k += PF) {
-      set_priority(total_units - k, total_units);
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
         if (k + j < np) process_pair(ring[j]);
@@ -477,7 +458,6 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     Win wa, wn;
     load_win(wb, wa);
     for (int u = wb; u < we; ++u) {
-      set_priority(kWinCost * (we - u), total_units);
       if (u + 1 < we) load_win(u + 1, wn);
       if (__any(win_slot_ok(u, r16))) process_win(wa);
       wa = wn;
@@ -504,113 +484,160 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   }
 }
 
-// Log-sum-exp merge of the split partials of one (sequence, KV head, pass),
-// then o = o' . R_V^T with R_V staged in LDS (rows padded to 129 floats so the
-// row-per-thread reads of a wave fall in distinct banks).  Every global load
-// of the work-group (R_V, the split maxima and sums, the first kChunk split
-// outputs of each channel) is issued before the first wait, so the merge
-// costs about one memory round trip.
+// Log-sum-exp merge of the split partials, then o = o' . R_V^T.
+//
+// Work-group = (KV head, pass, block of SB sequences, half of the output
+// columns); its 16 rows are the (sequence, query head) pairs of the block,
+// which is exactly one MFMA tile of rows.  All global loads (the half of R_V,
+// every split's max and sum, the first kChunk split outputs of each row
+// channel) are issued before the first wait; both column halves merge the
+// same rows.  The un-rotation runs on the fp32 matrix cores: o'[16 x 128]
+// times the R_V^T columns of the half, with those R_V rows staged in LDS
+// (padded to 132 floats so the operand reads of a wave fall in distinct
+// banks).
 template <int HP>
 __global__ __launch_bounds__(256) void merge_unrotate_kernel(CacheArgs c, SeqArgs s, int quota,
-                                                             int passes, int smax,
+                                                             int passes, int smax, int sb,
                                                              const float* __restrict__ partials,
                                                              float* __restrict__ out) {
   constexpr int PW = HP * kD + 2 * HP;
-  constexpr int kMaxS = 256;
   constexpr int kChunk = 8;                      // split outputs per channel per load round
-  constexpr int kOut = (HP * kD + 255) / 256;    // output channels per thread
-  __shared__ float rv[kD][kD + 1];
-  __shared__ float fin[HP][kD];
-  __shared__ float s_M[HP], s_L[HP];
-  // per-split maxima and sums, [smax][HP] each, in dynamic LDS (2 * smax * HP floats)
+  constexpr int kRows = 16;
+  constexpr int kLd = kD + 4;
+  __shared__ float rv[kD / 2][kLd];   // the half of R_V's rows (output columns) of this work-group
+  __shared__ float fin[kRows][kLd];
+  __shared__ float s_M[kRows], s_L[kRows];
+  __shared__ int s_ns[kRows];
+  // per-split maxima and sums, [kRows][smax] each, in dynamic LDS
   extern __shared__ float s_dyn[];
-  float (*s_m)[HP] = (float (*)[HP])s_dyn;
-  float (*s_l)[HP] = (float (*)[HP])(s_dyn + (size_t)smax * HP);
+  float* s_m = s_dyn;
+  float* s_l = s_dyn + (size_t)kRows * smax;
   const int tid = threadIdx.x;
   const int h = blockIdx.x / passes, pass = blockIdx.x % passes;
-  const int i = blockIdx.y;
   const int nh = min(HP, c.g - pass * HP);
-  const int slot = s.slots[i];
-  int len = s.lens[i];
-  const bool row_ok = slot >= 0 && slot < c.max_seqs && len >= 1;
-  if (!row_ok) len = 0;
-  const DecodeWork wk = decode_work(len, c.s_sink, c.s_keep, c.s_flush, c.ring_cap);
-  const int n_split = min(decode_splits(wk, quota, smax), kMaxS);
-  const float* recs = partials + (((size_t)i * c.hkv + h) * passes + pass) * smax * PW;
+  const int s0 = blockIdx.y * sb;
+  const int jh = 64 * blockIdx.z;   // output columns jh .. jh + 63
 
-  // ---- issue: R_V, per-split (max, sum), first chunk of split outputs
-  const float4* rg = (const float4*)(c.r_v + (size_t)h * kD * kD);
-  float4 rvv[kD * kD / 4 / 256];
+  // row r <-> (sequence s0 + r / nh, head hh = r % nh)
+  auto row_seq = [&](int r) { return s0 + r / nh; };
+  auto row_valid = [&](int r) { return r < sb * nh && row_seq(r) < s.n_seqs; };
+  auto rec_of = [&](int r) {
+    return partials + (((size_t)row_seq(r) * c.hkv + h) * passes + pass) * smax * PW;
+  };
+  // ---- issue every load first: R_V, the split maxima / sums and the first
+  // kChunk split outputs of each (row, channel).  Records exist for all smax
+  // splits of every row, so the loads need not wait for the split counts.
+  const float4* rg = (const float4*)(c.r_v + ((size_t)h * kD + jh) * kD);
+  float4 rvv[kD * kD / 8 / 256];
 #pragma unroll
-  for (int t = 0; t < kD * kD / 4 / 256; ++t) rvv[t] = rg[tid + 256 * t];
-  for (int t = tid; t < n_split * nh; t += 256) {
-    const int sp = t / nh, hh = t % nh;
-    s_m[sp][hh] = recs[(size_t)sp * PW + hh];
-    s_l[sp][hh] = recs[(size_t)sp * PW + HP + hh];
+  for (int t = 0; t < kD * kD / 8 / 256; ++t) rvv[t] = rg[tid + 256 * t];
+  const int nml = kRows * smax;
+  const int t_ml = tid < nml ? tid : 0;
+  float ml_m = 0.0f, ml_l = 0.0f;
+  if (tid < nml && row_valid(t_ml / smax)) {
+    const float* rec = rec_of(t_ml / smax) + (size_t)(t_ml % smax) * PW;
+    ml_m = rec[(t_ml / smax) % nh];
+    ml_l = rec[HP + (t_ml / smax) % nh];
   }
-  float ov[kOut][kChunk];
+  constexpr int kPer = kRows * kD / 256;   // (row, channel) pairs per thread
+  const int ch = tid % kD;
+  const int jmax = smax < kChunk ? smax : kChunk;
+  float ov[kPer][kChunk];
 #pragma unroll
-  for (int k = 0; k < kOut; ++k) {
-    const int idx = tid + 256 * k;
-    const int hh = idx / kD, ch = idx % kD;
-    const float* o = recs + 2 * HP + hh * kD + ch;
+  for (int k = 0; k < kPer; ++k) {
+    const int r = tid / kD + 2 * k;
+    const bool rv_ok = row_valid(r);
+    const float* o = rec_of(rv_ok ? r : 0) + 2 * HP + (r % nh) * kD + ch;
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j)
-      ov[k][j] = (hh < nh && j < n_split) ? o[(size_t)j * PW] : 0.0f;
+    for (int j = 0; j < kChunk; ++j) ov[k][j] = (rv_ok && j < jmax) ? o[(size_t)j * PW] : 0.0f;
+  }
+  int my_ns = 0;
+  if (tid < kRows && row_valid(tid)) {
+    const int i = row_seq(tid);
+    const int slot = s.slots[i];
+    const int len = s.lens[i];
+    const bool ok = slot >= 0 && slot < c.max_seqs && len >= 1;
+    my_ns = decode_splits(decode_work(ok ? len : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap),
+                          quota, smax);
   }
 #pragma unroll
-  for (int t = 0; t < kD * kD / 4 / 256; ++t) {
+  for (int t = 0; t < kD * kD / 8 / 256; ++t) {
     const int e = 4 * (tid + 256 * t);
-    const int row = e / kD, col = e % kD;
-    rv[row][col] = rvv[t].x;
-    rv[row][col + 1] = rvv[t].y;
-    rv[row][col + 2] = rvv[t].z;
-    rv[row][col + 3] = rvv[t].w;
+    *(float4*)(&rv[e / kD][e % kD]) = rvv[t];
   }
+  if (tid < nml) {
+    s_m[tid] = ml_m;
+    s_l[tid] = ml_l;
+  }
+  for (int t = tid + 256; t < nml; t += 256) {   // more than 16 splits: remaining maxima / sums
+    const int r = t / smax, sp = t % smax;
+    float m = 0.0f, l = 0.0f;
+    if (row_valid(r)) {
+      const float* rec = rec_of(r) + (size_t)sp * PW;
+      m = rec[r % nh];
+      l = rec[HP + r % nh];
+    }
+    s_m[t] = m;
+    s_l[t] = l;
+  }
+  if (tid < kRows) s_ns[tid] = my_ns;
   __syncthreads();
-  if (tid < nh) {   // log-sum-exp of head tid over its splits
+  if (tid < kRows) {   // log-sum-exp of row tid over its splits
+    const int ns = s_ns[tid];
     float M = kNegInf;
-    for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, s_m[sp][tid]);
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, s_m[tid * smax + sp]);
     float L = 0.0f;
-    for (int sp = 0; sp < n_split; ++sp)
-      L += (M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s_m[sp][tid] - M)) * s_l[sp][tid];
+    for (int sp = 0; sp < ns; ++sp) {   // the split's weight replaces its maximum
+      const float wt = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s_m[tid * smax + sp] - M);
+      L += wt * s_l[tid * smax + sp];
+      s_m[tid * smax + sp] = wt;
+    }
     s_M[tid] = M;
     s_L[tid] = L;
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < kOut; ++k) {
-    const int idx = tid + 256 * k;
-    const int hh = idx / kD, ch = idx % kD;
-    if (hh < nh) {
-      const float M = s_M[hh];
-      auto weight = [&](int sp) {
-        return M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s_m[sp][hh] - M);
-      };
-      float O = 0.0f;
+  for (int k = 0; k < kPer; ++k) {
+    const int r = tid / kD + 2 * k;
+    const int ns = s_ns[r];
+    auto weight = [&](int sp) { return s_m[r * smax + sp]; };
+    float O = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j)
-        if (j < n_split) O = __builtin_fmaf(weight(j), ov[k][j], O);
-      const float* o = recs + 2 * HP + hh * kD + ch;
-      for (int sp0 = kChunk; sp0 < n_split; sp0 += kChunk) {   // long contexts: more rounds
+    for (int j = 0; j < kChunk; ++j)
+      if (j < ns) O = __builtin_fmaf(weight(j), ov[k][j], O);
+    if (ns > kChunk) {   // long contexts: more load rounds
+      const float* o = rec_of(r) + 2 * HP + (r % nh) * kD + ch;
+      for (int sp0 = kChunk; sp0 < ns; sp0 += kChunk) {
         float v[kChunk];
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) v[j] = sp0 + j < n_split ? o[(size_t)(sp0 + j) * PW] : 0.0f;
+        for (int j = 0; j < kChunk; ++j) v[j] = sp0 + j < ns ? o[(size_t)(sp0 + j) * PW] : 0.0f;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j)
-          if (sp0 + j < n_split) O = __builtin_fmaf(weight(sp0 + j), v[j], O);
+          if (sp0 + j < ns) O = __builtin_fmaf(weight(sp0 + j), v[j], O);
       }
-      fin[hh][ch] = O / s_L[hh];
     }
+    fin[r][ch] = ns > 0 ? O / s_L[r] : 0.0f;
   }
   __syncthreads();
-  if (!row_ok) return;
-  for (int idx = tid; idx < nh * kD; idx += 256) {
-    const int hh = idx / kD, jo = idx % kD;
-    float sum = 0.0f;
-#pragma unroll 8
-    for (int cc = 0; cc < kD; ++cc) sum = __builtin_fmaf(fin[hh][cc], rv[jo][cc], sum);
-    out[((size_t)i * c.hq + (size_t)h * c.g + pass * HP + hh) * kD + jo] = sum;
+
+  // ---- o = o' . R_V^T on the fp32 matrix cores: wave w computes columns jh + 16w .. +15
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, kq = lane >> 4;
+  float4_t acc0 = {0.f, 0.f, 0.f, 0.f};
+  const int j0 = 16 * wave;
+#pragma unroll
+  for (int kb = 0; kb < kD / 4; ++kb)
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(fin[li][4 * kb + kq], rv[j0 + li][4 * kb + kq], acc0,
+                                                0, 0, 0);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int r = 4 * kq + v;   // output row of this lane's v-th value
+    if (!row_valid(r)) continue;
+    const int i = row_seq(r);
+    const int slot = s.slots[i];
+    if (slot < 0 || slot >= c.max_seqs || s.lens[i] < 1) continue;
+    float* o = out + ((size_t)i * c.hq + (size_t)h * c.g + pass * HP + r % nh) * kD;
+    o[jh + j0 + li] = acc0[v];
   }
 }
 
@@ -639,10 +666,12 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
     if (e != hipSuccess) return e;
   }
   if (phases & kDecodeMerge) {
-    dim3 mgrid(c.hkv * plan.passes, s.n_seqs);
-    const size_t dyn = 2 * sizeof(float) * (size_t)(plan.smax < 256 ? plan.smax : 256) * HP;
+    const int nh_full = c.g < HP ? c.g : HP;
+    const int sb = 16 / nh_full;   // sequences per merge work-group (16 rows)
+    dim3 mgrid(c.hkv * plan.passes, (s.n_seqs + sb - 1) / sb, 2);
+    const size_t dyn = 2 * sizeof(float) * 16 * (size_t)plan.smax;
     hipLaunchKernelGGL((merge_unrotate_kernel<HP>), mgrid, dim3(256), dyn, stream, c, s,
-                       plan.quota, plan.passes, plan.smax, partials, out);
+                       plan.quota, plan.passes, plan.smax, sb, partials, out);
     return hipGetLastError();
   }
   return hipSuccess;
