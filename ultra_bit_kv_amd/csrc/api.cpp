@@ -25,7 +25,7 @@ static_assert((kMaxPagesPerSeq / 2) +
               "decode work of the largest row must fit the split limits");
 // Split launch sizing: the work-groups of a launch fill this share of the
 // resident slots, so none waits for a second round.
-constexpr int kFillPercent = 97;
+constexpr int kFillPercent = 100;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // S_quant of the flush rule (WUSH-KV notes, "method step details").
@@ -397,16 +397,19 @@ int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_
       max_cost = std::max(max_cost, cost[i]);
     }
     const int cap = max_splits(c, ns);
+    // quota in 1/16 units; at most 255 pairs per split (the LDS page list)
+    auto splits_of = [&](int64_t c16, int64_t q) { return std::max<int64_t>(1, (16 * c16 + q - 1) / q); };
     auto items_of = [&](int64_t q) {
       int64_t n = 0;
-      for (int i = 0; i < ns; ++i) n += std::max<int64_t>(1, (cost[i] + q - 1) / q);
+      for (int i = 0; i < ns; ++i) n += splits_of(cost[i], q);
       return n * rows;
     };
-    int64_t quota = std::max<int64_t>(2, (total * rows + slots - 1) / slots);
-    quota = std::max<int64_t>(quota, (max_cost + cap - 1) / cap);
-    quota = std::min<int64_t>(quota, kMaxPairsPerSplit);
+    const int64_t q_max = 16 * (kMaxPairsPerSplit - 1);
+    int64_t quota = std::max<int64_t>(32, (16 * total * rows + slots - 1) / slots);
+    quota = std::max<int64_t>(quota, (16 * max_cost + cap - 1) / cap);
+    quota = std::min<int64_t>(quota, q_max);
     if (items_of(quota) > slots) {   // smallest quota in (quota, limit] that fits (items fall as quota grows)
-      int64_t lo = quota, hi = kMaxPairsPerSplit;
+      int64_t lo = quota, hi = q_max;
       while (hi - lo > 1) {
         const int64_t mid = (lo + hi) / 2;
         (items_of(mid) > slots ? lo : hi) = mid;
@@ -414,7 +417,7 @@ int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_
       quota = hi;
     }
     int64_t smax = 1;
-    for (int i = 0; i < ns; ++i) smax = std::max<int64_t>(smax, (cost[i] + quota - 1) / quota);
+    for (int i = 0; i < ns; ++i) smax = std::max<int64_t>(smax, splits_of(cost[i], quota));
     plan.quota = (int)quota;
     plan.smax = (int)smax;
     plan.grid = (int)items_of(quota);

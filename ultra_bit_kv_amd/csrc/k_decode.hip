@@ -133,6 +133,17 @@ constexpr int kMaxWgPages = 2 * kMaxPairsPerSplit;   // page ids staged per work
 constexpr int kPrefetch = 2;       // page pairs in flight per wave ahead of the one processed
 
 
+// Issue priority of the calling wave from its remaining share of the work:
+// waves of one SIMD otherwise issue oldest-first, so the first work-groups
+// on a compute unit run ahead and the last ones finish alone.
+__device__ __forceinline__ void set_priority(int remaining, int total) {
+  const int p = (4 * remaining - 1) / total;   // 0..3
+  if (p >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (p == 2) __builtin_amdgcn_s_setprio(2);
+  else if (p == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Work-group = one work item (sequence, context split, group of WH adjacent
 // KV heads, query-head pass); items are numbered sequence-major, then split,
 // then head group, and the launch has exactly one work-group per item.  A
@@ -225,6 +236,8 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int pe = (int)((unsigned)((split + 1) * n_pairs) / (unsigned)n_split);
   const int wb = (int)((unsigned)(split * n_wu) / (unsigned)n_split);
   const int we = (int)((unsigned)((split + 1) * n_wu) / (unsigned)n_split);
+  const int total_units = max(1, (pe - pb) + kWinCost * (we - wb));
+  set_priority(total_units, total_units);
   const uint16_t* wbase = c.win + ((size_t)(row_ok ? slot : 0) * c.hkv + h) * c.win_blocks *
                                       (2 * kPage * kD);
   struct Win {
@@ -443,6 +456,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   // ---- INT2 page pairs: accumulate in code units (code * 4^(j%4) * 2^-24)
   if (np > 0) {
     for (int k = 0; k < np; k += PF) {
+      set_priority(total_units - k, total_units);
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
         if (k + j < np) process_pair(ring[j]);
@@ -458,6 +472,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     Win wa, wn;
     load_win(wb, wa);
     for (int u = wb; u < we; ++u) {
+      set_priority(kWinCost * (we - u), total_units);
       if (u + 1 < we) load_win(u + 1, wn);
       if (__any(win_slot_ok(u, r16))) process_win(wa);
       wa = wn;

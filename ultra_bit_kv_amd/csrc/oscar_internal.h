@@ -83,7 +83,9 @@ hipError_t launch_dequant(const CacheArgs& c, int slot, int len, int t0, int t1,
 // its INT2 page pairs plus its BF16 window blocks; a window block (8 KB per
 // head) counts as kWinCost page pairs (2.5 KB per head at G = 64, plus the
 // extra MFMA work of the bf16 path).  The work is cut into splits of at most
-// `quota` units; every split is one work-group of the split launch.
+// quota16 / 16 units (the quota is fixed point with 4 fraction bits, so the
+// planner can fill the device closely); every split is one work-group of the
+// split launch.
 constexpr int kWinCost = 3;
 constexpr int kMaxSplits = 256;            // splits per (sequence, row), merge LDS bound
 constexpr int kMaxPairsPerSplit = 256;     // page ids staged per work-group
@@ -108,15 +110,15 @@ __host__ __device__ inline DecodeWork decode_work(int len, int s_sink, int s_kee
   return w;
 }
 
-__host__ __device__ inline int decode_splits(DecodeWork w, int quota, int smax) {
+__host__ __device__ inline int decode_splits(DecodeWork w, int quota16, int smax) {
   const int cost = w.n_pairs + kWinCost * w.n_wu;
-  const int n = cost > 0 ? (cost + quota - 1) / quota : 1;
+  const int n = cost > 0 ? (16 * cost + quota16 - 1) / quota16 : 1;
   return n < smax ? n : smax;
 }
 
 // INT2 split-K decode (partials to the workspace) and the merge / un-rotation launch.
 struct DecodePlan {
-  int quota;                     // work per context split, in page pairs (a window block = 3)
+  int quota;                     // work per context split in 1/16 page pairs (a window block = 3 pairs)
   int smax;                      // most splits of any sequence
   int hp;                        // query heads handled per pass (<= 16 / ng)
   int passes;                    // ceil(g / hp)
