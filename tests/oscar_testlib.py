@@ -37,10 +37,11 @@ def make_cache(w, lens, identity=False, spare_pages=0, max_seqs=None):
     return cache
 
 
-def fill(cache, w, lens, chunk=4096, seqs=None, max_tokens=1 << 18):
+def fill(cache, w, lens, chunk=4096, seqs=None, max_tokens=1 << 18, last_step=True):
     """Append positions [0, L - 1) of every sequence in chunks of up to
-    ``chunk`` tokens (at most ``max_tokens`` per call), then the last token of
-    each with its query (a decode step).  Returns the step's q_rot."""
+    ``chunk`` tokens (at most ``max_tokens`` per call), then (``last_step``)
+    the last token of each with its query (a decode step).  Returns the
+    step's q_rot (None without the last step)."""
     import torch
     seqs = list(range(len(lens))) if seqs is None else seqs
     lens = [int(x) for x in lens]
@@ -62,6 +63,9 @@ def fill(cache, w, lens, chunk=4096, seqs=None, max_tokens=1 << 18):
         cache.append_tokens(idx, [done[i] for i in idx], n_new, k, v)
         for i, n in zip(idx, n_new):
             done[i] += n
+    if not last_step:
+        torch.cuda.synchronize()
+        return None
     all_i = list(range(len(lens)))
     k = np.concatenate([w.keys(seqs[i], lens[i] - 1, lens[i]) for i in all_i])
     v = np.concatenate([w.values(seqs[i], lens[i] - 1, lens[i]) for i in all_i])
