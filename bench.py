@@ -121,50 +121,67 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_bytes": nbytes, "launches": 5}))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--layers", type=int, default=4)
-    ap.add_argument("--config", default="c3_bs64")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--copy-calibration", type=int, default=0,
-                    help="only run a device copy of this many bytes (counter calibration)")
-    args = ap.parse_args()
+def int2_pages(w, L):
+    """INT2 pages of a row of L tokens (closed form of the flush rule)."""
+    s_quant = w.s_sink + w.s_flush * max(0, (int(L) - w.s_sink - w.s_keep) // w.s_flush)
+    return -(-max(0, s_quant - w.s_sink) // 16)
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU (the decode path shards by "
-              "sequence / KV head with no exchange; multi-GPU runs are not part of it)",
-              file=sys.stderr)
-        sys.exit(2)
 
+def make_layer(w, lens_max, n):
+    """An empty cache sized for rows growing to lens_max (seeded page pool)."""
+    from ultra_bit_kv_amd import OscarKVCache
+    r_k, r_v = w.rotations()
+    kk, kv = w.kappas()
+    bt, total = w.page_pool([max(1, int2_pages(w, L)) for L in lens_max])
+    return OscarKVCache(num_q_heads=w.hq, num_kv_heads=w.hkv, group_size=w.group,
+                        s_sink=w.s_sink, s_keep=w.s_keep, s_flush=w.s_flush, max_seqs=n,
+                        max_pages_per_seq=bt.shape[1], num_pages=total, clip_k=kk, clip_v=kv,
+                        r_k=r_k, r_v=r_v, block_table=bt)
+
+
+def populate(cache, w, lens, chunk=8192, max_tokens=1 << 18):
+    """Append positions [0, L) of every row through the library's append path."""
+    done = [0] * len(lens)
+    while True:
+        idx, n_new, budget = [], [], max_tokens
+        for i, L in enumerate(lens):
+            k = min(chunk, int(L) - done[i], budget)
+            if k > 0:
+                idx.append(i)
+                n_new.append(k)
+                budget -= k
+            if budget == 0:
+                break
+        if not idx:
+            return
+        k = np.concatenate([w.keys(i, done[i], done[i] + m) for i, m in zip(idx, n_new)])
+        v = np.concatenate([w.values(i, done[i], done[i] + m) for i, m in zip(idx, n_new)])
+        cache.append_tokens(idx, [done[i] for i in idx], n_new, k, v)
+        for i, m in zip(idx, n_new):
+            done[i] += m
+
+
+def measure(w, n_layers, steps, warmup):
+    """Time `steps` decode steps of every row of workload w (after `warmup`),
+    cycling through n_layers copies of the populated cache."""
     import torch
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-
-    from synth import get
     from ultra_bit_kv_amd import SeqBatch, as_bf16
-    from tests.oscar_testlib import make_cache, fill
 
-    w = get(args.config)
     lens0 = w.lengths_after()                 # context of the first timed step, per layer
     n = len(lens0)
-    total_steps = args.warmup + args.steps
-    per_layer = -(-total_steps // args.layers)
+    total_steps = warmup + steps
+    per_layer = -(-total_steps // n_layers)
     grow = [int(L) + per_layer for L in lens0]
     t_setup = time.perf_counter()
 
     # layer 0 is populated through the library's own append path with L0 - 1
     # tokens; the other layers are copies.  Layer step k appends position
     # L0 - 1 + k, so the first step of every layer decodes a context of L0.
-    base = make_cache(w, grow, max_seqs=n)
-    fill(base, w, [int(L) - 1 for L in lens0], chunk=8192)
+    base = make_layer(w, grow, n)
+    populate(base, w, [int(L) - 1 for L in lens0])
     layers = [base]
-    for _ in range(1, args.layers):
-        c = make_cache(w, grow, max_seqs=n)
+    for _ in range(1, n_layers):
+        c = make_layer(w, grow, n)
         c.pages.copy_(base.pages)
         c.win.copy_(base.win)
         layers.append(c)
@@ -194,8 +211,8 @@ def main():
     setup_s = time.perf_counter() - t_setup
 
     def step(s, ev=None):
-        c = layers[s % args.layers]
-        d = steps_in[s // args.layers]
+        c = layers[s % n_layers]
+        d = steps_in[s // n_layers]
         c.append(d["app"], d["k"], d["v"], d["q"], q_rot=q_rot)
         # the decode step as its two launches, timed apart: the split kernel
         # (all cache traffic) and the log-sum-exp merge / un-rotation
@@ -208,44 +225,71 @@ def main():
         if ev is not None:
             ev[2].record()
 
-    for s in range(args.warmup):
+    for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
-           for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    for j in range(args.steps):
-        step(args.warmup + j, evs[j])
+    for j in range(steps):
+        step(warmup + j, evs[j])
     t_end.record()
     torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    dec_avg_ms = float(np.mean([a.elapsed_time(c) for a, b, c in evs]))
-    split_avg_ms = float(np.mean([a.elapsed_time(b) for a, b, c in evs]))
-    merge_avg_ms = float(np.mean([b.elapsed_time(c) for a, b, c in evs]))
-
-    # algorithmic bytes of the average decode launch (lengths grow during the run)
-    byts = []
-    for j in range(args.steps):
-        s = args.warmup + j
-        k = s // args.layers
-        byts.append(algorithmic_bytes(w, [int(L) + k for L in lens0]))
+    ms_step = t_start.elapsed_time(t_end) / steps
+    dec_ms = float(np.mean([a.elapsed_time(c) for a, b, c in evs]))
+    split_ms = float(np.mean([a.elapsed_time(b) for a, b, c in evs]))
+    merge_ms = float(np.mean([b.elapsed_time(c) for a, b, c in evs]))
+    # algorithmic bytes of the average split launch (lengths grow during the run)
+    byts = [algorithmic_bytes(w, [int(L) + (warmup + j) // n_layers for L in lens0])
+            for j in range(steps)]
     bytes_per_launch = float(np.mean(byts))
-    achieved = bytes_per_launch / (split_avg_ms * 1e-3) / 1e9
-    src_hash = decode_source_hash()
-    traffic = read_traffic(src_hash)
+    return {"w": w, "lens0": lens0, "n": n, "ms_step": ms_step, "dec_ms": dec_ms,
+            "split_ms": split_ms, "merge_ms": merge_ms, "bytes": bytes_per_launch,
+            "setup_s": setup_s}
 
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--config", default="c3_bs64")
+    ap.add_argument("--bs1-config", default="c2_qwen3_8b_bs1",
+                    help="the bs1 workload reported next to the headline ('' to skip)")
+    ap.add_argument("--bs1-layers", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="only run a device copy of this many bytes (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (the decode path shards by "
+              "sequence / KV head with no exchange; multi-GPU runs are not part of it)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    from synth import get
+
+    m = measure(get(args.config), args.layers, args.steps, args.warmup)
+    w, lens0, n = m["w"], m["lens0"], m["n"]
+    achieved = m["bytes"] / (m["split_ms"] * 1e-3) / 1e9
+    src_hash = decode_source_hash()
     res = {
         "metric": "INT2 paged decode-attn tokens/s + achieved HBM GB/s vs peak (bs1, bs64)",
-        "value": n / (ms_step * 1e-3),
+        "value": n / (m["ms_step"] * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": m["ms_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -257,19 +301,31 @@ def main():
             "windows": [w.s_sink, w.s_keep, w.s_flush], "context_min": int(lens0.min()),
             "context_max": int(lens0.max()), "layers_cycled": args.layers,
             "step": "rotate_quant_append(1 token/seq) + int2_decode_partials + int2_decode_merge",
-            "decode_ms": dec_avg_ms, "decode_split_ms": split_avg_ms,
-            "decode_merge_ms": merge_avg_ms, "append_ms": ms_step - dec_avg_ms,
-            "decode_call_GBs": bytes_per_launch / (dec_avg_ms * 1e-3) / 1e9,
+            "decode_ms": m["dec_ms"], "decode_split_ms": m["split_ms"],
+            "decode_merge_ms": m["merge_ms"], "append_ms": m["ms_step"] - m["dec_ms"],
+            "decode_call_GBs": m["bytes"] / (m["dec_ms"] * 1e-3) / 1e9,
             "decode_kernel_source": src_hash,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-            "kernel": "int2_decode_kernel", "algorithmic_bytes_per_launch": bytes_per_launch,
+            "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic(src_hash),
+            "kernel": "int2_decode_kernel", "algorithmic_bytes_per_launch": m["bytes"],
         },
         "cpu_baseline": None,
-        "setup_s": setup_s,
+        "setup_s": m["setup_s"],
     }
+    if args.bs1_config:
+        # bs1 latency: enough layer copies that the cache is not MALL-resident
+        b = measure(get(args.bs1_config), args.bs1_layers, args.steps, args.warmup)
+        res["bs1"] = {
+            "workload": f"{b['w'].name}: {b['w'].description}",
+            "context": int(b["lens0"][0]), "layers_cycled": args.bs1_layers,
+            "ms_per_step": b["ms_step"], "tokens_per_s": b["n"] / (b["ms_step"] * 1e-3),
+            "decode_ms": b["dec_ms"], "decode_split_ms": b["split_ms"],
+            "decode_merge_ms": b["merge_ms"], "append_ms": b["ms_step"] - b["dec_ms"],
+            "split_GBs": b["bytes"] / (b["split_ms"] * 1e-3) / 1e9,
+            "algorithmic_bytes_per_launch": b["bytes"],
+        }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, lens0, seconds=args.cpu_seconds)
     print(json.dumps(res), flush=True)
