@@ -21,7 +21,7 @@ constexpr int kMaxSink = 4096, kMaxKeep = 8192, kMaxFlush = 8192;
 constexpr int kMaxPagesPerSeq = 65536;
 static_assert((kMaxPagesPerSeq / 2) +
                       kWinCost * (kMaxSink / kPage + (kMaxKeep + kMaxFlush) / kPage + 1) <=
-                  (int64_t)kMaxSplits * kMaxPairsPerSplit,
+                  (int64_t)kMaxSplits * (kMaxPairsPerSplit - 1),
               "decode work of the largest row must fit the split limits");
 // Split launch sizing: the work-groups of a launch fill this share of the
 // resident slots, so none waits for a second round.
@@ -73,10 +73,10 @@ int64_t max_row_cost(const oscar_kv_config& c) {
   return pairs + kWinCost * wu;
 }
 
-// Fewest splits that keep every split within kMaxPairsPerSplit units (the
-// page-id list a work-group stages in LDS).
+// Fewest splits that keep every split within kMaxPairsPerSplit - 1 units
+// (the page-id list a work-group stages in LDS; the planner's largest quota).
 int min_splits(const oscar_kv_config& c) {
-  return (int)std::max<int64_t>(1, (max_row_cost(c) + kMaxPairsPerSplit - 1) / kMaxPairsPerSplit);
+  return (int)std::max<int64_t>(1, (max_row_cost(c) + kMaxPairsPerSplit - 2) / (kMaxPairsPerSplit - 1));
 }
 
 // Most splits per (sequence, KV head, pass) the workspace is sized for:
@@ -91,13 +91,16 @@ int max_splits(const oscar_kv_config& c, int n_seqs) {
   return (int)std::max<long long>(s, min_splits(c));
 }
 
-// Split partial records of one decode launch (at most kMaxScanSeqs sequences).
+// Split partial records of one decode launch (at most kMaxScanSeqs
+// sequences), then, when rows may have more than kMergeDirect splits, the
+// chunk records of the first merge launch.
 size_t partials_bytes(const oscar_kv_config& c, int n_seqs) {
   const DecodePlan p = head_passes(c);
-  const size_t rec = (size_t)p.hp * kD + 2 * p.hp;
+  const size_t rec = (size_t)rec_words(p.hp);
   const int ns = std::min(std::max(1, n_seqs), kMaxScanSeqs);
-  return align_up((size_t)ns * c.num_kv_heads * p.passes * max_splits(c, ns) * rec *
-                  sizeof(float));
+  const int cap = max_splits(c, ns);
+  const size_t per_row = (size_t)cap + (cap > kMergeDirect ? (cap + kMergeChunk - 1) / kMergeChunk : 0);
+  return align_up((size_t)ns * c.num_kv_heads * p.passes * per_row * rec * sizeof(float));
 }
 
 size_t staging_bytes(const oscar_kv_config& c, int64_t n_tok) {
@@ -382,6 +385,9 @@ int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_
   const int64_t rows = (int64_t)(c.num_kv_heads / plan.wh) * plan.passes;
   const int64_t slots =
       std::max<int64_t>(1, (int64_t)cus * decode_slots_per_cu(a, plan) * kFillPercent / 100);
+  // Every launch keeps to the split limit the workspace is sized for (that
+  // of a full launch), so a short last launch fits in it too.
+  const int cap = max_splits(c, std::min(n_seqs, kMaxScanSeqs));
   // Launches of at most kMaxScanSeqs sequences, in stream order.
   for (int s0 = 0; s0 < n_seqs; s0 += kMaxScanSeqs) {
     const int ns = std::min(kMaxScanSeqs, n_seqs - s0);
@@ -396,7 +402,6 @@ int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_
       total += cost[i];
       max_cost = std::max(max_cost, cost[i]);
     }
-    const int cap = max_splits(c, ns);
     // quota in 1/16 units; at most 255 pairs per split (the LDS page list)
     auto splits_of = [&](int64_t c16, int64_t q) { return std::max<int64_t>(1, (16 * c16 + q - 1) / q); };
     auto items_of = [&](int64_t q) {
@@ -418,6 +423,7 @@ int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_
     }
     int64_t smax = 1;
     for (int i = 0; i < ns; ++i) smax = std::max<int64_t>(smax, splits_of(cost[i], quota));
+    if (smax > cap) return OSCAR_ERR_CAPACITY;   // unreachable: cap >= min_splits
     plan.quota = (int)quota;
     plan.smax = (int)smax;
     plan.grid = (int)items_of(quota);

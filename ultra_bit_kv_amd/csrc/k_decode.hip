@@ -155,7 +155,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
                                                               int passes, int smax,
                                                               const uint16_t* __restrict__ q_rot,
                                                               float* __restrict__ partials) {
-  constexpr int PW = HP * kD + 2 * HP;   // floats per partial record
+  constexpr int PW = rec_words(HP);   // floats per partial record
   constexpr int NT = 64 * WH;
   __shared__ int s_pages[kMaxWgPages];
   __shared__ int s_wsum[WH];
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     rec[HP + hl] = st.l;
   }
   if (bval) {   // lane holds channels 32qd .. 32qd+31 of its head, in its own group
-    float* o = rec + 2 * HP + hl * kD + 32 * qd;
+    float* o = rec + rec_o_offset(HP) + hl * kD + 32 * qd;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float4_t lo = {acc[0][r] + st.z, acc[1][r] + st.z, acc[2][r] + st.z, acc[3][r] + st.z};
@@ -499,160 +499,172 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   }
 }
 
-// Log-sum-exp merge of the split partials, then o = o' . R_V^T.
-//
-// Work-group = (KV head, pass, block of SB sequences, half of the output
-// columns); its 16 rows are the (sequence, query head) pairs of the block,
-// which is exactly one MFMA tile of rows.  All global loads (the half of R_V,
-// every split's max and sum, the first kChunk split outputs of each row
-// channel) are issued before the first wait; both column halves merge the
-// same rows.  The un-rotation runs on the fp32 matrix cores: o'[16 x 128]
-// times the R_V^T columns of the half, with those R_V rows staged in LDS
-// (padded to 132 floats so the operand reads of a wave fall in distinct
-// banks).
+// Log-sum-exp merge of partial records (WUSH-KV notes, "method step
+// details": split outputs are combined by their maxima and sums).  A record
+// holds, per head, m (log2 domain), l = sum 2^(x - m) and the unnormalized
+// o' = sum 2^(x - m) v'; two records combine exactly as
+//   M = max(m1, m2), l = l1 2^(m1 - M) + l2 2^(m2 - M), o' likewise.
+
+// First of two merge launches for rows with many splits: work-group =
+// (sequence, KV head, pass, chunk of kMergeChunk splits); thread = (head of
+// the pass, 4 channels).  Every thread loads its head's maxima and sums
+// itself, so the kernel has no LDS and no barrier.  Output: one record per
+// chunk, in the same layout, with row stride smax2.
 template <int HP>
-__global__ __launch_bounds__(256) void merge_unrotate_kernel(CacheArgs c, SeqArgs s, int quota,
-                                                             int passes, int smax, int sb,
-                                                             const float* __restrict__ partials,
+__global__ __launch_bounds__(HP * 32 < 64 ? 64 : HP * 32) void merge_chunks_kernel(
+    CacheArgs c, SeqArgs s, int quota, int passes, int smax, int smax2,
+    const float* __restrict__ partials, float* __restrict__ merged) {
+  constexpr int W = rec_words(HP), OO = rec_o_offset(HP);
+  const int x = blockIdx.x;
+  const int pass = x % passes, h = (x / passes) % c.hkv, i = x / (passes * c.hkv);
+  const int nh = min(HP, c.g - pass * HP);
+  const int r = threadIdx.x >> 5, c4 = threadIdx.x & 31;
+  const int slot = s.slots[i], len = s.lens[i];
+  const bool ok = slot >= 0 && slot < c.max_seqs && len >= 1;
+  const int ns = decode_splits(decode_work(ok ? len : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap),
+                               quota, smax);
+  const int sp0 = blockIdx.y * kMergeChunk;
+  if (r >= nh || sp0 >= ns) return;
+  const int cnt = min(kMergeChunk, ns - sp0);
+  const size_t row = ((size_t)i * c.hkv + h) * passes + pass;
+  const float* rec = partials + (row * smax + sp0) * W;
+  float m[kMergeChunk], l[kMergeChunk];
+  float4_t o[kMergeChunk];
+#pragma unroll
+  for (int j = 0; j < kMergeChunk; ++j) {
+    const float* rj = rec + (size_t)(j < cnt ? j : 0) * W;
+    m[j] = rj[r];
+    l[j] = rj[HP + r];
+    o[j] = *(const float4_t*)(rj + OO + r * kD + 4 * c4);
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kMergeChunk; ++j)
+    if (j < cnt) M = fmaxf(M, m[j]);
+  float L = 0.0f;
+  float4_t O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMergeChunk; ++j) {
+    const float w = (j < cnt && m[j] != kNegInf) ? __builtin_amdgcn_exp2f(m[j] - M) : 0.0f;
+    L = __builtin_fmaf(w, l[j], L);
+    O[0] = __builtin_fmaf(w, o[j][0], O[0]);
+    O[1] = __builtin_fmaf(w, o[j][1], O[1]);
+    O[2] = __builtin_fmaf(w, o[j][2], O[2]);
+    O[3] = __builtin_fmaf(w, o[j][3], O[3]);
+  }
+  float* dst = merged + (row * smax2 + blockIdx.y) * W;
+  if (c4 == 0) {
+    dst[r] = M;
+    dst[HP + r] = L;
+  }
+  *(float4_t*)(dst + OO + r * kD + 4 * c4) = O;
+}
+
+// Final merge, then o = o' . R_V^T.
+//
+// Work-group = (KV head, pass, block of SB sequences): its 16 rows are the
+// (sequence, query head) pairs of the block, one MFMA tile of rows, and all
+// 128 output columns.  Thread = (row, 4 channels): it folds the row's
+// records in rounds of 8 with a running maximum, loading the maxima and
+// sums itself.  The merged o' rows go to LDS; wave w then computes output
+// columns 16w .. 16w+15 on the fp32 matrix cores, with lane (i, q) holding
+// R_V[16w + i][32q .. 32q+31] in registers (loaded at entry, before any
+// wait), so the contraction index of step (u, e) is k = 32q + 4u + e.
+template <int HP>
+__global__ __launch_bounds__(512) void merge_unrotate_kernel(CacheArgs c, SeqArgs s, int quota,
+                                                             int passes, int smax, int chunk,
+                                                             int stride, int sb,
+                                                             const float* __restrict__ recs,
                                                              float* __restrict__ out) {
-  constexpr int PW = HP * kD + 2 * HP;
-  constexpr int kChunk = 8;                      // split outputs per channel per load round
-  constexpr int kRows = 16;
-  constexpr int kLd = kD + 4;
-  __shared__ float rv[kD / 2][kLd];   // the half of R_V's rows (output columns) of this work-group
-  __shared__ float fin[kRows][kLd];
-  __shared__ float s_M[kRows], s_L[kRows];
-  __shared__ int s_ns[kRows];
-  // per-split maxima and sums, [kRows][smax] each, in dynamic LDS
-  extern __shared__ float s_dyn[];
-  float* s_m = s_dyn;
-  float* s_l = s_dyn + (size_t)kRows * smax;
-  const int tid = threadIdx.x;
+  constexpr int W = rec_words(HP), OO = rec_o_offset(HP);
+  constexpr int kRound = 8;
+  __shared__ float fin[16][kD + 4];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int li = lane & 15, kq = lane >> 4;
   const int h = blockIdx.x / passes, pass = blockIdx.x % passes;
   const int nh = min(HP, c.g - pass * HP);
   const int s0 = blockIdx.y * sb;
-  const int jh = 64 * blockIdx.z;   // output columns jh .. jh + 63
 
-  // row r <-> (sequence s0 + r / nh, head hh = r % nh)
-  auto row_seq = [&](int r) { return s0 + r / nh; };
-  auto row_valid = [&](int r) { return r < sb * nh && row_seq(r) < s.n_seqs; };
-  auto rec_of = [&](int r) {
-    return partials + (((size_t)row_seq(r) * c.hkv + h) * passes + pass) * smax * PW;
-  };
-  // ---- issue every load first: R_V, the split maxima / sums and the first
-  // kChunk split outputs of each (row, channel).  Records exist for all smax
-  // splits of every row, so the loads need not wait for the split counts.
-  const float4* rg = (const float4*)(c.r_v + ((size_t)h * kD + jh) * kD);
-  float4 rvv[kD * kD / 8 / 256];
+  const float4_t* rg = (const float4_t*)(c.r_v + ((size_t)h * kD + 16 * wave + li) * kD + 32 * kq);
+  float4_t rb[8];
 #pragma unroll
-  for (int t = 0; t < kD * kD / 8 / 256; ++t) rvv[t] = rg[tid + 256 * t];
-  const int nml = kRows * smax;
-  const int t_ml = tid < nml ? tid : 0;
-  float ml_m = 0.0f, ml_l = 0.0f;
-  if (tid < nml && row_valid(t_ml / smax)) {
-    const float* rec = rec_of(t_ml / smax) + (size_t)(t_ml % smax) * PW;
-    ml_m = rec[(t_ml / smax) % nh];
-    ml_l = rec[HP + (t_ml / smax) % nh];
-  }
-  constexpr int kPer = kRows * kD / 256;   // (row, channel) pairs per thread
-  const int ch = tid % kD;
-  const int jmax = smax < kChunk ? smax : kChunk;
-  float ov[kPer][kChunk];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int r = tid / kD + 2 * k;
-    const bool rv_ok = row_valid(r);
-    const float* o = rec_of(rv_ok ? r : 0) + 2 * HP + (r % nh) * kD + ch;
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) ov[k][j] = (rv_ok && j < jmax) ? o[(size_t)j * PW] : 0.0f;
-  }
-  int my_ns = 0;
-  if (tid < kRows && row_valid(tid)) {
-    const int i = row_seq(tid);
-    const int slot = s.slots[i];
-    const int len = s.lens[i];
+  for (int u = 0; u < 8; ++u) rb[u] = rg[u];
+
+  const int r = t >> 5, c4 = t & 31;
+  const int i = s0 + r / nh;
+  const bool valid = r < sb * nh && i < s.n_seqs;
+  int nrec = 0;
+  const float* rec = recs;
+  if (valid) {
+    const int slot = s.slots[i], len = s.lens[i];
     const bool ok = slot >= 0 && slot < c.max_seqs && len >= 1;
-    my_ns = decode_splits(decode_work(ok ? len : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap),
-                          quota, smax);
+    const int ns = decode_splits(
+        decode_work(ok ? len : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap), quota, smax);
+    nrec = (ns + chunk - 1) / chunk;
+    rec = recs + (((size_t)i * c.hkv + h) * passes + pass) * stride * W;
   }
+  const int hr = r % nh;
+  float M = kNegInf, L = 0.0f;
+  float4_t O = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < nrec; j0 += kRound) {
+    float m[kRound], l[kRound];
+    float4_t o[kRound];
 #pragma unroll
-  for (int t = 0; t < kD * kD / 8 / 256; ++t) {
-    const int e = 4 * (tid + 256 * t);
-    *(float4*)(&rv[e / kD][e % kD]) = rvv[t];
-  }
-  if (tid < nml) {
-    s_m[tid] = ml_m;
-    s_l[tid] = ml_l;
-  }
-  for (int t = tid + 256; t < nml; t += 256) {   // more than 16 splits: remaining maxima / sums
-    const int r = t / smax, sp = t % smax;
-    float m = 0.0f, l = 0.0f;
-    if (row_valid(r)) {
-      const float* rec = rec_of(r) + (size_t)sp * PW;
-      m = rec[r % nh];
-      l = rec[HP + r % nh];
+    for (int j = 0; j < kRound; ++j) {
+      const float* rj = rec + (size_t)(j0 + j < nrec ? j0 + j : j0) * W;
+      m[j] = rj[hr];
+      l[j] = rj[HP + hr];
+      o[j] = *(const float4_t*)(rj + OO + hr * kD + 4 * c4);
     }
-    s_m[t] = m;
-    s_l[t] = l;
-  }
-  if (tid < kRows) s_ns[tid] = my_ns;
-  __syncthreads();
-  if (tid < kRows) {   // log-sum-exp of row tid over its splits
-    const int ns = s_ns[tid];
-    float M = kNegInf;
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, s_m[tid * smax + sp]);
-    float L = 0.0f;
-    for (int sp = 0; sp < ns; ++sp) {   // the split's weight replaces its maximum
-      const float wt = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s_m[tid * smax + sp] - M);
-      L += wt * s_l[tid * smax + sp];
-      s_m[tid * smax + sp] = wt;
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < kRound; ++j)
+      if (j0 + j < nrec) Mn = fmaxf(Mn, m[j]);
+    const float sc = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+    L *= sc;
+    O[0] *= sc;
+    O[1] *= sc;
+    O[2] *= sc;
+    O[3] *= sc;
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) {
+      const float w = (j0 + j < nrec && m[j] != kNegInf) ? __builtin_amdgcn_exp2f(m[j] - Mn) : 0.0f;
+      L = __builtin_fmaf(w, l[j], L);
+      O[0] = __builtin_fmaf(w, o[j][0], O[0]);
+      O[1] = __builtin_fmaf(w, o[j][1], O[1]);
+      O[2] = __builtin_fmaf(w, o[j][2], O[2]);
+      O[3] = __builtin_fmaf(w, o[j][3], O[3]);
     }
-    s_M[tid] = M;
-    s_L[tid] = L;
+    M = Mn;
   }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int r = tid / kD + 2 * k;
-    const int ns = s_ns[r];
-    auto weight = [&](int sp) { return s_m[r * smax + sp]; };
-    float O = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j)
-      if (j < ns) O = __builtin_fmaf(weight(j), ov[k][j], O);
-    if (ns > kChunk) {   // long contexts: more load rounds
-      const float* o = rec_of(r) + 2 * HP + (r % nh) * kD + ch;
-      for (int sp0 = kChunk; sp0 < ns; sp0 += kChunk) {
-        float v[kChunk];
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) v[j] = sp0 + j < ns ? o[(size_t)(sp0 + j) * PW] : 0.0f;
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j)
-          if (sp0 + j < ns) O = __builtin_fmaf(weight(sp0 + j), v[j], O);
-      }
-    }
-    fin[r][ch] = ns > 0 ? O / s_L[r] : 0.0f;
+  float4_t f = {0.f, 0.f, 0.f, 0.f};
+  if (nrec > 0) {
+    f[0] = O[0] / L;
+    f[1] = O[1] / L;
+    f[2] = O[2] / L;
+    f[3] = O[3] / L;
   }
+  *(float4_t*)(&fin[r][4 * c4]) = f;
   __syncthreads();
 
-  // ---- o = o' . R_V^T on the fp32 matrix cores: wave w computes columns jh + 16w .. +15
-  const int lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 15, kq = lane >> 4;
-  float4_t acc0 = {0.f, 0.f, 0.f, 0.f};
-  const int j0 = 16 * wave;
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kb = 0; kb < kD / 4; ++kb)
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(fin[li][4 * kb + kq], rv[j0 + li][4 * kb + kq], acc0,
-                                                0, 0, 0);
+  for (int u = 0; u < 8; ++u) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fin[li][32 * kq + 4 * u + e], rb[u][e], acc, 0, 0,
+                                                 0);
+  }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int r = 4 * kq + v;   // output row of this lane's v-th value
-    if (!row_valid(r)) continue;
-    const int i = row_seq(r);
-    const int slot = s.slots[i];
-    if (slot < 0 || slot >= c.max_seqs || s.lens[i] < 1) continue;
-    float* o = out + ((size_t)i * c.hq + (size_t)h * c.g + pass * HP + r % nh) * kD;
-    o[jh + j0 + li] = acc0[v];
+    const int rr = 4 * kq + v;   // output row of this lane's v-th value
+    const int ii = s0 + rr / nh;
+    if (rr >= sb * nh || ii >= s.n_seqs) continue;
+    const int slot = s.slots[ii];
+    if (slot < 0 || slot >= c.max_seqs || s.lens[ii] < 1) continue;
+    float* o = out + ((size_t)ii * c.hq + (size_t)h * c.g + pass * HP + rr % nh) * kD;
+    o[16 * wave + li] = acc[v];
   }
 }
 
@@ -682,11 +694,24 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
   }
   if (phases & kDecodeMerge) {
     const int nh_full = c.g < HP ? c.g : HP;
-    const int sb = 16 / nh_full;   // sequences per merge work-group (16 rows)
-    dim3 mgrid(c.hkv * plan.passes, (s.n_seqs + sb - 1) / sb, 2);
-    const size_t dyn = 2 * sizeof(float) * 16 * (size_t)plan.smax;
-    hipLaunchKernelGGL((merge_unrotate_kernel<HP>), mgrid, dim3(256), dyn, stream, c, s,
-                       plan.quota, plan.passes, plan.smax, sb, partials, out);
+    const int sb = 16 / nh_full;   // sequences per final-merge work-group (16 rows)
+    const float* recs = partials;
+    int chunk = 1, stride = plan.smax;
+    if (plan.smax > kMergeDirect) {   // many splits: fold chunks of them first, in parallel
+      const int smax2 = (plan.smax + kMergeChunk - 1) / kMergeChunk;
+      float* merged = partials + (size_t)s.n_seqs * c.hkv * plan.passes * plan.smax * rec_words(HP);
+      const dim3 g1(s.n_seqs * c.hkv * plan.passes, smax2);
+      hipLaunchKernelGGL((merge_chunks_kernel<HP>), g1, dim3(HP * 32 < 64 ? 64 : HP * 32), 0,
+                         stream, c, s, plan.quota, plan.passes, plan.smax, smax2, partials, merged);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      recs = merged;
+      chunk = kMergeChunk;
+      stride = smax2;
+    }
+    const dim3 mgrid(c.hkv * plan.passes, (s.n_seqs + sb - 1) / sb);
+    hipLaunchKernelGGL((merge_unrotate_kernel<HP>), mgrid, dim3(512), 0, stream, c, s, plan.quota,
+                       plan.passes, plan.smax, chunk, stride, sb, recs, out);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -90,6 +90,15 @@ constexpr int kWinCost = 3;
 constexpr int kMaxSplits = 256;            // splits per (sequence, row), merge LDS bound
 constexpr int kMaxPairsPerSplit = 256;     // page ids staged per work-group
 constexpr int kMaxScanSeqs = 2048;         // sequences per decode launch
+constexpr int kMergeDirect = 32;           // most splits per row merged by one launch
+constexpr int kMergeChunk = 16;            // splits folded into one record by the first of two merge launches
+
+// Partial record of a (sequence, KV head, pass, split): the log2-domain
+// maxima and the sums of the pass's HP query heads, then their
+// unnormalized o' rows, which start 16 bytes into the record and stay
+// 16-byte aligned (the record length is a multiple of 4 floats).
+__host__ __device__ constexpr int rec_o_offset(int hp) { return 2 * hp < 4 ? 4 : 2 * hp; }
+__host__ __device__ constexpr int rec_words(int hp) { return rec_o_offset(hp) + hp * kD; }
 
 struct DecodeWork {
   int n_pairs;                   // INT2 page pairs
