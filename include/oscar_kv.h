@@ -220,6 +220,49 @@ int oscar_int2_decode_merge(const oscar_kv_cache* cache, int32_t n_seqs,
 int oscar_dequant(const oscar_kv_cache* cache, int32_t seq_slot, int32_t seq_len,
                   int32_t tok_begin, int32_t tok_end, float* k_out, float* v_out, void* stream);
 
+/* ---- Plain BF16 paged cache: the uncompressed comparison point ----------
+ * [OSCAR abstract and s5: KV memory and throughput against BF16; OScaR
+ * "efficiency": decode latency against BF16 FlashDecoding]
+ * No rotation, no windows: every token of a row sits in its logical page
+ * m = p / 16, slot p % 16, and the kernel computes
+ *   out = softmax(q K^T / sqrt(128)) V
+ * with the same split-K / log-sum-exp scheme as oscar_int2_decode_attn.
+ *  pages: bf16 [num_pages][Hkv][2][16][128]; part 0 holds the K rows of the
+ *         page's 16 slots (row-major, element 128 t + c), part 1 the V rows
+ *         in the same order.  Slots at or beyond a row's length are ignored.
+ *  block_table: int32 [max_seqs][max_pages_per_seq]: physical page of logical
+ *         page m; entries outside [0, num_pages) are skipped (their tokens
+ *         get zero weight). */
+typedef struct {
+  int32_t head_dim;           /* must be 128 */
+  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads, Hq / Hkv <= 256 */
+  int32_t num_kv_heads;       /* Hkv, 1 .. 64 */
+  int32_t page_size;          /* must be 16 */
+  int32_t max_seqs;           /* cache rows */
+  int32_t max_pages_per_seq;  /* block table width, <= 65536 */
+  int32_t num_pages;          /* physical pages in the pool */
+  const uint16_t* pages;      /* bf16 [num_pages][Hkv][2][16][128] */
+  const int32_t* block_table; /* [max_seqs][max_pages_per_seq] */
+} oscar_bf16_cache;
+
+/* Workspace bytes for oscar_bf16_paged_decode_attn with at most n_seqs
+ * sequences per call (0 for an invalid cache description). */
+size_t oscar_bf16_workspace_size(const oscar_bf16_cache* cache, int32_t n_seqs);
+
+/* Decode attention of one query per sequence over a BF16 paged cache row.
+ *  seq_slots[i], seq_lens[i]  cache row and its token count (>= 1); host and
+ *                             device copies as for oscar_int2_decode_attn
+ *  q      bf16 [n_seqs][Hq][128] queries (query head hq reads KV head hq / g)
+ *  out    fp32 [n_seqs][Hq][128]
+ * Errors: OSCAR_ERR_SHAPE / CAPACITY for an invalid description, slot or
+ * length, OSCAR_ERR_ARG for misaligned pointers or n_seqs outside
+ * [1, max_seqs], OSCAR_ERR_WORKSPACE, OSCAR_ERR_DEVICE, OSCAR_ERR_HIP. */
+int oscar_bf16_paged_decode_attn(const oscar_bf16_cache* cache, int32_t n_seqs,
+                                 const int32_t* seq_slots_host, const int32_t* seq_lens_host,
+                                 const int32_t* seq_slots, const int32_t* seq_lens,
+                                 const uint16_t* q, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Text for a status code (static storage). */
 const char* oscar_status_string(int status);
 

@@ -185,3 +185,62 @@ def test_dequant_argument_checks(L):
     assert f(ctypes.byref(cache), 0, 100, 0, 101, DUMMY, DUMMY, None) == -10
     assert f(ctypes.byref(cache), 5, 100, 0, 10, DUMMY, DUMMY, None) == -6
     assert f(ctypes.byref(cache), 0, 100, 0, 10, None, DUMMY, None) == -1
+
+
+# ---- plain BF16 paged cache (the uncompressed comparison point) ----------
+
+def bcache(**kw):
+    b = _lib.Bf16Cache(128, 32, 8, 16, 4, 100, 400, 0x1000, 0x1000)
+    for k, v in kw.items():
+        setattr(b, k, v)
+    return b
+
+
+def bdecode(L, b, slots, lens, ws_bytes=1 << 40, q=DUMMY, out=DUMMY, n=None):
+    keep = [_i32(slots), _i32(lens)]
+    return L.oscar_bf16_paged_decode_attn(ctypes.byref(b), len(slots) if n is None else n,
+                                          keep[0][1], keep[1][1], DUMMY, DUMMY, q, out, DUMMY,
+                                          ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw, status", [
+    ({"head_dim": 64}, -2), ({"page_size": 8}, -2), ({"num_kv_heads": 0}, -2),
+    ({"num_kv_heads": 65}, -2), ({"num_q_heads": 30}, -2),
+    ({"num_q_heads": 512, "num_kv_heads": 1}, -2),
+    ({"max_seqs": 0}, -6), ({"max_pages_per_seq": 65537}, -6), ({"num_pages": -1}, -6),
+])
+def test_bf16_description_checks(L, kw, status):
+    b = bcache(**kw)
+    assert bdecode(L, b, [0], [10]) == status
+    assert L.oscar_bf16_workspace_size(ctypes.byref(b), 4) == 0
+
+
+def test_bf16_workspace_size(L):
+    # g = 4 -> 4 heads per pass, one pass; a record is 8 + 4 * 128 floats.
+    # 16K records per launch: n = 4 -> 32 rows -> 256 splits (+16 chunk records)
+    b = bcache()
+    rec = 8 + 4 * 128
+    for n, cap in ((4, 256), (64, 32), (2048, 1)):
+        rows = n * 8
+        per_row = cap + (-(-cap // 16) if cap > 32 else 0)
+        want = -(-(rows * per_row * rec * 4) // 256) * 256
+        assert L.oscar_bf16_workspace_size(ctypes.byref(b), n) == want, n
+    # the largest row always fits: 65536 pages = 32768 pairs needs 129 splits
+    big = bcache(max_pages_per_seq=65536, max_seqs=4096)
+    assert L.oscar_bf16_workspace_size(ctypes.byref(big), 2048) >= 2048 * 8 * 129 * rec * 4
+
+
+def test_bf16_decode_argument_checks(L):
+    b = bcache()
+    assert bdecode(L, b, [0], [0]) == -10                              # empty row
+    assert bdecode(L, b, [9], [10]) == -6                              # slot
+    assert bdecode(L, b, [0], [100 * 16 + 1]) == -6                    # more pages than the row
+    assert bdecode(L, b, [0], [10], q=None) == -1
+    assert bdecode(L, b, [0], [10], out=None) == -1
+    assert bdecode(L, b, [0], [10], ws_bytes=100) == -7
+    assert bdecode(L, b, [0, 1, 2, 3, 0], [5] * 5) == -10              # n_seqs > max_seqs
+    assert bdecode(L, b, [0], [10], n=0) == -10
+    bad = ctypes.c_void_p(DUMMY.value + 4)
+    assert bdecode(L, b, [0], [10], q=bad) == -10
+    assert bdecode(L, bcache(num_pages=0), [0], [10]) == -6            # no pages to read
+    assert bdecode(L, b, [0, 3], [100 * 16, 1]) in (-9, -8, 0)         # valid: device check

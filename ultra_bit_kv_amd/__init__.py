@@ -5,5 +5,5 @@ paged GQA decode attention.  The compute runs in the HIP library
 Python binding.
 """
 
-from .cache import OscarKVCache, SeqBatch, as_bf16, bf16_bits  # noqa: F401
+from .cache import BF16PagedCache, OscarKVCache, SeqBatch, as_bf16, bf16_bits  # noqa: F401
 from ._lib import lib, OscarError, LIB_PATH  # noqa: F401

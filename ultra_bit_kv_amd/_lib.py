@@ -35,6 +35,12 @@ class KvCache(ctypes.Structure):
                 ("r_k", c_p), ("r_v", c_p)]
 
 
+class Bf16Cache(ctypes.Structure):
+    _fields_ = [("head_dim", c_i32), ("num_q_heads", c_i32), ("num_kv_heads", c_i32),
+                ("page_size", c_i32), ("max_seqs", c_i32), ("max_pages_per_seq", c_i32),
+                ("num_pages", c_i32), ("pages", c_p), ("block_table", c_p)]
+
+
 STATUS = {0: "OSCAR_OK", -1: "OSCAR_ERR_NULL", -2: "OSCAR_ERR_SHAPE", -3: "OSCAR_ERR_GROUP",
           -4: "OSCAR_ERR_CLIP", -5: "OSCAR_ERR_WINDOW", -6: "OSCAR_ERR_CAPACITY",
           -7: "OSCAR_ERR_WORKSPACE", -8: "OSCAR_ERR_DEVICE", -9: "OSCAR_ERR_HIP",
@@ -57,6 +63,9 @@ _PROTOS = {
     "oscar_int2_decode_merge": (c_i32, [ctypes.POINTER(KvCache), c_i32, c_p, c_p, c_p, c_p, c_p,
                                         c_p, c_size, c_p]),
     "oscar_dequant": (c_i32, [ctypes.POINTER(KvCache), c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p]),
+    "oscar_bf16_workspace_size": (c_size, [ctypes.POINTER(Bf16Cache), c_i32]),
+    "oscar_bf16_paged_decode_attn": (c_i32, [ctypes.POINTER(Bf16Cache), c_i32, c_p, c_p, c_p, c_p,
+                                             c_p, c_p, c_p, c_size, c_p]),
     "oscar_status_string": (ctypes.c_char_p, [c_i32]),
 }
 

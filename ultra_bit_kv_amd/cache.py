@@ -10,7 +10,7 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import KvCache, KvConfig, check, lib, MAX_KV_HEADS
+from ._lib import Bf16Cache, KvCache, KvConfig, check, lib, MAX_KV_HEADS
 
 D = 128
 PAGE = 16
@@ -208,3 +208,46 @@ class OscarKVCache:
         per = 2 * PAGE * D
         off = (slot * self.hkv + h) * nb * per
         return self.win[off:off + nb * per].cpu().numpy().view(np.uint16).reshape(nb, per)
+
+
+class BF16PagedCache:
+    """Device buffers of a plain BF16 paged KV cache (one layer) and
+    oscar_bf16_paged_decode_attn on it: the uncompressed comparison point.
+
+    ``pages`` is bf16 [num_pages, Hkv, 2, 16, 128] (part 0 = K rows of the
+    page's 16 slots, part 1 = V rows); the caller writes it.  Token p of a
+    row lives in logical page p // 16, slot p % 16."""
+
+    def __init__(self, *, num_q_heads, num_kv_heads, max_seqs, max_pages_per_seq, num_pages,
+                 block_table, device="cuda"):
+        self.device = device
+        self.pages = torch.zeros((max(1, num_pages), num_kv_heads, 2, PAGE, D), dtype=torch.bfloat16,
+                                 device=device)
+        bt = np.zeros((max_seqs, max(1, max_pages_per_seq)), np.int32)
+        src = np.asarray(block_table, np.int32)
+        bt[:src.shape[0], :src.shape[1]] = src
+        self.block_table = torch.from_numpy(bt).to(device)
+        self.st = Bf16Cache(D, num_q_heads, num_kv_heads, PAGE, max_seqs, max_pages_per_seq,
+                            num_pages, self.pages.data_ptr(), self.block_table.data_ptr())
+        self.hq, self.hkv = num_q_heads, num_kv_heads
+        self.workspace = None
+
+    def workspace_for(self, n_seqs):
+        need = lib().oscar_bf16_workspace_size(ctypes.byref(self.st), int(n_seqs))
+        if need == 0:
+            check(-2, "oscar_bf16_workspace_size")
+        if self.workspace is None or self.workspace.numel() < need:
+            self.workspace = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        return self.workspace
+
+    def decode(self, batch, q, out=None):
+        """oscar_bf16_paged_decode_attn: fp32 [n, Hq, 128]."""
+        assert q.dtype == torch.bfloat16 and q.shape == (batch.n, self.hq, D)
+        if out is None:
+            out = torch.empty((batch.n, self.hq, D), dtype=torch.float32, device=self.device)
+        ws = self.workspace_for(batch.n)
+        st = lib().oscar_bf16_paged_decode_attn(
+            ctypes.byref(self.st), batch.n, _hp(batch.slots), _hp(batch.lens), _p(batch.d_slots),
+            _p(batch.d_lens), _p(q), _p(out), _p(ws), ws.numel(), current_stream())
+        check(st, "oscar_bf16_paged_decode_attn")
+        return out

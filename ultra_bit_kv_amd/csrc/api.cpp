@@ -66,41 +66,46 @@ DecodePlan head_passes(const oscar_kv_config& c) {
   return p;
 }
 
-// Largest decode work (page pairs, a window block = kWinCost) of any row.
-int64_t max_row_cost(const oscar_kv_config& c) {
+// What the split limits of a decode call depend on: KV heads, query-head
+// passes and heads per pass, and the largest decode work of any row.
+struct DecodeShape {
+  int hkv, passes, hp;
+  int64_t max_cost;   // page pairs, a window block = kWinCost
+};
+
+DecodeShape int2_shape(const oscar_kv_config& c) {
+  const DecodePlan p = head_passes(c);
   const int64_t pairs = ((int64_t)c.max_pages_per_seq + 1) / 2;
   const int64_t wu = (c.s_sink + kPage - 1) / kPage + ring_cap(c) / kPage;
-  return pairs + kWinCost * wu;
+  return DecodeShape{c.num_kv_heads, p.passes, p.hp, pairs + kWinCost * wu};
 }
 
 // Fewest splits that keep every split within kMaxPairsPerSplit - 1 units
 // (the page-id list a work-group stages in LDS; the planner's largest quota).
-int min_splits(const oscar_kv_config& c) {
-  return (int)std::max<int64_t>(1, (max_row_cost(c) + kMaxPairsPerSplit - 2) / (kMaxPairsPerSplit - 1));
+int min_splits(const DecodeShape& sh) {
+  return (int)std::max<int64_t>(1, (sh.max_cost + kMaxPairsPerSplit - 2) / (kMaxPairsPerSplit - 1));
 }
 
 // Most splits per (sequence, KV head, pass) the workspace is sized for:
 // about 16K partial records per launch, at most kMaxSplits, and never fewer
 // than min_splits (the config limits keep min_splits <= kMaxSplits).
-int max_splits(const oscar_kv_config& c, int n_seqs) {
-  const DecodePlan p = head_passes(c);
+int max_splits(const DecodeShape& sh, int n_seqs) {
   const int ns = std::min(std::max(1, n_seqs), kMaxScanSeqs);
-  const long long rows = (long long)ns * c.num_kv_heads * p.passes;
+  const long long rows = (long long)ns * sh.hkv * sh.passes;
   long long s = (16384 + rows - 1) / rows;
   s = std::max(1LL, std::min((long long)kMaxSplits, s));
-  return (int)std::max<long long>(s, min_splits(c));
+  return (int)std::max<long long>(s, min_splits(sh));
 }
 
 // Split partial records of one decode launch (at most kMaxScanSeqs
 // sequences), then, when rows may have more than kMergeDirect splits, the
 // chunk records of the first merge launch.
-size_t partials_bytes(const oscar_kv_config& c, int n_seqs) {
-  const DecodePlan p = head_passes(c);
-  const size_t rec = (size_t)rec_words(p.hp);
+size_t partials_bytes(const DecodeShape& sh, int n_seqs) {
+  const size_t rec = (size_t)rec_words(sh.hp);
   const int ns = std::min(std::max(1, n_seqs), kMaxScanSeqs);
-  const int cap = max_splits(c, ns);
+  const int cap = max_splits(sh, ns);
   const size_t per_row = (size_t)cap + (cap > kMergeDirect ? (cap + kMergeChunk - 1) / kMergeChunk : 0);
-  return align_up((size_t)ns * c.num_kv_heads * p.passes * per_row * rec * sizeof(float));
+  return align_up((size_t)ns * sh.hkv * sh.passes * per_row * rec * sizeof(float));
 }
 
 size_t staging_bytes(const oscar_kv_config& c, int64_t n_tok) {
@@ -155,22 +160,23 @@ int check_device(int* cus = nullptr) {
 // Decode work of a row of len tokens (page pairs, a window block = kWinCost);
 // the kernels compute the same numbers from the device lengths with the same
 // function.
-int64_t decode_cost(int64_t len, const oscar_kv_config& c) {
-  const DecodeWork w = decode_work((int)len, c.s_sink, c.s_keep, c.s_flush, ring_cap(c));
+int64_t decode_cost(int64_t len, const CacheArgs& a) {
+  const DecodeWork w = decode_work((int)len, a.s_sink, a.s_keep, a.s_flush, a.ring_cap);
   return w.n_pairs + (int64_t)kWinCost * w.n_wu;
 }
 
 // Resident split work-groups per compute unit, once per (device, kernel shape).
-int decode_slots_per_cu(const CacheArgs& a, const DecodePlan& plan) {
+int decode_slots_per_cu(const CacheArgs& a, const DecodePlan& plan, bool bf16) {
   static std::mutex mu;
   static std::vector<std::pair<long long, int>> memo;
   int dev = 0;
   (void)hipGetDevice(&dev);
-  const long long key = ((((long long)dev * 8 + a.ng) * 32 + plan.hp) * 8 + plan.wh);
+  const long long key =
+      (((((long long)dev * 2 + (bf16 ? 1 : 0)) * 8 + a.ng) * 32 + plan.hp) * 8 + plan.wh);
   std::lock_guard<std::mutex> lock(mu);
   for (const auto& m : memo)
     if (m.first == key) return m.second;
-  const int n = decode_wgs_per_cu(a, plan);
+  const int n = bf16 ? bf16_decode_wgs_per_cu(plan) : decode_wgs_per_cu(a, plan);
   memo.emplace_back(key, n);
   return n;
 }
@@ -243,7 +249,8 @@ int64_t oscar_max_seq_len(const oscar_kv_config* c) {
 
 size_t oscar_workspace_size(const oscar_kv_config* c, int32_t n_seqs, int64_t max_new_tokens) {
   if (oscar_check_config(c) != OSCAR_OK || n_seqs < 0 || max_new_tokens < 0) return 0;
-  return std::max(partials_bytes(*c, std::max(1, (int)n_seqs)), staging_bytes(*c, max_new_tokens));
+  return std::max(partials_bytes(int2_shape(*c), std::max(1, (int)n_seqs)),
+                  staging_bytes(*c, max_new_tokens));
 }
 
 const char* oscar_status_string(int status) {
@@ -353,6 +360,132 @@ namespace {
 // Checks and the split plan shared by the decode entry points.  The plan
 // depends only on the configuration, the host lengths and the device, so the
 // split and merge calls of one decode step compute the same plan.
+// Plans and enqueues one split-K decode call (INT2 or BF16 pages) of
+// n_seqs checked sequences.
+int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, bool bf16,
+                    int n_seqs, const int32_t* seq_slots_host, const int32_t* seq_lens_host,
+                    const int32_t* seq_slots, const int32_t* seq_lens, const uint16_t* q,
+                    float* out, void* workspace, void* stream, int phases) {
+  int cus = 256;
+  int st = check_device(&cus);
+  if (st != OSCAR_OK) return st;
+  const int64_t rows = (int64_t)(a.hkv / plan.wh) * plan.passes;
+  const int64_t slots =
+      std::max<int64_t>(1, (int64_t)cus * decode_slots_per_cu(a, plan, bf16) * kFillPercent / 100);
+  // Every launch keeps to the split limit the workspace is sized for (that
+  // of a full launch), so a short last launch fits in it too.
+  const int cap = max_splits(sh, std::min(n_seqs, kMaxScanSeqs));
+  // Launches of at most kMaxScanSeqs sequences, in stream order.
+  for (int s0 = 0; s0 < n_seqs; s0 += kMaxScanSeqs) {
+    const int ns = std::min(kMaxScanSeqs, n_seqs - s0);
+    // Context splits: a work quota per split.  The smallest quota whose work
+    // items (one work-group each) all fit in one round of resident
+    // work-groups, so none waits for a second round; long sequences get
+    // more splits.  The quota never leaves the split limits.
+    std::vector<int64_t> cost(ns);
+    int64_t total = 0, max_cost = 0;
+    for (int i = 0; i < ns; ++i) {
+      cost[i] = decode_cost(seq_lens_host[s0 + i], a);
+      total += cost[i];
+      max_cost = std::max(max_cost, cost[i]);
+    }
+    // quota in 1/16 units; at most 255 pairs per split (the LDS page list)
+    auto splits_of = [&](int64_t c16, int64_t q16) {
+      return std::max<int64_t>(1, (16 * c16 + q16 - 1) / q16);
+    };
+    auto items_of = [&](int64_t q16) {
+      int64_t n = 0;
+      for (int i = 0; i < ns; ++i) n += splits_of(cost[i], q16);
+      return n * rows;
+    };
+    const int64_t q_max = 16 * (kMaxPairsPerSplit - 1);
+    int64_t quota = std::max<int64_t>(32, (16 * total * rows + slots - 1) / slots);
+    quota = std::max<int64_t>(quota, (16 * max_cost + cap - 1) / cap);
+    quota = std::min<int64_t>(quota, q_max);
+    if (items_of(quota) > slots) {   // smallest quota in (quota, limit] that fits (items fall as quota grows)
+      int64_t lo = quota, hi = q_max;
+      while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) / 2;
+        (items_of(mid) > slots ? lo : hi) = mid;
+      }
+      quota = hi;
+    }
+    int64_t smax = 1;
+    for (int i = 0; i < ns; ++i) smax = std::max<int64_t>(smax, splits_of(cost[i], quota));
+    if (smax > cap) return OSCAR_ERR_CAPACITY;   // unreachable: cap >= min_splits
+    plan.quota = (int)quota;
+    plan.smax = (int)smax;
+    plan.grid = (int)items_of(quota);
+    const SeqArgs sa{seq_slots + s0, seq_lens + s0, nullptr, ns};
+    const size_t qo = (size_t)s0 * a.hq * kD;
+    const uint16_t* qs = q ? q + qo : nullptr;
+    float* os = out ? out + qo : nullptr;
+    const hipError_t e =
+        bf16 ? launch_bf16_decode(a, sa, plan, qs, os, (float*)workspace, phases, (hipStream_t)stream)
+             : launch_decode(a, sa, plan, qs, os, (float*)workspace, phases, (hipStream_t)stream);
+    st = hip_status(e);
+    if (st != OSCAR_OK) return st;
+  }
+  return OSCAR_OK;
+}
+
+// ---- plain BF16 paged cache (the uncompressed comparison point) ----------
+
+int check_bf16(const oscar_bf16_cache* b) {
+  if (!b) return OSCAR_ERR_NULL;
+  if (b->head_dim != kD || b->page_size != kPage) return OSCAR_ERR_SHAPE;
+  if (b->num_kv_heads < 1 || b->num_kv_heads > OSCAR_MAX_KV_HEADS) return OSCAR_ERR_SHAPE;
+  if (b->num_q_heads < b->num_kv_heads || b->num_q_heads % b->num_kv_heads != 0)
+    return OSCAR_ERR_SHAPE;
+  if (b->num_q_heads / b->num_kv_heads > 256) return OSCAR_ERR_SHAPE;
+  if (b->max_seqs < 1 || b->max_pages_per_seq < 0 || b->num_pages < 0) return OSCAR_ERR_CAPACITY;
+  if (b->max_pages_per_seq > kMaxPagesPerSeq) return OSCAR_ERR_CAPACITY;
+  return OSCAR_OK;
+}
+
+// Query heads per pass: a power of two covering g, at most the 16 columns of
+// an MFMA tile.
+DecodePlan bf16_plan(const oscar_bf16_cache& b) {
+  const int g = b.num_q_heads / b.num_kv_heads;
+  int hp = 1;
+  while (hp < g && hp < 16) hp *= 2;
+  DecodePlan p{};
+  p.hp = hp;
+  p.passes = (g + hp - 1) / hp;
+  p.wh = b.num_kv_heads % 4 == 0 ? 4 : (b.num_kv_heads % 2 == 0 ? 2 : 1);
+  p.quota = 1;
+  p.smax = 1;
+  return p;
+}
+
+DecodeShape bf16_shape(const oscar_bf16_cache& b) {
+  const DecodePlan p = bf16_plan(b);
+  return DecodeShape{b.num_kv_heads, p.passes, p.hp, ((int64_t)b.max_pages_per_seq + 1) / 2};
+}
+
+// The BF16 cache as kernel arguments: no windows (s_sink = s_keep = 0,
+// s_flush = 1, so every token is a "page" token and decode_work counts the
+// row's page pairs); one page-head block = 16 K rows + 16 V rows of bf16.
+CacheArgs make_bf16_args(const oscar_bf16_cache& b) {
+  CacheArgs a{};
+  a.pages = (uint8_t*)b.pages;
+  a.block_table = b.block_table;
+  a.hq = b.num_q_heads;
+  a.hkv = b.num_kv_heads;
+  a.g = b.num_q_heads / b.num_kv_heads;
+  a.group = kD;
+  a.ng = 1;
+  a.s_sink = 0;
+  a.s_keep = 0;
+  a.s_flush = 1;
+  a.ring_cap = 0;
+  a.max_seqs = b.max_seqs;
+  a.max_pages = b.max_pages_per_seq;
+  a.num_pages = b.num_pages;
+  a.page_bytes = 2 * kPage * kD * (int)sizeof(uint16_t);
+  return a;
+}
+
 int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_slots_host,
                 const int32_t* seq_lens_host, const int32_t* seq_slots, const int32_t* seq_lens,
                 const uint16_t* q_rot, float* out, void* workspace, size_t workspace_bytes,
@@ -377,64 +510,12 @@ int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_
     if (len > max_len || int2_pages(len, c) > c.max_pages_per_seq) return OSCAR_ERR_CAPACITY;
     if (int2_pages(len, c) > 0 && c.num_pages < 1) return OSCAR_ERR_CAPACITY;
   }
-  if (workspace_bytes < partials_bytes(c, n_seqs)) return OSCAR_ERR_WORKSPACE;
-  int cus = 256;
-  if ((st = check_device(&cus)) != OSCAR_OK) return st;
-  const CacheArgs a = make_args(*cache);
-  DecodePlan plan = head_passes(c);
-  const int64_t rows = (int64_t)(c.num_kv_heads / plan.wh) * plan.passes;
-  const int64_t slots =
-      std::max<int64_t>(1, (int64_t)cus * decode_slots_per_cu(a, plan) * kFillPercent / 100);
-  // Every launch keeps to the split limit the workspace is sized for (that
-  // of a full launch), so a short last launch fits in it too.
-  const int cap = max_splits(c, std::min(n_seqs, kMaxScanSeqs));
-  // Launches of at most kMaxScanSeqs sequences, in stream order.
-  for (int s0 = 0; s0 < n_seqs; s0 += kMaxScanSeqs) {
-    const int ns = std::min(kMaxScanSeqs, n_seqs - s0);
-    // Context splits: a work quota per split.  The smallest quota whose work
-    // items (one work-group each) all fit in one round of resident
-    // work-groups, so none waits for a second round; long sequences get
-    // more splits.  The quota never leaves the split limits.
-    std::vector<int64_t> cost(ns);
-    int64_t total = 0, max_cost = 0;
-    for (int i = 0; i < ns; ++i) {
-      cost[i] = decode_cost(seq_lens_host[s0 + i], c);
-      total += cost[i];
-      max_cost = std::max(max_cost, cost[i]);
-    }
-    // quota in 1/16 units; at most 255 pairs per split (the LDS page list)
-    auto splits_of = [&](int64_t c16, int64_t q) { return std::max<int64_t>(1, (16 * c16 + q - 1) / q); };
-    auto items_of = [&](int64_t q) {
-      int64_t n = 0;
-      for (int i = 0; i < ns; ++i) n += splits_of(cost[i], q);
-      return n * rows;
-    };
-    const int64_t q_max = 16 * (kMaxPairsPerSplit - 1);
-    int64_t quota = std::max<int64_t>(32, (16 * total * rows + slots - 1) / slots);
-    quota = std::max<int64_t>(quota, (16 * max_cost + cap - 1) / cap);
-    quota = std::min<int64_t>(quota, q_max);
-    if (items_of(quota) > slots) {   // smallest quota in (quota, limit] that fits (items fall as quota grows)
-      int64_t lo = quota, hi = q_max;
-      while (hi - lo > 1) {
-        const int64_t mid = (lo + hi) / 2;
-        (items_of(mid) > slots ? lo : hi) = mid;
-      }
-      quota = hi;
-    }
-    int64_t smax = 1;
-    for (int i = 0; i < ns; ++i) smax = std::max<int64_t>(smax, splits_of(cost[i], quota));
-    if (smax > cap) return OSCAR_ERR_CAPACITY;   // unreachable: cap >= min_splits
-    plan.quota = (int)quota;
-    plan.smax = (int)smax;
-    plan.grid = (int)items_of(quota);
-    const SeqArgs sa{seq_slots + s0, seq_lens + s0, nullptr, ns};
-    const size_t qo = (size_t)s0 * c.num_q_heads * kD;
-    st = hip_status(launch_decode(a, sa, plan, q_rot ? q_rot + qo : nullptr, out ? out + qo : nullptr,
-                                  (float*)workspace, phases, (hipStream_t)stream));
-    if (st != OSCAR_OK) return st;
-  }
-  return OSCAR_OK;
+  if (workspace_bytes < partials_bytes(int2_shape(c), n_seqs)) return OSCAR_ERR_WORKSPACE;
+  return plan_and_launch(make_args(*cache), head_passes(c), int2_shape(c), false, n_seqs,
+                         seq_slots_host, seq_lens_host, seq_slots, seq_lens, q_rot, out, workspace,
+                         stream, phases);
 }
+
 
 }  // namespace
 
@@ -466,6 +547,39 @@ int oscar_int2_decode_merge(const oscar_kv_cache* cache, int32_t n_seqs,
                      out, workspace, workspace_bytes, stream, kDecodeMerge);
 }
 
+
+size_t oscar_bf16_workspace_size(const oscar_bf16_cache* cache, int32_t n_seqs) {
+  if (check_bf16(cache) != OSCAR_OK) return 0;
+  return partials_bytes(bf16_shape(*cache), std::max(1, (int)n_seqs));
+}
+
+int oscar_bf16_paged_decode_attn(const oscar_bf16_cache* cache, int32_t n_seqs,
+                                 const int32_t* seq_slots_host, const int32_t* seq_lens_host,
+                                 const int32_t* seq_slots, const int32_t* seq_lens,
+                                 const uint16_t* q, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  int st = check_bf16(cache);
+  if (st != OSCAR_OK) return st;
+  const oscar_bf16_cache& b = *cache;
+  if (!seq_slots_host || !seq_lens_host || !seq_slots || !seq_lens || !q || !out || !workspace ||
+      !b.pages || !b.block_table)
+    return OSCAR_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) || !aligned16(b.pages) ||
+      !aligned16(b.block_table))
+    return OSCAR_ERR_ARG;
+  if (n_seqs < 1 || n_seqs > b.max_seqs) return OSCAR_ERR_ARG;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int slot = seq_slots_host[i];
+    const int64_t len = seq_lens_host[i];
+    if (slot < 0 || slot >= b.max_seqs) return OSCAR_ERR_CAPACITY;
+    if (len < 1) return OSCAR_ERR_ARG;
+    if ((len + kPage - 1) / kPage > b.max_pages_per_seq || b.num_pages < 1) return OSCAR_ERR_CAPACITY;
+  }
+  if (workspace_bytes < partials_bytes(bf16_shape(b), n_seqs)) return OSCAR_ERR_WORKSPACE;
+  return plan_and_launch(make_bf16_args(b), bf16_plan(b), bf16_shape(b), true, n_seqs,
+                         seq_slots_host, seq_lens_host, seq_slots, seq_lens, q, out, workspace,
+                         stream, kDecodeSplit | kDecodeMerge);
+}
 
 int oscar_dequant(const oscar_kv_cache* cache, int32_t seq_slot, int32_t seq_len,
                   int32_t tok_begin, int32_t tok_end, float* k_out, float* v_out, void* stream) {

@@ -1,0 +1,371 @@
+// Pieces shared by the split-K decode kernels (INT2 mixed cache and plain
+// BF16 pages): wave-level reductions, the online softmax, the compact-grid
+// item lookup and the log-sum-exp merge of split partial records.
+#pragma once
+#include "device_common.h"
+
+namespace oscar {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+template <int SH>
+__device__ __forceinline__ float row_ror(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + SH, 0xF, 0xF, false));
+}
+
+// all-reduce over the four 16-lane rows (lanes n, n+16, n+32, n+48)
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                            false, false);
+  x = fmaxf(__builtin_bit_cast(float, (int)a[0]), __builtin_bit_cast(float, (int)a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                            false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)b[0]), __builtin_bit_cast(float, (int)b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                            false, false);
+  x = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                            false, false);
+  return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
+}
+
+__device__ __forceinline__ half8 codes_as_half8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                                uint32_t mask) {
+  u32x4 v = {w0 & mask, w1 & mask, w2 & mask, w3 & mask};
+  return __builtin_bit_cast(half8, v);
+}
+
+__device__ __forceinline__ float f16lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// fp16 pair (a * lo16(wa), b * lo16(wb)), rounded to fp16.
+__device__ __forceinline__ uint32_t mul_f32_by_f16lo_pack(float a, uint32_t wa, float b,
+                                                          uint32_t wb) {
+  const half2_t ha = __builtin_bit_cast(half2_t, wa);
+  const half2_t hb = __builtin_bit_cast(half2_t, wb);
+  half2_t r;
+  r.x = (_Float16)(a * (float)ha.x);
+  r.y = (_Float16)(b * (float)hb.x);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+struct SoftmaxState {
+  float m;   // running max (log2 domain), same in every lane of a column
+  float l;   // this lane's share of the running sum
+  float z;   // this lane's share of sum_t p_t * zero_v[t][group]
+};
+
+// Online-softmax update with a lazy max.  x holds logits in raw units; the
+// log2-domain logit is scale * x (scale > 0).  The reference max only moves
+// when a logit exceeds it by more than 8 (so p <= 2^8), which keeps most
+// tiles free of the accumulator rescale.
+template <int N>
+__device__ __forceinline__ void softmax_step(const float (&x)[N], float scale, float (&p)[N],
+                                             SoftmaxState& st, float4_t (&acc)[8]) {
+  float tmax = x[0];
+#pragma unroll
+  for (int k = 1; k < N; ++k) tmax = fmaxf(tmax, x[k]);
+  tmax = rows_max(tmax) * scale;
+  if (__any(tmax > st.m + 8.0f)) {
+    const float m_new = fmaxf(st.m, tmax);
+    const float alpha = m_new > st.m ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+    st.l *= alpha;
+    st.z *= alpha;
+    st.m = m_new;
+  }
+  const float mref = st.m == kNegInf ? 0.0f : st.m;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k], scale, -mref));
+    st.l += p[k];
+  }
+}
+
+constexpr int kMaxWgPages = 2 * kMaxPairsPerSplit;   // page ids staged per work-group
+
+
+// Issue priority of the calling wave from its remaining share of the work:
+// waves of one SIMD otherwise issue oldest-first, so the first work-groups
+// on a compute unit run ahead and the last ones finish alone.
+__device__ __forceinline__ void set_priority(int remaining, int total) {
+  const int p = (4 * remaining - 1) / total;   // 0..3
+  if (p >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (p == 2) __builtin_amdgcn_s_setprio(2);
+  else if (p == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+// The work item of this work-group in a compact grid: items are numbered
+// sequence-major and sequence k has items_of(slot, len) of them, so a
+// block-wide prefix sum over the sequences' counts finds the sequence.
+// s_item receives {sequence, item within it, its slot, its length}, or
+// s_item[0] = -1 when the device lengths give fewer items than the grid.
+// Ends with a barrier.
+template <int NT, class F>
+__device__ __forceinline__ void locate_item(const SeqArgs& s, F items_of, int* s_wsum,
+                                            int* s_item) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = s.n_seqs, per = (n + NT - 1) / NT;
+  const int k0 = min(tid * per, n), k1 = min(k0 + per, n);
+  int run = 0;
+  for (int k = k0; k < k1; ++k) run += items_of(s.slots[k], s.lens[k]);
+  int incl = run;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  if (tid == 0) s_item[0] = -1;
+  __syncthreads();
+  int off = incl - run;
+  for (int w2 = 0; w2 < wave; ++w2) off += s_wsum[w2];
+  const int item = blockIdx.x;
+  for (int k = k0; k < k1; ++k) {
+    const int sl = s.slots[k], ln = s.lens[k];
+    const int q = items_of(sl, ln);
+    if (item >= off && item < off + q) {   // exactly one (k, thread) matches
+      s_item[0] = k;
+      s_item[1] = item - off;
+      s_item[2] = sl;
+      s_item[3] = ln;
+    }
+    off += q;
+  }
+  __syncthreads();
+}
+
+// Log-sum-exp merge of partial records (WUSH-KV notes, "method step
+// details": split outputs are combined by their maxima and sums).  A record
+// holds, per head, m (log2 domain), l = sum 2^(x - m) and the unnormalized
+// o' = sum 2^(x - m) v'; two records combine exactly as
+//   M = max(m1, m2), l = l1 2^(m1 - M) + l2 2^(m2 - M), o' likewise.
+
+// First of two merge launches for rows with many splits: work-group =
+// (sequence, KV head, pass, chunk of kMergeChunk splits); thread = (head of
+// the pass, 4 channels).  Every thread loads its head's maxima and sums
+// itself, so the kernel has no LDS and no barrier.  Output: one record per
+// chunk, in the same layout, with row stride smax2.
+template <int HP>
+__global__ __launch_bounds__(HP * 32 < 64 ? 64 : HP * 32) void lse_chunks_kernel(
+    CacheArgs c, SeqArgs s, int quota, int passes, int smax, int smax2,
+    const float* __restrict__ partials, float* __restrict__ merged) {
+  constexpr int W = rec_words(HP), OO = rec_o_offset(HP);
+  const int x = blockIdx.x;
+  const int pass = x % passes, h = (x / passes) % c.hkv, i = x / (passes * c.hkv);
+  const int nh = min(HP, c.g - pass * HP);
+  const int r = threadIdx.x >> 5, c4 = threadIdx.x & 31;
+  const int slot = s.slots[i], len = s.lens[i];
+  const bool ok = slot >= 0 && slot < c.max_seqs && len >= 1;
+  const int ns = decode_splits(decode_work(ok ? len : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap),
+                               quota, smax);
+  const int sp0 = blockIdx.y * kMergeChunk;
+  if (r >= nh || sp0 >= ns) return;
+  const int cnt = min(kMergeChunk, ns - sp0);
+  const size_t row = ((size_t)i * c.hkv + h) * passes + pass;
+  const float* rec = partials + (row * smax + sp0) * W;
+  float m[kMergeChunk], l[kMergeChunk];
+  float4_t o[kMergeChunk];
+#pragma unroll
+  for (int j = 0; j < kMergeChunk; ++j) {
+    const float* rj = rec + (size_t)(j < cnt ? j : 0) * W;
+    m[j] = rj[r];
+    l[j] = rj[HP + r];
+    o[j] = *(const float4_t*)(rj + OO + r * kD + 4 * c4);
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kMergeChunk; ++j)
+    if (j < cnt) M = fmaxf(M, m[j]);
+  float L = 0.0f;
+  float4_t O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMergeChunk; ++j) {
+    const float w = (j < cnt && m[j] != kNegInf) ? __builtin_amdgcn_exp2f(m[j] - M) : 0.0f;
+    L = __builtin_fmaf(w, l[j], L);
+    O[0] = __builtin_fmaf(w, o[j][0], O[0]);
+    O[1] = __builtin_fmaf(w, o[j][1], O[1]);
+    O[2] = __builtin_fmaf(w, o[j][2], O[2]);
+    O[3] = __builtin_fmaf(w, o[j][3], O[3]);
+  }
+  float* dst = merged + (row * smax2 + blockIdx.y) * W;
+  if (c4 == 0) {
+    dst[r] = M;
+    dst[HP + r] = L;
+  }
+  *(float4_t*)(dst + OO + r * kD + 4 * c4) = O;
+}
+
+// Final merge, then (UNROT) o = o' . R_V^T.
+//
+// Work-group = (KV head, pass, block of SB sequences): its 16 rows are the
+// (sequence, query head) pairs of the block, one MFMA tile of rows, and all
+// 128 output columns.  Thread = (row, 4 channels): it folds the row's
+// records in rounds of 8 with a running maximum, loading the maxima and
+// sums itself.  Without UNROT the thread stores its 4 channels.  With it,
+// the merged o' rows go to LDS and wave w computes output columns
+// 16w .. 16w+15 on the fp32 matrix cores, with lane (i, q) holding
+// R_V[16w + i][32q .. 32q+31] in registers (loaded at entry, before any
+// wait), so the contraction index of step (u, e) is k = 32q + 4u + e.
+template <int HP, bool UNROT>
+__global__ __launch_bounds__(512) void lse_merge_kernel(CacheArgs c, SeqArgs s, int quota,
+                                                        int passes, int smax, int chunk,
+                                                        int stride, int sb,
+                                                        const float* __restrict__ recs,
+                                                        float* __restrict__ out) {
+  constexpr int W = rec_words(HP), OO = rec_o_offset(HP);
+  constexpr int kRound = 8;
+  __shared__ float fin[16][kD + 4];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int li = lane & 15, kq = lane >> 4;
+  const int h = blockIdx.x / passes, pass = blockIdx.x % passes;
+  const int nh = min(HP, c.g - pass * HP);
+  const int s0 = blockIdx.y * sb;
+
+  float4_t rb[8];
+  if constexpr (UNROT) {
+    const float4_t* rg =
+        (const float4_t*)(c.r_v + ((size_t)h * kD + 16 * wave + li) * kD + 32 * kq);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rb[u] = rg[u];
+  }
+
+  const int r = t >> 5, c4 = t & 31;
+  const int i = s0 + r / nh;
+  const bool valid = r < sb * nh && i < s.n_seqs;
+  int nrec = 0;
+  bool ok = false;
+  const float* rec = recs;
+  if (valid) {
+    const int slot = s.slots[i], len = s.lens[i];
+    ok = slot >= 0 && slot < c.max_seqs && len >= 1;
+    const int ns = decode_splits(
+        decode_work(ok ? len : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap), quota, smax);
+    nrec = (ns + chunk - 1) / chunk;
+    rec = recs + (((size_t)i * c.hkv + h) * passes + pass) * stride * W;
+  }
+  const int hr = r % nh;
+  float M = kNegInf, L = 0.0f;
+  float4_t O = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < nrec; j0 += kRound) {
+    float m[kRound], l[kRound];
+    float4_t o[kRound];
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) {
+      const float* rj = rec + (size_t)(j0 + j < nrec ? j0 + j : j0) * W;
+      m[j] = rj[hr];
+      l[j] = rj[HP + hr];
+      o[j] = *(const float4_t*)(rj + OO + hr * kD + 4 * c4);
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < kRound; ++j)
+      if (j0 + j < nrec) Mn = fmaxf(Mn, m[j]);
+    const float sc = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+    L *= sc;
+    O[0] *= sc;
+    O[1] *= sc;
+    O[2] *= sc;
+    O[3] *= sc;
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) {
+      const float w = (j0 + j < nrec && m[j] != kNegInf) ? __builtin_amdgcn_exp2f(m[j] - Mn) : 0.0f;
+      L = __builtin_fmaf(w, l[j], L);
+      O[0] = __builtin_fmaf(w, o[j][0], O[0]);
+      O[1] = __builtin_fmaf(w, o[j][1], O[1]);
+      O[2] = __builtin_fmaf(w, o[j][2], O[2]);
+      O[3] = __builtin_fmaf(w, o[j][3], O[3]);
+    }
+    M = Mn;
+  }
+  float4_t f = {0.f, 0.f, 0.f, 0.f};
+  if (nrec > 0) {
+    f[0] = O[0] / L;
+    f[1] = O[1] / L;
+    f[2] = O[2] / L;
+    f[3] = O[3] / L;
+  }
+  if constexpr (!UNROT) {
+    if (valid && ok)
+      *(float4_t*)(out + ((size_t)i * c.hq + (size_t)h * c.g + pass * HP + hr) * kD + 4 * c4) = f;
+    return;
+  }
+  *(float4_t*)(&fin[r][4 * c4]) = f;
+  __syncthreads();
+
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fin[li][32 * kq + 4 * u + e], rb[u][e], acc, 0, 0,
+                                                 0);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int rr = 4 * kq + v;   // output row of this lane's v-th value
+    const int ii = s0 + rr / nh;
+    if (rr >= sb * nh || ii >= s.n_seqs) continue;
+    const int slot = s.slots[ii];
+    if (slot < 0 || slot >= c.max_seqs || s.lens[ii] < 1) continue;
+    float* o = out + ((size_t)ii * c.hq + (size_t)h * c.g + pass * HP + rr % nh) * kD;
+    o[16 * wave + li] = acc[v];
+  }
+}
+
+
+// The merge launch(es) of a split-K decode step: chunk folding when a row may
+// have more than kMergeDirect splits (its records follow the split records
+// in the workspace), then the final merge.
+template <int HP, bool UNROT>
+hipError_t launch_merge(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
+                        float* partials, float* out, hipStream_t stream) {
+  const int nh_full = c.g < HP ? c.g : HP;
+  const int sb = 16 / nh_full;   // sequences per final-merge work-group (16 rows)
+  const float* recs = partials;
+  int chunk = 1, stride = plan.smax;
+  if (plan.smax > kMergeDirect) {
+    const int smax2 = (plan.smax + kMergeChunk - 1) / kMergeChunk;
+    float* merged = partials + (size_t)s.n_seqs * c.hkv * plan.passes * plan.smax * rec_words(HP);
+    const dim3 g1(s.n_seqs * c.hkv * plan.passes, smax2);
+    hipLaunchKernelGGL((lse_chunks_kernel<HP>), g1, dim3(HP * 32 < 64 ? 64 : HP * 32), 0, stream,
+                       c, s, plan.quota, plan.passes, plan.smax, smax2, partials, merged);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    recs = merged;
+    chunk = kMergeChunk;
+    stride = smax2;
+  }
+  const dim3 mgrid(c.hkv * plan.passes, (s.n_seqs + sb - 1) / sb);
+  hipLaunchKernelGGL((lse_merge_kernel<HP, UNROT>), mgrid, dim3(512), 0, stream, c, s, plan.quota,
+                     plan.passes, plan.smax, chunk, stride, sb, recs, out);
+  return hipGetLastError();
+}
+
+}  // namespace oscar

@@ -142,4 +142,13 @@ hipError_t launch_decode(const CacheArgs& c, const SeqArgs& s, const DecodePlan&
                          const uint16_t* q_rot, float* out, float* partials, int phases,
                          hipStream_t stream);
 
+// Split-K decode over a plain BF16 paged cache (c.pages = bf16
+// [num_pages][hkv][2][16][128], c.s_sink = c.s_keep = c.ring_cap = 0,
+// c.s_flush = 1, so decode_work counts its page pairs): split kernel and the
+// same merge, without un-rotation.
+hipError_t launch_bf16_decode(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
+                              const uint16_t* q, float* out, float* partials, int phases,
+                              hipStream_t stream);
+int bf16_decode_wgs_per_cu(const DecodePlan& plan);
+
 }  // namespace oscar
