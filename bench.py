@@ -58,6 +58,56 @@ def algorithmic_bytes(w, lens):
     return total
 
 
+def bf16_bytes(w, lens):
+    """Bytes a BF16 paged decode must move: K and V rows of every
+    token-head, one block-table entry per page, and the queries."""
+    total = 0
+    for L in lens:
+        L = int(L)
+        total += w.hkv * L * 512 + 4 * (-(-L // 16))
+    total += len(lens) * w.hq * 128 * 2
+    return total
+
+
+def measure_bf16(w, n_layers, steps, hold):
+    """Time `steps` BF16 paged decode calls over the lengths of workload w,
+    cycling through n_layers caches of seeded random bf16 pages."""
+    import torch
+    from ultra_bit_kv_amd import BF16PagedCache, SeqBatch
+
+    lens = [int(L) for L in w.lengths_after()]
+    n = len(lens)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    layers = []
+    for _ in range(n_layers):
+        bt, total = w.page_pool([-(-L // 16) for L in lens])
+        c = BF16PagedCache(num_q_heads=w.hq, num_kv_heads=w.hkv, max_seqs=n,
+                           max_pages_per_seq=bt.shape[1], num_pages=total, block_table=bt)
+        c.pages.normal_(generator=gen)
+        c.workspace_for(n)
+        layers.append(c)
+    batch = SeqBatch(np.arange(n), lens)
+    q = torch.randn((n, w.hq, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((n, w.hq, 128), dtype=torch.float32, device="cuda")
+    for s in range(2 * n_layers):
+        layers[s % n_layers].decode(batch, q, out)
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(steps)]
+    torch.cuda._sleep(int(hold))
+    for j in range(steps):
+        evs[j][0].record()
+        layers[j % n_layers].decode(batch, q, out)
+        evs[j][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    byts = bf16_bytes(w, lens)
+    del layers
+    torch.cuda.empty_cache()
+    return {"decode_ms": ms, "bytes": byts, "GBs": byts / (ms * 1e-3) / 1e9,
+            "layers_cycled": n_layers}
+
+
 def read_traffic(src_hash):
     try:
         t = json.load(open(TRAFFIC_FILE))
@@ -265,6 +315,8 @@ def main():
                     help="the bs1 workload reported next to the headline ('' to skip)")
     ap.add_argument("--bs1-layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16-compare", dest="bf16_compare", action="store_false",
+                    help="skip the BF16 paged-decode comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a device copy of this many bytes (counter calibration)")
@@ -331,6 +383,22 @@ def main():
             "split_GBs": b["bytes"] / (b["split_ms"] * 1e-3) / 1e9,
             "algorithmic_bytes_per_launch": b["bytes"],
         }
+    if args.bf16_compare:
+        # the uncompressed comparison point on the same shapes and lengths
+        bf = measure_bf16(get(args.config), 2, min(args.steps, 100), hold)
+        res["bf16_compare"] = {
+            "kernel": "oscar_bf16_paged_decode_attn (split + merge), same lengths",
+            "bs64_decode_ms": bf["decode_ms"], "bs64_GBs": bf["GBs"],
+            "bs64_bytes_per_call": bf["bytes"],
+            "bs64_int2_speedup": bf["decode_ms"] / m["dec_ms"],
+            "bs64_int2_bytes_ratio": bf["bytes"] / m["bytes"],
+        }
+        if args.bs1_config:
+            bf1 = measure_bf16(get(args.bs1_config), 8, min(args.steps, 100), hold)
+            res["bf16_compare"].update({
+                "bs1_decode_ms": bf1["decode_ms"], "bs1_GBs": bf1["GBs"],
+                "bs1_int2_speedup": bf1["decode_ms"] / res["bs1"]["decode_ms"],
+            })
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, lens0, seconds=args.cpu_seconds)
     print(json.dumps(res), flush=True)
