@@ -334,7 +334,7 @@ def main():
 
     from synth import get
 
-    hold = int(args.steps * 150e-6 * 2.4e9)   # covers the host's queueing of the timed steps
+    hold = int(args.steps * 1e-3 * 2.4e9)   # covers the host's queueing of the timed steps
     m = measure(get(args.config), args.layers, args.steps, args.warmup, hold)
     w, lens0, n = m["w"], m["lens0"], m["n"]
     achieved = m["bytes"] / (m["split_ms"] * 1e-3) / 1e9

@@ -202,7 +202,8 @@ int oscar_int2_decode_attn(const oscar_kv_cache* cache, int32_t n_seqs,
  *  oscar_int2_decode_partials: q_rot as above; writes the partial records
  *                              (max, sum, unnormalized o' per context split)
  *                              to the workspace.
- *  oscar_int2_decode_merge:    out as above; reads those records. */
+ *  oscar_int2_decode_merge:    out as above; reads those records.
+ * These two calls take at most 2048 sequences (OSCAR_ERR_ARG otherwise). */
 int oscar_int2_decode_partials(const oscar_kv_cache* cache, int32_t n_seqs,
                                const int32_t* seq_slots_host, const int32_t* seq_lens_host,
                                const int32_t* seq_slots, const int32_t* seq_lens,

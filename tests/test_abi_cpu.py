@@ -175,6 +175,13 @@ def test_decode_phase_argument_checks(L):
     assert merge(None) == -1                                          # the merge needs out
     assert part(DUMMY, ws=100) == -7 and merge(DUMMY, ws=100) == -7
     assert part(DUMMY) in (-9, -8, 0) and merge(DUMMY) in (-9, -8, 0)
+    # the separate calls share one launch's workspace: at most 2048 sequences
+    big = cfg(max_seqs=3000)
+    sl, ln = _i32(np.arange(2049)), _i32(np.full(2049, 10))
+    assert L.oscar_int2_decode_partials(ctypes.byref(_cache(big)), 2049, sl[1], ln[1], DUMMY, DUMMY,
+                                        DUMMY, DUMMY, 1 << 40, None) == -10
+    assert L.oscar_int2_decode_merge(ctypes.byref(_cache(big)), 2049, sl[1], ln[1], DUMMY, DUMMY,
+                                     DUMMY, DUMMY, 1 << 40, None) == -10
 
 
 def test_dequant_argument_checks(L):

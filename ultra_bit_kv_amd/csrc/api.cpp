@@ -416,6 +416,7 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
     plan.quota = (int)quota;
     plan.smax = (int)smax;
     plan.grid = (int)items_of(quota);
+    plan.cus = cus;
     const SeqArgs sa{seq_slots + s0, seq_lens + s0, nullptr, ns};
     const size_t qo = (size_t)s0 * a.hq * kD;
     const uint16_t* qs = q ? q + qo : nullptr;
@@ -501,6 +502,8 @@ int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_
   if (!aligned16(q_rot) || !aligned16(out) || !cache_aligned(*cache) || !aligned16(workspace))
     return OSCAR_ERR_ARG;
   if (n_seqs < 1 || n_seqs > c.max_seqs) return OSCAR_ERR_ARG;
+  // separate split and merge calls share one launch's workspace
+  if (phases != (kDecodeSplit | kDecodeMerge) && n_seqs > kMaxScanSeqs) return OSCAR_ERR_ARG;
   const int64_t max_len = oscar_max_seq_len(&c);
   for (int i = 0; i < n_seqs; ++i) {
     const int slot = seq_slots_host[i];

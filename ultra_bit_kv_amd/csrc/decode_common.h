@@ -56,15 +56,21 @@ __device__ __forceinline__ float f16hi(uint32_t w) {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-// fp16 pair (a * lo16(wa), b * lo16(wb)), rounded to fp16.
-__device__ __forceinline__ uint32_t mul_f32_by_f16lo_pack(float a, uint32_t wa, float b,
-                                                          uint32_t wb) {
+// The products a * lo16(wa) and b * lo16(wb) (fp16 scales) as fp16 pairs
+// split in two: hi = the products rounded to fp16, lo = the remainders
+// rounded to fp16, so hi + lo carries about 22 significant bits.
+__device__ __forceinline__ void mul_by_f16lo_split(float a, uint32_t wa, float b, uint32_t wb,
+                                                   uint32_t& hi, uint32_t& lo) {
   const half2_t ha = __builtin_bit_cast(half2_t, wa);
   const half2_t hb = __builtin_bit_cast(half2_t, wb);
-  half2_t r;
-  r.x = (_Float16)(a * (float)ha.x);
-  r.y = (_Float16)(b * (float)hb.x);
-  return __builtin_bit_cast(uint32_t, r);
+  const float pa = a * (float)ha.x, pb = b * (float)hb.x;
+  half2_t h, l;
+  h.x = (_Float16)pa;
+  h.y = (_Float16)pb;
+  l.x = (_Float16)(pa - (float)h.x);
+  l.y = (_Float16)(pb - (float)h.y);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
@@ -109,11 +115,15 @@ __device__ __forceinline__ void softmax_step(const float (&x)[N], float scale, f
 constexpr int kMaxWgPages = 2 * kMaxPairsPerSplit;   // page ids staged per work-group
 
 
-// Issue priority of the calling wave from its remaining share of the work:
-// waves of one SIMD otherwise issue oldest-first, so the first work-groups
-// on a compute unit run ahead and the last ones finish alone.
-__device__ __forceinline__ void set_priority(int remaining, int total) {
-  const int p = (4 * remaining - 1) / total;   // 0..3
+// Issue priority of the calling wave from its remaining share of the work
+// and its dispatch round (work-group b of a launch that fills the device
+// runs as the (b / cus)-th one on its compute unit).  Waves of one SIMD
+// otherwise issue oldest-first, so the work-groups placed first on a compute
+// unit run ahead and the last ones finish alone: a wave with more work
+// left, or placed later, gets a higher priority (4 levels; a round is worth
+// a third of a level).
+__device__ __forceinline__ void set_priority(int remaining, int total, int round) {
+  const int p = ((12 * remaining - 1) / total + (round < 3 ? round : 3)) / 3;
   if (p >= 3) __builtin_amdgcn_s_setprio(3);
   else if (p == 2) __builtin_amdgcn_s_setprio(2);
   else if (p == 1) __builtin_amdgcn_s_setprio(1);

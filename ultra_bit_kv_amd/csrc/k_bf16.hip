@@ -29,7 +29,7 @@ constexpr int kBfPrefetch = 2;   // pages in flight per wave ahead of the one pr
 
 template <int HP, int PF, int WH>
 __global__ __launch_bounds__(64 * WH) void bf16_decode_kernel(CacheArgs c, SeqArgs s, int quota,
-                                                              int passes, int smax,
+                                                              int passes, int smax, int cus,
                                                               const uint16_t* __restrict__ q,
                                                               float* __restrict__ partials) {
   constexpr int PW = rec_words(HP);
@@ -73,7 +73,8 @@ __global__ __launch_bounds__(64 * WH) void bf16_decode_kernel(CacheArgs c, SeqAr
   const int pe = (int)((unsigned)((split + 1) * n_pairs) / (unsigned)n_split);
   const int pg0 = 2 * pb;
   const int npg = max(0, min(min(2 * pe, n_pages) - pg0, kMaxWgPages));
-  set_priority(max(1, pe - pb), max(1, pe - pb));
+  const int rnd = blockIdx.x / cus;
+  set_priority(max(1, pe - pb), max(1, pe - pb), rnd);
   const int32_t* bt = c.block_table + (size_t)(row_ok ? slot : 0) * c.max_pages;
 
   const int hl = r16;              // this lane's MFMA column: query head hl of the pass
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(64 * WH) void bf16_decode_kernel(CacheArgs c, SeqAr
 #pragma unroll
     for (int j = 0; j < PF; ++j) load_page(j, ring[j]);
     for (int k = 0; k < npg; k += PF) {
-      set_priority(max(1, (npg - k + 1) / 2), max(1, pe - pb));
+      set_priority(max(1, (npg - k + 1) / 2), max(1, pe - pb), rnd);
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
         if (k + j < npg) process_page(ring[j]);
@@ -193,7 +194,7 @@ template <int HP, int WH>
 static void launch_split_t(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                            const uint16_t* q, float* partials, hipStream_t stream) {
   hipLaunchKernelGGL((bf16_decode_kernel<HP, kBfPrefetch, WH>), dim3(plan.grid), dim3(64 * WH), 0,
-                     stream, c, s, plan.quota, plan.passes, plan.smax, q, partials);
+                     stream, c, s, plan.quota, plan.passes, plan.smax, plan.cus, q, partials);
 }
 
 template <int HP>

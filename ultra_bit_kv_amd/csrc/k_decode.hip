@@ -21,8 +21,9 @@
 //         the column's group.  Scale and zero-point enter after the MFMA:
 //         q.k_hat = sum_g s_g (q_g . c_g) + z_g sum_{j in g} q_j.
 //   P.V:  A = V codes [16 channels x 32 tokens] (the page layout stores each
-//         lane's 32 codes contiguously), B = p * scale_v as fp16; the zero
-//         point term sum_t p_t z_t is accumulated on the VALU.
+//         lane's 32 codes contiguously), B = p * scale_v as fp16 hi + lo (two
+//         MFMAs, about 22 significant bits); the zero point term
+//         sum_t p_t z_t is accumulated on the VALU.
 // BF16 window block (16 tokens): bf16 MFMA for q.k, P split into bf16 hi + lo
 // for P.V.
 #include "decode_common.h"
@@ -39,7 +40,7 @@ constexpr int kPrefetch = 2;   // page pairs in flight per wave ahead of the one
 // so each page is fetched as one contiguous run of WH page-head blocks.
 template <int NG, int HP, int PF, int WH>
 __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqArgs s, int quota,
-                                                              int passes, int smax,
+                                                              int passes, int smax, int cus,
                                                               const uint16_t* __restrict__ q_rot,
                                                               float* __restrict__ partials) {
   constexpr int PW = rec_words(HP);   // floats per partial record
@@ -97,7 +98,8 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int wb = (int)((unsigned)(split * n_wu) / (unsigned)n_split);
   const int we = (int)((unsigned)((split + 1) * n_wu) / (unsigned)n_split);
   const int total_units = max(1, (pe - pb) + kWinCost * (we - wb));
-  set_priority(total_units, total_units);
+  const int rnd = blockIdx.x / cus;   // dispatch round on its compute unit
+  set_priority(total_units, total_units, rnd);
   const uint16_t* wbase = c.win + ((size_t)(row_ok ? slot : 0) * c.hkv + h) * c.win_blocks *
                                       (2 * kPage * kD);
   struct Win {
@@ -256,12 +258,13 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     }
     float p[8];
     softmax_step<8>(x, K1, p, st, acc);
-    u32x4 pw;   // P' = p * scale_v as fp16, k index 8 qd + e <-> (e < 4 ? A : B) row e % 4
-    pw[0] = mul_f32_by_f16lo_pack(p[0], d.vpa[0], p[1], d.vpa[1]);
-    pw[1] = mul_f32_by_f16lo_pack(p[2], d.vpa[2], p[3], d.vpa[3]);
-    pw[2] = mul_f32_by_f16lo_pack(p[4], d.vpb[0], p[5], d.vpb[1]);
-    pw[3] = mul_f32_by_f16lo_pack(p[6], d.vpb[2], p[7], d.vpb[3]);
-    const half8 pv = __builtin_bit_cast(half8, pw);
+    uint32_t ph[4], pl[4];
+    mul_by_f16lo_split(p[0], d.vpa[0], p[1], d.vpa[1], ph[0], pl[0]);
+    mul_by_f16lo_split(p[2], d.vpa[2], p[3], d.vpa[3], ph[1], pl[1]);
+    mul_by_f16lo_split(p[4], d.vpb[0], p[5], d.vpb[1], ph[2], pl[2]);
+    mul_by_f16lo_split(p[6], d.vpb[2], p[7], d.vpb[3], ph[3], pl[3]);
+    const half8 pv = __builtin_bit_cast(half8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+    const half8 pvl = __builtin_bit_cast(half8, u32x4{pl[0], pl[1], pl[2], pl[3]});
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       st.z = __builtin_fmaf(p[r], f16hi(d.vpa[r]), st.z);
@@ -275,6 +278,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
       const half8 a = (j < 4) ? codes_as_half8(w0, w1, w2, w3, mask)
                               : codes_as_half8(s0, s1, s2, s3, mask);
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pv, acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pvl, acc[j], 0, 0, 0);
     }
   };
 
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   // ---- INT2 page pairs: accumulate in code units (code * 4^(j%4) * 2^-24)
   if (np > 0) {
     for (int k = 0; k < np; k += PF) {
-      set_priority(total_units - k, total_units);
+      set_priority(total_units - k, total_units, rnd);
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
         if (k + j < np) process_pair(ring[j]);
@@ -332,7 +336,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     Win wa, wn;
     load_win(wb, wa);
     for (int u = wb; u < we; ++u) {
-      set_priority(kWinCost * (we - u), total_units);
+      set_priority(kWinCost * (we - u), total_units, rnd);
       if (u + 1 < we) load_win(u + 1, wn);
       if (__any(win_slot_ok(u, r16))) process_win(wa);
       wa = wn;
@@ -369,15 +373,15 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
     switch (wh) {
       case 4:
         hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 4>), grid, dim3(256), 0, stream,
-                           c, s, plan.quota, plan.passes, plan.smax, q_rot, partials);
+                           c, s, plan.quota, plan.passes, plan.smax, plan.cus, q_rot, partials);
         break;
       case 2:
         hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 2>), grid, dim3(128), 0, stream,
-                           c, s, plan.quota, plan.passes, plan.smax, q_rot, partials);
+                           c, s, plan.quota, plan.passes, plan.smax, plan.cus, q_rot, partials);
         break;
       default:
         hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 1>), grid, dim3(64), 0, stream,
-                           c, s, plan.quota, plan.passes, plan.smax, q_rot, partials);
+                           c, s, plan.quota, plan.passes, plan.smax, plan.cus, q_rot, partials);
         break;
     }
     const hipError_t e = hipGetLastError();

@@ -81,12 +81,12 @@ hipError_t launch_dequant(const CacheArgs& c, int slot, int len, int t0, int t1,
 //
 // The decode work of one (sequence, group of KV heads, query-head pass) is
 // its INT2 page pairs plus its BF16 window blocks; a window block (8 KB per
-// head) counts as kWinCost page pairs (2.5 KB per head at G = 64, plus the
-// extra MFMA work of the bf16 path).  The work is cut into splits of at most
+// head) counts as kWinCost page pairs (2.5 KB per head at G = 64): measured
+// per work-group, a window block takes about twice a pair's time.  The work is cut into splits of at most
 // quota16 / 16 units (the quota is fixed point with 4 fraction bits, so the
 // planner can fill the device closely); every split is one work-group of the
 // split launch.
-constexpr int kWinCost = 3;
+constexpr int kWinCost = 2;
 constexpr int kMaxSplits = 256;            // splits per (sequence, row), merge LDS bound
 constexpr int kMaxPairsPerSplit = 256;     // page ids staged per work-group
 constexpr int kMaxScanSeqs = 2048;         // sequences per decode launch
@@ -127,12 +127,13 @@ __host__ __device__ inline int decode_splits(DecodeWork w, int quota16, int smax
 
 // INT2 split-K decode (partials to the workspace) and the merge / un-rotation launch.
 struct DecodePlan {
-  int quota;                     // work per context split in 1/16 page pairs (a window block = 3 pairs)
+  int quota;                     // work per context split in 1/16 page pairs (a window block = kWinCost pairs)
   int smax;                      // most splits of any sequence
   int hp;                        // query heads handled per pass (<= 16 / ng)
   int passes;                    // ceil(g / hp)
   int wh;                        // KV heads (waves) per work-group
   int grid;                      // work-groups of the split launch (= its work items)
+  int cus;                       // compute units: work-group b runs in dispatch round b / cus
 };
 // Work-groups of the split kernel that fit on one compute unit.
 int decode_wgs_per_cu(const CacheArgs& c, const DecodePlan& plan);
