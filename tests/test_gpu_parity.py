@@ -181,3 +181,33 @@ def test_decode_many_splits_long_context():
         want = oracle_decode(w, 0, h, 20000, r_k, r_v)
         err, rel, ok = compare_attention(out[0, h * w.g:(h + 1) * w.g], want)
         assert ok, (h, err, rel)
+
+
+@pytest.mark.parametrize("hq, hkv, group, lens", [
+    (2, 2, 128, (300, 517)),     # one query head per KV head: two KV heads per wave, 1 head per pass
+    (4, 2, 128, (400, 90)),      # g = 2, one group
+    (4, 2, 32, (333, 700)),      # g = 2, four groups: two KV heads per wave, 2 heads per pass
+    (8, 2, 64, (260, 500)),      # g = 4, two groups: two KV heads per wave
+    (24, 6, 64, (350, 450)),     # six KV heads: three two-head waves, one work-group per row
+    (12, 3, 64, (300, 401)),     # odd KV head count: one KV head per wave
+    (48, 4, 128, (300, 340)),    # g = 12: one group, 16 heads per pass, one KV head per wave
+])
+def test_decode_head_layouts(hq, hkv, group, lens):
+    """Every (groups, heads per pass, KV heads per wave) layout of the split
+    kernel's MFMA columns against the oracle."""
+    from ultra_bit_kv_amd import SeqBatch
+    lens = list(lens)
+    w = get("c3_bs64").scaled(n_seqs=len(lens), hq=hq, hkv=hkv, group=group,
+                              lengths=("list", tuple(lens)))
+    cache = make_cache(w, lens)
+    q_rot = fill(cache, w, lens, chunk=256)
+    out = cache.decode(SeqBatch(range(len(lens)), lens), q_rot).cpu().numpy()
+    r_k, r_v = cache.host_r
+    worst = 0.0
+    for i, L in enumerate(lens):
+        for h in range(w.hkv):
+            want = oracle_decode(w, i, h, L, r_k, r_v)
+            err, rel, ok = compare_attention(out[i, h * w.g:(h + 1) * w.g], want)
+            worst = max(worst, err)
+            assert ok, (hq, hkv, group, L, h, err, rel)
+    print(f"[case] layout hq{hq} hkv{hkv} G{group} max_abs={worst:.3e}", flush=True)

@@ -46,21 +46,36 @@ int ring_cap(const oscar_kv_config& c) {
 
 int ng_of(const oscar_kv_config& c) { return kD / c.group_size; }
 
-// Query heads per decode pass: columns of a 16-wide MFMA tile are
-// (group, head) pairs, so hp * ng <= 16.  With more than one group the
-// columns of one head are hp apart and the group sum is log2(16 / hp) DPP
-// rotations, so hp = 16 / ng; with one group hp just covers g.
+// Query heads per decode pass and KV heads per wave: columns of a 16-wide
+// MFMA tile are (group, KV head of the wave, query head) triples, so
+// ng * kh * hp <= 16.  With more than one group the columns of one head are
+// kh * hp apart and the group sum is a cycle of DPP rotations, so
+// ng * kh * hp = 16.  A wave takes two KV heads when one head's columns
+// fill at most half a tile without a second pass (each pass re-reads the
+// codes), which halves the per-column work per byte.
 DecodePlan head_passes(const oscar_kv_config& c) {
   const int g = c.num_q_heads / c.num_kv_heads;
-  int hp = 16 / ng_of(c);
-  if (ng_of(c) == 1) {
-    hp = 1;
-    while (hp < g && hp < 16) hp *= 2;
+  const int ng = ng_of(c);
+  int pow2 = 1;
+  while (pow2 < g && pow2 < 16) pow2 *= 2;
+  const bool even = c.num_kv_heads % 2 == 0;
+  int hp, kh;
+  if (ng == 1) {
+    hp = pow2;
+    kh = (even && hp <= 8) ? 2 : 1;
+  } else if (even && pow2 <= 8 / ng) {
+    kh = 2;
+    hp = 8 / ng;
+  } else {
+    kh = 1;
+    hp = 16 / ng;
   }
   DecodePlan p{};
   p.hp = hp;
+  p.kh = kh;
   p.passes = (g + hp - 1) / hp;
-  p.wh = c.num_kv_heads % 4 == 0 ? 4 : (c.num_kv_heads % 2 == 0 ? 2 : 1);
+  const int waves = c.num_kv_heads / kh;   // KV head groups, one wave each
+  p.wh = waves % 4 == 0 ? 4 : (waves % 2 == 0 ? 2 : 1);
   p.quota = 1;
   p.smax = 1;
   return p;
@@ -172,7 +187,7 @@ int decode_slots_per_cu(const CacheArgs& a, const DecodePlan& plan, bool bf16) {
   int dev = 0;
   (void)hipGetDevice(&dev);
   const long long key =
-      (((((long long)dev * 2 + (bf16 ? 1 : 0)) * 8 + a.ng) * 32 + plan.hp) * 8 + plan.wh);
+      ((((((long long)dev * 2 + (bf16 ? 1 : 0)) * 8 + a.ng) * 32 + plan.hp) * 8 + plan.wh) * 4 + plan.kh);
   std::lock_guard<std::mutex> lock(mu);
   for (const auto& m : memo)
     if (m.first == key) return m.second;
@@ -369,7 +384,7 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
   int cus = 256;
   int st = check_device(&cus);
   if (st != OSCAR_OK) return st;
-  const int64_t rows = (int64_t)(a.hkv / plan.wh) * plan.passes;
+  const int64_t rows = (int64_t)(a.hkv / (plan.wh * plan.kh)) * plan.passes;
   const int64_t slots =
       std::max<int64_t>(1, (int64_t)cus * decode_slots_per_cu(a, plan, bf16) * kFillPercent / 100);
   // Every launch keeps to the split limit the workspace is sized for (that
@@ -453,6 +468,7 @@ DecodePlan bf16_plan(const oscar_bf16_cache& b) {
   DecodePlan p{};
   p.hp = hp;
   p.passes = (g + hp - 1) / hp;
+  p.kh = 1;
   p.wh = b.num_kv_heads % 4 == 0 ? 4 : (b.num_kv_heads % 2 == 0 ? 2 : 1);
   p.quota = 1;
   p.smax = 1;

@@ -38,7 +38,7 @@ constexpr int kPrefetch = 2;   // page pairs in flight per wave ahead of the one
 // work-group finds its item from a prefix sum over the sequences' item
 // counts.  Wave w owns KV head WH * group + w; all waves walk the same pages,
 // so each page is fetched as one contiguous run of WH page-head blocks.
-template <int NG, int HP, int PF, int WH>
+template <int NG, int HP, int KH, int PF, int WH>
 __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqArgs s, int quota,
                                                               int passes, int smax, int cus,
                                                               const uint16_t* __restrict__ q_rot,
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, qd = lane >> 4;
-  const int rows = (c.hkv / WH) * passes;
+  const int rows = (c.hkv / (WH * KH)) * passes;
 
   // ---- the item of this work-group
   locate_item<NT>(
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int local = __builtin_amdgcn_readfirstlane(s_item[1]);
   const int split = local / rows, row = local % rows;
   const int hgrp = row / passes, pass = row % passes;
-  const int h = hgrp * WH + wave;
+  const int hw = (hgrp * WH + wave) * KH;   // first KV head of this wave
 
   const int slot = __builtin_amdgcn_readfirstlane(s_item[2]);
   int len = __builtin_amdgcn_readfirstlane(s_item[3]);
@@ -100,11 +100,11 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int total_units = max(1, (pe - pb) + kWinCost * (we - wb));
   const int rnd = blockIdx.x / cus;   // dispatch round on its compute unit
   set_priority(total_units, total_units, rnd);
-  const uint16_t* wbase = c.win + ((size_t)(row_ok ? slot : 0) * c.hkv + h) * c.win_blocks *
+  const uint16_t* wbase = c.win + ((size_t)(row_ok ? slot : 0) * c.hkv + hw) * c.win_blocks *
                                       (2 * kPage * kD);
   struct Win {
     u32x4 kl[4], vl[4];
-    int u;
+    int u, k;   // block, KV head of the wave
   };
   auto win_block = [&](int u) { return u < sb_n ? u : c.sink_blocks + (u - sb_n); };
   auto win_slot_ok = [&](int u, int t) {
@@ -112,17 +112,19 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     const int off = (kPage * (u - sb_n) + t - b0 + c.ring_cap) % c.ring_cap;
     return off < cnt;
   };
-  auto load_win = [&](int u, Win& W) {
+  auto load_win = [&](int u, int k, Win& W) {
     W.u = u;
-    const uint16_t* bp = wbase + (size_t)win_block(u) * (2 * kPage * kD);
+    W.k = k;
+    const uint16_t* bp = wbase + ((size_t)k * c.win_blocks + win_block(u)) * (2 * kPage * kD);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       W.kl[k] = *(const u32x4*)(bp + r16 * kD + 32 * qd + 8 * k);
       W.vl[k] = *(const u32x4*)(bp + kPage * kD + 32 * (16 * qd + r16) + 8 * k);
     }
   };
-  // ---- per-lane MFMA column n = (group gi, head hl)
-  const int n = r16, gi = n / HP, hl = n % HP;
+  // ---- per-lane MFMA column n = (group gi, KV head kh of the wave, head hl of the pass)
+  const int n = r16, gi = n / (KH * HP), kh = (n / HP) % KH, hl = n % HP;
+  const int h = hw + kh;                                          // this column's KV head
   const bool colv = (gi < NG) && (hl < nh);
   const int grp_q = (NG == 1) ? 0 : (NG == 2 ? (qd >> 1) : qd);   // group of channels 32qd..32qd+31
   const bool bval = colv && (gi == grp_q);
@@ -179,7 +181,15 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     }
   }
 
-  const size_t head_off = (size_t)h * c.page_bytes;
+  // B operands of the q.k MFMAs on KV head k: this column's q' if it belongs to head k
+  half8 bqk[KH][4];
+#pragma unroll
+  for (int k = 0; k < KH; ++k)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) bqk[k][cc] = (KH == 1 || kh == k) ? bq[cc] : half8{};
+
+  const size_t head_off = (size_t)hw * c.page_bytes;              // the wave's first head
+  const size_t col_off = (size_t)kh * c.page_bytes;               // this column's head, relative
   const size_t page_stride = (size_t)c.hkv * c.page_bytes;
   const int gsel = gi < NG ? gi : 0;                              // in-bounds group for params
 
@@ -189,8 +199,8 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   SoftmaxState st{kNegInf, 0.0f, 0.0f};
 
   struct Pair {
-    u32x2 ka, kb, va, vb;
-    u32x4 kpa, kpb, vpa, vpb;
+    u32x2 ka[KH], kb[KH], va[KH], vb[KH];   // codes of each KV head of the wave
+    u32x4 kpa, kpb, vpa, vpb;                // scale / zero of this column's head and group
     int tok;      // INT2 token index of slot 0 of page A
     bool oka, okb;
   };
@@ -208,25 +218,31 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     d.tok = 32 * (pb + local);
     const uint8_t* A = c.pages + (size_t)pa * page_stride + head_off;
     const uint8_t* B = c.pages + (size_t)pbq * page_stride + head_off;
-    d.ka = *(const u32x2*)(A + koff);
-    d.kb = *(const u32x2*)(B + koff);
-    d.va = *(const u32x2*)(A + 512 + 8 * lane);
-    d.vb = *(const u32x2*)(B + 512 + 8 * lane);
-    d.kpa = *(const u32x4*)(A + poff);
-    d.kpb = *(const u32x4*)(B + poff);
-    d.vpa = *(const u32x4*)(A + vpoff);
-    d.vpb = *(const u32x4*)(B + vpoff);
+#pragma unroll
+    for (int k = 0; k < KH; ++k) {
+      d.ka[k] = *(const u32x2*)(A + k * c.page_bytes + koff);
+      d.kb[k] = *(const u32x2*)(B + k * c.page_bytes + koff);
+      d.va[k] = *(const u32x2*)(A + k * c.page_bytes + 512 + 8 * lane);
+      d.vb[k] = *(const u32x2*)(B + k * c.page_bytes + 512 + 8 * lane);
+    }
+    d.kpa = *(const u32x4*)(A + col_off + poff);
+    d.kpb = *(const u32x4*)(B + col_off + poff);
+    d.vpa = *(const u32x4*)(A + col_off + vpoff);
+    d.vpb = *(const u32x4*)(B + col_off + vpoff);
   };
 
-  auto qk_tile = [&](u32x2 kw) {
+  auto qk_tile = [&](const u32x2 (&kw)[KH]) {
     float4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      uint32_t w = (cc < 2) ? kw[0] : kw[1];
-      if (cc & 1) w >>= 8;
-      const u32x4 v = {w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u, w & 0x00C000C0u};
-      d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, v), bq[cc], d, 0, 0, 0);
-    }
+    for (int k = 0; k < KH; ++k)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        uint32_t w = (cc < 2) ? kw[k][0] : kw[k][1];
+        if (cc & 1) w >>= 8;
+        const u32x4 v = {w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u, w & 0x00C000C0u};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, v), bqk[k][cc], d, 0,
+                                                   0, 0);
+      }
     return d;
   };
 
@@ -239,13 +255,13 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
       x[r] = __builtin_fmaf(f16lo(d.kpa[r]), da[r], f16hi(d.kpa[r]) * qz);
       x[4 + r] = __builtin_fmaf(f16lo(d.kpb[r]), db[r], f16hi(d.kpb[r]) * qz);
     }
-    if constexpr (NG > 1) {   // sum the group partials: lanes n, n +- HP, ... of a 16-lane row
+    if constexpr (NG > 1) {   // sum the group partials: lanes n, n +- KH HP, ... of a 16-lane row
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        if constexpr (HP <= 8) x[k] += row_ror<8>(x[k]);
-        if constexpr (HP <= 4) x[k] += row_ror<4>(x[k]);
-        if constexpr (HP <= 2) x[k] += row_ror<2>(x[k]);
-        if constexpr (HP <= 1) x[k] += row_ror<1>(x[k]);
+        if constexpr (KH * HP <= 8) x[k] += row_ror<8>(x[k]);
+        if constexpr (KH * HP <= 4) x[k] += row_ror<4>(x[k]);
+        if constexpr (KH * HP <= 2) x[k] += row_ror<2>(x[k]);
+        if constexpr (KH * HP <= 1) x[k] += row_ror<1>(x[k]);
       }
     }
     if (!(d.oka && d.okb && d.tok + 32 <= nq)) {   // the pair holds slots past S_quant
@@ -263,22 +279,31 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     mul_by_f16lo_split(p[2], d.vpa[2], p[3], d.vpa[3], ph[1], pl[1]);
     mul_by_f16lo_split(p[4], d.vpb[0], p[5], d.vpb[1], ph[2], pl[2]);
     mul_by_f16lo_split(p[6], d.vpb[2], p[7], d.vpb[3], ph[3], pl[3]);
-    const half8 pv = __builtin_bit_cast(half8, u32x4{ph[0], ph[1], ph[2], ph[3]});
-    const half8 pvl = __builtin_bit_cast(half8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+    // B operands of the P.V MFMAs on KV head k: this column's P' if it belongs to head k
+    half8 pv[KH], pvl[KH];
+#pragma unroll
+    for (int k = 0; k < KH; ++k) {
+      const bool mine = KH == 1 || kh == k;
+      pv[k] = __builtin_bit_cast(half8, mine ? u32x4{ph[0], ph[1], ph[2], ph[3]} : u32x4{});
+      pvl[k] = __builtin_bit_cast(half8, mine ? u32x4{pl[0], pl[1], pl[2], pl[3]} : u32x4{});
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       st.z = __builtin_fmaf(p[r], f16hi(d.vpa[r]), st.z);
       st.z = __builtin_fmaf(p[4 + r], f16hi(d.vpb[r]), st.z);
     }
-    const uint32_t w0 = d.va[0], w1 = d.va[1], w2 = d.vb[0], w3 = d.vb[1];
-    const uint32_t s0 = w0 >> 8, s1 = w1 >> 8, s2 = w2 >> 8, s3 = w3 >> 8;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t mask = 0x00030003u << (2 * (j & 3));
-      const half8 a = (j < 4) ? codes_as_half8(w0, w1, w2, w3, mask)
-                              : codes_as_half8(s0, s1, s2, s3, mask);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pv, acc[j], 0, 0, 0);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pvl, acc[j], 0, 0, 0);
+    for (int k = 0; k < KH; ++k) {
+      const uint32_t w0 = d.va[k][0], w1 = d.va[k][1], w2 = d.vb[k][0], w3 = d.vb[k][1];
+      const uint32_t s0 = w0 >> 8, s1 = w1 >> 8, s2 = w2 >> 8, s3 = w3 >> 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t mask = 0x00030003u << (2 * (j & 3));
+        const half8 a = (j < 4) ? codes_as_half8(w0, w1, w2, w3, mask)
+                                : codes_as_half8(s0, s1, s2, s3, mask);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pv[k], acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pvl[k], acc[j], 0, 0, 0);
+      }
     }
   };
 
@@ -290,7 +315,8 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
                                                   0, 0, 0);
     float x[4], p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = win_slot_ok(W.u, 4 * qd + r) ? d[r] : kNegInf;
+    for (int r = 0; r < 4; ++r)   // only the columns of the block's KV head
+      x[r] = ((KH == 1 || kh == W.k) && win_slot_ok(W.u, 4 * qd + r)) ? d[r] : kNegInf;
     softmax_step<4>(x, C2, p, st, acc);
     uint32_t hi[4], lo[4];
 #pragma unroll
@@ -331,13 +357,16 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] *= 16777216.0f / (float)(1 << (2 * (j & 3)));
 
-  // ---- BF16 window blocks (true scale), one block in flight ahead
+  // ---- BF16 window blocks (true scale), each KV head of the wave in turn,
+  // one block in flight ahead
   if (wb < we) {
+    const int nw = (we - wb) * KH;
     Win wa, wn;
-    load_win(wb, wa);
-    for (int u = wb; u < we; ++u) {
+    load_win(wb, 0, wa);
+    for (int t = 0; t < nw; ++t) {
+      const int u = wb + t / KH;
       set_priority(kWinCost * (we - u), total_units, rnd);
-      if (u + 1 < we) load_win(u + 1, wn);
+      if (t + 1 < nw) load_win(wb + (t + 1) / KH, (t + 1) % KH, wn);
       if (__any(win_slot_ok(u, r16))) process_win(wa);
       wa = wn;
     }
@@ -347,7 +376,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   st.l = rows_sum(st.l);
   st.z = rows_sum(st.z);
   float* rec = partials + ((((size_t)i * c.hkv + h) * passes + pass) * smax + split) * PW;
-  if (qd == 0 && gi == 0 && hl < nh) {
+  if (qd == 0 && gi == 0 && hl < nh) {   // one lane per (KV head, query head) column
     rec[hl] = st.m;
     rec[HP + hl] = st.l;
   }
@@ -363,7 +392,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   }
 }
 
-template <int NG, int HP>
+template <int NG, int HP, int KH>
 static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                                   const uint16_t* q_rot, float* out, float* partials,
                                   int phases, hipStream_t stream) {
@@ -372,15 +401,15 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
     const dim3 grid(plan.grid);
     switch (wh) {
       case 4:
-        hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 4>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, kPrefetch, 4>), grid, dim3(256), 0, stream,
                            c, s, plan.quota, plan.passes, plan.smax, plan.cus, q_rot, partials);
         break;
       case 2:
-        hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 2>), grid, dim3(128), 0, stream,
+        hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, kPrefetch, 2>), grid, dim3(128), 0, stream,
                            c, s, plan.quota, plan.passes, plan.smax, plan.cus, q_rot, partials);
         break;
       default:
-        hipLaunchKernelGGL((int2_decode_kernel<NG, HP, kPrefetch, 1>), grid, dim3(64), 0, stream,
+        hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, kPrefetch, 1>), grid, dim3(64), 0, stream,
                            c, s, plan.quota, plan.passes, plan.smax, plan.cus, q_rot, partials);
         break;
     }
@@ -391,77 +420,89 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
   return hipSuccess;
 }
 
-template <int NG, int HP>
+template <int NG, int HP, int KH>
 static int wgs_per_cu_t(int wh) {
   int nb = 0;
   hipError_t e = hipErrorInvalidValue;
   switch (wh) {
     case 4:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, int2_decode_kernel<NG, HP, kPrefetch, 4>, 256, 0);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, int2_decode_kernel<NG, HP, KH, kPrefetch, 4>, 256, 0);
       break;
     case 2:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, int2_decode_kernel<NG, HP, kPrefetch, 2>, 128, 0);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, int2_decode_kernel<NG, HP, KH, kPrefetch, 2>, 128, 0);
       break;
     default:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, int2_decode_kernel<NG, HP, kPrefetch, 1>, 64, 0);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, int2_decode_kernel<NG, HP, KH, kPrefetch, 1>, 64, 0);
       break;
   }
   return e == hipSuccess && nb > 0 ? nb : 1;
 }
 
-template <int NG>
-static int wgs_per_cu_ng(const DecodePlan& plan) {
-  switch (plan.hp) {
-    case 1: return wgs_per_cu_t<NG, 1>(plan.wh);
-    case 2: return wgs_per_cu_t<NG, 2>(plan.wh);
-    case 4: return wgs_per_cu_t<NG, 4>(plan.wh);
-    case 8:
-      if constexpr (NG <= 2) return wgs_per_cu_t<NG, 8>(plan.wh);
-      break;
-    case 16:
-      if constexpr (NG == 1) return wgs_per_cu_t<NG, 16>(plan.wh);
-      break;
+// The (groups, heads per pass, KV heads per wave) shapes the planner uses:
+// one group: any power-of-two pass, two KV heads per wave up to 8 heads;
+// with ng groups the columns (group, KV head, head) fill the tile exactly.
+template <class F>
+static auto with_shape(int ng, int hp, int kh, F&& f) {
+  if (ng == 1) {
+    if (kh == 2) {
+      switch (hp) {
+        case 1: return f.template operator()<1, 1, 2>();
+        case 2: return f.template operator()<1, 2, 2>();
+        case 4: return f.template operator()<1, 4, 2>();
+        case 8: return f.template operator()<1, 8, 2>();
+      }
+    } else {
+      switch (hp) {
+        case 1: return f.template operator()<1, 1, 1>();
+        case 2: return f.template operator()<1, 2, 1>();
+        case 4: return f.template operator()<1, 4, 1>();
+        case 8: return f.template operator()<1, 8, 1>();
+        case 16: return f.template operator()<1, 16, 1>();
+      }
+    }
+  } else if (ng == 2) {
+    if (kh == 2 && hp == 4) return f.template operator()<2, 4, 2>();
+    if (kh == 1 && hp == 8) return f.template operator()<2, 8, 1>();
+  } else if (ng == 4) {
+    if (kh == 2 && hp == 2) return f.template operator()<4, 2, 2>();
+    if (kh == 1 && hp == 4) return f.template operator()<4, 4, 1>();
   }
-  return 1;
+  return f.fail();
 }
+
+struct OccupancyQuery {
+  const DecodePlan& plan;
+  template <int NG, int HP, int KH>
+  int operator()() const { return wgs_per_cu_t<NG, HP, KH>(plan.wh); }
+  int fail() const { return 1; }
+};
 
 int decode_wgs_per_cu(const CacheArgs& c, const DecodePlan& plan) {
-  switch (c.ng) {
-    case 1: return wgs_per_cu_ng<1>(plan);
-    case 2: return wgs_per_cu_ng<2>(plan);
-    case 4: return wgs_per_cu_ng<4>(plan);
-  }
-  return 1;
+  return with_shape(c.ng, plan.hp, plan.kh, OccupancyQuery{plan});
 }
 
-template <int NG>
-static hipError_t dispatch_hp(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
-                              const uint16_t* q_rot, float* out, float* partials,
-                              int phases, hipStream_t stream) {
-  switch (plan.hp) {
-    case 1: return launch_decode_t<NG, 1>(c, s, plan, q_rot, out, partials, phases, stream);
-    case 2: return launch_decode_t<NG, 2>(c, s, plan, q_rot, out, partials, phases, stream);
-    case 4: return launch_decode_t<NG, 4>(c, s, plan, q_rot, out, partials, phases, stream);
-    case 8:
-      if constexpr (NG <= 2) return launch_decode_t<NG, 8>(c, s, plan, q_rot, out, partials, phases, stream);
-      break;
-    case 16:
-      if constexpr (NG == 1) return launch_decode_t<NG, 16>(c, s, plan, q_rot, out, partials, phases, stream);
-      break;
+struct DecodeLaunch {
+  const CacheArgs& c;
+  const SeqArgs& s;
+  const DecodePlan& plan;
+  const uint16_t* q_rot;
+  float* out;
+  float* partials;
+  int phases;
+  hipStream_t stream;
+  template <int NG, int HP, int KH>
+  hipError_t operator()() const {
+    return launch_decode_t<NG, HP, KH>(c, s, plan, q_rot, out, partials, phases, stream);
   }
-  return hipErrorInvalidValue;
-}
+  hipError_t fail() const { return hipErrorInvalidValue; }
+};
 
 hipError_t launch_decode(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                          const uint16_t* q_rot, float* out, float* partials, int phases,
                          hipStream_t stream) {
   if (s.n_seqs <= 0 || plan.grid <= 0) return hipSuccess;
-  switch (c.ng) {
-    case 1: return dispatch_hp<1>(c, s, plan, q_rot, out, partials, phases, stream);
-    case 2: return dispatch_hp<2>(c, s, plan, q_rot, out, partials, phases, stream);
-    case 4: return dispatch_hp<4>(c, s, plan, q_rot, out, partials, phases, stream);
-  }
-  return hipErrorInvalidValue;
+  return with_shape(c.ng, plan.hp, plan.kh,
+                    DecodeLaunch{c, s, plan, q_rot, out, partials, phases, stream});
 }
 
 }  // namespace oscar

@@ -129,9 +129,10 @@ __host__ __device__ inline int decode_splits(DecodeWork w, int quota16, int smax
 struct DecodePlan {
   int quota;                     // work per context split in 1/16 page pairs (a window block = kWinCost pairs)
   int smax;                      // most splits of any sequence
-  int hp;                        // query heads handled per pass (<= 16 / ng)
+  int hp;                        // query heads handled per pass (ng * kh * hp <= 16)
   int passes;                    // ceil(g / hp)
-  int wh;                        // KV heads (waves) per work-group
+  int kh;                        // KV heads per wave (1, or 2 when a head's columns fill half a tile)
+  int wh;                        // waves per work-group
   int grid;                      // work-groups of the split launch (= its work items)
   int cus;                       // compute units: work-group b runs in dispatch round b / cus
 };
