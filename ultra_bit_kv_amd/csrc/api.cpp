@@ -390,6 +390,7 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
   // Every launch keeps to the split limit the workspace is sized for (that
   // of a full launch), so a short last launch fits in it too.
   const int cap = max_splits(sh, std::min(n_seqs, kMaxScanSeqs));
+  static thread_local ItemOrder order;
   // Launches of at most kMaxScanSeqs sequences, in stream order.
   for (int s0 = 0; s0 < n_seqs; s0 += kMaxScanSeqs) {
     const int ns = std::min(kMaxScanSeqs, n_seqs - s0);
@@ -432,6 +433,39 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
     plan.smax = (int)smax;
     plan.grid = (int)items_of(quota);
     plan.cus = cus;
+    // Deal the items out largest first: work-group b takes the b-th largest
+    // in its dispatch round, rounds alternating in direction, so the items
+    // sharing a compute unit (b, b + cus, ...) add up to about equal work.
+    order.n = 0;
+    if (plan.grid <= kMaxOrder) {
+      std::vector<std::pair<int, int>> items;   // (work units, item)
+      items.reserve(plan.grid);
+      int64_t base = 0;
+      for (int i = 0; i < ns; ++i) {
+        const DecodeWork w =
+            decode_work(seq_lens_host[s0 + i], a.s_sink, a.s_keep, a.s_flush, a.ring_cap);
+        const int nsp = (int)splits_of(cost[i], quota);
+        for (int sp = 0; sp < nsp; ++sp) {
+          const int pb = (int)((int64_t)sp * w.n_pairs / nsp), pe = (int)((int64_t)(sp + 1) * w.n_pairs / nsp);
+          const int wb = (int)((int64_t)sp * w.n_wu / nsp), we = (int)((int64_t)(sp + 1) * w.n_wu / nsp);
+          const int units = (pe - pb) + kWinCost * (we - wb);
+          for (int r = 0; r < rows; ++r) items.emplace_back(units, (int)((base + sp) * rows + r));
+        }
+        base += nsp;
+      }
+      std::stable_sort(items.begin(), items.end(),
+                       [](const std::pair<int, int>& x, const std::pair<int, int>& y) {
+                         return x.first > y.first;
+                       });
+      for (int b = 0; b < plan.grid; ++b) {
+        const int r = b / cus, col = b % cus;
+        const int in_round = std::min(cus, plan.grid - r * cus);   // items of this round
+        const int k = r * cus + ((r & 1) ? in_round - 1 - col : col);
+        order.idx[b] = (uint16_t)items[k].second;
+      }
+      order.n = plan.grid;
+    }
+    plan.order = &order;
     const SeqArgs sa{seq_slots + s0, seq_lens + s0, nullptr, ns};
     const size_t qo = (size_t)s0 * a.hq * kD;
     const uint16_t* qs = q ? q + qo : nullptr;

@@ -130,14 +130,14 @@ __device__ __forceinline__ void set_priority(int remaining, int total, int round
   else __builtin_amdgcn_s_setprio(0);
 }
 
-// The work item of this work-group in a compact grid: items are numbered
+// Where work item `item` of a compact grid lies: items are numbered
 // sequence-major and sequence k has items_of(slot, len) of them, so a
 // block-wide prefix sum over the sequences' counts finds the sequence.
 // s_item receives {sequence, item within it, its slot, its length}, or
 // s_item[0] = -1 when the device lengths give fewer items than the grid.
 // Ends with a barrier.
 template <int NT, class F>
-__device__ __forceinline__ void locate_item(const SeqArgs& s, F items_of, int* s_wsum,
+__device__ __forceinline__ void locate_item(const SeqArgs& s, F items_of, int item, int* s_wsum,
                                             int* s_item) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = s.n_seqs, per = (n + NT - 1) / NT;
@@ -155,7 +155,6 @@ __device__ __forceinline__ void locate_item(const SeqArgs& s, F items_of, int* s
   __syncthreads();
   int off = incl - run;
   for (int w2 = 0; w2 < wave; ++w2) off += s_wsum[w2];
-  const int item = blockIdx.x;
   for (int k = k0; k < k1; ++k) {
     const int sl = s.slots[k], ln = s.lens[k];
     const int q = items_of(sl, ln);

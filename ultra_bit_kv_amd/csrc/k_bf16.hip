@@ -29,7 +29,7 @@ constexpr int kBfPrefetch = 2;   // pages in flight per wave ahead of the one pr
 
 template <int HP, int PF, int WH>
 __global__ __launch_bounds__(64 * WH) void bf16_decode_kernel(CacheArgs c, SeqArgs s, int quota,
-                                                              int passes, int smax, int cus,
+                                                              int passes, int smax, int cus, ItemOrder order,
                                                               const uint16_t* __restrict__ q,
                                                               float* __restrict__ partials) {
   constexpr int PW = rec_words(HP);
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(64 * WH) void bf16_decode_kernel(CacheArgs c, SeqAr
         const DecodeWork wk = decode_work(ok ? ln : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap);
         return decode_splits(wk, quota, smax) * rows;
       },
-      s_wsum, s_item);
+      order.n > 0 ? (int)order.idx[blockIdx.x] : (int)blockIdx.x, s_wsum, s_item);
   if (s_item[0] < 0) return;   // uniform
   const int i = __builtin_amdgcn_readfirstlane(s_item[0]);
   const int local = __builtin_amdgcn_readfirstlane(s_item[1]);
@@ -194,7 +194,7 @@ template <int HP, int WH>
 static void launch_split_t(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                            const uint16_t* q, float* partials, hipStream_t stream) {
   hipLaunchKernelGGL((bf16_decode_kernel<HP, kBfPrefetch, WH>), dim3(plan.grid), dim3(64 * WH), 0,
-                     stream, c, s, plan.quota, plan.passes, plan.smax, plan.cus, q, partials);
+                     stream, c, s, plan.quota, plan.passes, plan.smax, plan.cus, *plan.order, q, partials);
 }
 
 template <int HP>

@@ -40,7 +40,7 @@ constexpr int kPrefetch = 2;   // page pairs in flight per wave ahead of the one
 // so each page is fetched as one contiguous run of WH page-head blocks.
 template <int NG, int HP, int KH, int PF, int WH>
 __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqArgs s, int quota,
-                                                              int passes, int smax, int cus,
+                                                              int passes, int smax, int cus, ItemOrder order,
                                                               const uint16_t* __restrict__ q_rot,
                                                               float* __restrict__ partials) {
   constexpr int PW = rec_words(HP);   // floats per partial record
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
         const DecodeWork wk = decode_work(ok ? ln : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap);
         return decode_splits(wk, quota, smax) * rows;
       },
-      s_wsum, s_item);
+      order.n > 0 ? (int)order.idx[blockIdx.x] : (int)blockIdx.x, s_wsum, s_item);
   if (s_item[0] < 0) return;   // uniform: the device lengths give fewer items than the grid
   const int i = __builtin_amdgcn_readfirstlane(s_item[0]);
   const int local = __builtin_amdgcn_readfirstlane(s_item[1]);
@@ -402,15 +402,18 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
     switch (wh) {
       case 4:
         hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, kPrefetch, 4>), grid, dim3(256), 0, stream,
-                           c, s, plan.quota, plan.passes, plan.smax, plan.cus, q_rot, partials);
+                           c, s, plan.quota, plan.passes, plan.smax, plan.cus, *plan.order, q_rot,
+                           partials);
         break;
       case 2:
         hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, kPrefetch, 2>), grid, dim3(128), 0, stream,
-                           c, s, plan.quota, plan.passes, plan.smax, plan.cus, q_rot, partials);
+                           c, s, plan.quota, plan.passes, plan.smax, plan.cus, *plan.order, q_rot,
+                           partials);
         break;
       default:
         hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, kPrefetch, 1>), grid, dim3(64), 0, stream,
-                           c, s, plan.quota, plan.passes, plan.smax, plan.cus, q_rot, partials);
+                           c, s, plan.quota, plan.passes, plan.smax, plan.cus, *plan.order, q_rot,
+                           partials);
         break;
     }
     const hipError_t e = hipGetLastError();

@@ -125,6 +125,17 @@ __host__ __device__ inline int decode_splits(DecodeWork w, int quota16, int smax
   return n < smax ? n : smax;
 }
 
+// Order in which the work-groups of a split launch take its work items:
+// work-group b takes item idx[b] (n > 0), or item b (n = 0).  Work-group b
+// of a launch that fills the device runs on compute unit b % cus, so the
+// planner deals the items out largest first, in alternating directions, to
+// even out the work of each compute unit.
+constexpr int kMaxOrder = 1024;
+struct ItemOrder {
+  int n;
+  uint16_t idx[kMaxOrder];
+};
+
 // INT2 split-K decode (partials to the workspace) and the merge / un-rotation launch.
 struct DecodePlan {
   int quota;                     // work per context split in 1/16 page pairs (a window block = kWinCost pairs)
@@ -135,6 +146,7 @@ struct DecodePlan {
   int wh;                        // waves per work-group
   int grid;                      // work-groups of the split launch (= its work items)
   int cus;                       // compute units: work-group b runs in dispatch round b / cus
+  const ItemOrder* order;        // work item of each work-group (host memory, passed by value)
 };
 // Work-groups of the split kernel that fit on one compute unit.
 int decode_wgs_per_cu(const CacheArgs& c, const DecodePlan& plan);
