@@ -343,6 +343,26 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
   uint16_t* stage_k = (uint16_t*)ws;
   uint16_t* stage_v = (uint16_t*)(ws + staging_bytes(c, n_tok) / 2);
 
+  // One launch for one-token appends (decode steps): no new row is flushed
+  // in the same call and no new row lands on a ring slot the flush reads.
+  bool one = true;
+  for (int i = 0; one && i < n_seqs; ++i) {
+    const int64_t n_new = (int64_t)cu_new_host[i + 1] - cu_new_host[i];
+    const int64_t lb = len_before_host[i];
+    one = n_new == 1 && (lb < s_quant(lb, c) || s_quant(lb + 1, c) <= lb) &&
+          lb - s_quant(lb, c) < a.ring_cap;
+  }
+  if (one) {
+    RotateJobs jobs{};
+    jobs.job[0] = RotateJob{k, cache->r_k, nullptr, k_rot, c.num_kv_heads, 1};
+    jobs.job[1] = RotateJob{v, cache->r_v, nullptr, v_rot, c.num_kv_heads, 1};
+    jobs.n = 2;
+    if (q_rot)
+      jobs.job[jobs.n++] = RotateJob{q, cache->r_k, q_rot, nullptr, c.num_q_heads,
+                                     c.num_q_heads / c.num_kv_heads};
+    return hip_status(
+        launch_append_one(a, clip, sa, jobs, (int)total_q, stage_k, stage_v, sm));
+  }
   // 1. rotate new rows: keys and values to staging, queries straight to q_rot
   RotateJobs jobs{};
   jobs.job[0] = RotateJob{k, cache->r_k, stage_k, k_rot, c.num_kv_heads, 1};

@@ -17,7 +17,7 @@
 // one element); the quantile, step and zero point are computed in fp64 with
 // contraction disabled, rounded once to fp16, and codes are decided against
 // the exact thresholds zero + (k - 1/2) scale.
-#include "device_common.h"
+#include "rotate_common.h"
 
 namespace oscar {
 
@@ -262,6 +262,89 @@ hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* st
   if (max_new <= 0 || s.n_seqs <= 0) return hipSuccess;
   dim3 grid(max_new, c.hkv, s.n_seqs);
   hipLaunchKernelGGL(place_kernel, grid, dim3(128), 0, stream, c, s, stage_k, stage_v);
+  return hipGetLastError();
+}
+
+// Appends of exactly one token per sequence in which no new row is flushed
+// and the new rows' ring slots are not among the flushed ones (every decode
+// step with S_keep >= 1): rotation, flush and placement in one launch.
+// Work-groups [0, total_q Hkv) quantize flushed ring rows; the others rotate
+// the new rows, 32 output columns each, writing keys and values straight
+// into their window slot and queries to q_rot.  jobs: 0 = keys, 1 = values,
+// 2 = queries (optional); dst_b of keys / values receives the rotated rows
+// if not null.
+__global__ __launch_bounds__(128) void append_one_kernel(CacheArgs c, ClipArgs clip, SeqArgs s,
+                                                         RotateJobs jobs, int total_q,
+                                                         const uint16_t* __restrict__ stage_k,
+                                                         const uint16_t* __restrict__ stage_v) {
+  __shared__ uint16_t xs[16][kD + 8];
+  const int nq = total_q * c.hkv;
+  int b = blockIdx.x;
+  if (b < nq) {   // uniform
+    quantize_item(c, clip, s, stage_k, stage_v, b / c.hkv, b % c.hkv);
+    return;
+  }
+  b -= nq;
+  const int n_tok = s.n_seqs;   // token t is sequence t's new token
+  const int blocks = (n_tok + 15) / 16;
+  const int z = b % 4;
+  b /= 4;
+  const int tb = b % blocks;
+  int y = b / blocks;
+  int job = 0;
+  RotateJob jd = jobs.job[0];
+  if (y >= jobs.job[0].heads) {
+    y -= jobs.job[0].heads;
+    job = 1;
+    jd = jobs.job[1];
+    if (jobs.n > 2 && y >= jobs.job[1].heads) {
+      y -= jobs.job[1].heads;
+      job = 2;
+      jd = jobs.job[2];
+    }
+  }
+  const int h = y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = 32 * z + 16 * wave + (lane & 15);
+  float rb[kD / 4];
+  load_r_slice(jd.r + (size_t)(h / jd.g) * kD * kD, j, rb);
+  auto out = [&](int tok, int col, uint16_t bits) {
+    const size_t o = ((size_t)tok * jd.heads + h) * kD + col;
+    if (job == 2) {
+      jd.dst_a[o] = bits;
+      return;
+    }
+    if (jd.dst_b) jd.dst_b[o] = bits;
+    const int slot = s.slots[tok];
+    const int p = s.lens[tok];   // the new token's position
+    if (slot < 0 || slot >= c.max_seqs || p < 0) return;
+    int blk, tt;
+    if (p < c.s_sink) {
+      blk = p / kPage;
+      tt = p % kPage;
+    } else if (p >= s_quant_of(p + 1, c.s_sink, c.s_keep, c.s_flush)) {
+      const int r = (p - c.s_sink) % c.ring_cap;
+      blk = c.sink_blocks + r / kPage;
+      tt = r % kPage;
+    } else {
+      return;   // excluded by the host: flushed in the same call
+    }
+    uint16_t* wb = c.win + (((size_t)slot * c.hkv + h) * c.win_blocks + blk) * (2 * kPage * kD);
+    if (job == 0) wb[tt * kD + col] = bits;
+    else wb[kPage * kD + v_window_index(tt, col)] = bits;
+  };
+  rotate_block<128>(jd.src, jd.heads, h, 16 * tb, n_tok, j, rb, xs, out);
+}
+
+hipError_t launch_append_one(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
+                             const RotateJobs& jobs, int total_q, const uint16_t* stage_k,
+                             const uint16_t* stage_v, hipStream_t stream) {
+  if (s.n_seqs <= 0) return hipSuccess;
+  int rows = 0;
+  for (int k = 0; k < jobs.n; ++k) rows += jobs.job[k].heads;
+  const long long grid = (long long)total_q * c.hkv + 4LL * ((s.n_seqs + 15) / 16) * rows;
+  hipLaunchKernelGGL(append_one_kernel, dim3((unsigned)grid), dim3(128), 0, stream, c, clip, s,
+                     jobs, total_q, stage_k, stage_v);
   return hipGetLastError();
 }
 

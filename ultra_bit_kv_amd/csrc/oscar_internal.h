@@ -73,6 +73,13 @@ hipError_t launch_flush_place(const CacheArgs& c, const ClipArgs& clip, const Se
 hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* stage_k,
                         const uint16_t* stage_v, int max_new, hipStream_t stream);
 
+// One-token append in one launch (rotate, flush, place): every sequence
+// appends exactly one token, none is flushed in the same call and no new row
+// lands on a ring slot the flush reads.  jobs: keys, values, queries (opt.).
+hipError_t launch_append_one(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
+                             const RotateJobs& jobs, int total_q, const uint16_t* stage_k,
+                             const uint16_t* stage_v, hipStream_t stream);
+
 // Decoded rows of one cache row.
 hipError_t launch_dequant(const CacheArgs& c, int slot, int len, int t0, int t1, float* k_out,
                           float* v_out, hipStream_t stream);

@@ -1,0 +1,67 @@
+// One 16-token block of rows of one head through a fixed rotation on the
+// fp64 matrix cores, shared by the rotation launch and the one-token append
+// launch.
+//
+// OSCAR summary page, section 4 and appendix B: rows are rotated by the fixed
+// per-layer, per-head rotation before they are written to the cache; WUSH-KV
+// notes, "method step details": the key transform is applied after RoPE to
+// every new key and every new query (queries use their KV head's R_K).
+//
+// Each product x_i * R_ij (bf16 significand x fp32 significand) is exact in
+// fp64 and the 128-term sum is accumulated in fp64, so the final bf16 rounding
+// is the rounding of the exact dot product (barring a tie closer than the fp64
+// accumulation error, ~1e-14 relative).  v_mfma_f64_16x16x4f64 computes each
+// output as a chain of fused multiply-adds in ascending k starting from the
+// accumulator, so 32 chained instructions give exactly the sequential fp64
+// FMA chain over k = 0..127 for a 16-token x 16-column tile.  Lane l supplies
+// A[i = l % 16][k = l / 16], B[k = l / 16][j = l % 16] and receives
+// D[i = l / 16 + 4 v][j = l % 16], v = 0..3 (checked on gfx950).
+#pragma once
+#include "device_common.h"
+
+namespace oscar {
+
+typedef double double4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_r __attribute__((ext_vector_type(4)));
+
+// This lane's share of the B operands: R[4 kb + l / 16][j] for kb = 0..31.
+__device__ __forceinline__ void load_r_slice(const float* R, int j, float (&rb)[kD / 4]) {
+  const int kq = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int kb = 0; kb < kD / 4; ++kb) rb[kb] = R[(size_t)(4 * kb + kq) * kD + j];
+}
+
+// Rotates rows t0 .. t0 + 15 (those < n_tok) of head h of src
+// ([n_tok][heads][128] bf16); a work-group of NT threads stages the rows in
+// xs, each wave produces the 16 output columns its lanes' rb slices hold
+// (column j of lane l), and out(tok, j, bf16 bits) stores the results.  Ends
+// with a barrier (xs may be reused).
+template <int NT, class Out>
+__device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ src, int heads, int h,
+                                             int t0, int n_tok, int j, const float (&rb)[kD / 4],
+                                             uint16_t (*xs)[kD + 8], Out out) {
+  const int tid = threadIdx.x, lane = tid & 63, kq = lane >> 4;
+  // staging: 16 rows x 16 chunks of 8 values
+#pragma unroll
+  for (int e = tid; e < 16 * 16; e += NT) {
+    const int xrow = e / 16, xc = 8 * (e % 16);
+    u32x4_r xw = {0u, 0u, 0u, 0u};
+    if (t0 + xrow < n_tok) xw = *(const u32x4_r*)(src + ((size_t)(t0 + xrow) * heads + h) * kD + xc);
+    *(u32x4_r*)(&xs[xrow][xc]) = xw;
+  }
+  __syncthreads();
+  double4_t acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int kb = 0; kb < kD / 4; ++kb) {
+    const double a = (double)bf16_bits_to_f32(xs[lane & 15][4 * kb + kq]);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)rb[kb], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int tok = t0 + kq + 4 * v;
+    if (tok < n_tok) out(tok, j, f64_to_bf16_rne(acc[v]));
+  }
+  __syncthreads();   // the next block overwrites xs
+}
+
+}  // namespace oscar
