@@ -134,6 +134,16 @@ typedef struct {
   uint16_t* win;              /* [max_seqs][Hkv][NB][2][16][128] bf16 windows */
   const float* r_k;           /* [Hkv][128][128] fp32 key/query rotation */
   const float* r_v;           /* [Hkv][128][128] fp32 value rotation */
+  /* Query transform [Hkv][128][128] fp32, or NULL: queries then use r_k.  A
+   * general invertible key transform T (WUSH-KV notes, "core method": any
+   * mutually inverse pair between the two factors of K^T Q leaves the scores
+   * unchanged) takes r_k = T and r_q = T^-T, so q' . k' = q . k. */
+  const float* r_q;
+  /* Non-zero: the value transform is absorbed into the output projection
+   * (OSCAR summary s4 "KV Cache Layout", WUSH-KV notes: W_O absorbs the
+   * inverse value transform), so decode returns o' in the rotated basis and
+   * does not read r_v. */
+  int32_t out_rotated;
 } oscar_kv_cache;
 
 /* Checks a configuration; returns OSCAR_OK or the first failing OSCAR_ERR_*. */
@@ -164,7 +174,8 @@ size_t oscar_workspace_size(const oscar_kv_config* cfg, int32_t n_seqs, int64_t 
  *  device arrays must hold the same values)
  *  k, v           bf16 [cu_new[n]][Hkv][128] post-RoPE keys / values
  *  q              bf16 [cu_new[n]][Hq][128] post-RoPE queries, or NULL
- *  q_rot          bf16 [cu_new[n]][Hq][128] out: q . R_K, or NULL (needs q)
+ *  q_rot          bf16 [cu_new[n]][Hq][128] out: q . R_K (q . r_q when the cache
+ *                 has a query transform), or NULL (needs q)
  *  k_rot, v_rot   bf16 [cu_new[n]][Hkv][128] out: the rotated rows, or NULL
  * Positions that the flush rule moves to INT2 are quantized into the pages
  * (previously recent rows are read from the ring before it is overwritten),
@@ -183,7 +194,8 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
  * [OSCAR s2, s4 "Decoding Attention Kernel"; OScaR "KV cache"]
  *  seq_lens[i]    tokens in the row, including the token just appended (>= 1)
  *  q_rot          bf16 [n_seqs][Hq][128] rotated queries (from the append call)
- *  out            fp32 [n_seqs][Hq][128]: softmax(q' K^T / sqrt(128)) V . R_V^T
+ *  out            fp32 [n_seqs][Hq][128]: softmax(q' K^T / sqrt(128)) V . R_V^T, or
+ *                 without the final R_V^T when cache->out_rotated is set
  * Split-K over the context: one launch writes partial results (max, sum,
  * unnormalized output) of each context split to the workspace, a second
  * launch merges them (log-sum-exp) and applies R_V^T. */

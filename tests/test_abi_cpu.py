@@ -105,8 +105,8 @@ def test_sizes(L):
 DUMMY = ctypes.c_void_p(0x1000)
 
 
-def _cache(c):
-    return KvCache(c, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+def _cache(c, r_q=None, out_rotated=0, r_v=0x1000):
+    return KvCache(c, 0x1000, 0x1000, 0x1000, 0x1000, r_v, r_q, out_rotated)
 
 
 def _i32(a):
@@ -251,3 +251,15 @@ def test_bf16_decode_argument_checks(L):
     assert bdecode(L, b, [0], [10], q=bad) == -10
     assert bdecode(L, bcache(num_pages=0), [0], [10]) == -6            # no pages to read
     assert bdecode(L, b, [0, 3], [100 * 16, 1]) in (-9, -8, 0)         # valid: device check
+
+
+def test_query_transform_and_absorbed_output_checks(L):
+    c = cfg()
+    keep = [_i32([0]), _i32([10])]
+    dec = lambda cache: L.oscar_int2_decode_attn(ctypes.byref(cache), 1, keep[0][1], keep[1][1],
+                                                 DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 1 << 40, None)
+    assert dec(_cache(c, r_v=None)) == -1                          # un-rotation needs R_V
+    assert dec(_cache(c, r_v=None, out_rotated=1)) in (-9, -8, 0)   # absorbed: R_V not read
+    assert dec(_cache(c, r_q=DUMMY.value + 4)) == -10               # misaligned query transform
+    assert append(L, c, [0], [0], [5], cache=_cache(c, r_q=DUMMY.value + 4)) == -10
+    assert append(L, c, [0], [0], [5], cache=_cache(c, r_q=DUMMY.value)) in (-9, -8, 0)

@@ -211,3 +211,47 @@ def test_decode_head_layouts(hq, hkv, group, lens):
             worst = max(worst, err)
             assert ok, (hq, hkv, group, L, h, err, rel)
     print(f"[case] layout hq{hq} hkv{hkv} G{group} max_abs={worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("out_rotated", [False, True])
+def test_query_transform_and_absorbed_output(out_rotated):
+    """A non-orthogonal key transform T with the query transform T^-T (scores
+    unchanged), and the absorbed-R_V output (rotated basis): q' bit-exact,
+    cache rows bit-exact, attention against the oracle."""
+    from ultra_bit_kv_amd import OscarKVCache, SeqBatch
+    from oracle import rotate as orot, attention as oatt
+    from tests.oscar_testlib import page_needs
+    w = get("c3_bs64").scaled(n_seqs=2, hkv=2, hq=8, lengths=("list", (300, 517)))
+    lens = [300, 517]
+    rng = np.random.default_rng(31)
+    rk0, r_v = w.rotations()
+    scale = rng.uniform(0.7, 1.4, (w.hkv, 1, 128)).astype(np.float32)
+    t = (rk0 * scale).astype(np.float32)                          # k' = k . T
+    r_q = np.stack([np.linalg.inv(t[h].astype(np.float64)).T for h in range(w.hkv)]).astype(np.float32)
+    kk, kv = w.kappas()
+    bt, total = w.page_pool(page_needs(w, lens))
+    cache = OscarKVCache(num_q_heads=w.hq, num_kv_heads=w.hkv, group_size=w.group,
+                         s_sink=w.s_sink, s_keep=w.s_keep, s_flush=w.s_flush, max_seqs=2,
+                         max_pages_per_seq=bt.shape[1], num_pages=total, clip_k=kk, clip_v=kv,
+                         r_k=t, r_v=r_v, block_table=bt, r_q=r_q, out_rotated=out_rotated)
+    cache.host_block_table = bt
+    cache.host_r = (t, r_v)
+    q_rot = fill(cache, w, lens, chunk=128)
+    out = cache.decode(SeqBatch([0, 1], lens), q_rot).cpu().numpy()
+    qr = q_rot.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    worst = 0.0
+    for i, L in enumerate(lens):
+        want_q = orot.rotate_heads_to_bf16(w.queries(i, L - 1, L), r_q, g=w.g)[0]
+        assert np.array_equal(qr[i], want_q), i
+        for h in range(w.hkv):
+            hc = oracle_head(w, i, h, L, t, r_v)
+            _check_head(cache, w, i, h, L, hc)
+            q64 = bf16_bits_to_f64(want_q[h * w.g:(h + 1) * w.g])
+            if out_rotated:
+                want = oatt.attend(q64, hc.k_dec, hc.v_dec)
+            else:
+                want = oatt.decode_head(q64, hc.k_dec, hc.v_dec, r_v[h])
+            err, rel, ok = compare_attention(out[i, h * w.g:(h + 1) * w.g], want)
+            worst = max(worst, err)
+            assert ok, (out_rotated, i, h, err, rel)
+    print(f"[case] query transform out_rotated={out_rotated} max_abs={worst:.3e}", flush=True)

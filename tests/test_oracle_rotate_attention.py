@@ -153,3 +153,38 @@ def test_head_cache_identity_rotation_segments():
     assert np.array_equal(kd[a:b], quant.dequant_rows(c, s16, z16, 128).astype(np.float32))
     rows = hc.window_rows()
     assert sorted(rows.values()) == list(range(4)) + list(range(b, n))
+
+
+def test_general_invertible_key_transform_keeps_scores():
+    # WUSH-KV notes, "core method": a mutually inverse pair between the two
+    # factors of K^T Q leaves the scores unchanged, so a non-orthogonal key
+    # transform T pairs with the query transform T^-T (row vectors)
+    rng = np.random.default_rng(23)
+    t = _haar(rng) * rng.uniform(0.5, 2.0, 128)[None, :]   # anisotropic scaling
+    tq = np.linalg.inv(t).T
+    q = rng.standard_normal((30, 128))
+    k = rng.standard_normal((60, 128))
+    lhs = rotate.rotate_f64(q, tq) @ rotate.rotate_f64(k, t).T
+    rhs = q @ k.T
+    scale = np.linalg.norm(q, axis=1)[:, None] * np.linalg.norm(k, axis=1)[None, :]
+    assert (np.abs(lhs - rhs) <= 1e-11 * scale).all()
+    # an orthogonal T is its own inverse transpose: the query transform is R_K
+    r = _haar(rng)
+    assert np.abs(np.linalg.inv(r).T - r).max() < 1e-12
+    # the same transform keeps attention itself unchanged when values are untouched
+    v = rng.standard_normal((60, 128))
+    o = attention.attend(rotate.rotate_f64(q[:4], tq), rotate.rotate_f64(k, t), v)
+    assert np.abs(o - attention.attend(q[:4], k, v)).max() < 1e-11
+
+
+def test_absorbed_value_transform_output_basis():
+    # OSCAR summary s4 / WUSH-KV notes: with R_V folded into the output
+    # projection the decode output stays in the rotated basis: o' = o . R_V
+    rng = np.random.default_rng(24)
+    rv = _haar(rng)
+    q = rng.standard_normal((4, 128))
+    k = rng.standard_normal((40, 128))
+    v = rng.standard_normal((40, 128))
+    o_rot = attention.attend(q, k, rotate.rotate_f64(v, rv))
+    assert np.abs(o_rot - rotate.rotate_f64(attention.attend(q, k, v), rv)).max() < 1e-12
+    assert np.abs(attention.unrotate(o_rot, rv) - attention.attend(q, k, v)).max() < 1e-12

@@ -32,7 +32,7 @@ class KvConfig(ctypes.Structure):
 
 class KvCache(ctypes.Structure):
     _fields_ = [("cfg", KvConfig), ("pages", c_p), ("block_table", c_p), ("win", c_p),
-                ("r_k", c_p), ("r_v", c_p)]
+                ("r_k", c_p), ("r_v", c_p), ("r_q", c_p), ("out_rotated", c_i32)]
 
 
 class Bf16Cache(ctypes.Structure):

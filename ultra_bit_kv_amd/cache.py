@@ -68,7 +68,7 @@ class OscarKVCache:
 
     def __init__(self, *, num_q_heads, num_kv_heads, group_size, s_sink, s_keep, s_flush,
                  max_seqs, max_pages_per_seq, num_pages, clip_k, clip_v, r_k, r_v, block_table,
-                 device="cuda"):
+                 r_q=None, out_rotated=False, device="cuda"):
         cfg = KvConfig()
         cfg.head_dim = D
         cfg.num_q_heads = num_q_heads
@@ -100,8 +100,14 @@ class OscarKVCache:
         self.r_k = torch.as_tensor(np.asarray(r_k, np.float32)).to(device).contiguous()
         self.r_v = torch.as_tensor(np.asarray(r_v, np.float32)).to(device).contiguous()
         assert self.r_k.shape == (num_kv_heads, D, D) and self.r_v.shape == (num_kv_heads, D, D)
+        # optional query transform (a non-orthogonal key transform T pairs with T^-T)
+        self.r_q = (torch.as_tensor(np.asarray(r_q, np.float32)).to(device).contiguous()
+                    if r_q is not None else None)
+        assert self.r_q is None or self.r_q.shape == (num_kv_heads, D, D)
         self.st = KvCache(cfg, self.pages.data_ptr(), self.block_table.data_ptr(),
-                          self.win.data_ptr(), self.r_k.data_ptr(), self.r_v.data_ptr())
+                          self.win.data_ptr(), self.r_k.data_ptr(), self.r_v.data_ptr(),
+                          self.r_q.data_ptr() if self.r_q is not None else None,
+                          1 if out_rotated else 0)
         self.workspace = None
         self.ring_capacity = L.oscar_ring_capacity(ctypes.byref(cfg))
         self.max_seq_len = L.oscar_max_seq_len(ctypes.byref(cfg))
@@ -154,7 +160,8 @@ class OscarKVCache:
         return q_rot, k_rot, v_rot
 
     def decode(self, batch, q_rot, out=None):
-        """oscar_int2_decode_attn: fp32 [n, Hq, 128] in the original basis."""
+        """oscar_int2_decode_attn: fp32 [n, Hq, 128] in the original basis (the
+        rotated basis when the cache was built with out_rotated)."""
         assert q_rot.dtype == torch.bfloat16 and q_rot.shape == (batch.n, self.hq, D)
         if out is None:
             out = torch.empty((batch.n, self.hq, D), dtype=torch.float32, device=self.device)

@@ -135,6 +135,7 @@ CacheArgs make_args(const oscar_kv_cache& k) {
   a.win = k.win;
   a.r_k = k.r_k;
   a.r_v = k.r_v;
+  a.unrot = k.out_rotated ? 0 : 1;
   a.hq = c.num_q_heads;
   a.hkv = c.num_kv_heads;
   a.g = c.num_q_heads / c.num_kv_heads;
@@ -200,6 +201,7 @@ int decode_slots_per_cu(const CacheArgs& a, const DecodePlan& plan, bool bf16) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 bool cache_aligned(const oscar_kv_cache& k) {
   return aligned16(k.pages) && aligned16(k.win) && aligned16(k.r_k) && aligned16(k.r_v) &&
+         aligned16(k.r_q) &&
          aligned16(k.block_table);
 }
 
@@ -358,8 +360,8 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
     jobs.job[1] = RotateJob{v, cache->r_v, nullptr, v_rot, c.num_kv_heads, 1};
     jobs.n = 2;
     if (q_rot)
-      jobs.job[jobs.n++] = RotateJob{q, cache->r_k, q_rot, nullptr, c.num_q_heads,
-                                     c.num_q_heads / c.num_kv_heads};
+      jobs.job[jobs.n++] = RotateJob{q, cache->r_q ? cache->r_q : cache->r_k, q_rot, nullptr,
+                                     c.num_q_heads, c.num_q_heads / c.num_kv_heads};
     return hip_status(
         launch_append_one(a, clip, sa, jobs, (int)total_q, stage_k, stage_v, sm));
   }
@@ -369,8 +371,8 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
   jobs.job[1] = RotateJob{v, cache->r_v, stage_v, v_rot, c.num_kv_heads, 1};
   jobs.n = 2;
   if (q_rot)
-    jobs.job[jobs.n++] = RotateJob{q, cache->r_k, q_rot, nullptr, c.num_q_heads,
-                                   c.num_q_heads / c.num_kv_heads};
+    jobs.job[jobs.n++] = RotateJob{q, cache->r_q ? cache->r_q : cache->r_k, q_rot, nullptr,
+                                   c.num_q_heads, c.num_q_heads / c.num_kv_heads};
   if ((st = hip_status(launch_rotate(jobs, (int)n_tok, sm))) != OSCAR_OK) return st;
   // 2+3 in one launch when no new row lands on a ring slot the flush reads
   bool disjoint = true;
@@ -566,7 +568,8 @@ int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_
   int st = oscar_check_config(&c);
   if (st != OSCAR_OK) return st;
   if (!seq_slots_host || !seq_lens_host || !seq_slots || !seq_lens || !workspace ||
-      !cache->pages || !cache->block_table || !cache->win || !cache->r_v)
+      !cache->pages || !cache->block_table || !cache->win ||
+      (!cache->r_v && !cache->out_rotated))
     return OSCAR_ERR_NULL;
   if (((phases & kDecodeSplit) && !q_rot) || ((phases & kDecodeMerge) && !out)) return OSCAR_ERR_NULL;
   if (!aligned16(q_rot) || !aligned16(out) || !cache_aligned(*cache) || !aligned16(workspace))

@@ -419,7 +419,9 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (phases & kDecodeMerge) return launch_merge<HP, true>(c, s, plan, partials, out, stream);
+  if (phases & kDecodeMerge)
+    return c.unrot ? launch_merge<HP, true>(c, s, plan, partials, out, stream)
+                   : launch_merge<HP, false>(c, s, plan, partials, out, stream);
   return hipSuccess;
 }
 

@@ -24,6 +24,7 @@ struct CacheArgs {
   int sink_blocks, win_blocks;   // ceil(s_sink / 16), sink_blocks + ring_cap / 16
   int max_seqs, max_pages, num_pages;
   int page_bytes;                // bytes of one page-head block
+  int unrot;                     // apply R_V^T after the merge (0: output in the rotated basis)
 };
 
 struct ClipArgs {
