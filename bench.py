@@ -35,7 +35,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "int2_decode_c3_bs64_traffic.json"
 
 def decode_source_hash():
     h = hashlib.sha256()
-    for f in ("k_decode.hip", "device_common.h", "oscar_internal.h"):
+    for f in ("k_decode.hip", "decode_common.h", "device_common.h", "oscar_internal.h", "api.cpp"):
         h.update(open(os.path.join(ROOT, "ultra_bit_kv_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
