@@ -24,6 +24,7 @@ Arithmetic is fp64 unless a step names a rounding.  Modules:
 * ``layout``    -- the documented on-HBM packing of pages and window blocks.
 * ``attention`` -- O5: decode attention over the decoded cache, split + merge.
 * ``cache``     -- builds the whole decoded cache state of a sequence.
+* ``prefill``   -- O6: causal attention of a new chunk over the mixed cache.
 """
 
-from . import rounding, rotate, placement, quant, layout, attention, cache  # noqa: F401
+from . import rounding, rotate, placement, quant, layout, attention, cache, prefill  # noqa: F401
