@@ -460,9 +460,8 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
     // sharing a compute unit (b, b + cus, ...) add up to about equal work.
     order.n = 0;
     if (plan.grid <= kMaxOrder) {
-      std::vector<std::pair<int, int>> items;   // (work units, item)
+      std::vector<std::pair<int, uint32_t>> items;   // (work units, sequence << 16 | item in it)
       items.reserve(plan.grid);
-      int64_t base = 0;
       for (int i = 0; i < ns; ++i) {
         const DecodeWork w =
             decode_work(seq_lens_host[s0 + i], a.s_sink, a.s_keep, a.s_flush, a.ring_cap);
@@ -471,19 +470,22 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
           const int pb = (int)((int64_t)sp * w.n_pairs / nsp), pe = (int)((int64_t)(sp + 1) * w.n_pairs / nsp);
           const int wb = (int)((int64_t)sp * w.n_wu / nsp), we = (int)((int64_t)(sp + 1) * w.n_wu / nsp);
           const int units = (pe - pb) + kWinCost * (we - wb);
-          for (int r = 0; r < rows; ++r) items.emplace_back(units, (int)((base + sp) * rows + r));
+          for (int r = 0; r < rows; ++r)
+            items.emplace_back(units, ((uint32_t)i << 16) | (uint32_t)(sp * rows + r));
         }
-        base += nsp;
       }
       std::stable_sort(items.begin(), items.end(),
-                       [](const std::pair<int, int>& x, const std::pair<int, int>& y) {
+                       [](const std::pair<int, uint32_t>& x, const std::pair<int, uint32_t>& y) {
                          return x.first > y.first;
                        });
       for (int b = 0; b < plan.grid; ++b) {
         const int r = b / cus, col = b % cus;
         const int in_round = std::min(cus, plan.grid - r * cus);   // items of this round
         const int k = r * cus + ((r & 1) ? in_round - 1 - col : col);
-        order.idx[b] = (uint16_t)items[k].second;
+        const uint32_t it = items[k].second;
+        order.item_of[b] = it;
+        order.slot[b] = seq_slots_host[s0 + (it >> 16)];
+        order.len[b] = seq_lens_host[s0 + (it >> 16)];
       }
       order.n = plan.grid;
     }

@@ -169,6 +169,32 @@ __device__ __forceinline__ void locate_item(const SeqArgs& s, F items_of, int it
   __syncthreads();
 }
 
+// The work item of this work-group: from the host's table when the launch
+// has one, otherwise located on the device (locate_item).  Returns false
+// when the device lengths give fewer items than the grid (uniform).
+struct WgItem {
+  int seq, local, slot, len;
+};
+template <int NT, class F>
+__device__ __forceinline__ bool work_item(const SeqArgs& s, const ItemOrder& order, F items_of,
+                                          int* s_wsum, int* s_item, WgItem& it) {
+  if (order.n > 0) {
+    const uint32_t w = order.item_of[blockIdx.x];
+    it.seq = (int)(w >> 16);
+    it.local = (int)(w & 0xFFFFu);
+    it.slot = order.slot[blockIdx.x];
+    it.len = order.len[blockIdx.x];
+    return true;
+  }
+  locate_item<NT>(s, items_of, (int)blockIdx.x, s_wsum, s_item);
+  if (s_item[0] < 0) return false;
+  it.seq = __builtin_amdgcn_readfirstlane(s_item[0]);
+  it.local = __builtin_amdgcn_readfirstlane(s_item[1]);
+  it.slot = __builtin_amdgcn_readfirstlane(s_item[2]);
+  it.len = __builtin_amdgcn_readfirstlane(s_item[3]);
+  return true;
+}
+
 // Log-sum-exp merge of partial records (WUSH-KV notes, "method step
 // details": split outputs are combined by their maxima and sums).  A record
 // holds, per head, m (log2 domain), l = sum 2^(x - m) and the unnormalized

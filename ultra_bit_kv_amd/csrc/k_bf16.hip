@@ -45,22 +45,23 @@ __global__ __launch_bounds__(64 * WH) void bf16_decode_kernel(CacheArgs c, SeqAr
   const int r16 = lane & 15, qd = lane >> 4;
   const int rows = (c.hkv / WH) * passes;
 
-  locate_item<NT>(
-      s,
-      [&](int sl, int ln) {
-        const bool ok = sl >= 0 && sl < c.max_seqs && ln >= 1;
-        const DecodeWork wk = decode_work(ok ? ln : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap);
-        return decode_splits(wk, quota, smax) * rows;
-      },
-      order.n > 0 ? (int)order.idx[blockIdx.x] : (int)blockIdx.x, s_wsum, s_item);
-  if (s_item[0] < 0) return;   // uniform
-  const int i = __builtin_amdgcn_readfirstlane(s_item[0]);
-  const int local = __builtin_amdgcn_readfirstlane(s_item[1]);
+  WgItem it;
+  if (!work_item<NT>(
+          s, order,
+          [&](int sl, int ln) {
+            const bool ok = sl >= 0 && sl < c.max_seqs && ln >= 1;
+            const DecodeWork wk = decode_work(ok ? ln : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap);
+            return decode_splits(wk, quota, smax) * rows;
+          },
+          s_wsum, s_item, it))
+    return;   // uniform
+  const int i = it.seq;
+  const int local = it.local;
   const int split = local / rows, row = local % rows;
   const int hgrp = row / passes, pass = row % passes;
   const int h = hgrp * WH + wave;
-  const int slot = __builtin_amdgcn_readfirstlane(s_item[2]);
-  int len = __builtin_amdgcn_readfirstlane(s_item[3]);
+  const int slot = it.slot;
+  int len = it.len;
   const bool row_ok = slot >= 0 && slot < c.max_seqs && len >= 1;
   if (!row_ok) len = 0;
   const int nh = min(HP, c.g - pass * HP);

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
                                                               float* __restrict__ partials) {
   constexpr int PW = rec_words(HP);   // floats per partial record
   constexpr int NT = 64 * WH;
-  __shared__ int s_pages[kMaxWgPages];
+  __shared__ __align__(8) int s_pages[kMaxWgPages];
   __shared__ int s_wsum[WH];
   __shared__ int s_item[4];   // sequence, item within it, its slot and length
 
@@ -56,23 +56,24 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int rows = (c.hkv / (WH * KH)) * passes;
 
   // ---- the item of this work-group
-  locate_item<NT>(
-      s,
-      [&](int sl, int ln) {
-        const bool ok = sl >= 0 && sl < c.max_seqs && ln >= 1;
-        const DecodeWork wk = decode_work(ok ? ln : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap);
-        return decode_splits(wk, quota, smax) * rows;
-      },
-      order.n > 0 ? (int)order.idx[blockIdx.x] : (int)blockIdx.x, s_wsum, s_item);
-  if (s_item[0] < 0) return;   // uniform: the device lengths give fewer items than the grid
-  const int i = __builtin_amdgcn_readfirstlane(s_item[0]);
-  const int local = __builtin_amdgcn_readfirstlane(s_item[1]);
+  WgItem it;
+  if (!work_item<NT>(
+          s, order,
+          [&](int sl, int ln) {
+            const bool ok = sl >= 0 && sl < c.max_seqs && ln >= 1;
+            const DecodeWork wk = decode_work(ok ? ln : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap);
+            return decode_splits(wk, quota, smax) * rows;
+          },
+          s_wsum, s_item, it))
+    return;   // uniform: the device lengths give fewer items than the grid
+  const int i = it.seq;
+  const int local = it.local;
   const int split = local / rows, row = local % rows;
   const int hgrp = row / passes, pass = row % passes;
   const int hw = (hgrp * WH + wave) * KH;   // first KV head of this wave
 
-  const int slot = __builtin_amdgcn_readfirstlane(s_item[2]);
-  int len = __builtin_amdgcn_readfirstlane(s_item[3]);
+  const int slot = it.slot;
+  int len = it.len;
   const bool row_ok = slot >= 0 && slot < c.max_seqs && len >= 1;
   if (!row_ok) len = 0;
   const int nh = min(HP, c.g - pass * HP);   // valid heads in this pass
@@ -140,6 +141,12 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) wq[cc] = colv ? *(const u32x4*)(qp + 8 * cc) : z;
   }
+  // The split's first BF16 window block is loaded before anything that waits
+  // on the block table: the window blocks are processed first, while the
+  // page ids and the first INT2 page pairs are on their way.
+  const int nw = (we - wb) * KH;   // window blocks of this wave (each KV head in turn)
+  Win wa, wn;
+  if (nw > 0) load_win(wb, 0, wa);
   const int n_wg_pages = min(2 * (pe - pb), kMaxWgPages);
   for (int t = tid; t < n_wg_pages; t += 64 * WH) {
     const int pg = 2 * pb + t;
@@ -208,9 +215,19 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int koff = (r16 * 8 + 2 * qd) * 4;
   const int poff = 1024 + 4 * (16 * gsel + 4 * qd);
   const int vpoff = poff + 64 * NG;
+  // Page ids of the next pair to load, read from LDS one load ahead so the
+  // LDS latency stays off the path that issues the page loads (loads are
+  // issued in order k = 0, 1, 2, ...; the tail re-reads the last pair).
+  int nx_a = 0, nx_b = 0;
+  auto fetch_ids = [&](int k) {
+    const int local = min(k, np - 1);
+    nx_a = s_pages[2 * local];
+    nx_b = s_pages[2 * local + 1];
+  };
   auto load_pair = [&](int k, Pair& d) {
-    const int local = min(k, np - 1);                             // tail loads re-read the last pair
-    int pa = s_pages[2 * local], pbq = s_pages[2 * local + 1];
+    const int local = min(k, np - 1);
+    int pa = nx_a, pbq = nx_b;
+    fetch_ids(k + 1);
     d.oka = pa >= 0;
     d.okb = pbq >= 0;
     if (!d.oka) pa = 0;
@@ -337,39 +354,39 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   };
 
   // ---- INT2 ring: PF page pairs in flight ahead of the one being processed
+  // (issued now, so they arrive while the window blocks are processed)
   Pair ring[PF];
   if (np > 0) {
+    fetch_ids(0);
 #pragma unroll
     for (int j = 0; j < PF; ++j) load_pair(j, ring[j]);
   }
 
-  // ---- INT2 page pairs: accumulate in code units (code * 4^(j%4) * 2^-24)
+  // ---- BF16 window blocks (true scale), each KV head of the wave in turn,
+  // one block in flight ahead
+  for (int t = 0; t < nw; ++t) {
+    const int u = wb + t / KH;
+    set_priority(kWinCost * (we - u) + np, total_units, rnd);
+    if (t + 1 < nw) load_win(wb + (t + 1) / KH, (t + 1) % KH, wn);
+    if (__any(win_slot_ok(u, r16))) process_win(wa);
+    wa = wn;
+  }
+
+  // ---- INT2 page pairs: accumulate in code units (code * 4^(j%4) * 2^-24);
+  // the window sums are moved to those units and back (powers of two, exact)
   if (np > 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= (float)(1 << (2 * (j & 3))) * (1.0f / 16777216.0f);
     for (int k = 0; k < np; k += PF) {
-      set_priority(total_units - k, total_units, rnd);
+      set_priority(np - k, total_units, rnd);
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
         if (k + j < np) process_pair(ring[j]);
         load_pair(k + j + PF, ring[j]);
       }
     }
-  }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] *= 16777216.0f / (float)(1 << (2 * (j & 3)));
-
-  // ---- BF16 window blocks (true scale), each KV head of the wave in turn,
-  // one block in flight ahead
-  if (wb < we) {
-    const int nw = (we - wb) * KH;
-    Win wa, wn;
-    load_win(wb, 0, wa);
-    for (int t = 0; t < nw; ++t) {
-      const int u = wb + t / KH;
-      set_priority(kWinCost * (we - u), total_units, rnd);
-      if (t + 1 < nw) load_win(wb + (t + 1) / KH, (t + 1) % KH, wn);
-      if (__any(win_slot_ok(u, r16))) process_win(wa);
-      wa = wn;
-    }
+    for (int j = 0; j < 8; ++j) acc[j] *= 16777216.0f / (float)(1 << (2 * (j & 3)));
   }
 
   // ---- this wave's partial record: (max, sum, unnormalized o') per head of the pass

@@ -133,15 +133,21 @@ __host__ __device__ inline int decode_splits(DecodeWork w, int quota16, int smax
   return n < smax ? n : smax;
 }
 
-// Order in which the work-groups of a split launch take its work items:
-// work-group b takes item idx[b] (n > 0), or item b (n = 0).  Work-group b
-// of a launch that fills the device runs on compute unit b % cus, so the
-// planner deals the items out largest first, in alternating directions, to
-// even out the work of each compute unit.
+// Work item of each work-group of a split launch, chosen on the host (n > 0):
+// work-group b takes item `local` of sequence `seq` (item_of[b] = seq << 16 |
+// local), whose cache row and length are slot[b] and len[b] (the host copies
+// of the call's arrays, which the device copies must equal), so a
+// work-group starts its loads without reading the sequence arrays first.
+// With n = 0 work-group b takes item b and finds its sequence on the device.
+// Work-group b of a launch that fills the device runs on compute unit
+// b % cus, so the planner deals the items out largest first, in alternating
+// directions, to even out the work of each compute unit.
 constexpr int kMaxOrder = 1024;
 struct ItemOrder {
   int n;
-  uint16_t idx[kMaxOrder];
+  uint32_t item_of[kMaxOrder];
+  int32_t slot[kMaxOrder];
+  int32_t len[kMaxOrder];
 };
 
 // INT2 split-K decode (partials to the workspace) and the merge / un-rotation launch.
