@@ -10,11 +10,14 @@ oscar_int2_decode_attn over the whole cache.  The step cycles through
 each step reads a cache that is not resident in the 256 MB MALL, as in a
 multi-layer model.
 
-Prints one JSON line.  `value` = sequences decoded per second (tokens/s).
-`roofline` is for the decode split kernel (all cache traffic): algorithmic
-bytes per launch (INT2 token-heads x (64 + 1024/G) B + BF16 window
-token-heads x 512 B + block-table entries x 4 B + q' in) over its average
-duration, measured with HIP events on the stream it runs on.
+Prints one JSON line.  `value` = sequences decoded per second (tokens/s),
+from timed steps with events only at the ends of the run (an event record
+between launches adds a gap to the stream).  `roofline` is for the decode
+split kernel (all cache traffic): algorithmic bytes per launch (INT2
+token-heads x (64 + 1024/G) B + BF16 window token-heads x 512 B +
+block-table entries x 4 B + q' in) over its average duration, measured with
+HIP events around each split launch, on the stream it runs on, in a second
+timed pass of the same number of steps.
 """
 
 import argparse
@@ -219,7 +222,7 @@ def measure(w, n_layers, steps, warmup, gpu_hold_cycles=0):
 
     lens0 = w.lengths_after()                 # context of the first timed step, per layer
     n = len(lens0)
-    total_steps = warmup + steps
+    total_steps = warmup + 2 * steps
     per_layer = -(-total_steps // n_layers)
     grow = [int(L) + per_layer for L in lens0]
     t_setup = time.perf_counter()
@@ -264,8 +267,9 @@ def measure(w, n_layers, steps, warmup, gpu_hold_cycles=0):
         c = layers[s % n_layers]
         d = steps_in[s // n_layers]
         c.append(d["app"], d["k"], d["v"], d["q"], q_rot=q_rot)
-        # the decode step as its two launches, timed apart: the split kernel
-        # (all cache traffic) and the log-sum-exp merge / un-rotation
+        # the decode step as its two launches, timed apart when events are
+        # given: the split kernel (all cache traffic) and the log-sum-exp
+        # merge / un-rotation
         if ev is not None:
             ev[0].record()
         c.decode_partials(d["dec"], q_rot)
@@ -275,33 +279,42 @@ def measure(w, n_layers, steps, warmup, gpu_hold_cycles=0):
         if ev is not None:
             ev[2].record()
 
+    def timed(first, evs=None):
+        """Time `steps` steps from step index `first` (events only at the ends
+        unless per-step events are given)."""
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        # A spin kernel ahead of the timed steps keeps the GPU busy while the
+        # host queues them, so the events time the GPU's execution of the
+        # queued steps rather than the host's submission rate.
+        torch.cuda._sleep(int(gpu_hold_cycles))
+        t_start.record()
+        for j in range(steps):
+            step(first + j, evs[j] if evs is not None else None)
+        t_end.record()
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / steps
+
     for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
+    # pass 1: the whole step, no event records between its launches (each
+    # record adds a gap to the stream); pass 2: the same number of steps with
+    # events around the split and merge launches, for the per-kernel times
+    ms_step = timed(warmup)
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    # A spin kernel ahead of the timed steps keeps the GPU busy while the host
-    # queues them, so the events time the GPU's execution of the queued steps
-    # rather than the host's submission rate (which paces small steps).
-    torch.cuda._sleep(int(gpu_hold_cycles))
-    t_start.record()
-    for j in range(steps):
-        step(warmup + j, evs[j])
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / steps
+    ms_step_ev = timed(warmup + steps, evs)
     dec_ms = float(np.mean([a.elapsed_time(c) for a, b, c in evs]))
     split_ms = float(np.mean([a.elapsed_time(b) for a, b, c in evs]))
     merge_ms = float(np.mean([b.elapsed_time(c) for a, b, c in evs]))
     # algorithmic bytes of the average split launch (lengths grow during the run)
-    byts = [algorithmic_bytes(w, [int(L) + (warmup + j) // n_layers for L in lens0])
+    byts = [algorithmic_bytes(w, [int(L) + (warmup + steps + j) // n_layers for L in lens0])
             for j in range(steps)]
     bytes_per_launch = float(np.mean(byts))
-    return {"w": w, "lens0": lens0, "n": n, "ms_step": ms_step, "dec_ms": dec_ms,
-            "split_ms": split_ms, "merge_ms": merge_ms, "bytes": bytes_per_launch,
-            "setup_s": setup_s}
+    return {"w": w, "lens0": lens0, "n": n, "ms_step": ms_step, "ms_step_ev": ms_step_ev,
+            "dec_ms": dec_ms, "split_ms": split_ms, "merge_ms": merge_ms,
+            "bytes": bytes_per_launch, "setup_s": setup_s}
 
 
 def main():
@@ -359,7 +372,8 @@ def main():
             "context_max": int(lens0.max()), "layers_cycled": args.layers,
             "step": "rotate_quant_append(1 token/seq) + int2_decode_partials + int2_decode_merge",
             "decode_ms": m["dec_ms"], "decode_split_ms": m["split_ms"],
-            "decode_merge_ms": m["merge_ms"], "append_ms": m["ms_step"] - m["dec_ms"],
+            "decode_merge_ms": m["merge_ms"], "append_ms": m["ms_step_ev"] - m["dec_ms"],
+            "ms_per_step_with_kernel_events": m["ms_step_ev"],
             "decode_call_GBs": m["bytes"] / (m["dec_ms"] * 1e-3) / 1e9,
             "decode_kernel_source": src_hash,
         },
@@ -379,7 +393,8 @@ def main():
             "context": int(b["lens0"][0]), "layers_cycled": args.bs1_layers,
             "ms_per_step": b["ms_step"], "tokens_per_s": b["n"] / (b["ms_step"] * 1e-3),
             "decode_ms": b["dec_ms"], "decode_split_ms": b["split_ms"],
-            "decode_merge_ms": b["merge_ms"], "append_ms": b["ms_step"] - b["dec_ms"],
+            "decode_merge_ms": b["merge_ms"], "append_ms": b["ms_step_ev"] - b["dec_ms"],
+            "ms_per_step_with_kernel_events": b["ms_step_ev"],
             "split_GBs": b["bytes"] / (b["split_ms"] * 1e-3) / 1e9,
             "algorithmic_bytes_per_launch": b["bytes"],
         }
