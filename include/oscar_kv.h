@@ -226,6 +226,38 @@ int oscar_int2_decode_merge(const oscar_kv_cache* cache, int32_t n_seqs,
                             const int32_t* seq_slots, const int32_t* seq_lens, float* out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Chunked-prefill attention: the new tokens of each sequence, just added by
+ * oscar_rotate_quant_append, attend causally over the mixed cache.
+ * [WUSH "method step details" (inference, Algorithm 2): the chunk's rows join
+ * the cache at full precision and grouped-query attention runs over the
+ * mixed-precision cache; OSCAR s2: softmax(Q K^T / sqrt(d)) V row by row]
+ *  seq_slots, len_before, cu_new  the arguments of that append call (host and
+ *                 device copies holding the same values)
+ *  q_rot          bf16 [cu_new[n]][Hq][128] rotated queries (the append's q_rot)
+ *  k_rot, v_rot   bf16 [cu_new[n]][Hkv][128] the chunk's rotated rows (the
+ *                 append's k_rot / v_rot outputs)
+ *  out            fp32 [cu_new[n]][Hq][128]: the query at chunk row j of sequence
+ *                 i (position P = len_before[i] + j) attends to positions 0 .. P:
+ *                 positions below len_before[i] as the cache holds them after the
+ *                 append (bf16 sink / recent rows, INT2 rows as scale * code +
+ *                 zero), the chunk's rows at their bf16 values whether or not the
+ *                 append moved them to INT2; softmax(q' K^T / sqrt(128)) V . R_V^T,
+ *                 without the R_V^T when cache->out_rotated is set.
+ * Unmapped INT2 pages (block-table entries outside [0, num_pages)) are skipped
+ * as in decode.  Keys and values are staged in fp16 (INT2 rows rounded once
+ * from the fp32 dequantized value) and accumulated in fp32.  Errors:
+ * OSCAR_ERR_NULL, OSCAR_ERR_ARG (misaligned pointers, cu_new[0] != 0, negative
+ * counts, repeated slots, n_seqs outside [1, min(max_seqs, 65535)]),
+ * OSCAR_ERR_CAPACITY (slot or length beyond the cache), OSCAR_ERR_DEVICE,
+ * OSCAR_ERR_HIP.  Needs no workspace. */
+int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
+                            const int32_t* seq_slots_host, const int32_t* len_before_host,
+                            const int32_t* cu_new_host,
+                            const int32_t* seq_slots, const int32_t* len_before,
+                            const int32_t* cu_new,
+                            const uint16_t* q_rot, const uint16_t* k_rot, const uint16_t* v_rot,
+                            float* out, void* stream);
+
 /* For checking: the decoded rows of positions [tok_begin, tok_end) of one
  * cache row holding seq_len tokens, in the rotated basis: bf16 window rows
  * widened to fp32, INT2 rows as scale * code + zero rounded once to fp32.

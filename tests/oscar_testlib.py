@@ -16,7 +16,7 @@ def page_needs(w, lens):
     return [max(1, placement.n_int2_pages(int(L), w.s_sink, w.s_keep, w.s_flush)) for L in lens]
 
 
-def make_cache(w, lens, identity=False, spare_pages=0, max_seqs=None):
+def make_cache(w, lens, identity=False, spare_pages=0, max_seqs=None, out_rotated=False):
     """An empty OscarKVCache sized for sequences growing to ``lens``."""
     from ultra_bit_kv_amd import OscarKVCache
     if identity:
@@ -31,7 +31,7 @@ def make_cache(w, lens, identity=False, spare_pages=0, max_seqs=None):
                          s_sink=w.s_sink, s_keep=w.s_keep, s_flush=w.s_flush,
                          max_seqs=max_seqs or len(lens), max_pages_per_seq=bt.shape[1],
                          num_pages=total, clip_k=kk, clip_v=kv, r_k=r_k, r_v=r_v,
-                         block_table=bt)
+                         block_table=bt, out_rotated=out_rotated)
     cache.host_block_table = bt
     cache.host_r = (r_k, r_v)
     return cache

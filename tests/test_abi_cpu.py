@@ -263,3 +263,33 @@ def test_query_transform_and_absorbed_output_checks(L):
     assert dec(_cache(c, r_q=DUMMY.value + 4)) == -10               # misaligned query transform
     assert append(L, c, [0], [0], [5], cache=_cache(c, r_q=DUMMY.value + 4)) == -10
     assert append(L, c, [0], [0], [5], cache=_cache(c, r_q=DUMMY.value)) in (-9, -8, 0)
+
+
+def prefill(L, c, slots, lb, n_new, q_rot=DUMMY, k_rot=DUMMY, v_rot=DUMMY, out=DUMMY,
+            cache=None, cu=None):
+    cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32) if cu is None else np.asarray(cu, np.int32)
+    keep = [_i32(slots), _i32(lb), _i32(cu)]
+    return L.oscar_int2_prefill_attn(
+        ctypes.byref(cache or _cache(c)), len(slots), keep[0][1], keep[1][1], keep[2][1],
+        DUMMY, DUMMY, DUMMY, q_rot, k_rot, v_rot, out, None)
+
+
+def test_prefill_argument_checks(L):
+    c = cfg()
+    assert prefill(L, c, [0], [0], [5], q_rot=None) == -1
+    assert prefill(L, c, [0], [0], [5], k_rot=None) == -1
+    assert prefill(L, c, [0], [0], [5], out=None) == -1
+    assert prefill(L, c, [0], [0], [5], cache=_cache(c, r_v=0)) == -1      # un-rotation needs R_V
+    assert prefill(L, c, [0], [0], [5], out=ctypes.c_void_p(0x1004)) == -10  # misaligned
+    assert prefill(L, c, [4], [0], [5]) == -6                               # slot >= max_seqs
+    assert prefill(L, c, [1, 1], [0, 0], [5, 5]) == -10                     # duplicate slot
+    assert prefill(L, c, [0], [-1], [5]) == -10                             # negative length
+    assert prefill(L, c, [0], [0], [5], cu=[1, 6]) == -10                   # cu_new[0] != 0
+    assert prefill(L, c, [0, 1], [0, 0], [5, 5], cu=[0, 5, 3]) == -10       # negative count
+    mx = L.oscar_max_seq_len(ctypes.byref(c))
+    assert prefill(L, c, [0], [mx - 2], [3]) == -6                          # beyond the row
+    assert prefill(L, c, [0, 1, 2, 3, 0], [0] * 5, [1] * 5) == -10          # n_seqs > max_seqs
+    # without R_V the rotated-basis output is still valid; a valid call reaches
+    # the device check (a HIP error without a GPU)
+    assert prefill(L, c, [0], [0], [5], cache=_cache(c, r_v=0, out_rotated=1)) in (-9, -8, 0)
+    assert prefill(L, c, [0, 2], [100, 0], [7, 300]) in (-9, -8, 0)

@@ -62,6 +62,8 @@ _PROTOS = {
                                            c_p, c_size, c_p]),
     "oscar_int2_decode_merge": (c_i32, [ctypes.POINTER(KvCache), c_i32, c_p, c_p, c_p, c_p, c_p,
                                         c_p, c_size, c_p]),
+    "oscar_int2_prefill_attn": (c_i32, [ctypes.POINTER(KvCache), c_i32, c_p, c_p, c_p, c_p, c_p,
+                                        c_p, c_p, c_p, c_p, c_p, c_p]),
     "oscar_dequant": (c_i32, [ctypes.POINTER(KvCache), c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p]),
     "oscar_bf16_workspace_size": (c_size, [ctypes.POINTER(Bf16Cache), c_i32]),
     "oscar_bf16_paged_decode_attn": (c_i32, [ctypes.POINTER(Bf16Cache), c_i32, c_p, c_p, c_p, c_p,

@@ -14,11 +14,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liboscar_kv.so")
-SOURCES = ["api.cpp", "k_rotate.hip", "k_quant.hip", "k_dequant.hip", "k_decode.hip", "k_bf16.hip"]
+SOURCES = ["api.cpp", "k_rotate.hip", "k_quant.hip", "k_dequant.hip", "k_decode.hip", "k_bf16.hip",
+           "k_prefill.hip"]
 # The decode kernels keep their MFMA accumulators in VGPRs so the (rare) online
 # softmax rescale multiplies them in place instead of copying AGPRs each step.
 EXTRA = {"k_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "k_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "k_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "k_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 # Packed fp32 VALU ops are turned off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

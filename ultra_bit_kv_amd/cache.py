@@ -192,6 +192,22 @@ class OscarKVCache:
         check(st, "oscar_int2_decode_merge")
         return out
 
+    def prefill_attn(self, batch, q_rot, k_rot, v_rot, out=None):
+        """oscar_int2_prefill_attn for the chunk of an append made with ``batch``
+        (a SeqBatch built with n_new): fp32 [n_tok, Hq, 128]."""
+        n_tok = int(batch.cu_new[-1])
+        assert q_rot.dtype == torch.bfloat16 and q_rot.shape == (n_tok, self.hq, D)
+        assert k_rot.dtype == torch.bfloat16 and k_rot.shape == (n_tok, self.hkv, D)
+        assert v_rot.dtype == torch.bfloat16 and v_rot.shape == (n_tok, self.hkv, D)
+        if out is None:
+            out = torch.empty((n_tok, self.hq, D), dtype=torch.float32, device=self.device)
+        st = lib().oscar_int2_prefill_attn(
+            ctypes.byref(self.st), batch.n, _hp(batch.slots), _hp(batch.lens), _hp(batch.cu_new),
+            _p(batch.d_slots), _p(batch.d_lens), _p(batch.d_cu_new), _p(q_rot), _p(k_rot),
+            _p(v_rot), _p(out), current_stream())
+        check(st, "oscar_int2_prefill_attn")
+        return out
+
     def dequant(self, slot, seq_len, t0, t1):
         """oscar_dequant: decoded (k, v) fp32 [t1 - t0, Hkv, 128], rotated basis."""
         k = torch.empty((max(0, t1 - t0), self.hkv, D), dtype=torch.float32, device=self.device)

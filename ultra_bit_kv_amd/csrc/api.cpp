@@ -659,6 +659,50 @@ int oscar_bf16_paged_decode_attn(const oscar_bf16_cache* cache, int32_t n_seqs,
                          stream, kDecodeSplit | kDecodeMerge);
 }
 
+int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
+                            const int32_t* seq_slots_host, const int32_t* len_before_host,
+                            const int32_t* cu_new_host, const int32_t* seq_slots,
+                            const int32_t* len_before, const int32_t* cu_new,
+                            const uint16_t* q_rot, const uint16_t* k_rot, const uint16_t* v_rot,
+                            float* out, void* stream) {
+  if (!cache) return OSCAR_ERR_NULL;
+  const oscar_kv_config& c = cache->cfg;
+  int st = oscar_check_config(&c);
+  if (st != OSCAR_OK) return st;
+  if (!seq_slots_host || !len_before_host || !cu_new_host || !seq_slots || !len_before ||
+      !cu_new || !q_rot || !k_rot || !v_rot || !out || !cache->pages || !cache->block_table ||
+      !cache->win || (!cache->out_rotated && !cache->r_v))
+    return OSCAR_ERR_NULL;
+  if (!aligned16(q_rot) || !aligned16(k_rot) || !aligned16(v_rot) || !aligned16(out) ||
+      !cache_aligned(*cache))
+    return OSCAR_ERR_ARG;
+  if (n_seqs < 1 || n_seqs > c.max_seqs || n_seqs > 65535) return OSCAR_ERR_ARG;
+  if (cu_new_host[0] != 0) return OSCAR_ERR_ARG;
+  const int64_t max_len = oscar_max_seq_len(&c);
+  const int g = c.num_q_heads / c.num_kv_heads;
+  std::vector<char> seen(c.max_seqs, 0);
+  int tiles = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int slot = seq_slots_host[i];
+    if (slot < 0 || slot >= c.max_seqs) return OSCAR_ERR_CAPACITY;
+    if (seen[slot]) return OSCAR_ERR_ARG;
+    seen[slot] = 1;
+    const int64_t n_new = (int64_t)cu_new_host[i + 1] - cu_new_host[i];
+    const int64_t lb = len_before_host[i];
+    if (n_new < 0 || lb < 0) return OSCAR_ERR_ARG;
+    if (lb + n_new > max_len || int2_pages(lb + n_new, c) > c.max_pages_per_seq)
+      return OSCAR_ERR_CAPACITY;
+    if (n_new * g > ((int64_t)1 << 30)) return OSCAR_ERR_ARG;
+    tiles = std::max(tiles, prefill_tiles((int)n_new, g));
+  }
+  const int64_t n_tok = cu_new_host[n_seqs];
+  if (n_tok > (int64_t)1 << 30) return OSCAR_ERR_ARG;
+  if ((st = check_device()) != OSCAR_OK) return st;
+  if (n_tok == 0) return OSCAR_OK;
+  const PrefillArgs pa{seq_slots, len_before, cu_new, q_rot, k_rot, v_rot, out, n_seqs, tiles};
+  return hip_status(launch_prefill(make_args(*cache), pa, (hipStream_t)stream));
+}
+
 int oscar_dequant(const oscar_kv_cache* cache, int32_t seq_slot, int32_t seq_len,
                   int32_t tok_begin, int32_t tok_end, float* k_out, float* v_out, void* stream) {
   if (!cache) return OSCAR_ERR_NULL;

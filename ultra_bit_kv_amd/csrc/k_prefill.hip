@@ -1,0 +1,281 @@
+// Chunked-prefill attention over the mixed INT2 / BF16 paged cache (gfx950).
+//
+// What is computed (WUSH-KV notes, "method step details", inference
+// (Algorithm 2): new keys and queries of a chunk are transformed, the chunk
+// joins the cache at full precision and grouped-query attention runs over the
+// mixed-precision cache; OSCAR summary page, section 2 "Attention and KV
+// cache": row-wise softmax(Q K^T / sqrt(d)) V):
+//   the query at chunk row j of a sequence (position P = len_before + j)
+//   attends to positions 0 .. P: positions below len_before as the cache holds
+//   them after the chunk's append (bf16 sink / recent rows, INT2 rows as
+//   scale * code + zero), the chunk's own rows at their bf16 rotated values
+//   (the append's k_rot / v_rot outputs), then o = o' . R_V^T.
+//
+// Work-group = (sequence, tile of 64 query rows, KV head); query row r of a
+// (sequence, KV head) is (chunk row r / g, head r % g), and wave w owns rows
+// 16w .. 16w+15 as the 16 columns of its MFMA tiles.  The key stream is cut
+// into 16-position blocks; the work-group stages each block in LDS as fp16
+// (K rows [token][channel] as fp16 hi + lo, V transposed [channel][token]),
+// decoding every
+// position from wherever it lives (sink, INT2 page, ring, chunk rows), one
+// block ahead in registers.  Per block and wave:
+//   S^T = K . Q^T   v_mfma_f32_16x16x32_f16, A = keys (hi, then lo), B = the
+//                   wave's query rows (fp16 from bf16, exact in the normal range)
+//   online softmax per column (query row), causal mask p <= P
+//   O^T += V^T . P^T  v_mfma_f32_16x16x16f16 with P split into fp16 hi + lo
+// then the normalized o' rows go through LDS and the fp32 matrix cores apply
+// R_V^T (wave w computes output channels 32w .. 32w+31 of all 64 rows).
+#include "decode_common.h"
+
+namespace oscar {
+
+namespace {
+
+constexpr int kPfRows = 64;    // query rows per work-group (4 waves x 16 columns)
+constexpr int kKRow = kD + 8;  // staged key row in fp16 (padded: rows start 4 banks apart)
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
+// One position's K and V row slice (8 channels) as fetched from HBM, before
+// decoding: kind 0 = zero row (past the end or an unmapped page), 1 = bf16
+// words, 2 = INT2 code words with their scale / zero words.
+struct RawSlice {
+  u32x4 k, v;
+  int kind;
+};
+
+__device__ __forceinline__ void bf16x2_to_f32(uint32_t w, float& lo, float& hi) {
+  lo = __uint_as_float(w << 16);
+  hi = __uint_as_float(w & 0xFFFF0000u);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void prefill_attn_kernel(CacheArgs c, PrefillArgs a) {
+  __shared__ __align__(16) _Float16 sk[kPage][kKRow];   // staged keys [token][channel], fp16 part
+  __shared__ __align__(16) _Float16 skl[kPage][kKRow];  // remainders k - fp16(k), fp16
+  __shared__ __align__(16) _Float16 svt[kD][kPage];     // staged values [channel][token]
+  __shared__ __align__(16) float fin[kPfRows][kD + 4];  // normalized o' rows
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, qd = lane >> 4;
+  const int i = blockIdx.y, h = blockIdx.z;
+  const int tile = a.tiles - 1 - (int)blockIdx.x;   // longest causal ranges first
+  const int slot = a.slots[i], lb = a.len_before[i];
+  const int t0 = a.cu_new[i], n_new = a.cu_new[i + 1] - t0;
+  const int rows = n_new * c.g;
+  if (slot < 0 || slot >= c.max_seqs || lb < 0 || n_new <= 0 || tile * kPfRows >= rows) return;
+  const int len = lb + n_new;                                     // cache length after the append
+  const int sq = s_quant_of(len, c.s_sink, c.s_keep, c.s_flush);  // INT2 below this position
+  const int32_t* bt = c.block_table + (size_t)slot * c.max_pages;
+  const uint16_t* wrow = c.win + ((size_t)slot * c.hkv + h) * c.win_blocks * (2 * kPage * kD);
+
+  // ---- this lane's query row (MFMA column) and the keys the work-group reads
+  const int row = tile * kPfRows + 16 * wave + r16;
+  const bool colv = row < rows;
+  const int pj = colv ? row / c.g : 0, hl = colv ? row % c.g : 0;
+  const int qpos = lb + pj;
+  const int wg_last = min(rows, (tile + 1) * kPfRows) - 1;
+  const int kend = lb + wg_last / c.g + 1;                        // keys [0, kend)
+  const int w_last = min(rows, tile * kPfRows + 16 * wave + 16) - 1;
+  const int wave_kend = w_last >= tile * kPfRows + 16 * wave ? lb + w_last / c.g + 1 : 0;
+
+  half8 bq[4];
+  {
+    const uint16_t* qp = a.q_rot + ((size_t)(t0 + pj) * c.hq + (size_t)h * c.g + hl) * kD + 8 * qd;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const u32x4 w = colv ? *(const u32x4*)(qp + 32 * cc) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float lo, hi;
+        bf16x2_to_f32(w[e], lo, hi);
+        bq[cc][2 * e] = (_Float16)lo;
+        bq[cc][2 * e + 1] = (_Float16)hi;
+      }
+    }
+  }
+
+  // ---- staging: thread (token t, channels 8u .. 8u+7) of a 16-position block
+  const int st_t = tid >> 4, st_u = tid & 15;
+  auto fetch = [&](int p0, RawSlice& r) {
+    const int p = p0 + st_t;
+    r.kind = 0;
+    r.k = r.v = u32x4{0u, 0u, 0u, 0u};
+    if (p >= len) return;
+    if (p >= lb) {   // a row of this chunk: the append's bf16 rotated row
+      const size_t o = ((size_t)(t0 + p - lb) * c.hkv + h) * kD + 8 * st_u;
+      r.k = *(const u32x4*)(a.k_rot + o);
+      r.v = *(const u32x4*)(a.v_rot + o);
+      r.kind = 1;
+    } else if (p < c.s_sink || p >= sq) {   // sink slot p, or ring slot (p - S_sink) mod R
+      const int bs = p < c.s_sink ? p : c.sink_blocks * kPage + (p - c.s_sink) % c.ring_cap;
+      const uint16_t* blk = wrow + (size_t)(bs / kPage) * (2 * kPage * kD);
+      const int tt = bs % kPage;
+      r.k = *(const u32x4*)(blk + tt * kD + 8 * st_u);
+      // V part: (token tt, channel 8u + j) at 32 (16 (tt / 4) + u) + 4 j + tt % 4
+      const uint16_t* vb = blk + kPage * kD + 32 * (16 * (tt >> 2) + st_u) + (tt & 3);
+      r.v = u32x4{(uint32_t)vb[0] | ((uint32_t)vb[4] << 16), (uint32_t)vb[8] | ((uint32_t)vb[12] << 16),
+                  (uint32_t)vb[16] | ((uint32_t)vb[20] << 16), (uint32_t)vb[24] | ((uint32_t)vb[28] << 16)};
+      r.kind = 1;
+    } else {   // INT2: logical page (p - S_sink) / 16, slot (p - S_sink) % 16
+      const int m = (p - c.s_sink) / kPage, sl = (p - c.s_sink) % kPage;
+      const int ph = m < c.max_pages ? bt[m] : -1;
+      if (ph < 0 || ph >= c.num_pages) return;
+      const uint32_t* pg = (const uint32_t*)(c.pages + ((size_t)ph * c.hkv + h) * c.page_bytes);
+      const int gr = (8 * st_u) / c.group;
+      r.k = u32x4{pg[8 * sl + (st_u >> 1)] >> (16 * (st_u & 1)), pg[256 + 16 * gr + sl], 0u, 0u};
+      r.v = u32x4{pg[128 + 2 * (16 * (sl >> 2) + st_u) + ((sl & 3) >> 1)] >> (16 * (sl & 1)),
+                  pg[256 + 16 * c.ng + 16 * gr + sl], 0u, 0u};
+      r.kind = 2;
+    }
+  };
+  auto deposit = [&](const RawSlice& r) {
+    float kv[8], vv[8];
+    if (r.kind == 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bf16x2_to_f32(r.k[e], kv[2 * e], kv[2 * e + 1]);
+        bf16x2_to_f32(r.v[e], vv[2 * e], vv[2 * e + 1]);
+      }
+    } else if (r.kind == 2) {
+      // scale * code + zero: the product is exact, so fmaf rounds once
+      const float ks = f16lo(r.k[1]), kz = f16hi(r.k[1]);
+      const float vs = f16lo(r.v[1]), vz = f16hi(r.v[1]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        kv[j] = __builtin_fmaf(ks, (float)((r.k[0] >> (2 * j)) & 3u), kz);
+        vv[j] = __builtin_fmaf(vs, (float)((r.v[0] >> (2 * j)) & 3u), vz);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kv[j] = vv[j] = 0.0f;
+    }
+    // keys as fp16 hi + lo (about 22 significant bits): a logit is sensitive
+    // to the key's rounding; bf16 rows are exact in hi alone
+    half8 kh, kl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      kh[j] = (_Float16)kv[j];
+      kl[j] = (_Float16)(kv[j] - (float)kh[j]);
+    }
+    *(half8*)&sk[st_t][8 * st_u] = kh;
+    *(half8*)&skl[st_t][8 * st_u] = kl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) svt[8 * st_u + j][st_t] = (_Float16)vv[j];
+  };
+
+  float4_t acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+  SoftmaxState st{kNegInf, 0.0f, 0.0f};
+  const float C2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
+
+  // Unmapped INT2 pages are read as zero rows with zero weight (as in decode):
+  // a per-block mask of such positions, built by the staging threads.
+  __shared__ int s_skip[kPage];
+  const int nblk = (kend + kPage - 1) / kPage;
+  RawSlice cur, nxt;
+  fetch(0, cur);
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int p0 = kb * kPage;
+    deposit(cur);
+    if (st_u == 0) s_skip[st_t] = (cur.kind == 0) ? 1 : 0;
+    if (kb + 1 < nblk) fetch(p0 + kPage, nxt);   // next block in flight during this one
+    __syncthreads();
+    if (p0 < wave_kend) {
+      float4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8*)&sk[r16][32 * cc + 8 * qd], bq[cc],
+                                                   d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8*)&skl[r16][32 * cc + 8 * qd], bq[cc],
+                                                   d, 0, 0, 0);
+      }
+      float x[4], p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kp = p0 + 4 * qd + r;
+        x[r] = (colv && kp <= qpos && !s_skip[4 * qd + r]) ? d[r] : kNegInf;
+      }
+      softmax_step<4>(x, C2, p, st, acc);
+      half4_t ph, pl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ph[r] = (_Float16)p[r];
+        pl[r] = (_Float16)(p[r] - (float)ph[r]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const half4_t av = *(const half4_t*)&svt[16 * j + r16][4 * qd];
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, ph, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pl, acc[j], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // the block is consumed before the next one is deposited
+    cur = nxt;
+  }
+
+  // ---- normalize, then o = o' . R_V^T (or o' when the value transform is absorbed)
+  const float l = rows_sum(st.l);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) fin[16 * wave + r16][16 * j + 4 * qd + r] = acc[j][r] * inv;
+  __syncthreads();
+  auto out_row = [&](int rr) {   // output row of work-group row rr, or nullptr
+    const int R = tile * kPfRows + rr;
+    if (R >= rows) return (float*)nullptr;
+    return a.out + ((size_t)(t0 + R / c.g) * c.hq + (size_t)h * c.g + R % c.g) * kD;
+  };
+  if (!c.unrot) {
+    for (int k = tid; k < kPfRows * (kD / 4); k += 256) {
+      const int rr = k / (kD / 4), c4 = k % (kD / 4);
+      float* o = out_row(rr);
+      if (o) *(float4_t*)(o + 4 * c4) = *(const float4_t*)&fin[rr][4 * c4];
+    }
+    return;
+  }
+  // lane (li, kq) holds R_V[32w + 16cb + li][32kq .. 32kq+31]: the contraction
+  // index of step (u, e) is k = 32kq + 4u + e, as in the decode merge
+  const int li = r16, kq = qd;
+  float4_t rb[2][8];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float4_t* rg =
+        (const float4_t*)(c.r_v + ((size_t)h * kD + 32 * wave + 16 * cb + li) * kD + 32 * kq);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rb[cb][u] = rg[u];
+  }
+#pragma unroll
+  for (int rb4 = 0; rb4 < kPfRows / 16; ++rb4) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float4_t o4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o4 = __builtin_amdgcn_mfma_f32_16x16x4f32(fin[16 * rb4 + li][32 * kq + 4 * u + e],
+                                                    rb[cb][u][e], o4, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float* o = out_row(16 * rb4 + 4 * kq + v);
+        if (o) o[32 * wave + 16 * cb + li] = o4[v];
+      }
+    }
+  }
+}
+
+hipError_t launch_prefill(const CacheArgs& c, const PrefillArgs& a, hipStream_t stream) {
+  if (a.n_seqs <= 0 || a.tiles <= 0) return hipSuccess;
+  const dim3 grid(a.tiles, a.n_seqs, c.hkv);
+  hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(256), 0, stream, c, a);
+  return hipGetLastError();
+}
+
+int prefill_tiles(int n_new, int g) { return (n_new * g + kPfRows - 1) / kPfRows; }
+
+}  // namespace oscar

@@ -81,6 +81,22 @@ hipError_t launch_append_one(const CacheArgs& c, const ClipArgs& clip, const Seq
                              const RotateJobs& jobs, int total_q, const uint16_t* stage_k,
                              const uint16_t* stage_v, hipStream_t stream);
 
+// Chunked-prefill attention: the new rows of each sequence (just appended)
+// attend causally to the cache before them and to each other.
+struct PrefillArgs {
+  const int32_t* slots;          // [n_seqs] cache rows
+  const int32_t* len_before;     // [n_seqs] tokens before the chunk
+  const int32_t* cu_new;         // [n_seqs + 1] chunk rows of sequence i: cu_new[i] .. cu_new[i+1]-1
+  const uint16_t* q_rot;         // bf16 [cu_new[n]][hq][128]
+  const uint16_t* k_rot;         // bf16 [cu_new[n]][hkv][128]
+  const uint16_t* v_rot;         // bf16 [cu_new[n]][hkv][128]
+  float* out;                    // fp32 [cu_new[n]][hq][128]
+  int n_seqs;
+  int tiles;                     // most query tiles of any sequence (grid x)
+};
+int prefill_tiles(int n_new, int g);
+hipError_t launch_prefill(const CacheArgs& c, const PrefillArgs& a, hipStream_t stream);
+
 // Decoded rows of one cache row.
 hipError_t launch_dequant(const CacheArgs& c, int slot, int len, int t0, int t1, float* k_out,
                           float* v_out, hipStream_t stream);
