@@ -161,6 +161,76 @@ def cpu_baseline(w, lens, seconds=12.0, n_sample=4):
                        f"decoded caches built beforehand, untimed")}
 
 
+PEAK_F16_MFMA_TFLOPS = 2500.0   # MI355X dense fp16 / bf16 matrix peak
+
+
+def prefill_flops(hq, lbs, ns):
+    """Algorithmic flops of chunked-prefill attention: each query head of the
+    chunk row at position P multiplies against P + 1 keys and values
+    (2 * 128 flops each for q.k and for p.v)."""
+    return sum(hq * 512 * (n * lb + n * (n + 1) // 2) for lb, n in zip(lbs, ns))
+
+
+def measure_prefill(w, lbs, ns, reps=10):
+    """oscar_int2_prefill_attn after one append of a chunk per sequence (the
+    prefixes are appended first through the library); median of `reps` timed
+    calls (HIP events on the stream the kernel runs on)."""
+    import torch
+    from ultra_bit_kv_amd import SeqBatch
+    lens = [lb + n for lb, n in zip(lbs, ns)]
+    cache = make_layer(w, lens, len(lens))
+    if max(lbs) > 0:
+        populate(cache, w, lbs)
+    idx = list(range(len(lbs)))
+    k = np.concatenate([w.keys(i, lbs[i], lens[i]) for i in idx])
+    v = np.concatenate([w.values(i, lbs[i], lens[i]) for i in idx])
+    q = np.concatenate([w.queries(i, lbs[i], lens[i]) for i in idx])
+    cache.workspace_for(len(idx), sum(ns))
+    q_rot, k_rot, v_rot = cache.append_tokens(idx, lbs, ns, k, v, q, want_rot=True)
+    b = SeqBatch(idx, lbs, ns)
+    out = cache.prefill_attn(b, q_rot, k_rot, v_rot)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, c in evs:
+        a.record()
+        cache.prefill_attn(b, q_rot, k_rot, v_rot, out)
+        c.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(c) for a, c in evs]))
+    fl = prefill_flops(w.hq, lbs, ns)
+    return {"ms": ms, "tflops": fl / (ms * 1e-3) / 1e12, "alg_tflop": fl / 1e12}
+
+
+def cpu_prefill_baseline(w, lb, n, seconds=6.0, rows=16):
+    """The oracle's chunked-prefill attention (O6) for a sample of chunk rows
+    of one sequence and KV head, on the host cores: algorithmic TFLOP/s."""
+    from threadpoolctl import threadpool_info
+    from oracle import rotate, prefill
+    from oracle.rounding import bf16_bits_to_f64
+    from tests.oscar_testlib import oracle_head
+    r_k, r_v = w.rotations()
+    hc = oracle_head(w, 0, 0, lb + n, r_k, r_v)
+    qr = bf16_bits_to_f64(rotate.rotate_heads_to_bf16(w.queries(0, lb, lb + n), r_k, g=w.g))
+    qr = qr[:, :w.g]
+    sample = list(range(n - rows, n))   # the longest rows
+    done = 0
+    fl = 0
+    t0 = time.perf_counter()
+    while True:
+        prefill.prefill_head(qr, hc, lb, r_v=r_v[0], rows=sample)
+        done += 1
+        fl += sum(w.g * 512 * (lb + j + 1) for j in sample)
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 oracle prefill attention of the last {rows} chunk rows (all {w.g} "
+                       f"query heads of KV head 0) of a {n}-token chunk after {lb} tokens, "
+                       f"repeated {done} times in {el:.1f} s; cache built beforehand, untimed")}
+
+
 def copy_calibration(nbytes):
     """A plain device copy of known size (for scaling FETCH_SIZE / WRITE_SIZE)."""
     import torch
@@ -331,6 +401,8 @@ def main():
     ap.add_argument("--no-bf16-compare", dest="bf16_compare", action="store_false",
                     help="skip the BF16 paged-decode comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-prefill", dest="prefill", action="store_false",
+                    help="skip the chunked-prefill attention legs")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -414,6 +486,30 @@ def main():
                 "bs1_decode_ms": bf1["decode_ms"], "bs1_GBs": bf1["GBs"],
                 "bs1_int2_speedup": bf1["decode_ms"] / res["bs1"]["decode_ms"],
             })
+    if args.prefill:
+        # chunked-prefill attention: the Qwen3-32B step's 16 fresh 2048-token
+        # chunks, and a 2048-token chunk after a 30720-token prefix (Qwen3-8B heads)
+        w5 = get("c5_qwen3_32b_step")
+        w5 = w5.scaled(n_seqs=w5.prefill_chunks,
+                       lengths=("list", tuple([w5.prefill_len] * w5.prefill_chunks)))
+        p5 = measure_prefill(w5, [0] * w5.prefill_chunks, [w5.prefill_len] * w5.prefill_chunks)
+        w2 = get("c2_qwen3_8b_bs1").scaled(lengths=("list", (32768,)))
+        p2 = measure_prefill(w2, [30720], [2048])
+        res["prefill"] = {
+            "kernel": "prefill_attn_kernel (oscar_int2_prefill_attn)",
+            "c5_chunks": {"workload": "16 fresh 2048-token chunks, 64 / 8 heads, G=128, windows "
+                                      "64/256/256", **p5,
+                          "roofline": {"bound": "mfma", "achieved": p5["tflops"],
+                                       "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": p5["tflops"] / PEAK_F16_MFMA_TFLOPS}},
+            "chunk_after_prefix": {"workload": "2048-token chunk after 30720 tokens, 32 / 8 "
+                                               "heads, G=128, windows 64/256/16", **p2,
+                                   "roofline": {"bound": "mfma", "achieved": p2["tflops"],
+                                                "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                                                "frac": p2["tflops"] / PEAK_F16_MFMA_TFLOPS}},
+        }
+        if not args.no_cpu_baseline:
+            res["prefill"]["cpu_baseline"] = cpu_prefill_baseline(w5, 0, w5.prefill_len)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, lens0, seconds=args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -33,6 +33,8 @@ namespace {
 
 constexpr int kPfRows = 64;    // query rows per work-group (4 waves x 16 columns)
 constexpr int kKRow = kD + 8;  // staged key row in fp16 (padded: rows start 4 banks apart)
+constexpr int kVRow = kPage + 4;  // staged value row (one channel) in fp16: a 40-byte stride
+                                  // spreads the 16 channel rows a wave writes over the banks
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
@@ -54,7 +56,7 @@ __device__ __forceinline__ void bf16x2_to_f32(uint32_t w, float& lo, float& hi) 
 __global__ __launch_bounds__(256) void prefill_attn_kernel(CacheArgs c, PrefillArgs a) {
   __shared__ __align__(16) _Float16 sk[kPage][kKRow];   // staged keys [token][channel], fp16 part
   __shared__ __align__(16) _Float16 skl[kPage][kKRow];  // remainders k - fp16(k), fp16
-  __shared__ __align__(16) _Float16 svt[kD][kPage];     // staged values [channel][token]
+  __shared__ __align__(16) _Float16 svt[kD][kVRow];     // staged values [channel][token]
   __shared__ __align__(16) float fin[kPfRows][kD + 4];  // normalized o' rows
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -175,6 +177,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(CacheArgs c, PrefillA
   // Unmapped INT2 pages are read as zero rows with zero weight (as in decode):
   // a per-block mask of such positions, built by the staging threads.
   __shared__ int s_skip[kPage];
+  const int int2_end = min(sq, lb);   // INT2 rows of the prefix: [S_sink, int2_end)
   const int nblk = (kend + kPage - 1) / kPage;
   RawSlice cur, nxt;
   fetch(0, cur);
@@ -187,11 +190,14 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(CacheArgs c, PrefillA
     if (p0 < wave_kend) {
       float4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
+      for (int cc = 0; cc < 4; ++cc)
         d = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8*)&sk[r16][32 * cc + 8 * qd], bq[cc],
                                                    d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8*)&skl[r16][32 * cc + 8 * qd], bq[cc],
-                                                   d, 0, 0, 0);
+      if (p0 + kPage > c.s_sink && p0 < int2_end) {   // INT2 rows; bf16 rows are exact in hi
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8*)&skl[r16][32 * cc + 8 * qd],
+                                                     bq[cc], d, 0, 0, 0);
       }
       float x[4], p[4];
 #pragma unroll
