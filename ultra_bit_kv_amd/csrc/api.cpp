@@ -413,6 +413,7 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
   // of a full launch), so a short last launch fits in it too.
   const int cap = max_splits(sh, std::min(n_seqs, kMaxScanSeqs));
   static thread_local ItemOrder order;
+  static thread_local SplitCounts counts;
   // Launches of at most kMaxScanSeqs sequences, in stream order.
   for (int s0 = 0; s0 < n_seqs; s0 += kMaxScanSeqs) {
     const int ns = std::min(kMaxScanSeqs, n_seqs - s0);
@@ -490,6 +491,9 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
       order.n = plan.grid;
     }
     plan.order = &order;
+    counts.n = ns;
+    for (int i = 0; i < ns; ++i) counts.ns[i] = (uint16_t)splits_of(cost[i], quota);
+    plan.counts = &counts;
     const SeqArgs sa{seq_slots + s0, seq_lens + s0, nullptr, ns};
     const size_t qo = (size_t)s0 * a.hq * kD;
     const uint16_t* qs = q ? q + qo : nullptr;

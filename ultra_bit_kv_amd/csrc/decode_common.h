@@ -206,19 +206,27 @@ __device__ __forceinline__ bool work_item(const SeqArgs& s, const ItemOrder& ord
 // the pass, 4 channels).  Every thread loads its head's maxima and sums
 // itself, so the kernel has no LDS and no barrier.  Output: one record per
 // chunk, in the same layout, with row stride smax2.
+// Split records of sequence i: the host's count when the launch carries the
+// table, else from the device length.
+__device__ __forceinline__ int split_records(const CacheArgs& c, const SeqArgs& s,
+                                             const SplitCounts& sc, int i, int quota, int smax) {
+  if (sc.n > 0) return sc.ns[i];
+  const int slot = s.slots[i], len = s.lens[i];
+  const bool ok = slot >= 0 && slot < c.max_seqs && len >= 1;
+  return decode_splits(decode_work(ok ? len : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap), quota,
+                       smax);
+}
+
 template <int HP>
 __global__ __launch_bounds__(HP * 32 < 64 ? 64 : HP * 32) void lse_chunks_kernel(
-    CacheArgs c, SeqArgs s, int quota, int passes, int smax, int smax2,
+    CacheArgs c, SeqArgs s, SplitCounts sc, int quota, int passes, int smax, int smax2,
     const float* __restrict__ partials, float* __restrict__ merged) {
   constexpr int W = rec_words(HP), OO = rec_o_offset(HP);
   const int x = blockIdx.x;
   const int pass = x % passes, h = (x / passes) % c.hkv, i = x / (passes * c.hkv);
   const int nh = min(HP, c.g - pass * HP);
   const int r = threadIdx.x >> 5, c4 = threadIdx.x & 31;
-  const int slot = s.slots[i], len = s.lens[i];
-  const bool ok = slot >= 0 && slot < c.max_seqs && len >= 1;
-  const int ns = decode_splits(decode_work(ok ? len : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap),
-                               quota, smax);
+  const int ns = split_records(c, s, sc, i, quota, smax);
   const int sp0 = blockIdx.y * kMergeChunk;
   if (r >= nh || sp0 >= ns) return;
   const int cnt = min(kMergeChunk, ns - sp0);
@@ -268,8 +276,8 @@ __global__ __launch_bounds__(HP * 32 < 64 ? 64 : HP * 32) void lse_chunks_kernel
 // R_V[16w + i][32q .. 32q+31] in registers (loaded at entry, before any
 // wait), so the contraction index of step (u, e) is k = 32q + 4u + e.
 template <int HP, bool UNROT>
-__global__ __launch_bounds__(512) void lse_merge_kernel(CacheArgs c, SeqArgs s, int quota,
-                                                        int passes, int smax, int chunk,
+__global__ __launch_bounds__(512) void lse_merge_kernel(CacheArgs c, SeqArgs s, SplitCounts sc,
+                                                        int quota, int passes, int smax, int chunk,
                                                         int stride, int sb,
                                                         const float* __restrict__ recs,
                                                         float* __restrict__ out) {
@@ -298,10 +306,13 @@ __global__ __launch_bounds__(512) void lse_merge_kernel(CacheArgs c, SeqArgs s, 
   bool ok = false;
   const float* rec = recs;
   if (valid) {
-    const int slot = s.slots[i], len = s.lens[i];
-    ok = slot >= 0 && slot < c.max_seqs && len >= 1;
-    const int ns = decode_splits(
-        decode_work(ok ? len : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap), quota, smax);
+    if (sc.n > 0) {
+      ok = true;   // the host checked every slot and length of the call
+    } else {
+      const int slot = s.slots[i], len = s.lens[i];
+      ok = slot >= 0 && slot < c.max_seqs && len >= 1;
+    }
+    const int ns = split_records(c, s, sc, i, quota, smax);
     nrec = (ns + chunk - 1) / chunk;
     rec = recs + (((size_t)i * c.hkv + h) * passes + pass) * stride * W;
   }
@@ -367,8 +378,10 @@ __global__ __launch_bounds__(512) void lse_merge_kernel(CacheArgs c, SeqArgs s, 
     const int rr = 4 * kq + v;   // output row of this lane's v-th value
     const int ii = s0 + rr / nh;
     if (rr >= sb * nh || ii >= s.n_seqs) continue;
-    const int slot = s.slots[ii];
-    if (slot < 0 || slot >= c.max_seqs || s.lens[ii] < 1) continue;
+    if (sc.n == 0) {
+      const int slot = s.slots[ii];
+      if (slot < 0 || slot >= c.max_seqs || s.lens[ii] < 1) continue;
+    }
     float* o = out + ((size_t)ii * c.hq + (size_t)h * c.g + pass * HP + rr % nh) * kD;
     o[16 * wave + li] = acc[v];
   }
@@ -390,7 +403,8 @@ hipError_t launch_merge(const CacheArgs& c, const SeqArgs& s, const DecodePlan& 
     float* merged = partials + (size_t)s.n_seqs * c.hkv * plan.passes * plan.smax * rec_words(HP);
     const dim3 g1(s.n_seqs * c.hkv * plan.passes, smax2);
     hipLaunchKernelGGL((lse_chunks_kernel<HP>), g1, dim3(HP * 32 < 64 ? 64 : HP * 32), 0, stream,
-                       c, s, plan.quota, plan.passes, plan.smax, smax2, partials, merged);
+                       c, s, *plan.counts, plan.quota, plan.passes, plan.smax, smax2, partials,
+                       merged);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     recs = merged;
@@ -398,7 +412,8 @@ hipError_t launch_merge(const CacheArgs& c, const SeqArgs& s, const DecodePlan& 
     stride = smax2;
   }
   const dim3 mgrid(c.hkv * plan.passes, (s.n_seqs + sb - 1) / sb);
-  hipLaunchKernelGGL((lse_merge_kernel<HP, UNROT>), mgrid, dim3(512), 0, stream, c, s, plan.quota,
+  hipLaunchKernelGGL((lse_merge_kernel<HP, UNROT>), mgrid, dim3(512), 0, stream, c, s,
+                     *plan.counts, plan.quota,
                      plan.passes, plan.smax, chunk, stride, sb, recs, out);
   return hipGetLastError();
 }

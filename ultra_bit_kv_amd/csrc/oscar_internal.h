@@ -166,6 +166,15 @@ struct ItemOrder {
   int32_t len[kMaxOrder];
 };
 
+// Split records of each sequence of a decode launch, as planned on the host,
+// for the merge launches: they then start loading records without reading
+// the sequence arrays first.  n = 0: the merge kernels derive the counts from
+// the device lengths.
+struct SplitCounts {
+  int n;
+  uint16_t ns[kMaxScanSeqs];
+};
+
 // INT2 split-K decode (partials to the workspace) and the merge / un-rotation launch.
 struct DecodePlan {
   int quota;                     // work per context split in 1/16 page pairs (a window block = kWinCost pairs)
@@ -177,6 +186,7 @@ struct DecodePlan {
   int grid;                      // work-groups of the split launch (= its work items)
   int cus;                       // compute units: work-group b runs in dispatch round b / cus
   const ItemOrder* order;        // work item of each work-group (host memory, passed by value)
+  const SplitCounts* counts;     // split records per sequence (host memory, passed by value)
 };
 // Work-groups of the split kernel that fit on one compute unit.
 int decode_wgs_per_cu(const CacheArgs& c, const DecodePlan& plan);
