@@ -11,10 +11,11 @@
 //   scale * code + zero), the chunk's own rows at their bf16 rotated values
 //   (the append's k_rot / v_rot outputs), then o = o' . R_V^T.
 //
-// Work-group = (sequence, tile of 64 query rows, KV head); query row r of a
-// (sequence, KV head) is (chunk row r / g, head r % g), and wave w owns rows
-// 16w .. 16w+15 as the 16 columns of its MFMA tiles.  The key stream is cut
-// into 16-position blocks; the work-group stages each block in LDS as fp16
+// Work-group = (sequence, tile of 128 query rows, KV head); query row r of a
+// (sequence, KV head) is (chunk row r / g, head r % g), and wave w (of 8) owns
+// rows 16w .. 16w+15 as the 16 columns of its MFMA tiles.  The key stream is
+// staged 32 positions per barrier, processed in 16-position blocks; the
+// work-group stages the keys in LDS as fp16
 // (K rows [token][channel] as fp16 hi + lo, V transposed [channel][token]),
 // decoding every
 // position from wherever it lives (sink, INT2 page, ring, chunk rows), one
@@ -23,18 +24,35 @@
 //                   wave's query rows (fp16 from bf16, exact in the normal range)
 //   online softmax per column (query row), causal mask p <= P
 //   O^T += V^T . P^T  v_mfma_f32_16x16x16f16 with P split into fp16 hi + lo
-// then the normalized o' rows go through LDS and the fp32 matrix cores apply
-// R_V^T (wave w computes output channels 32w .. 32w+31 of all 64 rows).
+// then the normalized o' rows go through LDS (reusing the staging space) and
+// the fp32 matrix cores apply R_V^T (wave w computes output channels
+// 16w .. 16w+15 of all 128 rows).
 #include "decode_common.h"
 
 namespace oscar {
 
 namespace {
 
-constexpr int kPfRows = 64;    // query rows per work-group (4 waves x 16 columns)
-constexpr int kKRow = kD + 8;  // staged key row in fp16 (padded: rows start 4 banks apart)
-constexpr int kVRow = kPage + 4;  // staged value row (one channel) in fp16: a 40-byte stride
-                                  // spreads the 16 channel rows a wave writes over the banks
+constexpr int kPfWaves = 8;                 // waves per work-group, 16 query rows each
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfRows = 16 * kPfWaves;       // query rows per work-group
+constexpr int kStagePos = 2;                 // key positions each staging thread takes
+constexpr int kStage = kPfThreads / 16 * kStagePos;   // key positions staged per barrier
+constexpr int kKRow = kD + 8;     // staged key row in fp16 (padded: rows start 4 banks apart)
+constexpr int kVRow = kStage + 4; // staged value row (one channel) in fp16: the 8-byte pad
+                                  // spreads the channel rows a wave writes over the banks
+
+// LDS: the staging buffers during the key loop, the normalized o' rows after it.
+struct PfStage {
+  _Float16 k[kStage][kKRow];    // keys [token][channel], fp16 part
+  _Float16 kl[kStage][kKRow];   // remainders k - fp16(k)
+  _Float16 vt[kD][kVRow];       // values [channel][token]
+  int skip[kStage];             // position unreadable (unmapped page or past the row)
+};
+struct PfFinal {
+  float o[kPfRows][kD + 4];
+};
+constexpr int kPfLds = sizeof(PfStage) > sizeof(PfFinal) ? sizeof(PfStage) : sizeof(PfFinal);
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
@@ -53,11 +71,10 @@ __device__ __forceinline__ void bf16x2_to_f32(uint32_t w, float& lo, float& hi) 
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void prefill_attn_kernel(CacheArgs c, PrefillArgs a) {
-  __shared__ __align__(16) _Float16 sk[kPage][kKRow];   // staged keys [token][channel], fp16 part
-  __shared__ __align__(16) _Float16 skl[kPage][kKRow];  // remainders k - fp16(k), fp16
-  __shared__ __align__(16) _Float16 svt[kD][kVRow];     // staged values [channel][token]
-  __shared__ __align__(16) float fin[kPfRows][kD + 4];  // normalized o' rows
+__global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(CacheArgs c, PrefillArgs a) {
+  __shared__ __align__(16) char smem[kPfLds];
+  PfStage& sg = *reinterpret_cast<PfStage*>(smem);
+  float(&fin)[kPfRows][kD + 4] = reinterpret_cast<PfFinal*>(smem)->o;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -99,10 +116,12 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(CacheArgs c, PrefillA
     }
   }
 
-  // ---- staging: thread (token t, channels 8u .. 8u+7) of a 16-position block
+  // ---- staging: thread (token t, channels 8u .. 8u+7) takes staged rows
+  // t + 32 m (m < kStagePos) of a stage
   const int st_t = tid >> 4, st_u = tid & 15;
-  auto fetch = [&](int p0, RawSlice& r) {
-    const int p = p0 + st_t;
+  constexpr int kRowStep = kPfThreads / 16;
+  auto fetch = [&](int p0, int m, RawSlice& r) {
+    const int p = p0 + st_t + kRowStep * m;
     r.kind = 0;
     r.k = r.v = u32x4{0u, 0u, 0u, 0u};
     if (p >= len) return;
@@ -133,7 +152,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(CacheArgs c, PrefillA
       r.kind = 2;
     }
   };
-  auto deposit = [&](const RawSlice& r) {
+  auto deposit = [&](const RawSlice& r, int m) {
+    const int row = st_t + kRowStep * m;
     float kv[8], vv[8];
     if (r.kind == 1) {
 #pragma unroll
@@ -162,10 +182,11 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(CacheArgs c, PrefillA
       kh[j] = (_Float16)kv[j];
       kl[j] = (_Float16)(kv[j] - (float)kh[j]);
     }
-    *(half8*)&sk[st_t][8 * st_u] = kh;
-    *(half8*)&skl[st_t][8 * st_u] = kl;
+    *(half8*)&sg.k[row][8 * st_u] = kh;
+    *(half8*)&sg.kl[row][8 * st_u] = kl;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) svt[8 * st_u + j][st_t] = (_Float16)vv[j];
+    for (int j = 0; j < 8; ++j) sg.vt[8 * st_u + j][row] = (_Float16)vv[j];
+    if (st_u == 0) sg.skip[row] = r.kind == 0 ? 1 : 0;
   };
 
   float4_t acc[8];
@@ -175,35 +196,41 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(CacheArgs c, PrefillA
   const float C2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
 
   // Unmapped INT2 pages are read as zero rows with zero weight (as in decode):
-  // a per-block mask of such positions, built by the staging threads.
-  __shared__ int s_skip[kPage];
+  // a per-stage mask of such positions, built by the staging threads.
   const int int2_end = min(sq, lb);   // INT2 rows of the prefix: [S_sink, int2_end)
-  const int nblk = (kend + kPage - 1) / kPage;
-  RawSlice cur, nxt;
-  fetch(0, cur);
-  for (int kb = 0; kb < nblk; ++kb) {
-    const int p0 = kb * kPage;
-    deposit(cur);
-    if (st_u == 0) s_skip[st_t] = (cur.kind == 0) ? 1 : 0;
-    if (kb + 1 < nblk) fetch(p0 + kPage, nxt);   // next block in flight during this one
+  const int nstage = (kend + kStage - 1) / kStage;
+  RawSlice cur[kStagePos], nxt[kStagePos];
+#pragma unroll
+  for (int m = 0; m < kStagePos; ++m) fetch(0, m, cur[m]);
+  for (int ks = 0; ks < nstage; ++ks) {
+    const int s0 = ks * kStage;
+#pragma unroll
+    for (int m = 0; m < kStagePos; ++m) deposit(cur[m], m);
+    if (ks + 1 < nstage) {   // next stage in flight during this one
+#pragma unroll
+      for (int m = 0; m < kStagePos; ++m) fetch(s0 + kStage, m, nxt[m]);
+    }
     __syncthreads();
-    if (p0 < wave_kend) {
+#pragma unroll
+    for (int sb = 0; sb < kStage / kPage; ++sb) {
+      const int p0 = s0 + kPage * sb, tb = kPage * sb;   // block start: position, staged row
+      if (p0 >= wave_kend) break;
       float4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc)
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8*)&sk[r16][32 * cc + 8 * qd], bq[cc],
-                                                   d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8*)&sg.k[tb + r16][32 * cc + 8 * qd],
+                                                   bq[cc], d, 0, 0, 0);
       if (p0 + kPage > c.s_sink && p0 < int2_end) {   // INT2 rows; bf16 rows are exact in hi
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8*)&skl[r16][32 * cc + 8 * qd],
-                                                     bq[cc], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              *(const half8*)&sg.kl[tb + r16][32 * cc + 8 * qd], bq[cc], d, 0, 0, 0);
       }
       float x[4], p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kp = p0 + 4 * qd + r;
-        x[r] = (colv && kp <= qpos && !s_skip[4 * qd + r]) ? d[r] : kNegInf;
+        x[r] = (colv && kp <= qpos && !sg.skip[tb + 4 * qd + r]) ? d[r] : kNegInf;
       }
       softmax_step<4>(x, C2, p, st, acc);
       half4_t ph, pl;
@@ -214,13 +241,14 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(CacheArgs c, PrefillA
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const half4_t av = *(const half4_t*)&svt[16 * j + r16][4 * qd];
+        const half4_t av = *(const half4_t*)&sg.vt[16 * j + r16][tb + 4 * qd];
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, ph, acc[j], 0, 0, 0);
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pl, acc[j], 0, 0, 0);
       }
     }
-    __syncthreads();   // the block is consumed before the next one is deposited
-    cur = nxt;
+    __syncthreads();   // the stage is consumed before the next one is deposited
+#pragma unroll
+    for (int m = 0; m < kStagePos; ++m) cur[m] = nxt[m];
   }
 
   // ---- normalize, then o = o' . R_V^T (or o' when the value transform is absorbed)
@@ -237,40 +265,36 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(CacheArgs c, PrefillA
     return a.out + ((size_t)(t0 + R / c.g) * c.hq + (size_t)h * c.g + R % c.g) * kD;
   };
   if (!c.unrot) {
-    for (int k = tid; k < kPfRows * (kD / 4); k += 256) {
+    for (int k = tid; k < kPfRows * (kD / 4); k += kPfThreads) {
       const int rr = k / (kD / 4), c4 = k % (kD / 4);
       float* o = out_row(rr);
       if (o) *(float4_t*)(o + 4 * c4) = *(const float4_t*)&fin[rr][4 * c4];
     }
     return;
   }
-  // lane (li, kq) holds R_V[32w + 16cb + li][32kq .. 32kq+31]: the contraction
-  // index of step (u, e) is k = 32kq + 4u + e, as in the decode merge
+  // lane (li, kq) holds R_V[16w + li][32kq .. 32kq+31]: the contraction index
+  // of step (u, e) is k = 32kq + 4u + e, as in the decode merge; wave w
+  // computes output channels 16w .. 16w+15 of every row
   const int li = r16, kq = qd;
-  float4_t rb[2][8];
+  float4_t rb[8];
+  {
+    const float4_t* rg = (const float4_t*)(c.r_v + ((size_t)h * kD + 16 * wave + li) * kD + 32 * kq);
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const float4_t* rg =
-        (const float4_t*)(c.r_v + ((size_t)h * kD + 32 * wave + 16 * cb + li) * kD + 32 * kq);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) rb[cb][u] = rg[u];
+    for (int u = 0; u < 8; ++u) rb[u] = rg[u];
   }
+  for (int rt = 0; rt < kPfRows / 16; ++rt) {
+    if (tile * kPfRows + 16 * rt >= rows) break;
+    float4_t o4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int rb4 = 0; rb4 < kPfRows / 16; ++rb4) {
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      float4_t o4 = {0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 4; ++e)
+        o4 = __builtin_amdgcn_mfma_f32_16x16x4f32(fin[16 * rt + li][32 * kq + 4 * u + e], rb[u][e],
+                                                  o4, 0, 0, 0);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          o4 = __builtin_amdgcn_mfma_f32_16x16x4f32(fin[16 * rb4 + li][32 * kq + 4 * u + e],
-                                                    rb[cb][u][e], o4, 0, 0, 0);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float* o = out_row(16 * rb4 + 4 * kq + v);
-        if (o) o[32 * wave + 16 * cb + li] = o4[v];
-      }
+    for (int v = 0; v < 4; ++v) {
+      float* o = out_row(16 * rt + 4 * kq + v);
+      if (o) o[16 * wave + li] = o4[v];
     }
   }
 }
@@ -278,7 +302,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(CacheArgs c, PrefillA
 hipError_t launch_prefill(const CacheArgs& c, const PrefillArgs& a, hipStream_t stream) {
   if (a.n_seqs <= 0 || a.tiles <= 0) return hipSuccess;
   const dim3 grid(a.tiles, a.n_seqs, c.hkv);
-  hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(256), 0, stream, c, a);
+  hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(kPfThreads), 0, stream, c, a);
   return hipGetLastError();
 }
 
