@@ -255,3 +255,23 @@ def test_query_transform_and_absorbed_output(out_rotated):
             worst = max(worst, err)
             assert ok, (out_rotated, i, h, err, rel)
     print(f"[case] query transform out_rotated={out_rotated} max_abs={worst:.3e}", flush=True)
+
+
+def test_large_grid_device_item_lookup():
+    """A launch with more work-groups than the host item table holds (one
+    KV head: one-wave work-groups, 200 sequences): the work-groups find their
+    items from the device lengths.  Sampled sequences against the oracle."""
+    from ultra_bit_kv_amd import SeqBatch
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.integers(560, 640, 200)]
+    w = get("c1_tiny").scaled(n_seqs=200, lengths=("list", tuple(lens)))
+    print(f"[case] large grid: {len(lens)} sequences, 1 KV head", flush=True)
+    cache = make_cache(w, lens)
+    q_rot = fill(cache, w, lens, chunk=700)
+    out = cache.decode(SeqBatch(range(len(lens)), lens), q_rot).cpu().numpy()
+    r_k, r_v = cache.host_r
+    for i in (0, 137):
+        want = oracle_decode(w, i, 0, lens[i], r_k, r_v)
+        err, rel, ok = compare_attention(out[i, :w.g], want)
+        assert ok, (i, err, rel)
+    print("[case] large grid ok", flush=True)
