@@ -22,8 +22,8 @@
 // block ahead in registers.  Per block and wave:
 //   S^T = K . Q^T   v_mfma_f32_16x16x32_f16, A = keys (hi, then lo), B = the
 //                   wave's query rows (fp16 from bf16, exact in the normal range)
-//   online softmax per column (query row), causal mask p <= P
-//   O^T += V^T . P^T  v_mfma_f32_16x16x16f16 with P split into fp16 hi + lo
+//   online softmax per column (query row) over 32 keys, causal mask p <= P
+//   O^T += V^T . P^T  v_mfma_f32_16x16x32_f16 with P split into fp16 hi + lo
 // then the normalized o' rows go through LDS (reusing the staging space) and
 // the fp32 matrix cores apply R_V^T (wave w computes output channels
 // 16w .. 16w+15 of all 128 rows).
@@ -212,38 +212,47 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(CacheArgs c, P
     }
     __syncthreads();
 #pragma unroll
-    for (int sb = 0; sb < kStage / kPage; ++sb) {
-      const int p0 = s0 + kPage * sb, tb = kPage * sb;   // block start: position, staged row
+    for (int sb = 0; sb < kStage / (2 * kPage); ++sb) {
+      // two 16-position blocks per softmax step: block b of the pair is
+      // staged rows tb + 16 b; K slot 8 qd + 4 b + r of the 32-key P.V MFMA
+      // is key 16 b + 4 qd + r, the lane's own softmax values
+      const int p0 = s0 + 2 * kPage * sb, tb = 2 * kPage * sb;
       if (p0 >= wave_kend) break;
-      float4_t d = {0.f, 0.f, 0.f, 0.f};
+      const bool int2 = p0 + 2 * kPage > c.s_sink && p0 < int2_end;   // bf16 rows are exact in hi
+      float x[8], p[8];
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8*)&sg.k[tb + r16][32 * cc + 8 * qd],
-                                                   bq[cc], d, 0, 0, 0);
-      if (p0 + kPage > c.s_sink && p0 < int2_end) {   // INT2 rows; bf16 rows are exact in hi
+      for (int b = 0; b < 2; ++b) {
+        float4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
           d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              *(const half8*)&sg.kl[tb + r16][32 * cc + 8 * qd], bq[cc], d, 0, 0, 0);
-      }
-      float x[4], p[4];
+              *(const half8*)&sg.k[tb + kPage * b + r16][32 * cc + 8 * qd], bq[cc], d, 0, 0, 0);
+        if (int2) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kp = p0 + 4 * qd + r;
-        x[r] = (colv && kp <= qpos && !sg.skip[tb + 4 * qd + r]) ? d[r] : kNegInf;
-      }
-      softmax_step<4>(x, C2, p, st, acc);
-      half4_t ph, pl;
+          for (int cc = 0; cc < 4; ++cc)
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                *(const half8*)&sg.kl[tb + kPage * b + r16][32 * cc + 8 * qd], bq[cc], d, 0, 0, 0);
+        }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 4; ++r) {
+          const int row = tb + kPage * b + 4 * qd + r;
+          x[4 * b + r] = (colv && s0 + row <= qpos && !sg.skip[row]) ? d[r] : kNegInf;
+        }
+      }
+      softmax_step<8>(x, C2, p, st, acc);
+      half8 ph, pl;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
         ph[r] = (_Float16)p[r];
         pl[r] = (_Float16)(p[r] - (float)ph[r]);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const half4_t av = *(const half4_t*)&sg.vt[16 * j + r16][tb + 4 * qd];
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, ph, acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pl, acc[j], 0, 0, 0);
+        const half4_t a0 = *(const half4_t*)&sg.vt[16 * j + r16][tb + 4 * qd];
+        const half4_t a1 = *(const half4_t*)&sg.vt[16 * j + r16][tb + kPage + 4 * qd];
+        const half8 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ph, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pl, acc[j], 0, 0, 0);
       }
     }
     __syncthreads();   // the stage is consumed before the next one is deposited
