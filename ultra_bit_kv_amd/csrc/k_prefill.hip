@@ -176,11 +176,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(CacheArgs c, P
     }
     // keys as fp16 hi + lo (about 22 significant bits): a logit is sensitive
     // to the key's rounding; bf16 rows are exact in hi alone
-    half8 kh, kl;
+    half8 kh, kl = {};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      kh[j] = (_Float16)kv[j];
-      kl[j] = (_Float16)(kv[j] - (float)kh[j]);
+    for (int j = 0; j < 8; ++j) kh[j] = (_Float16)kv[j];
+    if (r.kind == 2) {   // bf16 rows are exact in hi (up to fp16 subnormals)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kl[j] = (_Float16)(kv[j] - (float)kh[j]);
     }
     *(half8*)&sg.k[row][8 * st_u] = kh;
     *(half8*)&sg.kl[row][8 * st_u] = kl;
