@@ -685,7 +685,7 @@ int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
   const int64_t max_len = oscar_max_seq_len(&c);
   const int g = c.num_q_heads / c.num_kv_heads;
   std::vector<char> seen(c.max_seqs, 0);
-  int tiles = 0;
+  int64_t prefix = 0, chunk = 0;
   for (int i = 0; i < n_seqs; ++i) {
     const int slot = seq_slots_host[i];
     if (slot < 0 || slot >= c.max_seqs) return OSCAR_ERR_CAPACITY;
@@ -697,13 +697,22 @@ int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
     if (lb + n_new > max_len || int2_pages(lb + n_new, c) > c.max_pages_per_seq)
       return OSCAR_ERR_CAPACITY;
     if (n_new * g > ((int64_t)1 << 30)) return OSCAR_ERR_ARG;
-    tiles = std::max(tiles, prefill_tiles((int)n_new, g));
+    prefix += lb * n_new;
+    chunk += n_new * n_new / 2;
   }
+  // 16 waves per work-group when the chunks attend mostly to a cached prefix
+  // (a staged key block then serves twice the rows), else 8 (smaller tiles
+  // waste less of the causal triangle)
+  const int waves = prefix > chunk ? 16 : 8;
+  int tiles = 0;
+  for (int i = 0; i < n_seqs; ++i)
+    tiles = std::max(tiles, prefill_tiles(cu_new_host[i + 1] - cu_new_host[i], g, waves));
   const int64_t n_tok = cu_new_host[n_seqs];
   if (n_tok > (int64_t)1 << 30) return OSCAR_ERR_ARG;
   if ((st = check_device()) != OSCAR_OK) return st;
   if (n_tok == 0) return OSCAR_OK;
-  const PrefillArgs pa{seq_slots, len_before, cu_new, q_rot, k_rot, v_rot, out, n_seqs, tiles};
+  const PrefillArgs pa{seq_slots, len_before, cu_new, q_rot, k_rot, v_rot, out, n_seqs, tiles,
+                       waves};
   return hip_status(launch_prefill(make_args(*cache), pa, (hipStream_t)stream));
 }
 

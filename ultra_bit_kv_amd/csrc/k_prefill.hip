@@ -11,10 +11,12 @@
 //   scale * code + zero), the chunk's own rows at their bf16 rotated values
 //   (the append's k_rot / v_rot outputs), then o = o' . R_V^T.
 //
-// Work-group = (sequence, tile of 128 query rows, KV head); query row r of a
-// (sequence, KV head) is (chunk row r / g, head r % g), and wave w (of 8) owns
-// rows 16w .. 16w+15 as the 16 columns of its MFMA tiles.  The key stream is
-// staged 32 positions per barrier, processed in 16-position blocks; the
+// Work-group = (sequence, tile of 16 W query rows, KV head), W = 8 waves, or
+// 16 when the chunks attend mostly to a cached prefix (each staged key block
+// then serves more rows); query row r of a (sequence, KV head) is (chunk
+// row r / g, head r % g), and wave w owns rows 16w .. 16w+15 as the 16
+// columns of its MFMA tiles.  The key stream is
+// staged 64 positions per barrier, processed in 32-position steps; the
 // work-group stages the keys in LDS as fp16
 // (K rows [token][channel] as fp16 hi + lo, V transposed [channel][token]),
 // decoding every
@@ -26,33 +28,45 @@
 //   O^T += V^T . P^T  v_mfma_f32_16x16x32_f16 with P split into fp16 hi + lo
 // then the normalized o' rows go through LDS (reusing the staging space) and
 // the fp32 matrix cores apply R_V^T (wave w computes output channels
-// 16w .. 16w+15 of all 128 rows).
+// 16 (w % 8) .. 16 (w % 8) + 15 of its share of the rows).
 #include "decode_common.h"
 
 namespace oscar {
 
 namespace {
 
-constexpr int kPfWaves = 8;                 // waves per work-group, 16 query rows each
-constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kPfRows = 16 * kPfWaves;       // query rows per work-group
-constexpr int kStagePos = 2;                 // key positions each staging thread takes
-constexpr int kStage = kPfThreads / 16 * kStagePos;   // key positions staged per barrier
-constexpr int kKRow = kD + 8;     // staged key row in fp16 (padded: rows start 4 banks apart)
-constexpr int kVRow = kStage + 4; // staged value row (one channel) in fp16: the 8-byte pad
-                                  // spreads the channel rows a wave writes over the banks
+// Work-group shape: W waves of 16 query rows each; the staging threads take
+// 16 / (W / 4) ... positions each so that a stage always holds 64 positions.
+template <int W>
+struct PfShape {
+  static constexpr int kWaves = W;
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kRows = 16 * W;             // query rows per work-group
+  static constexpr int kStage = 64;                // key positions staged per barrier
+  static constexpr int kStagePos = kStage / (kThreads / 16);   // positions per staging thread
+  static constexpr int kKRow = kD + 8;   // staged key row in fp16 (padded: rows start 4 banks apart)
+  static constexpr int kVRow = kStage + 4;   // staged value row (one channel): the 8-byte pad
+                                             // spreads the rows a wave writes over the banks
+  static_assert(kStagePos * (kThreads / 16) == kStage, "a stage is 64 positions");
+};
 
 // LDS: the staging buffers during the key loop, the normalized o' rows after it.
+template <int W>
 struct PfStage {
-  _Float16 k[kStage][kKRow];    // keys [token][channel], fp16 part
-  _Float16 kl[kStage][kKRow];   // remainders k - fp16(k)
-  _Float16 vt[kD][kVRow];       // values [channel][token]
-  int skip[kStage];             // position unreadable (unmapped page or past the row)
+  using S = PfShape<W>;
+  _Float16 k[S::kStage][S::kKRow];    // keys [token][channel], fp16 part
+  _Float16 kl[S::kStage][S::kKRow];   // remainders k - fp16(k)
+  _Float16 vt[kD][S::kVRow];          // values [channel][token]
+  int skip[S::kStage];                // position unreadable (unmapped page or past the row)
 };
+template <int W>
 struct PfFinal {
-  float o[kPfRows][kD + 4];
+  float o[PfShape<W>::kRows][kD + 4];
 };
-constexpr int kPfLds = sizeof(PfStage) > sizeof(PfFinal) ? sizeof(PfStage) : sizeof(PfFinal);
+template <int W>
+constexpr int pf_lds() {
+  return sizeof(PfStage<W>) > sizeof(PfFinal<W>) ? sizeof(PfStage<W>) : sizeof(PfFinal<W>);
+}
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
@@ -71,10 +85,14 @@ __device__ __forceinline__ void bf16x2_to_f32(uint32_t w, float& lo, float& hi) 
 
 }  // namespace
 
-__global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(CacheArgs c, PrefillArgs a) {
-  __shared__ __align__(16) char smem[kPfLds];
-  PfStage& sg = *reinterpret_cast<PfStage*>(smem);
-  float(&fin)[kPfRows][kD + 4] = reinterpret_cast<PfFinal*>(smem)->o;
+template <int W>
+__global__ __launch_bounds__(64 * W) void prefill_attn_kernel(CacheArgs c, PrefillArgs a) {
+  using S = PfShape<W>;
+  constexpr int kPfWaves = S::kWaves, kPfThreads = S::kThreads, kPfRows = S::kRows;
+  constexpr int kStage = S::kStage, kStagePos = S::kStagePos;
+  __shared__ __align__(16) char smem[pf_lds<W>()];
+  PfStage<W>& sg = *reinterpret_cast<PfStage<W>*>(smem);
+  float(&fin)[kPfRows][kD + 4] = reinterpret_cast<PfFinal<W>*>(smem)->o;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -282,17 +300,21 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(CacheArgs c, P
     }
     return;
   }
-  // lane (li, kq) holds R_V[16w + li][32kq .. 32kq+31]: the contraction index
-  // of step (u, e) is k = 32kq + 4u + e, as in the decode merge; wave w
-  // computes output channels 16w .. 16w+15 of every row
+  // Wave w computes output channels 16 (w % 8) .. 16 (w % 8) + 15 of the row
+  // tiles rt = w / 8, w / 8 + kPfWaves / 8, ...; lane (li, kq) holds
+  // R_V[16 (w % 8) + li][32kq .. 32kq+31]: the contraction index of step
+  // (u, e) is k = 32kq + 4u + e, as in the decode merge
+  constexpr int kColBlocks = kD / 16;
+  static_assert(kPfWaves % kColBlocks == 0, "the epilogue splits the 128 output channels over the waves");
+  const int cb = wave % kColBlocks;
   const int li = r16, kq = qd;
   float4_t rb[8];
   {
-    const float4_t* rg = (const float4_t*)(c.r_v + ((size_t)h * kD + 16 * wave + li) * kD + 32 * kq);
+    const float4_t* rg = (const float4_t*)(c.r_v + ((size_t)h * kD + 16 * cb + li) * kD + 32 * kq);
 #pragma unroll
     for (int u = 0; u < 8; ++u) rb[u] = rg[u];
   }
-  for (int rt = 0; rt < kPfRows / 16; ++rt) {
+  for (int rt = wave / kColBlocks; rt < kPfRows / 16; rt += kPfWaves / kColBlocks) {
     if (tile * kPfRows + 16 * rt >= rows) break;
     float4_t o4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -304,7 +326,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(CacheArgs c, P
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       float* o = out_row(16 * rt + 4 * kq + v);
-      if (o) o[16 * wave + li] = o4[v];
+      if (o) o[16 * cb + li] = o4[v];
     }
   }
 }
@@ -312,10 +334,16 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(CacheArgs c, P
 hipError_t launch_prefill(const CacheArgs& c, const PrefillArgs& a, hipStream_t stream) {
   if (a.n_seqs <= 0 || a.tiles <= 0) return hipSuccess;
   const dim3 grid(a.tiles, a.n_seqs, c.hkv);
-  hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(kPfThreads), 0, stream, c, a);
+  if (a.waves == 16)
+    hipLaunchKernelGGL(prefill_attn_kernel<16>, grid, dim3(64 * 16), 0, stream, c, a);
+  else
+    hipLaunchKernelGGL(prefill_attn_kernel<8>, grid, dim3(64 * 8), 0, stream, c, a);
   return hipGetLastError();
 }
 
-int prefill_tiles(int n_new, int g) { return (n_new * g + kPfRows - 1) / kPfRows; }
+int prefill_tiles(int n_new, int g, int waves) {
+  const int rows = 16 * waves;
+  return (n_new * g + rows - 1) / rows;
+}
 
 }  // namespace oscar

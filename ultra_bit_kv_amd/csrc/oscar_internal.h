@@ -93,8 +93,9 @@ struct PrefillArgs {
   float* out;                    // fp32 [cu_new[n]][hq][128]
   int n_seqs;
   int tiles;                     // most query tiles of any sequence (grid x)
+  int waves;                     // 8 or 16 waves (16 query rows each) per work-group
 };
-int prefill_tiles(int n_new, int g);
+int prefill_tiles(int n_new, int g, int waves);
 hipError_t launch_prefill(const CacheArgs& c, const PrefillArgs& a, hipStream_t stream);
 
 // Decoded rows of one cache row.
