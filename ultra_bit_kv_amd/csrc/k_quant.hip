@@ -306,6 +306,17 @@ __global__ __launch_bounds__(128) void append_one_kernel(CacheArgs c, ClipArgs c
   const int h = y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = 32 * z + 16 * wave + (lane & 15);
+  // the cache rows and positions of this lane's four output tokens, loaded
+  // ahead of the rotation (they only decide where the results go)
+  int tslot[4], tpos[4];
+  if (job != 2) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = 16 * tb + (lane >> 4) + 4 * v;
+      tslot[v] = tok < n_tok ? s.slots[tok] : -1;
+      tpos[v] = tok < n_tok ? s.lens[tok] : -1;
+    }
+  }
   float rb[kD / 4];
   load_r_slice(jd.r + (size_t)(h / jd.g) * kD * kD, j, rb);
   auto out = [&](int tok, int col, uint16_t bits) {
@@ -315,8 +326,9 @@ __global__ __launch_bounds__(128) void append_one_kernel(CacheArgs c, ClipArgs c
       return;
     }
     if (jd.dst_b) jd.dst_b[o] = bits;
-    const int slot = s.slots[tok];
-    const int p = s.lens[tok];   // the new token's position
+    const int v = (tok - 16 * tb) >> 2;   // tok = 16 tb + lane / 16 + 4 v
+    const int slot = tslot[v];
+    const int p = tpos[v];   // the new token's position
     if (slot < 0 || slot >= c.max_seqs || p < 0) return;
     int blk, tt;
     if (p < c.s_sink) {
