@@ -18,7 +18,8 @@ Everything here is written from the three source pages:
 Arithmetic is fp64 unless a step names a rounding.  Modules:
 
 * ``rounding``  -- fp64 -> bf16 / fp16 single round-to-nearest-even.
-* ``rotate``    -- O1: x' = x . R, rounded once to bf16 (with an exactness guard).
+* ``rotate``    -- O1: x' = x . R, rounded once to bf16 (with an exactness guard),
+  for a dense R or the structured R = H (P_br) / sqrt(d).
 * ``placement`` -- O2: S_quant closed form, segments, ring slots, pages.
 * ``quant``     -- O3/O4: kappa-quantile clip, scale/zero, codes, dequant.
 * ``layout``    -- the documented on-HBM packing of pages and window blocks.

@@ -20,6 +20,8 @@ token is part of the context.  No mask, soft-cap or bias.
 
 import numpy as np
 
+from . import rotate
+
 D = 128
 
 
@@ -63,7 +65,7 @@ def attend_split(q, k, v, cuts):
 
 def unrotate(o_rot, r_v):
     """o = o' . R_V^T (row vectors)."""
-    return np.asarray(o_rot, dtype=np.float64) @ np.asarray(r_v, dtype=np.float64).T
+    return np.asarray(o_rot, dtype=np.float64) @ rotate.as_matrix(r_v).T
 
 
 def decode_head(q_rot, k_dec, v_dec, r_v):

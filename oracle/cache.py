@@ -22,7 +22,8 @@ PAGE = 16
 class HeadCache:
     """Cache of one sequence, one KV head, after ``length`` tokens.
 
-    k_bits, v_bits: post-RoPE bf16 bits [length, D]; r_k, r_v: fp32 [D, D];
+    k_bits, v_bits: post-RoPE bf16 bits [length, D]; r_k, r_v: fp32 [D, D] or
+    ``rotate.Hadamard``;
     kappa_k, kappa_v: fp32 clip ratios of this head.
     """
 
@@ -31,8 +32,8 @@ class HeadCache:
         self.length = n = k_bits.shape[0]
         self.group = group
         self.s_sink, self.s_keep, self.s_flush = s_sink, s_keep, s_flush
-        self.k_rot = rotate.rotate_to_bf16(k_bits, r_k)
-        self.v_rot = rotate.rotate_to_bf16(v_bits, r_v)
+        self.k_rot = rotate.rotate_rows_to_bf16(k_bits, r_k)
+        self.v_rot = rotate.rotate_rows_to_bf16(v_bits, r_v)
         self.sink, self.int2, self.recent = placement.segments(n, s_sink, s_keep, s_flush)
         a, b = self.int2
         self.kc, self.ks, self.kz = quant.quantize_rows(bf16_bits_to_f64(self.k_rot[a:b]), kappa_k, group)

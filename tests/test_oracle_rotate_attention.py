@@ -188,3 +188,98 @@ def test_absorbed_value_transform_output_basis():
     o_rot = attention.attend(q, k, rotate.rotate_f64(v, rv))
     assert np.abs(o_rot - rotate.rotate_f64(attention.attend(q, k, v), rv)).max() < 1e-12
     assert np.abs(attention.unrotate(o_rot, rv) - attention.attend(q, k, v)).max() < 1e-12
+
+
+# ---- structured rotation R = H (P_br) / sqrt(d) (OScaR notes, "Canalized
+# Rotation"; OSCAR summary page, section 5 "Rotation Analysis")
+
+def _bits(vals):
+    return f64_to_bf16_bits(np.asarray(vals, np.float64))
+
+
+def test_hadamard_signs_match_library_sylvester():
+    from scipy.linalg import hadamard
+    for d in (2, 4, 32, 128):
+        assert np.array_equal(rotate.hadamard_signs(d), hadamard(d))
+    assert np.array_equal(rotate.hadamard_signs(2), np.array([[1, 1], [1, -1]]))
+
+
+def test_hadamard_bit_reversal_permutation():
+    from scipy.linalg import hadamard
+    br = [rotate.bit_reverse(k, 7) for k in range(128)]
+    assert (br[0], br[1], br[3], br[64], br[127]) == (0, 64, 96, 1, 127)
+    assert sorted(br) == list(range(128)) and all(br[br[k]] == k for k in range(128))
+    s, h = rotate.hadamard_signs(128, True), hadamard(128)
+    assert np.array_equal(s, h[:, br])            # H P_br: columns of H in bit-reversed order
+    assert np.array_equal(s, h[br, :])            # which equals P_br H
+    assert np.all(s[1, :64] == 1) and np.all(s[1, 64:] == -1)
+    assert np.array_equal(rotate.hadamard_signs(128)[1], np.tile([1, -1], 64))
+
+
+@pytest.mark.parametrize("bitrev", [False, True])
+def test_hadamard_rotation_orthogonal_and_preserves_scores(bitrev):
+    r = rotate.Hadamard(128, bitrev).matrix()
+    assert np.abs(r @ r.T - np.eye(128)).max() < 1e-14
+    assert np.all(np.abs(np.abs(r) - 1 / math.sqrt(128)) < 1e-17)
+    rng = np.random.default_rng(3)
+    q, k = rng.standard_normal((4, 128)), rng.standard_normal((6, 128))
+    assert np.abs((q @ r) @ (k @ r).T - q @ k.T).max() < 1e-12
+
+
+@pytest.mark.parametrize("bitrev", [False, True])
+def test_hadamard_all_ones_row(bitrev):
+    # x . H = (128, 0, ..., 0), and bit reversal keeps index 0: x' = (sqrt(128), 0, ...),
+    # sqrt(128) = 11.3137... rounds to bf16 11.3125
+    out = rotate.hadamard_rotate_to_bf16(_bits(np.ones((1, 128))), bitrev)
+    assert bf16_bits_to_f64(out)[0, 0] == 11.3125 and out[0, 0] == 0x4135
+    assert np.all(bf16_bits_to_f64(out)[0, 1:] == 0)
+
+
+def test_hadamard_one_hot_spreads_energy_evenly():
+    # a one-hot row becomes a row of H / sqrt(d): every channel +-|k| / sqrt(d)
+    from scipy.linalg import hadamard
+    h = hadamard(128)
+    for i in (0, 1, 5, 127):
+        x = np.zeros((1, 128))
+        x[0, i] = 1.0
+        out = bf16_bits_to_f64(rotate.hadamard_rotate_to_bf16(_bits(x)))[0]
+        assert np.array_equal(out, 0.08837890625 * h[i])      # bf16(1 / sqrt(128))
+
+
+def test_round_scaled_ties_and_values():
+    from fractions import Fraction
+    # d = 64: s / 8 is rational, so exact ties occur and go to the even significand
+    assert rotate.round_scaled_to_bf16(Fraction(8) * (1 + Fraction(1, 256)), 64) == 0x3F80
+    assert rotate.round_scaled_to_bf16(Fraction(8) * (1 + Fraction(3, 256)), 64) == 0x3F82
+    assert rotate.round_scaled_to_bf16(-Fraction(8) * (1 + Fraction(1, 256)), 64) == 0xBF80
+    assert rotate.round_scaled_to_bf16(Fraction(8) * (1 + Fraction(5, 512)), 64) == 0x3F81
+    assert rotate.round_scaled_to_bf16(Fraction(1), 128) == 0x3DB5          # 1 / sqrt(128)
+    assert rotate.round_scaled_to_bf16(Fraction(0), 128) == 0
+
+
+@pytest.mark.parametrize("bitrev", [False, True])
+def test_hadamard_rotate_matches_dense_and_exact(bitrev):
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((48, 128)) * np.exp(rng.uniform(-3, 3, (48, 1)))
+    x[::7, 3] *= 300.0                               # channel outliers
+    xb = _bits(x)
+    got = rotate.hadamard_rotate_to_bf16(xb, bitrev)
+    dense = f64_to_bf16_bits(bf16_bits_to_f64(xb) @ rotate.Hadamard(128, bitrev).matrix())
+    assert np.array_equal(got, dense)
+    sg = rotate.hadamard_signs(128, bitrev)
+    xf = bf16_bits_to_f64(xb)
+    for i, j in [(0, 0), (5, 17), (7, 64), (47, 127), (21, 3)]:
+        s = sum((Fraction(a) * int(b) for a, b in zip(xf[i].tolist(), sg[:, j].tolist())), Fraction(0))
+        assert got[i, j] == rotate.round_scaled_to_bf16(s, 128)
+
+
+def test_hadamard_head_cache_and_unrotation():
+    rng = np.random.default_rng(5)
+    k = _bits(rng.standard_normal((40, 128)))
+    v = _bits(rng.standard_normal((40, 128)))
+    had = rotate.Hadamard(128, True)
+    hc = cache.HeadCache(k, v, had, had, 1.0, 1.0, 64, 4, 8, 8)
+    assert np.array_equal(hc.k_rot, rotate.hadamard_rotate_to_bf16(k, True))
+    o = rng.standard_normal((3, 128))
+    assert np.abs(attention.unrotate(o @ had.matrix(), had) - o).max() < 1e-12
