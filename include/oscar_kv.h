@@ -144,7 +144,31 @@ typedef struct {
    * inverse value transform), so decode returns o' in the rotated basis and
    * does not read r_v. */
   int32_t out_rotated;
+  /* Rotation kind.  OSCAR_ROT_DENSE: the matrices above.  The structured
+   * kinds rotate keys, values and queries of every head by one fixed
+   * orthogonal matrix built from Sylvester's Hadamard matrix H (entries
+   * H[i][k] = (-1)^popcount(i & k)), with no matrix in memory (r_k, r_v and
+   * r_q must be NULL, OSCAR_ERR_ARG otherwise):
+   *   OSCAR_ROT_HADAMARD         R = H / sqrt(128)  (OScaR notes, step one
+   *                              "Canalized Rotation"; the QuaRot-style baseline)
+   *   OSCAR_ROT_HADAMARD_BITREV  R = H P_br / sqrt(128), P_br the 7-bit
+   *                              bit-reversal permutation of the channels
+   *                              (OSCAR summary page, section 5 "Rotation
+   *                              Analysis": the Hadamard and bit-reversal
+   *                              factors of R = U H P_br)
+   * The rotated row is the bf16 rounding of x . R: the transform runs as a
+   * fast Walsh-Hadamard transform (7 butterfly stages, exact fp64 sums for
+   * rows whose magnitudes span less than 2^38) scaled once by fp64
+   * 1/sqrt(128).  The decode merge and the prefill epilogue un-rotate with
+   * R^T = R^-1 generated in registers. */
+  int32_t rotation;
 } oscar_kv_cache;
+
+enum oscar_rotation {
+  OSCAR_ROT_DENSE = 0,
+  OSCAR_ROT_HADAMARD = 1,
+  OSCAR_ROT_HADAMARD_BITREV = 2
+};
 
 /* Checks a configuration; returns OSCAR_OK or the first failing OSCAR_ERR_*. */
 int oscar_check_config(const oscar_kv_config* cfg);

@@ -16,10 +16,15 @@ def page_needs(w, lens):
     return [max(1, placement.n_int2_pages(int(L), w.s_sink, w.s_keep, w.s_flush)) for L in lens]
 
 
-def make_cache(w, lens, identity=False, spare_pages=0, max_seqs=None, out_rotated=False):
-    """An empty OscarKVCache sized for sequences growing to ``lens``."""
+def make_cache(w, lens, identity=False, spare_pages=0, max_seqs=None, out_rotated=False,
+               rotation=0):
+    """An empty OscarKVCache sized for sequences growing to ``lens``
+    (``rotation`` 1 / 2: the structured R = H / sqrt(128) / H P_br / sqrt(128))."""
     from ultra_bit_kv_amd import OscarKVCache
-    if identity:
+    if rotation:
+        had = [rotate.Hadamard(D, bitrev=rotation == 2)] * w.hkv
+        r_k = r_v = None
+    elif identity:
         eye = np.broadcast_to(np.eye(D, dtype=np.float32), (w.hkv, D, D)).copy()
         r_k = r_v = eye
     else:
@@ -31,9 +36,9 @@ def make_cache(w, lens, identity=False, spare_pages=0, max_seqs=None, out_rotate
                          s_sink=w.s_sink, s_keep=w.s_keep, s_flush=w.s_flush,
                          max_seqs=max_seqs or len(lens), max_pages_per_seq=bt.shape[1],
                          num_pages=total, clip_k=kk, clip_v=kv, r_k=r_k, r_v=r_v,
-                         block_table=bt, out_rotated=out_rotated)
+                         block_table=bt, out_rotated=out_rotated, rotation=rotation)
     cache.host_block_table = bt
-    cache.host_r = (r_k, r_v)
+    cache.host_r = (had, had) if rotation else (r_k, r_v)
     return cache
 
 

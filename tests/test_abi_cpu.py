@@ -105,8 +105,8 @@ def test_sizes(L):
 DUMMY = ctypes.c_void_p(0x1000)
 
 
-def _cache(c, r_q=None, out_rotated=0, r_v=0x1000):
-    return KvCache(c, 0x1000, 0x1000, 0x1000, 0x1000, r_v, r_q, out_rotated)
+def _cache(c, r_q=None, out_rotated=0, r_v=0x1000, r_k=0x1000, rotation=0):
+    return KvCache(c, 0x1000, 0x1000, 0x1000, r_k, r_v, r_q, out_rotated, rotation)
 
 
 def _i32(a):
@@ -293,3 +293,26 @@ def test_prefill_argument_checks(L):
     # the device check (a HIP error without a GPU)
     assert prefill(L, c, [0], [0], [5], cache=_cache(c, r_v=0, out_rotated=1)) in (-9, -8, 0)
     assert prefill(L, c, [0, 2], [100, 0], [7, 300]) in (-9, -8, 0)
+
+
+def test_structured_rotation_argument_checks(L):
+    c = cfg()
+    bare = dict(r_k=None, r_v=None)
+    for kind in (1, 2):
+        ok = _cache(c, rotation=kind, **bare)
+        # the structured kinds take no matrices; a valid call reaches the device check
+        assert append(L, c, [0], [0], [5], cache=ok) in (-9, -8, 0)
+        assert prefill(L, c, [0], [0], [5], cache=ok) in (-9, -8, 0)
+        keep = [_i32([0]), _i32([10])]
+        assert L.oscar_int2_decode_attn(ctypes.byref(ok), 1, keep[0][1], keep[1][1], DUMMY, DUMMY,
+                                        DUMMY, DUMMY, DUMMY, 1 << 40, None) in (-9, -8, 0)
+        # a matrix alongside a structured kind is rejected
+        for extra in (dict(r_k=0x1000, r_v=None), dict(r_k=None, r_v=0x1000),
+                      dict(r_k=None, r_v=None, r_q=0x1000)):
+            bad = _cache(c, rotation=kind, **extra)
+            assert append(L, c, [0], [0], [5], cache=bad) == -10
+            assert prefill(L, c, [0], [0], [5], cache=bad) == -10
+    for kind in (-1, 3):
+        assert append(L, c, [0], [0], [5], cache=_cache(c, rotation=kind, **bare)) in (-1, -10)
+        assert append(L, c, [0], [0], [5], cache=_cache(c, rotation=kind)) == -10
+        assert prefill(L, c, [0], [0], [5], cache=_cache(c, rotation=kind)) == -10

@@ -37,12 +37,14 @@ def _gpu():
     lib()
 
 
-def run_case(w, lbs, ns, out_rotated=False, identity=False, sample=None):
+def run_case(w, lbs, ns, out_rotated=False, identity=False, sample=None, rotation=0):
     from ultra_bit_kv_amd import SeqBatch
     print(f"[case] {w.name} G={w.group} Hq/Hkv={w.hq}/{w.hkv} windows=({w.s_sink},{w.s_keep},"
-          f"{w.s_flush}) len_before={lbs} n_new={ns} out_rotated={out_rotated}", flush=True)
+          f"{w.s_flush}) len_before={lbs} n_new={ns} out_rotated={out_rotated} "
+          f"rotation={rotation}", flush=True)
     lens = [lb + n for lb, n in zip(lbs, ns)]
-    cache = make_cache(w, [max(1, L) for L in lens], identity=identity, out_rotated=out_rotated)
+    cache = make_cache(w, [max(1, L) for L in lens], identity=identity, out_rotated=out_rotated,
+                       rotation=rotation)
     fill(cache, w, [lb + 1 for lb in lbs], chunk=512, last_step=False)    # positions [0, lb)
     idx = list(range(len(lbs)))
     k = np.concatenate([w.keys(i, lbs[i], lens[i]) for i in idx])

@@ -32,7 +32,12 @@ class KvConfig(ctypes.Structure):
 
 class KvCache(ctypes.Structure):
     _fields_ = [("cfg", KvConfig), ("pages", c_p), ("block_table", c_p), ("win", c_p),
-                ("r_k", c_p), ("r_v", c_p), ("r_q", c_p), ("out_rotated", c_i32)]
+                ("r_k", c_p), ("r_v", c_p), ("r_q", c_p), ("out_rotated", c_i32),
+                ("rotation", c_i32)]
+
+
+# rotation kinds of KvCache.rotation (oscar_rotation in oscar_kv.h)
+ROT_DENSE, ROT_HADAMARD, ROT_HADAMARD_BITREV = 0, 1, 2
 
 
 class Bf16Cache(ctypes.Structure):

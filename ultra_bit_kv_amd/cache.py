@@ -68,7 +68,10 @@ class OscarKVCache:
 
     def __init__(self, *, num_q_heads, num_kv_heads, group_size, s_sink, s_keep, s_flush,
                  max_seqs, max_pages_per_seq, num_pages, clip_k, clip_v, r_k, r_v, block_table,
-                 r_q=None, out_rotated=False, device="cuda"):
+                 r_q=None, out_rotated=False, rotation=0, device="cuda"):
+        """rotation: 0 uses the dense per-head r_k / r_v (/ r_q); 1 and 2 are the
+        structured R = H / sqrt(128) and H P_br / sqrt(128), which take
+        r_k = r_v = r_q = None."""
         cfg = KvConfig()
         cfg.head_dim = D
         cfg.num_q_heads = num_q_heads
@@ -97,17 +100,24 @@ class OscarKVCache:
         src = np.asarray(block_table, np.int32)
         bt[:src.shape[0], :src.shape[1]] = src
         self.block_table = torch.from_numpy(bt).to(device)
-        self.r_k = torch.as_tensor(np.asarray(r_k, np.float32)).to(device).contiguous()
-        self.r_v = torch.as_tensor(np.asarray(r_v, np.float32)).to(device).contiguous()
-        assert self.r_k.shape == (num_kv_heads, D, D) and self.r_v.shape == (num_kv_heads, D, D)
+        def dev(r):
+            return (torch.as_tensor(np.asarray(r, np.float32)).to(device).contiguous()
+                    if r is not None else None)
+
+        self.rotation = int(rotation)
+        self.r_k, self.r_v = dev(r_k), dev(r_v)
         # optional query transform (a non-orthogonal key transform T pairs with T^-T)
-        self.r_q = (torch.as_tensor(np.asarray(r_q, np.float32)).to(device).contiguous()
-                    if r_q is not None else None)
-        assert self.r_q is None or self.r_q.shape == (num_kv_heads, D, D)
+        self.r_q = dev(r_q)
+        if self.rotation == 0:
+            assert self.r_k.shape == (num_kv_heads, D, D) and self.r_v.shape == (num_kv_heads, D, D)
+            assert self.r_q is None or self.r_q.shape == (num_kv_heads, D, D)
+
+        def ptr(t):
+            return t.data_ptr() if t is not None else None
+
         self.st = KvCache(cfg, self.pages.data_ptr(), self.block_table.data_ptr(),
-                          self.win.data_ptr(), self.r_k.data_ptr(), self.r_v.data_ptr(),
-                          self.r_q.data_ptr() if self.r_q is not None else None,
-                          1 if out_rotated else 0)
+                          self.win.data_ptr(), ptr(self.r_k), ptr(self.r_v), ptr(self.r_q),
+                          1 if out_rotated else 0, self.rotation)
         self.workspace = None
         self.ring_capacity = L.oscar_ring_capacity(ctypes.byref(cfg))
         self.max_seq_len = L.oscar_max_seq_len(ctypes.byref(cfg))

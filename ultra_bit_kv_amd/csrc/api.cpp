@@ -136,6 +136,7 @@ CacheArgs make_args(const oscar_kv_cache& k) {
   a.r_k = k.r_k;
   a.r_v = k.r_v;
   a.unrot = k.out_rotated ? 0 : 1;
+  a.rot = k.rotation;
   a.hq = c.num_q_heads;
   a.hkv = c.num_kv_heads;
   a.g = c.num_q_heads / c.num_kv_heads;
@@ -204,6 +205,15 @@ bool cache_aligned(const oscar_kv_cache& k) {
          aligned16(k.r_q) &&
          aligned16(k.block_table);
 }
+
+// The rotation kind is one of the three, and the structured kinds take no
+// matrices.
+bool rotation_ok(const oscar_kv_cache& k) {
+  if (k.rotation == OSCAR_ROT_DENSE) return true;
+  return (k.rotation == OSCAR_ROT_HADAMARD || k.rotation == OSCAR_ROT_HADAMARD_BITREV) && !k.r_k &&
+         !k.r_v && !k.r_q;
+}
+bool dense(const oscar_kv_cache& k) { return k.rotation == OSCAR_ROT_DENSE; }
 
 thread_local char g_last_hip[160] = "";
 
@@ -300,8 +310,9 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
   if (st != OSCAR_OK) return st;
   if (!seq_slots_host || !len_before_host || !cu_new_host || !seq_slots || !len_before ||
       !cu_new || !k || !v || !workspace || !cache->pages || !cache->block_table || !cache->win ||
-      !cache->r_k || !cache->r_v)
+      (dense(*cache) && (!cache->r_k || !cache->r_v)))
     return OSCAR_ERR_NULL;
+  if (!rotation_ok(*cache)) return OSCAR_ERR_ARG;
   if (q_rot && !q) return OSCAR_ERR_NULL;
   if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(q_rot) || !aligned16(k_rot) ||
       !aligned16(v_rot) || !cache_aligned(*cache) || !aligned16(workspace))
@@ -359,6 +370,7 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
     jobs.job[0] = RotateJob{k, cache->r_k, nullptr, k_rot, c.num_kv_heads, 1};
     jobs.job[1] = RotateJob{v, cache->r_v, nullptr, v_rot, c.num_kv_heads, 1};
     jobs.n = 2;
+    jobs.kind = cache->rotation;
     if (q_rot)
       jobs.job[jobs.n++] = RotateJob{q, cache->r_q ? cache->r_q : cache->r_k, q_rot, nullptr,
                                      c.num_q_heads, c.num_q_heads / c.num_kv_heads};
@@ -370,6 +382,7 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
   jobs.job[0] = RotateJob{k, cache->r_k, stage_k, k_rot, c.num_kv_heads, 1};
   jobs.job[1] = RotateJob{v, cache->r_v, stage_v, v_rot, c.num_kv_heads, 1};
   jobs.n = 2;
+  jobs.kind = cache->rotation;
   if (q_rot)
     jobs.job[jobs.n++] = RotateJob{q, cache->r_q ? cache->r_q : cache->r_k, q_rot, nullptr,
                                    c.num_q_heads, c.num_q_heads / c.num_kv_heads};
@@ -575,8 +588,9 @@ int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_
   if (st != OSCAR_OK) return st;
   if (!seq_slots_host || !seq_lens_host || !seq_slots || !seq_lens || !workspace ||
       !cache->pages || !cache->block_table || !cache->win ||
-      (!cache->r_v && !cache->out_rotated))
+      (dense(*cache) && !cache->r_v && !cache->out_rotated))
     return OSCAR_ERR_NULL;
+  if (!rotation_ok(*cache)) return OSCAR_ERR_ARG;
   if (((phases & kDecodeSplit) && !q_rot) || ((phases & kDecodeMerge) && !out)) return OSCAR_ERR_NULL;
   if (!aligned16(q_rot) || !aligned16(out) || !cache_aligned(*cache) || !aligned16(workspace))
     return OSCAR_ERR_ARG;
@@ -675,8 +689,9 @@ int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
   if (st != OSCAR_OK) return st;
   if (!seq_slots_host || !len_before_host || !cu_new_host || !seq_slots || !len_before ||
       !cu_new || !q_rot || !k_rot || !v_rot || !out || !cache->pages || !cache->block_table ||
-      !cache->win || (!cache->out_rotated && !cache->r_v))
+      !cache->win || (dense(*cache) && !cache->out_rotated && !cache->r_v))
     return OSCAR_ERR_NULL;
+  if (!rotation_ok(*cache)) return OSCAR_ERR_ARG;
   if (!aligned16(q_rot) || !aligned16(k_rot) || !aligned16(v_rot) || !aligned16(out) ||
       !cache_aligned(*cache))
     return OSCAR_ERR_ARG;

@@ -264,6 +264,24 @@ __global__ __launch_bounds__(HP * 32 < 64 ? 64 : HP * 32) void lse_chunks_kernel
   *(float4_t*)(dst + OO + r * kD + 4 * c4) = O;
 }
 
+// Lane slice of R_V for the un-rotation o = o' . R_V^T on the fp32 matrix
+// cores: rb[u][e] = R_V[j][32 kq + 4u + e] of output channel j.  The
+// structured rotations generate their entries (R = H / sqrt(128) or
+// H P_br / sqrt(128), the same for every head) instead of reading a matrix.
+__device__ __forceinline__ void load_unrotation(const CacheArgs& c, int h, int j, int kq,
+                                                float4_t (&rb)[8]) {
+  if (c.rot) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rb[u][e] = hadamard_entry(c.rot, j, 32 * kq + 4 * u + e);
+    return;
+  }
+  const float4_t* rg = (const float4_t*)(c.r_v + ((size_t)h * kD + j) * kD + 32 * kq);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) rb[u] = rg[u];
+}
+
 // Final merge, then (UNROT) o = o' . R_V^T.
 //
 // Work-group = (KV head, pass, block of SB sequences): its 16 rows are the
@@ -292,12 +310,7 @@ __global__ __launch_bounds__(512) void lse_merge_kernel(CacheArgs c, SeqArgs s, 
   const int s0 = blockIdx.y * sb;
 
   float4_t rb[8];
-  if constexpr (UNROT) {
-    const float4_t* rg =
-        (const float4_t*)(c.r_v + ((size_t)h * kD + 16 * wave + li) * kD + 32 * kq);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) rb[u] = rg[u];
-  }
+  if constexpr (UNROT) load_unrotation(c, h, 16 * wave + li, kq, rb);
 
   const int r = t >> 5, c4 = t & 31;
   const int i = s0 + r / nh;

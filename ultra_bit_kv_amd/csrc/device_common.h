@@ -69,4 +69,16 @@ __device__ __forceinline__ int s_quant_of(int len, int s_sink, int s_keep, int s
   return s_sink + s_flush * k;
 }
 
+// Structured rotations (kind 1: R = H / sqrt(128), kind 2: R = H P_br / sqrt(128),
+// Sylvester's H[i][k] = (-1)^popcount(i & k), P_br the 7-bit bit reversal of
+// the column index): entry R[i][k] in fp32.
+constexpr float kInvSqrtDf = 0x1.6a09e6p-4f;   // fp32(sqrt(2)) / 16
+
+__device__ __forceinline__ int bitrev7(int k) { return (int)(__brev((unsigned)k) >> 25); }
+
+__device__ __forceinline__ float hadamard_entry(int kind, int i, int k) {
+  const int c = kind == 2 ? bitrev7(k) : k;
+  return (__popc((unsigned)(i & c)) & 1) ? -kInvSqrtDf : kInvSqrtDf;
+}
+
 }  // namespace oscar

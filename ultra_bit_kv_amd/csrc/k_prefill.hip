@@ -309,11 +309,7 @@ __global__ __launch_bounds__(64 * W) void prefill_attn_kernel(CacheArgs c, Prefi
   const int cb = wave % kColBlocks;
   const int li = r16, kq = qd;
   float4_t rb[8];
-  {
-    const float4_t* rg = (const float4_t*)(c.r_v + ((size_t)h * kD + 16 * cb + li) * kD + 32 * kq);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) rb[u] = rg[u];
-  }
+  load_unrotation(c, h, 16 * cb + li, kq, rb);
   for (int rt = wave / kColBlocks; rt < kPfRows / 16; rt += kPfWaves / kColBlocks) {
     if (tile * kPfRows + 16 * rt >= rows) break;
     float4_t o4 = {0.f, 0.f, 0.f, 0.f};

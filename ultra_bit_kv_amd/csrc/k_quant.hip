@@ -269,7 +269,8 @@ hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* st
 // and the new rows' ring slots are not among the flushed ones (every decode
 // step with S_keep >= 1): rotation, flush and placement in one launch.
 // Work-groups [0, total_q Hkv) quantize flushed ring rows; the others rotate
-// the new rows, 32 output columns each, writing keys and values straight
+// the new rows, 32 output columns each (whole rows for the structured
+// rotation), writing keys and values straight
 // into their window slot and queries to q_rot.  jobs: 0 = keys, 1 = values,
 // 2 = queries (optional); dst_b of keys / values receives the rotated rows
 // if not null.
@@ -287,8 +288,9 @@ __global__ __launch_bounds__(128) void append_one_kernel(CacheArgs c, ClipArgs c
   b -= nq;
   const int n_tok = s.n_seqs;   // token t is sequence t's new token
   const int blocks = (n_tok + 15) / 16;
-  const int z = b % 4;
-  b /= 4;
+  const int zc = jobs.kind ? 1 : 4;   // dense: four 32-column quarters
+  const int z = b % zc;
+  b /= zc;
   const int tb = b % blocks;
   int y = b / blocks;
   int job = 0;
@@ -304,6 +306,49 @@ __global__ __launch_bounds__(128) void append_one_kernel(CacheArgs c, ClipArgs c
     }
   }
   const int h = y;
+  if (jobs.kind) {   // structured rotation: whole rows, thread rows tid / 16 and tid / 16 + 8
+    int tslot[2], tpos[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int tok = 16 * tb + (threadIdx.x >> 4) + 8 * k;
+      tslot[k] = job != 2 && tok < n_tok ? s.slots[tok] : -1;
+      tpos[k] = job != 2 && tok < n_tok ? s.lens[tok] : -1;
+    }
+    auto out8 = [&](int tok, int c0, const uint16_t (&bits)[8]) {
+      u32x4_r w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = (uint32_t)bits[2 * q] | ((uint32_t)bits[2 * q + 1] << 16);
+      const size_t o = ((size_t)tok * jd.heads + h) * kD + c0;
+      if (job == 2) {
+        *(u32x4_r*)(jd.dst_a + o) = w;
+        return;
+      }
+      if (jd.dst_b) *(u32x4_r*)(jd.dst_b + o) = w;
+      const int k = (tok - 16 * tb) >> 3;
+      const int slot = tslot[k], p = tpos[k];
+      if (slot < 0 || slot >= c.max_seqs || p < 0) return;
+      int blk, tt;
+      if (p < c.s_sink) {
+        blk = p / kPage;
+        tt = p % kPage;
+      } else if (p >= s_quant_of(p + 1, c.s_sink, c.s_keep, c.s_flush)) {
+        const int r = (p - c.s_sink) % c.ring_cap;
+        blk = c.sink_blocks + r / kPage;
+        tt = r % kPage;
+      } else {
+        return;   // excluded by the host: flushed in the same call
+      }
+      uint16_t* wb = c.win + (((size_t)slot * c.hkv + h) * c.win_blocks + blk) * (2 * kPage * kD);
+      if (job == 0) {
+        *(u32x4_r*)(wb + tt * kD + c0) = w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wb[kPage * kD + v_window_index(tt, c0 + e)] = bits[e];
+      }
+    };
+    fwht_block<128>(jd.src, jd.heads, h, 16 * tb, n_tok, jobs.kind, xs, out8);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = 32 * z + 16 * wave + (lane & 15);
   // the cache rows and positions of this lane's four output tokens, loaded
@@ -354,7 +399,8 @@ hipError_t launch_append_one(const CacheArgs& c, const ClipArgs& clip, const Seq
   if (s.n_seqs <= 0) return hipSuccess;
   int rows = 0;
   for (int k = 0; k < jobs.n; ++k) rows += jobs.job[k].heads;
-  const long long grid = (long long)total_q * c.hkv + 4LL * ((s.n_seqs + 15) / 16) * rows;
+  const long long zc = jobs.kind ? 1 : 4;
+  const long long grid = (long long)total_q * c.hkv + zc * ((s.n_seqs + 15) / 16) * rows;
   hipLaunchKernelGGL(append_one_kernel, dim3((unsigned)grid), dim3(128), 0, stream, c, clip, s,
                      jobs, total_q, stage_k, stage_v);
   return hipGetLastError();

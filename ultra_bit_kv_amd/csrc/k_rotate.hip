@@ -3,9 +3,10 @@
 //
 // One launch rotates up to three row sets (keys, values, queries): grid.y
 // enumerates (set, head), grid.z the two 64-column halves of the output.
-// Wave w of a work-group owns 16 output columns and keeps their slice of R
+// Dense: wave w of a work-group owns 16 output columns and keeps their slice of R
 // (one value per k-quad per lane) in registers; the work-group walks TB
-// blocks of 16 tokens, staging each block's input rows in LDS.
+// blocks of 16 tokens, staging each block's input rows in LDS.  Structured
+// kinds: one work-group transforms whole rows (fwht_block), grid.z = 1.
 #include "rotate_common.h"
 
 namespace oscar {
@@ -27,6 +28,22 @@ __global__ __launch_bounds__(256) void rotate_kernel(RotateJobs jobs, int n_tok)
     }
   }
   const int h = y;
+  if (jobs.kind) {   // structured rotation: whole rows per work-group (grid.z = 1)
+    auto out8 = [&](int tok, int c0, const uint16_t (&bits)[8]) {
+      u32x4_r w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = (uint32_t)bits[2 * q] | ((uint32_t)bits[2 * q + 1] << 16);
+      const size_t o = ((size_t)tok * jd.heads + h) * kD + c0;
+      *(u32x4_r*)(jd.dst_a + o) = w;
+      if (jd.dst_b) *(u32x4_r*)(jd.dst_b + o) = w;
+    };
+    for (int b = 0; b < TB; ++b) {
+      const int t0 = (blockIdx.x * TB + b) * 16;
+      if (t0 >= n_tok) break;   // uniform
+      fwht_block<256>(jd.src, jd.heads, h, t0, n_tok, jobs.kind, xs, out8);
+    }
+    return;
+  }
   const int j = 64 * blockIdx.z + 16 * wave + (lane & 15);   // output column of this lane
   float rb[kD / 4];
   load_r_slice(jd.r + (size_t)(h / jd.g) * kD * kD, j, rb);
@@ -47,10 +64,11 @@ hipError_t launch_rotate(const RotateJobs& jobs, int n_tok, hipStream_t stream) 
   int rows = 0;
   for (int k = 0; k < jobs.n; ++k) rows += jobs.job[k].heads;
   const int blocks = (n_tok + 15) / 16;
+  const int zc = jobs.kind ? 1 : 2;   // dense: two 64-column halves
   if (blocks <= 64) {   // small calls (decode steps): one 16-token block per work-group
-    hipLaunchKernelGGL(rotate_kernel<1>, dim3(blocks, rows, 2), dim3(256), 0, stream, jobs, n_tok);
+    hipLaunchKernelGGL(rotate_kernel<1>, dim3(blocks, rows, zc), dim3(256), 0, stream, jobs, n_tok);
   } else {              // prefill: each work-group reuses its R slice over 8 blocks
-    hipLaunchKernelGGL(rotate_kernel<8>, dim3((blocks + 7) / 8, rows, 2), dim3(256), 0, stream,
+    hipLaunchKernelGGL(rotate_kernel<8>, dim3((blocks + 7) / 8, rows, zc), dim3(256), 0, stream,
                        jobs, n_tok);
   }
   return hipGetLastError();

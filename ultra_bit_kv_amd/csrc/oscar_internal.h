@@ -25,6 +25,7 @@ struct CacheArgs {
   int max_seqs, max_pages, num_pages;
   int page_bytes;                // bytes of one page-head block
   int unrot;                     // apply R_V^T after the merge (0: output in the rotated basis)
+  int rot;                       // 0: dense r_k / r_v; 1: H / sqrt(128); 2: H P_br / sqrt(128)
 };
 
 struct ClipArgs {
@@ -54,6 +55,7 @@ struct RotateJob {
 struct RotateJobs {
   RotateJob job[3];
   int n;
+  int kind;                      // 0: dense (the jobs' r); 1, 2: structured (r unused)
 };
 hipError_t launch_rotate(const RotateJobs& jobs, int n_tok, hipStream_t stream);
 

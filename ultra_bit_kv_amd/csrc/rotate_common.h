@@ -31,6 +31,21 @@ __device__ __forceinline__ void load_r_slice(const float* R, int j, float (&rb)[
   for (int kb = 0; kb < kD / 4; ++kb) rb[kb] = R[(size_t)(4 * kb + kq) * kD + j];
 }
 
+// Stages rows t0 .. t0 + 15 of head h of src in xs (rows >= n_tok as zeros),
+// 16 chunks of 8 values per row, and waits for the work-group.
+template <int NT>
+__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, int heads, int h,
+                                           int t0, int n_tok, uint16_t (*xs)[kD + 8]) {
+#pragma unroll
+  for (int e = threadIdx.x; e < 16 * 16; e += NT) {
+    const int xrow = e / 16, xc = 8 * (e % 16);
+    u32x4_r xw = {0u, 0u, 0u, 0u};
+    if (t0 + xrow < n_tok) xw = *(const u32x4_r*)(src + ((size_t)(t0 + xrow) * heads + h) * kD + xc);
+    *(u32x4_r*)(&xs[xrow][xc]) = xw;
+  }
+  __syncthreads();
+}
+
 // Rotates rows t0 .. t0 + 15 (those < n_tok) of head h of src
 // ([n_tok][heads][128] bf16); a work-group of NT threads stages the rows in
 // xs, each wave produces the 16 output columns its lanes' rb slices hold
@@ -41,15 +56,7 @@ __device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ src, i
                                              int t0, int n_tok, int j, const float (&rb)[kD / 4],
                                              uint16_t (*xs)[kD + 8], Out out) {
   const int tid = threadIdx.x, lane = tid & 63, kq = lane >> 4;
-  // staging: 16 rows x 16 chunks of 8 values
-#pragma unroll
-  for (int e = tid; e < 16 * 16; e += NT) {
-    const int xrow = e / 16, xc = 8 * (e % 16);
-    u32x4_r xw = {0u, 0u, 0u, 0u};
-    if (t0 + xrow < n_tok) xw = *(const u32x4_r*)(src + ((size_t)(t0 + xrow) * heads + h) * kD + xc);
-    *(u32x4_r*)(&xs[xrow][xc]) = xw;
-  }
-  __syncthreads();
+  stage_rows<NT>(src, heads, h, t0, n_tok, xs);
   double4_t acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int kb = 0; kb < kD / 4; ++kb) {
@@ -60,6 +67,71 @@ __device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ src, i
   for (int v = 0; v < 4; ++v) {
     const int tok = t0 + kq + 4 * v;
     if (tok < n_tok) out(tok, j, f64_to_bf16_rne(acc[v]));
+  }
+  __syncthreads();   // the next block overwrites xs
+}
+
+// ---- structured rotation --------------------------------------------------
+//
+// OScaR notes, step one "Canalized Rotation": the normalized Hadamard matrix
+// (entries +-1/sqrt(d), orthogonal) rotates keys and queries; OSCAR summary
+// page, section 5 "Rotation Analysis": the composed rotation ends with the
+// Hadamard factor and a bit-reversal permutation P_br.  Kind 1 is
+// R = H / sqrt(128), kind 2 R = H P_br / sqrt(128), with Sylvester's
+// H[i][k] = (-1)^popcount(i & k).
+//
+// The rotation runs as a fast Walsh-Hadamard transform: 7 butterfly stages
+// of fp64 additions.  Every intermediate is a signed sum of the row's bf16
+// values, exact in fp64 while the row's magnitudes span less than 2^38, so the
+// result is the rounding of (x . H) * fp64(1/sqrt(128)) to bf16.  P_br and H
+// commute (H[i][br(k)] = H[br(i)][k]), so kind 2 permutes the input:
+// x . H P_br = (x P_br) . H with (x P_br)_k = x_br(k).
+
+constexpr double kInvSqrtD = 0x1.6a09e667f3bcdp-4;   // fp64(sqrt(2)) / 16 = fp64(1 / sqrt(128))
+
+// Structured rotation of rows t0 .. t0 + 15 (those < n_tok) of head h of src:
+// a 16-lane group takes one row, its lane i the 8 elements 8i .. 8i+7 of the
+// (permuted) row; the butterflies over index bits 0-2 stay in the lane, those
+// over bits 3-6 pair lane i with lane i ^ 1, 2, 4, 8.  out(tok, c0, bits)
+// receives the bf16 bits of output channels c0 .. c0 + 7.  Ends with a
+// barrier (xs may be reused).
+template <int NT, class Out>
+__device__ __forceinline__ void fwht_block(const uint16_t* __restrict__ src, int heads, int h,
+                                           int t0, int n_tok, int kind, uint16_t (*xs)[kD + 8],
+                                           Out out) {
+  static_assert(NT % 16 == 0 && 256 % NT == 0, "whole rows per pass");
+  stage_rows<NT>(src, heads, h, t0, n_tok, xs);
+  const int li = threadIdx.x & 15;
+  for (int row = threadIdx.x >> 4; row < 16; row += NT / 16) {
+    double x[8];
+    if (kind == 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (double)bf16_bits_to_f32(xs[row][bitrev7(8 * li + e)]);
+    } else {
+      const u32x4_r w = *(const u32x4_r*)(&xs[row][8 * li]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (double)bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    }
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!(e & m)) {
+          const double a = x[e], b = x[e | m];
+          x[e] = a + b;
+          x[e | m] = a - b;
+        }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double y = __shfl_xor(x[e], m, 16);
+        x[e] = (li & m) ? y - x[e] : x[e] + y;
+      }
+    uint16_t bits[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bits[e] = f64_to_bf16_rne(x[e] * kInvSqrtD);
+    if (t0 + row < n_tok) out(t0 + row, 8 * li, bits);
   }
   __syncthreads();   // the next block overwrites xs
 }
