@@ -19,7 +19,9 @@ Readings taken (all in the design notes):
 2. Delta = (hi - lo) / 3, stored as fp16 ``s``; the zero point is stored as the
    fp16 *value* ``z`` = lo, so x_hat = s * code + z (the same affine map as
    Delta (Q - z') with z' = -lo / Delta, defined also when Delta = 0).
-3. Codes are taken from the stored fp16 s and z: round-half-to-even of
+3. A zero order statistic is +0 (-0 and +0 are the same value; the stored
+   zero point of a group whose lower clip limit is zero is then +0).
+4. Codes are taken from the stored fp16 s and z: round-half-to-even of
    (x - z) / s clamped to [0, 3], which equals
    [x > z + s/2] + [x >= z + 3s/2] + [x > z + 5s/2] exactly.  s = 0 gives code 0.
 """
@@ -50,7 +52,9 @@ def quantile_type7(sorted_groups, q):
 
 def clip_range(groups, kappa):
     """(lo, hi) clip limits of each group: Q(1 - kappa) and Q(kappa)."""
-    srt = np.sort(np.asarray(groups, dtype=np.float64), axis=-1)
+    # -0 and +0 are one value: a zero order statistic is taken as +0 (x + 0.0
+    # maps -0 to +0 and leaves every other value unchanged)
+    srt = np.sort(np.asarray(groups, dtype=np.float64), axis=-1) + 0.0
     kap = np.asarray(kappa, dtype=np.float32).astype(np.float64)
     hi = quantile_type7(srt, kap)
     lo = quantile_type7(srt, 1.0 - kap)

@@ -182,3 +182,20 @@ def test_bytes_per_token_head_match_pages():
     assert per_tok == {128: 72.0, 64: 80.0, 32: 96.0}
     assert round(bf16 / per_tok[32], 1) == mb["int2_ratio_g32"]
     assert per_tok[128] * 8 / 2 / 128 == mb["int2_bits_per_element_g128_without_windows"]
+
+
+def test_signed_zero_order_statistic_is_plus_zero():
+    # kappa = 1: lo is the group minimum; a group whose minimum is zero, held
+    # as -0 in some channels and +0 in others, stores the zero point +0
+    g = 32
+    x = np.abs(np.linspace(0.0, 3.0, g))
+    x[[0, 5, 9]] = -0.0
+    x[[1, 2]] = 0.0
+    lo, hi = quant.clip_range(x[None, :], 1.0)
+    assert lo[0] == 0.0 and not np.signbit(lo[0]) and hi[0] == 3.0
+    _, s, z = quant.quantize_rows(x[None, :], 1.0, g)
+    assert int(z[0, 0]) == 0x0000
+    # kappa < 1 whose lower quantile interpolates between -0 and +0 is +0 too
+    y = np.concatenate([[-1.0], [-0.0] * 10, [0.0] * 10, np.linspace(0.5, 2.0, g - 21)])
+    lo2, _ = quant.clip_range(y[None, :], 0.9)
+    assert lo2[0] == 0.0 and not np.signbit(lo2[0])
