@@ -202,6 +202,55 @@ def measure_prefill(w, lbs, ns, reps=10):
     return {"ms": ms, "tflops": fl / (ms * 1e-3) / 1e12, "alg_tflop": fl / 1e12}
 
 
+def append_bytes(w, ns):
+    """Algorithmic bytes of one append of fresh chunks (positions 0 .. n - 1
+    of each sequence) with their queries: the k, v and q rows in and q' out
+    (bf16), and every row's cache image out -- an INT2 row-head is K and V
+    codes plus fp16 scale/zero per group, a window row-head K and V bf16."""
+    per_int2 = 64 + 1024 // w.group
+    total = 0
+    for n in ns:
+        n = int(n)
+        s_quant = w.s_sink + w.s_flush * max(0, (n - w.s_sink - w.s_keep) // w.s_flush)
+        n_int2 = max(0, s_quant - w.s_sink)
+        n_bf16 = min(n, w.s_sink) + max(0, n - max(s_quant, w.s_sink))
+        total += n * (2 * w.hkv + 2 * w.hq) * 256
+        total += w.hkv * (n_int2 * per_int2 + n_bf16 * 512)
+    return total
+
+
+def measure_append(w, ns, rotation, reps=10):
+    """oscar_rotate_quant_append of one fresh chunk per sequence with queries
+    (rotation, quantization of the rows that reach INT2, window placement);
+    the chunk is re-appended at position 0, which rewrites the same rows.
+    Median of `reps` calls (HIP events on the calls' stream)."""
+    import torch
+    from ultra_bit_kv_amd import SeqBatch, as_bf16
+    cache = make_layer(w, ns, len(ns), rotation=rotation)
+    idx = list(range(len(ns)))
+    k = as_bf16(np.concatenate([w.keys(i, 0, ns[i]) for i in idx]))
+    v = as_bf16(np.concatenate([w.values(i, 0, ns[i]) for i in idx]))
+    q = as_bf16(np.concatenate([w.queries(i, 0, ns[i]) for i in idx]))
+    q_rot = torch.empty_like(q)
+    b = SeqBatch(idx, [0] * len(ns), ns)
+    cache.workspace_for(len(ns), sum(ns))
+    cache.append(b, k, v, q, q_rot)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, c in evs:
+        a.record()
+        cache.append(b, k, v, q, q_rot)
+        c.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(c) for a, c in evs]))
+    nb = append_bytes(w, ns)
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {"ms": ms, "alg_bytes": nb,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS}}
+
+
 def cpu_prefill_baseline(w, lb, n, seconds=6.0, rows=16):
     """The oracle's chunked-prefill attention (O6) for a sample of chunk rows
     of one sequence and KV head, on the host cores: algorithmic TFLOP/s."""
@@ -250,16 +299,17 @@ def int2_pages(w, L):
     return -(-max(0, s_quant - w.s_sink) // 16)
 
 
-def make_layer(w, lens_max, n):
-    """An empty cache sized for rows growing to lens_max (seeded page pool)."""
+def make_layer(w, lens_max, n, rotation=0):
+    """An empty cache sized for rows growing to lens_max (seeded page pool);
+    rotation 1 / 2: the structured R = H / sqrt(128) / H P_br / sqrt(128)."""
     from ultra_bit_kv_amd import OscarKVCache
-    r_k, r_v = w.rotations()
+    r_k, r_v = w.rotations() if rotation == 0 else (None, None)
     kk, kv = w.kappas()
     bt, total = w.page_pool([max(1, int2_pages(w, L)) for L in lens_max])
     return OscarKVCache(num_q_heads=w.hq, num_kv_heads=w.hkv, group_size=w.group,
                         s_sink=w.s_sink, s_keep=w.s_keep, s_flush=w.s_flush, max_seqs=n,
                         max_pages_per_seq=bt.shape[1], num_pages=total, clip_k=kk, clip_v=kv,
-                        r_k=r_k, r_v=r_v, block_table=bt)
+                        r_k=r_k, r_v=r_v, block_table=bt, rotation=rotation)
 
 
 def populate(cache, w, lens, chunk=8192, max_tokens=1 << 18):
@@ -403,6 +453,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-prefill", dest="prefill", action="store_false",
                     help="skip the chunked-prefill attention legs")
+    ap.add_argument("--no-rotation-modes", dest="rotation_modes", action="store_false",
+                    help="skip the dense / structured rotation append comparison")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -510,6 +562,20 @@ def main():
         }
         if not args.no_cpu_baseline:
             res["prefill"]["cpu_baseline"] = cpu_prefill_baseline(w5, 0, w5.prefill_len)
+    if args.rotation_modes:
+        # the Qwen3-32B step's append (16 fresh 2048-token chunks, 64 / 8
+        # heads) with the dense per-head rotation and the structured
+        # R = H P_br / sqrt(128) (fast Walsh-Hadamard transform)
+        w5 = get("c5_qwen3_32b_step")
+        ns5 = [w5.prefill_len] * w5.prefill_chunks
+        w5 = w5.scaled(n_seqs=len(ns5), lengths=("list", tuple(ns5)))
+        res["append_rotation_modes"] = {
+            "call": "oscar_rotate_quant_append (rotation + quantization + placement)",
+            "workload": "16 fresh 2048-token chunks with queries, 64 / 8 heads, G=128, "
+                        "windows 64/256/256",
+            "dense": measure_append(w5, ns5, 0),
+            "hadamard_bitrev": measure_append(w5, ns5, 2),
+        }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, lens0, seconds=args.cpu_seconds)
     print(json.dumps(res), flush=True)

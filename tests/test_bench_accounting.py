@@ -45,3 +45,17 @@ def test_timed_path_does_not_load_the_oracle():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                        cwd=str(__import__("pathlib").Path(bench.__file__).parent))
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_append_bytes_matches_oracle_placement(name):
+    w = CONFIGS[name]
+    ns = [1, 2, w.s_sink, w.s_sink + w.s_keep, w.s_sink + w.s_keep + w.s_flush + 3, 2048]
+    per = 64 + 1024 // w.group
+    want = 0
+    for n in ns:
+        sink, int2, rec = placement.segments(n, w.s_sink, w.s_keep, w.s_flush)
+        n2 = int2[1] - int2[0]
+        nb = (sink[1] - sink[0]) + (rec[1] - rec[0])
+        want += n * (2 * w.hkv + 2 * w.hq) * 256 + w.hkv * (n2 * per + nb * 512)
+    assert bench.append_bytes(w, ns) == want

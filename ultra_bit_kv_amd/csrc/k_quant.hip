@@ -30,20 +30,34 @@ __device__ __forceinline__ double lerp_quantile(double a, double b, double f) {
   return a + f * (b - a);
 }
 
+// Order-preserving 16-bit key of a bf16 value (larger value, larger key);
+// -0 is keyed as +0, so a zero order statistic is +0.
+__device__ __forceinline__ uint32_t bf16_order_key(uint32_t b) {
+  b = b == 0x8000u ? 0u : b;
+  return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+__device__ __forceinline__ float bf16_of_order_key(uint32_t k) {
+  return bf16_bits_to_f32(k & 0x8000u ? k & 0x7FFFu : ~k & 0xFFFFu);
+}
+
 // Quantize position `item` (of all the append's quantized positions) of KV
-// head h; run by a work-group of 128 threads.
+// head h; run by a work-group of 128 threads, wave 0 on the key row and wave
+// 1 on the value row, each on its own (no barrier, no LDS): lane l holds
+// channels 2l and 2l + 1.
+//
+// The clip limits need the order statistics s[i], s[i + 1] of each group
+// (type-7 quantiles).  They are found by a bitwise search over the
+// order-preserving keys of the bf16 values: from the top bit down, a bit of
+// the answer is set when fewer than i + 1 of the group's keys lie at or below
+// the prefix with that bit clear (two ballots per step count the group's
+// lanes).  s[i + 1] is s[i] when more than i + 1 keys lie at or below it,
+// else the group's smallest key above it.
 __device__ __forceinline__ void quantize_item(const CacheArgs& c, const ClipArgs& clip,
                                               const SeqArgs& s,
                                               const uint16_t* __restrict__ stage_k,
                                               const uint16_t* __restrict__ stage_v, int item,
                                               int h) {
 #pragma clang fp contract(off)
-  __shared__ float vals[2][kD];
-  __shared__ float sel[2][4][4];
-  __shared__ uint32_t nib[2][64];
-  __shared__ int s_run[2];
-  __shared__ int s_seq, s_before;
-
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;   // w: 0 = K, 1 = V
   // ---- sequence of this position: prefix sum of the per-sequence counts
   auto count_of = [&](int k) {
@@ -53,9 +67,10 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const ClipArgs
     return s_quant_of(lb + nn, c.s_sink, c.s_keep, c.s_flush) -
            s_quant_of(lb, c.s_sink, c.s_keep, c.s_flush);
   };
+  int i, before;
   {
-    const int n = s.n_seqs, per = (n + 127) / 128;
-    const int k0 = min((int)threadIdx.x * per, n), k1 = min(k0 + per, n);
+    const int n = s.n_seqs, per = (n + 63) / 64;
+    const int k0 = min(lane * per, n), k1 = min(k0 + per, n);
     int run = 0;
     for (int k = k0; k < k1; ++k) run += count_of(k);
     int incl = run;
@@ -64,26 +79,25 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const ClipArgs
       const int y = __shfl_up(incl, d);
       if (lane >= d) incl += y;
     }
-    if (lane == 63) s_run[w] = incl;
-    if (threadIdx.x == 0) s_seq = -1;
-    __syncthreads();
-    int off = (w == 1 ? s_run[0] : 0) + incl - run;
-    for (int k = k0; k < k1; ++k) {
-      const int q = count_of(k);
-      if (item >= off && item < off + q) {   // exactly one (k, thread) matches
-        s_seq = k;
-        s_before = off;
+    const bool hit = item >= incl - run && item < incl;   // exactly one lane, if any
+    const unsigned long long hits = __ballot(hit);
+    if (hits == 0ull) return;   // uniform: the device counts do not reach this item
+    int seq = -1, off = incl - run;
+    if (hit) {
+      for (int k = k0; k < k1; ++k) {
+        const int q = count_of(k);
+        if (seq < 0 && item < off + q) seq = k;
+        else if (seq < 0) off += q;
       }
-      off += q;
     }
-    __syncthreads();
+    const int src = __ffsll(hits) - 1;
+    i = __shfl(seq, src);
+    before = __shfl(off, src);
   }
-  const int i = s_seq;
-  if (i < 0) return;   // uniform: the device counts do not reach this item
   const int slot = s.slots[i];
   const int lb = s.lens[i];
   const int sqb = s_quant_of(lb, c.s_sink, c.s_keep, c.s_flush);
-  const int p = sqb + (item - s_before);
+  const int p = sqb + (item - before);
   const int m = (p - c.s_sink) / kPage, t = (p - c.s_sink) % kPage;
   const int phys = m < c.max_pages ? c.block_table[(size_t)slot * c.max_pages + m] : -1;
 
@@ -109,38 +123,42 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const ClipArgs
   if (phys < 0 || phys >= c.num_pages) return;   // uniform: unmapped page, nothing to store
   const float x0 = bf16_bits_to_f32(pair & 0xFFFFu);
   const float x1 = bf16_bits_to_f32(pair >> 16);
-  vals[w][2 * lane] = x0;
-  vals[w][2 * lane + 1] = x1;
-  __syncthreads();
 
-  // ---- ranks inside the group (G channels), order statistics for the quantiles
+  // ---- order statistics of this lane's group (G / 2 adjacent lanes)
   const int G = c.group;
-  const int gi = (2 * lane) / G;               // both of this lane's channels are in group gi
-  const int gs = gi * G;
-  const int c0 = 2 * lane, c1 = 2 * lane + 1;
-  int r0 = 0, r1 = 0;
-#pragma unroll 8
-  for (int jj = 0; jj < G; ++jj) {
-    const int j = gs + ((jj + gi) & (G - 1));  // per-group start offset avoids bank conflicts
-    const float v = vals[w][j];
-    r0 += (v < x0) || (v == x0 && j < c0);
-    r1 += (v < x1) || (v == x1 && j < c1);
-  }
+  const int lpg = G / 2;
+  const int gi = lane / lpg;
+  const unsigned long long gmask =
+      lpg == 64 ? ~0ull : (((1ull << lpg) - 1ull) << (lpg * gi));
+  const uint32_t key0 = bf16_order_key(pair & 0xFFFFu), key1 = bf16_order_key(pair >> 16);
+  auto count_le = [&](uint32_t tk) {
+    return __popcll(__ballot(key0 <= tk) & gmask) + __popcll(__ballot(key1 <= tk) & gmask);
+  };
   const double kap = (double)(w == 0 ? clip.k[h] : clip.v[h]);
   const double q_hi = kap, q_lo = 1.0 - kap;
   const double h_hi = (double)(G - 1) * q_hi, h_lo = (double)(G - 1) * q_lo;
   const double fl_hi = __builtin_floor(h_hi), fl_lo = __builtin_floor(h_lo);
   const int i_hi = (int)fl_hi, i_lo = (int)fl_lo;
-  const int want[4] = {i_lo, min(i_lo + 1, G - 1), i_hi, min(i_hi + 1, G - 1)};
+  uint32_t p_lo = 0, p_hi = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (r0 == want[k]) sel[w][gi][k] = x0;
-    if (r1 == want[k]) sel[w][gi][k] = x1;
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t below = (1u << bit) - 1u;
+    const int c_lo = count_le(p_lo | below), c_hi = count_le(p_hi | below);
+    if (c_lo < i_lo + 1) p_lo |= 1u << bit;
+    if (c_hi < i_hi + 1) p_hi |= 1u << bit;
   }
-  __syncthreads();
+  auto next_key = [&](uint32_t k, int idx) {   // key of s[min(idx + 1, G - 1)] given s[idx] = k
+    const int want = min(idx + 1, G - 1) + 1;
+    uint32_t nx = min(key0 > k ? key0 : 0x10000u, key1 > k ? key1 : 0x10000u);
+    for (int d = 1; d < lpg; d <<= 1) nx = min(nx, (uint32_t)__shfl_xor((int)nx, d));
+    return count_le(k) >= want ? k : nx;
+  };
+  const uint32_t p_lo1 = next_key(p_lo, i_lo), p_hi1 = next_key(p_hi, i_hi);
 
-  const double lo = lerp_quantile((double)sel[w][gi][0], (double)sel[w][gi][1], h_lo - fl_lo);
-  const double hi = lerp_quantile((double)sel[w][gi][2], (double)sel[w][gi][3], h_hi - fl_hi);
+  const double lo = lerp_quantile((double)bf16_of_order_key(p_lo), (double)bf16_of_order_key(p_lo1),
+                                  h_lo - fl_lo);
+  const double hi = lerp_quantile((double)bf16_of_order_key(p_hi), (double)bf16_of_order_key(p_hi1),
+                                  h_hi - fl_hi);
   const double delta = (hi - lo) / 3.0;
   const uint32_t s16 = f64_to_f16_rne(delta);
   const uint32_t z16 = f64_to_f16_rne(lo);
@@ -152,24 +170,24 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const ClipArgs
     q0 = (uint32_t)(d0 > t1) + (uint32_t)(d0 >= t2) + (uint32_t)(d0 > t3);
     q1 = (uint32_t)(d1 > t1) + (uint32_t)(d1 >= t2) + (uint32_t)(d1 > t3);
   }
-  nib[w][lane] = q0 | (q1 << 2);
-  __syncthreads();
+  const uint32_t nib = q0 | (q1 << 2);   // channels 2 lane, 2 lane + 1
 
   // ---- pack and store into the page-head block (layout in oscar_kv.h)
   uint8_t* base = c.pages + ((size_t)phys * c.hkv + h) * c.page_bytes;
   if (w == 0) {
-    if (lane < 8) {   // word (8t + lane): channels 16 lane .. 16 lane + 15 = nibbles 8 lane .. 8 lane + 7
-      uint32_t word = 0;
+    // word (8t + l / 8): channels 16 (l / 8) .. + 15 = the nibbles of lanes 8 (l / 8) .. + 7
+    uint32_t word = nib << (4 * (lane & 7));
 #pragma unroll
-      for (int k = 0; k < 8; ++k) word |= nib[0][8 * lane + k] << (4 * k);
-      ((uint32_t*)base)[8 * t + lane] = word;
-    }
+    for (int d = 1; d < 8; d <<= 1) word |= (uint32_t)__shfl_xor((int)word, d);
+    if ((lane & 7) == 0) ((uint32_t*)base)[8 * t + lane / 8] = word;
   } else {
-    if (lane < 16) {  // half-word of channels 8 lane .. 8 lane + 7 of slot t
-      uint32_t hw = 0;
+    // half-word of channels 8L .. 8L + 7 of slot t = the nibbles of lanes 4L .. 4L + 3
+    uint32_t hw = nib << (4 * (lane & 3));
 #pragma unroll
-      for (int k = 0; k < 4; ++k) hw |= nib[1][4 * lane + k] << (4 * k);
-      const int u = 2 * (16 * (t >> 2) + lane) + ((t & 3) >> 1);
+    for (int d = 1; d < 4; d <<= 1) hw |= (uint32_t)__shfl_xor((int)hw, d);
+    if ((lane & 3) == 0) {
+      const int L = lane / 4;
+      const int u = 2 * (16 * (t >> 2) + L) + ((t & 3) >> 1);
       ((uint16_t*)(base + 512))[2 * u + (t & 1)] = (uint16_t)hw;
     }
   }

@@ -122,12 +122,13 @@ __device__ __forceinline__ void fwht_block(const uint16_t* __restrict__ src, int
           x[e | m] = a - b;
         }
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
+    for (int m = 1; m < 16; m <<= 1) {
+      // the lane with bit m clear keeps a + b, its partner b - a: own value
+      // times +-1 plus the partner's, one exact-product fma
+      const double sg = (li & m) ? -1.0 : 1.0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double y = __shfl_xor(x[e], m, 16);
-        x[e] = (li & m) ? y - x[e] : x[e] + y;
-      }
+      for (int e = 0; e < 8; ++e) x[e] = __builtin_fma(x[e], sg, __shfl_xor(x[e], m, 16));
+    }
     uint16_t bits[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) bits[e] = f64_to_bf16_rne(x[e] * kInvSqrtD);
