@@ -346,10 +346,20 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
 
   hipStream_t sm = (hipStream_t)stream;
   const CacheArgs a = make_args(*cache);
-  ClipArgs clip{};
+  QuantArgs clip{};
   for (int h = 0; h < c.num_kv_heads; ++h) {
     clip.k[h] = c.clip_k[h];
     clip.v[h] = c.clip_v[h];
+  }
+  if (n_seqs <= kMaxQuantSeqs) {
+    clip.qn = n_seqs;
+    int64_t run = 0;
+    for (int i = 0; i < n_seqs; ++i) {
+      clip.q_before[i] = (int32_t)run;
+      const int64_t lb = len_before_host[i];
+      run += s_quant(lb + (int64_t)cu_new_host[i + 1] - cu_new_host[i], c) - s_quant(lb, c);
+    }
+    clip.q_before[n_seqs] = (int32_t)run;
   }
   SeqArgs sa{seq_slots, len_before, cu_new, n_seqs};
   uint8_t* ws = (uint8_t*)workspace;

@@ -40,6 +40,59 @@ __device__ __forceinline__ float bf16_of_order_key(uint32_t k) {
   return bf16_bits_to_f32(k & 0x8000u ? k & 0x7FFFu : ~k & 0xFFFFu);
 }
 
+// Keys of the order statistics s[i_lo], s[i_lo + 1], s[i_hi], s[i_hi + 1]
+// (indices clamped to the group) of this lane's group of 2 LPG channels (LPG
+// lanes, two keys per lane).  The per-group search state lives in scalar
+// registers: each step compares every key against its group's threshold once
+// per search (two ballots) and counts each group's bits of the ballots.
+template <int LPG>
+__device__ __forceinline__ void group_order_stats(uint32_t key0, uint32_t key1, int lane, int i_lo,
+                                                  int i_hi, uint32_t& k_lo, uint32_t& k_lo1,
+                                                  uint32_t& k_hi, uint32_t& k_hi1) {
+  constexpr int NG = 64 / LPG;
+  constexpr unsigned long long kLow = LPG == 64 ? ~0ull : (1ull << LPG) - 1ull;
+  const int gi = lane / LPG;
+  uint32_t plo[NG], phi[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) plo[g] = phi[g] = 0u;
+  auto mine = [&](const uint32_t (&v)[NG]) {
+    uint32_t r = v[0];
+#pragma unroll
+    for (int g = 1; g < NG; ++g) r = gi == g ? v[g] : r;
+    return r;
+  };
+  auto count = [&](unsigned long long b0, unsigned long long b1, int g) {
+    return __popcll((b0 >> (g * LPG)) & kLow) + __popcll((b1 >> (g * LPG)) & kLow);
+  };
+#pragma unroll
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t below = (1u << bit) - 1u;
+    const uint32_t tl = mine(plo) | below, th = mine(phi) | below;
+    const unsigned long long l0 = __ballot(key0 <= tl), l1 = __ballot(key1 <= tl);
+    const unsigned long long h0 = __ballot(key0 <= th), h1 = __ballot(key1 <= th);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (count(l0, l1, g) < i_lo + 1) plo[g] |= 1u << bit;
+      if (count(h0, h1, g) < i_hi + 1) phi[g] |= 1u << bit;
+    }
+  }
+  // s[i + 1] is s[i] when at least min(i + 1, G - 1) + 1 keys lie at or below
+  // it, else the group's smallest key above it
+  auto next_key = [&](uint32_t k, int idx) {
+    const int want = min(idx + 1, 2 * LPG - 1) + 1;
+    const unsigned long long b0 = __ballot(key0 <= k), b1 = __ballot(key1 <= k);
+    const int cnt = __popcll((b0 >> (gi * LPG)) & kLow) + __popcll((b1 >> (gi * LPG)) & kLow);
+    uint32_t nx = min(key0 > k ? key0 : 0x10000u, key1 > k ? key1 : 0x10000u);
+#pragma unroll
+    for (int d = 1; d < LPG; d <<= 1) nx = min(nx, (uint32_t)__shfl_xor((int)nx, d));
+    return cnt >= want ? k : nx;
+  };
+  k_lo = mine(plo);
+  k_hi = mine(phi);
+  k_lo1 = next_key(k_lo, i_lo);
+  k_hi1 = next_key(k_hi, i_hi);
+}
+
 // Quantize position `item` (of all the append's quantized positions) of KV
 // head h; run by a work-group of 128 threads, wave 0 on the key row and wave
 // 1 on the value row, each on its own (no barrier, no LDS): lane l holds
@@ -49,10 +102,9 @@ __device__ __forceinline__ float bf16_of_order_key(uint32_t k) {
 // (type-7 quantiles).  They are found by a bitwise search over the
 // order-preserving keys of the bf16 values: from the top bit down, a bit of
 // the answer is set when fewer than i + 1 of the group's keys lie at or below
-// the prefix with that bit clear (two ballots per step count the group's
-// lanes).  s[i + 1] is s[i] when more than i + 1 keys lie at or below it,
-// else the group's smallest key above it.
-__device__ __forceinline__ void quantize_item(const CacheArgs& c, const ClipArgs& clip,
+// the prefix with that bit clear (group_order_stats).  The sequence of the
+// position comes from the host's table when the call has one.
+__device__ __forceinline__ void quantize_item(const CacheArgs& c, const QuantArgs& clip,
                                               const SeqArgs& s,
                                               const uint16_t* __restrict__ stage_k,
                                               const uint16_t* __restrict__ stage_v, int item,
@@ -68,7 +120,17 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const ClipArgs
            s_quant_of(lb, c.s_sink, c.s_keep, c.s_flush);
   };
   int i, before;
-  {
+  if (clip.qn > 0) {   // the host's table: the last sequence starting at or before the item
+    if (item >= clip.q_before[clip.qn]) return;
+    int lo = 0, hi = clip.qn - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (clip.q_before[mid] <= item) lo = mid;
+      else hi = mid - 1;
+    }
+    i = lo;
+    before = clip.q_before[lo];
+  } else {
     const int n = s.n_seqs, per = (n + 63) / 64;
     const int k0 = min(lane * per, n), k1 = min(k0 + per, n);
     int run = 0;
@@ -126,34 +188,21 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const ClipArgs
 
   // ---- order statistics of this lane's group (G / 2 adjacent lanes)
   const int G = c.group;
-  const int lpg = G / 2;
-  const int gi = lane / lpg;
-  const unsigned long long gmask =
-      lpg == 64 ? ~0ull : (((1ull << lpg) - 1ull) << (lpg * gi));
+  const int gi = (2 * lane) / G;
   const uint32_t key0 = bf16_order_key(pair & 0xFFFFu), key1 = bf16_order_key(pair >> 16);
-  auto count_le = [&](uint32_t tk) {
-    return __popcll(__ballot(key0 <= tk) & gmask) + __popcll(__ballot(key1 <= tk) & gmask);
-  };
   const double kap = (double)(w == 0 ? clip.k[h] : clip.v[h]);
   const double q_hi = kap, q_lo = 1.0 - kap;
   const double h_hi = (double)(G - 1) * q_hi, h_lo = (double)(G - 1) * q_lo;
   const double fl_hi = __builtin_floor(h_hi), fl_lo = __builtin_floor(h_lo);
   const int i_hi = (int)fl_hi, i_lo = (int)fl_lo;
-  uint32_t p_lo = 0, p_hi = 0;
-#pragma unroll
-  for (int bit = 15; bit >= 0; --bit) {
-    const uint32_t below = (1u << bit) - 1u;
-    const int c_lo = count_le(p_lo | below), c_hi = count_le(p_hi | below);
-    if (c_lo < i_lo + 1) p_lo |= 1u << bit;
-    if (c_hi < i_hi + 1) p_hi |= 1u << bit;
+  uint32_t p_lo, p_lo1, p_hi, p_hi1;
+  if (G == 128) {
+    group_order_stats<64>(key0, key1, lane, i_lo, i_hi, p_lo, p_lo1, p_hi, p_hi1);
+  } else if (G == 64) {
+    group_order_stats<32>(key0, key1, lane, i_lo, i_hi, p_lo, p_lo1, p_hi, p_hi1);
+  } else {
+    group_order_stats<16>(key0, key1, lane, i_lo, i_hi, p_lo, p_lo1, p_hi, p_hi1);
   }
-  auto next_key = [&](uint32_t k, int idx) {   // key of s[min(idx + 1, G - 1)] given s[idx] = k
-    const int want = min(idx + 1, G - 1) + 1;
-    uint32_t nx = min(key0 > k ? key0 : 0x10000u, key1 > k ? key1 : 0x10000u);
-    for (int d = 1; d < lpg; d <<= 1) nx = min(nx, (uint32_t)__shfl_xor((int)nx, d));
-    return count_le(k) >= want ? k : nx;
-  };
-  const uint32_t p_lo1 = next_key(p_lo, i_lo), p_hi1 = next_key(p_hi, i_hi);
 
   const double lo = lerp_quantile((double)bf16_of_order_key(p_lo), (double)bf16_of_order_key(p_lo1),
                                   h_lo - fl_lo);
@@ -197,13 +246,13 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const ClipArgs
   }
 }
 
-__global__ __launch_bounds__(128) void quantize_kernel(CacheArgs c, ClipArgs clip, SeqArgs s,
+__global__ __launch_bounds__(128) void quantize_kernel(CacheArgs c, QuantArgs clip, SeqArgs s,
                                                        const uint16_t* __restrict__ stage_k,
                                                        const uint16_t* __restrict__ stage_v) {
   quantize_item(c, clip, s, stage_k, stage_v, blockIdx.x, blockIdx.y);
 }
 
-hipError_t launch_quantize(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
+hipError_t launch_quantize(const CacheArgs& c, const QuantArgs& clip, const SeqArgs& s,
                            const uint16_t* stage_k, const uint16_t* stage_v, int total_q,
                            hipStream_t stream) {
   if (total_q <= 0 || s.n_seqs <= 0) return hipSuccess;
@@ -251,7 +300,7 @@ __global__ __launch_bounds__(128) void place_kernel(CacheArgs c, SeqArgs s,
 // Quantize and place in one launch, for appends where no new row lands on a
 // ring slot that the flush reads (the two sets of work-groups then touch
 // disjoint memory).  Work-groups [0, total_q Hkv) quantize, the rest place.
-__global__ __launch_bounds__(128) void flush_place_kernel(CacheArgs c, ClipArgs clip, SeqArgs s,
+__global__ __launch_bounds__(128) void flush_place_kernel(CacheArgs c, QuantArgs clip, SeqArgs s,
                                                           const uint16_t* __restrict__ stage_k,
                                                           const uint16_t* __restrict__ stage_v,
                                                           int total_q, int max_new) {
@@ -265,7 +314,7 @@ __global__ __launch_bounds__(128) void flush_place_kernel(CacheArgs c, ClipArgs 
   }
 }
 
-hipError_t launch_flush_place(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
+hipError_t launch_flush_place(const CacheArgs& c, const QuantArgs& clip, const SeqArgs& s,
                               const uint16_t* stage_k, const uint16_t* stage_v, int total_q,
                               int max_new, hipStream_t stream) {
   if (s.n_seqs <= 0 || (total_q <= 0 && max_new <= 0)) return hipSuccess;
@@ -292,7 +341,7 @@ hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* st
 // into their window slot and queries to q_rot.  jobs: 0 = keys, 1 = values,
 // 2 = queries (optional); dst_b of keys / values receives the rotated rows
 // if not null.
-__global__ __launch_bounds__(128) void append_one_kernel(CacheArgs c, ClipArgs clip, SeqArgs s,
+__global__ __launch_bounds__(128) void append_one_kernel(CacheArgs c, QuantArgs clip, SeqArgs s,
                                                          RotateJobs jobs, int total_q,
                                                          const uint16_t* __restrict__ stage_k,
                                                          const uint16_t* __restrict__ stage_v) {
@@ -411,7 +460,7 @@ __global__ __launch_bounds__(128) void append_one_kernel(CacheArgs c, ClipArgs c
   rotate_block<128>(jd.src, jd.heads, h, 16 * tb, n_tok, j, rb, xs, out);
 }
 
-hipError_t launch_append_one(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
+hipError_t launch_append_one(const CacheArgs& c, const QuantArgs& clip, const SeqArgs& s,
                              const RotateJobs& jobs, int total_q, const uint16_t* stage_k,
                              const uint16_t* stage_v, hipStream_t stream) {
   if (s.n_seqs <= 0) return hipSuccess;

@@ -28,9 +28,15 @@ struct CacheArgs {
   int rot;                       // 0: dense r_k / r_v; 1: H / sqrt(128); 2: H P_br / sqrt(128)
 };
 
-struct ClipArgs {
+// Clip ratios, and the host's table of where each sequence's quantized
+// positions start among the call's (n = 0: the kernels find them from the
+// device arrays).
+constexpr int kMaxQuantSeqs = 1024;
+struct QuantArgs {
   float k[kMaxKvHeads];
   float v[kMaxKvHeads];
+  int qn;
+  int32_t q_before[kMaxQuantSeqs + 1];
 };
 
 // Per-call sequence metadata (device arrays provided by the caller).
@@ -62,13 +68,13 @@ hipError_t launch_rotate(const RotateJobs& jobs, int n_tok, hipStream_t stream);
 // Quantize every position that moves to INT2 in this append, from the ring
 // (old rows) or the staging rows (new tokens), into the pages.  total_q =
 // sum over sequences of S_quant(after) - S_quant(before) (< 2^31).
-hipError_t launch_quantize(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
+hipError_t launch_quantize(const CacheArgs& c, const QuantArgs& clip, const SeqArgs& s,
                            const uint16_t* stage_k, const uint16_t* stage_v, int total_q,
                            hipStream_t stream);
 
 // Both of the above in one launch; only valid when no new row lands on a ring
 // slot that the flush still reads.
-hipError_t launch_flush_place(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
+hipError_t launch_flush_place(const CacheArgs& c, const QuantArgs& clip, const SeqArgs& s,
                               const uint16_t* stage_k, const uint16_t* stage_v, int total_q,
                               int max_new, hipStream_t stream);
 
@@ -79,7 +85,7 @@ hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* st
 // One-token append in one launch (rotate, flush, place): every sequence
 // appends exactly one token, none is flushed in the same call and no new row
 // lands on a ring slot the flush reads.  jobs: keys, values, queries (opt.).
-hipError_t launch_append_one(const CacheArgs& c, const ClipArgs& clip, const SeqArgs& s,
+hipError_t launch_append_one(const CacheArgs& c, const QuantArgs& clip, const SeqArgs& s,
                              const RotateJobs& jobs, int total_q, const uint16_t* stage_k,
                              const uint16_t* stage_v, hipStream_t stream);
 
