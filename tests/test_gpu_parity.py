@@ -275,3 +275,26 @@ def test_large_grid_device_item_lookup():
         err, rel, ok = compare_attention(out[i, :w.g], want)
         assert ok, (i, err, rel)
     print("[case] large grid ok", flush=True)
+
+
+def test_append_many_sequences_device_lookup():
+    """600 sequences per append call: beyond the host's per-sequence table in
+    the kernel arguments (512), so the quantizer finds each position's
+    sequence with its own prefix sum over the device arrays (chunked appends
+    with flushes, then a one-token step); sampled rows bit-exact, decode
+    within the attention bar."""
+    from ultra_bit_kv_amd import SeqBatch
+    n = 600
+    lens = [30 + (7 * i) % 43 for i in range(n)]
+    w = get("c1_tiny").scaled(n_seqs=n, hq=2, hkv=1, s_sink=4, s_keep=8, s_flush=8, group=32,
+                              lengths=("list", tuple(lens)))
+    print(f"[case] {n} sequences, lens {min(lens)}..{max(lens)}", flush=True)
+    cache = make_cache(w, lens)
+    q_rot = fill(cache, w, lens, chunk=16)
+    r_k, r_v = cache.host_r
+    out = cache.decode(SeqBatch(range(n), lens), q_rot).cpu().numpy()
+    for i in list(range(0, n, 37)) + [n - 1]:
+        hc = oracle_head(w, i, 0, lens[i], r_k, r_v)
+        _check_head(cache, w, i, 0, lens[i], hc)
+        err, rel, ok = compare_attention(out[i, :w.g], oracle_decode(w, i, 0, lens[i], r_k, r_v, hc))
+        assert ok, (i, err, rel)

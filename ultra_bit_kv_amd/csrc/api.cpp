@@ -355,11 +355,11 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
     clip.qn = n_seqs;
     int64_t run = 0;
     for (int i = 0; i < n_seqs; ++i) {
-      clip.q_before[i] = (int32_t)run;
       const int64_t lb = len_before_host[i];
+      clip.q[i] = QuantSeq{(int32_t)run, seq_slots_host[i], (int32_t)lb, cu_new_host[i]};
       run += s_quant(lb + (int64_t)cu_new_host[i + 1] - cu_new_host[i], c) - s_quant(lb, c);
     }
-    clip.q_before[n_seqs] = (int32_t)run;
+    clip.q[n_seqs] = QuantSeq{(int32_t)run, -1, 0, cu_new_host[n_seqs]};
   }
   SeqArgs sa{seq_slots, len_before, cu_new, n_seqs};
   uint8_t* ws = (uint8_t*)workspace;

@@ -119,17 +119,20 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const QuantArg
     return s_quant_of(lb + nn, c.s_sink, c.s_keep, c.s_flush) -
            s_quant_of(lb, c.s_sink, c.s_keep, c.s_flush);
   };
-  int i, before;
+  int i, before, slot, lb, cu0;
   if (clip.qn > 0) {   // the host's table: the last sequence starting at or before the item
-    if (item >= clip.q_before[clip.qn]) return;
+    if (item >= clip.q[clip.qn].before) return;
     int lo = 0, hi = clip.qn - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (clip.q_before[mid] <= item) lo = mid;
+      if (clip.q[mid].before <= item) lo = mid;
       else hi = mid - 1;
     }
     i = lo;
-    before = clip.q_before[lo];
+    before = clip.q[lo].before;
+    slot = clip.q[lo].slot;
+    lb = clip.q[lo].len_before;
+    cu0 = clip.q[lo].cu_new;
   } else {
     const int n = s.n_seqs, per = (n + 63) / 64;
     const int k0 = min(lane * per, n), k1 = min(k0 + per, n);
@@ -155,9 +158,10 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const QuantArg
     const int src = __ffsll(hits) - 1;
     i = __shfl(seq, src);
     before = __shfl(off, src);
+    slot = s.slots[i];
+    lb = s.lens[i];
+    cu0 = s.cu_new[i];
   }
-  const int slot = s.slots[i];
-  const int lb = s.lens[i];
   const int sqb = s_quant_of(lb, c.s_sink, c.s_keep, c.s_flush);
   const int p = sqb + (item - before);
   const int m = (p - c.s_sink) / kPage, t = (p - c.s_sink) % kPage;
@@ -178,7 +182,7 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const QuantArg
              ((uint32_t)vb[v_window_index(tt, 2 * lane + 1)] << 16);
     }
   } else {
-    const size_t tok = (size_t)s.cu_new[i] + (p - lb);
+    const size_t tok = (size_t)cu0 + (p - lb);
     const uint16_t* src = (w == 0 ? stage_k : stage_v) + (tok * c.hkv + h) * kD;
     pair = *(const uint32_t*)(src + 2 * lane);
   }

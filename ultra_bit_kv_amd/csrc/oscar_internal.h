@@ -28,15 +28,18 @@ struct CacheArgs {
   int rot;                       // 0: dense r_k / r_v; 1: H / sqrt(128); 2: H P_br / sqrt(128)
 };
 
-// Clip ratios, and the host's table of where each sequence's quantized
-// positions start among the call's (n = 0: the kernels find them from the
-// device arrays).
-constexpr int kMaxQuantSeqs = 1024;
+// Clip ratios, and the host's per-sequence table: where each sequence's
+// quantized positions start among the call's, its cache row, length before
+// the call and first new token (qn = 0: the kernels read the device arrays).
+constexpr int kMaxQuantSeqs = 512;
+struct QuantSeq {
+  int32_t before, slot, len_before, cu_new;
+};
 struct QuantArgs {
   float k[kMaxKvHeads];
   float v[kMaxKvHeads];
   int qn;
-  int32_t q_before[kMaxQuantSeqs + 1];
+  QuantSeq q[kMaxQuantSeqs + 1];   // q[qn].before = the call's quantized positions
 };
 
 // Per-call sequence metadata (device arrays provided by the caller).
