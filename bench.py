@@ -334,9 +334,10 @@ def populate(cache, w, lens, chunk=8192, max_tokens=1 << 18):
             done[i] += m
 
 
-def measure(w, n_layers, steps, warmup, gpu_hold_cycles=0):
+def measure(w, n_layers, steps, warmup, gpu_hold_cycles=0, rotation=0):
     """Time `steps` decode steps of every row of workload w (after `warmup`),
-    cycling through n_layers copies of the populated cache."""
+    cycling through n_layers copies of the populated cache (``rotation``: the
+    cache's rotation kind)."""
     import torch
     from ultra_bit_kv_amd import SeqBatch, as_bf16
 
@@ -350,11 +351,11 @@ def measure(w, n_layers, steps, warmup, gpu_hold_cycles=0):
     # layer 0 is populated through the library's own append path with L0 - 1
     # tokens; the other layers are copies.  Layer step k appends position
     # L0 - 1 + k, so the first step of every layer decodes a context of L0.
-    base = make_layer(w, grow, n)
+    base = make_layer(w, grow, n, rotation=rotation)
     populate(base, w, [int(L) - 1 for L in lens0])
     layers = [base]
     for _ in range(1, n_layers):
-        c = make_layer(w, grow, n)
+        c = make_layer(w, grow, n, rotation=rotation)
         c.pages.copy_(base.pages)
         c.win.copy_(base.win)
         layers.append(c)
@@ -575,6 +576,14 @@ def main():
                         "windows 64/256/256",
             "dense": measure_append(w5, ns5, 0),
             "hadamard_bitrev": measure_append(w5, ns5, 2),
+        }
+        # the decode step of the headline workload with the structured rotation
+        # (the merge generates R^T instead of reading R_V)
+        hs = measure(w, args.layers, max(20, args.steps // 4), args.warmup, hold, rotation=2)
+        res["append_rotation_modes"]["decode_step_hadamard_bitrev"] = {
+            "workload": w.name, "steps": max(20, args.steps // 4), "ms_per_step": hs["ms_step"],
+            "decode_split_ms": hs["split_ms"], "decode_merge_ms": hs["merge_ms"],
+            "append_ms": hs["ms_step_ev"] - hs["dec_ms"],
         }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, lens0, seconds=args.cpu_seconds)

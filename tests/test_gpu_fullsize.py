@@ -42,12 +42,14 @@ def test_fullsize_long_context(name, samples):
     _check_decode(w, cache, q_rot, lens, samples)
 
 
-def test_fullsize_bs64():
-    """The benchmark's workload and launch plan: 64 sequences, U[4096, 8192]."""
+@pytest.mark.parametrize("rotation", [0, 2])
+def test_fullsize_bs64(rotation):
+    """The benchmark's workload and launch plan: 64 sequences, U[4096, 8192];
+    with the dense per-head rotation and the structured H P_br / sqrt(128)."""
     w = get("c3_bs64")
     lens = [int(x) for x in w.lengths_after()]
-    _case(f"c3_bs64 full size, {len(lens)} sequences")
-    cache = make_cache(w, lens, max_seqs=len(lens))
+    _case(f"c3_bs64 full size, {len(lens)} sequences, rotation {rotation}")
+    cache = make_cache(w, lens, max_seqs=len(lens), rotation=rotation)
     q_rot = fill(cache, w, lens, chunk=8192)
     rng = np.random.default_rng(11)
     seqs = [int(np.argmax(lens)), int(np.argmin(lens))] + list(rng.choice(len(lens), 2, replace=False))
