@@ -26,6 +26,8 @@ Arithmetic is fp64 unless a step names a rounding.  Modules:
 * ``attention`` -- O5: decode attention over the decoded cache, split + merge.
 * ``cache``     -- builds the whole decoded cache state of a sequence.
 * ``prefill``   -- O6: causal attention of a new chunk over the mixed cache.
+* ``ots``       -- O7: the OScaR variant (per-token key scale, per-channel INT2
+  keys over blocks of G tokens); not yet on the GPU path.
 """
 
-from . import rounding, rotate, placement, quant, layout, attention, cache, prefill  # noqa: F401
+from . import rounding, rotate, placement, quant, layout, attention, cache, prefill, ots  # noqa: F401

@@ -1,0 +1,103 @@
+"""O7 (the OScaR variant): Hadamard-rotated keys scaled to unit norm per token
+(Omni-Token Scaling) and quantized per channel over blocks of G tokens.
+
+Test infrastructure (see ``oracle/__init__.py``).  Not yet on the GPU path:
+this module fixes what the variant computes.
+
+Sources:
+* OScaR notes, background "KIVI and the per-channel paradigm": keys are
+  quantized per channel in blocks of G tokens, values per token; for channel j
+  and block g, Delta = (max - min) / (2^b - 1), z = -min / Delta,
+  Q = clamp(round(K / Delta + z), 0, 2^b - 1), K^ = Delta (Q - z); the newest
+  R = 128 tokens stay in a BF16 residual buffer that is quantized when full.
+* OScaR notes, step one "Canalized Rotation" (k~ = H k, normalized H) and step
+  two "Omni-Token Scaling": s_t = ||H k_t||_2, the quantized row is
+  H k_t / s_t, s_t is stored beside the codes as one BF16 scalar per token,
+  and k^ = s_t Delta_{j,g} (Q - z_{j,g}); the storage analysis puts a key
+  token-head at 32 B of codes + 2 B of scale.
+* OScaR notes, the algorithm listing (normalized keys enter the BF16
+  residual buffer; a full buffer is quantized per channel) and the cache
+  layout figure (codes, Delta and z in BF16, s per token in BF16).
+
+Readings (the notes leave these open):
+1. Rounding: k~ is the bf16 rounding of x . H / sqrt(d) (``rotate.Hadamard``);
+   s16 = bf16(||k~||_2) from the fp64 norm of the bf16 row; the buffered row is
+   u16 = bf16(k~ / s16).  Blocks are quantized from u16.
+2. Delta16 = bf16((max - min) / 3) and z16 = bf16(-min / Delta16) (for
+   Delta16 = 0 see 4); codes come
+   from the stored Delta16, z16: Q = clamp(rne(u / Delta16 + z16), 0, 3), taken
+   exactly as [v > 1/2] + [v >= 3/2] + [v > 5/2] with v = u / Delta16 + z16.
+3. Parameter count: one (Delta, z) per channel per block of G tokens; the
+   layout figure's "(S/G) x (d/G)" is read as a garble of (S/G) x d.
+4. A constant channel (max = min) has Delta16 = 0; it decodes to min, kept as
+   z16 = bf16(min) with Delta16 = 0 (K^ = z16 when Delta16 = 0).
+5. Dequantized key: k^ = s16 * Delta16 * (Q - z16) in fp64.
+"""
+
+import numpy as np
+
+from . import rotate
+from .rounding import f64_to_bf16_bits, bf16_bits_to_f64
+
+
+def ots_scale(k_rot_bits):
+    """(s16, u16) bits for bf16 rotated key rows [N, d]: s16 = bf16(||k~||_2),
+    u16 = bf16(k~ / s16)."""
+    k = bf16_bits_to_f64(np.asarray(k_rot_bits, np.uint16))
+    s16 = f64_to_bf16_bits(np.sqrt((k * k).sum(axis=1)))
+    s = bf16_bits_to_f64(s16)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        u = np.where(s[:, None] > 0, k / np.where(s > 0, s, 1.0)[:, None], 0.0)
+    return s16, f64_to_bf16_bits(u)
+
+
+def channel_quantize(u_bits):
+    """Per-channel INT2 of one block of G tokens, u16 rows [G, d]:
+    (codes uint8 [G, d], delta16 [d], z16 [d]) as bf16 bits."""
+    u = bf16_bits_to_f64(np.asarray(u_bits, np.uint16))
+    mn, mx = u.min(axis=0), u.max(axis=0)
+    d16 = f64_to_bf16_bits((mx - mn) / 3.0)
+    dl = bf16_bits_to_f64(d16)
+    const = dl == 0
+    with np.errstate(invalid="ignore", divide="ignore"):
+        z16 = np.where(const, f64_to_bf16_bits(mn), f64_to_bf16_bits(-mn / np.where(const, 1.0, dl)))
+    z = bf16_bits_to_f64(z16)
+    # v > t  <=>  u > Delta (t - z): Delta (8-bit) times t - z (exact in fp64)
+    # is exact, so each threshold comparison is exact
+    codes = np.zeros(u.shape, np.uint8)
+    for t, strict in ((0.5, True), (1.5, False), (2.5, True)):
+        thr = dl * (t - z)
+        hit = u > thr if strict else u >= thr
+        codes += np.where(const[None, :], False, hit).astype(np.uint8)
+    return codes, d16, z16
+
+
+def channel_dequant(codes, d16, z16):
+    """Normalized rows u^ [G, d] of a block (before the per-token scale)."""
+    dl = bf16_bits_to_f64(d16)
+    z = bf16_bits_to_f64(z16)
+    q = np.asarray(codes, np.float64)
+    return np.where(dl[None, :] == 0, z[None, :], dl[None, :] * (q - z[None, :]))
+
+
+def ots_keys(k_bits, group, bitrev=False):
+    """Decoded keys [N, d] (rotated basis) of N post-RoPE bf16 key rows of one
+    head, N a multiple of ``group``: rotate, scale, quantize each block of
+    ``group`` consecutive tokens per channel, dequantize, rescale."""
+    k_bits = np.asarray(k_bits, np.uint16)
+    n = k_bits.shape[0]
+    assert n % group == 0
+    k_rot = rotate.hadamard_rotate_to_bf16(k_bits, bitrev)
+    s16, u16 = ots_scale(k_rot)
+    s = bf16_bits_to_f64(s16)
+    out = np.empty(k_bits.shape, np.float64)
+    for b in range(0, n, group):
+        c, d16, z16 = channel_quantize(u16[b:b + group])
+        out[b:b + group] = s[b:b + group, None] * channel_dequant(c, d16, z16)
+    return out
+
+
+def key_bytes_per_token_head(d=128, bits=2):
+    """Bytes of one key token-head in the OTS layout besides the per-block
+    parameters: packed codes plus the BF16 scale."""
+    return d * bits // 8 + 2
