@@ -194,8 +194,9 @@ size_t oscar_workspace_size(const oscar_kv_config* cfg, int32_t n_seqs, int64_t 
  *  len_before[i]  tokens already in that row
  *  cu_new[i]      prefix sums of new-token counts, cu_new[0] = 0,
  *                 new tokens of sequence i are rows cu_new[i] .. cu_new[i+1]-1
- *  (_host arrays are read on the host for checks and launch sizes; the
- *  device arrays must hold the same values)
+ *  (_host arrays are read on the host for checks, launch sizes and the
+ *  per-sequence table passed in the kernel arguments of calls with at most
+ *  512 sequences; the device arrays must hold the same values)
  *  k, v           bf16 [cu_new[n]][Hkv][128] post-RoPE keys / values
  *  q              bf16 [cu_new[n]][Hq][128] post-RoPE queries, or NULL
  *  q_rot          bf16 [cu_new[n]][Hq][128] out: q . R_K (q . r_q when the cache
