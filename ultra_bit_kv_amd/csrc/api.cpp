@@ -322,7 +322,7 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
   const int64_t max_len = oscar_max_seq_len(&c);
   std::vector<char> seen(c.max_seqs, 0);
   int64_t total_q = 0;
-  int max_new = 0;
+  int max_keep = 0;   // most new rows of one sequence that stay in BF16
   for (int i = 0; i < n_seqs; ++i) {
     const int slot = seq_slots_host[i];
     if (slot < 0 || slot >= c.max_seqs) return OSCAR_ERR_CAPACITY;
@@ -335,7 +335,10 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
     if (int2_pages(lb + n_new, c) > c.max_pages_per_seq) return OSCAR_ERR_CAPACITY;
     if (int2_pages(lb + n_new, c) > 0 && c.num_pages < 1) return OSCAR_ERR_CAPACITY;
     total_q += s_quant(lb + n_new, c) - s_quant(lb, c);
-    max_new = std::max<int>(max_new, (int)n_new);
+    // new rows that stay in BF16: the sink part and the part from S_quant on
+    const int64_t in_sink = std::max<int64_t>(0, std::min<int64_t>(lb + n_new, c.s_sink) - lb);
+    const int64_t in_ring = std::max<int64_t>(0, lb + n_new - std::max(lb, s_quant(lb + n_new, c)));
+    max_keep = std::max<int>(max_keep, (int)(in_sink + in_ring));
   }
   const int64_t n_tok = cu_new_host[n_seqs];
   if (n_tok > (int64_t)1 << 30 || total_q > (int64_t)1 << 30) return OSCAR_ERR_ARG;
@@ -405,12 +408,12 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
     if (n_new > 0 && (lb + n_new - 1) - s_quant(lb, c) >= a.ring_cap) disjoint = false;
   }
   if (disjoint)
-    return hip_status(launch_flush_place(a, clip, sa, stage_k, stage_v, (int)total_q, max_new, sm));
+    return hip_status(launch_flush_place(a, clip, sa, stage_k, stage_v, (int)total_q, max_keep, sm));
   // 2. quantize every position that crosses S_quant (reads the ring first)
   if ((st = hip_status(launch_quantize(a, clip, sa, stage_k, stage_v, (int)total_q, sm))) != OSCAR_OK)
     return st;
   // 3. new rows that stay BF16 go to the sink / ring
-  return hip_status(launch_place(a, sa, stage_k, stage_v, max_new, sm));
+  return hip_status(launch_place(a, sa, stage_k, stage_v, max_keep, sm));
 }
 
 }  // extern "C"

@@ -265,7 +265,9 @@ hipError_t launch_quantize(const CacheArgs& c, const QuantArgs& clip, const SeqA
   return hipGetLastError();
 }
 
-// New rows that stay in BF16: sink positions and positions at or beyond S_quant.
+// New rows that stay in BF16: sink positions and positions at or beyond S_quant
+// (work-group x = ti enumerates them; the host sizes the grid by the largest
+// such count of the call).
 __device__ __forceinline__ void place_item(const CacheArgs& c, const SeqArgs& s,
                                            const uint16_t* __restrict__ stage_k,
                                            const uint16_t* __restrict__ stage_v, int ti, int h,
@@ -274,9 +276,13 @@ __device__ __forceinline__ void place_item(const CacheArgs& c, const SeqArgs& s,
   const int slot = s.slots[i];
   const int lb = s.lens[i];
   const int n_new = s.cu_new[i + 1] - s.cu_new[i];
-  if (slot < 0 || slot >= c.max_seqs || lb < 0 || ti >= n_new) return;
-  const int p = lb + ti;
+  if (slot < 0 || slot >= c.max_seqs || lb < 0 || n_new <= 0) return;
   const int sqa = s_quant_of(lb + n_new, c.s_sink, c.s_keep, c.s_flush);
+  // ti enumerates the new rows that stay in BF16: the sink part first, then
+  // the rows from S_quant on
+  const int in_sink = max(0, min(lb + n_new, c.s_sink) - lb);
+  const int p = ti < in_sink ? lb + ti : max(lb, sqa) + (ti - in_sink);
+  if (p >= lb + n_new) return;
   int blk, tt;
   if (p < c.s_sink) {
     blk = p / kPage;
@@ -289,7 +295,7 @@ __device__ __forceinline__ void place_item(const CacheArgs& c, const SeqArgs& s,
     return;  // quantized straight into the pages
   }
   uint16_t* wb = c.win + (((size_t)slot * c.hkv + h) * c.win_blocks + blk) * (2 * kPage * kD);
-  const size_t tok = (size_t)s.cu_new[i] + ti;
+  const size_t tok = (size_t)s.cu_new[i] + (p - lb);
   const size_t src = (tok * c.hkv + h) * kD + ch;
   wb[tt * kD + ch] = stage_k[src];
   wb[kPage * kD + v_window_index(tt, ch)] = stage_v[src];
