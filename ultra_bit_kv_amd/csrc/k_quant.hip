@@ -301,10 +301,14 @@ __device__ __forceinline__ void place_item(const CacheArgs& c, const SeqArgs& s,
   wb[kPage * kD + v_window_index(tt, ch)] = stage_v[src];
 }
 
+constexpr int kPlaceRows = 4;   // rows per work-group of place_kernel
+
 __global__ __launch_bounds__(128) void place_kernel(CacheArgs c, SeqArgs s,
                                                     const uint16_t* __restrict__ stage_k,
                                                     const uint16_t* __restrict__ stage_v) {
-  place_item(c, s, stage_k, stage_v, blockIdx.x, blockIdx.y, blockIdx.z);
+#pragma unroll
+  for (int r = 0; r < kPlaceRows; ++r)
+    place_item(c, s, stage_k, stage_v, blockIdx.x * kPlaceRows + r, blockIdx.y, blockIdx.z);
 }
 
 // Quantize and place in one launch, for appends where no new row lands on a
@@ -337,7 +341,7 @@ hipError_t launch_flush_place(const CacheArgs& c, const QuantArgs& clip, const S
 hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* stage_k,
                         const uint16_t* stage_v, int max_new, hipStream_t stream) {
   if (max_new <= 0 || s.n_seqs <= 0) return hipSuccess;
-  dim3 grid(max_new, c.hkv, s.n_seqs);
+  dim3 grid((max_new + kPlaceRows - 1) / kPlaceRows, c.hkv, s.n_seqs);
   hipLaunchKernelGGL(place_kernel, grid, dim3(128), 0, stream, c, s, stage_k, stage_v);
   return hipGetLastError();
 }
