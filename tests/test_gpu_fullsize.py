@@ -29,15 +29,16 @@ def _check_decode(w, cache, q_rot, lens, samples):
         assert ok, (i, h, err, rel)
 
 
-@pytest.mark.parametrize("name,samples", [
-    ("c2_qwen3_8b_bs1", [(0, 0), (0, 5)]),
-    ("c4_long_bs1", [(0, 2)]),
+@pytest.mark.parametrize("name,samples,rotation", [
+    ("c2_qwen3_8b_bs1", [(0, 0), (0, 5)], 0),
+    ("c2_qwen3_8b_bs1", [(0, 3)], 1),        # structured H / sqrt(128): two-level merge un-rotation
+    ("c4_long_bs1", [(0, 2)], 0),
 ])
-def test_fullsize_long_context(name, samples):
+def test_fullsize_long_context(name, samples, rotation):
     w = get(name)
     lens = [int(x) for x in w.lengths_after()]
-    _case(f"{name} full size, lens {lens}")
-    cache = make_cache(w, lens)
+    _case(f"{name} full size, lens {lens}, rotation {rotation}")
+    cache = make_cache(w, lens, rotation=rotation)
     q_rot = fill(cache, w, lens, chunk=8192)
     _check_decode(w, cache, q_rot, lens, samples)
 
