@@ -89,6 +89,28 @@ __device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ src, i
 
 constexpr double kInvSqrtD = 0x1.6a09e667f3bcdp-4;   // fp64(sqrt(2)) / 16 = fp64(1 / sqrt(128))
 
+// The value of lane l ^ m (m = 1, 2, 4, 8; within a 16-lane row).  m = 1, 2
+// and 8 are DPP moves of the two halves (quad_perm [1,0,3,2], [2,3,0,1] and
+// row_ror:8, which maps lane i of a row to i + 8 mod 16 = i ^ 8); m = 4 goes
+// through the LDS crossbar.
+__device__ __forceinline__ double lane_xor(double v, int m) {
+  if (m == 4) return __shfl_xor(v, 4, 16);
+  const int ctrl = m == 1 ? 0xB1 : (m == 2 ? 0x4E : 0x128);
+  const long long b = __double_as_longlong(v);
+  int lo = (int)(b & 0xFFFFFFFFll), hi = (int)(b >> 32);
+  if (ctrl == 0xB1) {
+    lo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, false);
+    hi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, false);
+  } else if (ctrl == 0x4E) {
+    lo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, false);
+    hi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, false);
+  } else {
+    lo = __builtin_amdgcn_mov_dpp(lo, 0x128, 0xF, 0xF, false);
+    hi = __builtin_amdgcn_mov_dpp(hi, 0x128, 0xF, 0xF, false);
+  }
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
 // Structured rotation of rows t0 .. t0 + 15 (those < n_tok) of head h of src:
 // a 16-lane group takes one row, its lane i the 8 elements 8i .. 8i+7 of the
 // (permuted) row; the butterflies over index bits 0-2 stay in the lane, those
@@ -127,7 +149,7 @@ __device__ __forceinline__ void fwht_block(const uint16_t* __restrict__ src, int
       // times +-1 plus the partner's, one exact-product fma
       const double sg = (li & m) ? -1.0 : 1.0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = __builtin_fma(x[e], sg, __shfl_xor(x[e], m, 16));
+      for (int e = 0; e < 8; ++e) x[e] = __builtin_fma(x[e], sg, lane_xor(x[e], m));
     }
     uint16_t bits[8];
 #pragma unroll
