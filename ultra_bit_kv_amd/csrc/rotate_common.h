@@ -89,15 +89,26 @@ __device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ src, i
 
 constexpr double kInvSqrtD = 0x1.6a09e667f3bcdp-4;   // fp64(sqrt(2)) / 16 = fp64(1 / sqrt(128))
 
-// The value of lane l ^ m (m = 1, 2, 4, 8; within a 16-lane row).  m = 1, 2
-// and 8 are DPP moves of the two halves (quad_perm [1,0,3,2], [2,3,0,1] and
-// row_ror:8, which maps lane i of a row to i + 8 mod 16 = i ^ 8); m = 4 goes
-// through the LDS crossbar.
+// The value of lane l ^ m (m = 1, 2, 4, 8; within a 16-lane row), as DPP
+// moves of the two halves: quad_perm [1,0,3,2] and [2,3,0,1] for m = 1, 2;
+// row_ror:8 for m = 8 (row_ror:n gives lane i of a row the value of lane
+// i - n mod 16; i - 8 mod 16 = i ^ 8); for m = 4, row_ror:12 (lane i + 4,
+// which is i ^ 4 when bit 2 of i is clear) or row_ror:4 (lane i - 4, i ^ 4
+// when it is set).
 __device__ __forceinline__ double lane_xor(double v, int m) {
-  if (m == 4) return __shfl_xor(v, 4, 16);
-  const int ctrl = m == 1 ? 0xB1 : (m == 2 ? 0x4E : 0x128);
   const long long b = __double_as_longlong(v);
   int lo = (int)(b & 0xFFFFFFFFll), hi = (int)(b >> 32);
+  if (m == 4) {
+    const int lo_up = __builtin_amdgcn_mov_dpp(lo, 0x12C, 0xF, 0xF, false);   // lane i + 4
+    const int hi_up = __builtin_amdgcn_mov_dpp(hi, 0x12C, 0xF, 0xF, false);
+    const int lo_dn = __builtin_amdgcn_mov_dpp(lo, 0x124, 0xF, 0xF, false);   // lane i - 4
+    const int hi_dn = __builtin_amdgcn_mov_dpp(hi, 0x124, 0xF, 0xF, false);
+    const bool set = (threadIdx.x & 4) != 0;
+    lo = set ? lo_dn : lo_up;
+    hi = set ? hi_dn : hi_up;
+    return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+  }
+  const int ctrl = m == 1 ? 0xB1 : (m == 2 ? 0x4E : 0x128);
   if (ctrl == 0xB1) {
     lo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, false);
     hi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, false);
