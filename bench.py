@@ -1,23 +1,34 @@
 """Benchmark: INT2 paged decode attention (OSCAR-style cache) on one MI355X.
 
-Workload (default): bs64 decode, 32 query / 8 KV heads, head_dim 128, context
+Headline (default): bs64 decode, 32 query / 8 KV heads, head_dim 128, context
 lengths U[4096, 8192] per sequence, G = 64, windows 64 / 256 (flush 16),
 clip 0.96 / 0.92, shuffled pages.  One step = one decode step of every
 sequence through the whole hot path: oscar_rotate_quant_append with one new
 token per sequence (rotate q/k/v, flush + quantize, window placement) and then
-oscar_int2_decode_attn over the whole cache.  The step cycles through
-``--layers`` independent layer caches (copies of the same populated cache), so
-each step reads a cache that is not resident in the 256 MB MALL, as in a
-multi-layer model.
+the decode (oscar_int2_decode_partials + oscar_int2_decode_merge) over the
+whole cache.  The step cycles through ``--layers`` independent layer caches
+(copies of the same populated cache), so each step reads a cache that is not
+resident in the 256 MB MALL, as in a multi-layer model.
 
-Prints one JSON line.  `value` = sequences decoded per second (tokens/s),
-from timed steps with events only at the ends of the run (an event record
-between launches adds a gap to the stream).  `roofline` is for the decode
-split kernel (all cache traffic): algorithmic bytes per launch (INT2
-token-heads x (64 + 1024/G) B + BF16 window token-heads x 512 B +
-block-table entries x 4 B + q' in) over its average duration, measured with
-HIP events around each split launch, on the stream it runs on, in a second
-timed pass of the same number of steps.
+Prints one JSON line.  `value` = sequences decoded per second (tokens/s) from
+exactly --steps steps after --warmup warm-up steps, timed with events only
+at the ends of the run (an event record between launches adds a gap to the
+stream) and queued behind a spin kernel long enough to cover the host's
+queueing.  `roofline` is for the decode split kernel (all cache traffic):
+algorithmic bytes per launch (INT2 token-heads x (64 + 1024/G) B + BF16
+window token-heads x 512 B + block-table entries x 4 B + q' in) over its
+average duration, measured with HIP events around each split launch, on the
+stream it runs on, in a second timed pass of the same number of steps.
+
+Legs reported beside the headline (--legs): bs1 (Qwen3-8B shape, 32K
+context; eager and replayed from a HIP graph), c1 (tiny, MALL-resident), c4
+(128K context), c5 (the Qwen3-32B serving step: one append carrying 256
+decode tokens and 16 fresh 2048-token chunks, then the decode of the 256
+sequences, timed together), probe (a plain HBM read kernel: the measured
+read ceiling), bf16 (the BF16 paged decode on the same shapes), prefill
+(chunked-prefill attention), rotation (dense vs structured rotation in the
+append).  Each leg times at least --leg-steps steps; every layer copy gets an
+untimed step first.
 """
 
 import argparse
@@ -74,7 +85,8 @@ def bf16_bytes(w, lens):
 
 def measure_bf16(w, n_layers, steps, hold):
     """Time `steps` BF16 paged decode calls over the lengths of workload w,
-    cycling through n_layers caches of seeded random bf16 pages."""
+    cycling through n_layers caches of seeded random bf16 pages (hold: cycles
+    of the spin kernel queued ahead of the timed calls)."""
     import torch
     from ultra_bit_kv_amd import BF16PagedCache, SeqBatch
 
@@ -334,16 +346,59 @@ def populate(cache, w, lens, chunk=8192, max_tokens=1 << 18):
             done[i] += m
 
 
-def measure(w, n_layers, steps, warmup, gpu_hold_cycles=0, rotation=0):
-    """Time `steps` decode steps of every row of workload w (after `warmup`),
-    cycling through n_layers copies of the populated cache (``rotation``: the
-    cache's rotation kind)."""
+CLOCK_HZ = 2.4e9   # shader clock the spin kernel counts (MI355X peak engine clock)
+
+
+def pct(xs):
+    """Median, p10 and p90 of a list of durations."""
+    a = np.asarray(xs, np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90))}
+
+
+def hold_for(host_s):
+    """Spin-kernel length (cycles) that covers `host_s` seconds of host-side
+    queueing three times over (at least 5 ms)."""
+    return int(max(3.0 * host_s, 5e-3) * CLOCK_HZ)
+
+
+def timed_region(enqueue, n, hold_cycles):
+    """GPU time of `n` calls of enqueue(j) queued behind a spin kernel, so the
+    events time the GPU's execution of the queue, not the host's submission.
+    Returns (ms per call, host seconds spent queueing)."""
+    import torch
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(hold_cycles))
+    t_start.record()
+    h0 = time.perf_counter()
+    for j in range(n):
+        enqueue(j)
+    host = time.perf_counter() - h0
+    t_end.record()
+    torch.cuda.synchronize()
+    return t_start.elapsed_time(t_end) / n, host
+
+
+def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0):
+    """Decode steps of every row of workload w, cycling through n_layers
+    copies of the populated cache (``rotation``: the cache's rotation kind).
+
+    Every layer copy gets at least one untimed step before timing (the first
+    call on a cache pays one-off host and device costs).  Pass 1 times
+    exactly `steps` steps with events only at its ends (``ms_step``); pass 2
+    the same number with events around the append, split and merge launches
+    of each step.  With graph_steps > 0 a further `graph_steps` steps are
+    captured into one HIP graph and replayed `graph_reps` times (timed as a
+    whole), which removes the host's launch path from the figure."""
     import torch
     from ultra_bit_kv_amd import SeqBatch, as_bf16
 
-    lens0 = w.lengths_after()                 # context of the first timed step, per layer
+    lens0 = w.lengths_after()                 # context of the first step, per layer
     n = len(lens0)
-    total_steps = warmup + 2 * steps
+    warm = max(warmup, n_layers)
+    total_steps = warm + 2 * steps + graph_steps
     per_layer = -(-total_steps // n_layers)
     grow = [int(L) + per_layer for L in lens0]
     t_setup = time.perf_counter()
@@ -387,55 +442,221 @@ def measure(w, n_layers, steps, warmup, gpu_hold_cycles=0, rotation=0):
     def step(s, ev=None):
         c = layers[s % n_layers]
         d = steps_in[s // n_layers]
+        if ev is not None:
+            ev[0].record()
         c.append(d["app"], d["k"], d["v"], d["q"], q_rot=q_rot)
         # the decode step as its two launches, timed apart when events are
         # given: the split kernel (all cache traffic) and the log-sum-exp
         # merge / un-rotation
         if ev is not None:
-            ev[0].record()
+            ev[1].record()
         c.decode_partials(d["dec"], q_rot)
         if ev is not None:
-            ev[1].record()
+            ev[2].record()
         c.decode_merge(d["dec"], out)
         if ev is not None:
-            ev[2].record()
+            ev[3].record()
 
-    def timed(first, evs=None):
-        """Time `steps` steps from step index `first` (events only at the ends
-        unless per-step events are given)."""
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        # A spin kernel ahead of the timed steps keeps the GPU busy while the
-        # host queues them, so the events time the GPU's execution of the
-        # queued steps rather than the host's submission rate.
-        torch.cuda._sleep(int(gpu_hold_cycles))
-        t_start.record()
-        for j in range(steps):
-            step(first + j, evs[j] if evs is not None else None)
-        t_end.record()
-        torch.cuda.synchronize()
-        return t_start.elapsed_time(t_end) / steps
-
-    for s in range(warmup):
+    for s in range(warm):
         step(s)
     torch.cuda.synchronize()
+    # host queueing time of a step, measured on the warm-up path
+    h0 = time.perf_counter()
+    step(warm - 1)
+    host_step = time.perf_counter() - h0
+    torch.cuda.synchronize()
+    hold = hold_for(host_step * steps * 4)   # pass 2 also records 4 events per step
     # pass 1: the whole step, no event records between its launches (each
-    # record adds a gap to the stream); pass 2: the same number of steps with
-    # events around the split and merge launches, for the per-kernel times
-    ms_step = timed(warmup)
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
-    ms_step_ev = timed(warmup + steps, evs)
-    dec_ms = float(np.mean([a.elapsed_time(c) for a, b, c in evs]))
-    split_ms = float(np.mean([a.elapsed_time(b) for a, b, c in evs]))
-    merge_ms = float(np.mean([b.elapsed_time(c) for a, b, c in evs]))
+    # record adds a gap to the stream)
+    ms_step, host1 = timed_region(lambda j: step(warm + j), steps, hold)
+    # pass 2: the same number of steps with events around each launch
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
+    ms_step_ev, host2 = timed_region(lambda j: step(warm + steps + j, evs[j]), steps, hold)
+    app = [a.elapsed_time(b) for a, b, c, d in evs]
+    split = [b.elapsed_time(c) for a, b, c, d in evs]
+    merge = [c.elapsed_time(d) for a, b, c, d in evs]
+    dec = [b.elapsed_time(d) for a, b, c, d in evs]
+    whole = [a.elapsed_time(d) for a, b, c, d in evs]
     # algorithmic bytes of the average split launch (lengths grow during the run)
-    byts = [algorithmic_bytes(w, [int(L) + (warmup + steps + j) // n_layers for L in lens0])
+    byts = [algorithmic_bytes(w, [int(L) + (warm + steps + j) // n_layers for L in lens0])
             for j in range(steps)]
-    bytes_per_launch = float(np.mean(byts))
-    return {"w": w, "lens0": lens0, "n": n, "ms_step": ms_step, "ms_step_ev": ms_step_ev,
-            "dec_ms": dec_ms, "split_ms": split_ms, "merge_ms": merge_ms,
-            "bytes": bytes_per_launch, "setup_s": setup_s}
+    res = {"w": w, "lens0": lens0, "n": n, "ms_step": ms_step, "ms_step_ev": ms_step_ev,
+           "dec_ms": float(np.mean(dec)), "split_ms": float(np.mean(split)),
+           "merge_ms": float(np.mean(merge)), "append_ms": float(np.mean(app)),
+           "split_pct": pct(split), "step_pct": pct(whole),
+           "bytes": float(np.mean(byts)), "setup_s": setup_s, "warm": warm,
+           "host_ms_per_step": 1e3 * host1 / steps, "hold_ms": 1e3 * hold / CLOCK_HZ,
+           # pass 1 waited on the host if the host took longer to queue the
+           # steps than the spin kernel held the GPU
+           "host_bound": host1 > hold / CLOCK_HZ}
+    if graph_steps:
+        g0 = warm + 2 * steps
+        for j in range(graph_steps):      # the captured steps run once eagerly first
+            step(g0 + j)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(graph_steps):
+                step(g0 + j)
+        g.replay()                        # replays re-run the same steps: same work
+        torch.cuda.synchronize()
+        ms_rep, _ = timed_region(lambda j: g.replay(), graph_reps, hold_for(1e-3 * graph_reps))
+        res["graph"] = {"steps_per_graph": graph_steps, "replays": graph_reps,
+                        "ms_per_step": ms_rep / graph_steps}
+        del g
+    return res
+
+
+def leg_summary(m, peak_probe=None):
+    """The per-leg record of a measure() result."""
+    w = m["w"]
+    gbs = m["bytes"] / (m["split_ms"] * 1e-3) / 1e9
+    out = {
+        "workload": f"{w.name}: {w.description}",
+        "batch": m["n"], "context_min": int(m["lens0"].min()), "context_max": int(m["lens0"].max()),
+        "warmup_steps": m["warm"],
+        "ms_per_step": m["ms_step"], "tokens_per_s": m["n"] / (m["ms_step"] * 1e-3),
+        "step_ms_events": m["step_pct"],
+        "decode_ms": m["dec_ms"], "decode_split_ms": m["split_ms"],
+        "decode_split_ms_pct": m["split_pct"], "decode_merge_ms": m["merge_ms"],
+        "append_ms": m["append_ms"], "ms_per_step_with_kernel_events": m["ms_step_ev"],
+        "algorithmic_bytes_per_launch": m["bytes"],
+        "split_GBs": gbs, "split_frac_of_peak": gbs / PEAK_HBM_GBS,
+        "decode_call_GBs": m["bytes"] / (m["dec_ms"] * 1e-3) / 1e9,
+        "host_ms_per_step": m["host_ms_per_step"], "gpu_hold_ms": m["hold_ms"],
+        "host_bound": m["host_bound"],
+    }
+    if peak_probe:
+        out["split_frac_of_read_probe"] = gbs / peak_probe
+    if "graph" in m:
+        g = m["graph"]
+        out["graph"] = dict(g, tokens_per_s=m["n"] / (g["ms_per_step"] * 1e-3))
+    return out
+
+
+def measure_probe(nbytes=1 << 30, reps=20, chunk_bytes=10240, chunk_total=325 << 20):
+    """The read probe (oscar_read_probe): a sequential sweep of `nbytes` and a
+    gather of shuffled `chunk_bytes` chunks (the size of one INT2 page of the
+    bs64 workload across its 8 KV heads) adding up to `chunk_total` bytes, the
+    bs64 decode step's traffic; median GB/s of `reps` calls each."""
+    import ctypes
+    import torch
+    from ultra_bit_kv_amd import lib
+    from ultra_bit_kv_amd._lib import check
+    L = lib()
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(7)
+    grid = 2048
+    sink = torch.empty(4 * grid, dtype=torch.int32, device="cuda")
+    n_ch = nbytes // chunk_bytes
+    pick = np.random.default_rng(77).permutation(n_ch)[:chunk_total // chunk_bytes].astype(np.int32)
+    ids = torch.from_numpy(pick).to("cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run(chunks):
+        if chunks:
+            st = L.oscar_read_probe(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                    ctypes.c_void_p(ids.data_ptr()), len(pick), chunk_bytes,
+                                    ctypes.c_void_p(sink.data_ptr()), grid, 4 * grid, stream)
+        else:
+            st = L.oscar_read_probe(ctypes.c_void_p(buf.data_ptr()), nbytes, None, 0, 0,
+                                    ctypes.c_void_p(sink.data_ptr()), grid, 4 * grid, stream)
+        check(st, "oscar_read_probe")
+
+    res = {}
+    for name, chunks, nb in (("sequential", False, nbytes), ("shuffled_chunks", True,
+                                                            len(pick) * chunk_bytes)):
+        for _ in range(3):
+            run(chunks)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(5e-3 * CLOCK_HZ))
+        for a, b in evs:
+            a.record()
+            run(chunks)
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        res[name] = {"bytes": nb, "ms": ms, "GBs": nb / (ms * 1e-3) / 1e9,
+                     "frac_of_peak": nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    res["shuffled_chunks"]["chunk_bytes"] = chunk_bytes
+    res["kernel"] = "oscar_read_probe (16-byte loads, 2048 work-groups of 256 threads)"
+    del buf
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_c5_step(w, reps):
+    """The Qwen3-32B-shaped serving step as one unit: one
+    oscar_rotate_quant_append carrying every decode sequence's new token (the
+    sequences at the longer length cross a 256-token flush) and the fresh
+    2048-token prefill chunks, then oscar_int2_decode_attn over the decode
+    sequences.  The same step is repeated (re-appending the same positions
+    rewrites the same rows: the same work each time)."""
+    import torch
+    from ultra_bit_kv_amd import SeqBatch, as_bf16
+    lens = [int(x) for x in w.lengths_after()]            # decode sequences, after the step
+    n_dec, n_pre, plen = len(lens), w.prefill_chunks, w.prefill_len
+    t0 = time.perf_counter()
+    cache = make_layer(w, lens + [plen] * n_pre, n_dec + n_pre)
+    populate(cache, w, [L - 1 for L in lens] + [0] * n_pre)
+    slots = list(range(n_dec + n_pre))
+    before = [L - 1 for L in lens] + [0] * n_pre
+    n_new = [1] * n_dec + [plen] * n_pre
+    k = as_bf16(np.concatenate([w.keys(i, b, b + m) for i, b, m in zip(slots, before, n_new)]))
+    v = as_bf16(np.concatenate([w.values(i, b, b + m) for i, b, m in zip(slots, before, n_new)]))
+    q = as_bf16(np.concatenate([w.queries(i, b, b + m) for i, b, m in zip(slots, before, n_new)]))
+    q_rot = torch.empty_like(q)
+    app = SeqBatch(slots, before, n_new)
+    dec = SeqBatch(list(range(n_dec)), lens)
+    out = torch.empty((n_dec, w.hq, 128), dtype=torch.float32, device="cuda")
+    cache.workspace_for(n_dec + n_pre, int(sum(n_new)))
+    qd = q_rot[:n_dec]
+    setup_s = time.perf_counter() - t0
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        cache.append(app, k, v, q, q_rot)
+        if ev is not None:
+            ev[1].record()
+        cache.decode_partials(dec, qd)
+        if ev is not None:
+            ev[2].record()
+        cache.decode_merge(dec, out)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    ms, host = timed_region(lambda j: step(), reps, hold_for(4e-3 * reps))
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(reps)]
+    timed_region(lambda j: step(evs[j]), reps, hold_for(4e-3 * reps))
+    app_ms = [a.elapsed_time(b) for a, b, c, d in evs]
+    split = [b.elapsed_time(c) for a, b, c, d in evs]
+    merge = [c.elapsed_time(d) for a, b, c, d in evs]
+    byts = algorithmic_bytes(w, lens)
+    gbs = byts / (float(np.mean(split)) * 1e-3) / 1e9
+    n_tok = int(sum(n_new))
+    return {
+        "workload": f"{w.name}: {w.description}",
+        "step": "one rotate_quant_append (decode tokens + prefill chunks, dense rotation) + "
+                "int2_decode_partials + int2_decode_merge",
+        "decode_seqs": n_dec, "prefill_chunks": n_pre, "prefill_len": plen,
+        "flushing_seqs": int(sum(1 for L in lens if w.lengths[0] == "mix" and L == w.lengths[3])),
+        "reps": reps, "ms_per_step": ms,
+        "decode_tokens_per_s": n_dec / (ms * 1e-3),
+        "tokens_per_s_incl_prefill": n_tok / (ms * 1e-3),
+        "append_ms": pct(app_ms), "decode_split_ms": pct(split), "decode_merge_ms": pct(merge),
+        "decode_algorithmic_bytes": byts, "decode_split_GBs": gbs,
+        "decode_split_frac_of_peak": gbs / PEAK_HBM_GBS,
+        "host_ms_per_step": 1e3 * host / reps, "setup_s": setup_s,
+    }
+
+
+LEGS = ("bs1", "c1", "c4", "c5", "probe", "bf16", "prefill", "rotation")
 
 
 def main():
@@ -445,17 +666,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--config", default="c3_bs64")
-    ap.add_argument("--bs1-config", default="c2_qwen3_8b_bs1",
-                    help="the bs1 workload reported next to the headline ('' to skip)")
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated legs reported next to the headline ('' for none): "
+                         + ", ".join(LEGS))
+    ap.add_argument("--leg-steps", type=int, default=100,
+                    help="timed steps per leg (at least --steps)")
     ap.add_argument("--bs1-layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-bf16-compare", dest="bf16_compare", action="store_false",
-                    help="skip the BF16 paged-decode comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-prefill", dest="prefill", action="store_false",
-                    help="skip the chunked-prefill attention legs")
-    ap.add_argument("--no-rotation-modes", dest="rotation_modes", action="store_false",
-                    help="skip the dense / structured rotation append comparison")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -472,8 +690,17 @@ def main():
 
     from synth import get
 
-    hold = int(args.steps * 1e-3 * 2.4e9)   # covers the host's queueing of the timed steps
-    m = measure(get(args.config), args.layers, args.steps, args.warmup, hold)
+    legs = [x for x in args.legs.split(",") if x]
+    for x in legs:
+        if x not in LEGS:
+            sys.exit(f"bench.py: unknown leg {x!r} (legs: {', '.join(LEGS)})")
+    ls = max(args.steps, args.leg_steps)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    log(f"headline {args.config}: {args.steps} steps after {args.warmup} warm-up")
+    m = measure(get(args.config), args.layers, args.steps, args.warmup)
     w, lens0, n = m["w"], m["lens0"], m["n"]
     achieved = m["bytes"] / (m["split_ms"] * 1e-3) / 1e9
     src_hash = decode_source_hash()
@@ -497,9 +724,12 @@ def main():
             "context_max": int(lens0.max()), "layers_cycled": args.layers,
             "step": "rotate_quant_append(1 token/seq) + int2_decode_partials + int2_decode_merge",
             "decode_ms": m["dec_ms"], "decode_split_ms": m["split_ms"],
-            "decode_merge_ms": m["merge_ms"], "append_ms": m["ms_step_ev"] - m["dec_ms"],
+            "decode_split_ms_pct": m["split_pct"], "step_ms_events": m["step_pct"],
+            "decode_merge_ms": m["merge_ms"], "append_ms": m["append_ms"],
             "ms_per_step_with_kernel_events": m["ms_step_ev"],
             "decode_call_GBs": m["bytes"] / (m["dec_ms"] * 1e-3) / 1e9,
+            "host_ms_per_step": m["host_ms_per_step"], "gpu_hold_ms": m["hold_ms"],
+            "host_bound": m["host_bound"],
             "decode_kernel_source": src_hash,
         },
         "roofline": {
@@ -510,22 +740,39 @@ def main():
         "cpu_baseline": None,
         "setup_s": m["setup_s"],
     }
-    if args.bs1_config:
-        # bs1 latency: enough layer copies that the cache is not MALL-resident
-        b = measure(get(args.bs1_config), args.bs1_layers, args.steps, args.warmup, hold)
-        res["bs1"] = {
-            "workload": f"{b['w'].name}: {b['w'].description}",
-            "context": int(b["lens0"][0]), "layers_cycled": args.bs1_layers,
-            "ms_per_step": b["ms_step"], "tokens_per_s": b["n"] / (b["ms_step"] * 1e-3),
-            "decode_ms": b["dec_ms"], "decode_split_ms": b["split_ms"],
-            "decode_merge_ms": b["merge_ms"], "append_ms": b["ms_step_ev"] - b["dec_ms"],
-            "ms_per_step_with_kernel_events": b["ms_step_ev"],
-            "split_GBs": b["bytes"] / (b["split_ms"] * 1e-3) / 1e9,
-            "algorithmic_bytes_per_launch": b["bytes"],
-        }
-    if args.bf16_compare:
+    probe = None
+    if "probe" in legs:
+        log("read probe")
+        res["read_probe"] = measure_probe()
+        probe = res["read_probe"]["shuffled_chunks"]["GBs"]
+        res["roofline"]["frac_of_read_probe"] = achieved / probe
+    if "bs1" in legs:
+        # bs1 latency (C2, 32K context): enough layer copies that the cache is
+        # not MALL-resident, every copy warmed, plus the same steps replayed
+        # from a HIP graph (no host launch path)
+        log(f"bs1 leg: {ls} steps, {args.bs1_layers} layers")
+        b = measure(get("c2_qwen3_8b_bs1"), args.bs1_layers, ls, args.warmup,
+                    graph_steps=args.bs1_layers, graph_reps=20)
+        res["bs1"] = leg_summary(b, probe)
+        res["bs1"]["layers_cycled"] = args.bs1_layers
+    if "c1" in legs:
+        log("c1 leg")
+        c1 = measure(get("c1_tiny"), 8, ls, args.warmup)
+        res["c1"] = leg_summary(c1, probe)
+        res["c1"]["layers_cycled"] = 8
+        res["c1"]["note"] = "0.14 MB per call: resident in the 256 MB MALL (launch-latency bound)"
+    if "c4" in legs:
+        log("c4 leg")
+        c4 = measure(get("c4_long_bs1"), 4, ls, args.warmup, graph_steps=4, graph_reps=20)
+        res["c4"] = leg_summary(c4, probe)
+        res["c4"]["layers_cycled"] = 4
+    if "c5" in legs:
+        log("c5 serving step")
+        res["c5_step"] = measure_c5_step(get("c5_qwen3_32b_step"), reps=20)
+    if "bf16" in legs:
+        log("bf16 comparison")
         # the uncompressed comparison point on the same shapes and lengths
-        bf = measure_bf16(get(args.config), 2, min(args.steps, 100), hold)
+        bf = measure_bf16(get(args.config), 2, min(ls, 100), hold_for(2e-3 * min(ls, 100)))
         res["bf16_compare"] = {
             "kernel": "oscar_bf16_paged_decode_attn (split + merge), same lengths",
             "bs64_decode_ms": bf["decode_ms"], "bs64_GBs": bf["GBs"],
@@ -533,13 +780,15 @@ def main():
             "bs64_int2_speedup": bf["decode_ms"] / m["dec_ms"],
             "bs64_int2_bytes_ratio": bf["bytes"] / m["bytes"],
         }
-        if args.bs1_config:
-            bf1 = measure_bf16(get(args.bs1_config), 8, min(args.steps, 100), hold)
+        if "bs1" in res:
+            bf1 = measure_bf16(get("c2_qwen3_8b_bs1"), 8, min(ls, 100),
+                               hold_for(2e-3 * min(ls, 100)))
             res["bf16_compare"].update({
                 "bs1_decode_ms": bf1["decode_ms"], "bs1_GBs": bf1["GBs"],
                 "bs1_int2_speedup": bf1["decode_ms"] / res["bs1"]["decode_ms"],
             })
-    if args.prefill:
+    if "prefill" in legs:
+        log("prefill legs")
         # chunked-prefill attention: the Qwen3-32B step's 16 fresh 2048-token
         # chunks, and a 2048-token chunk after a 30720-token prefix (Qwen3-8B heads)
         w5 = get("c5_qwen3_32b_step")
@@ -563,7 +812,8 @@ def main():
         }
         if not args.no_cpu_baseline:
             res["prefill"]["cpu_baseline"] = cpu_prefill_baseline(w5, 0, w5.prefill_len)
-    if args.rotation_modes:
+    if "rotation" in legs:
+        log("append rotation modes")
         # the Qwen3-32B step's append (16 fresh 2048-token chunks, 64 / 8
         # heads) with the dense per-head rotation and the structured
         # R = H P_br / sqrt(128) (fast Walsh-Hadamard transform)
@@ -579,13 +829,14 @@ def main():
         }
         # the decode step of the headline workload with the structured rotation
         # (the merge generates R^T instead of reading R_V)
-        hs = measure(w, args.layers, max(20, args.steps // 4), args.warmup, hold, rotation=2)
+        hs = measure(w, args.layers, max(20, args.steps // 4), args.warmup, rotation=2)
         res["append_rotation_modes"]["decode_step_hadamard_bitrev"] = {
             "workload": w.name, "steps": max(20, args.steps // 4), "ms_per_step": hs["ms_step"],
             "decode_split_ms": hs["split_ms"], "decode_merge_ms": hs["merge_ms"],
-            "append_ms": hs["ms_step_ev"] - hs["dec_ms"],
+            "append_ms": hs["append_ms"],
         }
     if not args.no_cpu_baseline:
+        log("cpu baseline")
         res["cpu_baseline"] = cpu_baseline(w, lens0, seconds=args.cpu_seconds)
     print(json.dumps(res), flush=True)
 

@@ -30,8 +30,8 @@
  *  - bf16 and fp16 values travel as uint16_t bit patterns.
  *  - Every pointer argument is a DEVICE pointer unless its name ends in
  *    _host.  Device buffers (cache arrays, rows, workspace, output) must be
- *    16-byte aligned (OSCAR_ERR_ARG otherwise).  The caller owns all memory; the library allocates nothing and
- *    keeps no state between calls.
+ *    16-byte aligned (OSCAR_ERR_ARG otherwise).  The caller owns all memory;
+ *    the library allocates nothing and keeps no state between calls.
  *  - Calls enqueue work on `stream` (a hipStream_t; NULL = default stream)
  *    and return without waiting.  Calls that touch the same cache or the
  *    same workspace must be ordered on one stream by the caller.
@@ -285,7 +285,11 @@ int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
 
 /* For checking: the decoded rows of positions [tok_begin, tok_end) of one
  * cache row holding seq_len tokens, in the rotated basis: bf16 window rows
- * widened to fp32, INT2 rows as scale * code + zero rounded once to fp32.
+ * widened to fp32, INT2 rows as scale * code + zero rounded once to fp32 --
+ * the values the decode kernel reads.
+ * [OSCAR s4 "Decoding Attention Kernel": INT2 segments are unpacked to
+ * floating point (scale times code plus zero point) and BF16 segments read
+ * as they are; OScaR "integer quantization basics": the dequantizer]
  *  k_out, v_out   fp32 [tok_end - tok_begin][Hkv][128] */
 int oscar_dequant(const oscar_kv_cache* cache, int32_t seq_slot, int32_t seq_len,
                   int32_t tok_begin, int32_t tok_end, float* k_out, float* v_out, void* stream);

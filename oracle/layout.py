@@ -76,6 +76,35 @@ def pack_page_head(kc, vc, ks, kz, vs, vz, group):
     return out.view(np.uint8)
 
 
+def pack_page_heads(kc, vc, ks, kz, vs, vz, group):
+    """Many page-head blocks at once: uint8 [N, PB] from codes [N, 16, 128] and
+    params [N, 16, ng].  The same word layout as ``pack_page_head``, written
+    with array operations so whole caches can be packed quickly; the tests
+    check it against ``pack_page_head`` block by block."""
+    kc = np.asarray(kc, dtype=np.uint32)
+    vc = np.asarray(vc, dtype=np.uint32)
+    n = kc.shape[0]
+    ng = D // group
+    out = np.zeros((n, page_head_bytes(group) // 4), dtype=np.uint32)
+    # K: word (8 t + w), channel 16 w + i at bits 2i
+    kk = kc.reshape(n, PAGE, 8, 16)
+    sh = (2 * np.arange(16, dtype=np.uint32))
+    out[:, 0:128] = np.bitwise_or.reduce(kk << sh, axis=3).reshape(n, 128)
+    # V: word 2 (16 a + m) + e, slot 4a + 2e + s, channel 8m + j at bits 16 s + 2j
+    vv = vc.reshape(n, 4, 2, 2, 16, 8)                      # [n, a, e, s, m, j]
+    shv = (16 * np.arange(2, dtype=np.uint32))[:, None, None] + (2 * np.arange(8, dtype=np.uint32))
+    words = np.bitwise_or.reduce(vv << shv, axis=(3, 5))   # [n, a, e, m]
+    out[:, 128:256] = words.transpose(0, 1, 3, 2).reshape(n, 128)
+    # params: word (16 gr + t) = scale | zero << 16
+    def params(s16, z16):
+        s = np.asarray(s16, dtype=np.uint32)
+        z = np.asarray(z16, dtype=np.uint32)
+        return (s | (z << np.uint32(16))).transpose(0, 2, 1).reshape(n, 16 * ng)
+    out[:, 256:256 + 16 * ng] = params(ks, kz)
+    out[:, 256 + 16 * ng:256 + 32 * ng] = params(vs, vz)
+    return out.view(np.uint8)
+
+
 def unpack_page_head(block, group):
     """Inverse of ``pack_page_head``: (kc, vc, ks, kz, vs, vz)."""
     ng = D // group

@@ -19,7 +19,9 @@ Recipe (seed = 1000 + config index):
   (stream [seed, 5]).
 * K, V, Q: standard normal fp32, generated in blocks of 256 positions
   (streams [seed, 6 / 7 / 8, seq, block]); keys get the outlier channels x20
-  and the first n_sink positions x sink_scale (low-norm attention sinks).
+  and the first n_sink positions x sink_scale (low-norm attention sinks);
+  values are multiplied by v_scale (1 in the five workloads; large-value
+  test cases only).
 * physical pages: a seeded permutation of the page pool (stream [seed, 9]),
   or the identity.
 """
@@ -34,10 +36,11 @@ BLOCK = 256
 
 
 def bf16_from_f32(x):
-    """fp32 -> bf16 bits, round to nearest even (torch's CPU cast, multi-threaded)."""
-    import torch
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    """fp32 -> bf16 bits, round to nearest even on the 16 dropped bits (finite
+    inputs; the same bits as torch's float -> bfloat16 cast)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    out = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    return (out >> np.uint32(16)).astype(np.uint16)
 
 
 @dataclass(frozen=True)
@@ -60,6 +63,7 @@ class Workload:
     prefill_chunks: int = 0  # fresh sequences each appending one chunk in the step
     prefill_len: int = 0
     extra_pages: int = 0     # spare pages per sequence for appends after setup
+    v_scale: float = 1.0     # values drawn from N(0, v_scale^2) (1 in the five workloads)
     description: str = ""
     meta: dict = field(default_factory=dict, compare=False)
 
@@ -136,7 +140,10 @@ class Workload:
         return bf16_from_f32(x)
 
     def values(self, seq, p0, p1):
-        return bf16_from_f32(self._blocks(7, seq, p0, p1, self.hkv))
+        x = self._blocks(7, seq, p0, p1, self.hkv)
+        if self.v_scale != 1.0:
+            x *= np.float32(self.v_scale)
+        return bf16_from_f32(x)
 
     def queries(self, seq, p0, p1):
         return bf16_from_f32(self._blocks(8, seq, p0, p1, self.hq))

@@ -17,6 +17,8 @@ from ultra_bit_kv_amd._lib import KvCache, KvConfig
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "oscar_kv.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -26,9 +28,12 @@ def L():
     return _lib.lib()
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(oscar_\w+)\s*\(", text, re.M)))
+def declared_functions(headers=(HEADER,)):
+    names = set()
+    for hdr in headers:
+        text = open(hdr).read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(oscar_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_three_calls():
@@ -39,8 +44,24 @@ def test_header_declares_the_three_calls():
 
 
 def test_every_declared_symbol_is_exported(L):
-    for n in declared_functions():
+    names = declared_functions(HEADERS)
+    assert "oscar_read_probe" in names
+    for n in names:
         assert hasattr(L, n), n
+
+
+def test_read_probe_argument_checks(L):
+    f = L.oscar_read_probe
+    buf, sink = DUMMY, DUMMY
+    assert f(None, 1024, None, 0, 0, sink, 1, 4, None) == -1
+    assert f(buf, 1024, None, 0, 0, None, 1, 4, None) == -1
+    assert f(ctypes.c_void_p(DUMMY.value + 4), 1024, None, 0, 0, sink, 1, 4, None) == -10
+    assert f(buf, 1000, None, 0, 0, sink, 1, 4, None) == -10          # not a multiple of 1 KB
+    assert f(buf, 1024, None, 0, 0, sink, 2, 4, None) == -10          # sink too small for the grid
+    assert f(buf, 1024, None, 0, 0, sink, 0, 4, None) == -10
+    assert f(buf, 4096, DUMMY, 4, 1000, sink, 1, 4, None) == -10      # chunk size
+    assert f(buf, 4096, DUMMY, -1, 1024, sink, 1, 4, None) == -10
+    assert f(buf, 4096, None, 0, 0, sink, 1, 4, None) in (-9, -8, 0)  # reaches the device check
 
 
 def cfg(**kw):
@@ -316,3 +337,4 @@ def test_structured_rotation_argument_checks(L):
         assert append(L, c, [0], [0], [5], cache=_cache(c, rotation=kind, **bare)) in (-1, -10)
         assert append(L, c, [0], [0], [5], cache=_cache(c, rotation=kind)) == -10
         assert prefill(L, c, [0], [0], [5], cache=_cache(c, rotation=kind)) == -10
+

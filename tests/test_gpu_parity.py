@@ -49,10 +49,13 @@ def small(name):
         w = get("c3_bs64").scaled(n_seqs=2, hkv=2, hq=8, s_sink=5, s_keep=40, s_flush=24,
                                    group=32, lengths=("list", (250, 401)))
         return w, [250, 401]
+    if name == "bigv":      # value rows of magnitude ~1e3: fp16 value scales above 128
+        w = get("c3_bs64").scaled(n_seqs=2, v_scale=1000.0, lengths=("list", (700, 1100)))
+        return w, [700, 1100]
     raise KeyError(name)
 
 
-CASES = ["c1", "c2s", "c3s", "c4s", "c5s", "demote1", "oddflush"]
+CASES = ["c1", "c2s", "c3s", "c4s", "c5s", "demote1", "oddflush", "bigv"]
 
 
 def _check_head(cache, w, i, h, L, hc):
@@ -102,7 +105,10 @@ def test_append_bit_exact_and_decode(name, identity):
             hc = oracle_head(w, i, h, L, r_k, r_v)
             _check_head(cache, w, i, h, L, hc)
             want = oracle_decode(w, i, h, L, r_k, r_v, hc)
-            err, rel, ok = compare_attention(out[i, h * w.g:(h + 1) * w.g], want)
+            # the error budget is relative to the values' magnitude (fp32
+            # accumulation, P' as fp16 hi + lo): the absolute bar scales with it
+            err, rel, ok = compare_attention(out[i, h * w.g:(h + 1) * w.g], want,
+                                             tol_abs=2e-3 * w.v_scale)
             worst = (max(worst[0], err), max(worst[1], rel))
             assert ok, (name, i, h, err, rel)
     print(f"[case] {name} max_abs={worst[0]:.3e} rel_l2={worst[1]:.3e}", flush=True)

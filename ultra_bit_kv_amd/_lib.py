@@ -74,6 +74,8 @@ _PROTOS = {
     "oscar_bf16_paged_decode_attn": (c_i32, [ctypes.POINTER(Bf16Cache), c_i32, c_p, c_p, c_p, c_p,
                                              c_p, c_p, c_p, c_size, c_p]),
     "oscar_status_string": (ctypes.c_char_p, [c_i32]),
+    "oscar_round_f64_host": (c_i32, [c_i32, c_p, c_p, c_i64]),
+    "oscar_read_probe": (c_i32, [c_p, c_size, c_p, c_i32, c_i32, c_p, c_i32, c_i32, c_p]),
 }
 
 _LIB = None

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liboscar_kv.so")
 SOURCES = ["api.cpp", "k_rotate.hip", "k_quant.hip", "k_dequant.hip", "k_decode.hip", "k_bf16.hip",
-           "k_prefill.hip"]
+           "k_prefill.hip", "k_probe.hip"]
 # The decode kernels keep their MFMA accumulators in VGPRs so the (rare) online
 # softmax rescale multiplies them in place instead of copying AGPRs each step.
 EXTRA = {"k_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],

@@ -134,8 +134,7 @@ class OscarKVCache:
     def workspace_for(self, n_seqs, max_new_tokens):
         need = lib().oscar_workspace_size(ctypes.byref(self.cfg), int(n_seqs), int(max_new_tokens))
         if self.workspace is None or self.workspace.numel() < need:
-            # zero-filled: the leading counters must start at zero
-            self.workspace = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self.workspace
 
     # ------------------------------------------------------------------ calls

@@ -7,6 +7,8 @@
 #include <mutex>
 #include <vector>
 
+#include "device_common.h"
+#include "oscar_check.h"
 #include "oscar_internal.h"
 #include "oscar_kv.h"
 
@@ -425,10 +427,12 @@ namespace {
 // split and merge calls of one decode step compute the same plan.
 // Plans and enqueues one split-K decode call (INT2 or BF16 pages) of
 // n_seqs checked sequences.
+// cap_override > 0: the most splits per row the workspace holds (a fixed
+// scratch buffer), instead of the limit oscar_workspace_size sizes for.
 int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, bool bf16,
                     int n_seqs, const int32_t* seq_slots_host, const int32_t* seq_lens_host,
                     const int32_t* seq_slots, const int32_t* seq_lens, const uint16_t* q,
-                    float* out, void* workspace, void* stream, int phases) {
+                    float* out, void* workspace, void* stream, int phases, int cap_override = 0) {
   int cus = 256;
   int st = check_device(&cus);
   if (st != OSCAR_OK) return st;
@@ -437,7 +441,7 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
       std::max<int64_t>(1, (int64_t)cus * decode_slots_per_cu(a, plan, bf16) * kFillPercent / 100);
   // Every launch keeps to the split limit the workspace is sized for (that
   // of a full launch), so a short last launch fits in it too.
-  const int cap = max_splits(sh, std::min(n_seqs, kMaxScanSeqs));
+  const int cap = cap_override > 0 ? cap_override : max_splits(sh, std::min(n_seqs, kMaxScanSeqs));
   static thread_local ItemOrder order;
   static thread_local SplitCounts counts;
   // Launches of at most kMaxScanSeqs sequences, in stream order.
@@ -447,7 +451,8 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
     // items (one work-group each) all fit in one round of resident
     // work-groups, so none waits for a second round; long sequences get
     // more splits.  The quota never leaves the split limits.
-    std::vector<int64_t> cost(ns);
+    static thread_local std::vector<int64_t> cost;
+    cost.resize(ns);
     int64_t total = 0, max_cost = 0;
     for (int i = 0; i < ns; ++i) {
       cost[i] = decode_cost(seq_lens_host[s0 + i], a);
@@ -477,7 +482,8 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
     }
     int64_t smax = 1;
     for (int i = 0; i < ns; ++i) smax = std::max<int64_t>(smax, splits_of(cost[i], quota));
-    if (smax > cap) return OSCAR_ERR_CAPACITY;   // unreachable: cap >= min_splits
+    // unreachable: cap >= min_splits, or (fixed scratch) checked by the caller
+    if (smax > cap) return cap_override > 0 ? OSCAR_ERR_WORKSPACE : OSCAR_ERR_CAPACITY;
     plan.quota = (int)quota;
     plan.smax = (int)smax;
     plan.grid = (int)items_of(quota);
@@ -487,7 +493,8 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
     // sharing a compute unit (b, b + cus, ...) add up to about equal work.
     order.n = 0;
     if (plan.grid <= kMaxOrder) {
-      std::vector<std::pair<int, uint32_t>> items;   // (work units, sequence << 16 | item in it)
+      static thread_local std::vector<std::pair<int, uint32_t>> items;   // (work units, sequence << 16 | item in it)
+      items.clear();
       items.reserve(plan.grid);
       for (int i = 0; i < ns; ++i) {
         const DecodeWork w =
@@ -763,3 +770,12 @@ int oscar_dequant(const oscar_kv_cache* cache, int32_t seq_slot, int32_t seq_len
 }
 
 }  // extern "C"
+
+extern "C" int oscar_round_f64_host(int32_t target, const double* x, uint16_t* out, int64_t n) {
+  if (!x || !out) return OSCAR_ERR_NULL;
+  if (n < 0 || target < 0 || target > 2) return OSCAR_ERR_ARG;
+  for (int64_t i = 0; i < n; ++i)
+    out[i] = target == 0 ? oscar::f64_to_bf16_rne(x[i])
+                         : (target == 1 ? oscar::f64_to_f16_rne(x[i]) : oscar::f64_to_bf16_rne_normal(x[i]));
+  return OSCAR_OK;
+}

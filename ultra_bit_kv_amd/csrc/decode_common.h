@@ -55,6 +55,18 @@ __device__ __forceinline__ float f16hi(uint32_t w) {
 }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+
+// Bit pattern of the largest fp16 scale (low halves) of eight scale | zero
+// words.  Scales are (hi - lo) / 3 >= 0, and the bit patterns of
+// non-negative fp16 values are ordered like the values.
+__device__ __forceinline__ uint32_t max_scale_bits(const u32x4& a, const u32x4& b) {
+  auto m = [](uint32_t x, uint32_t y) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, x),
+                                                                  __builtin_bit_cast(ushort2_t, y)));
+  };
+  return m(m(m(a[0], a[1]), m(a[2], a[3])), m(m(b[0], b[1]), m(b[2], b[3]))) & 0xFFFFu;
+}
 
 // The products a * lo16(wa) and b * lo16(wb) (fp16 scales) as fp16 pairs
 // split in two: hi = the products rounded to fp16, lo = the remainders
@@ -86,16 +98,17 @@ struct SoftmaxState {
 
 // Online-softmax update with a lazy max.  x holds logits in raw units; the
 // log2-domain logit is scale * x (scale > 0).  The reference max only moves
-// when a logit exceeds it by more than 8 (so p <= 2^8), which keeps most
-// tiles free of the accumulator rescale.
+// when a logit exceeds it by more than `slack` (so p <= 2^slack), which keeps
+// most tiles free of the accumulator rescale; slack = 0 keeps every p <= 1.
 template <int N>
 __device__ __forceinline__ void softmax_step(const float (&x)[N], float scale, float (&p)[N],
-                                             SoftmaxState& st, float4_t (&acc)[8]) {
+                                             SoftmaxState& st, float4_t (&acc)[8],
+                                             float slack = 8.0f) {
   float tmax = x[0];
 #pragma unroll
   for (int k = 1; k < N; ++k) tmax = fmaxf(tmax, x[k]);
   tmax = rows_max(tmax) * scale;
-  if (__any(tmax > st.m + 8.0f)) {
+  if (__any(tmax > st.m + slack)) {
     const float m_new = fmaxf(st.m, tmax);
     const float alpha = m_new > st.m ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.0f;
 #pragma unroll
@@ -195,8 +208,9 @@ __device__ __forceinline__ bool work_item(const SeqArgs& s, const ItemOrder& ord
   return true;
 }
 
-// Log-sum-exp merge of partial records (WUSH-KV notes, "method step
-// details": split outputs are combined by their maxima and sums).  A record
+// Log-sum-exp merge of partial records (OSCAR summary page, section 4
+// "Decoding Attention Kernel": segments of the sequence are processed by
+// separate launches and their partial results merged afterwards).  A record
 // holds, per head, m (log2 domain), l = sum 2^(x - m) and the unnormalized
 // o' = sum 2^(x - m) v'; two records combine exactly as
 //   M = max(m1, m2), l = l1 2^(m1 - M) + l2 2^(m2 - M), o' likewise.

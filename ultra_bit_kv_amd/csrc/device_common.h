@@ -19,10 +19,11 @@ namespace oscar {
 // significand that rounds up to the next power of two carries into the
 // exponent field by the addition itself.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint16_t round_f64_to_short_float(double x, int emin, int mant_bits,
-                                                             int bias, uint32_t inf_bits,
-                                                             uint32_t nan_bits) {
-  const uint64_t b = (uint64_t)__double_as_longlong(x);
+__host__ __device__ __forceinline__ uint16_t round_f64_to_short_float(double x, int emin,
+                                                                      int mant_bits, int bias,
+                                                                      uint32_t inf_bits,
+                                                                      uint32_t nan_bits) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
   const uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
   const double a = __builtin_fabs(x);
   if (a != a) return (uint16_t)(sign | nan_bits);
@@ -42,12 +43,27 @@ __device__ __forceinline__ uint16_t round_f64_to_short_float(double x, int emin,
   return (uint16_t)(sign | bits);
 }
 
-__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+__host__ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
   return round_f64_to_short_float(x, -126, 7, 127, 0x7F80u, 0x7FC0u);
 }
 
-__device__ __forceinline__ uint16_t f64_to_f16_rne(double x) {
+__host__ __device__ __forceinline__ uint16_t f64_to_f16_rne(double x) {
   return round_f64_to_short_float(x, -14, 10, 15, 0x7C00u, 0x7E00u);
+}
+
+// fp64 -> bf16 round-to-nearest-even on the bit pattern for results in the
+// bf16 normal range (exponent field 897 .. 1150): the 45 dropped significand
+// bits round by adding 2^44 - 1 plus the kept lowest bit, a carry moving into
+// the exponent; zeros, subnormals and overflow take f64_to_bf16_rne.
+__host__ __device__ __forceinline__ uint16_t f64_to_bf16_rne_normal(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t e = (uint32_t)(b >> 52) & 0x7FFu;
+  if (e < 897u || e > 1150u) return f64_to_bf16_rne(x);
+  const uint64_t mag = b & 0x7FFFFFFFFFFFFFFFull;
+  const uint64_t r = mag + 0xFFFFFFFFFFFull + ((mag >> 45) & 1ull);
+  uint32_t bits = (uint32_t)(r >> 45) - (896u << 7);
+  if (bits >= 0x7F80u) bits = 0x7F80u;
+  return (uint16_t)(((uint32_t)(b >> 48) & 0x8000u) | bits);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {

@@ -289,8 +289,12 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
         if (!(d.okb && ta + 16 + r < nq)) x[4 + r] = kNegInf;
       }
     }
+    // P' = p * scale_v enters the MFMA as fp16: with p <= 2^8 (the lazy
+    // max) a value scale of 128 or more could overflow it, so such a pair
+    // takes the exact max (p <= 1, P' <= scale <= 65504)
+    const bool big_scale = max_scale_bits(d.vpa, d.vpb) >= 0x5800u;   // fp16 128.0
     float p[8];
-    softmax_step<8>(x, K1, p, st, acc);
+    softmax_step<8>(x, K1, p, st, acc, __any(big_scale) ? 0.0f : 8.0f);
     uint32_t ph[4], pl[4];
     mul_by_f16lo_split(p[0], d.vpa[0], p[1], d.vpa[1], ph[0], pl[0]);
     mul_by_f16lo_split(p[2], d.vpa[2], p[3], d.vpa[3], ph[1], pl[1]);

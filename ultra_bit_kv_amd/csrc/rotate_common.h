@@ -89,21 +89,6 @@ __device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ src, i
 
 constexpr double kInvSqrtD = 0x1.6a09e667f3bcdp-4;   // fp64(sqrt(2)) / 16 = fp64(1 / sqrt(128))
 
-// fp64 -> bf16 round-to-nearest-even on the bit pattern for results in the
-// bf16 normal range (exponent field 897 .. 1150): the 45 dropped significand
-// bits round by adding 2^44 - 1 plus the kept lowest bit, a carry moving into
-// the exponent; zeros, subnormals and overflow take f64_to_bf16_rne.
-__device__ __forceinline__ uint16_t f64_to_bf16_rne_normal(double x) {
-  const uint64_t b = (uint64_t)__double_as_longlong(x);
-  const uint32_t e = (uint32_t)(b >> 52) & 0x7FFu;
-  if (e < 897u || e > 1150u) return f64_to_bf16_rne(x);
-  const uint64_t mag = b & 0x7FFFFFFFFFFFFFFFull;
-  const uint64_t r = mag + 0xFFFFFFFFFFFull + ((mag >> 45) & 1ull);
-  uint32_t bits = (uint32_t)(r >> 45) - (896u << 7);
-  if (bits >= 0x7F80u) bits = 0x7F80u;
-  return (uint16_t)(((uint32_t)(b >> 48) & 0x8000u) | bits);
-}
-
 // The value of lane l ^ m (m = 1, 2, 4, 8; within a 16-lane row), as DPP
 // moves of the two halves: quad_perm [1,0,3,2] and [2,3,0,1] for m = 1, 2;
 // row_ror:8 for m = 8 (row_ror:n gives lane i of a row the value of lane
