@@ -362,23 +362,31 @@ def hold_for(host_s):
     return int(max(3.0 * host_s, 5e-3) * CLOCK_HZ)
 
 
-def timed_region(enqueue, n, hold_cycles):
+def timed_region(enqueue, n, hold_cycles, retries=2):
     """GPU time of `n` calls of enqueue(j) queued behind a spin kernel, so the
     events time the GPU's execution of the queue, not the host's submission.
-    Returns (ms per call, host seconds spent queueing)."""
+    When the host took longer to queue the calls than the spin kernel held
+    the GPU (the GPU then waited on the host), the same calls are timed again
+    behind a longer spin.  Returns (ms per call, host seconds spent queueing,
+    whether the last attempt was still host-bound)."""
     import torch
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(hold_cycles))
-    t_start.record()
-    h0 = time.perf_counter()
-    for j in range(n):
-        enqueue(j)
-    host = time.perf_counter() - h0
-    t_end.record()
-    torch.cuda.synchronize()
-    return t_start.elapsed_time(t_end) / n, host
+    for attempt in range(retries + 1):
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(hold_cycles))
+        t_start.record()
+        h0 = time.perf_counter()
+        for j in range(n):
+            enqueue(j)
+        host = time.perf_counter() - h0
+        t_end.record()
+        torch.cuda.synchronize()
+        bound = host > hold_cycles / CLOCK_HZ
+        if not bound:
+            break
+        hold_cycles = hold_for(host)
+    return t_start.elapsed_time(t_end) / n, host, bound
 
 
 def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0):
@@ -468,10 +476,10 @@ def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0)
     hold = hold_for(host_step * steps * 4)   # pass 2 also records 4 events per step
     # pass 1: the whole step, no event records between its launches (each
     # record adds a gap to the stream)
-    ms_step, host1 = timed_region(lambda j: step(warm + j), steps, hold)
+    ms_step, host1, bound1 = timed_region(lambda j: step(warm + j), steps, hold)
     # pass 2: the same number of steps with events around each launch
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
-    ms_step_ev, host2 = timed_region(lambda j: step(warm + steps + j, evs[j]), steps, hold)
+    ms_step_ev, host2, _ = timed_region(lambda j: step(warm + steps + j, evs[j]), steps, hold)
     app = [a.elapsed_time(b) for a, b, c, d in evs]
     split = [b.elapsed_time(c) for a, b, c, d in evs]
     merge = [c.elapsed_time(d) for a, b, c, d in evs]
@@ -487,8 +495,8 @@ def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0)
            "bytes": float(np.mean(byts)), "setup_s": setup_s, "warm": warm,
            "host_ms_per_step": 1e3 * host1 / steps, "hold_ms": 1e3 * hold / CLOCK_HZ,
            # pass 1 waited on the host if the host took longer to queue the
-           # steps than the spin kernel held the GPU
-           "host_bound": host1 > hold / CLOCK_HZ}
+           # steps than the spin kernel held the GPU (after retries)
+           "host_bound": bound1}
     if graph_steps:
         g0 = warm + 2 * steps
         for j in range(graph_steps):      # the captured steps run once eagerly first
@@ -500,7 +508,7 @@ def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0)
                 step(g0 + j)
         g.replay()                        # replays re-run the same steps: same work
         torch.cuda.synchronize()
-        ms_rep, _ = timed_region(lambda j: g.replay(), graph_reps, hold_for(1e-3 * graph_reps))
+        ms_rep, _, _ = timed_region(lambda j: g.replay(), graph_reps, hold_for(1e-3 * graph_reps))
         res["graph"] = {"steps_per_graph": graph_steps, "replays": graph_reps,
                         "ms_per_step": ms_rep / graph_steps}
         del g
@@ -631,7 +639,7 @@ def measure_c5_step(w, reps):
     for _ in range(3):
         step()
     torch.cuda.synchronize()
-    ms, host = timed_region(lambda j: step(), reps, hold_for(4e-3 * reps))
+    ms, host, _ = timed_region(lambda j: step(), reps, hold_for(4e-3 * reps))
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(reps)]
     timed_region(lambda j: step(evs[j]), reps, hold_for(4e-3 * reps))
     app_ms = [a.elapsed_time(b) for a, b, c, d in evs]
