@@ -31,7 +31,9 @@
  *  - Every pointer argument is a DEVICE pointer unless its name ends in
  *    _host.  Device buffers (cache arrays, rows, workspace, output) must be
  *    16-byte aligned (OSCAR_ERR_ARG otherwise).  The caller owns all memory;
- *    the library allocates nothing and keeps no state between calls.
+ *    the library allocates nothing and keeps no state between calls (the one
+ *    exception is the fixed device scratch of
+ *    oscar_int2_decode_attn_noalloc, declared below).
  *  - Calls enqueue work on `stream` (a hipStream_t; NULL = default stream)
  *    and return without waiting.  Calls that touch the same cache or the
  *    same workspace must be ordered on one stream by the caller.
@@ -250,6 +252,27 @@ int oscar_int2_decode_merge(const oscar_kv_cache* cache, int32_t n_seqs,
                             const int32_t* seq_slots_host, const int32_t* seq_lens_host,
                             const int32_t* seq_slots, const int32_t* seq_lens, float* out,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* oscar_int2_decode_attn without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * and harnesses that forbid hipMalloc).  It computes what
+ * oscar_int2_decode_attn computes with the same kernels; the split records
+ * go to a fixed 64 MiB scratch array that the library holds on each GPU it
+ * runs on until the process ends.  The call allocates nothing.
+ * Limit: the records of a launch (at most 2048 sequences) must fit in the
+ * scratch: a launch of n sequences keeps at most S splits per (sequence, KV
+ * head, query-head pass) with n * Hkv * passes * (S + ceil(S / 16) if S > 32)
+ * * record bytes <= 64 MiB, and a call whose longest row needs more splits
+ * returns OSCAR_ERR_WORKSPACE with nothing enqueued.  Every call on a GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (different
+ * streams, or different host threads without ordering) race and must not be
+ * made.  The scratch needs no clearing: every record the merge reads is
+ * written by the split launch of the same call.  Other errors as for
+ * oscar_int2_decode_attn. */
+int oscar_int2_decode_attn_noalloc(const oscar_kv_cache* cache, int32_t n_seqs,
+                                   const int32_t* seq_slots_host, const int32_t* seq_lens_host,
+                                   const int32_t* seq_slots, const int32_t* seq_lens,
+                                   const uint16_t* q_rot, float* out, void* stream);
 
 /* Chunked-prefill attention: the new tokens of each sequence, just added by
  * oscar_rotate_quant_append, attend causally over the mixed cache.

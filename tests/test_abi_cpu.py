@@ -338,3 +338,27 @@ def test_structured_rotation_argument_checks(L):
         assert append(L, c, [0], [0], [5], cache=_cache(c, rotation=kind)) == -10
         assert prefill(L, c, [0], [0], [5], cache=_cache(c, rotation=kind)) == -10
 
+
+def test_noalloc_decode_argument_checks(L):
+    """oscar_int2_decode_attn_noalloc: the host checks of the workspace form,
+    and a launch whose split records cannot fit the fixed scratch is refused
+    before anything reaches the device."""
+    f = L.oscar_int2_decode_attn_noalloc
+
+    def call(c, slots, lens, q=DUMMY, out=DUMMY):
+        cache = KvCache(c, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None, 0, 0)
+        s = np.asarray(slots, np.int32)
+        ln = np.asarray(lens, np.int32)
+        return f(ctypes.byref(cache), len(s), s.ctypes.data_as(ctypes.c_void_p),
+                 ln.ctypes.data_as(ctypes.c_void_p), DUMMY, DUMMY, q, out, None)
+
+    c = cfg()
+    assert call(c, [0], [0]) == -10
+    assert call(c, [9], [10]) == -6
+    assert call(c, [0], [10], out=None) == -1
+    assert call(c, [0], [10], q=ctypes.c_void_p(DUMMY.value + 4)) == -10
+    assert call(c, [0], [10]) in (-9, -8, 0)
+    # 2048 sequences x 64 KV heads x one query head each: one split record
+    # per row is already 2048 * 64 * 528 B > 64 MiB
+    big = cfg(num_q_heads=64, num_kv_heads=64, max_seqs=2048, max_pages_per_seq=4)
+    assert call(big, list(range(2048)), [10] * 2048) == -7

@@ -63,6 +63,8 @@ _PROTOS = {
                                           c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_size, c_p]),
     "oscar_int2_decode_attn": (c_i32, [ctypes.POINTER(KvCache), c_i32, c_p, c_p, c_p, c_p, c_p, c_p,
                                        c_p, c_size, c_p]),
+    "oscar_int2_decode_attn_noalloc": (c_i32, [ctypes.POINTER(KvCache), c_i32, c_p, c_p, c_p, c_p,
+                                               c_p, c_p, c_p]),
     "oscar_int2_decode_partials": (c_i32, [ctypes.POINTER(KvCache), c_i32, c_p, c_p, c_p, c_p, c_p,
                                            c_p, c_size, c_p]),
     "oscar_int2_decode_merge": (c_i32, [ctypes.POINTER(KvCache), c_i32, c_p, c_p, c_p, c_p, c_p,

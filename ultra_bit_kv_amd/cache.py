@@ -181,6 +181,17 @@ class OscarKVCache:
         check(st, "oscar_int2_decode_attn")
         return out
 
+    def decode_noalloc(self, batch, q_rot, out):
+        """oscar_int2_decode_attn_noalloc: the same decode with the split
+        records in the library's fixed device scratch (no workspace)."""
+        assert q_rot.dtype == torch.bfloat16 and q_rot.shape == (batch.n, self.hq, D)
+        assert out.dtype == torch.float32 and out.shape == (batch.n, self.hq, D)
+        st = lib().oscar_int2_decode_attn_noalloc(
+            ctypes.byref(self.st), batch.n, _hp(batch.slots), _hp(batch.lens), _p(batch.d_slots),
+            _p(batch.d_lens), _p(q_rot), _p(out), current_stream())
+        check(st, "oscar_int2_decode_attn_noalloc")
+        return out
+
     def decode_partials(self, batch, q_rot):
         """oscar_int2_decode_partials: the split launch of a decode step."""
         assert q_rot.dtype == torch.bfloat16 and q_rot.shape == (batch.n, self.hq, D)

@@ -598,21 +598,63 @@ CacheArgs make_bf16_args(const oscar_bf16_cache& b) {
   return a;
 }
 
+// ---- fixed device scratch of oscar_int2_decode_attn_noalloc ---------------
+// A file-scope device array: each GPU the library runs on holds its own copy
+// until the process ends.  Host code never uses the array's name as an
+// address: the per-device address comes from hipGetSymbolAddress, taken once
+// per device with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t device_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+// Most splits per row whose partial records (and the chunk records of the
+// first merge launch) fit in the scratch for a launch of n_seqs sequences.
+int scratch_splits(const DecodeShape& sh, int n_seqs) {
+  const int ns = std::min(std::max(1, n_seqs), kMaxScanSeqs);
+  const size_t per_split = (size_t)ns * sh.hkv * sh.passes * rec_words(sh.hp) * sizeof(float);
+  int best = 0;
+  for (int cap = 1; cap <= kMaxSplits; ++cap) {
+    const size_t recs = cap + (cap > kMergeDirect ? (cap + kMergeChunk - 1) / kMergeChunk : 0);
+    if (per_split * recs > kScratchBytes) break;
+    best = cap;
+  }
+  return best;
+}
+
+// noalloc: the split records go to the fixed scratch instead of `workspace`.
 int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_slots_host,
                 const int32_t* seq_lens_host, const int32_t* seq_slots, const int32_t* seq_lens,
                 const uint16_t* q_rot, float* out, void* workspace, size_t workspace_bytes,
-                void* stream, int phases) {
+                void* stream, int phases, bool noalloc = false) {
   if (!cache) return OSCAR_ERR_NULL;
   const oscar_kv_config& c = cache->cfg;
   int st = oscar_check_config(&c);
   if (st != OSCAR_OK) return st;
-  if (!seq_slots_host || !seq_lens_host || !seq_slots || !seq_lens || !workspace ||
+  if (!seq_slots_host || !seq_lens_host || !seq_slots || !seq_lens || (!noalloc && !workspace) ||
       !cache->pages || !cache->block_table || !cache->win ||
       (dense(*cache) && !cache->r_v && !cache->out_rotated))
     return OSCAR_ERR_NULL;
   if (!rotation_ok(*cache)) return OSCAR_ERR_ARG;
   if (((phases & kDecodeSplit) && !q_rot) || ((phases & kDecodeMerge) && !out)) return OSCAR_ERR_NULL;
-  if (!aligned16(q_rot) || !aligned16(out) || !cache_aligned(*cache) || !aligned16(workspace))
+  if (!aligned16(q_rot) || !aligned16(out) || !cache_aligned(*cache) ||
+      (!noalloc && !aligned16(workspace)))
     return OSCAR_ERR_ARG;
   if (n_seqs < 1 || n_seqs > c.max_seqs) return OSCAR_ERR_ARG;
   // separate split and merge calls share one launch's workspace
@@ -626,10 +668,24 @@ int decode_step(const oscar_kv_cache* cache, int32_t n_seqs, const int32_t* seq_
     if (len > max_len || int2_pages(len, c) > c.max_pages_per_seq) return OSCAR_ERR_CAPACITY;
     if (int2_pages(len, c) > 0 && c.num_pages < 1) return OSCAR_ERR_CAPACITY;
   }
-  if (workspace_bytes < partials_bytes(int2_shape(c), n_seqs)) return OSCAR_ERR_WORKSPACE;
-  return plan_and_launch(make_args(*cache), head_passes(c), int2_shape(c), false, n_seqs,
-                         seq_slots_host, seq_lens_host, seq_slots, seq_lens, q_rot, out, workspace,
-                         stream, phases);
+  const CacheArgs args = make_args(*cache);
+  int cap = 0;
+  if (noalloc) {
+    // the longest row must fit its splits in the scratch at the largest
+    // split quota (kMaxPairsPerSplit - 1 work units per split)
+    cap = scratch_splits(int2_shape(c), n_seqs);
+    int64_t max_cost = 0;
+    for (int i = 0; i < n_seqs; ++i) max_cost = std::max(max_cost, decode_cost(seq_lens_host[i], args));
+    if (cap < 1 || (max_cost + kMaxPairsPerSplit - 2) / (kMaxPairsPerSplit - 1) > cap)
+      return OSCAR_ERR_WORKSPACE;
+    if ((st = check_device()) != OSCAR_OK) return st;
+    if ((st = hip_status(device_scratch(&workspace))) != OSCAR_OK) return st;
+  } else if (workspace_bytes < partials_bytes(int2_shape(c), n_seqs)) {
+    return OSCAR_ERR_WORKSPACE;
+  }
+  return plan_and_launch(args, head_passes(c), int2_shape(c), false, n_seqs, seq_slots_host,
+                         seq_lens_host, seq_slots, seq_lens, q_rot, out, workspace, stream, phases,
+                         cap);
 }
 
 
@@ -663,6 +719,14 @@ int oscar_int2_decode_merge(const oscar_kv_cache* cache, int32_t n_seqs,
                      out, workspace, workspace_bytes, stream, kDecodeMerge);
 }
 
+
+int oscar_int2_decode_attn_noalloc(const oscar_kv_cache* cache, int32_t n_seqs,
+                                   const int32_t* seq_slots_host, const int32_t* seq_lens_host,
+                                   const int32_t* seq_slots, const int32_t* seq_lens,
+                                   const uint16_t* q_rot, float* out, void* stream) {
+  return decode_step(cache, n_seqs, seq_slots_host, seq_lens_host, seq_slots, seq_lens, q_rot, out,
+                     nullptr, 0, stream, kDecodeSplit | kDecodeMerge, true);
+}
 
 size_t oscar_bf16_workspace_size(const oscar_bf16_cache* cache, int32_t n_seqs) {
   if (check_bf16(cache) != OSCAR_OK) return 0;
