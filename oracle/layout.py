@@ -17,6 +17,16 @@ PB = 1024 + 128 * ng with ng = 128 / G:
                       for group gr, slot t.
   [1024+64ng, PB)     V params, same order.
 
+OScaR page-head block (keys per channel over blocks of 32 tokens, G = 32),
+1568 bytes:
+  [0, 512)            K codes, as above.
+  [512, 1024)         V codes, as above.
+  [1024, 1280)        V params, as above (4 groups).
+  [1280, 1312)        K token scales: bf16 s_t of slot t at uint16 index t.
+  [1312, 1568)        K channel params of channels 64 h .. 64 h + 63, h = (logical
+                      INT2 page) mod 2 (the page's half of its 32-token block):
+                      uint32 word j = bf16 Delta | bf16 z << 16 of channel 64 h + j.
+
 Window block (16 token slots, bf16), 2 * 16 * 128 elements:
   [0, 2048)           K, row-major: element 128 t + c.
   [2048, 4096)        V: element 2048 + 32 (16 (t // 4) + c // 8) + 4 (c % 8) + t % 4.
@@ -74,6 +84,36 @@ def pack_page_head(kc, vc, ks, kz, vs, vz, group):
     out[256:256 + 16 * ng] = pack_params(ks, kz)
     out[256 + 16 * ng:256 + 32 * ng] = pack_params(vs, vz)
     return out.view(np.uint8)
+
+
+OTS_PAGE_HEAD_BYTES = 1568
+
+
+def pack_ots_page_head(kc, vc, ks16, kd16, kz16, vs, vz, group=32):
+    """One OScaR page-head block as uint8 [1568]: codes [16, 128], token scales
+    [16], the page's 64 channel (Delta, z) pairs, value params [16, 4]."""
+    assert group == 32
+    out = np.zeros(OTS_PAGE_HEAD_BYTES // 4, dtype=np.uint32)
+    out[0:128] = pack_k_codes(kc)
+    out[128:256] = pack_v_codes(vc)
+    out[256:320] = pack_params(vs, vz)
+    ts = np.asarray(ks16, dtype=np.uint32).reshape(PAGE)
+    out[320:328] = ts[0::2] | (ts[1::2] << np.uint32(16))
+    out[328:392] = (np.asarray(kd16, dtype=np.uint32) |
+                    (np.asarray(kz16, dtype=np.uint32) << np.uint32(16)))
+    return out.view(np.uint8)
+
+
+def unpack_ots_page_head(block):
+    """Inverse of ``pack_ots_page_head``: (kc, vc, ks16, kd16, kz16, vs, vz)."""
+    w = np.ascontiguousarray(block).view(np.uint32)
+    kc, vc, _, _, vs, vz = unpack_page_head(np.concatenate([block[:1024], np.zeros(256, np.uint8),
+                                                            block[1024:1280]]), 32)
+    ts = np.empty(PAGE, np.uint16)
+    ts[0::2] = w[320:328] & 0xFFFF
+    ts[1::2] = w[320:328] >> 16
+    cp = w[328:392]
+    return kc, vc, ts, (cp & 0xFFFF).astype(np.uint16), (cp >> 16).astype(np.uint16), vs, vz
 
 
 def pack_page_heads(kc, vc, ks, kz, vs, vz, group):

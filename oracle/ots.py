@@ -101,3 +101,110 @@ def key_bytes_per_token_head(d=128, bits=2):
     """Bytes of one key token-head in the OTS layout besides the per-block
     parameters: packed codes plus the BF16 scale."""
     return d * bits // 8 + 2
+
+
+# ---------------------------------------------------------------------------
+# The OScaR variant as a whole cache (one sequence, one KV head).
+#
+# Placement, windows and values are those of the OSCAR cache (``cache.py``):
+# the BF16 sink and recent windows hold the rotated rows, values are quantized
+# per token over channel groups of G (O3, with the head's value clip ratio;
+# OScaR's per-token value quantizer is its min-max case kappa = 1).  Keys of
+# the INT2 segment take the OScaR path: Omni-Token Scaling, then per-channel
+# INT2 over blocks of G consecutive INT2 tokens (the segment starts at S_sink
+# and grows by S_flush, a multiple of G, so blocks never straddle a flush).
+#
+# Reading taken (beyond readings 1-5 above): the residual BF16 buffer holds the
+# rotated key row itself; the per-token norm and the normalized row are taken
+# when the row is quantized.  Normalizing on entry and storing s_t beside the
+# buffered row would quantize the same bits (s16 and u16 are functions of the
+# bf16 row); the BF16 window is then read back as the rotated row, not as
+# s16 * u16.
+# ---------------------------------------------------------------------------
+
+D = 128
+PAGE = 16
+
+
+class OtsHeadCache:
+    """OScaR cache of one sequence, one KV head, after ``length`` tokens.
+
+    k_bits, v_bits: post-RoPE bf16 bits [length, D]; r_k, r_v: fp32 [D, D] or
+    ``rotate.Hadamard``; kappa_v: the value clip ratio; group: G (key block
+    length in tokens and value group width in channels).
+    """
+
+    def __init__(self, k_bits, v_bits, r_k, r_v, kappa_v, group, s_sink, s_keep, s_flush):
+        from . import placement, quant
+        assert s_flush % group == 0, "key blocks must not straddle a flush"
+        self.length = k_bits.shape[0]
+        self.group = group
+        self.s_sink, self.s_keep, self.s_flush = s_sink, s_keep, s_flush
+        self.k_rot = rotate.rotate_rows_to_bf16(k_bits, r_k)
+        self.v_rot = rotate.rotate_rows_to_bf16(v_bits, r_v)
+        self.sink, self.int2, self.recent = placement.segments(self.length, s_sink, s_keep, s_flush)
+        a, b = self.int2
+        nq = b - a
+        assert nq % group == 0
+        # keys: per-token scale and normalized rows, then one (Delta, z) per
+        # channel per block of `group` tokens
+        self.ks16, u16 = ots_scale(self.k_rot[a:b]) if nq else (np.zeros(0, np.uint16),
+                                                                np.zeros((0, D), np.uint16))
+        nb = nq // group
+        self.kc = np.zeros((nq, D), np.uint8)
+        self.kd16 = np.zeros((nb, D), np.uint16)
+        self.kz16 = np.zeros((nb, D), np.uint16)
+        for blk in range(nb):
+            r = slice(blk * group, (blk + 1) * group)
+            self.kc[r], self.kd16[blk], self.kz16[blk] = channel_quantize(u16[r])
+        # values: per token, groups of `group` channels (O3)
+        self.vc, self.vs, self.vz = quant.quantize_rows(bf16_bits_to_f64(self.v_rot[a:b]), kappa_v,
+                                                        group)
+        k_dec = bf16_bits_to_f64(self.k_rot)
+        v_dec = bf16_bits_to_f64(self.v_rot)
+        if nq:
+            s = bf16_bits_to_f64(self.ks16)
+            for blk in range(nb):
+                r = slice(blk * group, (blk + 1) * group)
+                k_dec[a + blk * group:a + (blk + 1) * group] = (
+                    s[r, None] * channel_dequant(self.kc[r], self.kd16[blk], self.kz16[blk]))
+            v_dec[a:b] = quant.dequant_rows(self.vc, self.vs, self.vz, group)
+        self.k_dec, self.v_dec = k_dec, v_dec
+
+    def dequant_f32(self):
+        """Decoded rows as fp32 (one rounding of the fp64 values) [length, D]."""
+        return self.k_dec.astype(np.float32), self.v_dec.astype(np.float32)
+
+    def page_block(self, m):
+        """Expected OTS page-head block of logical INT2 page m, and its valid slots."""
+        from . import layout
+        a, b = self.int2
+        p0 = self.s_sink + PAGE * m
+        n_valid = max(0, min(PAGE, b - p0))
+        r = slice(p0 - a, p0 - a + n_valid)
+        ng = D // self.group
+        kc = np.zeros((PAGE, D), np.uint8)
+        vc = np.zeros((PAGE, D), np.uint8)
+        ks = np.zeros(PAGE, np.uint16)
+        vs = np.zeros((PAGE, ng), np.uint16)
+        vz = np.zeros_like(vs)
+        kc[:n_valid], vc[:n_valid], ks[:n_valid] = self.kc[r], self.vc[r], self.ks16[r]
+        vs[:n_valid], vz[:n_valid] = self.vs[r], self.vz[r]
+        blk = (PAGE * m) // self.group                       # key block of this page
+        half = ((PAGE * m) % self.group) // PAGE             # which channel half it stores
+        ch = slice(64 * half, 64 * half + 64)
+        return layout.pack_ots_page_head(kc, vc, ks, self.kd16[blk, ch], self.kz16[blk, ch], vs, vz,
+                                         self.group), n_valid
+
+    def window_rows(self):
+        """{(block, slot): position} of every valid window slot."""
+        from . import placement
+        sb = -(-self.s_sink // PAGE)
+        cap = placement.ring_capacity(self.s_keep, self.s_flush)
+        out = {}
+        for p in range(*self.sink):
+            out[(p // PAGE, p % PAGE)] = p
+        for p in range(*self.recent):
+            r = (p - self.s_sink) % cap
+            out[(sb + r // PAGE, r % PAGE)] = p
+        return out
