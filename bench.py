@@ -389,7 +389,24 @@ def timed_region(enqueue, n, hold_cycles, retries=2):
     return t_start.elapsed_time(t_end) / n, host, bound
 
 
-def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0):
+def timed_regions(enqueue, n, region, hold_cycles):
+    """timed_region over n calls cut into regions of at most `region` calls
+    (the HIP runtime stops accepting launches once about 50 calls with the
+    decode kernels' large argument tables are queued, so a long queue behind
+    the spin kernel would time the host).  Returns (ms per call, host
+    seconds, host-bound in any region)."""
+    tot_ms = host = 0.0
+    bound = False
+    for r0 in range(0, n, region):
+        m = min(region, n - r0)
+        ms, h, b = timed_region(lambda j: enqueue(r0 + j), m, hold_cycles)
+        tot_ms += ms * m
+        host += h
+        bound = bound or b
+    return tot_ms / n, host, bound
+
+
+def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0, region=0):
     """Decode steps of every row of workload w, cycling through n_layers
     copies of the populated cache (``rotation``: the cache's rotation kind).
 
@@ -399,7 +416,8 @@ def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0)
     the same number with events around the append, split and merge launches
     of each step.  With graph_steps > 0 a further `graph_steps` steps are
     captured into one HIP graph and replayed `graph_reps` times (timed as a
-    whole), which removes the host's launch path from the figure."""
+    whole), which removes the host's launch path from the figure.  region > 0:
+    both passes time their steps in regions of at most `region` steps."""
     import torch
     from ultra_bit_kv_amd import SeqBatch, as_bf16
 
@@ -476,10 +494,11 @@ def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0)
     hold = hold_for(host_step * steps * 4)   # pass 2 also records 4 events per step
     # pass 1: the whole step, no event records between its launches (each
     # record adds a gap to the stream)
-    ms_step, host1, bound1 = timed_region(lambda j: step(warm + j), steps, hold)
+    reg = region if region > 0 else steps
+    ms_step, host1, bound1 = timed_regions(lambda j: step(warm + j), steps, reg, hold)
     # pass 2: the same number of steps with events around each launch
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
-    ms_step_ev, host2, _ = timed_region(lambda j: step(warm + steps + j, evs[j]), steps, hold)
+    ms_step_ev, host2, _ = timed_regions(lambda j: step(warm + steps + j, evs[j]), steps, reg, hold)
     app = [a.elapsed_time(b) for a, b, c, d in evs]
     split = [b.elapsed_time(c) for a, b, c, d in evs]
     merge = [c.elapsed_time(d) for a, b, c, d in evs]
@@ -494,6 +513,7 @@ def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0)
            "split_pct": pct(split), "step_pct": pct(whole),
            "bytes": float(np.mean(byts)), "setup_s": setup_s, "warm": warm,
            "host_ms_per_step": 1e3 * host1 / steps, "hold_ms": 1e3 * hold / CLOCK_HZ,
+           "steps_per_timed_region": reg,
            # pass 1 waited on the host if the host took longer to queue the
            # steps than the spin kernel held the GPU (after retries)
            "host_bound": bound1}
@@ -532,7 +552,7 @@ def leg_summary(m, peak_probe=None):
         "split_GBs": gbs, "split_frac_of_peak": gbs / PEAK_HBM_GBS,
         "decode_call_GBs": m["bytes"] / (m["dec_ms"] * 1e-3) / 1e9,
         "host_ms_per_step": m["host_ms_per_step"], "gpu_hold_ms": m["hold_ms"],
-        "host_bound": m["host_bound"],
+        "host_bound": m["host_bound"], "steps_per_timed_region": m["steps_per_timed_region"],
     }
     if peak_probe:
         out["split_frac_of_read_probe"] = gbs / peak_probe
@@ -760,18 +780,18 @@ def main():
         # from a HIP graph (no host launch path)
         log(f"bs1 leg: {ls} steps, {args.bs1_layers} layers")
         b = measure(get("c2_qwen3_8b_bs1"), args.bs1_layers, ls, args.warmup,
-                    graph_steps=args.bs1_layers, graph_reps=20)
+                    graph_steps=args.bs1_layers, graph_reps=20, region=16)
         res["bs1"] = leg_summary(b, probe)
         res["bs1"]["layers_cycled"] = args.bs1_layers
     if "c1" in legs:
         log("c1 leg")
-        c1 = measure(get("c1_tiny"), 8, ls, args.warmup)
+        c1 = measure(get("c1_tiny"), 8, ls, args.warmup, region=16)
         res["c1"] = leg_summary(c1, probe)
         res["c1"]["layers_cycled"] = 8
         res["c1"]["note"] = "0.14 MB per call: resident in the 256 MB MALL (launch-latency bound)"
     if "c4" in legs:
         log("c4 leg")
-        c4 = measure(get("c4_long_bs1"), 4, ls, args.warmup, graph_steps=4, graph_reps=20)
+        c4 = measure(get("c4_long_bs1"), 4, ls, args.warmup, graph_steps=4, graph_reps=20, region=16)
         res["c4"] = leg_summary(c4, probe)
         res["c4"]["layers_cycled"] = 4
     if "c5" in legs:

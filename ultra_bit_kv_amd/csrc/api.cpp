@@ -78,6 +78,7 @@ DecodePlan head_passes(const oscar_kv_config& c) {
   p.passes = (g + hp - 1) / hp;
   const int waves = c.num_kv_heads / kh;   // KV head groups, one wave each
   p.wh = waves % 4 == 0 ? 4 : (waves % 2 == 0 ? 2 : 1);
+  p.ring = 2;
   p.quota = 1;
   p.smax = 1;
   return p;
@@ -191,7 +192,8 @@ int decode_slots_per_cu(const CacheArgs& a, const DecodePlan& plan, bool bf16) {
   int dev = 0;
   (void)hipGetDevice(&dev);
   const long long key =
-      ((((((long long)dev * 2 + (bf16 ? 1 : 0)) * 8 + a.ng) * 32 + plan.hp) * 8 + plan.wh) * 4 + plan.kh);
+      (((((((long long)dev * 2 + (bf16 ? 1 : 0)) * 8 + a.ng) * 32 + plan.hp) * 8 + plan.wh) * 4 +
+        plan.kh) * 8 + plan.ring);
   std::lock_guard<std::mutex> lock(mu);
   for (const auto& m : memo)
     if (m.first == key) return m.second;

@@ -55,6 +55,15 @@ __device__ __forceinline__ float f16hi(uint32_t w) {
 }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// hi16(w) (an fp16 value) times b in fp32 with one rounding, as one
+// mixed-precision multiply-add (a zero product gives +0).  w must not come
+// straight from the exp unit or a matrix instruction (no wait states).
+__device__ __forceinline__ float f16hi_mul(uint32_t w, float b) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(b));
+  return r;
+}
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 
 // Bit pattern of the largest fp16 scale (low halves) of eight scale | zero
@@ -70,19 +79,23 @@ __device__ __forceinline__ uint32_t max_scale_bits(const u32x4& a, const u32x4& 
 
 // The products a * lo16(wa) and b * lo16(wb) (fp16 scales) as fp16 pairs
 // split in two: hi = the products rounded to fp16, lo = the remainders
-// rounded to fp16, so hi + lo carries about 22 significant bits.
+// a * s - hi (one fused multiply-add each) rounded to fp16, so hi + lo
+// carries about 22 significant bits.  Mixed-precision fused multiply-adds
+// that write one fp16 half each; the leading s_nop gives a and b, which
+// come from the exp unit, the wait state such a result needs before a VALU
+// reads it.
 __device__ __forceinline__ void mul_by_f16lo_split(float a, uint32_t wa, float b, uint32_t wb,
                                                    uint32_t& hi, uint32_t& lo) {
-  const half2_t ha = __builtin_bit_cast(half2_t, wa);
-  const half2_t hb = __builtin_bit_cast(half2_t, wb);
-  const float pa = a * (float)ha.x, pb = b * (float)hb.x;
-  half2_t h, l;
-  h.x = (_Float16)pa;
-  h.y = (_Float16)pb;
-  l.x = (_Float16)(pa - (float)h.x);
-  l.y = (_Float16)(pb - (float)h.y);
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, l);
+  uint32_t h, l;
+  asm("s_nop 0\n\t"
+      "v_fma_mixlo_f16 %0, %2, %3, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mixhi_f16 %0, %4, %5, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel:[0,0,0] op_sel_hi:[0,1,1]\n\t"
+      "v_fma_mixhi_f16 %1, %4, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,1,1]"
+      : "=&v"(h), "=&v"(l)
+      : "v"(a), "v"(wa), "v"(b), "v"(wb));
+  hi = h;
+  lo = l;
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
@@ -91,9 +104,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
 }
 
 struct SoftmaxState {
-  float m;   // running max (log2 domain), same in every lane of a column
-  float l;   // this lane's share of the running sum
-  float z;   // this lane's share of sum_t p_t * zero_v[t][group]
+  float m;    // running max (log2 domain), same in every lane of a column
+  float l;    // this lane's share of the running sum
+  float z;    // this lane's share of sum_t p_t * zero_v[t][group]
+  float mr;   // the max subtracted before exp2: m, or 0 while m = -inf
 };
 
 // Online-softmax update with a lazy max.  x holds logits in raw units; the
@@ -104,11 +118,13 @@ template <int N>
 __device__ __forceinline__ void softmax_step(const float (&x)[N], float scale, float (&p)[N],
                                              SoftmaxState& st, float4_t (&acc)[8],
                                              float slack = 8.0f) {
-  float tmax = x[0];
+  float lmax = x[0];
 #pragma unroll
-  for (int k = 1; k < N; ++k) tmax = fmaxf(tmax, x[k]);
-  tmax = rows_max(tmax) * scale;
-  if (__any(tmax > st.m + slack)) {
+  for (int k = 1; k < N; ++k) lmax = fmaxf(lmax, x[k]);
+  // a column's maximum passes the bound exactly when one of its lanes'
+  // maxima does (scale > 0), so the cross-lane reduction only runs then
+  if (__any(lmax * scale > st.m + slack)) {
+    const float tmax = rows_max(lmax) * scale;
     const float m_new = fmaxf(st.m, tmax);
     const float alpha = m_new > st.m ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.0f;
 #pragma unroll
@@ -116,11 +132,11 @@ __device__ __forceinline__ void softmax_step(const float (&x)[N], float scale, f
     st.l *= alpha;
     st.z *= alpha;
     st.m = m_new;
+    st.mr = m_new == kNegInf ? 0.0f : m_new;
   }
-  const float mref = st.m == kNegInf ? 0.0f : st.m;
 #pragma unroll
   for (int k = 0; k < N; ++k) {
-    p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k], scale, -mref));
+    p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k], scale, -st.mr));
     st.l += p[k];
   }
 }
@@ -140,6 +156,26 @@ __device__ __forceinline__ void set_priority(int remaining, int total, int round
   if (p >= 3) __builtin_amdgcn_s_setprio(3);
   else if (p == 2) __builtin_amdgcn_s_setprio(2);
   else if (p == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+// The same priorities for a fixed total and round, as thresholds on the
+// remaining work: the level is the number of thresholds reached.
+struct PrioSteps {
+  int r1, r2, r3;
+};
+__device__ __forceinline__ PrioSteps prio_steps(int total, int round) {
+  const int rr = round < 3 ? round : 3;
+  auto at = [&](int level) {   // least remaining work whose level is >= `level`
+    const int x = 3 * level - rr;
+    return x > 0 ? (total * x + 12) / 12 : 0;
+  };
+  return PrioSteps{at(1), at(2), at(3)};
+}
+__device__ __forceinline__ void set_priority(const PrioSteps& t, int remaining) {
+  if (remaining >= t.r3) __builtin_amdgcn_s_setprio(3);
+  else if (remaining >= t.r2) __builtin_amdgcn_s_setprio(2);
+  else if (remaining >= t.r1) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
 }
 

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(64 * WH) void bf16_decode_kernel(CacheArgs c, SeqAr
   float4_t acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-  SoftmaxState st{kNegInf, 0.0f, 0.0f};
+  SoftmaxState st{kNegInf, 0.0f, 0.0f, 0.0f};
 
   struct Page {
     u32x4 k[4], v[4];

@@ -30,21 +30,69 @@
 
 namespace oscar {
 
-constexpr int kPrefetch = 2;   // page pairs in flight per wave ahead of the one processed
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+
+// One direct-to-LDS load: each lane's 16 bytes at src + OFF go to
+// dst + OFF + 16 * lane (dst is the same for the whole wave; the immediate
+// offset applies to both addresses).
+template <int OFF = 0>
+__device__ __forceinline__ void load_lds16(const uint8_t* src, lds_u8* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, OFF, 0);
+}
+
+// A wave-uniform address kept in scalar registers, so that a per-lane 32-bit
+// offset added to it gives a scalar-base + vector-offset load address.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+
+// Bytes of one page for the KH consecutive KV heads of a wave (their
+// page-head blocks are contiguous in a page), and the direct-to-LDS loads
+// (1 KB per wave instruction, 16 bytes per lane) that bring it in.
+template <int NG, int KH>
+struct PairGeom {
+  static constexpr int PB = 1024 + 128 * NG;         // page-head block
+  static constexpr int RB = KH * PB;                  // one page of the wave's heads
+  static constexpr int NI = (RB + 1023) / 1024;       // loads per page
+  static constexpr int LAST_LANES = (RB - 1024 * (NI - 1)) / 16;   // lanes of the last load
+  static constexpr int PAIR_LOADS = 2 * NI;
+  static constexpr int WIN_LOADS = 4;                 // one window half: 16 rows x 256 B
+  static constexpr int SLOT = 2 * RB > 4096 ? 2 * RB : 4096;
+};
 
 // Work-group = one work item (sequence, context split, group of WH adjacent
-// KV heads, query-head pass); items are numbered sequence-major, then split,
-// then head group, and the launch has exactly one work-group per item.  A
-// work-group finds its item from a prefix sum over the sequences' item
-// counts.  Wave w owns KV head WH * group + w; all waves walk the same pages,
-// so each page is fetched as one contiguous run of WH page-head blocks.
-template <int NG, int HP, int KH, int PF, int WH>
+// KV head groups, query-head pass); items are numbered sequence-major, then
+// split, then head group, and the launch has exactly one work-group per
+// item.  Wave w owns KV heads KH (WH group + w) ...; all waves walk the same
+// blocks and pages.
+//
+// Everything a wave reads from the cache streams through a ring of D slots
+// in LDS, one ring per wave, filled by direct-to-LDS loads (data in flight
+// costs no registers): first the split's BF16 window blocks, each as two
+// ring items per KV head of the wave (its 16 K rows, then its 16 V rows),
+// then its INT2 page pairs (one item: the wave's KV heads' bytes of both
+// pages).  Item j + D is requested as soon as item j has been read out of its
+// slot into registers, so D - 1 items are in flight while one is processed.
+// Each item is waited for with an exact vmcnt: the loads of the items after
+// it are counted from their types (a window half is 4 loads, a pair 2 NI),
+// the tail re-requests the last item so the counts stay exact, and no other
+// vector memory access of the wave is outstanding meanwhile.
+template <int NG, int HP, int KH, int WH, int D>
 __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqArgs s, int quota,
                                                               int passes, int smax, int cus, ItemOrder order,
                                                               const uint16_t* __restrict__ q_rot,
                                                               float* __restrict__ partials) {
+  using G = PairGeom<NG, KH>;
   constexpr int PW = rec_words(HP);   // floats per partial record
   constexpr int NT = 64 * WH;
+  static_assert(D >= 2 && D <= 4, "ring depth");
+  static_assert((D - 1) * G::PAIR_LOADS <= 63, "vmcnt limit");
+  __shared__ __align__(16) uint8_t s_ring[WH * D * G::SLOT];
   __shared__ __align__(8) int s_pages[kMaxWgPages];
   __shared__ int s_wsum[WH];
   __shared__ int s_item[4];   // sequence, item within it, its slot and length
@@ -99,29 +147,13 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int wb = (int)((unsigned)(split * n_wu) / (unsigned)n_split);
   const int we = (int)((unsigned)((split + 1) * n_wu) / (unsigned)n_split);
   const int total_units = max(1, (pe - pb) + kWinCost * (we - wb));
-  const int rnd = blockIdx.x / cus;   // dispatch round on its compute unit
-  set_priority(total_units, total_units, rnd);
-  const uint16_t* wbase = c.win + ((size_t)(row_ok ? slot : 0) * c.hkv + hw) * c.win_blocks *
-                                      (2 * kPage * kD);
-  struct Win {
-    u32x4 kl[4], vl[4];
-    int u, k;   // block, KV head of the wave
-  };
+  const PrioSteps prio = prio_steps(total_units, blockIdx.x / cus);   // (dispatch round on its CU)
+  set_priority(prio, total_units);
   auto win_block = [&](int u) { return u < sb_n ? u : c.sink_blocks + (u - sb_n); };
   auto win_slot_ok = [&](int u, int t) {
     if (u < sb_n) return kPage * u + t < nsink;
     const int off = (kPage * (u - sb_n) + t - b0 + c.ring_cap) % c.ring_cap;
     return off < cnt;
-  };
-  auto load_win = [&](int u, int k, Win& W) {
-    W.u = u;
-    W.k = k;
-    const uint16_t* bp = wbase + ((size_t)k * c.win_blocks + win_block(u)) * (2 * kPage * kD);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      W.kl[k] = *(const u32x4*)(bp + r16 * kD + 32 * qd + 8 * k);
-      W.vl[k] = *(const u32x4*)(bp + kPage * kD + 32 * (16 * qd + r16) + 8 * k);
-    }
   };
   // ---- per-lane MFMA column n = (group gi, KV head kh of the wave, head hl of the pass)
   const int n = r16, gi = n / (KH * HP), kh = (n / HP) % KH, hl = n % HP;
@@ -133,6 +165,100 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const float K1 = C2 * 16777216.0f;                              // undo the 2^-24 code scaling
 
   // ---- the lane's 32 query channels straight into registers; the split's page ids to LDS
+  // ---- the ring of this wave.  Its address is passed through an empty asm
+  // statement: the compiler then cannot assume anything about the ring's
+  // contents, which only the direct-to-LDS loads write.
+  lds_u8* ring = (lds_u8*)(s_ring + wave * (D * G::SLOT));
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+s"(ring)::"memory");   // (an SGPR operand: device code only)
+#endif
+  const int np = min(pe - pb, kMaxPairsPerSplit);                 // pairs of this split
+  const int nwin = 2 * (we - wb) * KH;                            // window items (K, V halves)
+  const int n_items = nwin + np;
+  const size_t page_stride = (size_t)c.hkv * G::PB;
+  const uint8_t* wave_base = c.pages + (size_t)hw * G::PB;        // the wave's first head of page 0
+  const uint8_t* win_base = (const uint8_t*)(c.win + ((size_t)(row_ok ? slot : 0) * c.hkv + hw) *
+                                                         c.win_blocks * (2 * kPage * kD));
+  // page ids of pair k (the split's last pair for k >= np); -1: unmapped
+  auto pair_ids = [&](int k) { return *(const u32x2*)&s_pages[2 * max(0, min(k, np - 1))]; };
+  // Window half placement in LDS: 16-byte chunk (t, j) of a half (row t, bytes
+  // 16 j .. 16 j + 15 of its 256) sits at chunk 16 t + (j ^ t), so the 16
+  // lanes that read one column of chunks hit 16 different bank groups.  Load
+  // m of a half writes LDS chunks 64 m + lane, i.e. row t = 4 m + lane / 16;
+  // woff[m] is where that lane's (swizzled) chunk of row t lies in the half.
+  uint32_t woff[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t jj = lane & 15, t0 = lane >> 4;
+    woff[m] = 256 * t0 + 16 * (jj ^ (t0 + 4 * m));
+  }
+  auto request_win = [&](int item, lds_u8* dst) {
+    const int tt = item >> 1, half = item & 1;
+    const int u = wb + tt / KH, k = tt % KH;
+    const uint8_t* src = uniform_ptr(win_base + ((size_t)k * c.win_blocks + win_block(u)) *
+                                                    (4 * kPage * kD) + half * (2 * kPage * kD));
+    load_lds16<0>(src + woff[0], dst);
+    load_lds16<1024>(src + woff[1], dst);
+    load_lds16<2048>(src + woff[2], dst);
+    load_lds16<3072>(src + woff[3], dst);
+  };
+  auto request_pair = [&](u32x2 ids, lds_u8* dst) {
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      int ph = __builtin_amdgcn_readfirstlane((int)ids[pg]);
+      if (ph < 0) ph = 0;   // unmapped: any valid page, its logits are masked
+      const uint8_t* src = uniform_ptr(wave_base + (size_t)ph * page_stride) + (uint32_t)(16 * lane);
+      lds_u8* d = dst + pg * G::RB;
+      load_lds16<0>(src, d);
+      if (G::NI > 2 || lane < G::LAST_LANES) load_lds16<1024>(src, d);
+      if constexpr (G::NI > 2) {
+        if (G::NI > 3 || lane < G::LAST_LANES) load_lds16<2048>(src, d);
+      }
+      if constexpr (G::NI > 3) {
+        static_assert(G::NI == 4, "at most four loads per page");
+        if (lane < G::LAST_LANES) load_lds16<3072>(src, d);
+      }
+    }
+  };
+  // request item j (the last item for j >= n_items) into slot j % D
+  auto request = [&](int j, u32x2 ids) {
+    const int jj = min(j, n_items - 1);
+    lds_u8* dst = ring + (j % D) * G::SLOT;
+    if (jj < nwin) request_win(jj, dst);
+    else request_pair(ids, dst);
+  };
+  // wait until item j is in its slot: the D - 1 items after it (clamped to
+  // the last item) may still be loading
+  auto wait_item = [&](int j) {
+    const int wins = max(0, min(D - 1, nwin - (j + 1)));   // window halves among them
+    const int wins_c = n_items - 1 < nwin ? D - 1 : wins;   // all of them when the last item is one
+    if constexpr (D == 2) {
+      if (wins_c) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::WIN_LOADS) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::PAIR_LOADS) : "memory");
+    } else if constexpr (D == 3) {
+      if (wins_c == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::WIN_LOADS) : "memory");
+      else if (wins_c == 1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::WIN_LOADS + G::PAIR_LOADS) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::PAIR_LOADS) : "memory");
+    } else {
+      if (wins_c == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * G::WIN_LOADS) : "memory");
+      else if (wins_c == 2)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::WIN_LOADS + G::PAIR_LOADS) : "memory");
+      else if (wins_c == 1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::WIN_LOADS + 2 * G::PAIR_LOADS) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * G::PAIR_LOADS) : "memory");
+    }
+  };
+
+  // the first window items do not depend on the page ids: request them
+  // before the query and page-id loads (requests stay in item order)
+  const int d_pre = np == 0 ? D : min(D, nwin);
+  if (n_items > 0) {
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < d_pre) request(d, u32x2{0u, 0u});
+  }
+
   u32x4 wq[4];
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -141,18 +267,15 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) wq[cc] = colv ? *(const u32x4*)(qp + 8 * cc) : z;
   }
-  // The split's first BF16 window block is loaded before anything that waits
-  // on the block table: the window blocks are processed first, while the
-  // page ids and the first INT2 page pairs are on their way.
-  const int nw = (we - wb) * KH;   // window blocks of this wave (each KV head in turn)
-  Win wa, wn;
-  if (nw > 0) load_win(wb, 0, wa);
   const int n_wg_pages = min(2 * (pe - pb), kMaxWgPages);
+  int bad_ids = 0;   // a page holding INT2 tokens without a valid page id
   for (int t = tid; t < n_wg_pages; t += 64 * WH) {
     const int pg = 2 * pb + t;
     int ph = -1;
     if (pg < n_pages && pg < c.max_pages) ph = bt[pg];
-    s_pages[t] = (ph >= 0 && ph < c.num_pages) ? ph : -1;
+    const bool ok = ph >= 0 && ph < c.num_pages;
+    s_pages[t] = ok ? ph : -1;
+    bad_ids |= (!ok && pg < n_pages);
   }
   // group sums of q' for the zero-point term: each lane adds its 32 channels
   // if they lie in its column's group, then the four lanes of the column add up
@@ -167,8 +290,19 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   qsum = rows_sum(qsum);
   // INT2 logits in raw units x = s * D + z * qsum * 2^-24, log2 logit = K1 * x
   const float qz = colv ? qsum * (1.0f / 16777216.0f) : 0.0f;
-  __syncthreads();   // page ids visible
+  // page ids visible; ids_ok: every page of the split's pairs with INT2
+  // tokens is mapped, so only the last pairs (past S_quant) need masks
+  const bool ids_ok = !__syncthreads_or(bad_ids);
 
+  if (n_items > 0) {
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d >= d_pre) request(d, pair_ids(d - nwin));
+  }
+
+  // ---- B operands: the bf16 query for the window blocks, and for the INT2
+  // codes q' scaled by 4^-v (chunk cc, K index 8 qd + 2v + e <-> channel
+  // 32 qd + 16 (cc/2) + 4 (cc%2) + v + 8 e), zero outside the column's group
   bf16x8 bw[4];
   half8 bq[4];
 #pragma unroll
@@ -178,7 +312,6 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     for (int v = 0; v < 4; ++v) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        // K index 8 qd + 2v + e of chunk cc <-> channel 32 qd + cl
         const int cl = 16 * (cc >> 1) + 4 * (cc & 1) + v + 8 * e;
         const uint32_t word = wq[cl >> 3][(cl & 7) >> 1];
         const uint32_t bits = (cl & 1) ? (word >> 16) : (word & 0xFFFFu);
@@ -187,211 +320,199 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
       }
     }
   }
-
-  // B operands of the q.k MFMAs on KV head k: this column's q' if it belongs to head k
-  half8 bqk[KH][4];
-#pragma unroll
-  for (int k = 0; k < KH; ++k)
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) bqk[k][cc] = (KH == 1 || kh == k) ? bq[cc] : half8{};
-
-  const size_t head_off = (size_t)hw * c.page_bytes;              // the wave's first head
-  const size_t col_off = (size_t)kh * c.page_bytes;               // this column's head, relative
-  const size_t page_stride = (size_t)c.hkv * c.page_bytes;
   const int gsel = gi < NG ? gi : 0;                              // in-bounds group for params
 
   float4_t acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-  SoftmaxState st{kNegInf, 0.0f, 0.0f};
+  SoftmaxState st{kNegInf, 0.0f, 0.0f, 0.0f};
 
-  struct Pair {
-    u32x2 ka[KH], kb[KH], va[KH], vb[KH];   // codes of each KV head of the wave
-    u32x4 kpa, kpb, vpa, vpb;                // scale / zero of this column's head and group
-    int tok;      // INT2 token index of slot 0 of page A
-    bool oka, okb;
-  };
-  const int np = min(pe - pb, kMaxPairsPerSplit);                 // pairs of this split
-  const int koff = (r16 * 8 + 2 * qd) * 4;
-  const int poff = 1024 + 4 * (16 * gsel + 4 * qd);
-  const int vpoff = poff + 64 * NG;
-  // Page ids of the next pair to load, read from LDS one load ahead so the
-  // LDS latency stays off the path that issues the page loads (loads are
-  // issued in order k = 0, 1, 2, ...; the tail re-reads the last pair).
-  int nx_a = 0, nx_b = 0;
-  auto fetch_ids = [&](int k) {
-    const int local = min(k, np - 1);
-    nx_a = s_pages[2 * local];
-    nx_b = s_pages[2 * local + 1];
-  };
-  auto load_pair = [&](int k, Pair& d) {
-    const int local = min(k, np - 1);
-    int pa = nx_a, pbq = nx_b;
-    fetch_ids(k + 1);
-    d.oka = pa >= 0;
-    d.okb = pbq >= 0;
-    if (!d.oka) pa = 0;
-    if (!d.okb) pbq = pa;
-    d.tok = 32 * (pb + local);
-    const uint8_t* A = c.pages + (size_t)pa * page_stride + head_off;
-    const uint8_t* B = c.pages + (size_t)pbq * page_stride + head_off;
+  const int koff = (r16 * 8 + 2 * qd) * 4;                        // K codes of this lane
+  const int poff = 1024 + 4 * (16 * gsel + 4 * qd);               // K params of this lane's column
+  const int vpoff = poff + 64 * NG;                               // V params
+
+  // ---- BF16 window blocks (true scale), each KV head of the wave in turn
+  // K half: lane (r16, qd) reads row r16, channels 32 qd + 8 cc .. + 7, i.e.
+  // chunk (r16, 4 qd + cc); V half: the bf16 P.V operand order of the window
+  // layout, chunk (lane / 4 .. , ...): lane (r16, qd) reads chunks
+  // 4 (16 qd + r16) + cc, i.e. row t = (16 qd + r16) / 4, j = 4 ((16 qd + r16) % 4) + cc.
+  short4_t win_phi = {0, 0, 0, 0}, win_plo = {0, 0, 0, 0};
+  for (int it_w = 0; it_w < nwin; ++it_w) {
+    const int tt = it_w >> 1, half = it_w & 1;
+    const int u = wb + tt / KH, k = tt % KH;
+    set_priority(prio, kWinCost * (we - u) + np);
+    wait_item(it_w);
+    const lds_u8* P = ring + (it_w % D) * G::SLOT;
+    u32x4 rv[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      int t, j;
+      if (half == 0) {
+        t = r16;
+        j = 4 * qd + cc;
+      } else {
+        const int a = 16 * qd + r16;
+        t = a >> 2;
+        j = 4 * (a & 3) + cc;
+      }
+      rv[cc] = *(lds_u32x4*)(P + 16 * (16 * t + (j ^ t)));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    request(it_w + D, pair_ids(it_w + D - nwin));
+    const bool live = __any(win_slot_ok(u, r16));   // uniform
+    if (!live) continue;
+    if (half == 0) {
+      float4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rv[cc]), bw[cc], d,
+                                                    0, 0, 0);
+      float x[4], p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)   // only the columns of the block's KV head
+        x[r] = ((KH == 1 || kh == k) && win_slot_ok(u, 4 * qd + r)) ? d[r] : kNegInf;
+      softmax_step<4>(x, C2, p, st, acc);
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        hi[r] = f32_to_bf16_rne(p[r]);
+        lo[r] = f32_to_bf16_rne(p[r] - __uint_as_float(hi[r] << 16));
+      }
+      win_phi = short4_t{(short)hi[0], (short)hi[1], (short)hi[2], (short)hi[3]};
+      win_plo = short4_t{(short)lo[0], (short)lo[1], (short)lo[2], (short)lo[3]};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x4 src = rv[j >> 1];
+        const u32x2 pr = (j & 1) ? u32x2{src[2], src[3]} : u32x2{src[0], src[1]};
+        const short4_t a = __builtin_bit_cast(short4_t, pr);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, win_phi, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, win_plo, acc[j], 0, 0, 0);
+      }
+    }
+  }
+
+  // q.k of one page (16 tokens) for the wave's KV heads: each head's codes
+  // against the same query operand; each column keeps the sum of its head
+  auto qk_page = [&](const u32x2 (&kw)[KH]) {
+    float4_t sel = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KH; ++k) {
-      d.ka[k] = *(const u32x2*)(A + k * c.page_bytes + koff);
-      d.kb[k] = *(const u32x2*)(B + k * c.page_bytes + koff);
-      d.va[k] = *(const u32x2*)(A + k * c.page_bytes + 512 + 8 * lane);
-      d.vb[k] = *(const u32x2*)(B + k * c.page_bytes + 512 + 8 * lane);
-    }
-    d.kpa = *(const u32x4*)(A + col_off + poff);
-    d.kpb = *(const u32x4*)(B + col_off + poff);
-    d.vpa = *(const u32x4*)(A + col_off + vpoff);
-    d.vpb = *(const u32x4*)(B + col_off + vpoff);
-  };
-
-  auto qk_tile = [&](const u32x2 (&kw)[KH]) {
-    float4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < KH; ++k)
+      float4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         uint32_t w = (cc < 2) ? kw[k][0] : kw[k][1];
         if (cc & 1) w >>= 8;
         const u32x4 v = {w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u, w & 0x00C000C0u};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, v), bqk[k][cc], d, 0,
-                                                   0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, v), bq[cc], d, 0, 0, 0);
       }
-    return d;
+      if (KH == 1 || kh == k) sel = d;
+    }
+    return sel;
   };
-
-  auto process_pair = [&](const Pair& d) {
-    const float4_t da = qk_tile(d.ka);
-    const float4_t db = qk_tile(d.kb);
-    float x[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = __builtin_fmaf(f16lo(d.kpa[r]), da[r], f16hi(d.kpa[r]) * qz);
-      x[4 + r] = __builtin_fmaf(f16lo(d.kpb[r]), db[r], f16hi(d.kpb[r]) * qz);
-    }
-    if constexpr (NG > 1) {   // sum the group partials: lanes n, n +- KH HP, ... of a 16-lane row
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if constexpr (KH * HP <= 8) x[k] += row_ror<8>(x[k]);
-        if constexpr (KH * HP <= 4) x[k] += row_ror<4>(x[k]);
-        if constexpr (KH * HP <= 2) x[k] += row_ror<2>(x[k]);
-        if constexpr (KH * HP <= 1) x[k] += row_ror<1>(x[k]);
-      }
-    }
-    if (!(d.oka && d.okb && d.tok + 32 <= nq)) {   // the pair holds slots past S_quant
-      const int ta = d.tok + 4 * qd;   // INT2 token index of row 0 of tile A in this lane
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (!(d.oka && ta + r < nq)) x[r] = kNegInf;
-        if (!(d.okb && ta + 16 + r < nq)) x[4 + r] = kNegInf;
-      }
-    }
-    // P' = p * scale_v enters the MFMA as fp16: with p <= 2^8 (the lazy
-    // max) a value scale of 128 or more could overflow it, so such a pair
-    // takes the exact max (p <= 1, P' <= scale <= 65504)
-    const bool big_scale = max_scale_bits(d.vpa, d.vpb) >= 0x5800u;   // fp16 128.0
-    float p[8];
-    softmax_step<8>(x, K1, p, st, acc, __any(big_scale) ? 0.0f : 8.0f);
-    uint32_t ph[4], pl[4];
-    mul_by_f16lo_split(p[0], d.vpa[0], p[1], d.vpa[1], ph[0], pl[0]);
-    mul_by_f16lo_split(p[2], d.vpa[2], p[3], d.vpa[3], ph[1], pl[1]);
-    mul_by_f16lo_split(p[4], d.vpb[0], p[5], d.vpb[1], ph[2], pl[2]);
-    mul_by_f16lo_split(p[6], d.vpb[2], p[7], d.vpb[3], ph[3], pl[3]);
-    // B operands of the P.V MFMAs on KV head k: this column's P' if it belongs to head k
-    half8 pv[KH], pvl[KH];
-#pragma unroll
-    for (int k = 0; k < KH; ++k) {
-      const bool mine = KH == 1 || kh == k;
-      pv[k] = __builtin_bit_cast(half8, mine ? u32x4{ph[0], ph[1], ph[2], ph[3]} : u32x4{});
-      pvl[k] = __builtin_bit_cast(half8, mine ? u32x4{pl[0], pl[1], pl[2], pl[3]} : u32x4{});
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      st.z = __builtin_fmaf(p[r], f16hi(d.vpa[r]), st.z);
-      st.z = __builtin_fmaf(p[4 + r], f16hi(d.vpb[r]), st.z);
-    }
-#pragma unroll
-    for (int k = 0; k < KH; ++k) {
-      const uint32_t w0 = d.va[k][0], w1 = d.va[k][1], w2 = d.vb[k][0], w3 = d.vb[k][1];
-      const uint32_t s0 = w0 >> 8, s1 = w1 >> 8, s2 = w2 >> 8, s3 = w3 >> 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t mask = 0x00030003u << (2 * (j & 3));
-        const half8 a = (j < 4) ? codes_as_half8(w0, w1, w2, w3, mask)
-                                : codes_as_half8(s0, s1, s2, s3, mask);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pv[k], acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pvl[k], acc[j], 0, 0, 0);
-      }
-    }
-  };
-
-  auto process_win = [&](const Win& W) {
-    float4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, W.kl[cc]), bw[cc], d,
-                                                  0, 0, 0);
-    float x[4], p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)   // only the columns of the block's KV head
-      x[r] = ((KH == 1 || kh == W.k) && win_slot_ok(W.u, 4 * qd + r)) ? d[r] : kNegInf;
-    softmax_step<4>(x, C2, p, st, acc);
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      hi[r] = f32_to_bf16_rne(p[r]);
-      lo[r] = f32_to_bf16_rne(p[r] - __uint_as_float(hi[r] << 16));
-    }
-    const short4_t phi = {(short)hi[0], (short)hi[1], (short)hi[2], (short)hi[3]};
-    const short4_t plo = {(short)lo[0], (short)lo[1], (short)lo[2], (short)lo[3]};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x4 src = W.vl[j >> 1];
-      const u32x2 pr = (j & 1) ? u32x2{src[2], src[3]} : u32x2{src[0], src[1]};
-      const short4_t a = __builtin_bit_cast(short4_t, pr);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, acc[j], 0, 0, 0);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, acc[j], 0, 0, 0);
-    }
-  };
-
-  // ---- INT2 ring: PF page pairs in flight ahead of the one being processed
-  // (issued now, so they arrive while the window blocks are processed)
-  Pair ring[PF];
-  if (np > 0) {
-    fetch_ids(0);
-#pragma unroll
-    for (int j = 0; j < PF; ++j) load_pair(j, ring[j]);
-  }
-
-  // ---- BF16 window blocks (true scale), each KV head of the wave in turn,
-  // one block in flight ahead
-  for (int t = 0; t < nw; ++t) {
-    const int u = wb + t / KH;
-    set_priority(kWinCost * (we - u) + np, total_units, rnd);
-    if (t + 1 < nw) load_win(wb + (t + 1) / KH, (t + 1) % KH, wn);
-    if (__any(win_slot_ok(u, r16))) process_win(wa);
-    wa = wn;
-  }
 
   // ---- INT2 page pairs: accumulate in code units (code * 4^(j%4) * 2^-24);
   // the window sums are moved to those units and back (powers of two, exact)
   if (np > 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] *= (float)(1 << (2 * (j & 3))) * (1.0f / 16777216.0f);
-    for (int k = 0; k < np; k += PF) {
-      set_priority(np - k, total_units, rnd);
+  }
+  // page ids of the pair requested next, read from LDS one iteration ahead
+  // so that no LDS round trip lies between the wait for a slot and the
+  // request that refills it
+  u32x2 nxt = pair_ids(D);
+  for (int k = 0; k < np; ++k) {
+    const int item = nwin + k;
+    const u32x2 req = nxt;
+    nxt = pair_ids(k + D + 1);
+    set_priority(prio, np - k);
+    wait_item(item);
+    const lds_u8* P = ring + (item % D) * G::SLOT;
+    u32x2 ka[KH], kb[KH], va[KH], vb[KH];
 #pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        if (k + j < np) process_pair(ring[j]);
-        load_pair(k + j + PF, ring[j]);
+    for (int kk = 0; kk < KH; ++kk) {
+      ka[kk] = *(lds_u32x2*)(P + kk * G::PB + koff);
+      kb[kk] = *(lds_u32x2*)(P + G::RB + kk * G::PB + koff);
+      va[kk] = *(lds_u32x2*)(P + kk * G::PB + 512 + 8 * lane);
+      vb[kk] = *(lds_u32x2*)(P + G::RB + kk * G::PB + 512 + 8 * lane);
+    }
+    const u32x4 kpa = *(lds_u32x4*)(P + kh * G::PB + poff);
+    const u32x4 kpb = *(lds_u32x4*)(P + G::RB + kh * G::PB + poff);
+    const u32x4 vpa = *(lds_u32x4*)(P + kh * G::PB + vpoff);
+    const u32x4 vpb = *(lds_u32x4*)(P + G::RB + kh * G::PB + vpoff);
+    // the slot is free again once its contents are in registers
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    request(item + D, req);
+
+    const float4_t da = qk_page(ka);
+    const float4_t db = qk_page(kb);
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = __builtin_fmaf(f16lo(kpa[r]), da[r], f16hi_mul(kpa[r], qz));
+      x[4 + r] = __builtin_fmaf(f16lo(kpb[r]), db[r], f16hi_mul(kpb[r], qz));
+    }
+    if constexpr (NG > 1) {   // sum the group partials: lanes n, n +- KH HP, ... of a 16-lane row
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if constexpr (KH * HP <= 8) x[t] += row_ror<8>(x[t]);
+        if constexpr (KH * HP <= 4) x[t] += row_ror<4>(x[t]);
+        if constexpr (KH * HP <= 2) x[t] += row_ror<2>(x[t]);
+        if constexpr (KH * HP <= 1) x[t] += row_ror<1>(x[t]);
       }
     }
+    const int tok = 32 * (pb + k);   // INT2 token index of slot 0 of page A
+    if (!(ids_ok && tok + 32 <= nq)) {   // slots past S_quant, or unmapped pages
+      const u32x2 own = pair_ids(k);
+      const bool oka = (int)own[0] >= 0, okb = (int)own[1] >= 0;
+      const int ta = tok + 4 * qd;   // INT2 token index of row 0 of tile A in this lane
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (!(oka && ta + r < nq)) x[r] = kNegInf;
+        if (!(okb && ta + 16 + r < nq)) x[4 + r] = kNegInf;
+      }
+    }
+    // P' = p * scale_v enters the MFMA as fp16: with p <= 2^8 (the lazy
+    // max) a value scale of 128 or more could overflow it, so such a pair
+    // takes the exact max (p <= 1, P' <= scale <= 65504)
+    const bool big_scale = max_scale_bits(vpa, vpb) >= 0x5800u;   // fp16 128.0
+    float p[8];
+    softmax_step<8>(x, K1, p, st, acc, __any(big_scale) ? 0.0f : 8.0f);
+    uint32_t ph[4], pl[4];
+    mul_by_f16lo_split(p[0], vpa[0], p[1], vpa[1], ph[0], pl[0]);
+    mul_by_f16lo_split(p[2], vpa[2], p[3], vpa[3], ph[1], pl[1]);
+    mul_by_f16lo_split(p[4], vpb[0], p[5], vpb[1], ph[2], pl[2]);
+    mul_by_f16lo_split(p[6], vpb[2], p[7], vpb[3], ph[3], pl[3]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      st.z = __builtin_fmaf(p[r], f16hi(vpa[r]), st.z);
+      st.z = __builtin_fmaf(p[4 + r], f16hi(vpb[r]), st.z);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk) {
+      // B operands of the P.V MFMAs on KV head kk: this column's P' if it belongs to head kk
+      const bool mine = KH == 1 || kh == kk;
+      const half8 pv = __builtin_bit_cast(half8, mine ? u32x4{ph[0], ph[1], ph[2], ph[3]} : u32x4{});
+      const half8 pvl = __builtin_bit_cast(half8, mine ? u32x4{pl[0], pl[1], pl[2], pl[3]} : u32x4{});
+      const uint32_t w0 = va[kk][0], w1 = va[kk][1], w2 = vb[kk][0], w3 = vb[kk][1];
+      const uint32_t s0 = w0 >> 8, s1 = w1 >> 8, s2 = w2 >> 8, s3 = w3 >> 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t mask = 0x00030003u << (2 * (j & 3));
+        const half8 a = (j < 4) ? codes_as_half8(w0, w1, w2, w3, mask)
+                                : codes_as_half8(s0, s1, s2, s3, mask);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pv, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pvl, acc[j], 0, 0, 0);
+      }
+    }
+  }
+  if (np > 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] *= 16777216.0f / (float)(1 << (2 * (j & 3)));
   }
+  // (the last D requests re-read the last item; they are waited for before
+  // the ring's LDS can be released at the end of the work-group)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- this wave's partial record: (max, sum, unnormalized o') per head of the pass
   st.l = rows_sum(st.l);
@@ -413,31 +534,50 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   }
 }
 
+// Calls f.template run<WH, D>() for the plan's waves per work-group and ring depth.
+template <class F>
+static auto with_waves_ring(int wh, int ring, F&& f) {
+  (void)ring;
+  if (wh == 4) return f.template run<4, 2>();
+  if (wh == 2) return f.template run<2, 2>();
+  return f.template run<1, 2>();
+}
+
+template <int NG, int HP, int KH>
+struct SplitLaunch {
+  const CacheArgs& c;
+  const SeqArgs& s;
+  const DecodePlan& plan;
+  const uint16_t* q_rot;
+  float* partials;
+  hipStream_t stream;
+  template <int WH, int D>
+  hipError_t run() const {
+    hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, WH, D>), dim3(plan.grid), dim3(64 * WH), 0,
+                       stream, c, s, plan.quota, plan.passes, plan.smax, plan.cus, *plan.order, q_rot,
+                       partials);
+    return hipGetLastError();
+  }
+};
+
+template <int NG, int HP, int KH>
+struct SplitOccupancy {
+  template <int WH, int D>
+  int run() const {
+    int nb = 0;
+    auto* kernel = &int2_decode_kernel<NG, HP, KH, WH, D>;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 64 * WH, 0);
+    return e == hipSuccess && nb > 0 ? nb : 1;
+  }
+};
+
 template <int NG, int HP, int KH>
 static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                                   const uint16_t* q_rot, float* out, float* partials,
                                   int phases, hipStream_t stream) {
-  const int wh = plan.wh;
   if (phases & kDecodeSplit) {
-    const dim3 grid(plan.grid);
-    switch (wh) {
-      case 4:
-        hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, kPrefetch, 4>), grid, dim3(256), 0, stream,
-                           c, s, plan.quota, plan.passes, plan.smax, plan.cus, *plan.order, q_rot,
-                           partials);
-        break;
-      case 2:
-        hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, kPrefetch, 2>), grid, dim3(128), 0, stream,
-                           c, s, plan.quota, plan.passes, plan.smax, plan.cus, *plan.order, q_rot,
-                           partials);
-        break;
-      default:
-        hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, kPrefetch, 1>), grid, dim3(64), 0, stream,
-                           c, s, plan.quota, plan.passes, plan.smax, plan.cus, *plan.order, q_rot,
-                           partials);
-        break;
-    }
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = with_waves_ring(plan.wh, plan.ring,
+                                         SplitLaunch<NG, HP, KH>{c, s, plan, q_rot, partials, stream});
     if (e != hipSuccess) return e;
   }
   if (phases & kDecodeMerge)
@@ -447,21 +587,8 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
 }
 
 template <int NG, int HP, int KH>
-static int wgs_per_cu_t(int wh) {
-  int nb = 0;
-  hipError_t e = hipErrorInvalidValue;
-  switch (wh) {
-    case 4:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, int2_decode_kernel<NG, HP, KH, kPrefetch, 4>, 256, 0);
-      break;
-    case 2:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, int2_decode_kernel<NG, HP, KH, kPrefetch, 2>, 128, 0);
-      break;
-    default:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, int2_decode_kernel<NG, HP, KH, kPrefetch, 1>, 64, 0);
-      break;
-  }
-  return e == hipSuccess && nb > 0 ? nb : 1;
+static int wgs_per_cu_t(int wh, int ring) {
+  return with_waves_ring(wh, ring, SplitOccupancy<NG, HP, KH>{});
 }
 
 // The (groups, heads per pass, KV heads per wave) shapes the planner uses:
@@ -499,7 +626,7 @@ static auto with_shape(int ng, int hp, int kh, F&& f) {
 struct OccupancyQuery {
   const DecodePlan& plan;
   template <int NG, int HP, int KH>
-  int operator()() const { return wgs_per_cu_t<NG, HP, KH>(plan.wh); }
+  int operator()() const { return wgs_per_cu_t<NG, HP, KH>(plan.wh, plan.ring); }
   int fail() const { return 1; }
 };
 

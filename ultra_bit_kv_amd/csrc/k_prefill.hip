@@ -211,7 +211,7 @@ __global__ __launch_bounds__(64 * W) void prefill_attn_kernel(CacheArgs c, Prefi
   float4_t acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-  SoftmaxState st{kNegInf, 0.0f, 0.0f};
+  SoftmaxState st{kNegInf, 0.0f, 0.0f, 0.0f};
   const float C2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
 
   // Unmapped INT2 pages are read as zero rows with zero weight (as in decode):
