@@ -83,6 +83,30 @@
  *  pages and win must be zero-filled once when allocated (slots that were
  *  never written are read with zero weight, so they must hold finite data).
  *
+ * OScaR key mode (cfg.key_mode = OSCAR_KEYS_OTS)                 [OScaR]
+ *  Keys of the INT2 segment are quantized as in the OScaR notes (step two
+ *  "Omni-Token Scaling" and the background "KIVI and the per-channel
+ *  paradigm"): for each rotated bf16 key row k~ (one token, one KV head),
+ *  s = bf16_rne(sqrt(sum_j k~_j^2)) (squares summed in fp64, correctly
+ *  rounded square root) and u_j = bf16_rne(k~_j / s) (u = 0 when s = 0);
+ *  then over each block of 32 consecutive INT2 positions (INT2 tokens
+ *  32b .. 32b + 31, i.e. logical pages 2b and 2b + 1) and each channel j:
+ *  Delta_j = bf16_rne((max_t u - min_t u) / 3), z_j = bf16_rne(-min_t u /
+ *  Delta_j) and code = [u > Delta (1/2 - z)] + [u >= Delta (3/2 - z)] +
+ *  [u > Delta (5/2 - z)] (fp64, exact); a constant channel (Delta_j = 0)
+ *  keeps z_j = bf16_rne(min_t u) and codes 0.  Dequantized key:
+ *  s * Delta_j * (code - z_j), or s * z_j when Delta_j = 0.  Values are
+ *  quantized per token exactly as in the default mode (clip_v, G = 32);
+ *  clip_k is not used.  Requires group_size = 32 and s_flush a multiple of
+ *  32 (a flush then moves whole key blocks).  Page-head block of 1568 bytes:
+ *   [0, 512)      K codes, the layout above
+ *   [512, 1024)   V codes, the layout above
+ *   [1024, 1280)  V params, the layout above (ng = 4)
+ *   [1280, 1312)  the 16 token scales s (bf16; slot t at bytes 1280 + 2t)
+ *   [1312, 1568)  uint32 word i: bf16 Delta (bits 0..15) | bf16 z (bits 16..31)
+ *                 of channel 64 (m % 2) + i of the key block of logical page m
+ *  98 bytes per INT2 token and KV head (5.2x fewer than bf16).
+ *
  * Status codes: 0 on success, a negative OSCAR_ERR_* otherwise.
  */
 #ifndef OSCAR_KV_H
@@ -127,7 +151,13 @@ typedef struct {
   int32_t num_pages;          /* physical pages in the pool */
   float clip_k[OSCAR_MAX_KV_HEADS]; /* kappa for keys, per KV head, in [0.5, 1] */
   float clip_v[OSCAR_MAX_KV_HEADS]; /* kappa for values, per KV head, in [0.5, 1] */
+  int32_t key_mode;           /* OSCAR_KEYS_CLIP (0) or OSCAR_KEYS_OTS (1), see above */
 } oscar_kv_config;
+
+enum oscar_key_mode {
+  OSCAR_KEYS_CLIP = 0,        /* per-token clipped groups of G channels (OSCAR) */
+  OSCAR_KEYS_OTS = 1          /* per-token scale, per-channel blocks of 32 tokens (OScaR) */
+};
 
 typedef struct {
   oscar_kv_config cfg;
@@ -172,11 +202,16 @@ enum oscar_rotation {
   OSCAR_ROT_HADAMARD_BITREV = 2
 };
 
-/* Checks a configuration; returns OSCAR_OK or the first failing OSCAR_ERR_*. */
+/* Checks a configuration; returns OSCAR_OK or the first failing OSCAR_ERR_*
+ * (an unknown key_mode is OSCAR_ERR_ARG; OScaR key mode with group_size != 32
+ * is OSCAR_ERR_GROUP and with s_flush % 32 != 0 OSCAR_ERR_WINDOW). */
 int oscar_check_config(const oscar_kv_config* cfg);
 
-/* Byte sizes of the caller-allocated cache buffers (0 for an invalid cfg). */
+/* Byte sizes of the caller-allocated cache buffers (0 for an invalid cfg).
+ * oscar_page_head_bytes: PB of the default key mode for a group size;
+ * oscar_config_page_head_bytes: PB of a configuration (1568 in OScaR key mode). */
 size_t oscar_page_head_bytes(int32_t group_size);
+size_t oscar_config_page_head_bytes(const oscar_kv_config* cfg);
 size_t oscar_pages_bytes(const oscar_kv_config* cfg);
 size_t oscar_win_bytes(const oscar_kv_config* cfg);
 int32_t oscar_ring_capacity(const oscar_kv_config* cfg);
@@ -225,7 +260,9 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
  *                 without the final R_V^T when cache->out_rotated is set
  * Split-K over the context: one launch writes partial results (max, sum,
  * unnormalized output) of each context split to the workspace, a second
- * launch merges them (log-sum-exp) and applies R_V^T. */
+ * launch merges them (log-sum-exp) and applies R_V^T.  In OScaR key mode
+ * the INT2 keys enter as s * Delta_j * (code - z_j) [OScaR, "Omni-Token
+ * Scaling": the token scale multiplies the per-channel dequantized row]. */
 int oscar_int2_decode_attn(const oscar_kv_cache* cache, int32_t n_seqs,
                            const int32_t* seq_slots_host, const int32_t* seq_lens_host,
                            const int32_t* seq_slots, const int32_t* seq_lens,
@@ -297,7 +334,8 @@ int oscar_int2_decode_attn_noalloc(const oscar_kv_cache* cache, int32_t n_seqs,
  * OSCAR_ERR_NULL, OSCAR_ERR_ARG (misaligned pointers, cu_new[0] != 0, negative
  * counts, repeated slots, n_seqs outside [1, min(max_seqs, 65535)]),
  * OSCAR_ERR_CAPACITY (slot or length beyond the cache), OSCAR_ERR_DEVICE,
- * OSCAR_ERR_HIP.  Needs no workspace. */
+ * OSCAR_ERR_HIP; a cache in OScaR key mode is OSCAR_ERR_ARG (prefill over
+ * such a cache is not provided).  Needs no workspace. */
 int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
                             const int32_t* seq_slots_host, const int32_t* len_before_host,
                             const int32_t* cu_new_host,
@@ -308,8 +346,9 @@ int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
 
 /* For checking: the decoded rows of positions [tok_begin, tok_end) of one
  * cache row holding seq_len tokens, in the rotated basis: bf16 window rows
- * widened to fp32, INT2 rows as scale * code + zero rounded once to fp32 --
- * the values the decode kernel reads.
+ * widened to fp32, INT2 rows as scale * code + zero rounded once to fp32 (in
+ * OScaR key mode INT2 keys as s * (Delta_j * (code - z_j)) in fp64, rounded
+ * once to fp32) -- the values the decode kernel reads.
  * [OSCAR s4 "Decoding Attention Kernel": INT2 segments are unpacked to
  * floating point (scale times code plus zero point) and BF16 segments read
  * as they are; OScaR "integer quantization basics": the dequantizer]

@@ -1,8 +1,8 @@
 """O7 (the OScaR variant): Hadamard-rotated keys scaled to unit norm per token
 (Omni-Token Scaling) and quantized per channel over blocks of G tokens.
 
-Test infrastructure (see ``oracle/__init__.py``).  Not yet on the GPU path:
-this module fixes what the variant computes.
+Test infrastructure (see ``oracle/__init__.py``): what the variant computes,
+against which the library's OScaR key mode is checked.
 
 Sources:
 * OScaR notes, background "KIVI and the per-channel paradigm": keys are
@@ -21,8 +21,12 @@ Sources:
 
 Readings (the notes leave these open):
 1. Rounding: k~ is the bf16 rounding of x . H / sqrt(d) (``rotate.Hadamard``);
-   s16 = bf16(||k~||_2) from the fp64 norm of the bf16 row; the buffered row is
-   u16 = bf16(k~ / s16).  Blocks are quantized from u16.
+   s16 = bf16(sqrt(S)) with S the sum of the squared bf16 entries rounded
+   once to fp64 (exactly rounded, so independent of the summation order; the
+   squares of bf16 values are exact in fp64, and whenever their bits span at
+   most 53 positions S itself is exact) and sqrt the correctly rounded fp64
+   square root; the buffered row is u16 = bf16(k~ / s16) from the correctly
+   rounded fp64 quotient.  Blocks are quantized from u16.
 2. Delta16 = bf16((max - min) / 3) and z16 = bf16(-min / Delta16) (for
    Delta16 = 0 see 4); codes come
    from the stored Delta16, z16: Q = clamp(rne(u / Delta16 + z16), 0, 3), taken
@@ -34,6 +38,8 @@ Readings (the notes leave these open):
 5. Dequantized key: k^ = s16 * Delta16 * (Q - z16) in fp64.
 """
 
+import math
+
 import numpy as np
 
 from . import rotate
@@ -44,7 +50,8 @@ def ots_scale(k_rot_bits):
     """(s16, u16) bits for bf16 rotated key rows [N, d]: s16 = bf16(||k~||_2),
     u16 = bf16(k~ / s16)."""
     k = bf16_bits_to_f64(np.asarray(k_rot_bits, np.uint16))
-    s16 = f64_to_bf16_bits(np.sqrt((k * k).sum(axis=1)))
+    sq = np.array([math.fsum(row) for row in (k * k)], np.float64).reshape(k.shape[0])
+    s16 = f64_to_bf16_bits(np.sqrt(sq))
     s = bf16_bits_to_f64(s16)
     with np.errstate(invalid="ignore", divide="ignore"):
         u = np.where(s[:, None] > 0, k / np.where(s > 0, s, 1.0)[:, None], 0.0)

@@ -191,6 +191,14 @@ CONFIGS = {
         prefill_chunks=16, prefill_len=2048,
         description="Qwen3-32B shape serving step: 256 decode tokens (8 sequences flush 256 "
                     "tokens), plus 16 fresh 2048-token prefill chunks"),
+    # The OScaR key mode's workload (OScaR notes, efficiency benchmarks: batch
+    # 48 at a 4K context, G = 32): keys with outlier channels go through the
+    # token scale and per-channel blocks of 32; values keep the per-token
+    # min-max quantizer (clip 1); no sink, no kept window, 128-token flushes.
+    "ots_bs48": Workload(
+        "ots_bs48", 6, n_seqs=48, hq=32, hkv=8, group=32, s_sink=0, s_keep=0, s_flush=128,
+        kappa=(1.0, 1.0), lengths=("fixed", 4096), outliers=(),
+        description="OScaR key mode: bs48, context 4096, G=32, flush 128, no windows"),
 }
 
 

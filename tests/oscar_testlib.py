@@ -17,7 +17,7 @@ def page_needs(w, lens):
 
 
 def make_cache(w, lens, identity=False, spare_pages=0, max_seqs=None, out_rotated=False,
-               rotation=0):
+               rotation=0, key_mode=0):
     """An empty OscarKVCache sized for sequences growing to ``lens``
     (``rotation`` 1 / 2: the structured R = H / sqrt(128) / H P_br / sqrt(128))."""
     from ultra_bit_kv_amd import OscarKVCache
@@ -36,7 +36,8 @@ def make_cache(w, lens, identity=False, spare_pages=0, max_seqs=None, out_rotate
                          s_sink=w.s_sink, s_keep=w.s_keep, s_flush=w.s_flush,
                          max_seqs=max_seqs or len(lens), max_pages_per_seq=bt.shape[1],
                          num_pages=total, clip_k=kk, clip_v=kv, r_k=r_k, r_v=r_v,
-                         block_table=bt, out_rotated=out_rotated, rotation=rotation)
+                         block_table=bt, out_rotated=out_rotated, rotation=rotation,
+                         key_mode=key_mode)
     cache.host_block_table = bt
     cache.host_r = (had, had) if rotation else (r_k, r_v)
     return cache
@@ -78,6 +79,14 @@ def fill(cache, w, lens, chunk=4096, seqs=None, max_tokens=1 << 18, last_step=Tr
     q_rot, _, _ = cache.append_tokens(all_i, [L - 1 for L in lens], [1] * len(lens), k, v, q)
     torch.cuda.synchronize()
     return q_rot
+
+
+def oracle_ots_head(w, seq, h, L, r_k, r_v):
+    """The OScaR key mode's oracle cache of one (sequence, KV head)."""
+    from oracle.ots import OtsHeadCache
+    _, kv = w.kappas()
+    return OtsHeadCache(w.keys(seq, 0, L)[:, h], w.values(seq, 0, L)[:, h], r_k[h], r_v[h], kv[h],
+                        w.group, w.s_sink, w.s_keep, w.s_flush)
 
 
 def oracle_head(w, seq, h, L, r_k, r_v):

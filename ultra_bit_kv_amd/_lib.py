@@ -26,8 +26,12 @@ class KvConfig(ctypes.Structure):
         ("group_size", c_i32), ("page_size", c_i32), ("s_sink", c_i32), ("s_keep", c_i32),
         ("s_flush", c_i32), ("max_seqs", c_i32), ("max_pages_per_seq", c_i32),
         ("num_pages", c_i32), ("clip_k", ctypes.c_float * MAX_KV_HEADS),
-        ("clip_v", ctypes.c_float * MAX_KV_HEADS),
+        ("clip_v", ctypes.c_float * MAX_KV_HEADS), ("key_mode", c_i32),
     ]
+
+
+# key modes of KvConfig.key_mode (oscar_key_mode in oscar_kv.h)
+KEYS_CLIP, KEYS_OTS = 0, 1
 
 
 class KvCache(ctypes.Structure):
@@ -54,6 +58,7 @@ STATUS = {0: "OSCAR_OK", -1: "OSCAR_ERR_NULL", -2: "OSCAR_ERR_SHAPE", -3: "OSCAR
 _PROTOS = {
     "oscar_check_config": (c_i32, [ctypes.POINTER(KvConfig)]),
     "oscar_page_head_bytes": (c_size, [c_i32]),
+    "oscar_config_page_head_bytes": (c_size, [ctypes.POINTER(KvConfig)]),
     "oscar_pages_bytes": (c_size, [ctypes.POINTER(KvConfig)]),
     "oscar_win_bytes": (c_size, [ctypes.POINTER(KvConfig)]),
     "oscar_ring_capacity": (c_i32, [ctypes.POINTER(KvConfig)]),

@@ -68,10 +68,11 @@ class OscarKVCache:
 
     def __init__(self, *, num_q_heads, num_kv_heads, group_size, s_sink, s_keep, s_flush,
                  max_seqs, max_pages_per_seq, num_pages, clip_k, clip_v, r_k, r_v, block_table,
-                 r_q=None, out_rotated=False, rotation=0, device="cuda"):
+                 r_q=None, out_rotated=False, rotation=0, key_mode=0, device="cuda"):
         """rotation: 0 uses the dense per-head r_k / r_v (/ r_q); 1 and 2 are the
         structured R = H / sqrt(128) and H P_br / sqrt(128), which take
-        r_k = r_v = r_q = None."""
+        r_k = r_v = r_q = None.  key_mode: 0 the per-token clipped key groups,
+        1 the OScaR token scale with per-channel key blocks (group_size 32)."""
         cfg = KvConfig()
         cfg.head_dim = D
         cfg.num_q_heads = num_q_heads
@@ -82,6 +83,7 @@ class OscarKVCache:
         cfg.max_seqs = max_seqs
         cfg.max_pages_per_seq = max_pages_per_seq
         cfg.num_pages = num_pages
+        cfg.key_mode = int(key_mode)
         ck = np.asarray(clip_k, np.float32)
         cv = np.asarray(clip_v, np.float32)
         assert ck.shape == (num_kv_heads,) and cv.shape == (num_kv_heads,) and num_kv_heads <= MAX_KV_HEADS
@@ -121,7 +123,8 @@ class OscarKVCache:
         self.workspace = None
         self.ring_capacity = L.oscar_ring_capacity(ctypes.byref(cfg))
         self.max_seq_len = L.oscar_max_seq_len(ctypes.byref(cfg))
-        self.page_head_bytes = L.oscar_page_head_bytes(group_size)
+        self.page_head_bytes = L.oscar_config_page_head_bytes(ctypes.byref(cfg))
+        self.key_mode = int(key_mode)
 
     @property
     def hq(self):

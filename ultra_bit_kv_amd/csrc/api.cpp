@@ -48,6 +48,11 @@ int ring_cap(const oscar_kv_config& c) {
 
 int ng_of(const oscar_kv_config& c) { return kD / c.group_size; }
 
+size_t page_bytes_of(const oscar_kv_config& c) {
+  return c.key_mode == OSCAR_KEYS_OTS ? (size_t)kOtsPageBytes
+                                      : 1024 + 128 * (size_t)(kD / c.group_size);
+}
+
 // Query heads per decode pass and KV heads per wave: columns of a 16-wide
 // MFMA tile are (group, KV head of the wave, query head) triples, so
 // ng * kh * hp <= 16.  With more than one group the columns of one head are
@@ -62,7 +67,10 @@ DecodePlan head_passes(const oscar_kv_config& c) {
   while (pow2 < g && pow2 < 16) pow2 *= 2;
   const bool even = c.num_kv_heads % 2 == 0;
   int hp, kh;
-  if (ng == 1) {
+  if (c.key_mode == OSCAR_KEYS_OTS) {   // (G = 32) one KV head per wave, 4 heads per pass
+    kh = 1;
+    hp = 4;
+  } else if (ng == 1) {
     hp = pow2;
     kh = (even && hp <= 8) ? 2 : 1;
   } else if (even && pow2 <= 8 / ng) {
@@ -154,7 +162,8 @@ CacheArgs make_args(const oscar_kv_cache& k) {
   a.max_seqs = c.max_seqs;
   a.max_pages = c.max_pages_per_seq;
   a.num_pages = c.num_pages;
-  a.page_bytes = (int)oscar_page_head_bytes(c.group_size);
+  a.page_bytes = (int)page_bytes_of(c);
+  a.key_mode = c.key_mode;
   return a;
 }
 
@@ -192,8 +201,8 @@ int decode_slots_per_cu(const CacheArgs& a, const DecodePlan& plan, bool bf16) {
   int dev = 0;
   (void)hipGetDevice(&dev);
   const long long key =
-      (((((((long long)dev * 2 + (bf16 ? 1 : 0)) * 8 + a.ng) * 32 + plan.hp) * 8 + plan.wh) * 4 +
-        plan.kh) * 8 + plan.ring);
+      ((((((((long long)dev * 2 + (bf16 ? 1 : 0)) * 8 + a.ng) * 32 + plan.hp) * 8 + plan.wh) * 4 +
+         plan.kh) * 8 + plan.ring) * 2 + (bf16 ? 0 : a.key_mode));
   std::lock_guard<std::mutex> lock(mu);
   for (const auto& m : memo)
     if (m.first == key) return m.second;
@@ -247,6 +256,12 @@ int oscar_check_config(const oscar_kv_config* c) {
   if (c->s_sink > kMaxSink || c->s_keep > kMaxKeep || c->s_flush > kMaxFlush) return OSCAR_ERR_WINDOW;
   if (c->max_seqs < 1 || c->max_pages_per_seq < 0 || c->num_pages < 0) return OSCAR_ERR_CAPACITY;
   if (c->max_pages_per_seq > kMaxPagesPerSeq) return OSCAR_ERR_CAPACITY;
+  if (c->key_mode != OSCAR_KEYS_CLIP && c->key_mode != OSCAR_KEYS_OTS) return OSCAR_ERR_ARG;
+  if (c->key_mode == OSCAR_KEYS_OTS) {
+    // one (Delta, z) per channel per block of 32 INT2 tokens; flushes move whole blocks
+    if (c->group_size != kOtsBlock) return OSCAR_ERR_GROUP;
+    if (c->s_flush % kOtsBlock != 0) return OSCAR_ERR_WINDOW;
+  }
   return OSCAR_OK;
 }
 
@@ -255,9 +270,14 @@ size_t oscar_page_head_bytes(int32_t group_size) {
   return 1024 + 128 * (size_t)(kD / group_size);
 }
 
+size_t oscar_config_page_head_bytes(const oscar_kv_config* c) {
+  if (oscar_check_config(c) != OSCAR_OK) return 0;
+  return page_bytes_of(*c);
+}
+
 size_t oscar_pages_bytes(const oscar_kv_config* c) {
   if (oscar_check_config(c) != OSCAR_OK) return 0;
-  return (size_t)c->num_pages * c->num_kv_heads * oscar_page_head_bytes(c->group_size);
+  return (size_t)c->num_pages * c->num_kv_heads * page_bytes_of(*c);
 }
 
 int32_t oscar_ring_capacity(const oscar_kv_config* c) {
@@ -375,7 +395,9 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
 
   // One launch for one-token appends (decode steps): no new row is flushed
   // in the same call and no new row lands on a ring slot the flush reads.
-  bool one = true;
+  // (in OScaR key mode only when nothing is quantized: keys move to INT2 in
+  // whole blocks through the key-block kernel)
+  bool one = c.key_mode == OSCAR_KEYS_CLIP || total_q == 0;
   for (int i = 0; one && i < n_seqs; ++i) {
     const int64_t n_new = (int64_t)cu_new_host[i + 1] - cu_new_host[i];
     const int64_t lb = len_before_host[i];
@@ -404,6 +426,11 @@ int oscar_rotate_quant_append(const oscar_kv_cache* cache, int32_t n_seqs,
     jobs.job[jobs.n++] = RotateJob{q, cache->r_q ? cache->r_q : cache->r_k, q_rot, nullptr,
                                    c.num_q_heads, c.num_q_heads / c.num_kv_heads};
   if ((st = hip_status(launch_rotate(jobs, (int)n_tok, sm))) != OSCAR_OK) return st;
+  // OScaR keys: whole blocks, before any new row can overwrite a ring slot
+  // they read (the value rows follow in the quantize launch)
+  if (c.key_mode == OSCAR_KEYS_OTS &&
+      (st = hip_status(launch_ots_keys(a, clip, sa, stage_k, (int)total_q, sm))) != OSCAR_OK)
+    return st;
   // 2+3 in one launch when no new row lands on a ring slot the flush reads
   bool disjoint = true;
   for (int i = 0; disjoint && i < n_seqs; ++i) {
@@ -777,7 +804,7 @@ int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
       !cu_new || !q_rot || !k_rot || !v_rot || !out || !cache->pages || !cache->block_table ||
       !cache->win || (dense(*cache) && !cache->out_rotated && !cache->r_v))
     return OSCAR_ERR_NULL;
-  if (!rotation_ok(*cache)) return OSCAR_ERR_ARG;
+  if (!rotation_ok(*cache) || c.key_mode != OSCAR_KEYS_CLIP) return OSCAR_ERR_ARG;
   if (!aligned16(q_rot) || !aligned16(k_rot) || !aligned16(v_rot) || !aligned16(out) ||
       !cache_aligned(*cache))
     return OSCAR_ERR_ARG;

@@ -98,6 +98,24 @@ __device__ __forceinline__ void mul_by_f16lo_split(float a, uint32_t wa, float b
   lo = l;
 }
 
+// q (two fp16 values) times (d0, d1) (fp32) as fp16 pairs split in two:
+// hi = the products rounded to fp16, lo = the remainders q d - hi (one fused
+// multiply-add each) rounded to fp16.  For an 11-bit q and an 8-bit d the
+// product has at most 19 bits, so hi + lo holds it exactly (22 bits) while
+// both stay in the fp16 normal range.
+__device__ __forceinline__ void mul_f16pair_split(uint32_t q, float d0, float d1, uint32_t& hi,
+                                                  uint32_t& lo) {
+  uint32_t h, l;
+  asm("v_fma_mixlo_f16 %0, %2, %3, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %2, %4, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixhi_f16 %1, %2, %4, -%0 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+      : "=&v"(h), "=&v"(l)
+      : "v"(q), "v"(d0), "v"(d1));
+  hi = h;
+  lo = l;
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;

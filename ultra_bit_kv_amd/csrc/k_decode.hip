@@ -54,9 +54,9 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 // Bytes of one page for the KH consecutive KV heads of a wave (their
 // page-head blocks are contiguous in a page), and the direct-to-LDS loads
 // (1 KB per wave instruction, 16 bytes per lane) that bring it in.
-template <int NG, int KH>
+template <int NG, int KH, int KM>
 struct PairGeom {
-  static constexpr int PB = 1024 + 128 * NG;         // page-head block
+  static constexpr int PB = KM ? kOtsPageBytes : 1024 + 128 * NG;   // page-head block
   static constexpr int RB = KH * PB;                  // one page of the wave's heads
   static constexpr int NI = (RB + 1023) / 1024;       // loads per page
   static constexpr int LAST_LANES = (RB - 1024 * (NI - 1)) / 16;   // lanes of the last load
@@ -82,12 +82,13 @@ struct PairGeom {
 // it are counted from their types (a window half is 4 loads, a pair 2 NI),
 // the tail re-requests the last item so the counts stay exact, and no other
 // vector memory access of the wave is outstanding meanwhile.
-template <int NG, int HP, int KH, int WH, int D>
+template <int NG, int HP, int KH, int WH, int D, int KM>
 __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqArgs s, int quota,
                                                               int passes, int smax, int cus, ItemOrder order,
                                                               const uint16_t* __restrict__ q_rot,
                                                               float* __restrict__ partials) {
-  using G = PairGeom<NG, KH>;
+  using G = PairGeom<NG, KH, KM>;
+  static_assert(KM == 0 || (NG == 4 && KH == 1), "OScaR keys: G = 32 values, one KV head per wave");
   constexpr int PW = rec_words(HP);   // floats per partial record
   constexpr int NT = 64 * WH;
   static_assert(D >= 2 && D <= 4, "ring depth");
@@ -290,6 +291,35 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   qsum = rows_sum(qsum);
   // INT2 logits in raw units x = s * D + z * qsum * 2^-24, log2 logit = K1 * x
   const float qz = colv ? qsum * (1.0f / 16777216.0f) : 0.0f;
+  // OScaR keys: q . k_hat = s_t (sum_j q_j Delta_j c_tj - C), C = sum_j q_j o_j
+  // with o_j = Delta_j z_j (-z_j for a constant channel), per key block.  The
+  // query enters the MFMA scaled by 2^sh (wave-uniform), chosen so that
+  // |q| 2^sh < 2^14: q 2^sh 4^-v Delta stays in the fp16 normal range.  qo:
+  // this lane's column's query at channels 32 gi + 8 qd .. + 7, times
+  // 2^(sh - 24), for its share of C.
+  int sh = 0;
+  float qo[KM ? 8 : 1];
+  if constexpr (KM) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = max(m, max(wq[cc][e] & 0x7FFFu, (wq[cc][e] >> 16) & 0x7FFFu));
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+    sh = min(100, max(-100, 13 - ((int)(m >> 7) - 127)));
+    sh = __builtin_amdgcn_readfirstlane(sh);
+    const float f = __builtin_ldexpf(1.0f, sh - 24);
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (colv)
+      w = *(const u32x4*)(q_rot + ((size_t)i * c.hq + (size_t)h * c.g + (size_t)pass * HP + hl) * kD +
+                          32 * gi + 8 * qd);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qo[2 * e] = bf16_bits_to_f32(w[e] & 0xFFFFu) * f;
+      qo[2 * e + 1] = bf16_bits_to_f32(w[e] >> 16) * f;
+    }
+  }
   // page ids visible; ids_ok: every page of the split's pairs with INT2
   // tokens is mapped, so only the last pairs (past S_quant) need masks
   const bool ids_ok = !__syncthreads_or(bad_ids);
@@ -316,7 +346,8 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
         const uint32_t word = wq[cl >> 3][(cl & 7) >> 1];
         const uint32_t bits = (cl & 1) ? (word >> 16) : (word & 0xFFFFu);
         const float qv = bval ? bf16_bits_to_f32(bits) : 0.0f;
-        bq[cc][2 * v + e] = (_Float16)(qv * (1.0f / (float)(1 << (2 * v))));
+        bq[cc][2 * v + e] = (_Float16)(KM ? qv * __builtin_ldexpf(1.0f, sh - 2 * v)
+                                          : qv * (1.0f / (float)(1 << (2 * v))));
       }
     }
   }
@@ -329,7 +360,8 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
 
   const int koff = (r16 * 8 + 2 * qd) * 4;                        // K codes of this lane
   const int poff = 1024 + 4 * (16 * gsel + 4 * qd);               // K params of this lane's column
-  const int vpoff = poff + 64 * NG;                               // V params
+  const int vpoff = (KM ? 1024 : 1024 + 64 * NG) + 4 * (16 * gsel + 4 * qd);   // V params
+  const float K1o = KM ? C2 * __builtin_ldexpf(1.0f, 24 - sh) : K1;   // log2 logit per raw unit
 
   // ---- BF16 window blocks (true scale), each KV head of the wave in turn
   // K half: lane (r16, qd) reads row r16, channels 32 qd + 8 cc .. + 7, i.e.
@@ -436,29 +468,95 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
       va[kk] = *(lds_u32x2*)(P + kk * G::PB + 512 + 8 * lane);
       vb[kk] = *(lds_u32x2*)(P + G::RB + kk * G::PB + 512 + 8 * lane);
     }
-    const u32x4 kpa = *(lds_u32x4*)(P + kh * G::PB + poff);
-    const u32x4 kpb = *(lds_u32x4*)(P + G::RB + kh * G::PB + poff);
     const u32x4 vpa = *(lds_u32x4*)(P + kh * G::PB + vpoff);
     const u32x4 vpb = *(lds_u32x4*)(P + G::RB + kh * G::PB + vpoff);
-    // the slot is free again once its contents are in registers
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    request(item + D, req);
-
-    const float4_t da = qk_page(ka);
-    const float4_t db = qk_page(kb);
+    // sum the group partials: lanes n, n +- KH HP, ... of a 16-lane row
+    auto group_sum = [&](float (&y)[8]) {
+      if constexpr (NG > 1) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          if constexpr (KH * HP <= 8) y[t] += row_ror<8>(y[t]);
+          if constexpr (KH * HP <= 4) y[t] += row_ror<4>(y[t]);
+          if constexpr (KH * HP <= 2) y[t] += row_ror<2>(y[t]);
+          if constexpr (KH * HP <= 1) y[t] += row_ror<1>(y[t]);
+        }
+      }
+    };
     float x[8];
+    if constexpr (!KM) {
+      const u32x4 kpa = *(lds_u32x4*)(P + kh * G::PB + poff);
+      const u32x4 kpb = *(lds_u32x4*)(P + G::RB + kh * G::PB + poff);
+      // the slot is free again once its contents are in registers
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      request(item + D, req);
+      const float4_t da = qk_page(ka);
+      const float4_t db = qk_page(kb);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = __builtin_fmaf(f16lo(kpa[r]), da[r], f16hi_mul(kpa[r], qz));
-      x[4 + r] = __builtin_fmaf(f16lo(kpb[r]), db[r], f16hi_mul(kpb[r], qz));
-    }
-    if constexpr (NG > 1) {   // sum the group partials: lanes n, n +- KH HP, ... of a 16-lane row
+      for (int r = 0; r < 4; ++r) {
+        x[r] = __builtin_fmaf(f16lo(kpa[r]), da[r], f16hi_mul(kpa[r], qz));
+        x[4 + r] = __builtin_fmaf(f16lo(kpb[r]), db[r], f16hi_mul(kpb[r], qz));
+      }
+      group_sum(x);
+    } else {
+      // OScaR key block = this pair.  B operand per chunk: q 2^sh 4^-v times
+      // the channel's Delta, as fp16 hi + lo (the 16-bit product, exactly
+      // up to fp16 range); the channels of the lane's group (32 qd ..) have
+      // their (Delta, z) words in page qd / 2.
+      const lds_u8* pbw = P + (qd >> 1) * G::RB + kOtsChanOffset + 4 * 32 * (qd & 1);
+      float4_t da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if constexpr (KH * HP <= 8) x[t] += row_ror<8>(x[t]);
-        if constexpr (KH * HP <= 4) x[t] += row_ror<4>(x[t]);
-        if constexpr (KH * HP <= 2) x[t] += row_ror<2>(x[t]);
-        if constexpr (KH * HP <= 1) x[t] += row_ror<1>(x[t]);
+      for (int cc = 0; cc < 4; ++cc) {
+        const int base = 16 * (cc >> 1) + 4 * (cc & 1);   // channel 32 qd + base + v + 8 e
+        const u32x4 w0 = *(lds_u32x4*)(pbw + 4 * base);
+        const u32x4 w1 = *(lds_u32x4*)(pbw + 4 * (base + 8));
+        const u32x4 qb = __builtin_bit_cast(u32x4, bq[cc]);
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          mul_f16pair_split(qb[v], __uint_as_float(w0[v] << 16), __uint_as_float(w1[v] << 16), hw[v],
+                            lw[v]);
+        const u32x4 hi = {hw[0], hw[1], hw[2], hw[3]}, lo = {lw[0], lw[1], lw[2], lw[3]};
+        uint32_t wa = (cc < 2) ? ka[0][0] : ka[0][1];
+        uint32_t wb2 = (cc < 2) ? kb[0][0] : kb[0][1];
+        if (cc & 1) {
+          wa >>= 8;
+          wb2 >>= 8;
+        }
+        const u32x4 ca = {wa & 0x00030003u, wa & 0x000C000Cu, wa & 0x00300030u, wa & 0x00C000C0u};
+        const u32x4 cb = {wb2 & 0x00030003u, wb2 & 0x000C000Cu, wb2 & 0x00300030u, wb2 & 0x00C000C0u};
+        const half8 h8 = __builtin_bit_cast(half8, hi), l8 = __builtin_bit_cast(half8, lo);
+        da = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ca), h8, da, 0, 0, 0);
+        da = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ca), l8, da, 0, 0, 0);
+        db = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, cb), h8, db, 0, 0, 0);
+        db = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, cb), l8, db, 0, 0, 0);
+      }
+      // this column group's share of C: channels 32 gi + 8 qd .. + 7, then
+      // the four lanes of the column
+      const lds_u8* pcw = P + (gsel >> 1) * G::RB + kOtsChanOffset + 4 * (32 * (gsel & 1) + 8 * qd);
+      const u32x4 c0 = *(lds_u32x4*)pcw, c1 = *(lds_u32x4*)(pcw + 16);
+      const u32x2 tsa = *(lds_u32x2*)(P + kOtsScaleOffset + 8 * qd);
+      const u32x2 tsb = *(lds_u32x2*)(P + G::RB + kOtsScaleOffset + 8 * qd);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      request(item + D, req);
+      float cp = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = e < 4 ? c0[e] : c1[e - 4];
+        const float dl = __uint_as_float(w << 16), z = __uint_as_float(w & 0xFFFF0000u);
+        cp = __builtin_fmaf(qo[e], dl != 0.0f ? dl * z : -z, cp);
+      }
+      cp = rows_sum(cp);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = da[r] - cp;
+        x[4 + r] = db[r] - cp;
+      }
+      group_sum(x);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {   // token scales of rows 4 qd + r
+        const uint32_t wa = tsa[r >> 1], wb3 = tsb[r >> 1];
+        x[r] *= bf16_bits_to_f32((r & 1) ? wa >> 16 : wa & 0xFFFFu);
+        x[4 + r] *= bf16_bits_to_f32((r & 1) ? wb3 >> 16 : wb3 & 0xFFFFu);
       }
     }
     const int tok = 32 * (pb + k);   // INT2 token index of slot 0 of page A
@@ -477,7 +575,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     // takes the exact max (p <= 1, P' <= scale <= 65504)
     const bool big_scale = max_scale_bits(vpa, vpb) >= 0x5800u;   // fp16 128.0
     float p[8];
-    softmax_step<8>(x, K1, p, st, acc, __any(big_scale) ? 0.0f : 8.0f);
+    softmax_step<8>(x, K1o, p, st, acc, __any(big_scale) ? 0.0f : 8.0f);
     uint32_t ph[4], pl[4];
     mul_by_f16lo_split(p[0], vpa[0], p[1], vpa[1], ph[0], pl[0]);
     mul_by_f16lo_split(p[2], vpa[2], p[3], vpa[3], ph[1], pl[1]);
@@ -534,16 +632,19 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   }
 }
 
-// Calls f.template run<WH, D>() for the plan's waves per work-group and ring depth.
-template <class F>
-static auto with_waves_ring(int wh, int ring, F&& f) {
-  (void)ring;
-  if (wh == 4) return f.template run<4, 2>();
-  if (wh == 2) return f.template run<2, 2>();
-  return f.template run<1, 2>();
+// Calls f.template run<WH, D>() for the plan's waves per work-group; the
+// ring has two slots, three in OScaR key mode (its pair loop frees a slot
+// only after the key dot products, which read the block's channel
+// parameters from the slot).
+template <int KM, class F>
+static auto with_waves_ring(int wh, F&& f) {
+  constexpr int D = KM ? 3 : 2;
+  if (wh == 4) return f.template run<4, D>();
+  if (wh == 2) return f.template run<2, D>();
+  return f.template run<1, D>();
 }
 
-template <int NG, int HP, int KH>
+template <int NG, int HP, int KH, int KM>
 struct SplitLaunch {
   const CacheArgs& c;
   const SeqArgs& s;
@@ -553,31 +654,31 @@ struct SplitLaunch {
   hipStream_t stream;
   template <int WH, int D>
   hipError_t run() const {
-    hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, WH, D>), dim3(plan.grid), dim3(64 * WH), 0,
+    hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, WH, D, KM>), dim3(plan.grid), dim3(64 * WH), 0,
                        stream, c, s, plan.quota, plan.passes, plan.smax, plan.cus, *plan.order, q_rot,
                        partials);
     return hipGetLastError();
   }
 };
 
-template <int NG, int HP, int KH>
+template <int NG, int HP, int KH, int KM>
 struct SplitOccupancy {
   template <int WH, int D>
   int run() const {
     int nb = 0;
-    auto* kernel = &int2_decode_kernel<NG, HP, KH, WH, D>;
+    auto* kernel = &int2_decode_kernel<NG, HP, KH, WH, D, KM>;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 64 * WH, 0);
     return e == hipSuccess && nb > 0 ? nb : 1;
   }
 };
 
-template <int NG, int HP, int KH>
+template <int NG, int HP, int KH, int KM>
 static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                                   const uint16_t* q_rot, float* out, float* partials,
                                   int phases, hipStream_t stream) {
   if (phases & kDecodeSplit) {
-    const hipError_t e = with_waves_ring(plan.wh, plan.ring,
-                                         SplitLaunch<NG, HP, KH>{c, s, plan, q_rot, partials, stream});
+    const hipError_t e =
+        with_waves_ring<KM>(plan.wh, SplitLaunch<NG, HP, KH, KM>{c, s, plan, q_rot, partials, stream});
     if (e != hipSuccess) return e;
   }
   if (phases & kDecodeMerge)
@@ -586,52 +687,57 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
   return hipSuccess;
 }
 
-template <int NG, int HP, int KH>
-static int wgs_per_cu_t(int wh, int ring) {
-  return with_waves_ring(wh, ring, SplitOccupancy<NG, HP, KH>{});
+template <int NG, int HP, int KH, int KM>
+static int wgs_per_cu_t(int wh) {
+  return with_waves_ring<KM>(wh, SplitOccupancy<NG, HP, KH, KM>{});
 }
 
-// The (groups, heads per pass, KV heads per wave) shapes the planner uses:
-// one group: any power-of-two pass, two KV heads per wave up to 8 heads;
-// with ng groups the columns (group, KV head, head) fill the tile exactly.
+// The (groups, heads per pass, KV heads per wave, key mode) shapes the
+// planner uses: one group: any power-of-two pass, two KV heads per wave up
+// to 8 heads; with ng groups the columns (group, KV head, head) fill the
+// tile exactly; OScaR keys: G = 32, one KV head per wave, 4 heads per pass.
 template <class F>
-static auto with_shape(int ng, int hp, int kh, F&& f) {
+static auto with_shape(int ng, int hp, int kh, int km, F&& f) {
+  if (km) {
+    if (ng == 4 && kh == 1 && hp == 4) return f.template operator()<4, 4, 1, 1>();
+    return f.fail();
+  }
   if (ng == 1) {
     if (kh == 2) {
       switch (hp) {
-        case 1: return f.template operator()<1, 1, 2>();
-        case 2: return f.template operator()<1, 2, 2>();
-        case 4: return f.template operator()<1, 4, 2>();
-        case 8: return f.template operator()<1, 8, 2>();
+        case 1: return f.template operator()<1, 1, 2, 0>();
+        case 2: return f.template operator()<1, 2, 2, 0>();
+        case 4: return f.template operator()<1, 4, 2, 0>();
+        case 8: return f.template operator()<1, 8, 2, 0>();
       }
     } else {
       switch (hp) {
-        case 1: return f.template operator()<1, 1, 1>();
-        case 2: return f.template operator()<1, 2, 1>();
-        case 4: return f.template operator()<1, 4, 1>();
-        case 8: return f.template operator()<1, 8, 1>();
-        case 16: return f.template operator()<1, 16, 1>();
+        case 1: return f.template operator()<1, 1, 1, 0>();
+        case 2: return f.template operator()<1, 2, 1, 0>();
+        case 4: return f.template operator()<1, 4, 1, 0>();
+        case 8: return f.template operator()<1, 8, 1, 0>();
+        case 16: return f.template operator()<1, 16, 1, 0>();
       }
     }
   } else if (ng == 2) {
-    if (kh == 2 && hp == 4) return f.template operator()<2, 4, 2>();
-    if (kh == 1 && hp == 8) return f.template operator()<2, 8, 1>();
+    if (kh == 2 && hp == 4) return f.template operator()<2, 4, 2, 0>();
+    if (kh == 1 && hp == 8) return f.template operator()<2, 8, 1, 0>();
   } else if (ng == 4) {
-    if (kh == 2 && hp == 2) return f.template operator()<4, 2, 2>();
-    if (kh == 1 && hp == 4) return f.template operator()<4, 4, 1>();
+    if (kh == 2 && hp == 2) return f.template operator()<4, 2, 2, 0>();
+    if (kh == 1 && hp == 4) return f.template operator()<4, 4, 1, 0>();
   }
   return f.fail();
 }
 
 struct OccupancyQuery {
   const DecodePlan& plan;
-  template <int NG, int HP, int KH>
-  int operator()() const { return wgs_per_cu_t<NG, HP, KH>(plan.wh, plan.ring); }
+  template <int NG, int HP, int KH, int KM>
+  int operator()() const { return wgs_per_cu_t<NG, HP, KH, KM>(plan.wh); }
   int fail() const { return 1; }
 };
 
 int decode_wgs_per_cu(const CacheArgs& c, const DecodePlan& plan) {
-  return with_shape(c.ng, plan.hp, plan.kh, OccupancyQuery{plan});
+  return with_shape(c.ng, plan.hp, plan.kh, c.key_mode, OccupancyQuery{plan});
 }
 
 struct DecodeLaunch {
@@ -643,9 +749,9 @@ struct DecodeLaunch {
   float* partials;
   int phases;
   hipStream_t stream;
-  template <int NG, int HP, int KH>
+  template <int NG, int HP, int KH, int KM>
   hipError_t operator()() const {
-    return launch_decode_t<NG, HP, KH>(c, s, plan, q_rot, out, partials, phases, stream);
+    return launch_decode_t<NG, HP, KH, KM>(c, s, plan, q_rot, out, partials, phases, stream);
   }
   hipError_t fail() const { return hipErrorInvalidValue; }
 };
@@ -654,7 +760,7 @@ hipError_t launch_decode(const CacheArgs& c, const SeqArgs& s, const DecodePlan&
                          const uint16_t* q_rot, float* out, float* partials, int phases,
                          hipStream_t stream) {
   if (s.n_seqs <= 0 || plan.grid <= 0) return hipSuccess;
-  return with_shape(c.ng, plan.hp, plan.kh,
+  return with_shape(c.ng, plan.hp, plan.kh, c.key_mode,
                     DecodeLaunch{c, s, plan, q_rot, out, partials, phases, stream});
 }
 

@@ -4,7 +4,10 @@
 // (OScaR notes, "integer quantization basics": x_hat = Delta (Q - z), with the
 // zero point stored as the fp16 value of the group's lower clip limit).
 // scale * code is exact in fp32 (11-bit times 2-bit), so the fused
-// multiply-add rounds the exact value once.
+// multiply-add rounds the exact value once.  In OScaR key mode an INT2 key is
+// s * (Delta * (code - z)) in fp64 (OScaR notes, step two "Omni-Token
+// Scaling"), or s * z for a constant channel, rounded once to fp32; the
+// channel's (Delta, z) sit in the page of its half of the key block.
 #include "device_common.h"
 
 namespace oscar {
@@ -41,7 +44,7 @@ __global__ __launch_bounds__(128) void dequant_kernel(CacheArgs c, int slot, int
       const uint32_t* kw = (const uint32_t*)base;
       const uint32_t* vw = (const uint32_t*)(base + 512);
       const uint32_t* kp = (const uint32_t*)(base + 1024);
-      const uint32_t* vp = kp + 16 * c.ng;
+      const uint32_t* vp = (const uint32_t*)(base + v_param_offset(c));
       const uint32_t kc = (kw[8 * t + ch / 16] >> (2 * (ch % 16))) & 3u;
       const uint32_t vc =
           (vw[2 * (16 * (t >> 2) + ch / 8) + ((t & 3) >> 1)] >> (16 * (t & 1) + 2 * (ch % 8))) & 3u;
@@ -53,6 +56,22 @@ __global__ __launch_bounds__(128) void dequant_kernel(CacheArgs c, int slot, int
       const float vz = (float)__builtin_bit_cast(_Float16, (uint16_t)(vpw >> 16));
       kv = __builtin_fmaf(ks, (float)kc, kz);
       vv = __builtin_fmaf(vs, (float)vc, vz);
+      if (c.key_mode) {
+        const int mc = (m & ~1) + (ch >> 6);   // page holding channel ch's (Delta, z)
+        const int pc = mc < c.max_pages ? c.block_table[(size_t)slot * c.max_pages + mc] : -1;
+        if (pc < 0 || pc >= c.num_pages) {
+          kv = __builtin_nanf("");
+        } else {
+          const uint8_t* cb = c.pages + ((size_t)pc * c.hkv + h) * c.page_bytes;
+          const uint32_t cw = ((const uint32_t*)(cb + kOtsChanOffset))[ch & 63];
+          const double dl = (double)bf16_bits_to_f32(cw & 0xFFFFu);
+          const double z = (double)bf16_bits_to_f32(cw >> 16);
+          const double sv =
+              (double)bf16_bits_to_f32(((const uint16_t*)(base + kOtsScaleOffset))[t]);
+          const double un = dl == 0.0 ? z : dl * ((double)kc - z);
+          kv = (float)(sv * un);
+        }
+      }
     }
   }
   k_out[o] = kv;

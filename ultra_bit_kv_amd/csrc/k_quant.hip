@@ -93,35 +93,24 @@ __device__ __forceinline__ void group_order_stats(uint32_t key0, uint32_t key1, 
   k_hi1 = next_key(k_hi, i_hi);
 }
 
-// Quantize position `item` (of all the append's quantized positions) of KV
-// head h; run by a work-group of 128 threads, wave 0 on the key row and wave
-// 1 on the value row, each on its own (no barrier, no LDS): lane l holds
-// channels 2l and 2l + 1.
-//
-// The clip limits need the order statistics s[i], s[i + 1] of each group
-// (type-7 quantiles).  They are found by a bitwise search over the
-// order-preserving keys of the bf16 values: from the top bit down, a bit of
-// the answer is set when fewer than i + 1 of the group's keys lie at or below
-// the prefix with that bit clear (group_order_stats).  The sequence of the
-// position comes from the host's table when the call has one.
-__device__ __forceinline__ void quantize_item(const CacheArgs& c, const QuantArgs& clip,
-                                              const SeqArgs& s,
-                                              const uint16_t* __restrict__ stage_k,
-                                              const uint16_t* __restrict__ stage_v, int item,
-                                              int h) {
-#pragma clang fp contract(off)
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;   // w: 0 = K, 1 = V
-  // ---- sequence of this position: prefix sum of the per-sequence counts
+// The sequence of quantized position `item` of an append (positions of all
+// sequences numbered consecutively, sequence-major): its index i, the first
+// item of that sequence, its cache row, length before the append and first
+// new-token row.  From the host's table when the call has one, else by a
+// prefix sum over the device counts S_quant(after) - S_quant(before) that
+// the whole wave runs.  False (uniform) when the item lies past them.
+__device__ __forceinline__ bool locate_quant_position(const CacheArgs& c, const QuantArgs& clip,
+                                                      const SeqArgs& s, int item, int lane, int& i,
+                                                      int& before, int& slot, int& lb, int& cu0) {
   auto count_of = [&](int k) {
-    const int lb = s.lens[k];
+    const int l0 = s.lens[k];
     const int nn = s.cu_new[k + 1] - s.cu_new[k];
-    if (s.slots[k] < 0 || s.slots[k] >= c.max_seqs || lb < 0 || nn < 0) return 0;
-    return s_quant_of(lb + nn, c.s_sink, c.s_keep, c.s_flush) -
-           s_quant_of(lb, c.s_sink, c.s_keep, c.s_flush);
+    if (s.slots[k] < 0 || s.slots[k] >= c.max_seqs || l0 < 0 || nn < 0) return 0;
+    return s_quant_of(l0 + nn, c.s_sink, c.s_keep, c.s_flush) -
+           s_quant_of(l0, c.s_sink, c.s_keep, c.s_flush);
   };
-  int i, before, slot, lb, cu0;
   if (clip.qn > 0) {   // the host's table: the last sequence starting at or before the item
-    if (item >= clip.q[clip.qn].before) return;
+    if (item >= clip.q[clip.qn].before) return false;
     int lo = 0, hi = clip.qn - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -146,7 +135,7 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const QuantArg
     }
     const bool hit = item >= incl - run && item < incl;   // exactly one lane, if any
     const unsigned long long hits = __ballot(hit);
-    if (hits == 0ull) return;   // uniform: the device counts do not reach this item
+    if (hits == 0ull) return false;   // uniform: the device counts do not reach this item
     int seq = -1, off = incl - run;
     if (hit) {
       for (int k = k0; k < k1; ++k) {
@@ -162,6 +151,30 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const QuantArg
     lb = s.lens[i];
     cu0 = s.cu_new[i];
   }
+  return true;
+}
+
+// Quantize position `item` (of all the append's quantized positions) of KV
+// head h; run by a work-group of 128 threads, wave 0 on the key row and wave
+// 1 on the value row, each on its own (no barrier, no LDS): lane l holds
+// channels 2l and 2l + 1.
+//
+// The clip limits need the order statistics s[i], s[i + 1] of each group
+// (type-7 quantiles).  They are found by a bitwise search over the
+// order-preserving keys of the bf16 values: from the top bit down, a bit of
+// the answer is set when fewer than i + 1 of the group's keys lie at or below
+// the prefix with that bit clear (group_order_stats).  The sequence of the
+// position comes from the host's table when the call has one.
+__device__ __forceinline__ void quantize_item(const CacheArgs& c, const QuantArgs& clip,
+                                              const SeqArgs& s,
+                                              const uint16_t* __restrict__ stage_k,
+                                              const uint16_t* __restrict__ stage_v, int item,
+                                              int h) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;   // w: 0 = K, 1 = V
+  if (w == 0 && c.key_mode) return;   // OScaR keys: ots_key_block
+  int i, before, slot, lb, cu0;
+  if (!locate_quant_position(c, clip, s, item, lane, i, before, slot, lb, cu0)) return;
   const int sqb = s_quant_of(lb, c.s_sink, c.s_keep, c.s_flush);
   const int p = sqb + (item - before);
   const int m = (p - c.s_sink) / kPage, t = (p - c.s_sink) % kPage;
@@ -245,7 +258,7 @@ __device__ __forceinline__ void quantize_item(const CacheArgs& c, const QuantArg
     }
   }
   if ((2 * lane) % G == 0) {
-    uint32_t* prm = (uint32_t*)(base + 1024 + (w == 0 ? 0 : 64 * c.ng));
+    uint32_t* prm = (uint32_t*)(base + (w == 0 ? 1024 : v_param_offset(c)));
     prm[16 * gi + t] = s16 | (z16 << 16);
   }
 }
@@ -262,6 +275,159 @@ hipError_t launch_quantize(const CacheArgs& c, const QuantArgs& clip, const SeqA
   if (total_q <= 0 || s.n_seqs <= 0) return hipSuccess;
   dim3 grid(total_q, c.hkv);
   hipLaunchKernelGGL(quantize_kernel, grid, dim3(128), 0, stream, c, clip, s, stage_k, stage_v);
+  return hipGetLastError();
+}
+
+// OScaR key block `blk` of KV head h: the append's quantized positions
+// 32 blk .. 32 blk + 31 (one sequence: its count is a multiple of 32), i.e.
+// INT2 tokens that fill logical pages m0 and m0 + 1 (OScaR notes, step two
+// "Omni-Token Scaling" and "KIVI and the per-channel paradigm").  256
+// threads; thread (t = tid / 8, part = tid % 8) first holds channels
+// 16 part .. 16 part + 15 of the block's token t:
+//  1. s = bf16(sqrt(sum of squares)) of the rotated bf16 row (fp64; the
+//     squares are exact and the sum is exact whenever their bits span at
+//     most 53 positions, so the fixed summation order does not matter then),
+//     u = bf16(k / s) (fp64 quotient, 0 when s = 0) to LDS;
+//  2. thread (hh = tid / 128, j = tid % 128): min / max of channel j over
+//     tokens 16 hh .. 16 hh + 15, combined through LDS; Delta = bf16((max -
+//     min) / 3), z = bf16(-min / Delta) (bf16(min) when Delta = 0), and the
+//     codes of its 16 tokens against the exact fp64 thresholds;
+//  3. thread (t, part) packs the 16 codes of its word.
+__device__ __forceinline__ void ots_key_block(const CacheArgs& c, const QuantArgs& clip,
+                                              const SeqArgs& s,
+                                              const uint16_t* __restrict__ stage_k, int blk,
+                                              int h) {
+#pragma clang fp contract(off)
+  __shared__ __align__(16) uint16_t s_u[kOtsBlock][kD];   // normalized rows (bf16 bits)
+  __shared__ float s_mm[2][2][kD];                         // [token half][min, max][channel]
+  __shared__ __align__(16) uint8_t s_code[kOtsBlock][kD];
+  __shared__ uint16_t s_scale[kOtsBlock];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int item0 = kOtsBlock * blk;
+  int i, before, slot, lb, cu0;
+  // (every wave finds the same sequence: the result is uniform over the work-group)
+  if (!locate_quant_position(c, clip, s, item0, lane, i, before, slot, lb, cu0)) return;
+  const int sqb = s_quant_of(lb, c.s_sink, c.s_keep, c.s_flush);
+  const int p0 = sqb + (item0 - before);
+  const int m0 = (p0 - c.s_sink) / kPage;   // even: p0 - S_sink is a multiple of 32
+  auto phys_of = [&](int m) {
+    const int ph = m < c.max_pages ? c.block_table[(size_t)slot * c.max_pages + m] : -1;
+    return (ph >= 0 && ph < c.num_pages) ? ph : -1;
+  };
+  const int page_a = phys_of(m0), page_b = phys_of(m0 + 1);
+  auto block_of = [&](int t) -> uint8_t* {   // page-head block holding token t, or null
+    const int ph = t < kPage ? page_a : page_b;
+    return ph < 0 ? nullptr : c.pages + ((size_t)ph * c.hkv + h) * c.page_bytes;
+  };
+
+  // ---- 1. token scale and normalized row
+  {
+    const int t = tid >> 3, part = tid & 7;
+    const int p = p0 + t;
+    const uint16_t* src;
+    if (p < lb) {   // an old row, still in the recent ring
+      const int r = (p - c.s_sink) % c.ring_cap;
+      src = c.win + (((size_t)slot * c.hkv + h) * c.win_blocks + c.sink_blocks + r / kPage) *
+                        (2 * kPage * kD) + (r % kPage) * kD;
+    } else {        // a new row of this append
+      src = stage_k + ((size_t)cu0 + (p - lb)) * c.hkv * kD + (size_t)h * kD;
+    }
+    const u32x4_r w0 = *(const u32x4_r*)(src + 16 * part);
+    const u32x4_r w1 = *(const u32x4_r*)(src + 16 * part + 8);
+    double x[16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = (double)bf16_bits_to_f32(w0[e] & 0xFFFFu);
+      x[2 * e + 1] = (double)bf16_bits_to_f32(w0[e] >> 16);
+      x[8 + 2 * e] = (double)bf16_bits_to_f32(w1[e] & 0xFFFFu);
+      x[9 + 2 * e] = (double)bf16_bits_to_f32(w1[e] >> 16);
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ss += x[e] * x[e];
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    const uint32_t s16 = f64_to_bf16_rne(__builtin_sqrt(ss));
+    const double sv = (double)bf16_bits_to_f32(s16);
+    uint32_t packed[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t a = sv > 0.0 ? f64_to_bf16_rne(x[2 * e] / sv) : 0u;
+      const uint32_t b = sv > 0.0 ? f64_to_bf16_rne(x[2 * e + 1] / sv) : 0u;
+      packed[e] = a | (b << 16);
+    }
+    *(u32x4_r*)&s_u[t][16 * part] = u32x4_r{packed[0], packed[1], packed[2], packed[3]};
+    *(u32x4_r*)&s_u[t][16 * part + 8] = u32x4_r{packed[4], packed[5], packed[6], packed[7]};
+    if (part == 0) s_scale[t] = (uint16_t)s16;
+  }
+  __syncthreads();
+
+  // ---- 2. per-channel parameters and codes
+  {
+    const int j = tid & (kD - 1), hh = tid >> 7;
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    float u[kPage];
+#pragma unroll
+    for (int r = 0; r < kPage; ++r) {
+      u[r] = bf16_bits_to_f32(s_u[kPage * hh + r][j]);
+      mn = fminf(mn, u[r]);
+      mx = fmaxf(mx, u[r]);
+    }
+    s_mm[hh][0][j] = mn;
+    s_mm[hh][1][j] = mx;
+    __syncthreads();
+    // a zero extreme is taken as +0
+    mn = fminf(s_mm[0][0][j], s_mm[1][0][j]) + 0.0f;
+    mx = fmaxf(s_mm[0][1][j], s_mm[1][1][j]) + 0.0f;
+    const double dmn = (double)mn, dmx = (double)mx;
+    const uint32_t d16 = f64_to_bf16_rne((dmx - dmn) / 3.0);
+    const double dl = (double)bf16_bits_to_f32(d16);
+    const uint32_t z16 = dl == 0.0 ? f64_to_bf16_rne(dmn) : f64_to_bf16_rne(-dmn / dl);
+    const double z = (double)bf16_bits_to_f32(z16);
+    const double t1 = dl * (0.5 - z), t2 = dl * (1.5 - z), t3 = dl * (2.5 - z);
+#pragma unroll
+    for (int r = 0; r < kPage; ++r) {
+      const double v = (double)u[r];
+      const uint32_t q = dl == 0.0 ? 0u : (uint32_t)(v > t1) + (uint32_t)(v >= t2) + (uint32_t)(v > t3);
+      s_code[kPage * hh + r][j] = (uint8_t)q;
+    }
+    if (hh == 0) {   // channel j's (Delta, z) in the page of its half
+      uint8_t* base = block_of(j < 64 ? 0 : kPage);
+      if (base) ((uint32_t*)(base + kOtsChanOffset))[j & 63] = d16 | (z16 << 16);
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. pack codes (word 8 t + part: channels 16 part + e at bits 2e) and scales
+  {
+    const int t = tid >> 3, part = tid & 7;
+    const u32x4_r cw = *(const u32x4_r*)&s_code[t][16 * part];   // 16 codes, one per byte
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t b = cw[e];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) word |= ((b >> (8 * k)) & 3u) << (2 * (4 * e + k));
+    }
+    uint8_t* base = block_of(t);
+    if (base) {
+      ((uint32_t*)base)[8 * (t % kPage) + part] = word;
+      if (part == 0) ((uint16_t*)(base + kOtsScaleOffset))[t % kPage] = s_scale[t];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void ots_key_kernel(CacheArgs c, QuantArgs clip, SeqArgs s,
+                                                      const uint16_t* __restrict__ stage_k) {
+  ots_key_block(c, clip, s, stage_k, blockIdx.x, blockIdx.y);
+}
+
+hipError_t launch_ots_keys(const CacheArgs& c, const QuantArgs& clip, const SeqArgs& s,
+                           const uint16_t* stage_k, int total_q, hipStream_t stream) {
+  if (total_q <= 0 || s.n_seqs <= 0) return hipSuccess;
+  dim3 grid(total_q / kOtsBlock, c.hkv);
+  hipLaunchKernelGGL(ots_key_kernel, grid, dim3(256), 0, stream, c, clip, s, stage_k);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ struct CacheArgs {
   int sink_blocks, win_blocks;   // ceil(s_sink / 16), sink_blocks + ring_cap / 16
   int max_seqs, max_pages, num_pages;
   int page_bytes;                // bytes of one page-head block
+  int key_mode;                  // 0: per-token clipped key groups; 1: OScaR token scale + channel blocks
   int unrot;                     // apply R_V^T after the merge (0: output in the rotated basis)
   int rot;                       // 0: dense r_k / r_v; 1: H / sqrt(128); 2: H P_br / sqrt(128)
 };
@@ -80,6 +81,22 @@ hipError_t launch_quantize(const CacheArgs& c, const QuantArgs& clip, const SeqA
 hipError_t launch_flush_place(const CacheArgs& c, const QuantArgs& clip, const SeqArgs& s,
                               const uint16_t* stage_k, const uint16_t* stage_v, int total_q,
                               int max_new, hipStream_t stream);
+
+// OScaR key mode: the key blocks (32 INT2 positions, one KV head) that move
+// to INT2 in this append, from the ring (old rows) or the staging rows (new
+// tokens), into the pages; total_q as for launch_quantize (a multiple of 32
+// per sequence).
+hipError_t launch_ots_keys(const CacheArgs& c, const QuantArgs& clip, const SeqArgs& s,
+                           const uint16_t* stage_k, int total_q, hipStream_t stream);
+
+// Byte offset of the value parameters in a page-head block.
+__host__ __device__ inline int v_param_offset(const CacheArgs& c) {
+  return c.key_mode ? 1024 : 1024 + 64 * c.ng;
+}
+constexpr int kOtsBlock = 32;         // OScaR key block: INT2 tokens per channel (Delta, z)
+constexpr int kOtsPageBytes = 1568;   // OScaR page-head block
+constexpr int kOtsScaleOffset = 1280; // token scales (bf16) in the block
+constexpr int kOtsChanOffset = 1312;  // channel (Delta, z) words in the block
 
 // Copy staging rows of new tokens that land in the sink or the ring.
 hipError_t launch_place(const CacheArgs& c, const SeqArgs& s, const uint16_t* stage_k,
