@@ -24,7 +24,9 @@ Legs reported beside the headline (--legs): bs1 (Qwen3-8B shape, 32K
 context; eager and replayed from a HIP graph), c1 (tiny, MALL-resident), c4
 (128K context), c5 (the Qwen3-32B serving step: one append carrying 256
 decode tokens and 16 fresh 2048-token chunks, then the decode of the 256
-sequences, timed together), probe (a plain HBM read kernel: the measured
+sequences, timed together), ots (the OScaR key mode: bs48 at a 4K context,
+G = 32, Hadamard rotation; with the BF16 decode at the same shape), probe
+(a plain HBM read kernel: the measured
 read ceiling), bf16 (the BF16 paged decode on the same shapes), prefill
 (chunked-prefill attention), rotation (dense vs structured rotation in the
 append).  Each leg times at least --leg-steps steps; every layer copy gets an
@@ -54,13 +56,23 @@ def decode_source_hash():
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, lens):
+def int2_token_head_bytes(w, key_mode=0):
+    """Cache bytes of one INT2 token-head: K and V codes (32 B each) and
+    fp16 scale/zero per group of K and of V; in the OScaR key mode the V
+    groups, the token's bf16 scale and its share of its key block's
+    per-channel bf16 (Delta, z) (128 x 4 B per 32 tokens)."""
+    if key_mode:
+        return 64 + 512 // w.group + 2 + 128 * 4 // 32
+    return 64 + 1024 // w.group
+
+
+def algorithmic_bytes(w, lens, key_mode=0):
     """Bytes the split launch of one decode step must move, from the cache
-    format: every INT2 token-head (codes + fp16 scale/zero per group), every
-    BF16 window token-head (K and V rows), one block-table entry per INT2
-    page, and the rotated queries (bf16).  The flush boundary S_quant is the
-    closed form of the placement rule."""
-    per_int2 = 64 + 1024 // w.group
+    format: every INT2 token-head (int2_token_head_bytes), every BF16 window
+    token-head (K and V rows), one block-table entry per INT2 page, and the
+    rotated queries (bf16).  The flush boundary S_quant is the closed form of
+    the placement rule."""
+    per_int2 = int2_token_head_bytes(w, key_mode)
     total = 0
     for L in lens:
         L = int(L)
@@ -311,9 +323,10 @@ def int2_pages(w, L):
     return -(-max(0, s_quant - w.s_sink) // 16)
 
 
-def make_layer(w, lens_max, n, rotation=0):
+def make_layer(w, lens_max, n, rotation=0, key_mode=0):
     """An empty cache sized for rows growing to lens_max (seeded page pool);
-    rotation 1 / 2: the structured R = H / sqrt(128) / H P_br / sqrt(128)."""
+    rotation 1 / 2: the structured R = H / sqrt(128) / H P_br / sqrt(128);
+    key_mode 1: the OScaR keys."""
     from ultra_bit_kv_amd import OscarKVCache
     r_k, r_v = w.rotations() if rotation == 0 else (None, None)
     kk, kv = w.kappas()
@@ -321,7 +334,7 @@ def make_layer(w, lens_max, n, rotation=0):
     return OscarKVCache(num_q_heads=w.hq, num_kv_heads=w.hkv, group_size=w.group,
                         s_sink=w.s_sink, s_keep=w.s_keep, s_flush=w.s_flush, max_seqs=n,
                         max_pages_per_seq=bt.shape[1], num_pages=total, clip_k=kk, clip_v=kv,
-                        r_k=r_k, r_v=r_v, block_table=bt, rotation=rotation)
+                        r_k=r_k, r_v=r_v, block_table=bt, rotation=rotation, key_mode=key_mode)
 
 
 def populate(cache, w, lens, chunk=8192, max_tokens=1 << 18):
@@ -406,7 +419,8 @@ def timed_regions(enqueue, n, region, hold_cycles):
     return tot_ms / n, host, bound
 
 
-def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0, region=0):
+def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0, region=0,
+            key_mode=0):
     """Decode steps of every row of workload w, cycling through n_layers
     copies of the populated cache (``rotation``: the cache's rotation kind).
 
@@ -432,11 +446,11 @@ def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0,
     # layer 0 is populated through the library's own append path with L0 - 1
     # tokens; the other layers are copies.  Layer step k appends position
     # L0 - 1 + k, so the first step of every layer decodes a context of L0.
-    base = make_layer(w, grow, n, rotation=rotation)
+    base = make_layer(w, grow, n, rotation=rotation, key_mode=key_mode)
     populate(base, w, [int(L) - 1 for L in lens0])
     layers = [base]
     for _ in range(1, n_layers):
-        c = make_layer(w, grow, n, rotation=rotation)
+        c = make_layer(w, grow, n, rotation=rotation, key_mode=key_mode)
         c.pages.copy_(base.pages)
         c.win.copy_(base.win)
         layers.append(c)
@@ -505,7 +519,7 @@ def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0,
     dec = [b.elapsed_time(d) for a, b, c, d in evs]
     whole = [a.elapsed_time(d) for a, b, c, d in evs]
     # algorithmic bytes of the average split launch (lengths grow during the run)
-    byts = [algorithmic_bytes(w, [int(L) + (warm + steps + j) // n_layers for L in lens0])
+    byts = [algorithmic_bytes(w, [int(L) + (warm + steps + j) // n_layers for L in lens0], key_mode)
             for j in range(steps)]
     res = {"w": w, "lens0": lens0, "n": n, "ms_step": ms_step, "ms_step_ev": ms_step_ev,
            "dec_ms": float(np.mean(dec)), "split_ms": float(np.mean(split)),
@@ -684,7 +698,7 @@ def measure_c5_step(w, reps):
     }
 
 
-LEGS = ("bs1", "c1", "c4", "c5", "probe", "bf16", "prefill", "rotation")
+LEGS = ("bs1", "c1", "c4", "c5", "ots", "probe", "bf16", "prefill", "rotation")
 
 
 def main():
@@ -797,6 +811,19 @@ def main():
     if "c5" in legs:
         log("c5 serving step")
         res["c5_step"] = measure_c5_step(get("c5_qwen3_32b_step"), reps=20)
+    if "ots" in legs:
+        log("ots leg")
+        wo = get("ots_bs48")
+        mo = measure(wo, 4, ls, args.warmup, rotation=1, region=16, key_mode=1)
+        res["ots"] = leg_summary(mo, probe)
+        res["ots"]["layers_cycled"] = 4
+        res["ots"]["rotation"] = "H / sqrt(128)"
+        res["ots"]["int2_bytes_per_token_head"] = int2_token_head_bytes(wo, 1)
+        bfo = measure_bf16(wo, 2, min(ls, 100), hold_for(2e-3 * min(ls, 100)))
+        res["ots"]["bf16_decode_ms"] = bfo["decode_ms"]
+        res["ots"]["bf16_GBs"] = bfo["GBs"]
+        res["ots"]["int2_speedup_vs_bf16"] = bfo["decode_ms"] / res["ots"]["decode_ms"]
+        res["ots"]["bytes_ratio_vs_bf16"] = bfo["bytes"] / mo["bytes"]
     if "bf16" in legs:
         log("bf16 comparison")
         # the uncompressed comparison point on the same shapes and lengths
