@@ -81,9 +81,11 @@ __device__ __forceinline__ uint32_t max_scale_bits(const u32x4& a, const u32x4& 
 // split in two: hi = the products rounded to fp16, lo = the remainders
 // a * s - hi (one fused multiply-add each) rounded to fp16, so hi + lo
 // carries about 22 significant bits.  Mixed-precision fused multiply-adds
-// that write one fp16 half each; the leading s_nop gives a and b, which
+// that write one fp16 half each.  The leading s_nop gives a and b, which
 // come from the exp unit, the wait state such a result needs before a VALU
-// reads it.
+// reads it; the trailing one the two wait states a matrix instruction needs
+// before it reads a VGPR a VALU wrote (the compiler does not see into the
+// asm, and hi / lo feed MFMAs).
 __device__ __forceinline__ void mul_by_f16lo_split(float a, uint32_t wa, float b, uint32_t wb,
                                                    uint32_t& hi, uint32_t& lo) {
   uint32_t h, l;
@@ -91,7 +93,8 @@ __device__ __forceinline__ void mul_by_f16lo_split(float a, uint32_t wa, float b
       "v_fma_mixlo_f16 %0, %2, %3, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]\n\t"
       "v_fma_mixhi_f16 %0, %4, %5, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]\n\t"
       "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel:[0,0,0] op_sel_hi:[0,1,1]\n\t"
-      "v_fma_mixhi_f16 %1, %4, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,1,1]"
+      "v_fma_mixhi_f16 %1, %4, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,1,1]\n\t"
+      "s_nop 1"
       : "=&v"(h), "=&v"(l)
       : "v"(a), "v"(wa), "v"(b), "v"(wb));
   hi = h;
@@ -102,14 +105,16 @@ __device__ __forceinline__ void mul_by_f16lo_split(float a, uint32_t wa, float b
 // hi = the products rounded to fp16, lo = the remainders q d - hi (one fused
 // multiply-add each) rounded to fp16.  For an 11-bit q and an 8-bit d the
 // product has at most 19 bits, so hi + lo holds it exactly (22 bits) while
-// both stay in the fp16 normal range.
+// both stay in the fp16 normal range.  The trailing s_nop gives the matrix
+// instructions that read hi / lo the two wait states after a VALU write.
 __device__ __forceinline__ void mul_f16pair_split(uint32_t q, float d0, float d1, uint32_t& hi,
                                                   uint32_t& lo) {
   uint32_t h, l;
   asm("v_fma_mixlo_f16 %0, %2, %3, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n\t"
       "v_fma_mixhi_f16 %0, %2, %4, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
       "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
-      "v_fma_mixhi_f16 %1, %2, %4, -%0 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+      "v_fma_mixhi_f16 %1, %2, %4, -%0 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+      "s_nop 1"
       : "=&v"(h), "=&v"(l)
       : "v"(q), "v"(d0), "v"(d1));
   hi = h;
