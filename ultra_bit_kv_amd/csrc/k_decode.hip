@@ -138,8 +138,8 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int sb_n = (nsink + kPage - 1) / kPage;
   const int ring_lo = max(sq, c.s_sink);
   const int cnt = len > ring_lo ? len - ring_lo : 0;
-  const int b0 = (ring_lo - c.s_sink) % c.ring_cap;
-  const int rb_n = cnt > 0 ? c.ring_cap / kPage : 0;
+  const int b0 = cnt > 0 ? (ring_lo - c.s_sink) % c.ring_cap : 0;
+  const int rb_n = ring_blocks_live(len, ring_lo, c.s_sink, c.ring_cap);
   const int n_wu = sb_n + rb_n;
   const int n_split = decode_splits(DecodeWork{n_pairs, n_wu}, quota, smax);
   // (products stay below 2^31 within the config limits)
@@ -150,10 +150,13 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int total_units = max(1, (pe - pb) + kWinCost * (we - wb));
   const PrioSteps prio = prio_steps(total_units, blockIdx.x / cus);   // (dispatch round on its CU)
   set_priority(prio, total_units);
-  auto win_block = [&](int u) { return u < sb_n ? u : c.sink_blocks + (u - sb_n); };
+  // window block u: sink block u, then the live ring blocks from the one
+  // holding the oldest live row (b0), in ring order
+  auto ring_blk = [&](int u) { return (b0 / kPage + (u - sb_n)) % (c.ring_cap / kPage); };
+  auto win_block = [&](int u) { return u < sb_n ? u : c.sink_blocks + ring_blk(u); };
   auto win_slot_ok = [&](int u, int t) {
     if (u < sb_n) return kPage * u + t < nsink;
-    const int off = (kPage * (u - sb_n) + t - b0 + c.ring_cap) % c.ring_cap;
+    const int off = (kPage * ring_blk(u) + t - b0 + c.ring_cap) % c.ring_cap;
     return off < cnt;
   };
   // ---- per-lane MFMA column n = (group gi, KV head kh of the wave, head hl of the pass)

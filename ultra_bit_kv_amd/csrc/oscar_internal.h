@@ -155,8 +155,18 @@ __host__ __device__ constexpr int rec_words(int hp) { return rec_o_offset(hp) + 
 
 struct DecodeWork {
   int n_pairs;                   // INT2 page pairs
-  int n_wu;                      // BF16 window blocks visited
+  int n_wu;                      // BF16 window blocks visited (sink blocks, then live ring blocks)
 };
+
+// Ring blocks that hold live rows: the live slots are the cnt = len -
+// ring_lo offsets b0, b0 + 1, ... (mod R) from b0 = (ring_lo - S_sink) mod R;
+// the blocks visited are b0 / 16, b0 / 16 + 1, ... (mod R / 16).
+__host__ __device__ inline int ring_blocks_live(int len, int ring_lo, int s_sink, int ring_cap) {
+  if (ring_cap <= 0 || len <= ring_lo) return 0;
+  const int cnt = len - ring_lo, b0 = (ring_lo - s_sink) % ring_cap;
+  const int nb = (b0 % kPage + cnt + kPage - 1) / kPage;
+  return nb < ring_cap / kPage ? nb : ring_cap / kPage;
+}
 
 __host__ __device__ inline DecodeWork decode_work(int len, int s_sink, int s_keep, int s_flush,
                                                   int ring_cap) {
@@ -168,7 +178,7 @@ __host__ __device__ inline DecodeWork decode_work(int len, int s_sink, int s_kee
   w.n_pairs = ((nq + kPage - 1) / kPage + 1) / 2;
   const int nsink = len < s_sink ? len : s_sink;
   const int ring_lo = sq > s_sink ? sq : s_sink;
-  w.n_wu = (nsink + kPage - 1) / kPage + (len > ring_lo ? ring_cap / kPage : 0);
+  w.n_wu = (nsink + kPage - 1) / kPage + ring_blocks_live(len, ring_lo, s_sink, ring_cap);
   return w;
 }
 
