@@ -36,6 +36,9 @@ Readings (the notes leave these open):
 4. A constant channel (max = min) has Delta16 = 0; it decodes to min, kept as
    z16 = bf16(min) with Delta16 = 0 (K^ = z16 when Delta16 = 0).
 5. Dequantized key: k^ = s16 * Delta16 * (Q - z16) in fp64.
+6. A zero extreme of a channel's block (min or max) is taken as +0: -0 and
+   +0 are the same value, and the stored z of a block whose minimum is zero
+   is then bf16(-0 / Delta) = -0 whichever zero the block held.
 """
 
 import math
@@ -62,7 +65,7 @@ def channel_quantize(u_bits):
     """Per-channel INT2 of one block of G tokens, u16 rows [G, d]:
     (codes uint8 [G, d], delta16 [d], z16 [d]) as bf16 bits."""
     u = bf16_bits_to_f64(np.asarray(u_bits, np.uint16))
-    mn, mx = u.min(axis=0), u.max(axis=0)
+    mn, mx = u.min(axis=0) + 0.0, u.max(axis=0) + 0.0   # a zero extreme is +0 (reading 6)
     d16 = f64_to_bf16_bits((mx - mn) / 3.0)
     dl = bf16_bits_to_f64(d16)
     const = dl == 0

@@ -110,3 +110,34 @@ def test_ots_keys_error_bound_and_token_norm_imbalance():
 def test_storage_figure():
     # "32 + 2 = 34 bytes" per INT2 key token-head with OTS at d = 128
     assert ots.key_bytes_per_token_head(128) == 34
+
+
+def test_norm_independent_of_channel_order():
+    # rows whose squares span more than 53 bits (so a running fp64 sum would
+    # depend on the order): the token scale and the normalized row are the
+    # same for every permutation of the channels (reading 1: one rounding of
+    # the exact sum), and the scale is bf16(sqrt) of the exact rational sum
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        row = rng.standard_normal(128) * 2.0 ** rng.integers(-30, 30, 128)
+        k = _b(row[None, :])
+        s16, u16 = ots.ots_scale(k)
+        exact = sum(Fraction(float(x)) ** 2 for x in bf16_bits_to_f64(k[0]))
+        assert s16[0] == _b(np.sqrt(np.float64(float(exact))))[0]
+        for _ in range(3):
+            p = rng.permutation(128)
+            s2, u2 = ots.ots_scale(k[:, p])
+            assert s2[0] == s16[0] and np.array_equal(u2[0], u16[0, p])
+
+
+def test_zero_extreme_is_positive_zero():
+    # a channel whose block minimum is zero, held once as -0 and once as +0:
+    # both give the same parameters (reading 6)
+    base = np.linspace(0.0, 0.75, 32)
+    a = _b(base[:, None])
+    b = a.copy()
+    b[0, 0] = 0x8000                     # -0 in place of +0
+    ca, da, za = ots.channel_quantize(a)
+    cb, db, zb = ots.channel_quantize(b)
+    assert np.array_equal(ca, cb) and np.array_equal(da, db) and np.array_equal(za, zb)
+    assert za[0] == 0x8000               # bf16(-(+0) / Delta) = -0
