@@ -202,7 +202,7 @@ int decode_slots_per_cu(const CacheArgs& a, const DecodePlan& plan, bool bf16) {
   (void)hipGetDevice(&dev);
   const long long key =
       ((((((((long long)dev * 2 + (bf16 ? 1 : 0)) * 8 + a.ng) * 32 + plan.hp) * 8 + plan.wh) * 4 +
-         plan.kh) * 8 + plan.ring) * 2 + (bf16 ? 0 : a.key_mode));
+         plan.kh) * 8 + plan.ring) * 2 + (bf16 ? 0 : a.key_mode)) * 2 + (bf16 ? 0 : plan.ps);
   std::lock_guard<std::mutex> lock(mu);
   for (const auto& m : memo)
     if (m.first == key) return m.second;
@@ -465,12 +465,23 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
   int cus = 256;
   int st = check_device(&cus);
   if (st != OSCAR_OK) return st;
-  const int64_t rows = (int64_t)(a.hkv / (plan.wh * plan.kh)) * plan.passes;
-  const int64_t slots =
-      std::max<int64_t>(1, (int64_t)cus * decode_slots_per_cu(a, plan, bf16) * kFillPercent / 100);
   // Every launch keeps to the split limit the workspace is sized for (that
   // of a full launch), so a short last launch fits in it too.
   const int cap = cap_override > 0 ? cap_override : max_splits(sh, std::min(n_seqs, kMaxScanSeqs));
+  // Work-group rows: WH groups of KH KV heads per work-group, or (when such
+  // items cannot fill the device within the split limit: small batches) one
+  // group of KH heads whose pairs the WH waves divide.
+  const int64_t rows_heads = (int64_t)(a.hkv / (plan.wh * plan.kh)) * plan.passes;
+  plan.ps = 0;
+  if (!bf16 && plan.wh > 1) {
+    plan.ps = 1;
+    const int64_t slots_ps =
+        std::max<int64_t>(1, (int64_t)cus * decode_slots_per_cu(a, plan, bf16) * kFillPercent / 100);
+    plan.ps = (int64_t)std::min(n_seqs, kMaxScanSeqs) * rows_heads * cap < slots_ps ? 1 : 0;
+  }
+  const int64_t rows = plan.ps ? (int64_t)(a.hkv / plan.kh) * plan.passes : rows_heads;
+  const int64_t slots =
+      std::max<int64_t>(1, (int64_t)cus * decode_slots_per_cu(a, plan, bf16) * kFillPercent / 100);
   static thread_local ItemOrder order;
   static thread_local SplitCounts counts;
   // Launches of at most kMaxScanSeqs sequences, in stream order.

@@ -82,7 +82,7 @@ struct PairGeom {
 // it are counted from their types (a window half is 4 loads, a pair 2 NI),
 // the tail re-requests the last item so the counts stay exact, and no other
 // vector memory access of the wave is outstanding meanwhile.
-template <int NG, int HP, int KH, int WH, int D, int KM>
+template <int NG, int HP, int KH, int WH, int D, int KM, int PS>
 __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqArgs s, int quota,
                                                               int passes, int smax, int cus, ItemOrder order,
                                                               const uint16_t* __restrict__ q_rot,
@@ -102,7 +102,12 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, qd = lane >> 4;
-  const int rows = (c.hkv / (WH * KH)) * passes;
+  // PS = 0: the WH waves take WH groups of KH adjacent KV heads, all walking
+  // the split's blocks and pages; PS = 1 (small batches): the waves share one
+  // group of KH heads and divide the split's pairs and window blocks, then
+  // combine their softmax states (fewer, larger work-groups' worth of
+  // records; three work-groups per compute unit even for one sequence)
+  const int rows = (PS ? c.hkv / KH : c.hkv / (WH * KH)) * passes;
 
   // ---- the item of this work-group
   WgItem it;
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const int local = it.local;
   const int split = local / rows, row = local % rows;
   const int hgrp = row / passes, pass = row % passes;
-  const int hw = (hgrp * WH + wave) * KH;   // first KV head of this wave
+  const int hw = (PS ? hgrp : hgrp * WH + wave) * KH;   // first KV head of this wave
 
   const int slot = it.slot;
   int len = it.len;
@@ -176,15 +181,22 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("" : "+s"(ring)::"memory");   // (an SGPR operand: device code only)
 #endif
-  const int np = min(pe - pb, kMaxPairsPerSplit);                 // pairs of this split
-  const int nwin = 2 * (we - wb) * KH;                            // window items (K, V halves)
+  // this wave's pairs k (split pair pair_of(k)) and window blocks (win_u)
+  const int sp_pairs = min(pe - pb, kMaxPairsPerSplit);           // pairs of this split
+  const int np = PS ? (sp_pairs > wave ? (sp_pairs - wave + WH - 1) / WH : 0) : sp_pairs;
+  const int nwb = PS ? (we - wb > wave ? (we - wb - wave + WH - 1) / WH : 0) : we - wb;
+  const int nwin = 2 * nwb * KH;                                  // window items (K, V halves)
+  auto pair_of = [&](int k) { return PS ? wave + WH * k : k; };
+  auto win_u = [&](int tt) { return PS ? wb + wave + WH * (tt / KH) : wb + tt / KH; };
   const int n_items = nwin + np;
   const size_t page_stride = (size_t)c.hkv * G::PB;
   const uint8_t* wave_base = c.pages + (size_t)hw * G::PB;        // the wave's first head of page 0
   const uint8_t* win_base = (const uint8_t*)(c.win + ((size_t)(row_ok ? slot : 0) * c.hkv + hw) *
                                                          c.win_blocks * (2 * kPage * kD));
   // page ids of pair k (the split's last pair for k >= np); -1: unmapped
-  auto pair_ids = [&](int k) { return *(const u32x2*)&s_pages[2 * max(0, min(k, np - 1))]; };
+  auto pair_ids = [&](int k) {
+    return *(const u32x2*)&s_pages[2 * pair_of(max(0, min(k, np - 1)))];
+  };
   // Window half placement in LDS: 16-byte chunk (t, j) of a half (row t, bytes
   // 16 j .. 16 j + 15 of its 256) sits at chunk 16 t + (j ^ t), so the 16
   // lanes that read one column of chunks hit 16 different bank groups.  Load
@@ -198,7 +210,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   }
   auto request_win = [&](int item, lds_u8* dst) {
     const int tt = item >> 1, half = item & 1;
-    const int u = wb + tt / KH, k = tt % KH;
+    const int u = win_u(tt), k = tt % KH;
     const uint8_t* src = uniform_ptr(win_base + ((size_t)k * c.win_blocks + win_block(u)) *
                                                     (4 * kPage * kD) + half * (2 * kPage * kD));
     load_lds16<0>(src + woff[0], dst);
@@ -323,6 +335,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
       qo[2 * e + 1] = bf16_bits_to_f32(w[e] >> 16) * f;
     }
   }
+
   // page ids visible; ids_ok: every page of the split's pairs with INT2
   // tokens is mapped, so only the last pairs (past S_quant) need masks
   const bool ids_ok = !__syncthreads_or(bad_ids);
@@ -374,7 +387,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   short4_t win_phi = {0, 0, 0, 0}, win_plo = {0, 0, 0, 0};
   for (int it_w = 0; it_w < nwin; ++it_w) {
     const int tt = it_w >> 1, half = it_w & 1;
-    const int u = wb + tt / KH, k = tt % KH;
+    const int u = win_u(tt), k = tt % KH;
     set_priority(prio, kWinCost * (we - u) + np);
     wait_item(it_w);
     const lds_u8* P = ring + (it_w % D) * G::SLOT;
@@ -513,12 +526,12 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
         const u32x4 w0 = *(lds_u32x4*)(pbw + 4 * base);
         const u32x4 w1 = *(lds_u32x4*)(pbw + 4 * (base + 8));
         const u32x4 qb = __builtin_bit_cast(u32x4, bq[cc]);
-        uint32_t hw[4], lw[4];
+        uint32_t hv[4], lv[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          mul_f16pair_split(qb[v], __uint_as_float(w0[v] << 16), __uint_as_float(w1[v] << 16), hw[v],
-                            lw[v]);
-        const u32x4 hi = {hw[0], hw[1], hw[2], hw[3]}, lo = {lw[0], lw[1], lw[2], lw[3]};
+          mul_f16pair_split(qb[v], __uint_as_float(w0[v] << 16), __uint_as_float(w1[v] << 16), hv[v],
+                            lv[v]);
+        const u32x4 hi = {hv[0], hv[1], hv[2], hv[3]}, lo = {lv[0], lv[1], lv[2], lv[3]};
         uint32_t wa = (cc < 2) ? ka[0][0] : ka[0][1];
         uint32_t wb2 = (cc < 2) ? kb[0][0] : kb[0][1];
         if (cc & 1) {
@@ -562,7 +575,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
         x[4 + r] *= bf16_bits_to_f32((r & 1) ? wb3 >> 16 : wb3 & 0xFFFFu);
       }
     }
-    const int tok = 32 * (pb + k);   // INT2 token index of slot 0 of page A
+    const int tok = 32 * (pb + pair_of(k));   // INT2 token index of slot 0 of page A
     if (!(ids_ok && tok + 32 <= nq)) {   // slots past S_quant, or unmapped pages
       const u32x2 own = pair_ids(k);
       const bool oka = (int)own[0] >= 0, okb = (int)own[1] >= 0;
@@ -618,6 +631,47 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   // ---- this wave's partial record: (max, sum, unnormalized o') per head of the pass
   st.l = rows_sum(st.l);
   st.z = rows_sum(st.z);
+  if constexpr (PS && WH > 1) {
+    // the waves hold partial states of the same columns: rescale each to the
+    // common maximum and add them up in wave 0, through the idle ring's LDS
+    // ([WH][16] maxima, then waves 1.. : 32 accumulator values, l and z per lane)
+    float* sm = (float*)s_ring;
+    float* sb = sm + WH * 16;
+    static_assert((WH * 16 + (WH - 1) * 64 * 34) * 4 <= WH * D * G::SLOT, "combine space");
+    __syncthreads();   // every wave's ring is idle (each has waited for all its loads)
+    if (qd == 0) sm[wave * 16 + r16] = st.m;
+    __syncthreads();
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < WH; ++w) M = fmaxf(M, sm[w * 16 + r16]);
+    const float sc = st.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(st.m - M);
+    if (wave > 0) {
+      float* dst = sb + ((wave - 1) * 64 + lane) * 34;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[4 * j + r] = acc[j][r] * sc;
+      dst[32] = st.l * sc;
+      dst[33] = st.z * sc;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= sc;
+    st.l *= sc;
+    st.z *= sc;
+#pragma unroll
+    for (int w = 1; w < WH; ++w) {
+      const float* src = sb + ((w - 1) * 64 + lane) * 34;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] += src[4 * j + r];
+      st.l += src[32];
+      st.z += src[33];
+    }
+    st.m = M;
+  }
   float* rec = partials + ((((size_t)i * c.hkv + h) * passes + pass) * smax + split) * PW;
   if (qd == 0 && gi == 0 && hl < nh) {   // one lane per (KV head, query head) column
     rec[hl] = st.m;
@@ -647,7 +701,7 @@ static auto with_waves_ring(int wh, F&& f) {
   return f.template run<1, D>();
 }
 
-template <int NG, int HP, int KH, int KM>
+template <int NG, int HP, int KH, int KM, int PS>
 struct SplitLaunch {
   const CacheArgs& c;
   const SeqArgs& s;
@@ -657,19 +711,19 @@ struct SplitLaunch {
   hipStream_t stream;
   template <int WH, int D>
   hipError_t run() const {
-    hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, WH, D, KM>), dim3(plan.grid), dim3(64 * WH), 0,
+    hipLaunchKernelGGL((int2_decode_kernel<NG, HP, KH, WH, D, KM, PS>), dim3(plan.grid), dim3(64 * WH), 0,
                        stream, c, s, plan.quota, plan.passes, plan.smax, plan.cus, *plan.order, q_rot,
                        partials);
     return hipGetLastError();
   }
 };
 
-template <int NG, int HP, int KH, int KM>
+template <int NG, int HP, int KH, int KM, int PS>
 struct SplitOccupancy {
   template <int WH, int D>
   int run() const {
     int nb = 0;
-    auto* kernel = &int2_decode_kernel<NG, HP, KH, WH, D, KM>;
+    auto* kernel = &int2_decode_kernel<NG, HP, KH, WH, D, KM, PS>;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 64 * WH, 0);
     return e == hipSuccess && nb > 0 ? nb : 1;
   }
@@ -681,7 +735,8 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
                                   int phases, hipStream_t stream) {
   if (phases & kDecodeSplit) {
     const hipError_t e =
-        with_waves_ring<KM>(plan.wh, SplitLaunch<NG, HP, KH, KM>{c, s, plan, q_rot, partials, stream});
+        plan.ps ? with_waves_ring<KM>(plan.wh, SplitLaunch<NG, HP, KH, KM, 1>{c, s, plan, q_rot, partials, stream})
+                : with_waves_ring<KM>(plan.wh, SplitLaunch<NG, HP, KH, KM, 0>{c, s, plan, q_rot, partials, stream});
     if (e != hipSuccess) return e;
   }
   if (phases & kDecodeMerge)
@@ -691,8 +746,9 @@ static hipError_t launch_decode_t(const CacheArgs& c, const SeqArgs& s, const De
 }
 
 template <int NG, int HP, int KH, int KM>
-static int wgs_per_cu_t(int wh) {
-  return with_waves_ring<KM>(wh, SplitOccupancy<NG, HP, KH, KM>{});
+static int wgs_per_cu_t(int wh, int ps) {
+  return ps ? with_waves_ring<KM>(wh, SplitOccupancy<NG, HP, KH, KM, 1>{})
+            : with_waves_ring<KM>(wh, SplitOccupancy<NG, HP, KH, KM, 0>{});
 }
 
 // The (groups, heads per pass, KV heads per wave, key mode) shapes the
@@ -735,7 +791,7 @@ static auto with_shape(int ng, int hp, int kh, int km, F&& f) {
 struct OccupancyQuery {
   const DecodePlan& plan;
   template <int NG, int HP, int KH, int KM>
-  int operator()() const { return wgs_per_cu_t<NG, HP, KH, KM>(plan.wh); }
+  int operator()() const { return wgs_per_cu_t<NG, HP, KH, KM>(plan.wh, plan.ps); }
   int fail() const { return 1; }
 };
 

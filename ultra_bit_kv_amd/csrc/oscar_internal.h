@@ -223,6 +223,7 @@ struct DecodePlan {
   int kh;                        // KV heads per wave (1, or 2 when a head's columns fill half a tile)
   int wh;                        // waves per work-group
   int ring;                      // INT2 split kernel: page pairs per wave in its LDS ring (2 or 4)
+  int ps;                        // INT2 split kernel: 1 = the waves of a work-group share one KV-head group
   int grid;                      // work-groups of the split launch (= its work items)
   int cus;                       // compute units: work-group b runs in dispatch round b / cus
   const ItemOrder* order;        // work item of each work-group (host memory, passed by value)
