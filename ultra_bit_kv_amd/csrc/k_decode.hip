@@ -65,6 +65,19 @@ struct PairGeom {
   static constexpr int SLOT = 2 * RB > 4096 ? 2 * RB : 4096;
 };
 
+// LDS of the split kernel: the ring, the split's page ids, the item lookup
+// and (QS) a query block of 256 * KH * HP bytes per wave.  The query gets
+// its own block when three work-groups per compute unit still fit (1 KB per
+// work-group kept for allocation granularity); otherwise it passes through
+// the ring's last slot before that slot's first item is requested.
+template <int NG, int HP, int KH, int WH, int D, int KM>
+struct DecodeLds {
+  using G = PairGeom<NG, KH, KM>;
+  static constexpr int BASE = WH * D * G::SLOT + 4 * kMaxWgPages + 64;
+  static constexpr int QB = 256 * KH * HP;
+  static constexpr bool QS = 3 * (BASE + WH * QB + 1024) <= 160 * 1024;
+};
+
 // Work-group = one work item (sequence, context split, group of WH adjacent
 // KV head groups, query-head pass); items are numbered sequence-major, then
 // split, then head group, and the launch has exactly one work-group per
@@ -95,6 +108,8 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   static_assert((D - 1) * G::PAIR_LOADS <= 63, "vmcnt limit");
   __shared__ __align__(16) uint8_t s_ring[WH * D * G::SLOT];
   __shared__ __align__(8) int s_pages[kMaxWgPages];
+  using L = DecodeLds<NG, HP, KH, WH, D, KM>;
+  __shared__ __align__(16) uint8_t s_qblk[L::QS ? WH * L::QB : 16];
   __shared__ int s_wsum[WH];
   __shared__ int s_item[4];   // sequence, item within it, its slot and length
 
@@ -173,7 +188,6 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   const float C2 = kLog2e * 0.08838834764831845f;                // log2(e) / sqrt(128)
   const float K1 = C2 * 16777216.0f;                              // undo the 2^-24 code scaling
 
-  // ---- the lane's 32 query channels straight into registers; the split's page ids to LDS
   // ---- the ring of this wave.  Its address is passed through an empty asm
   // statement: the compiler then cannot assume anything about the ring's
   // contents, which only the direct-to-LDS loads write.
@@ -266,32 +280,95 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     }
   };
 
-  // the first window items do not depend on the page ids: request them
-  // before the query and page-id loads (requests stay in item order)
-  const int d_pre = np == 0 ? D : min(D, nwin);
+  // ---- start-up, in this order (all direct-to-LDS): the split's page ids
+  // (wave w: ids 64 w .. 64 w + 63), the query rows of the wave's columns
+  // (into the wave's query block, or ring slot D - 1), the first window
+  // items (into slots 0 .. D - 2 when the query uses slot D - 1); then, once
+  // the ids and the query are in, the window item of slot D - 1 if it was
+  // held back, the check of the ids, one barrier and the first pairs.
+  // Nothing waits for window data before the barrier, and the ring requests
+  // stay in item order.
+  const int n_wg_pages = min(2 * (pe - pb), kMaxWgPages);
+  const int id_lim = min(n_pages, c.max_pages) - 2 * pb;   // ids t < id_lim lie in the row, with INT2 tokens
+  if (64 * wave < n_wg_pages) {
+    const int t = 64 * wave + lane;
+    if (t < id_lim && t < n_wg_pages)
+      __builtin_amdgcn_global_load_lds(bt + 2 * pb + t, (lds_u8*)(s_pages + 64 * wave), 4, 0, 0);
+    else if (t < n_wg_pages)
+      s_pages[t] = -1;
+  }
+  // Query block: row kk * HP + hl = query head (hw + kk) g + pass HP + hl,
+  // 256 bytes each; load m brings 16-byte chunks 64 m + lane.
+  lds_u8* const qblk = L::QS ? (lds_u8*)(s_qblk + wave * L::QB) : ring + (D - 1) * G::SLOT;
+  {
+    lds_u8* qdst = qblk;
+    constexpr int QR = KH * HP;
+    static_assert(256 * QR <= G::SLOT, "the query block fits a ring slot");
+#pragma unroll
+    for (int m = 0; m < (QR + 3) / 4; ++m) {
+      const int x = 64 * m + lane, r = x >> 4;
+      const int kk = r / HP, hq_l = r % HP;
+      if (r < QR && hq_l < nh) {
+        const uint8_t* src = (const uint8_t*)(q_rot + ((size_t)i * c.hq + (size_t)(hw + kk) * c.g +
+                                                        (size_t)pass * HP + hq_l) * kD) + 16 * (x & 15);
+        load_lds16<0>(src, qdst + 1024 * m);
+      }
+    }
+  }
+  // items that need no page id: the windows (and, without pairs, the
+  // re-requests of the last window)
+  const int d_win = np == 0 ? D : min(D, nwin);
+  const int d_a = L::QS ? d_win : min(d_win, D - 1);   // requested before the query is read
   if (n_items > 0) {
 #pragma unroll
     for (int d = 0; d < D; ++d)
-      if (d < d_pre) request(d, u32x2{0u, 0u});
+      if (d < d_a) request(d, u32x2{0u, 0u});
   }
-
+  // wait for the ids and the query: only the d_a window items (4 loads each) are younger
+  {
+    const int after = n_items > 0 ? d_a : 0;
+    if (after == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::WIN_LOADS) : "memory");
+    else if (after == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::WIN_LOADS) : "memory");
+    else if (after == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * G::WIN_LOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * G::WIN_LOADS) : "memory");
+  }
   u32x4 wq[4];
   {
+    const lds_u8* qrow = qblk + 256 * (kh * HP + hl) + 64 * qd;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    const uint16_t* qp = q_rot + ((size_t)i * c.hq + (size_t)h * c.g + (size_t)pass * HP +
-                                  (colv ? hl : 0)) * kD + 32 * qd;
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) wq[cc] = colv ? *(const u32x4*)(qp + 8 * cc) : z;
+    for (int cc = 0; cc < 4; ++cc) {
+      const u32x4 v = *(lds_u32x4*)(qrow + 16 * cc);
+      wq[cc] = colv ? v : z;
+    }
   }
-  const int n_wg_pages = min(2 * (pe - pb), kMaxWgPages);
+  u32x4 wqo = {0u, 0u, 0u, 0u};   // OScaR keys: channels 32 gi + 8 qd .. + 7 of the column's head
+  if constexpr (KM) {
+    const u32x4 v = *(lds_u32x4*)(qblk + 256 * (kh * HP + hl) + 2 * (32 * (gi < NG ? gi : 0) + 8 * qd));
+    if (colv) wqo = v;
+  }
+  // slot D - 1 is free once the query is in registers
+  if constexpr (!L::QS) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (n_items > 0 && d_win == D) request(D - 1, u32x2{0u, 0u});
+  }
+
+  // check the wave's ids in place (-1: unmapped); longer splits load the
+  // rest here
   int bad_ids = 0;   // a page holding INT2 tokens without a valid page id
-  for (int t = tid; t < n_wg_pages; t += 64 * WH) {
-    const int pg = 2 * pb + t;
-    int ph = -1;
-    if (pg < n_pages && pg < c.max_pages) ph = bt[pg];
-    const bool ok = ph >= 0 && ph < c.num_pages;
-    s_pages[t] = ok ? ph : -1;
-    bad_ids |= (!ok && pg < n_pages);
+  auto check_ids = [&](int t) {
+    if (t < n_wg_pages) {
+      int ph = s_pages[t];
+      const bool ok = t < id_lim && ph >= 0 && ph < c.num_pages;
+      if (!ok) s_pages[t] = -1;
+      bad_ids |= (!ok && t < n_pages - 2 * pb);
+    }
+  };
+  check_ids(64 * wave + lane);
+  for (int t = 64 * (wave + WH) + lane; t - lane < n_wg_pages; t += 64 * WH) {   // long splits
+    if (t < n_wg_pages) s_pages[t] = t < id_lim ? bt[2 * pb + t] : -1;
+    check_ids(t);
   }
   // group sums of q' for the zero-point term: each lane adds its 32 channels
   // if they lie in its column's group, then the four lanes of the column add up
@@ -325,25 +402,30 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
     sh = min(100, max(-100, 13 - ((int)(m >> 7) - 127)));
     sh = __builtin_amdgcn_readfirstlane(sh);
     const float f = __builtin_ldexpf(1.0f, sh - 24);
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (colv)
-      w = *(const u32x4*)(q_rot + ((size_t)i * c.hq + (size_t)h * c.g + (size_t)pass * HP + hl) * kD +
-                          32 * gi + 8 * qd);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      qo[2 * e] = bf16_bits_to_f32(w[e] & 0xFFFFu) * f;
-      qo[2 * e + 1] = bf16_bits_to_f32(w[e] >> 16) * f;
+      qo[2 * e] = bf16_bits_to_f32(wqo[e] & 0xFFFFu) * f;
+      qo[2 * e + 1] = bf16_bits_to_f32(wqo[e] >> 16) * f;
     }
   }
 
   // page ids visible; ids_ok: every page of the split's pairs with INT2
-  // tokens is mapped, so only the last pairs (past S_quant) need masks
-  const bool ids_ok = !__syncthreads_or(bad_ids);
+  // tokens is mapped, so only the last pairs (past S_quant) need masks.  The
+  // barrier carries no memory fence (a fence would wait for the window loads
+  // in flight): the ids' loads were waited for with the query, and the LDS
+  // writes of this wave complete with lgkmcnt(0).
+  const bool wbad = __any(bad_ids);
+  if (lane == 0) s_wsum[wave] = wbad ? 1 : 0;   // (free: the item lookup is done)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  int any_bad = 0;
+#pragma unroll
+  for (int w = 0; w < WH; ++w) any_bad |= s_wsum[w];
+  const bool ids_ok = !any_bad;
 
   if (n_items > 0) {
 #pragma unroll
     for (int d = 0; d < D; ++d)
-      if (d >= d_pre) request(d, pair_ids(d - nwin));
+      if (d >= d_win) request(d, pair_ids(d - nwin));
   }
 
   // ---- B operands: the bf16 query for the window blocks, and for the INT2
