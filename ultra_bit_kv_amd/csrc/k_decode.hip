@@ -78,6 +78,31 @@ struct DecodeLds {
   static constexpr bool QS = 3 * (BASE + WH * QB + 1024) <= 160 * 1024;
 };
 
+// s_waitcnt vmcnt for na loads groups in flight of which w are window halves
+// (WL loads each) and na - w page pairs (PL loads each), 0 <= w <= na < D.
+template <int WL, int PL, int NA, int W>
+__device__ __forceinline__ void vm_wait_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W * WL + (NA - W) * PL) : "memory");
+}
+template <int D, int WL, int PL>
+__device__ __forceinline__ void wait_loads(int na, int w) {
+  static_assert(D >= 2 && D <= 4, "ring depth");
+  if (na == 0) return vm_wait_n<WL, PL, 0, 0>();
+  if (na == 1) return w ? vm_wait_n<WL, PL, 1, 1>() : vm_wait_n<WL, PL, 1, 0>();
+  if constexpr (D >= 3) {
+    if (na == 2) {
+      if (w == 2) return vm_wait_n<WL, PL, 2, 2>();
+      return w ? vm_wait_n<WL, PL, 2, 1>() : vm_wait_n<WL, PL, 2, 0>();
+    }
+  }
+  if constexpr (D >= 4) {
+    if (w == 3) return vm_wait_n<WL, PL, 3, 3>();
+    if (w == 2) return vm_wait_n<WL, PL, 3, 2>();
+    return w ? vm_wait_n<WL, PL, 3, 1>() : vm_wait_n<WL, PL, 3, 0>();
+  }
+  vm_wait_n<WL, PL, 0, 0>();   // (not reached)
+}
+
 // Work-group = one work item (sequence, context split, group of WH adjacent
 // KV head groups, query-head pass); items are numbered sequence-major, then
 // split, then head group, and the launch has exactly one work-group per
@@ -90,11 +115,11 @@ struct DecodeLds {
 // ring items per KV head of the wave (its 16 K rows, then its 16 V rows),
 // then its INT2 page pairs (one item: the wave's KV heads' bytes of both
 // pages).  Item j + D is requested as soon as item j has been read out of its
-// slot into registers, so D - 1 items are in flight while one is processed.
+// slot into registers, so D items are in flight while one is processed.
 // Each item is waited for with an exact vmcnt: the loads of the items after
-// it are counted from their types (a window half is 4 loads, a pair 2 NI),
-// the tail re-requests the last item so the counts stay exact, and no other
-// vector memory access of the wave is outstanding meanwhile.
+// it (up to j + D - 1 and the last item) are counted from their types (a
+// window half is 4 loads, a pair 2 NI), and no other vector memory access of
+// the wave is outstanding meanwhile.
 template <int NG, int HP, int KH, int WH, int D, int KM, int PS>
 __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqArgs s, int quota,
                                                               int passes, int smax, int cus, ItemOrder order,
@@ -250,34 +275,20 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
       }
     }
   };
-  // request item j (the last item for j >= n_items) into slot j % D
+  // request item j into slot j % D (nothing past the last item)
   auto request = [&](int j, u32x2 ids) {
-    const int jj = min(j, n_items - 1);
+    if (j >= n_items) return;
     lds_u8* dst = ring + (j % D) * G::SLOT;
-    if (jj < nwin) request_win(jj, dst);
+    if (j < nwin) request_win(j, dst);
     else request_pair(ids, dst);
   };
-  // wait until item j is in its slot: the D - 1 items after it (clamped to
-  // the last item) may still be loading
+  // wait until item j is in its slot: the items after it up to j + D - 1
+  // that exist may still be loading (windows first, then pairs)
   auto wait_item = [&](int j) {
-    const int wins = max(0, min(D - 1, nwin - (j + 1)));   // window halves among them
-    const int wins_c = n_items - 1 < nwin ? D - 1 : wins;   // all of them when the last item is one
-    if constexpr (D == 2) {
-      if (wins_c) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::WIN_LOADS) : "memory");
-      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::PAIR_LOADS) : "memory");
-    } else if constexpr (D == 3) {
-      if (wins_c == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::WIN_LOADS) : "memory");
-      else if (wins_c == 1)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::WIN_LOADS + G::PAIR_LOADS) : "memory");
-      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::PAIR_LOADS) : "memory");
-    } else {
-      if (wins_c == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * G::WIN_LOADS) : "memory");
-      else if (wins_c == 2)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::WIN_LOADS + G::PAIR_LOADS) : "memory");
-      else if (wins_c == 1)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::WIN_LOADS + 2 * G::PAIR_LOADS) : "memory");
-      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * G::PAIR_LOADS) : "memory");
-    }
+    const int last = min(j + D - 1, n_items - 1);
+    const int na = max(0, last - j);                      // items in flight after j
+    const int wins = max(0, min(last, nwin - 1) - j);     // window halves among them
+    wait_loads<D, G::WIN_LOADS, G::PAIR_LOADS>(na, wins);
   };
 
   // ---- start-up, in this order (all direct-to-LDS): the split's page ids
@@ -315,8 +326,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
       }
     }
   }
-  // items that need no page id: the windows (and, without pairs, the
-  // re-requests of the last window)
+  // items that need no page id: the windows
   const int d_win = np == 0 ? D : min(D, nwin);
   const int d_a = L::QS ? d_win : min(d_win, D - 1);   // requested before the query is read
   if (n_items > 0) {
@@ -326,7 +336,7 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
   }
   // wait for the ids and the query: only the d_a window items (4 loads each) are younger
   {
-    const int after = n_items > 0 ? d_a : 0;
+    const int after = min(d_a, n_items);
     if (after == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::WIN_LOADS) : "memory");
     else if (after == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::WIN_LOADS) : "memory");
@@ -706,8 +716,6 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] *= 16777216.0f / (float)(1 << (2 * (j & 3)));
   }
-  // (the last D requests re-read the last item; they are waited for before
-  // the ring's LDS can be released at the end of the work-group)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- this wave's partial record: (max, sum, unnormalized o') per head of the pass
