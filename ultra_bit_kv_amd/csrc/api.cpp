@@ -499,6 +499,12 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
       total += cost[i];
       max_cost = std::max(max_cost, cost[i]);
     }
+    // Small batches whose work gives a full round of work-groups fewer than
+    // two units per wave: two thirds of the round (fewer records to merge,
+    // the split no slower; measured on a 32K bs1 row: split -0.6 us, merge
+    // -0.7 us; a 128K bs1 row keeps the full round)
+    int64_t slots_l = slots;
+    if (plan.ps && total * rows < 2 * slots * plan.wh) slots_l = std::max<int64_t>(1, slots * 2 / 3);
     // quota in 1/16 units; at most 255 pairs per split (the LDS page list)
     auto splits_of = [&](int64_t c16, int64_t q16) {
       return std::max<int64_t>(1, (16 * c16 + q16 - 1) / q16);
@@ -509,14 +515,14 @@ int plan_and_launch(const CacheArgs& a, DecodePlan plan, const DecodeShape& sh, 
       return n * rows;
     };
     const int64_t q_max = 16 * (kMaxPairsPerSplit - 1);
-    int64_t quota = std::max<int64_t>(32, (16 * total * rows + slots - 1) / slots);
+    int64_t quota = std::max<int64_t>(32, (16 * total * rows + slots_l - 1) / slots_l);
     quota = std::max<int64_t>(quota, (16 * max_cost + cap - 1) / cap);
     quota = std::min<int64_t>(quota, q_max);
-    if (items_of(quota) > slots) {   // smallest quota in (quota, limit] that fits (items fall as quota grows)
+    if (items_of(quota) > slots_l) {   // smallest quota in (quota, limit] that fits (items fall as quota grows)
       int64_t lo = quota, hi = q_max;
       while (hi - lo > 1) {
         const int64_t mid = (lo + hi) / 2;
-        (items_of(mid) > slots ? lo : hi) = mid;
+        (items_of(mid) > slots_l ? lo : hi) = mid;
       }
       quota = hi;
     }
