@@ -18,7 +18,8 @@
 // columns of its MFMA tiles.  The key stream is
 // staged 64 positions per barrier, processed in 32-position steps; the
 // work-group stages the keys in LDS as fp16
-// (K rows [token][channel] as fp16 hi + lo, V transposed [channel][token]),
+// (K rows [token][channel] as fp16 hi + lo, V transposed [row][token] with
+// row 16 j + u holding channel 8 u + j),
 // decoding every
 // position from wherever it lives (sink, INT2 page, ring, chunk rows), one
 // block ahead in registers.  Per block and wave:
@@ -35,19 +36,20 @@ namespace oscar {
 
 namespace {
 
-// Work-group shape: W waves of 16 query rows each; the staging threads take
-// 16 / (W / 4) ... positions each so that a stage always holds 64 positions.
+// Work-group shape: W waves of 16 query rows each.  Staging: 512 threads,
+// thread (token pair tp, channel octet u) takes positions 2 tp, 2 tp + 1 of a
+// 64-position stage, channels 8 u .. 8 u + 7.
 template <int W>
 struct PfShape {
   static constexpr int kWaves = W;
   static constexpr int kThreads = 64 * W;
   static constexpr int kRows = 16 * W;             // query rows per work-group
   static constexpr int kStage = 64;                // key positions staged per barrier
-  static constexpr int kStagePos = kStage / (kThreads / 16);   // positions per staging thread
+  static constexpr int kStageThreads = 512;        // (kStage / 2) pairs x 16 octets
   static constexpr int kKRow = kD + 8;   // staged key row in fp16 (padded: rows start 4 banks apart)
-  static constexpr int kVRow = kStage + 4;   // staged value row (one channel): the 8-byte pad
-                                             // spreads the rows a wave writes over the banks
-  static_assert(kStagePos * (kThreads / 16) == kStage, "a stage is 64 positions");
+  static constexpr int kVRow = kStage + 4;   // staged value row (one channel), 34 dwords: the
+                                             // 16 rows one instruction writes start on distinct banks
+  static_assert(kThreads >= kStageThreads, "a stage is 64 positions");
 };
 
 // LDS: the staging buffers during the key loop, the normalized o' rows after it.
@@ -56,7 +58,7 @@ struct PfStage {
   using S = PfShape<W>;
   _Float16 k[S::kStage][S::kKRow];    // keys [token][channel], fp16 part
   _Float16 kl[S::kStage][S::kKRow];   // remainders k - fp16(k)
-  _Float16 vt[kD][S::kVRow];          // values [channel][token]
+  _Float16 vt[kD][S::kVRow];          // values [row][token], row 16 j + u = channel 8 u + j
   int skip[S::kStage];                // position unreadable (unmapped page or past the row)
 };
 template <int W>
@@ -86,10 +88,10 @@ __device__ __forceinline__ void bf16x2_to_f32(uint32_t w, float& lo, float& hi) 
 }  // namespace
 
 template <int W>
-__global__ __launch_bounds__(64 * W) void prefill_attn_kernel(CacheArgs c, PrefillArgs a) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) void prefill_attn_kernel(CacheArgs c, PrefillArgs a) {
   using S = PfShape<W>;
   constexpr int kPfWaves = S::kWaves, kPfThreads = S::kThreads, kPfRows = S::kRows;
-  constexpr int kStage = S::kStage, kStagePos = S::kStagePos;
+  constexpr int kStage = S::kStage;
   __shared__ __align__(16) char smem[pf_lds<W>()];
   PfStage<W>& sg = *reinterpret_cast<PfStage<W>*>(smem);
   float(&fin)[kPfRows][kD + 4] = reinterpret_cast<PfFinal<W>*>(smem)->o;
@@ -134,12 +136,12 @@ __global__ __launch_bounds__(64 * W) void prefill_attn_kernel(CacheArgs c, Prefi
     }
   }
 
-  // ---- staging: thread (token t, channels 8u .. 8u+7) takes staged rows
-  // t + 32 m (m < kStagePos) of a stage
-  const int st_t = tid >> 4, st_u = tid & 15;
-  constexpr int kRowStep = kPfThreads / 16;
+  // ---- staging: thread (token pair tp, channels 8u .. 8u+7) takes staged
+  // rows 2 tp + m (m < 2) of a stage; threads from 512 on do not stage
+  const bool stager = tid < S::kStageThreads;
+  const int st_tp = tid >> 4, st_u = tid & 15;
   auto fetch = [&](int p0, int m, RawSlice& r) {
-    const int p = p0 + st_t + kRowStep * m;
+    const int p = p0 + 2 * st_tp + m;
     r.kind = 0;
     r.k = r.v = u32x4{0u, 0u, 0u, 0u};
     if (p >= len) return;
@@ -170,8 +172,9 @@ __global__ __launch_bounds__(64 * W) void prefill_attn_kernel(CacheArgs c, Prefi
       r.kind = 2;
     }
   };
-  auto deposit = [&](const RawSlice& r, int m) {
-    const int row = st_t + kRowStep * m;
+  // K rows as fp16 hi / lo of one position; returns its values as fp16
+  auto deposit = [&](const RawSlice& r, int m, half8& vh) {
+    const int row = 2 * st_tp + m;
     float kv[8], vv[8];
     if (r.kind == 1) {
 #pragma unroll
@@ -204,8 +207,24 @@ __global__ __launch_bounds__(64 * W) void prefill_attn_kernel(CacheArgs c, Prefi
     *(half8*)&sg.k[row][8 * st_u] = kh;
     *(half8*)&sg.kl[row][8 * st_u] = kl;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sg.vt[8 * st_u + j][row] = (_Float16)vv[j];
+    for (int j = 0; j < 8; ++j) vh[j] = (_Float16)vv[j];
     if (st_u == 0) sg.skip[row] = r.kind == 0 ? 1 : 0;
+  };
+  // both positions: the values go out as one 32-bit word (two tokens) per
+  // channel, channel 8u + j to row 16 j + u
+  auto deposit2 = [&](const RawSlice (&r)[2]) {
+    half8 v0, v1;
+    deposit(r[0], 0, v0);
+    deposit(r[1], 1, v1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // (the vector elements go through locals: a bit cast of an element
+      // of an ext_vector value compiles to element 0 for every j here)
+      const _Float16 e0 = v0[j], e1 = v1[j];
+      const uint32_t w = (uint32_t)__builtin_bit_cast(uint16_t, e0) |
+                         ((uint32_t)__builtin_bit_cast(uint16_t, e1) << 16);
+      __builtin_memcpy(&sg.vt[16 * j + st_u][2 * st_tp], &w, 4);   // (a byte copy: no type punning)
+    }
   };
 
   float4_t acc[8];
@@ -218,16 +237,19 @@ __global__ __launch_bounds__(64 * W) void prefill_attn_kernel(CacheArgs c, Prefi
   // a per-stage mask of such positions, built by the staging threads.
   const int int2_end = min(sq, lb);   // INT2 rows of the prefix: [S_sink, int2_end)
   const int nstage = (kend + kStage - 1) / kStage;
-  RawSlice cur[kStagePos], nxt[kStagePos];
+  RawSlice cur[2], nxt[2];
+  if (stager) {
 #pragma unroll
-  for (int m = 0; m < kStagePos; ++m) fetch(0, m, cur[m]);
+    for (int m = 0; m < 2; ++m) fetch(0, m, cur[m]);
+  }
   for (int ks = 0; ks < nstage; ++ks) {
     const int s0 = ks * kStage;
+    if (stager) {
+      deposit2(cur);
+      if (ks + 1 < nstage) {   // next stage in flight during this one
 #pragma unroll
-    for (int m = 0; m < kStagePos; ++m) deposit(cur[m], m);
-    if (ks + 1 < nstage) {   // next stage in flight during this one
-#pragma unroll
-      for (int m = 0; m < kStagePos; ++m) fetch(s0 + kStage, m, nxt[m]);
+        for (int m = 0; m < 2; ++m) fetch(s0 + kStage, m, nxt[m]);
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -276,16 +298,17 @@ __global__ __launch_bounds__(64 * W) void prefill_attn_kernel(CacheArgs c, Prefi
     }
     __syncthreads();   // the stage is consumed before the next one is deposited
 #pragma unroll
-    for (int m = 0; m < kStagePos; ++m) cur[m] = nxt[m];
+    for (int m = 0; m < 2; ++m) cur[m] = nxt[m];
   }
 
   // ---- normalize, then o = o' . R_V^T (or o' when the value transform is absorbed)
   const float l = rows_sum(st.l);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  // acc[j][r] is staged value row 16 j + 4 qd + r, i.e. channel 32 qd + 8 r + j
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) fin[16 * wave + r16][16 * j + 4 * qd + r] = acc[j][r] * inv;
+    for (int r = 0; r < 4; ++r) fin[16 * wave + r16][32 * qd + 8 * r + j] = acc[j][r] * inv;
   __syncthreads();
   auto out_row = [&](int rr) {   // output row of work-group row rr, or nullptr
     const int R = tile * kPfRows + rr;
