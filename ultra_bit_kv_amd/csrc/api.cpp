@@ -831,6 +831,7 @@ int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
   const int g = c.num_q_heads / c.num_kv_heads;
   std::vector<char> seen(c.max_seqs, 0);
   int64_t prefix = 0, chunk = 0;
+  int bf16_only = 1;   // every key below the chunks is a bf16 row
   for (int i = 0; i < n_seqs; ++i) {
     const int slot = seq_slots_host[i];
     if (slot < 0 || slot >= c.max_seqs) return OSCAR_ERR_CAPACITY;
@@ -844,6 +845,7 @@ int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
     if (n_new * g > ((int64_t)1 << 30)) return OSCAR_ERR_ARG;
     prefix += lb * n_new;
     chunk += n_new * n_new / 2;
+    if (std::min(s_quant(lb + n_new, c), lb) > c.s_sink) bf16_only = 0;
   }
   // 16 waves per work-group when the chunks attend mostly to a cached prefix
   // (a staged key block then serves twice the rows), else 8 (smaller tiles
@@ -857,7 +859,7 @@ int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
   if ((st = check_device()) != OSCAR_OK) return st;
   if (n_tok == 0) return OSCAR_OK;
   const PrefillArgs pa{seq_slots, len_before, cu_new, q_rot, k_rot, v_rot, out, n_seqs, tiles,
-                       waves};
+                       waves, bf16_only};
   return hip_status(launch_prefill(make_args(*cache), pa, (hipStream_t)stream));
 }
 

@@ -87,7 +87,12 @@ __device__ __forceinline__ void bf16x2_to_f32(uint32_t w, float& lo, float& hi) 
 
 }  // namespace
 
-template <int W>
+// BF: no sequence of the launch has INT2 rows below its chunk, so every key
+// and value is a bf16 row (sink, ring, the chunk itself): they are staged as
+// their own bits and run on the bf16 matrix cores (exact keys and values,
+// P as bf16 hi + lo).  Otherwise keys are staged as fp16 (hi + lo for the
+// steps that hold INT2 rows) and values as fp16, on the fp16 matrix cores.
+template <int W, bool BF>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) void prefill_attn_kernel(CacheArgs c, PrefillArgs a) {
   using S = PfShape<W>;
   constexpr int kPfWaves = S::kWaves, kPfThreads = S::kThreads, kPfRows = S::kRows;
@@ -120,12 +125,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
   const int w_last = min(rows, tile * kPfRows + 16 * wave + 16) - 1;
   const int wave_kend = w_last >= tile * kPfRows + 16 * wave ? lb + w_last / c.g + 1 : 0;
 
-  half8 bq[4];
+  half8 bq[4];     // the query in fp16 (exact in the normal range), for the INT2 steps
+  bf16x8 bqb[4];   // and its bf16 bits, for the steps over bf16 rows
   {
     const uint16_t* qp = a.q_rot + ((size_t)(t0 + pj) * c.hq + (size_t)h * c.g + hl) * kD + 8 * qd;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const u32x4 w = colv ? *(const u32x4*)(qp + 32 * cc) : u32x4{0u, 0u, 0u, 0u};
+      bqb[cc] = __builtin_bit_cast(bf16x8, w);
+      if constexpr (BF) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float lo, hi;
@@ -135,6 +143,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
       }
     }
   }
+
+  // fp16 staging: a 32-position step holding INT2 rows of the prefix
+  // ([S_sink, int2_end)) also gets the keys' fp16 remainders (bf16 rows are
+  // exact in fp16 alone)
+  const int int2_end = min(sq, lb);
+  auto step_int2 = [&](int p0) { return p0 + 2 * kPage > c.s_sink && p0 < int2_end; };
 
   // ---- staging: thread (token pair tp, channels 8u .. 8u+7) takes staged
   // rows 2 tp + m (m < 2) of a stage; threads from 512 on do not stage
@@ -176,6 +190,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
   auto deposit = [&](const RawSlice& r, int m, half8& vh) {
     const int row = 2 * st_tp + m;
     float kv[8], vv[8];
+    if (st_u == 0) sg.skip[row] = r.kind == 0 ? 1 : 0;
     if (r.kind == 1) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -208,11 +223,30 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
     *(half8*)&sg.kl[row][8 * st_u] = kl;
 #pragma unroll
     for (int j = 0; j < 8; ++j) vh[j] = (_Float16)vv[j];
-    if (st_u == 0) sg.skip[row] = r.kind == 0 ? 1 : 0;
   };
   // both positions: the values go out as one 32-bit word (two tokens) per
   // channel, channel 8u + j to row 16 j + u
   auto deposit2 = [&](const RawSlice (&r)[2]) {
+    if constexpr (BF) {
+      // the rows' own bits (kind 1) or zeros (kind 0)
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const u32x4 k0 = r[0].kind == 1 ? r[0].k : z, k1 = r[1].kind == 1 ? r[1].k : z;
+      const u32x4 a0 = r[0].kind == 1 ? r[0].v : z, a1 = r[1].kind == 1 ? r[1].v : z;
+      __builtin_memcpy(&sg.k[2 * st_tp][8 * st_u], &k0, 16);
+      __builtin_memcpy(&sg.k[2 * st_tp + 1][8 * st_u], &k1, 16);
+      if (st_u == 0) {
+        sg.skip[2 * st_tp] = r[0].kind == 0 ? 1 : 0;
+        sg.skip[2 * st_tp + 1] = r[1].kind == 0 ? 1 : 0;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {   // channels 8u + 2e (low halves), 8u + 2e + 1 (high halves)
+        const uint32_t wl = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
+        const uint32_t wh = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
+        __builtin_memcpy(&sg.vt[16 * (2 * e) + st_u][2 * st_tp], &wl, 4);
+        __builtin_memcpy(&sg.vt[16 * (2 * e + 1) + st_u][2 * st_tp], &wh, 4);
+      }
+      return;
+    }
     half8 v0, v1;
     deposit(r[0], 0, v0);
     deposit(r[1], 1, v1);
@@ -235,7 +269,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
 
   // Unmapped INT2 pages are read as zero rows with zero weight (as in decode):
   // a per-stage mask of such positions, built by the staging threads.
-  const int int2_end = min(sq, lb);   // INT2 rows of the prefix: [S_sink, int2_end)
   const int nstage = (kend + kStage - 1) / kStage;
   RawSlice cur[2], nxt[2];
   if (stager) {
@@ -259,20 +292,28 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
       // is key 16 b + 4 qd + r, the lane's own softmax values
       const int p0 = s0 + 2 * kPage * sb, tb = 2 * kPage * sb;
       if (p0 >= wave_kend) break;
-      const bool int2 = p0 + 2 * kPage > c.s_sink && p0 < int2_end;   // bf16 rows are exact in hi
       float x[8], p[8];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         float4_t d = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BF) {
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              *(const half8*)&sg.k[tb + kPage * b + r16][32 * cc + 8 * qd], bq[cc], d, 0, 0, 0);
-        if (int2) {
+          for (int cc = 0; cc < 4; ++cc) {
+            bf16x8 kb;
+            __builtin_memcpy(&kb, &sg.k[tb + kPage * b + r16][32 * cc + 8 * qd], 16);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, bqb[cc], d, 0, 0, 0);
+          }
+        } else {
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc)
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                *(const half8*)&sg.kl[tb + kPage * b + r16][32 * cc + 8 * qd], bq[cc], d, 0, 0, 0);
+                *(const half8*)&sg.k[tb + kPage * b + r16][32 * cc + 8 * qd], bq[cc], d, 0, 0, 0);
+          if (step_int2(p0)) {
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+              d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  *(const half8*)&sg.kl[tb + kPage * b + r16][32 * cc + 8 * qd], bq[cc], d, 0, 0, 0);
+          }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -281,19 +322,39 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
         }
       }
       softmax_step<8>(x, C2, p, st, acc);
-      half8 ph, pl;
+      if constexpr (!BF) {
+        half8 ph, pl;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        ph[r] = (_Float16)p[r];
-        pl[r] = (_Float16)(p[r] - (float)ph[r]);
-      }
+        for (int r = 0; r < 8; ++r) {
+          ph[r] = (_Float16)p[r];
+          pl[r] = (_Float16)(p[r] - (float)ph[r]);
+        }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const half4_t a0 = *(const half4_t*)&sg.vt[16 * j + r16][tb + 4 * qd];
-        const half4_t a1 = *(const half4_t*)&sg.vt[16 * j + r16][tb + kPage + 4 * qd];
-        const half8 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ph, acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pl, acc[j], 0, 0, 0);
+        for (int j = 0; j < 8; ++j) {
+          const half4_t a0 = *(const half4_t*)&sg.vt[16 * j + r16][tb + 4 * qd];
+          const half4_t a1 = *(const half4_t*)&sg.vt[16 * j + r16][tb + kPage + 4 * qd];
+          const half8 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ph, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pl, acc[j], 0, 0, 0);
+        }
+      } else {
+        // P as bf16 hi + lo (about 16 significant bits)
+        bf16x8 ph, pl;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const __bf16 hh = (__bf16)p[r];
+          ph[r] = hh;
+          pl[r] = (__bf16)(p[r] - (float)hh);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          u32x2 w0, w1;
+          __builtin_memcpy(&w0, &sg.vt[16 * j + r16][tb + 4 * qd], 8);
+          __builtin_memcpy(&w1, &sg.vt[16 * j + r16][tb + kPage + 4 * qd], 8);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ph, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl, acc[j], 0, 0, 0);
+        }
       }
     }
     __syncthreads();   // the stage is consumed before the next one is deposited
@@ -353,10 +414,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
 hipError_t launch_prefill(const CacheArgs& c, const PrefillArgs& a, hipStream_t stream) {
   if (a.n_seqs <= 0 || a.tiles <= 0) return hipSuccess;
   const dim3 grid(a.tiles, a.n_seqs, c.hkv);
-  if (a.waves == 16)
-    hipLaunchKernelGGL(prefill_attn_kernel<16>, grid, dim3(64 * 16), 0, stream, c, a);
-  else
-    hipLaunchKernelGGL(prefill_attn_kernel<8>, grid, dim3(64 * 8), 0, stream, c, a);
+  if (a.waves == 16) {
+    if (a.bf16_only) hipLaunchKernelGGL((prefill_attn_kernel<16, true>), grid, dim3(64 * 16), 0, stream, c, a);
+    else hipLaunchKernelGGL((prefill_attn_kernel<16, false>), grid, dim3(64 * 16), 0, stream, c, a);
+  } else {
+    if (a.bf16_only) hipLaunchKernelGGL((prefill_attn_kernel<8, true>), grid, dim3(64 * 8), 0, stream, c, a);
+    else hipLaunchKernelGGL((prefill_attn_kernel<8, false>), grid, dim3(64 * 8), 0, stream, c, a);
+  }
   return hipGetLastError();
 }
 

@@ -122,6 +122,7 @@ struct PrefillArgs {
   int n_seqs;
   int tiles;                     // most query tiles of any sequence (grid x)
   int waves;                     // 8 or 16 waves (16 query rows each) per work-group
+  int bf16_only;                 // no sequence has INT2 rows below its chunk
 };
 int prefill_tiles(int n_new, int g, int waves);
 hipError_t launch_prefill(const CacheArgs& c, const PrefillArgs& a, hipStream_t stream);
