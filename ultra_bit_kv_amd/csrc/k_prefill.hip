@@ -124,6 +124,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
   const int kend = lb + wg_last / c.g + 1;                        // keys [0, kend)
   const int w_last = min(rows, tile * kPfRows + 16 * wave + 16) - 1;
   const int wave_kend = w_last >= tile * kPfRows + 16 * wave ? lb + w_last / c.g + 1 : 0;
+  const int wave_qmin = lb + (tile * kPfRows + 16 * wave) / c.g;   // position of the wave's first row
 
   half8 bq[4];     // the query in fp16 (exact in the normal range), for the INT2 steps
   bf16x8 bqb[4];   // and its bf16 bits, for the steps over bf16 rows
@@ -234,10 +235,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
       const u32x4 a0 = r[0].kind == 1 ? r[0].v : z, a1 = r[1].kind == 1 ? r[1].v : z;
       __builtin_memcpy(&sg.k[2 * st_tp][8 * st_u], &k0, 16);
       __builtin_memcpy(&sg.k[2 * st_tp + 1][8 * st_u], &k1, 16);
-      if (st_u == 0) {
-        sg.skip[2 * st_tp] = r[0].kind == 0 ? 1 : 0;
-        sg.skip[2 * st_tp + 1] = r[1].kind == 0 ? 1 : 0;
-      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {   // channels 8u + 2e (low halves), 8u + 2e + 1 (high halves)
         const uint32_t wl = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
@@ -315,10 +312,22 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
                   *(const half8*)&sg.kl[tb + kPage * b + r16][32 * cc + 8 * qd], bq[cc], d, 0, 0, 0);
           }
         }
+        if constexpr (BF) {
+          // (rows past the end, the only zero rows here, lie past every query position)
+          if (p0 + 2 * kPage - 1 <= wave_qmin) {   // the whole step is below every row of the wave
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = tb + kPage * b + 4 * qd + r;
-          x[4 * b + r] = (colv && s0 + row <= qpos && !sg.skip[row]) ? d[r] : kNegInf;
+            for (int r = 0; r < 4; ++r) x[4 * b + r] = colv ? d[r] : kNegInf;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              x[4 * b + r] = (colv && s0 + tb + kPage * b + 4 * qd + r <= qpos) ? d[r] : kNegInf;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = tb + kPage * b + 4 * qd + r;
+            x[4 * b + r] = (colv && s0 + row <= qpos && !sg.skip[row]) ? d[r] : kNegInf;
+          }
         }
       }
       softmax_step<8>(x, C2, p, st, acc);
