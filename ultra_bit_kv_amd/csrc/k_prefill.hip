@@ -290,6 +290,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
       const int p0 = s0 + 2 * kPage * sb, tb = 2 * kPage * sb;
       if (p0 >= wave_kend) break;
       float x[8], p[8];
+      // fp16 mode: no unreadable row (unmapped page) among the step's 32
+      bool clean = true;
+      if constexpr (!BF) clean = !__any(sg.skip[tb + (lane & 31)]);
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         float4_t d = {0.f, 0.f, 0.f, 0.f};
@@ -322,6 +325,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
             for (int r = 0; r < 4; ++r)
               x[4 * b + r] = (colv && s0 + tb + kPage * b + 4 * qd + r <= qpos) ? d[r] : kNegInf;
           }
+        } else if (clean && p0 + 2 * kPage - 1 <= wave_qmin) {   // no mask in this step
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[4 * b + r] = colv ? d[r] : kNegInf;
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
