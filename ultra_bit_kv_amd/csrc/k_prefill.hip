@@ -61,13 +61,22 @@ struct PfStage {
   _Float16 vt[kD][S::kVRow];          // values [row][token], row 16 j + u = channel 8 u + j
   int skip[S::kStage];                // position unreadable (unmapped page or past the row)
 };
+// bf16 mode: two stage buffers (keys as bf16 bits, values transposed), so a
+// stage is deposited while the previous one is read, one barrier per stage
+template <int W>
+struct PfStageBF {
+  using S = PfShape<W>;
+  _Float16 k[2][S::kStage][S::kKRow];
+  _Float16 vt[2][kD][S::kVRow];
+};
 template <int W>
 struct PfFinal {
   float o[PfShape<W>::kRows][kD + 4];
 };
-template <int W>
+template <int W, bool BF>
 constexpr int pf_lds() {
-  return sizeof(PfStage<W>) > sizeof(PfFinal<W>) ? sizeof(PfStage<W>) : sizeof(PfFinal<W>);
+  constexpr int st = BF ? (int)sizeof(PfStageBF<W>) : (int)sizeof(PfStage<W>);
+  return st > (int)sizeof(PfFinal<W>) ? st : (int)sizeof(PfFinal<W>);
 }
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -97,8 +106,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
   using S = PfShape<W>;
   constexpr int kPfWaves = S::kWaves, kPfThreads = S::kThreads, kPfRows = S::kRows;
   constexpr int kStage = S::kStage;
-  __shared__ __align__(16) char smem[pf_lds<W>()];
+  __shared__ __align__(16) char smem[pf_lds<W, BF>()];
   PfStage<W>& sg = *reinterpret_cast<PfStage<W>*>(smem);
+  PfStageBF<W>& sbf = *reinterpret_cast<PfStageBF<W>*>(smem);
   float(&fin)[kPfRows][kD + 4] = reinterpret_cast<PfFinal<W>*>(smem)->o;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -227,20 +237,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
   };
   // both positions: the values go out as one 32-bit word (two tokens) per
   // channel, channel 8u + j to row 16 j + u
-  auto deposit2 = [&](const RawSlice (&r)[2]) {
+  auto deposit2 = [&](const RawSlice (&r)[2], int buf) {
     if constexpr (BF) {
       // the rows' own bits (kind 1) or zeros (kind 0)
       const u32x4 z = {0u, 0u, 0u, 0u};
       const u32x4 k0 = r[0].kind == 1 ? r[0].k : z, k1 = r[1].kind == 1 ? r[1].k : z;
       const u32x4 a0 = r[0].kind == 1 ? r[0].v : z, a1 = r[1].kind == 1 ? r[1].v : z;
-      __builtin_memcpy(&sg.k[2 * st_tp][8 * st_u], &k0, 16);
-      __builtin_memcpy(&sg.k[2 * st_tp + 1][8 * st_u], &k1, 16);
+      __builtin_memcpy(&sbf.k[buf][2 * st_tp][8 * st_u], &k0, 16);
+      __builtin_memcpy(&sbf.k[buf][2 * st_tp + 1][8 * st_u], &k1, 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {   // channels 8u + 2e (low halves), 8u + 2e + 1 (high halves)
         const uint32_t wl = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
         const uint32_t wh = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
-        __builtin_memcpy(&sg.vt[16 * (2 * e) + st_u][2 * st_tp], &wl, 4);
-        __builtin_memcpy(&sg.vt[16 * (2 * e + 1) + st_u][2 * st_tp], &wh, 4);
+        __builtin_memcpy(&sbf.vt[buf][16 * (2 * e) + st_u][2 * st_tp], &wl, 4);
+        __builtin_memcpy(&sbf.vt[buf][16 * (2 * e + 1) + st_u][2 * st_tp], &wh, 4);
       }
       return;
     }
@@ -267,21 +277,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
   // Unmapped INT2 pages are read as zero rows with zero weight (as in decode):
   // a per-stage mask of such positions, built by the staging threads.
   const int nstage = (kend + kStage - 1) / kStage;
-  RawSlice cur[2], nxt[2];
-  if (stager) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m) fetch(0, m, cur[m]);
-  }
-  for (int ks = 0; ks < nstage; ++ks) {
+  // the 64 positions of stage ks, from buffer buf (bf16 mode; else the one buffer)
+  auto run_stage = [&](int ks, int buf) {
     const int s0 = ks * kStage;
-    if (stager) {
-      deposit2(cur);
-      if (ks + 1 < nstage) {   // next stage in flight during this one
-#pragma unroll
-        for (int m = 0; m < 2; ++m) fetch(s0 + kStage, m, nxt[m]);
-      }
-    }
-    __syncthreads();
 #pragma unroll
     for (int sb = 0; sb < kStage / (2 * kPage); ++sb) {
       // two 16-position blocks per softmax step: block b of the pair is
@@ -300,7 +298,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
             bf16x8 kb;
-            __builtin_memcpy(&kb, &sg.k[tb + kPage * b + r16][32 * cc + 8 * qd], 16);
+            __builtin_memcpy(&kb, &sbf.k[buf][tb + kPage * b + r16][32 * cc + 8 * qd], 16);
             d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, bqb[cc], d, 0, 0, 0);
           }
         } else {
@@ -364,17 +362,57 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           u32x2 w0, w1;
-          __builtin_memcpy(&w0, &sg.vt[16 * j + r16][tb + 4 * qd], 8);
-          __builtin_memcpy(&w1, &sg.vt[16 * j + r16][tb + kPage + 4 * qd], 8);
+          __builtin_memcpy(&w0, &sbf.vt[buf][16 * j + r16][tb + 4 * qd], 8);
+          __builtin_memcpy(&w1, &sbf.vt[buf][16 * j + r16][tb + kPage + 4 * qd], 8);
           const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ph, acc[j], 0, 0, 0);
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl, acc[j], 0, 0, 0);
         }
       }
     }
-    __syncthreads();   // the stage is consumed before the next one is deposited
+  };
+  RawSlice cur[2], nxt[2];
+  if constexpr (BF) {
+    if (stager) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) cur[m] = nxt[m];
+      for (int m = 0; m < 2; ++m) fetch(0, m, cur[m]);
+      deposit2(cur, 0);
+      if (1 < nstage) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) fetch(kStage, m, nxt[m]);
+      }
+    }
+    __syncthreads();
+    for (int ks = 0; ks < nstage; ++ks) {
+      run_stage(ks, ks & 1);
+      if (stager && ks + 1 < nstage) {   // the next stage into the other buffer
+        deposit2(nxt, (ks + 1) & 1);
+        if (ks + 2 < nstage) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) fetch((ks + 2) * kStage, m, nxt[m]);
+        }
+      }
+      __syncthreads();   // stage ks + 1 in, stage ks read by every wave
+    }
+  } else {
+    if (stager) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) fetch(0, m, cur[m]);
+    }
+    for (int ks = 0; ks < nstage; ++ks) {
+      if (stager) {
+        deposit2(cur, 0);
+        if (ks + 1 < nstage) {   // next stage in flight during this one
+#pragma unroll
+          for (int m = 0; m < 2; ++m) fetch((ks + 1) * kStage, m, nxt[m]);
+        }
+      }
+      __syncthreads();
+      run_stage(ks, 0);
+      __syncthreads();   // the stage is consumed before the next one is deposited
+#pragma unroll
+      for (int m = 0; m < 2; ++m) cur[m] = nxt[m];
+    }
   }
 
   // ---- normalize, then o = o' . R_V^T (or o' when the value transform is absorbed)
