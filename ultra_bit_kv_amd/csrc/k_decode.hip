@@ -453,7 +453,9 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
         const int cl = 16 * (cc >> 1) + 4 * (cc & 1) + v + 8 * e;
         const uint32_t word = wq[cl >> 3][(cl & 7) >> 1];
         const uint32_t bits = (cl & 1) ? (word >> 16) : (word & 0xFFFFu);
-        const float qv = bval ? bf16_bits_to_f32(bits) : 0.0f;
+        // (OScaR keys have no channel groups: every column takes all 128
+        // channels of its head, so no group partials need adding up)
+        const float qv = (KM ? colv : bval) ? bf16_bits_to_f32(bits) : 0.0f;
         bq[cc][2 * v + e] = (_Float16)(KM ? qv * __builtin_ldexpf(1.0f, sh - 2 * v)
                                           : qv * (1.0f / (float)(1 << (2 * v))));
       }
@@ -654,12 +656,16 @@ __global__ __launch_bounds__(64 * WH) void int2_decode_kernel(CacheArgs c, SeqAr
         cp = __builtin_fmaf(qo[e], dl != 0.0f ? dl * z : -z, cp);
       }
       cp = rows_sum(cp);
+      // C over all channels: the four group columns of the head add up
+      if constexpr (KH * HP <= 8) cp += row_ror<8>(cp);
+      if constexpr (KH * HP <= 4) cp += row_ror<4>(cp);
+      if constexpr (KH * HP <= 2) cp += row_ror<2>(cp);
+      if constexpr (KH * HP <= 1) cp += row_ror<1>(cp);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         x[r] = da[r] - cp;
         x[4 + r] = db[r] - cp;
       }
-      group_sum(x);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {   // token scales of rows 4 qd + r
         const uint32_t wa = tsa[r >> 1], wb3 = tsb[r >> 1];
