@@ -85,6 +85,14 @@ def test_fresh_prefill_quantized_chunk_rows():
     run_case(get("c1_tiny"), [0], [301])
 
 
+def test_prefix_in_windows_bf16_rows_only():
+    # prefixes still held by the sink and the ring (no INT2 row below any
+    # chunk): every key and value of the call is a bf16 row; ragged chunks,
+    # stage boundaries inside the sink, ring and chunk rows
+    w = get("c1_tiny").scaled(n_seqs=3, lengths=("list", (120, 77, 120)))
+    run_case(w, [100, 3, 60], [20, 74, 60])
+
+
 def test_chunk_longer_than_ring_identity():
     run_case(get("c1_tiny").scaled(s_keep=40, s_flush=16), [500], [600], identity=True)
 
