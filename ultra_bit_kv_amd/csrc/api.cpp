@@ -847,19 +847,19 @@ int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
     chunk += n_new * n_new / 2;
     if (std::min(s_quant(lb + n_new, c), lb) > c.s_sink) bf16_only = 0;
   }
-  // 16 waves per work-group when the chunks attend mostly to a cached prefix
-  // (a staged key block then serves twice the rows), else 8 (smaller tiles
-  // waste less of the causal triangle)
-  const int waves = prefix > chunk ? 16 : 8;
+  // Query rows per work-group: 256 when the chunks attend mostly to a cached
+  // INT2 prefix (a staged key block then serves twice the rows), else 128
+  // (smaller tiles waste less of the causal triangle; bf16 mode always)
+  const int blocks = (!bf16_only && prefix > chunk) ? 16 : 8;
   int tiles = 0;
   for (int i = 0; i < n_seqs; ++i)
-    tiles = std::max(tiles, prefill_tiles(cu_new_host[i + 1] - cu_new_host[i], g, waves));
+    tiles = std::max(tiles, prefill_tiles(cu_new_host[i + 1] - cu_new_host[i], g, blocks));
   const int64_t n_tok = cu_new_host[n_seqs];
   if (n_tok > (int64_t)1 << 30) return OSCAR_ERR_ARG;
   if ((st = check_device()) != OSCAR_OK) return st;
   if (n_tok == 0) return OSCAR_OK;
   const PrefillArgs pa{seq_slots, len_before, cu_new, q_rot, k_rot, v_rot, out, n_seqs, tiles,
-                       waves, bf16_only};
+                       blocks, bf16_only};
   return hip_status(launch_prefill(make_args(*cache), pa, (hipStream_t)stream));
 }
 

@@ -28,7 +28,7 @@
 //   online softmax per column (query row) over 32 keys, causal mask p <= P
 //   O^T += V^T . P^T  v_mfma_f32_16x16x32_f16 with P split into fp16 hi + lo
 // then the normalized o' rows go through LDS (reusing the staging space) and
-// the fp32 matrix cores apply R_V^T (wave w computes output channels
+// the bf16 matrix cores apply R_V^T as hi + lo products (wave w computes output channels
 // 16 (w % 8) .. 16 (w % 8) + 15 of its share of the rows).
 #include "decode_common.h"
 
@@ -36,19 +36,24 @@ namespace oscar {
 
 namespace {
 
-// Work-group shape: W waves of 16 query rows each.  Staging: 512 threads,
-// thread (token pair tp, channel octet u) takes positions 2 tp, 2 tp + 1 of a
-// 64-position stage, channels 8 u .. 8 u + 7.
-template <int W>
+// Work-group shape: W waves of 16 RB query rows each (RB blocks of 16, the
+// columns of RB MFMA tiles that share every key and value operand read from
+// LDS).  Staging: 512 threads, thread (token pair tp, channel octet u) takes
+// positions 2 tp, 2 tp + 1 of a 64-position stage, channels 8 u .. 8 u + 7.
+template <int W, int RB = 1>
 struct PfShape {
   static constexpr int kWaves = W;
   static constexpr int kThreads = 64 * W;
-  static constexpr int kRows = 16 * W;             // query rows per work-group
+  static constexpr int kRows = 16 * W * RB;        // query rows per work-group
   static constexpr int kStage = 64;                // key positions staged per barrier
   static constexpr int kStageThreads = 512;        // (kStage / 2) pairs x 16 octets
   static constexpr int kKRow = kD + 8;   // staged key row in fp16 (padded: rows start 4 banks apart)
   static constexpr int kVRow = kStage + 4;   // staged value row (one channel), 34 dwords: the
                                              // 16 rows one instruction writes start on distinct banks
+  // bf16 mode: value rows of 72 (16-byte aligned, 16 rows on distinct bank
+  // quads), each 32-key group ordered so that a lane's 8 keys of a P.V
+  // step (4 qd .. 4 qd + 3, 16 + 4 qd .. 16 + 4 qd + 3) are adjacent
+  static constexpr int kVRowBF = kStage + 8;
   static_assert(kThreads >= kStageThreads, "a stage is 64 positions");
 };
 
@@ -67,16 +72,16 @@ template <int W>
 struct PfStageBF {
   using S = PfShape<W>;
   _Float16 k[2][S::kStage][S::kKRow];
-  _Float16 vt[2][kD][S::kVRow];
+  _Float16 vt[2][kD][S::kVRowBF];
 };
-template <int W>
+template <int W, int RB>
 struct PfFinal {
-  float o[PfShape<W>::kRows][kD + 4];
+  float o[PfShape<W, RB>::kRows][kD + 4];
 };
-template <int W, bool BF>
+template <int W, bool BF, int RB>
 constexpr int pf_lds() {
   constexpr int st = BF ? (int)sizeof(PfStageBF<W>) : (int)sizeof(PfStage<W>);
-  return st > (int)sizeof(PfFinal<W>) ? st : (int)sizeof(PfFinal<W>);
+  return st > (int)sizeof(PfFinal<W, RB>) ? st : (int)sizeof(PfFinal<W, RB>);
 }
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -94,6 +99,16 @@ __device__ __forceinline__ void bf16x2_to_f32(uint32_t w, float& lo, float& hi) 
   hi = __uint_as_float(w & 0xFFFF0000u);
 }
 
+// x as bf16 hi + lo: hi = RNE(x), lo = RNE(x - hi) (x - hi is exact in fp32)
+__device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 b = (__bf16)x[e];
+    hi[e] = b;
+    lo[e] = (__bf16)(x[e] - (float)b);
+  }
+}
+
 }  // namespace
 
 // BF: no sequence of the launch has INT2 rows below its chunk, so every key
@@ -101,15 +116,16 @@ __device__ __forceinline__ void bf16x2_to_f32(uint32_t w, float& lo, float& hi) 
 // their own bits and run on the bf16 matrix cores (exact keys and values,
 // P as bf16 hi + lo).  Otherwise keys are staged as fp16 (hi + lo for the
 // steps that hold INT2 rows) and values as fp16, on the fp16 matrix cores.
-template <int W, bool BF>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) void prefill_attn_kernel(CacheArgs c, PrefillArgs a) {
-  using S = PfShape<W>;
+template <int W, bool BF, int RB>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 4 : 2))) void prefill_attn_kernel(CacheArgs c, PrefillArgs a) {
+  static_assert(RB == 1 || BF, "two row blocks per wave: bf16 mode");
+  using S = PfShape<W, RB>;
   constexpr int kPfWaves = S::kWaves, kPfThreads = S::kThreads, kPfRows = S::kRows;
   constexpr int kStage = S::kStage;
-  __shared__ __align__(16) char smem[pf_lds<W, BF>()];
+  __shared__ __align__(16) char smem[pf_lds<W, BF, RB>()];
   PfStage<W>& sg = *reinterpret_cast<PfStage<W>*>(smem);
   PfStageBF<W>& sbf = *reinterpret_cast<PfStageBF<W>*>(smem);
-  float(&fin)[kPfRows][kD + 4] = reinterpret_cast<PfFinal<W>*>(smem)->o;
+  float(&fin)[kPfRows][kD + 4] = reinterpret_cast<PfFinal<W, RB>*>(smem)->o;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -125,32 +141,37 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
   const int32_t* bt = c.block_table + (size_t)slot * c.max_pages;
   const uint16_t* wrow = c.win + ((size_t)slot * c.hkv + h) * c.win_blocks * (2 * kPage * kD);
 
-  // ---- this lane's query row (MFMA column) and the keys the work-group reads
-  const int row = tile * kPfRows + 16 * wave + r16;
-  const bool colv = row < rows;
-  const int pj = colv ? row / c.g : 0, hl = colv ? row % c.g : 0;
-  const int qpos = lb + pj;
+  // ---- this lane's query rows (MFMA column r16 of each of the wave's RB
+  // row blocks) and the keys the work-group reads
+  const int wrow0 = tile * kPfRows + 16 * RB * wave;              // the wave's first row
+  bool colv[RB];
+  int qpos[RB];
   const int wg_last = min(rows, (tile + 1) * kPfRows) - 1;
   const int kend = lb + wg_last / c.g + 1;                        // keys [0, kend)
-  const int w_last = min(rows, tile * kPfRows + 16 * wave + 16) - 1;
-  const int wave_kend = w_last >= tile * kPfRows + 16 * wave ? lb + w_last / c.g + 1 : 0;
-  const int wave_qmin = lb + (tile * kPfRows + 16 * wave) / c.g;   // position of the wave's first row
+  const int w_last = min(rows, wrow0 + 16 * RB) - 1;
+  const int wave_kend = w_last >= wrow0 ? lb + w_last / c.g + 1 : 0;
+  const int wave_qmin = lb + wrow0 / c.g;                         // position of the wave's first row
 
-  half8 bq[4];     // the query in fp16 (exact in the normal range), for the INT2 steps
-  bf16x8 bqb[4];   // and its bf16 bits, for the steps over bf16 rows
-  {
+  half8 bq[RB][4];     // the query in fp16 (exact in the normal range), for the INT2 steps
+  bf16x8 bqb[RB][4];   // and its bf16 bits, for the steps over bf16 rows
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = wrow0 + 16 * rb + r16;
+    colv[rb] = row < rows;
+    const int pj = colv[rb] ? row / c.g : 0, hl = colv[rb] ? row % c.g : 0;
+    qpos[rb] = lb + pj;
     const uint16_t* qp = a.q_rot + ((size_t)(t0 + pj) * c.hq + (size_t)h * c.g + hl) * kD + 8 * qd;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      const u32x4 w = colv ? *(const u32x4*)(qp + 32 * cc) : u32x4{0u, 0u, 0u, 0u};
-      bqb[cc] = __builtin_bit_cast(bf16x8, w);
+      const u32x4 w = colv[rb] ? *(const u32x4*)(qp + 32 * cc) : u32x4{0u, 0u, 0u, 0u};
+      bqb[rb][cc] = __builtin_bit_cast(bf16x8, w);
       if constexpr (BF) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float lo, hi;
         bf16x2_to_f32(w[e], lo, hi);
-        bq[cc][2 * e] = (_Float16)lo;
-        bq[cc][2 * e + 1] = (_Float16)hi;
+        bq[rb][cc][2 * e] = (_Float16)lo;
+        bq[rb][cc][2 * e + 1] = (_Float16)hi;
       }
     }
   }
@@ -186,6 +207,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
                   (uint32_t)vb[16] | ((uint32_t)vb[20] << 16), (uint32_t)vb[24] | ((uint32_t)vb[28] << 16)};
       r.kind = 1;
     } else {   // INT2: logical page (p - S_sink) / 16, slot (p - S_sink) % 16
+      if constexpr (BF) return;   // (none below a bf16-mode chunk)
       const int m = (p - c.s_sink) / kPage, sl = (p - c.s_sink) % kPage;
       const int ph = m < c.max_pages ? bt[m] : -1;
       if (ph < 0 || ph >= c.num_pages) return;
@@ -245,12 +267,16 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
       const u32x4 a0 = r[0].kind == 1 ? r[0].v : z, a1 = r[1].kind == 1 ? r[1].v : z;
       __builtin_memcpy(&sbf.k[buf][2 * st_tp][8 * st_u], &k0, 16);
       __builtin_memcpy(&sbf.k[buf][2 * st_tp + 1][8 * st_u], &k1, 16);
+      // staged column of stage positions 2 tp, 2 tp + 1 (key kk of its
+      // 32-key group goes to 8 ((kk % 16) / 4) + 4 (kk / 16) + kk % 4)
+      const int kk = (2 * st_tp) & 31;
+      const int vc = (2 * st_tp - kk) + 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {   // channels 8u + 2e (low halves), 8u + 2e + 1 (high halves)
         const uint32_t wl = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
         const uint32_t wh = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
-        __builtin_memcpy(&sbf.vt[buf][16 * (2 * e) + st_u][2 * st_tp], &wl, 4);
-        __builtin_memcpy(&sbf.vt[buf][16 * (2 * e + 1) + st_u][2 * st_tp], &wh, 4);
+        __builtin_memcpy(&sbf.vt[buf][16 * (2 * e) + st_u][vc], &wl, 4);
+        __builtin_memcpy(&sbf.vt[buf][16 * (2 * e + 1) + st_u][vc], &wh, 4);
       }
       return;
     }
@@ -268,17 +294,23 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
     }
   };
 
-  float4_t acc[8];
+  float4_t acc[RB][8];
+  SoftmaxState st[RB];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-  SoftmaxState st{kNegInf, 0.0f, 0.0f, 0.0f};
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[rb][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    st[rb] = SoftmaxState{kNegInf, 0.0f, 0.0f, 0.0f};
+  }
   const float C2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
 
   // Unmapped INT2 pages are read as zero rows with zero weight (as in decode):
   // a per-stage mask of such positions, built by the staging threads.
   const int nstage = (kend + kStage - 1) / kStage;
   // the 64 positions of stage ks, from buffer buf (bf16 mode; else the one buffer)
-  auto run_stage = [&](int ks, int buf) {
+  // mid() runs before the first step in every wave (bf16 mode: the staging
+  // of later stages), whatever the wave's key range
+  auto run_stage = [&](int ks, int buf, auto&& mid) {
     const int s0 = ks * kStage;
 #pragma unroll
     for (int sb = 0; sb < kStage / (2 * kPage); ++sb) {
@@ -286,96 +318,121 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
       // staged rows tb + 16 b; K slot 8 qd + 4 b + r of the 32-key P.V MFMA
       // is key 16 b + 4 qd + r, the lane's own softmax values
       const int p0 = s0 + 2 * kPage * sb, tb = 2 * kPage * sb;
-      if (p0 >= wave_kend) break;
-      float x[8], p[8];
+      if (sb == 0) mid();
+      if (p0 >= wave_kend) continue;
+      float x[RB][8], p[RB][8];
       // fp16 mode: no unreadable row (unmapped page) among the step's 32
       bool clean = true;
       if constexpr (!BF) clean = !__any(sg.skip[tb + (lane & 31)]);
+      // the whole step lies below every row of the wave: no causal mask
+      const bool below = p0 + 2 * kPage - 1 <= wave_qmin;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        float4_t d = {0.f, 0.f, 0.f, 0.f};
+        float4_t d[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) d[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
         if constexpr (BF) {
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
             bf16x8 kb;
             __builtin_memcpy(&kb, &sbf.k[buf][tb + kPage * b + r16][32 * cc + 8 * qd], 16);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, bqb[cc], d, 0, 0, 0);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              d[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, bqb[rb][cc], d[rb], 0, 0, 0);
           }
         } else {
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc)
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                *(const half8*)&sg.k[tb + kPage * b + r16][32 * cc + 8 * qd], bq[cc], d, 0, 0, 0);
+            d[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                *(const half8*)&sg.k[tb + kPage * b + r16][32 * cc + 8 * qd], bq[0][cc], d[0], 0, 0, 0);
           if (step_int2(p0)) {
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc)
-              d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                  *(const half8*)&sg.kl[tb + kPage * b + r16][32 * cc + 8 * qd], bq[cc], d, 0, 0, 0);
+              d[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  *(const half8*)&sg.kl[tb + kPage * b + r16][32 * cc + 8 * qd], bq[0][cc], d[0], 0, 0, 0);
           }
         }
-        if constexpr (BF) {
-          // (rows past the end, the only zero rows here, lie past every query position)
-          if (p0 + 2 * kPage - 1 <= wave_qmin) {   // the whole step is below every row of the wave
 #pragma unroll
-            for (int r = 0; r < 4; ++r) x[4 * b + r] = colv ? d[r] : kNegInf;
+        for (int rb = 0; rb < RB; ++rb) {
+          if constexpr (BF) {
+            // (rows past the end, the only zero rows here, lie past every
+            // query position; a column past the last query row has a zero
+            // query, finite logits and an output that is never stored)
+            if (below) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) x[rb][4 * b + r] = d[rb][r];
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                x[rb][4 * b + r] = s0 + tb + kPage * b + 4 * qd + r <= qpos[rb] ? d[rb][r] : kNegInf;
+            }
+          } else if (clean && below) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[rb][4 * b + r] = colv[rb] ? d[rb][r] : kNegInf;
           } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              x[4 * b + r] = (colv && s0 + tb + kPage * b + 4 * qd + r <= qpos) ? d[r] : kNegInf;
-          }
-        } else if (clean && p0 + 2 * kPage - 1 <= wave_qmin) {   // no mask in this step
-#pragma unroll
-          for (int r = 0; r < 4; ++r) x[4 * b + r] = colv ? d[r] : kNegInf;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = tb + kPage * b + 4 * qd + r;
-            x[4 * b + r] = (colv && s0 + row <= qpos && !sg.skip[row]) ? d[r] : kNegInf;
+            for (int r = 0; r < 4; ++r) {
+              const int row = tb + kPage * b + 4 * qd + r;
+              x[rb][4 * b + r] =
+                  (colv[rb] && s0 + row <= qpos[rb] && !sg.skip[row]) ? d[rb][r] : kNegInf;
+            }
           }
         }
       }
-      softmax_step<8>(x, C2, p, st, acc);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) softmax_step<8>(x[rb], C2, p[rb], st[rb], acc[rb]);
       if constexpr (!BF) {
         half8 ph, pl;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          ph[r] = (_Float16)p[r];
-          pl[r] = (_Float16)(p[r] - (float)ph[r]);
+          ph[r] = (_Float16)p[0][r];
+          pl[r] = (_Float16)(p[0][r] - (float)ph[r]);
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const half4_t a0 = *(const half4_t*)&sg.vt[16 * j + r16][tb + 4 * qd];
           const half4_t a1 = *(const half4_t*)&sg.vt[16 * j + r16][tb + kPage + 4 * qd];
           const half8 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ph, acc[j], 0, 0, 0);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pl, acc[j], 0, 0, 0);
+          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ph, acc[0][j], 0, 0, 0);
+          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pl, acc[0][j], 0, 0, 0);
         }
       } else {
         // P as bf16 hi + lo (about 16 significant bits)
-        bf16x8 ph, pl;
+        bf16x8 ph[RB], pl[RB];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const __bf16 hh = (__bf16)p[r];
-          ph[r] = hh;
-          pl[r] = (__bf16)(p[r] - (float)hh);
-        }
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const __bf16 hh = (__bf16)p[rb][r];
+            ph[rb][r] = hh;
+            pl[rb][r] = (__bf16)(p[rb][r] - (float)hh);
+          }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          u32x2 w0, w1;
-          __builtin_memcpy(&w0, &sbf.vt[buf][16 * j + r16][tb + 4 * qd], 8);
-          __builtin_memcpy(&w1, &sbf.vt[buf][16 * j + r16][tb + kPage + 4 * qd], 8);
-          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ph, acc[j], 0, 0, 0);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl, acc[j], 0, 0, 0);
+          bf16x8 av;   // keys tb + 4 qd .. + 3, then tb + 16 + 4 qd .. + 3
+          __builtin_memcpy(&av, &sbf.vt[buf][16 * j + r16][tb + 8 * qd], 16);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ph[rb], acc[rb][j], 0, 0, 0);
+            acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl[rb], acc[rb][j], 0, 0, 0);
+          }
         }
       }
     }
   };
   RawSlice cur[2], nxt[2];
+  // Every thread waits here for its query loads (and a stager for its first
+  // stage).  The query feeds the first MFMA of the key loop; left to the
+  // compiler, the wait for it lands inside the loop, where it becomes a wait
+  // for every load in flight (the next stages' rows) once per stage.
+  constexpr int kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)
   if constexpr (BF) {
     if (stager) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) fetch(0, m, cur[m]);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (stager) {
       deposit2(cur, 0);
       if (1 < nstage) {
 #pragma unroll
@@ -383,15 +440,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
       }
     }
     __syncthreads();
+    // Stage ks + 1 goes into the other buffer (free: every wave has passed
+    // the barrier after reading it as stage ks - 1) and stage ks + 2 is
+    // fetched between the two steps of stage ks: the loads then have a whole
+    // stage of work to arrive before the next wait for them
+    // (unconditional: every thread stages, a fetch past the row gives zero
+    // rows, and the last deposits land in a buffer no step reads; a branch
+    // here makes the compiler wait for these loads at the next MFMA)
+    static_assert(!BF || S::kThreads == S::kStageThreads, "bf16 mode: every thread stages");
     for (int ks = 0; ks < nstage; ++ks) {
-      run_stage(ks, ks & 1);
-      if (stager && ks + 1 < nstage) {   // the next stage into the other buffer
+      run_stage(ks, ks & 1, [&] {
         deposit2(nxt, (ks + 1) & 1);
-        if (ks + 2 < nstage) {
 #pragma unroll
-          for (int m = 0; m < 2; ++m) fetch((ks + 2) * kStage, m, nxt[m]);
-        }
-      }
+        for (int m = 0; m < 2; ++m) fetch((ks + 2) * kStage, m, nxt[m]);
+      });
       __syncthreads();   // stage ks + 1 in, stage ks read by every wave
     }
   } else {
@@ -399,6 +461,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
 #pragma unroll
       for (int m = 0; m < 2; ++m) fetch(0, m, cur[m]);
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     for (int ks = 0; ks < nstage; ++ks) {
       if (stager) {
         deposit2(cur, 0);
@@ -408,7 +471,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
         }
       }
       __syncthreads();
-      run_stage(ks, 0);
+      run_stage(ks, 0, [] {});
       __syncthreads();   // the stage is consumed before the next one is deposited
 #pragma unroll
       for (int m = 0; m < 2; ++m) cur[m] = nxt[m];
@@ -416,13 +479,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
   }
 
   // ---- normalize, then o = o' . R_V^T (or o' when the value transform is absorbed)
-  const float l = rows_sum(st.l);
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  // acc[j][r] is staged value row 16 j + 4 qd + r, i.e. channel 32 qd + 8 r + j
+  // acc[rb][j][r] is staged value row 16 j + 4 qd + r, i.e. channel 32 qd + 8 r + j
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l = rows_sum(st[rb].l);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) fin[16 * wave + r16][32 * qd + 8 * r + j] = acc[j][r] * inv;
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        fin[16 * (RB * wave + rb) + r16][32 * qd + 8 * r + j] = acc[rb][j][r] * inv;
+  }
   __syncthreads();
   auto out_row = [&](int rr) {   // output row of work-group row rr, or nullptr
     const int R = tile * kPfRows + rr;
@@ -438,24 +505,45 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
     return;
   }
   // Wave w computes output channels 16 (w % 8) .. 16 (w % 8) + 15 of the row
-  // tiles rt = w / 8, w / 8 + kPfWaves / 8, ...; lane (li, kq) holds
-  // R_V[16 (w % 8) + li][32kq .. 32kq+31]: the contraction index of step
-  // (u, e) is k = 32kq + 4u + e, as in the decode merge
+  // tiles rt = w / 8, w / 8 + kPfWaves / 8, ... on the bf16 matrix cores:
+  // both operands as bf16 hi + lo (o' . R = o'_hi R_hi + o'_hi R_lo + o'_lo
+  // R_hi, each factor held to about 16 bits; a sixteenth of the fp32
+  // matrix cores' time for the same product).  For the 32-channel chunk kc,
+  // lane (li, kq) holds o' row 16 rt + li and R_V row 16 (w % 8) + li at
+  // channels 32 kc + 8 kq .. + 7.
   constexpr int kColBlocks = kD / 16;
   static_assert(kPfWaves % kColBlocks == 0, "the epilogue splits the 128 output channels over the waves");
   const int cb = wave % kColBlocks;
   const int li = r16, kq = qd;
-  float4_t rb[8];
-  load_unrotation(c, h, 16 * cb + li, kq, rb);
+  bf16x8 rh[4], rl[4];
+  {
+    const int j = 16 * cb + li;
+    const float* rg = c.r_v + ((size_t)h * kD + j) * kD;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      float f[8];
+      if (c.rot) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = hadamard_entry(c.rot, j, 32 * kc + 8 * kq + e);
+      } else {
+        __builtin_memcpy(f, rg + 32 * kc + 8 * kq, 32);
+      }
+      split_bf16(f, rh[kc], rl[kc]);
+    }
+  }
   for (int rt = wave / kColBlocks; rt < kPfRows / 16; rt += kPfWaves / kColBlocks) {
     if (tile * kPfRows + 16 * rt >= rows) break;
     float4_t o4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        o4 = __builtin_amdgcn_mfma_f32_16x16x4f32(fin[16 * rt + li][32 * kq + 4 * u + e], rb[u][e],
-                                                  o4, 0, 0, 0);
+    for (int kc = 0; kc < 4; ++kc) {
+      float f[8];
+      __builtin_memcpy(f, &fin[16 * rt + li][32 * kc + 8 * kq], 32);
+      bf16x8 ah, al;
+      split_bf16(f, ah, al);
+      o4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, rh[kc], o4, 0, 0, 0);
+      o4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, rl[kc], o4, 0, 0, 0);
+      o4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, rh[kc], o4, 0, 0, 0);
+    }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       float* o = out_row(16 * rt + 4 * kq + v);
@@ -467,18 +555,22 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
 hipError_t launch_prefill(const CacheArgs& c, const PrefillArgs& a, hipStream_t stream) {
   if (a.n_seqs <= 0 || a.tiles <= 0) return hipSuccess;
   const dim3 grid(a.tiles, a.n_seqs, c.hkv);
-  if (a.waves == 16) {
-    if (a.bf16_only) hipLaunchKernelGGL((prefill_attn_kernel<16, true>), grid, dim3(64 * 16), 0, stream, c, a);
-    else hipLaunchKernelGGL((prefill_attn_kernel<16, false>), grid, dim3(64 * 16), 0, stream, c, a);
+  // (the host sizes the tiles for these shapes: 8 row blocks in bf16 mode)
+  if (a.bf16_only) {
+    if (a.blocks != 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_attn_kernel<8, true, 1>), grid, dim3(64 * 8), 0, stream, c, a);
+  } else if (a.blocks == 16) {
+    hipLaunchKernelGGL((prefill_attn_kernel<16, false, 1>), grid, dim3(64 * 16), 0, stream, c, a);
+  } else if (a.blocks == 8) {
+    hipLaunchKernelGGL((prefill_attn_kernel<8, false, 1>), grid, dim3(64 * 8), 0, stream, c, a);
   } else {
-    if (a.bf16_only) hipLaunchKernelGGL((prefill_attn_kernel<8, true>), grid, dim3(64 * 8), 0, stream, c, a);
-    else hipLaunchKernelGGL((prefill_attn_kernel<8, false>), grid, dim3(64 * 8), 0, stream, c, a);
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-int prefill_tiles(int n_new, int g, int waves) {
-  const int rows = 16 * waves;
+int prefill_tiles(int n_new, int g, int blocks) {
+  const int rows = 16 * blocks;
   return (n_new * g + rows - 1) / rows;
 }
 

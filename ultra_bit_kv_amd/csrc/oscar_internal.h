@@ -121,10 +121,10 @@ struct PrefillArgs {
   float* out;                    // fp32 [cu_new[n]][hq][128]
   int n_seqs;
   int tiles;                     // most query tiles of any sequence (grid x)
-  int waves;                     // 8 or 16 waves (16 query rows each) per work-group
+  int blocks;                    // query rows per work-group / 16: 8 or 16 (bf16 mode: 16)
   int bf16_only;                 // no sequence has INT2 rows below its chunk
 };
-int prefill_tiles(int n_new, int g, int waves);
+int prefill_tiles(int n_new, int g, int blocks);
 hipError_t launch_prefill(const CacheArgs& c, const PrefillArgs& a, hipStream_t stream);
 
 // Decoded rows of one cache row.
