@@ -261,10 +261,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
   // channel, channel 8u + j to row 16 j + u
   auto deposit2 = [&](const RawSlice (&r)[2], int buf) {
     if constexpr (BF) {
-      // the rows' own bits (kind 1) or zeros (kind 0)
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const u32x4 k0 = r[0].kind == 1 ? r[0].k : z, k1 = r[1].kind == 1 ? r[1].k : z;
-      const u32x4 a0 = r[0].kind == 1 ? r[0].v : z, a1 = r[1].kind == 1 ? r[1].v : z;
+      // the rows' own bits (kind 1) or zeros (kind 0: fetch leaves the
+      // words zero; no kind 2 below a bf16-mode chunk)
+      const u32x4 k0 = r[0].k, k1 = r[1].k, a0 = r[0].v, a1 = r[1].v;
       __builtin_memcpy(&sbf.k[buf][2 * st_tp][8 * st_u], &k0, 16);
       __builtin_memcpy(&sbf.k[buf][2 * st_tp + 1][8 * st_u], &k1, 16);
       // staged column of stage positions 2 tp, 2 tp + 1 (key kk of its
