@@ -298,8 +298,8 @@ int oscar_int2_decode_merge(const oscar_kv_cache* cache, int32_t n_seqs,
  * runs on until the process ends.  The call allocates nothing.
  * Limit: the records of a launch (at most 2048 sequences) must fit in the
  * scratch: a launch of n sequences keeps at most S splits per (sequence, KV
- * head, query-head pass) with n * Hkv * passes * (S + ceil(S / 16) if S > 32)
- * * record bytes <= 64 MiB, and a call whose longest row needs more splits
+ * head, query-head pass) with n * Hkv * passes * S * record bytes <= 64 MiB,
+ * and a call whose longest row needs more splits
  * returns OSCAR_ERR_WORKSPACE with nothing enqueued.  Every call on a GPU
  * shares that GPU's scratch: calls that overlap on one GPU (different
  * streams, or different host threads without ordering) race and must not be

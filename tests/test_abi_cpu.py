@@ -245,13 +245,12 @@ def test_bf16_description_checks(L, kw, status):
 
 def test_bf16_workspace_size(L):
     # g = 4 -> 4 heads per pass, one pass; a record is 8 + 4 * 128 floats.
-    # 16K records per launch: n = 4 -> 32 rows -> 256 splits (+16 chunk records)
+    # 16K records per launch: n = 4 -> 32 rows -> 256 splits
     b = bcache()
     rec = 8 + 4 * 128
     for n, cap in ((4, 256), (64, 32), (2048, 1)):
         rows = n * 8
-        per_row = cap + (-(-cap // 16) if cap > 32 else 0)
-        want = -(-(rows * per_row * rec * 4) // 256) * 256
+        want = -(-(rows * cap * rec * 4) // 256) * 256
         assert L.oscar_bf16_workspace_size(ctypes.byref(b), n) == want, n
     # the largest row always fits: 65536 pages = 32768 pairs needs 129 splits
     big = bcache(max_pages_per_seq=65536, max_seqs=4096)

@@ -123,15 +123,12 @@ int max_splits(const DecodeShape& sh, int n_seqs) {
   return (int)std::max<long long>(s, min_splits(sh));
 }
 
-// Split partial records of one decode launch (at most kMaxScanSeqs
-// sequences), then, when rows may have more than kMergeDirect splits, the
-// chunk records of the first merge launch.
+// Split partial records of one decode launch (at most kMaxScanSeqs sequences).
 size_t partials_bytes(const DecodeShape& sh, int n_seqs) {
   const size_t rec = (size_t)rec_words(sh.hp);
   const int ns = std::min(std::max(1, n_seqs), kMaxScanSeqs);
   const int cap = max_splits(sh, ns);
-  const size_t per_row = (size_t)cap + (cap > kMergeDirect ? (cap + kMergeChunk - 1) / kMergeChunk : 0);
-  return align_up((size_t)ns * sh.hkv * sh.passes * per_row * rec * sizeof(float));
+  return align_up((size_t)ns * sh.hkv * sh.passes * (size_t)cap * rec * sizeof(float));
 }
 
 size_t staging_bytes(const oscar_kv_config& c, int64_t n_tok) {
@@ -670,18 +667,12 @@ hipError_t device_scratch(void** out) {
   return hipSuccess;
 }
 
-// Most splits per row whose partial records (and the chunk records of the
-// first merge launch) fit in the scratch for a launch of n_seqs sequences.
+// Most splits per row whose partial records fit in the scratch for a launch
+// of n_seqs sequences.
 int scratch_splits(const DecodeShape& sh, int n_seqs) {
   const int ns = std::min(std::max(1, n_seqs), kMaxScanSeqs);
   const size_t per_split = (size_t)ns * sh.hkv * sh.passes * rec_words(sh.hp) * sizeof(float);
-  int best = 0;
-  for (int cap = 1; cap <= kMaxSplits; ++cap) {
-    const size_t recs = cap + (cap > kMergeDirect ? (cap + kMergeChunk - 1) / kMergeChunk : 0);
-    if (per_split * recs > kScratchBytes) break;
-    best = cap;
-  }
-  return best;
+  return (int)std::min<size_t>(kMaxSplits, kScratchBytes / per_split);
 }
 
 // noalloc: the split records go to the fixed scratch instead of `workspace`.

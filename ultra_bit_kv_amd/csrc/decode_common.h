@@ -274,11 +274,6 @@ __device__ __forceinline__ bool work_item(const SeqArgs& s, const ItemOrder& ord
 // o' = sum 2^(x - m) v'; two records combine exactly as
 //   M = max(m1, m2), l = l1 2^(m1 - M) + l2 2^(m2 - M), o' likewise.
 
-// First of two merge launches for rows with many splits: work-group =
-// (sequence, KV head, pass, chunk of kMergeChunk splits); thread = (head of
-// the pass, 4 channels).  Every thread loads its head's maxima and sums
-// itself, so the kernel has no LDS and no barrier.  Output: one record per
-// chunk, in the same layout, with row stride smax2.
 // Split records of sequence i: the host's count when the launch carries the
 // table, else from the device length.
 __device__ __forceinline__ int split_records(const CacheArgs& c, const SeqArgs& s,
@@ -288,53 +283,6 @@ __device__ __forceinline__ int split_records(const CacheArgs& c, const SeqArgs& 
   const bool ok = slot >= 0 && slot < c.max_seqs && len >= 1;
   return decode_splits(decode_work(ok ? len : 0, c.s_sink, c.s_keep, c.s_flush, c.ring_cap), quota,
                        smax);
-}
-
-template <int HP>
-__global__ __launch_bounds__(HP * 32 < 64 ? 64 : HP * 32) void lse_chunks_kernel(
-    CacheArgs c, SeqArgs s, SplitCounts sc, int quota, int passes, int smax, int smax2,
-    const float* __restrict__ partials, float* __restrict__ merged) {
-  constexpr int W = rec_words(HP), OO = rec_o_offset(HP);
-  const int x = blockIdx.x;
-  const int pass = x % passes, h = (x / passes) % c.hkv, i = x / (passes * c.hkv);
-  const int nh = min(HP, c.g - pass * HP);
-  const int r = threadIdx.x >> 5, c4 = threadIdx.x & 31;
-  const int ns = split_records(c, s, sc, i, quota, smax);
-  const int sp0 = blockIdx.y * kMergeChunk;
-  if (r >= nh || sp0 >= ns) return;
-  const int cnt = min(kMergeChunk, ns - sp0);
-  const size_t row = ((size_t)i * c.hkv + h) * passes + pass;
-  const float* rec = partials + (row * smax + sp0) * W;
-  float m[kMergeChunk], l[kMergeChunk];
-  float4_t o[kMergeChunk];
-#pragma unroll
-  for (int j = 0; j < kMergeChunk; ++j) {
-    const float* rj = rec + (size_t)(j < cnt ? j : 0) * W;
-    m[j] = rj[r];
-    l[j] = rj[HP + r];
-    o[j] = *(const float4_t*)(rj + OO + r * kD + 4 * c4);
-  }
-  float M = kNegInf;
-#pragma unroll
-  for (int j = 0; j < kMergeChunk; ++j)
-    if (j < cnt) M = fmaxf(M, m[j]);
-  float L = 0.0f;
-  float4_t O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < kMergeChunk; ++j) {
-    const float w = (j < cnt && m[j] != kNegInf) ? __builtin_amdgcn_exp2f(m[j] - M) : 0.0f;
-    L = __builtin_fmaf(w, l[j], L);
-    O[0] = __builtin_fmaf(w, o[j][0], O[0]);
-    O[1] = __builtin_fmaf(w, o[j][1], O[1]);
-    O[2] = __builtin_fmaf(w, o[j][2], O[2]);
-    O[3] = __builtin_fmaf(w, o[j][3], O[3]);
-  }
-  float* dst = merged + (row * smax2 + blockIdx.y) * W;
-  if (c4 == 0) {
-    dst[r] = M;
-    dst[HP + r] = L;
-  }
-  *(float4_t*)(dst + OO + r * kD + 4 * c4) = O;
 }
 
 // Lane slice of R_V for the un-rotation o = o' . R_V^T on the fp32 matrix
@@ -474,33 +422,142 @@ __global__ __launch_bounds__(512) void lse_merge_kernel(CacheArgs c, SeqArgs s, 
 }
 
 
-// The merge launch(es) of a split-K decode step: chunk folding when a row may
-// have more than kMergeDirect splits (its records follow the split records
-// in the workspace), then the final merge.
+// One launch for rows with many splits: work-group = (sequence, KV head,
+// pass, query head of the pass), 1024 threads = 32 split groups x 32
+// channel quads.  Thread (g, c4) folds splits g, g + 32, ... (8 per load
+// round, all 8 loads issued together) with a running maximum, the 32 group
+// states are folded through LDS, and (UNROT) output channel n = t / 8 of
+// o = o' . R_V^T is the sum of 8 partial products of 16 channels each (its
+// R_V row slice is loaded at entry, before any record).
+template <int HP, bool UNROT>
+__global__ __launch_bounds__(1024) void lse_wide_kernel(CacheArgs c, SeqArgs s, SplitCounts sc,
+                                                        int quota, int passes, int smax,
+                                                        const float* __restrict__ partials,
+                                                        float* __restrict__ out) {
+  constexpr int W = rec_words(HP), OO = rec_o_offset(HP);
+  constexpr int kG = 32, kRound = 8;
+  __shared__ float s_o[kG][kD];
+  __shared__ float s_ml[kG][2];
+  __shared__ float s_fin[kD];
+  const int t = threadIdx.x, g = t >> 5, c4 = t & 31;
+  const int x = blockIdx.x, hr = blockIdx.y;
+  const int pass = x % passes, h = (x / passes) % c.hkv, i = x / (passes * c.hkv);
+  const int nh = min(HP, c.g - pass * HP);
+  if (hr >= nh) return;   // (uniform)
+
+  const int n_out = t >> 3, part = t & 7;   // output channel, its 16-channel share of the sum
+  float rv[16];
+  if constexpr (UNROT) {
+    if (c.rot) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rv[e] = hadamard_entry(c.rot, n_out, 16 * part + e);
+    } else {
+      const float4_t* rg = (const float4_t*)(c.r_v + ((size_t)h * kD + n_out) * kD + 16 * part);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4_t q = rg[u];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rv[4 * u + e] = q[e];
+      }
+    }
+  }
+  bool ok;
+  if (sc.n > 0) {
+    ok = true;   // the host checked every slot and length of the call
+  } else {
+    const int slot = s.slots[i], len = s.lens[i];
+    ok = slot >= 0 && slot < c.max_seqs && len >= 1;
+  }
+  const int ns = split_records(c, s, sc, i, quota, smax);
+  const float* rec = partials + (((size_t)i * c.hkv + h) * passes + pass) * smax * W;
+  float M = kNegInf, L = 0.0f;
+  float4_t O = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = g; j0 < ns; j0 += kG * kRound) {
+    float m[kRound], l[kRound];
+    float4_t o[kRound];
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      const int j = j0 + kG * r;
+      const float* rj = rec + (size_t)(j < ns ? j : j0) * W;
+      m[r] = rj[hr];
+      l[r] = rj[HP + hr];
+      o[r] = *(const float4_t*)(rj + OO + hr * kD + 4 * c4);
+    }
+    float Mn = M;
+#pragma unroll
+    for (int r = 0; r < kRound; ++r)
+      if (j0 + kG * r < ns) Mn = fmaxf(Mn, m[r]);
+    const float sc0 = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+    L *= sc0;
+    O[0] *= sc0;
+    O[1] *= sc0;
+    O[2] *= sc0;
+    O[3] *= sc0;
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      const float w =
+          (j0 + kG * r < ns && m[r] != kNegInf) ? __builtin_amdgcn_exp2f(m[r] - Mn) : 0.0f;
+      L = __builtin_fmaf(w, l[r], L);
+      O[0] = __builtin_fmaf(w, o[r][0], O[0]);
+      O[1] = __builtin_fmaf(w, o[r][1], O[1]);
+      O[2] = __builtin_fmaf(w, o[r][2], O[2]);
+      O[3] = __builtin_fmaf(w, o[r][3], O[3]);
+    }
+    M = Mn;
+  }
+  *(float4_t*)&s_o[g][4 * c4] = O;
+  if (c4 == 0) {
+    s_ml[g][0] = M;
+    s_ml[g][1] = L;
+  }
+  __syncthreads();
+  if (t < kD) {
+    float Mf = kNegInf;
+#pragma unroll 8
+    for (int gg = 0; gg < kG; ++gg) Mf = fmaxf(Mf, s_ml[gg][0]);
+    float Lf = 0.0f, of = 0.0f;
+#pragma unroll 8
+    for (int gg = 0; gg < kG; ++gg) {
+      const float mg = s_ml[gg][0];
+      const float w = mg == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mg - Mf);
+      Lf = __builtin_fmaf(w, s_ml[gg][1], Lf);
+      of = __builtin_fmaf(w, s_o[gg][t], of);
+    }
+    s_fin[t] = ns > 0 ? of / Lf : 0.0f;
+  }
+  __syncthreads();
+  if (!ok) return;   // (uniform)
+  float* orow = out + ((size_t)i * c.hq + (size_t)h * c.g + pass * HP + hr) * kD;
+  if constexpr (!UNROT) {
+    if (t < kD) orow[t] = s_fin[t];
+    return;
+  }
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc = __builtin_fmaf(s_fin[16 * part + e], rv[e], acc);
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (part == 0) orow[n_out] = acc;
+}
+
+// The merge launch of a split-K decode step: the wide merge when a row may
+// have more than kMergeDirect splits, else the 16-row final merge.
 template <int HP, bool UNROT>
 hipError_t launch_merge(const CacheArgs& c, const SeqArgs& s, const DecodePlan& plan,
                         float* partials, float* out, hipStream_t stream) {
+  if (plan.smax > kMergeDirect) {
+    const dim3 g1(s.n_seqs * c.hkv * plan.passes, HP);
+    hipLaunchKernelGGL((lse_wide_kernel<HP, UNROT>), g1, dim3(1024), 0, stream, c, s, *plan.counts,
+                       plan.quota, plan.passes, plan.smax, partials, out);
+    return hipGetLastError();
+  }
   const int nh_full = c.g < HP ? c.g : HP;
   const int sb = 16 / nh_full;   // sequences per final-merge work-group (16 rows)
-  const float* recs = partials;
-  int chunk = 1, stride = plan.smax;
-  if (plan.smax > kMergeDirect) {
-    const int smax2 = (plan.smax + kMergeChunk - 1) / kMergeChunk;
-    float* merged = partials + (size_t)s.n_seqs * c.hkv * plan.passes * plan.smax * rec_words(HP);
-    const dim3 g1(s.n_seqs * c.hkv * plan.passes, smax2);
-    hipLaunchKernelGGL((lse_chunks_kernel<HP>), g1, dim3(HP * 32 < 64 ? 64 : HP * 32), 0, stream,
-                       c, s, *plan.counts, plan.quota, plan.passes, plan.smax, smax2, partials,
-                       merged);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    recs = merged;
-    chunk = kMergeChunk;
-    stride = smax2;
-  }
   const dim3 mgrid(c.hkv * plan.passes, (s.n_seqs + sb - 1) / sb);
   hipLaunchKernelGGL((lse_merge_kernel<HP, UNROT>), mgrid, dim3(512), 0, stream, c, s,
                      *plan.counts, plan.quota,
-                     plan.passes, plan.smax, chunk, stride, sb, recs, out);
+                     plan.passes, plan.smax, 1, plan.smax, sb, partials, out);
   return hipGetLastError();
 }
 

@@ -145,7 +145,6 @@ constexpr int kMaxSplits = 256;            // splits per (sequence, row), merge 
 constexpr int kMaxPairsPerSplit = 256;     // page ids staged per work-group
 constexpr int kMaxScanSeqs = 2048;         // sequences per decode launch
 constexpr int kMergeDirect = 32;           // most splits per row merged by one launch
-constexpr int kMergeChunk = 16;            // splits folded into one record by the first of two merge launches
 
 // Partial record of a (sequence, KV head, pass, split): the log2-domain
 // maxima and the sums of the pass's HP query heads, then their
@@ -207,8 +206,8 @@ struct ItemOrder {
 };
 
 // Split records of each sequence of a decode launch, as planned on the host,
-// for the merge launches: they then start loading records without reading
-// the sequence arrays first.  n = 0: the merge kernels derive the counts from
+// for the merge launch: it then starts loading records without reading the
+// sequence arrays first.  n = 0: the merge kernels derive the counts from
 // the device lengths.
 struct SplitCounts {
   int n;
