@@ -850,7 +850,8 @@ int oscar_int2_prefill_attn(const oscar_kv_cache* cache, int32_t n_seqs,
   if ((st = check_device()) != OSCAR_OK) return st;
   if (n_tok == 0) return OSCAR_OK;
   const PrefillArgs pa{seq_slots, len_before, cu_new, q_rot, k_rot, v_rot, out, n_seqs, tiles,
-                       blocks, bf16_only};
+                       blocks, bf16_only, div_magic((uint32_t)g),
+                       div_magic((uint32_t)std::max(1, ring_cap(c)))};
   return hip_status(launch_prefill(make_args(*cache), pa, (hipStream_t)stream));
 }
 

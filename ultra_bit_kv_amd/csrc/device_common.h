@@ -92,6 +92,19 @@ constexpr float kInvSqrtDf = 0x1.6a09e6p-4f;   // fp32(sqrt(2)) / 16
 
 __device__ __forceinline__ int bitrev7(int k) { return (int)(__brev((unsigned)k) >> 25); }
 
+// x / d and x % d (r) for 0 <= x < 2^31 and d >= 1, with m = floor(2^32 / d)
+// (m = 0 for d = 1): umulhi(x, m) is the quotient or one less (x m / 2^32
+// lies within x / 2^32 < 1 below x / d), so one correction makes it exact.
+__device__ __forceinline__ uint32_t div_by_magic(uint32_t x, uint32_t d, uint32_t m, uint32_t& r) {
+  uint32_t q = m ? __umulhi(x, m) : x;
+  r = x - q * d;
+  if (r >= d) {
+    q += 1;
+    r -= d;
+  }
+  return q;
+}
+
 __device__ __forceinline__ float hadamard_entry(int kind, int i, int k) {
   const int c = kind == 2 ? bitrev7(k) : k;
   return (__popc((unsigned)(i & c)) & 1) ? -kInvSqrtDf : kInvSqrtDf;

@@ -146,11 +146,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
   const int wrow0 = tile * kPfRows + 16 * RB * wave;              // the wave's first row
   bool colv[RB];
   int qpos[RB];
+  // (row / g and row % g by a magic multiplier: a plain division would keep
+  // a reciprocal in a vector register through the key loop)
+  auto div_g = [&](int x, uint32_t& rem) {
+    return (int)div_by_magic((uint32_t)x, (uint32_t)c.g, a.g_magic, rem);
+  };
+  uint32_t rem_;
   const int wg_last = min(rows, (tile + 1) * kPfRows) - 1;
-  const int kend = lb + wg_last / c.g + 1;                        // keys [0, kend)
+  const int kend = lb + div_g(wg_last, rem_) + 1;                 // keys [0, kend)
   const int w_last = min(rows, wrow0 + 16 * RB) - 1;
-  const int wave_kend = w_last >= wrow0 ? lb + w_last / c.g + 1 : 0;
-  const int wave_qmin = lb + wrow0 / c.g;                         // position of the wave's first row
+  const int wave_kend = w_last >= wrow0 ? lb + div_g(w_last, rem_) + 1 : 0;
+  const int wave_qmin = lb + div_g(wrow0, rem_);                  // position of the wave's first row
 
   half8 bq[RB][4];     // the query in fp16 (exact in the normal range), for the INT2 steps
   bf16x8 bqb[RB][4];   // and its bf16 bits, for the steps over bf16 rows
@@ -158,7 +164,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
   for (int rb = 0; rb < RB; ++rb) {
     const int row = wrow0 + 16 * rb + r16;
     colv[rb] = row < rows;
-    const int pj = colv[rb] ? row / c.g : 0, hl = colv[rb] ? row % c.g : 0;
+    uint32_t hl_u;
+    const int pj_u = div_g(row, hl_u);
+    const int pj = colv[rb] ? pj_u : 0, hl = colv[rb] ? (int)hl_u : 0;
     qpos[rb] = lb + pj;
     const uint16_t* qp = a.q_rot + ((size_t)(t0 + pj) * c.hq + (size_t)h * c.g + hl) * kD + 8 * qd;
 #pragma unroll
@@ -197,7 +205,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
       r.v = *(const u32x4*)(a.v_rot + o);
       r.kind = 1;
     } else if (p < c.s_sink || p >= sq) {   // sink slot p, or ring slot (p - S_sink) mod R
-      const int bs = p < c.s_sink ? p : c.sink_blocks * kPage + (p - c.s_sink) % c.ring_cap;
+      uint32_t rs;   // ring slot (p - S_sink) mod R
+      div_by_magic((uint32_t)max(p - c.s_sink, 0), (uint32_t)c.ring_cap, a.ring_magic, rs);
+      const int bs = p < c.s_sink ? p : c.sink_blocks * kPage + (int)rs;
       const uint16_t* blk = wrow + (size_t)(bs / kPage) * (2 * kPage * kD);
       const int tt = bs % kPage;
       r.k = *(const u32x4*)(blk + tt * kD + 8 * st_u);
@@ -212,7 +222,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
       const int ph = m < c.max_pages ? bt[m] : -1;
       if (ph < 0 || ph >= c.num_pages) return;
       const uint32_t* pg = (const uint32_t*)(c.pages + ((size_t)ph * c.hkv + h) * c.page_bytes);
-      const int gr = (8 * st_u) / c.group;
+      const int gr = (st_u * c.ng) >> 4;   // group of channels 8u .. 8u + 7: 8u / G with G = 128 / ng
       r.k = u32x4{pg[8 * sl + (st_u >> 1)] >> (16 * (st_u & 1)), pg[256 + 16 * gr + sl], 0u, 0u};
       r.v = u32x4{pg[128 + 2 * (16 * (sl >> 2) + st_u) + ((sl & 3) >> 1)] >> (16 * (sl & 1)),
                   pg[256 + 16 * c.ng + 16 * gr + sl], 0u, 0u};
@@ -493,7 +503,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
   auto out_row = [&](int rr) {   // output row of work-group row rr, or nullptr
     const int R = tile * kPfRows + rr;
     if (R >= rows) return (float*)nullptr;
-    return a.out + ((size_t)(t0 + R / c.g) * c.hq + (size_t)h * c.g + R % c.g) * kD;
+    uint32_t hr_;
+    const int pr = div_g(R, hr_);
+    return a.out + ((size_t)(t0 + pr) * c.hq + (size_t)h * c.g + hr_) * kD;
   };
   if (!c.unrot) {
     for (int k = tid; k < kPfRows * (kD / 4); k += kPfThreads) {

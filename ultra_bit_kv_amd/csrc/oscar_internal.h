@@ -121,9 +121,14 @@ struct PrefillArgs {
   float* out;                    // fp32 [cu_new[n]][hq][128]
   int n_seqs;
   int tiles;                     // most query tiles of any sequence (grid x)
-  int blocks;                    // query rows per work-group / 16: 8 or 16 (bf16 mode: 16)
+  int blocks;                    // query rows per work-group / 16: 8 or 16 (bf16 mode: 8)
   int bf16_only;                 // no sequence has INT2 rows below its chunk
+  uint32_t g_magic;              // floor(2^32 / g), 0 for g = 1 (see div_magic)
+  uint32_t ring_magic;           // floor(2^32 / ring_cap), 0 for ring_cap = 1
 };
+// floor(2^32 / d) for d >= 2, 0 for d = 1: with it a kernel divides without
+// a reciprocal held in vector registers (div_by_magic).
+inline uint32_t div_magic(uint32_t d) { return d > 1 ? (uint32_t)((1ull << 32) / d) : 0u; }
 int prefill_tiles(int n_new, int g, int blocks);
 hipError_t launch_prefill(const CacheArgs& c, const PrefillArgs& a, hipStream_t stream);
 
