@@ -189,6 +189,29 @@ def test_decode_many_splits_long_context():
         assert ok, (h, err, rel)
 
 
+@pytest.mark.parametrize("hq, hkv, group, length", [
+    (48, 4, 128, 12000),   # g = 12 in a 16-head pass: the merge's work-groups for heads 12..15 stay idle
+    (24, 6, 64, 9000),     # g = 4, two groups, three two-head waves
+])
+def test_decode_many_splits_head_layouts(hq, hkv, group, length):
+    """Rows with more than 32 splits (the one-launch wide merge) for head
+    layouts whose last query-head pass is partly empty, against the oracle."""
+    from ultra_bit_kv_amd import SeqBatch
+    w = get("c3_bs64").scaled(n_seqs=1, hq=hq, hkv=hkv, group=group, lengths=("list", (length,)))
+    lens = [length]
+    cache = make_cache(w, lens)
+    q_rot = fill(cache, w, lens, chunk=4096)
+    out = cache.decode(SeqBatch([0], lens), q_rot).cpu().numpy()
+    r_k, r_v = cache.host_r
+    worst = 0.0
+    for h in range(w.hkv):
+        want = oracle_decode(w, 0, h, length, r_k, r_v)
+        err, rel, ok = compare_attention(out[0, h * w.g:(h + 1) * w.g], want)
+        worst = max(worst, err)
+        assert ok, (hq, hkv, group, h, err, rel)
+    print(f"[case] many splits hq{hq} hkv{hkv} G{group} L{length} max_abs={worst:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("hq, hkv, group, lens", [
     (2, 2, 128, (300, 517)),     # one query head per KV head: two KV heads per wave, 1 head per pass
     (4, 2, 128, (400, 90)),      # g = 2, one group

@@ -105,9 +105,10 @@ def test_ragged_batch_groups(group):
     run_case(w, [333, 0, 400, 690], [150, 270, 0, 9])
 
 
-@pytest.mark.parametrize("hq,hkv", [(16, 2), (2, 2), (32, 2)])
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (2, 2), (32, 2), (24, 2), (12, 4)])
 def test_gqa_shapes(hq, hkv):
-    # GQA 8 (the Qwen3-32B shape's ratio, G = 128, flush 256), 1 and 16
+    # GQA 8 (the Qwen3-32B shape's ratio, G = 128, flush 256), 1, 16, 12 and 3 (row / g by a
+    # magic multiplier in the kernel: also g not a power of two)
     w = get("c5_qwen3_32b_step").scaled(n_seqs=2, hq=hq, hkv=hkv, lengths=("list", (800, 900)))
     run_case(w, [530, 640], [130, 77])
 
