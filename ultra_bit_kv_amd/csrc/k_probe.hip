@@ -22,21 +22,25 @@ __device__ __forceinline__ void store_wave(uint32_t acc, uint32_t* sink) {
   if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = acc;
 }
 
-// Sequential sweep: thread t of the grid reads elements t, t + T, t + 2T, ...
-// (T = grid threads), kUnroll loads issued before any is used.
+// Sequential sweep: work-group b reads its own contiguous slice of the
+// buffer (n16 / grid elements, rounded up to whole 4 KB steps), its 256
+// threads 16 bytes apart, kUnroll consecutive 4 KB steps issued before any
+// is used (each work-group walks its slice in address order).
 __global__ __launch_bounds__(kThreads) void probe_seq_kernel(const u32x4* __restrict__ buf,
                                                              size_t n16, uint32_t* __restrict__ sink) {
-  const size_t T = (size_t)gridDim.x * kThreads;
-  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t per = ((n16 + gridDim.x - 1) / gridDim.x + kThreads - 1) / kThreads * kThreads;
+  const size_t b0 = (size_t)blockIdx.x * per;
+  const size_t b1 = b0 + per < n16 ? b0 + per : n16;
+  size_t i = b0 + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + (kUnroll - 1) * T < n16; i += kUnroll * T) {
+  for (; i + (kUnroll - 1) * kThreads < b1; i += kUnroll * kThreads) {
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = buf[i + u * T];
+    for (int u = 0; u < kUnroll; ++u) v[u] = buf[i + u * kThreads];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= fold(v[u]);
   }
-  for (; i < n16; i += T) acc ^= fold(buf[i]);
+  for (; i < b1; i += kThreads) acc ^= fold(buf[i]);
   store_wave(acc, sink);
 }
 
