@@ -420,7 +420,7 @@ def timed_regions(enqueue, n, region, hold_cycles):
 
 
 def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0, region=0,
-            key_mode=0):
+            key_mode=0, split_only=False):
     """Decode steps of every row of workload w, cycling through n_layers
     copies of the populated cache (``rotation``: the cache's rotation kind).
 
@@ -431,7 +431,12 @@ def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0,
     of each step.  With graph_steps > 0 a further `graph_steps` steps are
     captured into one HIP graph and replayed `graph_reps` times (timed as a
     whole), which removes the host's launch path from the figure.  region > 0:
-    both passes time their steps in regions of at most `region` steps."""
+    both passes time their steps in regions of at most `region` steps.
+    split_only: a third pass times `steps` split launches alone, back to
+    back, each layer copy in turn at the length its last step of pass 2
+    left it (its cache as that step decoded it), with events only at the
+    ends of each region (``split_only_ms``, ``split_only_bytes``): the
+    kernel's duration without the event records of pass 2 between launches."""
     import torch
     from ultra_bit_kv_amd import SeqBatch, as_bf16
 
@@ -513,6 +518,21 @@ def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0,
     # pass 2: the same number of steps with events around each launch
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
     ms_step_ev, host2, _ = timed_regions(lambda j: step(warm + steps + j, evs[j]), steps, reg, hold)
+    split_only_res = {}
+    if split_only:
+        last = {}
+        for j in range(steps):
+            last[(warm + steps + j) % n_layers] = warm + steps + j
+        order = sorted(last)
+
+        def split_step(j):
+            li = order[j % len(order)]
+            layers[li].decode_partials(steps_in[last[li] // n_layers]["dec"], q_rot)
+
+        ms_so, _, _ = timed_regions(split_step, steps, reg, hold)
+        so_bytes = [algorithmic_bytes(w, [int(L) + last[order[j % len(order)]] // n_layers for L in lens0],
+                                      key_mode) for j in range(steps)]
+        split_only_res = {"split_only_ms": ms_so, "split_only_bytes": float(np.mean(so_bytes))}
     app = [a.elapsed_time(b) for a, b, c, d in evs]
     split = [b.elapsed_time(c) for a, b, c, d in evs]
     merge = [c.elapsed_time(d) for a, b, c, d in evs]
@@ -527,7 +547,7 @@ def measure(w, n_layers, steps, warmup, rotation=0, graph_steps=0, graph_reps=0,
            "split_pct": pct(split), "step_pct": pct(whole),
            "bytes": float(np.mean(byts)), "setup_s": setup_s, "warm": warm,
            "host_ms_per_step": 1e3 * host1 / steps, "hold_ms": 1e3 * hold / CLOCK_HZ,
-           "steps_per_timed_region": reg,
+           "steps_per_timed_region": reg, **split_only_res,
            # pass 1 waited on the host if the host took longer to queue the
            # steps than the spin kernel held the GPU (after retries)
            "host_bound": bound1}
@@ -744,9 +764,12 @@ def main():
     log(f"headline {args.config}: {args.steps} steps after {args.warmup} warm-up")
     # (regions of at most 32 steps behind the spin kernel: a longer queue of
     # these launches blocks the host, see timed_regions)
-    m = measure(get(args.config), args.layers, args.steps, args.warmup, region=32)
+    m = measure(get(args.config), args.layers, args.steps, args.warmup, region=32, split_only=True)
     w, lens0, n = m["w"], m["lens0"], m["n"]
-    achieved = m["bytes"] / (m["split_ms"] * 1e-3) / 1e9
+    # the split kernel's rate from the split-only pass (events at the ends of
+    # back-to-back split launches); the per-launch events of pass 2 add their
+    # own gaps to each launch (decode_split_ms below)
+    achieved = m["split_only_bytes"] / (m["split_only_ms"] * 1e-3) / 1e9
     src_hash = decode_source_hash()
     res = {
         "metric": "INT2 paged decode-attn tokens/s + achieved HBM GB/s vs peak (bs1, bs64)",
@@ -769,6 +792,7 @@ def main():
             "step": "rotate_quant_append(1 token/seq) + int2_decode_partials + int2_decode_merge",
             "decode_ms": m["dec_ms"], "decode_split_ms": m["split_ms"],
             "decode_split_ms_pct": m["split_pct"], "step_ms_events": m["step_pct"],
+            "decode_split_only_ms": m["split_only_ms"],
             "decode_merge_ms": m["merge_ms"], "append_ms": m["append_ms"],
             "ms_per_step_with_kernel_events": m["ms_step_ev"],
             "decode_call_GBs": m["bytes"] / (m["dec_ms"] * 1e-3) / 1e9,
@@ -779,7 +803,9 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic(src_hash),
-            "kernel": "int2_decode_kernel", "algorithmic_bytes_per_launch": m["bytes"],
+            "kernel": "int2_decode_kernel", "algorithmic_bytes_per_launch": m["split_only_bytes"],
+            "duration": "split-only pass: back-to-back split launches over the layer copies, "
+                        "events at the region ends",
         },
         "cpu_baseline": None,
         "setup_s": m["setup_s"],
