@@ -85,6 +85,8 @@ constexpr int pf_lds() {
 }
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_v __attribute__((ext_vector_type(2)));
 
 // One position's K and V row slice (8 channels) as fetched from HBM, before
 // decoding: kind 0 = zero row (past the end or an unmapped page), 1 = bf16
@@ -393,9 +395,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
       if constexpr (!BF) {
         half8 ph, pl;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          ph[r] = (_Float16)p[0][r];
-          pl[r] = (_Float16)(p[0][r] - (float)ph[r]);
+        for (int r = 0; r < 8; r += 2) {   // fp16 hi / lo, one packed conversion per pair
+          const half2_t h2 = __builtin_convertvector(float2_v{p[0][r], p[0][r + 1]}, half2_t);
+          const float2_v hf = __builtin_convertvector(h2, float2_v);
+          const half2_t l2 = __builtin_convertvector(float2_v{p[0][r] - hf[0], p[0][r + 1] - hf[1]}, half2_t);
+          ph[r] = h2[0];
+          ph[r + 1] = h2[1];
+          pl[r] = l2[0];
+          pl[r + 1] = l2[1];
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -406,15 +413,22 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
           acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pl, acc[0][j], 0, 0, 0);
         }
       } else {
-        // P as bf16 hi + lo (about 16 significant bits)
+        // P as bf16 hi + lo (about 16 significant bits): one packed
+        // conversion per pair, the hi halves back to fp32 by shift and mask
         bf16x8 ph[RB], pl[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const __bf16 hh = (__bf16)p[rb][r];
-            ph[rb][r] = hh;
-            pl[rb][r] = (__bf16)(p[rb][r] - (float)hh);
+          for (int r = 0; r < 8; r += 2) {
+            const bf16x2_t h2 = __builtin_convertvector(float2_v{p[rb][r], p[rb][r + 1]}, bf16x2_t);
+            const uint32_t hb = __builtin_bit_cast(uint32_t, h2);
+            const float h0 = __builtin_bit_cast(float, hb << 16);
+            const float h1 = __builtin_bit_cast(float, hb & 0xFFFF0000u);
+            const bf16x2_t l2 = __builtin_convertvector(float2_v{p[rb][r] - h0, p[rb][r + 1] - h1}, bf16x2_t);
+            ph[rb][r] = h2[0];
+            ph[rb][r + 1] = h2[1];
+            pl[rb][r] = l2[0];
+            pl[rb][r + 1] = l2[1];
           }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
