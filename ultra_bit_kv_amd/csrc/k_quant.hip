@@ -61,8 +61,8 @@ __device__ __forceinline__ void group_order_stats(uint32_t key0, uint32_t key1, 
     for (int g = 1; g < NG; ++g) r = gi == g ? v[g] : r;
     return r;
   };
-  auto count = [&](unsigned long long b0, unsigned long long b1, int g) {
-    return __popcll((b0 >> (g * LPG)) & kLow) + __popcll((b1 >> (g * LPG)) & kLow);
+  auto count = [&](unsigned long long b0, unsigned long long b1, int g) -> int {
+    return (int)(__popcll((b0 >> (g * LPG)) & kLow) + __popcll((b1 >> (g * LPG)) & kLow));
   };
 #pragma unroll
   for (int bit = 15; bit >= 0; --bit) {
