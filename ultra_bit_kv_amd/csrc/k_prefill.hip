@@ -132,8 +132,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, qd = lane >> 4;
-  const int i = blockIdx.y, h = blockIdx.z;
-  const int tile = a.tiles - 1 - (int)blockIdx.x;   // longest causal ranges first
+  // work-group b takes tile rank b / (sequences x KV heads): the tiles with
+  // the longest causal ranges of every (sequence, KV head) first, the
+  // shortest last, so the launch does not end on a long tile
+  const int groups = a.n_seqs * c.hkv;
+  const int b = (int)blockIdx.x, grp = b % groups;
+  const int i = grp / c.hkv, h = grp % c.hkv;
+  const int tile = a.tiles - 1 - b / groups;
   const int slot = a.slots[i], lb = a.len_before[i];
   const int t0 = a.cu_new[i], n_new = a.cu_new[i + 1] - t0;
   const int rows = n_new * c.g;
@@ -579,7 +584,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
 
 hipError_t launch_prefill(const CacheArgs& c, const PrefillArgs& a, hipStream_t stream) {
   if (a.n_seqs <= 0 || a.tiles <= 0) return hipSuccess;
-  const dim3 grid(a.tiles, a.n_seqs, c.hkv);
+  const dim3 grid((unsigned)a.tiles * (unsigned)a.n_seqs * (unsigned)c.hkv);
   // (the host sizes the tiles for these shapes: 8 row blocks in bf16 mode)
   if (a.bf16_only) {
     if (a.blocks != 8) return hipErrorInvalidValue;
