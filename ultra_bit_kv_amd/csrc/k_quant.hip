@@ -556,10 +556,12 @@ __global__ __launch_bounds__(128) void append_one_kernel(CacheArgs c, QuantArgs 
   if (jobs.kind) {   // structured rotation: whole rows, thread rows tid / 16 and tid / 16 + 8
     int tslot[2], tpos[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < 2; ++k) {   // (loads from a clamped index, all issued together)
       const int tok = 16 * tb + (threadIdx.x >> 4) + 8 * k;
-      tslot[k] = job != 2 && tok < n_tok ? s.slots[tok] : -1;
-      tpos[k] = job != 2 && tok < n_tok ? s.lens[tok] : -1;
+      const int tc = min(tok, n_tok - 1);
+      const int none = job != 2 && tok < n_tok ? 0 : -1;   // (or-ed in: the loads stay unconditional)
+      tslot[k] = s.slots[tc] | none;
+      tpos[k] = s.lens[tc] | none;
     }
     auto out8 = [&](int tok, int c0, const uint16_t (&bits)[8]) {
       u32x4_r w;
@@ -600,14 +602,16 @@ __global__ __launch_bounds__(128) void append_one_kernel(CacheArgs c, QuantArgs 
   const int j = 32 * z + 16 * wave + (lane & 15);
   // the cache rows and positions of this lane's four output tokens, loaded
   // ahead of the rotation (they only decide where the results go)
+  // (loads from a clamped index, unconditional: a load under a branch makes
+  // the compiler wait for it at the branch's end, one round trip per token)
   int tslot[4], tpos[4];
-  if (job != 2) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int tok = 16 * tb + (lane >> 4) + 4 * v;
-      tslot[v] = tok < n_tok ? s.slots[tok] : -1;
-      tpos[v] = tok < n_tok ? s.lens[tok] : -1;
-    }
+  for (int v = 0; v < 4; ++v) {
+    const int tok = 16 * tb + (lane >> 4) + 4 * v;
+    const int tc = min(tok, n_tok - 1);
+    const int none = job != 2 && tok < n_tok ? 0 : -1;   // (or-ed in: the loads stay unconditional)
+    tslot[v] = s.slots[tc] | none;
+    tpos[v] = s.lens[tc] | none;
   }
   float rb[kD / 4];
   load_r_slice(jd.r + (size_t)(h / jd.g) * kD * kD, j, rb);
